@@ -1,0 +1,808 @@
+/*
+ * da2_oracle.c -- plain, slow, obviously correct CPU oracle for the
+ * DraftAttention2 hot path (low-resolution-guided, block-sparse, mixed
+ * FP8 / MXFP4 / skip attention for video diffusion transformers).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant generator with the HIP library: every rule below
+ * is restated from the pages, in fp64 unless a step fixes another precision.
+ *
+ * Sources (page titles; sections named on each page):
+ *   [DA2]  "DraftAttention2: Fast Video Diffusion with Low-Resolution-Guided
+ *           Mixed-Precision Attention" -- Sec. 3.1 (Eq. 1 pooled descriptors,
+ *           Eq. 2 draft map, joint allocation of sparsity and precision),
+ *           Sec. 3.3 (fused quantization and reordering, phased execution,
+ *           cross-precision accumulation), App. B.3/B.4 (shared
+ *           normalization), App. C.1 (routing and precision formats),
+ *           App. C.2 (spatial packing).
+ *   [DA1]  "DraftAttention: Fast Video Diffusion via Low-Resolution Attention
+ *           Guidance" -- abstract (reorder, block-sparse attention, restore
+ *           the original order).
+ * Number formats: OCP 8-bit floating point (E4M3, "fn" variant: no inf,
+ * max 448) and OCP Microscaling v1.0 (E2M1 elements, E8M0 scale, blocks of
+ * 32), as fixed for this path in place of the paper's INT8/NVFP4 paths.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - token order of the input is (frame, y, x) raster;
+ *   - regions are the 8x8 grid of every frame (C = 64 tokens, no padding),
+ *     region order frame-major then raster, raster order inside a region;
+ *   - pooled sums run over the 64 tokens in region order, in fp64;
+ *   - logits are fixed-order fma chains over channels 0..d-1 times 1/sqrt(d);
+ *   - exp of the draft softmax is a Cody-Waite reduction (fdlibm's split of
+ *     ln 2) followed by a degree-13 Taylor polynomial in Horner form;
+ *   - row sums of the draft softmax are sequential over key regions;
+ *   - ranking key is the bit pattern of fp32(A); ties by ascending pair index;
+ *   - quotas: T8 = round-half-up(hi_bp * n / 10^4), Tk likewise for hi+lo;
+ *   - FP8 Q/K scale per 64-token block, FP8 V scale per channel over all
+ *     tokens, MXFP4 groups along channels for Q/K and along keys for V;
+ *   - attention weights are quantized per 64-key tile relative to the
+ *     running max: FP8 as e4m3(w * 2^8) * 2^-8, MXFP4 per 32 keys.
+ * Parity: every exported function is pinned by a CPU test against closed
+ * forms, brute force or a library routine (see the test suite).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_BLK 64 /* tokens per region: an 8x8 square */
+
+/* ------------------------------------------------------------------ */
+/* bf16 and IEEE helpers                                               */
+/* ------------------------------------------------------------------ */
+static float bf16f(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static uint32_t f32bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+/* ------------------------------------------------------------------ */
+/* O1 layout: [DA2] App. C.2 and Sec. 3.3 (compact spatial packing).    */
+/* For H_v, W_v multiples of 8 and C = 64 the balanced, minimum-        */
+/* perimeter partition of each frame is the 8x8 grid.                   */
+/* perm[pos] = original token index of reordered position pos.         */
+/* ------------------------------------------------------------------ */
+int or_layout(int F, int Hv, int Wv, int32_t *perm)
+{
+    if (F <= 0 || Hv <= 0 || Wv <= 0 || Hv % 8 || Wv % 8)
+        return -1;
+    int Ry = Hv / 8, Rx = Wv / 8;
+    for (int f = 0; f < F; f++)
+        for (int ry = 0; ry < Ry; ry++)
+            for (int rx = 0; rx < Rx; rx++) {
+                int a = (f * Ry + ry) * Rx + rx;
+                for (int iy = 0; iy < 8; iy++)
+                    for (int ix = 0; ix < 8; ix++) {
+                        int pos = a * OR_BLK + iy * 8 + ix;
+                        int y = ry * 8 + iy, x = rx * 8 + ix;
+                        perm[pos] = (f * Hv + y) * Wv + x;
+                    }
+            }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O2 pooled descriptors: [DA2] Sec. 3.1 Eq. (1), App. C.1.             */
+/* X is one head, [N][d] bf16.  avg[a][c] = (sum over the region in     */
+/* region order, fp64) / n_a with n_a = 64; mx[a][c] = signed max,      */
+/* first occurrence kept on equal values.                               */
+/* ------------------------------------------------------------------ */
+void or_pool_head(const uint16_t *X, int d, const int32_t *perm, int R,
+                  double *avg, float *mx)
+{
+    for (int a = 0; a < R; a++)
+        for (int c = 0; c < d; c++) {
+            double s = 0.0;
+            float m = bf16f(X[(size_t)perm[a * OR_BLK] * d + c]);
+            for (int i = 0; i < OR_BLK; i++) {
+                float v = bf16f(X[(size_t)perm[a * OR_BLK + i] * d + c]);
+                s += (double)v;
+                if (v > m)
+                    m = v;
+            }
+            avg[(size_t)a * d + c] = s / (double)OR_BLK;
+            mx[(size_t)a * d + c] = m;
+        }
+}
+
+/* ------------------------------------------------------------------ */
+/* exp used by the draft softmax.  Cody-Waite reduction with the split  */
+/* of ln 2 into a 32-significant-bit head and its remainder (the fdlibm */
+/* constants), then the Taylor series of e^r to degree 13 in Horner     */
+/* form with fma, then scaling by 2^k.  Arguments below -708 give 0 so  */
+/* every nonzero result is a normal number.                             */
+/* ------------------------------------------------------------------ */
+static const double OR_LN2_HI = 6.93147180369123816490e-01;
+static const double OR_LN2_LO = 1.90821492927058770002e-10;
+static const double OR_INV_LN2 = 1.44269504088896338700e+00;
+
+void or_exp_constants(double *out /* [3 + 14] */)
+{
+    out[0] = OR_LN2_HI;
+    out[1] = OR_LN2_LO;
+    out[2] = OR_INV_LN2;
+    double fact = 1.0;
+    for (int j = 0; j <= 13; j++) {
+        if (j > 0)
+            fact *= (double)j; /* j! is exact in double for j <= 18 */
+        out[3 + j] = 1.0 / fact;
+    }
+}
+
+double or_exp(double x)
+{
+    if (x < -708.0)
+        return 0.0;
+    double coef[17];
+    or_exp_constants(coef);
+    double k = rint(x * OR_INV_LN2);
+    double r = fma(-k, OR_LN2_HI, x);
+    r = fma(-k, OR_LN2_LO, r);
+    double p = coef[3 + 13];
+    for (int j = 12; j >= 0; j--)
+        p = fma(p, r, coef[3 + j]);
+    return ldexp(p, (int)k);
+}
+
+/* ------------------------------------------------------------------ */
+/* O3..O5 draft map and ranking keys: [DA2] Sec. 3.1 Eq. (2), App. C.1  */
+/* (both branches normalize over key regions).                          */
+/* A = (1 - lambda) softmax(avgQ avgK^T / sqrt d)                        */
+/*   +      lambda  softmax(maxQ maxK^T / sqrt d);                        */
+/* key = bit pattern of fp32(A) (RNE).  Optionally returns A in fp64.   */
+/* ------------------------------------------------------------------ */
+static double fma_chain(const double *x, const double *y, int d)
+{
+    double acc = 0.0;
+    for (int c = 0; c < d; c++)
+        acc = fma(x[c], y[c], acc);
+    return acc;
+}
+
+static void softmax_row_spec(const double *L, int R, double *p)
+{
+    double m = L[0];
+    for (int b = 1; b < R; b++)
+        if (L[b] > m)
+            m = L[b];
+    double Z = 0.0;
+    for (int b = 0; b < R; b++) {
+        p[b] = or_exp(L[b] - m);
+        Z += p[b];
+    }
+    for (int b = 0; b < R; b++)
+        p[b] = p[b] / Z;
+}
+
+void or_draft_keys_head(const double *qa, const double *ka, const float *qm,
+                        const float *km, int R, int d, double lambda,
+                        uint32_t *keys, double *A /* may be NULL */)
+{
+    double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double w0 = 1.0 - lambda;
+    double *qmd = malloc(sizeof(double) * (size_t)R * d);
+    double *kmd = malloc(sizeof(double) * (size_t)R * d);
+    for (size_t i = 0; i < (size_t)R * d; i++) {
+        qmd[i] = (double)qm[i];
+        kmd[i] = (double)km[i];
+    }
+#pragma omp parallel
+    {
+        double *La = malloc(sizeof(double) * R), *Lm = malloc(sizeof(double) * R);
+        double *pa = malloc(sizeof(double) * R), *pm = malloc(sizeof(double) * R);
+#pragma omp for schedule(dynamic, 4)
+        for (int a = 0; a < R; a++) {
+            for (int b = 0; b < R; b++) {
+                La[b] = fma_chain(qa + (size_t)a * d, ka + (size_t)b * d, d) * inv_sqrt_d;
+                Lm[b] = fma_chain(qmd + (size_t)a * d, kmd + (size_t)b * d, d) * inv_sqrt_d;
+            }
+            softmax_row_spec(La, R, pa);
+            softmax_row_spec(Lm, R, pm);
+            for (int b = 0; b < R; b++) {
+                double t0 = w0 * pa[b];
+                double t1 = lambda * pm[b];
+                double Ab = t0 + t1;
+                keys[(size_t)a * R + b] = f32bits((float)Ab);
+                if (A)
+                    A[(size_t)a * R + b] = Ab;
+            }
+        }
+        free(La);
+        free(Lm);
+        free(pa);
+        free(pm);
+    }
+    free(qmd);
+    free(kmd);
+}
+
+/* Logits of both branches for one head (the first step of the keys above),
+ * exported so the tests can pin the fixed evaluation order. */
+void or_draft_logits_head(const double *qa, const double *ka, const float *qm,
+                          const float *km, int R, int d, double *La, double *Lm)
+{
+    double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double *x = malloc(sizeof(double) * d), *y = malloc(sizeof(double) * d);
+    for (int a = 0; a < R; a++)
+        for (int b = 0; b < R; b++) {
+            La[(size_t)a * R + b] = fma_chain(qa + (size_t)a * d, ka + (size_t)b * d, d) * inv_sqrt_d;
+            for (int c = 0; c < d; c++) {
+                x[c] = (double)qm[(size_t)a * d + c];
+                y[c] = (double)km[(size_t)b * d + c];
+            }
+            Lm[(size_t)a * R + b] = fma_chain(x, y, d) * inv_sqrt_d;
+        }
+    free(x);
+    free(y);
+}
+
+/* ------------------------------------------------------------------ */
+/* O6 quotas: [DA2] Sec. 3.1 (T = T16 + T8 + T4), App. C.1 (integer     */
+/* quotas from precision fractions).  Budgets in basis points of n      */
+/* (n = R^2 for head scope, R for row scope), rounded half up.          */
+/* ------------------------------------------------------------------ */
+void or_quotas(int64_t n, int32_t hi_bp, int32_t lo_bp, int64_t *T8, int64_t *Tk)
+{
+    *T8 = ((int64_t)hi_bp * n + 5000) / 10000;
+    *Tk = ((int64_t)(hi_bp + lo_bp) * n + 5000) / 10000;
+}
+
+/* ------------------------------------------------------------------ */
+/* O7 ranking: [DA2] Sec. 3.1 (ranking across the whole map of a head), */
+/* App. C.1 (ties by region-pair index), Sec. 3.2 (larger score ->      */
+/* higher precision).  Order = key descending, pair index ascending;    */
+/* rank < T8 -> tier 8, rank < Tk -> tier 4, else 0 (skip).             */
+/* scope 0: one ranking over all R^2 pairs; scope 1: one per query row. */
+/* ------------------------------------------------------------------ */
+static int cmp_u64(const void *x, const void *y)
+{
+    uint64_t a = *(const uint64_t *)x, b = *(const uint64_t *)y;
+    return (a > b) - (a < b);
+}
+
+void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T8, int64_t Tk,
+                  uint8_t *tier)
+{
+    int64_t n = (int64_t)R * R;
+    if (scope == 0) {
+        /* composite: larger key first (complemented), then smaller index */
+        uint64_t *ord = malloc(sizeof(uint64_t) * (size_t)n);
+        for (int64_t i = 0; i < n; i++)
+            ord[i] = ((uint64_t)(~keys[i]) << 32) | (uint64_t)i;
+        qsort(ord, (size_t)n, sizeof(uint64_t), cmp_u64);
+        for (int64_t r = 0; r < n; r++) {
+            uint32_t idx = (uint32_t)(ord[r] & 0xffffffffu);
+            tier[idx] = r < T8 ? 8 : (r < Tk ? 4 : 0);
+        }
+        free(ord);
+    } else {
+        uint64_t *ord = malloc(sizeof(uint64_t) * (size_t)R);
+        for (int a = 0; a < R; a++) {
+            for (int b = 0; b < R; b++)
+                ord[b] = ((uint64_t)(~keys[(size_t)a * R + b]) << 32) | (uint64_t)b;
+            qsort(ord, (size_t)R, sizeof(uint64_t), cmp_u64);
+            for (int r = 0; r < R; r++) {
+                uint32_t b = (uint32_t)(ord[r] & 0xffffffffu);
+                tier[(size_t)a * R + b] = r < T8 ? 8 : (r < Tk ? 4 : 0);
+            }
+        }
+        free(ord);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Plan for a whole [B,H] problem: pooling, keys, ranking.               */
+/* q, k: [B,H,N,d] contiguous bf16.  Outputs (each may be NULL except    */
+/* keys and tier): avg [B,H,R,d] fp64 (Q then K arrays), mx f32.         */
+/* ------------------------------------------------------------------ */
+int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+            const uint16_t *k, int32_t hi_bp, int32_t lo_bp, double lambda, int scope,
+            uint32_t *keys, uint8_t *tier, double *qavg, double *kavg, float *qmx,
+            float *kmx)
+{
+    int N = F * Hv * Wv, R = N / OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * N);
+    if (or_layout(F, Hv, Wv, perm)) {
+        free(perm);
+        return -1;
+    }
+    int64_t T8, Tk;
+    or_quotas(scope == 0 ? (int64_t)R * R : (int64_t)R, hi_bp, lo_bp, &T8, &Tk);
+    double *qa = malloc(sizeof(double) * (size_t)R * d), *ka = malloc(sizeof(double) * (size_t)R * d);
+    float *qm = malloc(sizeof(float) * (size_t)R * d), *km = malloc(sizeof(float) * (size_t)R * d);
+    for (int bh = 0; bh < B * H; bh++) {
+        const uint16_t *qh = q + (size_t)bh * N * d, *kh = k + (size_t)bh * N * d;
+        or_pool_head(qh, d, perm, R, qa, qm);
+        or_pool_head(kh, d, perm, R, ka, km);
+        if (qavg) memcpy(qavg + (size_t)bh * R * d, qa, sizeof(double) * (size_t)R * d);
+        if (kavg) memcpy(kavg + (size_t)bh * R * d, ka, sizeof(double) * (size_t)R * d);
+        if (qmx) memcpy(qmx + (size_t)bh * R * d, qm, sizeof(float) * (size_t)R * d);
+        if (kmx) memcpy(kmx + (size_t)bh * R * d, km, sizeof(float) * (size_t)R * d);
+        or_draft_keys_head(qa, ka, qm, km, R, d, lambda, keys + (size_t)bh * R * R, NULL);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; bh++)
+        or_rank_head(keys + (size_t)bh * R * R, R, scope, T8, Tk, tier + (size_t)bh * R * R);
+    free(qa); free(ka); free(qm); free(km); free(perm);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Number formats (OCP FP8 E4M3 "fn", OCP MX E2M1 + E8M0).              */
+/* Rounding to nearest, ties to even; magnitudes above the largest      */
+/* finite value saturate.  The sign bit is the sign bit of the input,   */
+/* also when the magnitude rounds to zero.                              */
+/* ------------------------------------------------------------------ */
+double or_e4m3_value(int code)
+{
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp((double)m, -9);
+    return s ? -v : v;
+}
+
+double or_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e ? ldexp(1.0 + m / 2.0, e - 1) : 0.5 * m;
+    return s ? -v : v;
+}
+
+uint8_t or_e4m3_encode(double v)
+{
+    uint8_t sgn = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= 448.0)
+        return sgn | 0x7e;
+    int e;
+    frexp(a, &e);
+    int E = e - 1;                       /* floor(log2 a) for a > 0 */
+    if (a == 0.0 || E < -6)
+        E = -6;                          /* subnormal spacing 2^-9 */
+    double q = ldexp(1.0, E - 3);
+    double r = rint(a / q) * q;          /* a / q is exact */
+    if (r == 0.0)
+        return sgn;
+    frexp(r, &e);
+    E = e - 1;
+    if (E < -6)
+        return sgn | (uint8_t)ldexp(r, 9);             /* subnormal: r = m 2^-9 */
+    int m = (int)ldexp(r, 3 - E) - 8;                   /* r = (1 + m/8) 2^E */
+    return sgn | (uint8_t)(((E + 7) << 3) | m);
+}
+
+uint8_t or_e2m1_encode(double v)
+{
+    uint8_t sgn = signbit(v) ? 8 : 0;
+    double a = fabs(v);
+    if (a >= 6.0)
+        return sgn | 7;
+    int e;
+    frexp(a, &e);
+    int E = e - 1;
+    if (a == 0.0 || E < 0)
+        E = 0;                           /* subnormal spacing 0.5 */
+    double q = ldexp(1.0, E - 1);
+    double r = rint(a / q) * q;
+    if (r == 0.0)
+        return sgn;
+    if (r < 1.0)
+        return sgn | 1;                  /* 0.5 */
+    frexp(r, &e);
+    E = e - 1;
+    int m = (int)ldexp(r, 1 - E) - 2;    /* r = (1 + m/2) 2^E */
+    return sgn | (uint8_t)(((E + 1) << 1) | m);
+}
+
+/* E8M0 exponent of an MX block: floor(log2 amax) - 2 (2 = exponent of the
+ * largest E2M1 power of two), clamped to the E8M0 range; amax = 0 -> -127. */
+int or_mx_exponent(double amax)
+{
+    if (amax == 0.0)
+        return -127;
+    int e;
+    frexp(amax, &e);
+    int E = (e - 1) - 2;
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
+    return E;
+}
+
+/* ------------------------------------------------------------------ */
+/* O8/O9 operand quantization: [DA2] Sec. 3.3 (fused quantization and   */
+/* reordering).  All outputs are in reordered token order pos.          */
+/*  Q/K FP8 : one fp32 scale per 64-token block: s = amax/448 (fp32     */
+/*            division), code = e4m3(fp32(x * (448/amax))).              */
+/*  Q/K MX  : per token, per 32 channels: E8M0 + E2M1 codes of x 2^-E.  */
+/*  V FP8   : one fp32 scale per channel over all N tokens.             */
+/*  V MX    : per channel, per 32 consecutive keys of a block.          */
+/* Codes are stored one per byte (E2M1 in the low nibble).              */
+/* ------------------------------------------------------------------ */
+static void fp8_scale(float amax, float *s, float *inv)
+{
+    if (amax == 0.0f) {
+        *s = 1.0f;
+        *inv = 0.0f;
+    } else {
+        *s = amax / 448.0f;
+        *inv = 448.0f / amax;
+    }
+}
+
+void or_quant_qk_head(const uint16_t *X, int N, int d, const int32_t *perm,
+                      uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
+{
+    int R = N / OR_BLK;
+    for (int a = 0; a < R; a++) {
+        float amax = 0.0f;
+        for (int i = 0; i < OR_BLK; i++)
+            for (int c = 0; c < d; c++) {
+                float v = fabsf(bf16f(X[(size_t)perm[a * OR_BLK + i] * d + c]));
+                if (v > amax) amax = v;
+            }
+        float s, inv;
+        fp8_scale(amax, &s, &inv);
+        s8[a] = s;
+        for (int i = 0; i < OR_BLK; i++)
+            for (int c = 0; c < d; c++) {
+                float v = bf16f(X[(size_t)perm[a * OR_BLK + i] * d + c]);
+                float prod = v * inv;
+                c8[((size_t)a * OR_BLK + i) * d + c] = or_e4m3_encode((double)prod);
+            }
+    }
+    for (int pos = 0; pos < N; pos++)
+        for (int g = 0; g < d / 32; g++) {
+            double amax = 0.0;
+            for (int j = 0; j < 32; j++) {
+                double v = fabs((double)bf16f(X[(size_t)perm[pos] * d + 32 * g + j]));
+                if (v > amax) amax = v;
+            }
+            int E = or_mx_exponent(amax);
+            e4[(size_t)pos * (d / 32) + g] = (uint8_t)(E + 127);
+            for (int j = 0; j < 32; j++) {
+                double v = (double)bf16f(X[(size_t)perm[pos] * d + 32 * g + j]);
+                c4[(size_t)pos * d + 32 * g + j] = or_e2m1_encode(ldexp(v, -E));
+            }
+        }
+}
+
+/* V: c8 [N][d] codes, s8 [d] scales, c4 [N][d] codes, e4 [R][2][d] exponents */
+void or_quant_v_head(const uint16_t *X, int N, int d, const int32_t *perm,
+                     uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
+{
+    int R = N / OR_BLK;
+    for (int c = 0; c < d; c++) {
+        float amax = 0.0f;
+        for (int n = 0; n < N; n++) {
+            float v = fabsf(bf16f(X[(size_t)n * d + c]));
+            if (v > amax) amax = v;
+        }
+        float s, inv;
+        fp8_scale(amax, &s, &inv);
+        s8[c] = s;
+        for (int pos = 0; pos < N; pos++) {
+            float v = bf16f(X[(size_t)perm[pos] * d + c]);
+            float prod = v * inv;
+            c8[(size_t)pos * d + c] = or_e4m3_encode((double)prod);
+        }
+    }
+    for (int a = 0; a < R; a++)
+        for (int g = 0; g < 2; g++)
+            for (int c = 0; c < d; c++) {
+                double amax = 0.0;
+                for (int j = 0; j < 32; j++) {
+                    int pos = a * OR_BLK + 32 * g + j;
+                    double v = fabs((double)bf16f(X[(size_t)perm[pos] * d + c]));
+                    if (v > amax) amax = v;
+                }
+                int E = or_mx_exponent(amax);
+                e4[((size_t)a * 2 + g) * d + c] = (uint8_t)(E + 127);
+                for (int j = 0; j < 32; j++) {
+                    int pos = a * OR_BLK + 32 * g + j;
+                    double v = (double)bf16f(X[(size_t)perm[pos] * d + c]);
+                    c4[(size_t)pos * d + c] = or_e2m1_encode(ldexp(v, -E));
+                }
+            }
+}
+
+/* Whole-problem quantization into canonical layouts:
+ *   qk8 [B,H,N,d] codes, qks8 [B,H,R] scales, qk4 [B,H,N,d], qke4 [B,H,N,d/32]
+ *   v8  [B,H,N,d],       vs8  [B,H,d],        v4  [B,H,N,d], ve4  [B,H,R,2,d] */
+int or_quant_qk(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
+                uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
+{
+    int N = F * Hv * Wv, R = N / OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * N);
+    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; bh++)
+        or_quant_qk_head(X + (size_t)bh * N * d, N, d, perm, c8 + (size_t)bh * N * d,
+                         s8 + (size_t)bh * R, c4 + (size_t)bh * N * d,
+                         e4 + (size_t)bh * N * (d / 32));
+    free(perm);
+    return 0;
+}
+
+int or_quant_v(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
+               uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
+{
+    int N = F * Hv * Wv, R = N / OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * N);
+    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * H; bh++)
+        or_quant_v_head(X + (size_t)bh * N * d, N, d, perm, c8 + (size_t)bh * N * d,
+                        s8 + (size_t)bh * d, c4 + (size_t)bh * N * d,
+                        e4 + (size_t)bh * R * 2 * d);
+    free(perm);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O10 attention over kept tiles: [DA2] Sec. 3.1 (all retained blocks   */
+/* of a query share one softmax normalization and output), Sec. 3.3     */
+/* (consecutive precision phases; shared online-softmax statistics and  */
+/* accumulator), App. B.3 (w = e^{s - h}, Z^q = sum of unquantized w),  */
+/* App. B.4 (O = sum(w_hat V_hat) / Z^q), App. C.1 (rows with no        */
+/* retained key return zero).                                           */
+/* Phases in descending precision: tier 16 (oracle-only, unquantized    */
+/* operands and weights), tier 8 (FP8), tier 4 (MXFP4); tiles ascending */
+/* inside a phase; running max updated once per 64-key tile.            */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int N, d, R;
+    const int32_t *perm;
+    double *qf, *kf, *vf;    /* unquantized, reordered [N][d] */
+    double *q8, *k8, *v8;    /* FP8 dequantized */
+    double *q4, *k4, *v4;    /* MXFP4 dequantized */
+} head_ops;
+
+static void head_ops_build(head_ops *h, const uint16_t *q, const uint16_t *k,
+                           const uint16_t *v, int N, int d, const int32_t *perm)
+{
+    int R = N / OR_BLK;
+    size_t nd = (size_t)N * d;
+    h->N = N; h->d = d; h->R = R; h->perm = perm;
+    double **arrs[9] = {&h->qf, &h->kf, &h->vf, &h->q8, &h->k8, &h->v8, &h->q4, &h->k4, &h->v4};
+    for (int i = 0; i < 9; i++)
+        *arrs[i] = malloc(sizeof(double) * nd);
+    uint8_t *c8 = malloc(nd), *c4 = malloc(nd);
+    uint8_t *e4 = malloc(nd / 32 + (size_t)R * 2 * d);
+    float *s8 = malloc(sizeof(float) * (size_t)(R > d ? R : d));
+    const uint16_t *src[3] = {q, k, v};
+    double *full[3] = {h->qf, h->kf, h->vf};
+    double *d8[3] = {h->q8, h->k8, h->v8};
+    double *d4[3] = {h->q4, h->k4, h->v4};
+    for (int t = 0; t < 3; t++) {
+        for (int pos = 0; pos < N; pos++)
+            for (int c = 0; c < d; c++)
+                full[t][(size_t)pos * d + c] = (double)bf16f(src[t][(size_t)perm[pos] * d + c]);
+        if (t < 2) {
+            or_quant_qk_head(src[t], N, d, perm, c8, s8, c4, e4);
+            for (int pos = 0; pos < N; pos++)
+                for (int c = 0; c < d; c++) {
+                    size_t i = (size_t)pos * d + c;
+                    d8[t][i] = or_e4m3_value(c8[i]) * (double)s8[pos / OR_BLK];
+                    d4[t][i] = ldexp(or_e2m1_value(c4[i]), (int)e4[(size_t)pos * (d / 32) + c / 32] - 127);
+                }
+        } else {
+            or_quant_v_head(src[t], N, d, perm, c8, s8, c4, e4);
+            for (int pos = 0; pos < N; pos++)
+                for (int c = 0; c < d; c++) {
+                    size_t i = (size_t)pos * d + c;
+                    int a = pos / OR_BLK, g = (pos % OR_BLK) / 32;
+                    d8[t][i] = or_e4m3_value(c8[i]) * (double)s8[c];
+                    d4[t][i] = ldexp(or_e2m1_value(c4[i]), (int)e4[((size_t)a * 2 + g) * d + c] - 127);
+                }
+        }
+    }
+    free(c8); free(c4); free(e4); free(s8);
+}
+
+static void head_ops_free(head_ops *h)
+{
+    double *arrs[9] = {h->qf, h->kf, h->vf, h->q8, h->k8, h->v8, h->q4, h->k4, h->v4};
+    for (int i = 0; i < 9; i++)
+        free(arrs[i]);
+}
+
+/* Weight quantizers for one 64-key tile, w[64] in key order. */
+static void quant_weights(int tier, const double *w, double *wq)
+{
+    if (tier == 16) {
+        for (int j = 0; j < OR_BLK; j++) wq[j] = w[j];
+    } else if (tier == 8) {
+        for (int j = 0; j < OR_BLK; j++)
+            wq[j] = ldexp(or_e4m3_value(or_e4m3_encode(ldexp(w[j], 8))), -8);
+    } else {
+        for (int g = 0; g < 2; g++) {
+            double amax = 0.0;
+            for (int j = 0; j < 32; j++)
+                if (fabs(w[32 * g + j]) > amax) amax = fabs(w[32 * g + j]);
+            int E = or_mx_exponent(amax);
+            for (int j = 0; j < 32; j++)
+                wq[32 * g + j] = ldexp(or_e2m1_value(or_e2m1_encode(ldexp(w[32 * g + j], -E))), E);
+        }
+    }
+}
+
+/* Optional per-row trace for the tests: for every processed key (in
+ * processing order) its reordered position, tier, s_hat, w, w_hat and the
+ * running max after its tile. */
+typedef struct {
+    int64_t cap, n;
+    int32_t *key;
+    int32_t *tier;
+    double *s, *w, *wq, *m;
+    double Z;
+} row_trace;
+
+static void attention_row(const head_ops *h, const uint8_t *tier_row, int u,
+                          double *out, row_trace *tr)
+{
+    int d = h->d, R = h->R;
+    double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double m = -INFINITY, Z = 0.0;
+    double *acc = calloc(d, sizeof(double));
+    double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
+    static const int phases[3] = {16, 8, 4};
+    for (int ph = 0; ph < 3; ph++) {
+        int p = phases[ph];
+        const double *Q = p == 16 ? h->qf : (p == 8 ? h->q8 : h->q4);
+        const double *K = p == 16 ? h->kf : (p == 8 ? h->k8 : h->k4);
+        const double *V = p == 16 ? h->vf : (p == 8 ? h->v8 : h->v4);
+        for (int b = 0; b < R; b++) {
+            if (tier_row[b] != p)
+                continue;
+            double tmax = -INFINITY;
+            for (int j = 0; j < OR_BLK; j++) {
+                const double *qu = Q + (size_t)u * d, *kv = K + ((size_t)b * OR_BLK + j) * d;
+                double dot = 0.0;
+                for (int c = 0; c < d; c++)
+                    dot += qu[c] * kv[c];
+                s[j] = dot * inv_sqrt_d;
+                if (s[j] > tmax) tmax = s[j];
+            }
+            double mn = tmax > m ? tmax : m;
+            double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
+            Z *= alpha;
+            for (int c = 0; c < d; c++)
+                acc[c] *= alpha;
+            for (int j = 0; j < OR_BLK; j++) {
+                w[j] = exp(s[j] - mn);
+                Z += w[j];
+            }
+            quant_weights(p, w, wq);
+            for (int j = 0; j < OR_BLK; j++) {
+                const double *vv = V + ((size_t)b * OR_BLK + j) * d;
+                for (int c = 0; c < d; c++)
+                    acc[c] += wq[j] * vv[c];
+            }
+            m = mn;
+            if (tr) {
+                for (int j = 0; j < OR_BLK && tr->n < tr->cap; j++, tr->n++) {
+                    tr->key[tr->n] = b * OR_BLK + j;
+                    tr->tier[tr->n] = p;
+                    tr->s[tr->n] = s[j];
+                    tr->w[tr->n] = w[j];
+                    tr->wq[tr->n] = wq[j];
+                    tr->m[tr->n] = mn;
+                }
+            }
+        }
+    }
+    for (int c = 0; c < d; c++)
+        out[c] = Z > 0.0 ? acc[c] / Z : 0.0;
+    if (tr)
+        tr->Z = Z;
+    free(acc);
+}
+
+/* q,k,v: [B,H,N,d] bf16; tier: [B,H,R,R] in {0,4,8,16}.
+ * qblocks: nqb query regions evaluated for every (b,h) (NULL -> all R).
+ * out: [B,H,nqb,64,d] fp64, row (j,i) belongs to original token
+ * perm[qblocks[j]*64 + i] (restore is done by the caller's indexing). */
+int or_attention(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+                 const uint16_t *k, const uint16_t *v, const uint8_t *tier, int nqb,
+                 const int32_t *qblocks, double *out)
+{
+    int N = F * Hv * Wv, R = N / OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * N);
+    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    if (!qblocks) nqb = R;
+    for (int bh = 0; bh < B * H; bh++) {
+        head_ops h;
+        size_t off = (size_t)bh * N * d;
+        head_ops_build(&h, q + off, k + off, v + off, N, d, perm);
+        const uint8_t *tm = tier + (size_t)bh * R * R;
+#pragma omp parallel for schedule(dynamic, 8)
+        for (int r = 0; r < nqb * OR_BLK; r++) {
+            int j = r / OR_BLK, i = r % OR_BLK;
+            int a = qblocks ? qblocks[j] : j;
+            attention_row(&h, tm + (size_t)a * R, a * OR_BLK + i,
+                          out + (((size_t)bh * nqb + j) * OR_BLK + i) * d, NULL);
+        }
+        head_ops_free(&h);
+    }
+    free(perm);
+    return 0;
+}
+
+/* Trace of one query row (reordered position u) of one head.  Returns the
+ * number of processed keys (may exceed cap; only cap entries are written). */
+int64_t or_attention_trace(int F, int Hv, int Wv, int d, const uint16_t *q,
+                           const uint16_t *k, const uint16_t *v, const uint8_t *tier,
+                           int u, int64_t cap, int32_t *key, int32_t *tr_tier, double *s,
+                           double *w, double *wq, double *m, double *Z, double *out)
+{
+    int N = F * Hv * Wv, R = N / OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * N);
+    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    head_ops h;
+    head_ops_build(&h, q, k, v, N, d, perm);
+    row_trace tr = {cap, 0, key, tr_tier, s, w, wq, m, 0.0};
+    attention_row(&h, tier + (size_t)(u / OR_BLK) * R, u, out, &tr);
+    *Z = tr.Z;
+    head_ops_free(&h);
+    free(perm);
+    return tr.n;
+}
+
+/* ------------------------------------------------------------------ */
+/* O12 dense reference: softmax(Q K^T / sqrt d) V in fp64 over all N    */
+/* keys, two passes (max, then exp and sums), for chosen original-order */
+/* query rows.  out: [B,H,nrows,d].                                     */
+/* ------------------------------------------------------------------ */
+int or_dense(int B, int H, int N, int d, const uint16_t *q, const uint16_t *k,
+             const uint16_t *v, int nrows, const int32_t *rows, double *out)
+{
+    double inv_sqrt_d = 1.0 / sqrt((double)d);
+    for (int bh = 0; bh < B * H; bh++) {
+        size_t off = (size_t)bh * N * d;
+        double *kf = malloc(sizeof(double) * (size_t)N * d), *vf = malloc(sizeof(double) * (size_t)N * d);
+        for (size_t i = 0; i < (size_t)N * d; i++) {
+            kf[i] = bf16f(k[off + i]);
+            vf[i] = bf16f(v[off + i]);
+        }
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int r = 0; r < nrows; r++) {
+            double *qu = malloc(sizeof(double) * d), *s = malloc(sizeof(double) * N);
+            for (int c = 0; c < d; c++)
+                qu[c] = bf16f(q[off + (size_t)rows[r] * d + c]);
+            double m = -INFINITY;
+            for (int n = 0; n < N; n++) {
+                double dot = 0.0;
+                for (int c = 0; c < d; c++)
+                    dot += qu[c] * kf[(size_t)n * d + c];
+                s[n] = dot * inv_sqrt_d;
+                if (s[n] > m) m = s[n];
+            }
+            double Z = 0.0;
+            double *o = out + ((size_t)bh * nrows + r) * d;
+            for (int c = 0; c < d; c++) o[c] = 0.0;
+            for (int n = 0; n < N; n++) {
+                double w = exp(s[n] - m);
+                Z += w;
+                for (int c = 0; c < d; c++)
+                    o[c] += w * vf[(size_t)n * d + c];
+            }
+            for (int c = 0; c < d; c++) o[c] /= Z;
+            free(qu);
+            free(s);
+        }
+        free(kf);
+        free(vf);
+    }
+    return 0;
+}

@@ -1,0 +1,294 @@
+"""ctypes front end of the CPU oracle (liboracle.so, built from da2_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The product library
+never loads this module or the shared object behind it.
+
+All tensors are numpy arrays.  Q/K/V are uint16 bfloat16 bit patterns,
+contiguous [B, H, N, d] with tokens in (frame, y, x) raster order.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "da2_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+BLK = 64
+
+GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+           "-shared", "-Wall", "-o", _LIB, _SRC, "-lm"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain C, no contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = list(GCC_CMD)
+        cmd[cmd.index(_LIB)] = tmp
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        i32, i64, f64 = C.c_int32, C.c_int64, C.c_double
+        L.or_layout.argtypes = [C.c_int, C.c_int, C.c_int, P]
+        L.or_layout.restype = C.c_int
+        L.or_pool_head.argtypes = [P, C.c_int, P, C.c_int, P, P]
+        L.or_exp_constants.argtypes = [P]
+        L.or_exp.argtypes = [f64]
+        L.or_exp.restype = f64
+        L.or_draft_keys_head.argtypes = [P, P, P, P, C.c_int, C.c_int, f64, P, P]
+        L.or_draft_logits_head.argtypes = [P, P, P, P, C.c_int, C.c_int, P, P]
+        L.or_quotas.argtypes = [i64, i32, i32, P, P]
+        L.or_rank_head.argtypes = [P, C.c_int, C.c_int, i64, i64, P]
+        L.or_plan.argtypes = [C.c_int] * 6 + [P, P, i32, i32, f64, C.c_int, P, P, P, P, P, P]
+        L.or_plan.restype = C.c_int
+        L.or_e4m3_value.argtypes = [C.c_int]
+        L.or_e4m3_value.restype = f64
+        L.or_e2m1_value.argtypes = [C.c_int]
+        L.or_e2m1_value.restype = f64
+        L.or_e4m3_encode.argtypes = [f64]
+        L.or_e4m3_encode.restype = C.c_uint8
+        L.or_e2m1_encode.argtypes = [f64]
+        L.or_e2m1_encode.restype = C.c_uint8
+        L.or_mx_exponent.argtypes = [f64]
+        L.or_mx_exponent.restype = C.c_int
+        L.or_quant_qk.argtypes = [C.c_int] * 6 + [P, P, P, P, P]
+        L.or_quant_qk.restype = C.c_int
+        L.or_quant_v.argtypes = [C.c_int] * 6 + [P, P, P, P, P]
+        L.or_quant_v.restype = C.c_int
+        L.or_attention.argtypes = [C.c_int] * 6 + [P, P, P, P, C.c_int, P, P]
+        L.or_attention.restype = C.c_int
+        L.or_attention_trace.argtypes = [C.c_int] * 4 + [P, P, P, P, C.c_int, i64,
+                                                         P, P, P, P, P, P, P, P]
+        L.or_attention_trace.restype = i64
+        L.or_dense.argtypes = [C.c_int] * 4 + [P, P, P, C.c_int, P, P]
+        L.or_dense.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _u16(x):
+    x = np.ascontiguousarray(x)
+    assert x.dtype == np.uint16, x.dtype
+    return x
+
+
+# ---------------------------------------------------------------- layout
+def layout(F, Hv, Wv) -> np.ndarray:
+    perm = np.empty(F * Hv * Wv, dtype=np.int32)
+    if lib().or_layout(F, Hv, Wv, _p(perm)):
+        raise ValueError("H_v and W_v must be positive multiples of 8")
+    return perm
+
+
+# ---------------------------------------------------------------- draft
+def pool_head(X: np.ndarray, F, Hv, Wv):
+    """X: [N, d] uint16 -> (avg [R, d] f64, max [R, d] f32)."""
+    X = _u16(X)
+    N, d = X.shape
+    R = N // BLK
+    perm = layout(F, Hv, Wv)
+    avg = np.empty((R, d), np.float64)
+    mx = np.empty((R, d), np.float32)
+    lib().or_pool_head(_p(X), d, _p(perm), R, _p(avg), _p(mx))
+    return avg, mx
+
+
+def exp_constants() -> np.ndarray:
+    out = np.empty(17, np.float64)
+    lib().or_exp_constants(_p(out))
+    return out
+
+
+def exp_spec(x) -> np.ndarray:
+    f = lib().or_exp
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([f(float(v)) for v in x.reshape(-1)]).reshape(x.shape)
+
+
+def draft_keys_head(qa, ka, qm, km, lam, want_A=False):
+    qa = np.ascontiguousarray(qa, np.float64)
+    ka = np.ascontiguousarray(ka, np.float64)
+    qm = np.ascontiguousarray(qm, np.float32)
+    km = np.ascontiguousarray(km, np.float32)
+    R, d = qa.shape
+    keys = np.empty((R, R), np.uint32)
+    A = np.empty((R, R), np.float64) if want_A else None
+    lib().or_draft_keys_head(_p(qa), _p(ka), _p(qm), _p(km), R, d, float(lam), _p(keys),
+                             _p(A) if want_A else None)
+    return (keys, A) if want_A else keys
+
+
+def draft_logits_head(qa, ka, qm, km):
+    qa = np.ascontiguousarray(qa, np.float64)
+    ka = np.ascontiguousarray(ka, np.float64)
+    qm = np.ascontiguousarray(qm, np.float32)
+    km = np.ascontiguousarray(km, np.float32)
+    R, d = qa.shape
+    La = np.empty((R, R), np.float64)
+    Lm = np.empty((R, R), np.float64)
+    lib().or_draft_logits_head(_p(qa), _p(ka), _p(qm), _p(km), R, d, _p(La), _p(Lm))
+    return La, Lm
+
+
+def quotas(n, hi_bp, lo_bp):
+    t8 = C.c_int64()
+    tk = C.c_int64()
+    lib().or_quotas(int(n), int(hi_bp), int(lo_bp), C.byref(t8), C.byref(tk))
+    return t8.value, tk.value
+
+
+def rank_head(keys: np.ndarray, T8, Tk, scope=0) -> np.ndarray:
+    keys = np.ascontiguousarray(keys, np.uint32)
+    R = keys.shape[0]
+    tier = np.empty((R, R), np.uint8)
+    lib().or_rank_head(_p(keys), R, int(scope), int(T8), int(Tk), _p(tier))
+    return tier
+
+
+def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False):
+    """Full plan for [B,H,N,d] inputs -> dict(keys [B,H,R,R] u32, tier u8, ...)."""
+    q = _u16(q)
+    k = _u16(k)
+    B, H, N, d = q.shape
+    R = N // BLK
+    keys = np.empty((B, H, R, R), np.uint32)
+    tier = np.empty((B, H, R, R), np.uint8)
+    out = {"keys": keys, "tier": tier}
+    ptrs = [None] * 4
+    if descriptors:
+        out["qavg"] = np.empty((B, H, R, d), np.float64)
+        out["kavg"] = np.empty((B, H, R, d), np.float64)
+        out["qmax"] = np.empty((B, H, R, d), np.float32)
+        out["kmax"] = np.empty((B, H, R, d), np.float32)
+        ptrs = [_p(out[n]) for n in ("qavg", "kavg", "qmax", "kmax")]
+    rc = lib().or_plan(B, H, F, Hv, Wv, d, _p(q), _p(k), int(hi_bp), int(lo_bp), float(lam),
+                       int(scope), _p(keys), _p(tier), *ptrs)
+    if rc:
+        raise ValueError("bad shape")
+    return out
+
+
+# ---------------------------------------------------------------- formats
+def e4m3_value(code: int) -> float:
+    return lib().or_e4m3_value(int(code))
+
+
+def e2m1_value(code: int) -> float:
+    return lib().or_e2m1_value(int(code))
+
+
+def e4m3_encode(x) -> np.ndarray:
+    f = lib().or_e4m3_encode
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([f(float(v)) for v in x.reshape(-1)], np.uint8).reshape(x.shape)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    f = lib().or_e2m1_encode
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([f(float(v)) for v in x.reshape(-1)], np.uint8).reshape(x.shape)
+
+
+def mx_exponent(amax: float) -> int:
+    return lib().or_mx_exponent(float(amax))
+
+
+def quant_qk(X, F, Hv, Wv):
+    """-> dict(c8 [B,H,N,d] u8, s8 [B,H,R] f32, c4 [B,H,N,d] u8, e4 [B,H,N,d/32] u8),
+    token axis in reordered position order."""
+    X = _u16(X)
+    B, H, N, d = X.shape
+    R = N // BLK
+    o = {"c8": np.empty((B, H, N, d), np.uint8), "s8": np.empty((B, H, R), np.float32),
+         "c4": np.empty((B, H, N, d), np.uint8), "e4": np.empty((B, H, N, d // 32), np.uint8)}
+    lib().or_quant_qk(B, H, F, Hv, Wv, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
+                      _p(o["e4"]))
+    return o
+
+
+def quant_v(X, F, Hv, Wv):
+    """-> dict(c8 [B,H,N,d], s8 [B,H,d], c4 [B,H,N,d], e4 [B,H,R,2,d])."""
+    X = _u16(X)
+    B, H, N, d = X.shape
+    R = N // BLK
+    o = {"c8": np.empty((B, H, N, d), np.uint8), "s8": np.empty((B, H, d), np.float32),
+         "c4": np.empty((B, H, N, d), np.uint8), "e4": np.empty((B, H, R, 2, d), np.uint8)}
+    lib().or_quant_v(B, H, F, Hv, Wv, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
+                     _p(o["e4"]))
+    return o
+
+
+# ---------------------------------------------------------------- attention
+def attention(q, k, v, tier, F, Hv, Wv, qblocks=None):
+    """Tiered attention.  qblocks=None: all rows, returned [B,H,N,d] in original
+    token order.  Otherwise [B,H,len(qblocks),64,d]; row (j,i) is original
+    token perm[qblocks[j]*64+i]."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    tier = np.ascontiguousarray(tier, np.uint8)
+    B, H, N, d = q.shape
+    R = N // BLK
+    assert tier.shape == (B, H, R, R)
+    if qblocks is None:
+        out = np.empty((B, H, R, BLK, d), np.float64)
+        lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), R, None, _p(out))
+        perm = layout(F, Hv, Wv)
+        full = np.empty((B, H, N, d), np.float64)
+        full[:, :, perm, :] = out.reshape(B, H, N, d)
+        return full
+    qb = np.ascontiguousarray(qblocks, np.int32)
+    out = np.empty((B, H, len(qb), BLK, d), np.float64)
+    lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), len(qb), _p(qb),
+                       _p(out))
+    return out
+
+
+def attention_trace(q, k, v, tier, F, Hv, Wv, u, cap=None):
+    """One head ([N,d] inputs, [R,R] tier), one reordered query position u."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    tier = np.ascontiguousarray(tier, np.uint8)
+    N, d = q.shape
+    if cap is None:
+        cap = N + 64
+    key = np.empty(cap, np.int32)
+    tt = np.empty(cap, np.int32)
+    s, w, wq, m = (np.empty(cap, np.float64) for _ in range(4))
+    Z = C.c_double()
+    out = np.empty(d, np.float64)
+    n = lib().or_attention_trace(F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), int(u), cap,
+                                 _p(key), _p(tt), _p(s), _p(w), _p(wq), _p(m), C.byref(Z),
+                                 _p(out))
+    n = min(n, cap)
+    return {"key": key[:n], "tier": tt[:n], "s": s[:n], "w": w[:n], "wq": wq[:n], "m": m[:n],
+            "Z": Z.value, "out": out}
+
+
+def dense(q, k, v, rows):
+    """fp64 softmax attention over all keys for original-order rows -> [B,H,len,d]."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, N, d = q.shape
+    rows = np.ascontiguousarray(rows, np.int32)
+    out = np.empty((B, H, len(rows), d), np.float64)
+    lib().or_dense(B, H, N, d, _p(q), _p(k), _p(v), len(rows), _p(rows), _p(out))
+    return out

@@ -1,0 +1,236 @@
+"""Pins of the oracle's tiered attention (CPU).
+
+* an oracle-only full-precision tier (16) over every tile equals dense
+  softmax attention (textbook closed form, numpy);
+* with skipped tiles the full-precision result equals brute-force masked
+  attention, rows with no kept key are zero (App. C.1), and the
+  sparsification bound of Eq. (4) holds;
+* relabelling frames (regions move with them) leaves the restored output
+  unchanged;
+* the quantized tile loop is re-derived from its trace: phase order, tile
+  order, running max, w, quantized weights, Z and the output (App. B.3/B.4),
+  and the B.4 identity holds.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from video_diffusion_dit_frame_amd import synth
+from video_diffusion_dit_frame_amd.synth import bf16_bits_to_f32
+from tests.test_oracle_formats import E2M1_POS, brute_nearest
+
+F, HV, WV, D = 2, 16, 16, 64
+
+
+@pytest.fixture(scope="module")
+def qkv():
+    return synth.make_qkv(1, 2, F, HV, WV, D, 77, True)
+
+
+def f64(x):
+    return bf16_bits_to_f32(x).astype(np.float64)
+
+
+def dense_np(q, k, v, mask=None):
+    s = q @ k.T / math.sqrt(q.shape[1])
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(s - m)
+    Z = w.sum(axis=1, keepdims=True)
+    return np.where(Z > 0, (w @ v) / np.where(Z > 0, Z, 1.0), 0.0), w / np.where(Z > 0, Z, 1.0)
+
+
+def token_mask(orc, tier_rr):
+    """[R,R] tier map -> [N,N] keep mask in original token order."""
+    perm = orc.layout(F, HV, WV)
+    R = tier_rr.shape[0]
+    blk = np.empty(F * HV * WV, np.int64)
+    blk[perm] = np.arange(perm.size) // 64
+    return tier_rr[blk[:, None], blk[None, :]] > 0
+
+
+def test_full_tier_equals_dense(orc, qkv):
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    tier = np.full((1, 2, R, R), 16, np.uint8)
+    out = orc.attention(q, k, v, tier, F, HV, WV)
+    for h in range(2):
+        want, _ = dense_np(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]))
+        assert np.abs(out[0, h] - want).max() <= 1e-12 * np.abs(want).max()
+    rows = np.arange(0, q.shape[2], 29, dtype=np.int32)
+    dn = orc.dense(q, k, v, rows)
+    assert np.abs(dn - out[:, :, rows]).max() <= 1e-12
+
+
+def test_full_tier_masked_equals_brute_force(orc, qkv):
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    rng = np.random.default_rng(4)
+    tier = np.where(rng.random((1, 2, R, R)) < 0.4, 16, 0).astype(np.uint8)
+    tier[0, 0, 3, :] = 0  # an empty query region
+    out = orc.attention(q, k, v, tier, F, HV, WV)
+    for h in range(2):
+        mask = token_mask(orc, tier[0, h])
+        want, _ = dense_np(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), mask)
+        assert np.abs(out[0, h] - want).max() <= 1e-12
+    perm = orc.layout(F, HV, WV)
+    assert (out[0, 0, perm[3 * 64:4 * 64]] == 0).all()
+
+
+def test_constant_values_give_constant_output(orc, qkv):
+    q, k, _ = qkv
+    v = np.full_like(q, 0x3FC0)  # 1.5
+    R = q.shape[2] // 64
+    rng = np.random.default_rng(8)
+    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 16, 0).astype(np.uint8)
+    tier[..., 0] = 16
+    out = orc.attention(q, k, v, tier, F, HV, WV)
+    assert np.abs(out - 1.5).max() <= 1e-13
+
+
+def test_sparsification_bound_eq4(orc, qkv):
+    """||O_dense - O_Omega|| <= 2 V_max delta_u (full-precision kept tiles)."""
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    rng = np.random.default_rng(12)
+    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 16, 0).astype(np.uint8)
+    tier[..., 0] = 16
+    out = orc.attention(q, k, v, tier, F, HV, WV)
+    for h in range(2):
+        Q, K, V = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
+        od, P = dense_np(Q, K, V)
+        mask = token_mask(orc, tier[0, h])
+        delta = (P * ~mask).sum(axis=1)
+        vmax = np.linalg.norm(V, axis=1).max()
+        err = np.linalg.norm(od - out[0, h], axis=1)
+        assert (err <= 2 * vmax * delta * (1 + 1e-9) + 1e-12).all()
+
+
+def test_frame_relabelling_invariance(orc, qkv):
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    rng = np.random.default_rng(2)
+    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 16, 0).astype(np.uint8)
+    out = orc.attention(q, k, v, tier, F, HV, WV)
+    # swap the two frames: token blocks and region ids move together
+    N1 = HV * WV
+    tokp = np.concatenate([np.arange(N1, 2 * N1), np.arange(0, N1)])
+    R1 = R // F
+    regp = np.concatenate([np.arange(R1, 2 * R1), np.arange(0, R1)])
+    out2 = orc.attention(q[:, :, tokp], k[:, :, tokp], v[:, :, tokp],
+                         tier[:, :, regp][:, :, :, regp].copy(), F, HV, WV)
+    assert np.abs(out2 - out[:, :, tokp]).max() <= 1e-12
+
+
+def _deq(orc, q, k, v):
+    """Dequantized reordered operands of head 0 from the oracle's codes."""
+    val8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    val4 = np.concatenate([E2M1_POS, -E2M1_POS])
+    oq, ok, ov = orc.quant_qk(q, F, HV, WV), orc.quant_qk(k, F, HV, WV), orc.quant_v(v, F, HV, WV)
+    out = {}
+    for name, o in (("q", oq), ("k", ok)):
+        out[name + "8"] = val8[o["c8"][0, 0]] * np.repeat(o["s8"][0, 0], 64)[:, None]
+        out[name + "4"] = val4[o["c4"][0, 0]] * np.exp2(np.repeat(o["e4"][0, 0].astype(np.int64) - 127, 32, axis=1))
+    out["v8"] = val8[ov["c8"][0, 0]] * ov["s8"][0, 0][None, :]
+    e = ov["e4"][0, 0].astype(np.int64) - 127  # [R,2,d]
+    out["v4"] = val4[ov["c4"][0, 0]] * np.exp2(np.repeat(e, 32, axis=1).reshape(-1, e.shape[-1]))
+    return out
+
+
+@pytest.mark.parametrize("u", [5, 200, 451])
+def test_quantized_tile_loop_from_trace(orc, qkv, u):
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    rng = np.random.default_rng(u)
+    tier = rng.choice(np.array([0, 4, 8], np.uint8), size=(1, 2, R, R), p=[0.4, 0.35, 0.25])
+    tr = orc.attention_trace(q[0, 0], k[0, 0], v[0, 0], tier[0, 0], F, HV, WV, u)
+    ops = _deq(orc, q, k, v)
+    a = u // 64
+    row = tier[0, 0, a]
+    # phase order: all FP8 tiles ascending, then all MXFP4 tiles ascending
+    order = [b for b in range(R) if row[b] == 8] + [b for b in range(R) if row[b] == 4]
+    assert np.array_equal(tr["key"], np.concatenate([np.arange(b * 64, b * 64 + 64) for b in order]))
+    assert np.array_equal(tr["tier"], np.repeat([row[b] for b in order], 64))
+    p = tr["tier"]
+    Q = np.where(p[:, None] == 8, ops["q8"][u][None, :], ops["q4"][u][None, :])
+    K = np.where(p[:, None] == 8, ops["k8"][tr["key"]], ops["k4"][tr["key"]])
+    V = np.where(p[:, None] == 8, ops["v8"][tr["key"]], ops["v4"][tr["key"]])
+    s = (Q * K).sum(axis=1) / math.sqrt(D)
+    assert np.allclose(tr["s"], s, rtol=1e-13, atol=1e-13)
+    tile_max = tr["s"].reshape(-1, 64).max(axis=1)
+    run = np.maximum.accumulate(tile_max)
+    assert np.array_equal(tr["m"], np.repeat(run, 64))
+    assert np.allclose(tr["w"], np.exp(tr["s"] - tr["m"]), rtol=1e-15, atol=0)
+    # quantized weights
+    w = tr["w"].reshape(-1, 64)
+    wq = tr["wq"].reshape(-1, 64)
+    val8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for t in range(w.shape[0]):
+        if p[t * 64] == 8:
+            codes = brute_nearest(w[t] * 256.0, val8[:127])
+            assert np.array_equal(wq[t], val8[codes] / 256.0)
+        else:
+            for g in range(2):
+                wg = w[t, 32 * g:32 * g + 32]
+                E = int(np.clip(np.frexp(wg.max())[1] - 1 - 2, -127, 127))
+                codes = brute_nearest(wg * 2.0 ** -E, E2M1_POS)
+                assert np.array_equal(wq[t, 32 * g:32 * g + 32], E2M1_POS[codes] * 2.0 ** E)
+    # shared normalization (B.3/B.4): every weight rescaled to the final max
+    mf = tr["m"][-1]
+    scale = np.exp(tr["m"] - mf)
+    Z = (tr["w"] * scale).sum()
+    assert abs(tr["Z"] - Z) <= 1e-12 * Z
+    want = ((tr["wq"] * scale)[:, None] * V).sum(axis=0) / Z
+    assert np.allclose(tr["out"], want, rtol=1e-11, atol=1e-13)
+    # B.4 identity with z = exact weights of the retained support, O_Omega the
+    # unquantized retained output (h_u = final max)
+    Qf = f64(q[0, 0])[orc.layout(F, HV, WV)][u]
+    Kf = f64(k[0, 0])[orc.layout(F, HV, WV)][tr["key"]]
+    Vf = f64(v[0, 0])[orc.layout(F, HV, WV)][tr["key"]]
+    z = np.exp(Kf @ Qf / math.sqrt(D) - mf)
+    O_om = (z[:, None] * Vf).sum(axis=0) / z.sum()
+    wr, wqr = tr["w"] * scale, tr["wq"] * scale
+    lhs = Z * (tr["out"] - O_om)
+    rhs = ((wr - z)[:, None] * (Vf - O_om)).sum(0) + (wr[:, None] * (V - Vf)).sum(0) \
+        + ((wqr - wr)[:, None] * V).sum(0)
+    assert np.allclose(lhs, rhs, rtol=1e-9, atol=1e-9 * np.abs(lhs).max())
+
+
+def test_empty_row_is_zero(orc, qkv):
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    tier = np.full((1, 2, R, R), 8, np.uint8)
+    tier[0, 1, 7] = 0
+    out = orc.attention(q, k, v, tier, F, HV, WV, qblocks=np.array([7, 2], np.int32))
+    assert (out[0, 1, 0] == 0).all() and np.abs(out[0, 1, 1]).max() > 0
+
+
+def test_zero_skip_error_within_quantization_envelope(orc, qkv):
+    """With nothing skipped, the error against dense attention is bounded by
+    the B.4 terms built from actual reconstruction residuals."""
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    for t in (8, 4):
+        tier = np.full((1, 2, R, R), t, np.uint8)
+        for u in (17, 300):
+            tr = orc.attention_trace(q[0, 0], k[0, 0], v[0, 0], tier[0, 0], F, HV, WV, u)
+            perm = orc.layout(F, HV, WV)
+            Qf = f64(q[0, 0])[perm][u]
+            Kf = f64(k[0, 0])[perm][tr["key"]]
+            Vf = f64(v[0, 0])[perm][tr["key"]]
+            ops = _deq(orc, q, k, v)
+            V = ops["v%d" % t][tr["key"]]
+            mf = tr["m"][-1]
+            z = np.exp(Kf @ Qf / math.sqrt(D) - mf)
+            Od = (z[:, None] * Vf).sum(0) / z.sum()
+            sc = np.exp(tr["m"] - mf)
+            wr, wqr = tr["w"] * sc, tr["wq"] * sc
+            Z = wr.sum()
+            env = (np.linalg.norm(((wr - z)[:, None] * (Vf - Od)).sum(0))
+                   + np.linalg.norm((wr[:, None] * (V - Vf)).sum(0))
+                   + np.linalg.norm(((wqr - wr)[:, None] * V).sum(0))) / Z
+            assert np.linalg.norm(tr["out"] - Od) <= env * (1 + 1e-9) + 1e-13

@@ -1,0 +1,44 @@
+"""Workloads: video-DiT attention layers (8x8 spatial regions, 64 tokens).
+
+Each entry: batch B, heads H, head_dim d, latent frames F x height Hv x width
+Wv (tokens N = F*Hv*Wv in raster order), and budgets as (FP8, MXFP4) shares
+of the R^2 region pairs in basis points; the rest is skipped.
+"""
+from dataclasses import dataclass, field
+from typing import List, Tuple
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    d: int
+    F: int
+    Hv: int
+    Wv: int
+    budgets: Tuple[Tuple[int, int], ...]
+    seed: int
+    outliers: bool = True
+    lam: float = 0.2
+
+    @property
+    def N(self) -> int:
+        return self.F * self.Hv * self.Wv
+
+    @property
+    def R(self) -> int:
+        return self.N // 64
+
+
+SEED0 = 20260926
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 64, 4, 16, 16, ((2500, 2500),), SEED0 + 0, outliers=False),
+    "wan1.3b": Workload("wan1.3b", 1, 12, 128, 21, 32, 48, ((1500, 3500),), SEED0 + 1),
+    "wan14b-720p": Workload("wan14b-720p", 1, 40, 128, 21, 48, 80, ((1000, 3000),), SEED0 + 2),
+    "hunyuan": Workload("hunyuan", 1, 24, 128, 33, 48, 80, ((1000, 3000),), SEED0 + 3),
+    "sweep-wan14b-cfg": Workload("sweep-wan14b-cfg", 2, 40, 128, 21, 48, 80,
+                                 ((500, 1500), (1000, 3000), (2000, 4000), (0, 6000), (10000, 0)),
+                                 SEED0 + 4),
+}
