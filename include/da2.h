@@ -1,0 +1,161 @@
+/*
+ * da2.h -- C ABI of libda2: the DraftAttention2 hot path on MI355X (gfx950).
+ *
+ * The operation (DraftAttention2: Fast Video Diffusion with Low-Resolution-
+ * Guided Mixed-Precision Attention, Sec. 3.1 and App. C.1): for every head,
+ * pool Q and K over 8x8 spatial regions of each latent frame (Eq. 1), build
+ * the mixed average/max draft attention map over region pairs (Eq. 2), rank
+ * all R^2 region pairs of the head, and give the top T8 pairs the 8-bit tier
+ * (FP8 E4M3), the next T4 the 4-bit tier (MXFP4 E2M1 with E8M0 scales per 32
+ * values) and skip the rest.  Attention (Sec. 3.3 "phased execution",
+ * "cross-precision accumulation"; App. B.3/B.4) then evaluates every kept
+ * 64x64 tile at full resolution with its tier's precision, FP8 phase first,
+ * MXFP4 phase second, sharing one online softmax and one output accumulator,
+ * and writes the output in the original token order ("DraftAttention: Fast
+ * Video Diffusion via Low-Resolution Attention Guidance", abstract).
+ *
+ * Conventions
+ *   - Tokens of one (batch, head) are N = frames*height*width latent
+ *     positions in (frame, y, x) raster order; height and width are
+ *     multiples of 8; regions are the 8x8 cells, R = N/64 of them, numbered
+ *     frame-major then raster; inside a region tokens are in raster order.
+ *   - Q, K, V are bfloat16 device arrays addressed as
+ *     base + b*stride_b + h*stride_h + n*stride_n + c (element units, the
+ *     channel index c is contiguous).  head_dim is 64 or 128.  Base pointers
+ *     and strides must keep every token row 16-byte aligned.
+ *   - The output O uses the same element strides in its own element type
+ *     (fp32 or bf16).
+ *   - Tier maps are uint8 [B, H, R, R] (query region a, key region b) with
+ *     values 8 (FP8), 4 (MXFP4) or 0 (skip).
+ *   - All calls are asynchronous on the given HIP stream.  Nothing is
+ *     synchronised except where stated.  Device buffers (inputs, outputs,
+ *     the workspace) belong to the caller; the library allocates only the
+ *     small host objects da2_layout_t and da2_plan_t.
+ *   - Errors are returned as da2_status.  Argument and shape checks happen
+ *     before any launch, so a failed call writes nothing.  DA2_ERR_HIP
+ *     reports a launch failure (the HIP error is left in the runtime).
+ */
+#ifndef DA2_H
+#define DA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DA2_OK = 0,
+    DA2_ERR_INVALID_ARG = 1,       /* null pointer, bad budget, bad dtype, misalignment */
+    DA2_ERR_UNSUPPORTED_SHAPE = 2, /* head_dim not 64/128, height/width not multiples of 8, too large */
+    DA2_ERR_WORKSPACE = 3,         /* workspace smaller than da2_workspace_bytes() */
+    DA2_ERR_PLAN_MISMATCH = 4,     /* q/k pointers differ from the ones the plan was built on, or no plan */
+    DA2_ERR_HIP = 5                /* a kernel launch failed */
+} da2_status;
+
+typedef struct {
+    int32_t batch, heads, head_dim;  /* B, H, d */
+    int32_t frames, height, width;   /* F, H_v, W_v of the latent video */
+    int64_t stride_b, stride_h, stride_n; /* element strides of Q/K/V/O */
+} da2_shape;
+
+typedef struct {
+    int32_t hi_bp;   /* share of region pairs in the FP8 tier, basis points of n */
+    int32_t lo_bp;   /* share in the MXFP4 tier; hi_bp + lo_bp <= 10000 */
+    double lambda;   /* weight of the max-pooled branch of the draft map, in [0, 1] */
+    int32_t scope;   /* 0: one ranking per head over n = R*R pairs (the paper's);
+                        1: one ranking per query region over n = R pairs */
+} da2_budget;
+
+typedef struct da2_layout_s da2_layout_t;
+typedef struct da2_plan_s da2_plan_t;
+
+/* Region layout of one problem shape (App. C.2: the partition is built once
+ * and reused across layers and denoising steps).  Host only, no GPU work. */
+da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out);
+void da2_layout_destroy(da2_layout_t *layout);
+
+/* Bytes of device workspace a plan on this layout needs (256-byte aligned
+ * base required).  Holds packed operands, draft state, tier map, schedule. */
+size_t da2_workspace_bytes(const da2_layout_t *layout);
+
+/* Bind a caller-owned device workspace to a new plan object (host only). */
+da2_status da2_plan_create(const da2_layout_t *layout, void *workspace, size_t workspace_bytes,
+                           da2_plan_t **out);
+void da2_plan_destroy(da2_plan_t *plan);
+
+/* da2_plan: draft-guided tier planning (Sec. 3.1, App. C.1) plus the fused
+ * Q/K operand preparation (Sec. 3.3): reorder, pool, quantize Q and K to FP8
+ * (one fp32 scale per 64-token block) and MXFP4, score the draft map, rank
+ * and assign tiers, and build the per-query-region schedule.  Quotas per
+ * ranking: T8 = round_half_up(hi_bp*n/10^4), Tk = round_half_up((hi_bp +
+ * lo_bp)*n/10^4), T4 = Tk - T8; ties between equal scores go to the smaller
+ * pair index a*R+b.  q and k must stay unchanged until da2_attention on this
+ * plan has run (stream order). */
+da2_status da2_plan(da2_plan_t *plan, const void *q, const void *k, const da2_budget *budget,
+                    hipStream_t stream);
+
+/* Same as da2_plan but with a caller-supplied tier map (device, [B,H,R,R],
+ * values in {0,4,8}; other values are treated as skip).  Pooling and draft
+ * scoring are not run. */
+da2_status da2_plan_from_tier_map(da2_plan_t *plan, const void *q, const void *k,
+                                  const uint8_t *tier_map, hipStream_t stream);
+
+/* Copy the plan's tier map to dst (device, [B,H,R,R] uint8). */
+da2_status da2_plan_tier_map(const da2_plan_t *plan, uint8_t *dst, hipStream_t stream);
+
+/* da2_attention: V preparation (FP8 with one fp32 scale per channel over all
+ * tokens; MXFP4 along keys in groups of 32 inside each region) and the
+ * phased mixed-precision attention over the plan's kept tiles, written to o
+ * in the original token order.  out_dtype: 0 = bf16, 1 = fp32.  q and k must
+ * be the pointers the plan was built on (DA2_ERR_PLAN_MISMATCH otherwise).
+ * Rows whose query region keeps no tile are written as zero (App. C.1). */
+da2_status da2_attention(da2_plan_t *plan, const void *q, const void *k, const void *v, void *o,
+                         int32_t out_dtype, hipStream_t stream);
+
+/* Debug exports in canonical layouts, for tests (device destination):
+ *   DA2_DBG_Q_FP8 / K_FP8 / V_FP8   : uint8 codes [B,H,N,d], token axis in region order
+ *   DA2_DBG_Q_FP8_SCALE / K_...     : fp32 [B,H,R];  V: fp32 [B,H,d]
+ *   DA2_DBG_Q_MX / K_MX / V_MX      : uint8 E2M1 codes [B,H,N,d] (one per byte)
+ *   DA2_DBG_Q_MX_SCALE / K_...      : uint8 E8M0 [B,H,N,d/32];  V: [B,H,R,2,d]
+ *   DA2_DBG_Q_AVG / K_AVG           : fp64 [B,H,R,d];  Q_MAX / K_MAX: fp32 [B,H,R,d]
+ *   DA2_DBG_KEYS                    : uint32 [B,H,R,R] (bits of fp32 draft score)
+ *   DA2_DBG_SCHEDULE                : int32 [B,H,R,2+R]: n8, n4, then FP8 key
+ *                                     regions ascending, then MXFP4 ascending, then -1
+ * V entries are valid after da2_attention. */
+enum {
+    DA2_DBG_Q_FP8 = 0, DA2_DBG_Q_FP8_SCALE, DA2_DBG_Q_MX, DA2_DBG_Q_MX_SCALE,
+    DA2_DBG_K_FP8, DA2_DBG_K_FP8_SCALE, DA2_DBG_K_MX, DA2_DBG_K_MX_SCALE,
+    DA2_DBG_V_FP8, DA2_DBG_V_FP8_SCALE, DA2_DBG_V_MX, DA2_DBG_V_MX_SCALE,
+    DA2_DBG_Q_AVG, DA2_DBG_K_AVG, DA2_DBG_Q_MAX, DA2_DBG_K_MAX,
+    DA2_DBG_KEYS, DA2_DBG_SCHEDULE, DA2_DBG_COUNT
+};
+da2_status da2_plan_debug(const da2_plan_t *plan, int32_t which, void *dst, hipStream_t stream);
+
+/* Bytes written by da2_plan_debug for `which` (0 for unknown values). */
+size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which);
+
+/* Kernel timing of the attention kernel itself (measurement aid).
+ * da2_plan_timing(plan, 1) starts recording a pair of HIP events around the
+ * attention kernel of every later da2_attention call on this plan (up to
+ * 4096 calls; older pairs are kept, further calls are not recorded);
+ * da2_plan_timing(plan, 0) stops and discards them.  da2_plan_timing_read
+ * waits for the recorded events and writes up to `max` per-call durations in
+ * milliseconds to `ms` (host memory), the count to *n. */
+da2_status da2_plan_timing(da2_plan_t *plan, int32_t enable);
+da2_status da2_plan_timing_read(da2_plan_t *plan, float *ms, int32_t max, int32_t *n);
+
+/* Host-side helpers (no GPU work). */
+const char *da2_status_string(da2_status status);
+/* Constants of the fp64 exp used by the draft softmax: ln2 head, ln2 tail,
+ * 1/ln2, then the 14 Taylor coefficients 1/j!, j = 0..13 (17 doubles). */
+void da2_exp_constants(double *out17);
+/* The quotas the ranking uses for n pairs: T8 and Tk = T8 + T4. */
+void da2_quotas(int64_t n, int32_t hi_bp, int32_t lo_bp, int64_t *t8, int64_t *tk);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DA2_H */

@@ -77,6 +77,10 @@ def lib():
         L.or_attention_trace.argtypes = [C.c_int] * 4 + [P, P, P, P, C.c_int, i64,
                                                          P, P, P, P, P, P, P, P]
         L.or_attention_trace.restype = i64
+        L.or_attention_kp.argtypes = [C.c_int] * 6 + [P, P, P, P, C.c_int, P, P, P]
+        L.or_attention_kp.restype = C.c_int
+        L.or_mfma_fp8_dot64.argtypes = [P, P, C.c_float]
+        L.or_mfma_fp8_dot64.restype = C.c_float
         L.or_dense.argtypes = [C.c_int] * 4 + [P, P, P, C.c_int, P, P]
         L.or_dense.restype = C.c_int
         _lib = L
@@ -262,6 +266,39 @@ def attention(q, k, v, tier, F, Hv, Wv, qblocks=None):
     lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), len(qb), _p(qb),
                        _p(out))
     return out
+
+
+def attention_kp(q, k, v, tier, F, Hv, Wv, qblocks=None):
+    """Tiered attention with the weight-quantization decisions taken in the
+    kernel's precision.  Returns (out, allow), each laid out like
+    attention(); allow bounds the effect of undetermined decisions and of
+    the matrix-core accumulation of P V."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    tier = np.ascontiguousarray(tier, np.uint8)
+    B, H, N, d = q.shape
+    R = N // BLK
+    assert tier.shape == (B, H, R, R)
+    nq = R if qblocks is None else len(qblocks)
+    qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
+    out = np.empty((B, H, nq, BLK, d), np.float64)
+    allow = np.empty((B, H, nq, BLK, d), np.float64)
+    lib().or_attention_kp(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), nq,
+                          None if qb is None else _p(qb), _p(out), _p(allow))
+    if qblocks is not None:
+        return out, allow
+    perm = layout(F, Hv, Wv)
+    fo = np.empty((B, H, N, d), np.float64)
+    fa = np.empty((B, H, N, d), np.float64)
+    fo[:, :, perm, :] = out.reshape(B, H, N, d)
+    fa[:, :, perm, :] = allow.reshape(B, H, N, d)
+    return fo, fa
+
+
+def mfma_fp8_dot64(a_codes, b_codes, c_in=0.0) -> float:
+    a = np.ascontiguousarray(a_codes, np.uint8)
+    b = np.ascontiguousarray(b_codes, np.uint8)
+    assert a.size == 64 and b.size == 64
+    return float(lib().or_mfma_fp8_dot64(_p(a), _p(b), float(c_in)))
 
 
 def attention_trace(q, k, v, tier, F, Hv, Wv, u, cap=None):

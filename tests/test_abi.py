@@ -1,0 +1,108 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/da2.h declares, validates arguments before any launch, and its host
+constants agree with the oracle's."""
+import ctypes as C
+import os
+
+import numpy as np
+import pytest
+
+from video_diffusion_dit_frame_amd import da2
+
+pytestmark = pytest.mark.skipif(not os.path.exists(da2.LIB_PATH), reason="libda2.so not built")
+
+OK, INVALID, SHAPE, WORKSPACE, MISMATCH = 0, 1, 2, 3, 4
+
+
+def test_exports_every_declared_function():
+    L = da2.lib()
+    names = da2.header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None):
+    N = F * Hv * Wv
+    sn = d if sn is None else sn
+    sh = N * d if sh is None else sh
+    sb = H * N * d if sb is None else sb
+    s = da2.Shape(B, H, d, F, Hv, Wv, sb, sh, sn)
+    h = C.c_void_p()
+    st = da2.lib().da2_layout_create(C.byref(s), C.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), OK),
+    (dict(d=96), SHAPE),
+    (dict(Hv=12), SHAPE),
+    (dict(Wv=20), SHAPE),
+    (dict(F=0), SHAPE),
+    (dict(B=0), SHAPE),
+    (dict(sn=60), INVALID),       # row stride below head_dim
+    (dict(sn=68), INVALID),       # rows not 16-byte aligned
+    (dict(F=200, Hv=128, Wv=128), SHAPE),  # too many regions
+])
+def test_layout_validation(kw, want):
+    st, h = _layout(**kw)
+    assert st == want
+    if st == OK:
+        da2.lib().da2_layout_destroy(h)
+
+
+def test_workspace_and_plan_validation():
+    L = da2.lib()
+    st, lay = _layout()
+    assert st == OK
+    need = L.da2_workspace_bytes(lay)
+    assert need > 0
+    p = C.c_void_p()
+    fake = C.c_void_p(1 << 20)  # never dereferenced: validation fails or no launch happens
+    assert L.da2_plan_create(lay, fake, need - 1, C.byref(p)) == WORKSPACE
+    assert L.da2_plan_create(lay, C.c_void_p((1 << 20) + 16), need, C.byref(p)) == WORKSPACE
+    assert L.da2_plan_create(lay, fake, need, C.byref(p)) == OK
+    q = C.c_void_p(1 << 24)
+    for hi, lo, lam, scope in [(-1, 0, 0.2, 0), (0, -5, 0.2, 0), (6000, 4001, 0.2, 0),
+                               (100, 100, 1.5, 0), (100, 100, float("nan"), 0), (100, 100, 0.2, 2)]:
+        b = da2.Budget(hi, lo, lam, scope)
+        assert L.da2_plan(p, q, q, C.byref(b), None) == INVALID
+    b = da2.Budget(100, 100, 0.2, 0)
+    assert L.da2_plan(p, C.c_void_p((1 << 24) + 2), q, C.byref(b), None) == INVALID  # misaligned
+    assert L.da2_plan(p, None, q, C.byref(b), None) == INVALID
+    # attention before any plan: mismatch; bad dtype: invalid
+    assert L.da2_attention(p, q, q, q, q, 1, None) == MISMATCH
+    assert L.da2_attention(p, q, q, q, q, 7, None) == INVALID
+    assert L.da2_plan_tier_map(p, q, None) == MISMATCH
+    assert L.da2_plan_debug(p, 99, q, None) == INVALID
+    L.da2_plan_destroy(p)
+    L.da2_layout_destroy(lay)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert da2.status_string(s)
+
+
+def test_exp_constants_agree_with_oracle(orc):
+    assert np.array_equal(da2.exp_constants(), orc.exp_constants())
+
+
+def test_quotas_agree_with_oracle(orc):
+    rng = np.random.default_rng(0)
+    for _ in range(500):
+        n = int(rng.integers(1, 5_000_000))
+        hi = int(rng.integers(0, 10001))
+        lo = int(rng.integers(0, 10001 - hi))
+        assert da2.quotas(n, hi, lo) == orc.quotas(n, hi, lo)
+
+
+def test_debug_sizes():
+    st, lay = _layout(B=2, H=3, d=128, F=1, Hv=16, Wv=24)
+    L = da2.lib()
+    B, H, d, N, R = 2, 3, 128, 384, 6
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["Q_FP8"]) == B * H * N * d
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["KEYS"]) == B * H * R * R * 4
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["V_MX_SCALE"]) == B * H * R * 2 * d
+    assert L.da2_plan_debug_bytes(lay, 1234) == 0
+    L.da2_layout_destroy(lay)

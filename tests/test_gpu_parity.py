@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: pooled descriptors, draft keys, tier maps, schedules and every
+quantized code and scale.  Attention output (fp32) within rel-L2 <= 1e-3 and
+max-abs <= 5e-3 of the oracle on the same quantized operands and tier map;
+the error against dense fp64 attention is printed alongside.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+# (B, H, F, Hv, Wv, d, seed, outliers, hi, lo)
+TINY = (1, 2, 4, 16, 16, 64, 20260926, False, 2500, 2500)
+# several logit tiles and rank chunks, both with ragged tails
+MEDIUM = (1, 2, 2, 64, 72, 128, 11, True, 1500, 3500)
+RAGGED = (2, 1, 3, 24, 40, 128, 12, True, 1000, 3000)
+
+
+def _case(c):
+    B, H, F, Hv, Wv, d, seed, outl, hi, lo = c
+    q, k, v = G.inputs(B, H, F, Hv, Wv, d, seed, outl)
+    return dict(B=B, H=H, F=F, Hv=Hv, Wv=Wv, d=d, hi=hi, lo=lo, q=q, k=k, v=v)
+
+
+@pytest.fixture(scope="module", params=[TINY, MEDIUM, RAGGED], ids=["tiny", "medium", "ragged"])
+def case(request):
+    c = _case(request.param)
+    P, qd, kd = G.run_plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], c["hi"], c["lo"])
+    o = G.run_attention(P, qd, kd, c["v"])
+    c.update(P=P, qd=qd, kd=kd, o=o.cpu().numpy())
+    c["oracle_plan"] = O.plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], c["hi"], c["lo"],
+                              descriptors=True)
+    return c
+
+
+def test_operands_bit_exact(case):
+    P, F, Hv, Wv = case["P"], case["F"], case["Hv"], case["Wv"]
+    for name, x in (("Q", case["q"]), ("K", case["k"])):
+        o = O.quant_qk(x, F, Hv, Wv)
+        assert np.array_equal(G.host(P.debug(name + "_FP8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_MX"), np.uint8).reshape(o["c4"].shape), o["c4"]), name
+        assert np.array_equal(G.host(P.debug(name + "_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"]), name
+    o = O.quant_v(case["v"], F, Hv, Wv)
+    assert np.array_equal(G.host(P.debug("V_FP8"), np.uint8).reshape(o["c8"].shape), o["c8"])
+    assert np.array_equal(G.host(P.debug("V_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"])
+    assert np.array_equal(G.host(P.debug("V_MX"), np.uint8).reshape(o["c4"].shape), o["c4"])
+    assert np.array_equal(G.host(P.debug("V_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"])
+
+
+def test_descriptors_bit_exact(case):
+    P, op = case["P"], case["oracle_plan"]
+    for name, key, dt in (("Q_AVG", "qavg", np.float64), ("K_AVG", "kavg", np.float64),
+                          ("Q_MAX", "qmax", np.float32), ("K_MAX", "kmax", np.float32)):
+        got = G.host(P.debug(name), dt).reshape(op[key].shape)
+        assert np.array_equal(got, op[key]), name
+
+
+def test_keys_and_tier_map_bit_exact(case):
+    P, op = case["P"], case["oracle_plan"]
+    keys = G.host(P.debug("KEYS"), np.uint32).reshape(op["keys"].shape)
+    assert np.array_equal(keys, op["keys"])
+    tier = P.tier_map().cpu().numpy()
+    assert np.array_equal(tier, op["tier"])
+    R = tier.shape[-1]
+    T8, Tk = O.quotas(R * R, case["hi"], case["lo"])
+    assert ((tier == 8).sum(axis=(2, 3)) == T8).all()
+    assert ((tier == 4).sum(axis=(2, 3)) == Tk - T8).all()
+
+
+def test_schedule_exact(case):
+    P, op = case["P"], case["oracle_plan"]
+    sch = G.host(P.debug("SCHEDULE"), np.int32).reshape(op["tier"].shape[:3] + (-1,))
+    assert np.array_equal(sch, G.schedule_from_tier(op["tier"]))
+
+
+def test_attention_matches_oracle(case):
+    c = case
+    ref, allow = O.attention_kp(c["q"], c["k"], c["v"], c["oracle_plan"]["tier"], c["F"], c["Hv"],
+                                c["Wv"])
+    rl, ma = G.check_kp(c["o"], ref, allow, "plan tier map")
+    exact = O.attention(c["q"], c["k"], c["v"], c["oracle_plan"]["tier"], c["F"], c["Hv"], c["Wv"])
+    rows = np.arange(0, c["q"].shape[2], 97, dtype=np.int32)
+    dn = O.dense(c["q"], c["k"], c["v"], rows)
+    print("vs kernel-precision oracle: rel_l2 %.3e max_abs %.3e | vs fp64-decision oracle %.3e |"
+          " vs dense fp64 %.3e" % (rl, ma, G.rel_l2(c["o"], exact), G.rel_l2(c["o"][:, :, rows], dn)))
+
+
+def test_row_scope_tier_map():
+    c = _case(TINY)
+    P, qd, kd = G.run_plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], c["hi"], c["lo"], scope=1)
+    ref = O.plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], c["hi"], c["lo"], scope=1)
+    tier = P.tier_map().cpu().numpy()
+    assert np.array_equal(tier, ref["tier"])
+    R = tier.shape[-1]
+    T8, Tk = O.quotas(R, c["hi"], c["lo"])
+    assert ((tier == 8).sum(axis=3) == T8).all() and ((tier == 4).sum(axis=3) == Tk - T8).all()
+
+
+@pytest.mark.parametrize("lam", [0.0, 1.0])
+def test_lambda_extremes_bit_exact(lam):
+    c = _case(TINY)
+    P, qd, kd = G.run_plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], 1000, 3000, lam=lam)
+    ref = O.plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], 1000, 3000, lam=lam)
+    assert np.array_equal(P.tier_map().cpu().numpy(), ref["tier"])
+    keys = G.host(P.debug("KEYS"), np.uint32).reshape(ref["keys"].shape)
+    assert np.array_equal(keys, ref["keys"])
+
+
+def _tier_families(B, H, R, seed):
+    rng = np.random.default_rng(seed)
+    fam = {
+        "all8": np.full((B, H, R, R), 8, np.uint8),
+        "all4": np.full((B, H, R, R), 4, np.uint8),
+        "random": rng.choice(np.array([0, 4, 8], np.uint8), size=(B, H, R, R), p=[0.5, 0.3, 0.2]),
+        "skip_all": np.zeros((B, H, R, R), np.uint8),
+    }
+    t = rng.choice(np.array([0, 4, 8], np.uint8), size=(B, H, R, R), p=[0.4, 0.3, 0.3])
+    t[:, :, ::3, :] = 0          # empty query regions
+    fam["empty_rows"] = t
+    s = np.zeros((B, H, R, R), np.uint8)
+    s[:, :, :, R // 2] = 8       # a single FP8 tile per row
+    s[:, :, 1::2, R // 2] = 4    # or a single MXFP4 tile
+    fam["single_tile"] = s
+    return fam
+
+
+@pytest.mark.parametrize("which", [TINY, RAGGED], ids=["tiny", "ragged"])
+def test_attention_tier_families(which):
+    c = _case(which)
+    F, Hv, Wv = c["F"], c["Hv"], c["Wv"]
+    from video_diffusion_dit_frame_amd import da2
+
+    qd, kd, vd = G.dev(c["q"]), G.dev(c["k"]), G.dev(c["v"])
+    L = da2.Layout.for_tensor(qd, F, Hv, Wv)
+    P = da2.Plan(L)
+    B, H, N, d = c["q"].shape
+    R = N // 64
+    for name, tier in _tier_families(B, H, R, 5).items():
+        P.plan_from_tier_map(qd, kd, torch.from_numpy(tier).cuda())
+        o = torch.empty(vd.shape, dtype=torch.float32, device="cuda")
+        P.attention(qd, kd, vd, o)
+        got = o.cpu().numpy()
+        assert np.array_equal(P.tier_map().cpu().numpy(), tier)
+        ref, allow = O.attention_kp(c["q"], c["k"], c["v"], tier, F, Hv, Wv)
+        if name == "skip_all":
+            assert (got == 0).all()
+            continue
+        G.check_kp(got, ref, allow, name)
+        if name == "empty_rows":
+            perm = O.layout(F, Hv, Wv)
+            dead = perm.reshape(R, 64)[::3].reshape(-1)
+            assert (got[:, :, dead] == 0).all()
+
+
+def test_strided_layout_matches_contiguous():
+    """[B, N, H, d] storage (the usual DiT layout) gives identical results."""
+    c = _case(RAGGED)
+    F, Hv, Wv = c["F"], c["Hv"], c["Wv"]
+    P1, q1, k1 = G.run_plan(c["q"], c["k"], F, Hv, Wv, c["hi"], c["lo"])
+    o1 = G.run_attention(P1, q1, k1, c["v"]).cpu().numpy()
+    P2, q2, k2 = G.run_plan(c["q"], c["k"], F, Hv, Wv, c["hi"], c["lo"], layout_bnhd=True)
+    o2 = G.run_attention(P2, q2, k2, c["v"])
+    assert o2.stride(1) == o2.shape[3]
+    assert np.array_equal(P1.tier_map().cpu().numpy(), P2.tier_map().cpu().numpy())
+    assert np.array_equal(o1, o2.cpu().numpy())
+
+
+def test_bf16_output():
+    c = _case(TINY)
+    P, qd, kd = G.run_plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], c["hi"], c["lo"])
+    o32 = G.run_attention(P, qd, kd, c["v"]).cpu()
+    o16 = G.run_attention(P, qd, kd, c["v"], torch.bfloat16).cpu()
+    # the bf16 output is the fp32 output rounded to nearest even
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_deterministic():
+    c = _case(MEDIUM)
+    outs = []
+    for _ in range(2):
+        P, qd, kd = G.run_plan(c["q"], c["k"], c["F"], c["Hv"], c["Wv"], c["hi"], c["lo"])
+        o = G.run_attention(P, qd, kd, c["v"]).cpu().numpy()
+        outs.append((P.tier_map().cpu().numpy(), G.host(P.debug("KEYS"), np.uint32), o))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)

@@ -1,0 +1,157 @@
+// da2_device.h -- device helpers shared by the libda2 kernels: bf16 access,
+// region geometry, exact FP8 / MXFP4 encoders for operand preparation and the
+// fp64 exp of the draft softmax.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da2 {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Original token index of position i (0..63) of region a.  Regions are the
+// 8x8 cells of every frame, frame-major then raster; tokens in raster order.
+__device__ __forceinline__ int region_token(int a, int i, int Ry, int Rx, int Hv, int Wv)
+{
+    int f = a / (Ry * Rx);
+    int r = a - f * Ry * Rx;
+    int ry = r / Rx, rx = r - ry * Rx;
+    return (f * Hv + ry * 8 + (i >> 3)) * Wv + rx * 8 + (i & 7);
+}
+
+// Logical key (0..63) held in row i (0..31) of the key operand of MFMA half m.
+// The 32x32 accumulator puts row i at register 4*(i/8) + i%4 of lane half
+// (i/4)%2; this permutation makes lane half hf own keys 32*hf .. 32*hf+31,
+// slot s = 16*m + register, so one lane holds a whole 32-key MX group.
+__device__ __forceinline__ int key_of_row(int i, int m)
+{
+    return 32 * ((i >> 2) & 1) + 16 * m + 4 * (i >> 3) + (i & 3);
+}
+
+// ---------------------------------------------------------------------------
+// OCP FP8 E4M3 ("fn") encoder, round to nearest even, saturating at 448.
+// Works on the fp32 bit pattern: normals keep exponent and the top three
+// mantissa bits with an integer RNE on the rest; below 2^-6 the grid is
+// 2^-9, handled by an exact scale and rint.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint8_t enc_e4m3(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    uint32_t s = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;
+    if (a >= 0x43e00000u)  // >= 448
+        return (uint8_t)(s | 0x7eu);
+    if (a < 0x3c800000u) {  // < 2^-6
+        float t = __uint_as_float(a) * 512.0f;
+        return (uint8_t)(s | (uint32_t)__builtin_rintf(t));
+    }
+    uint32_t m = a >> 20, rem = a & 0xfffffu;
+    m += (rem > 0x80000u) || (rem == 0x80000u && (m & 1u));
+    return (uint8_t)(s | (m - (120u << 3)));
+}
+
+// OCP E2M1 magnitude code of an exact non-negative value, nearest with ties to
+// the even code, saturating at 6: the grid 0, .5, 1, 1.5, 2, 3, 4, 6 has
+// midpoints .25 .75 1.25 1.75 2.5 3.5 5, and a tie goes up exactly when the
+// upper neighbour has the even code (.75, 1.75, 3.5).
+__device__ __forceinline__ uint32_t enc_e2m1_mag(double a)
+{
+    return (uint32_t)(a > 0.25) + (uint32_t)(a >= 0.75) + (uint32_t)(a > 1.25) +
+           (uint32_t)(a >= 1.75) + (uint32_t)(a > 2.5) + (uint32_t)(a >= 3.5) +
+           (uint32_t)(a > 5.0);
+}
+
+// floor(log2 x) for finite x > 0 (normal or subnormal fp32).
+__device__ __forceinline__ int floor_log2_f32(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    int e = (int)((u >> 23) & 0xffu);
+    if (e)
+        return e - 127;
+    return (31 - __builtin_clz(u & 0x7fffffu)) - 149;
+}
+
+// E8M0 block exponent of an MX block with largest magnitude amax:
+// floor(log2 amax) - 2, clamped to [-127, 127]; amax = 0 gives -127.
+__device__ __forceinline__ int mx_exponent(float amax)
+{
+    if (amax == 0.0f)
+        return -127;
+    int E = floor_log2_f32(amax) - 2;
+    return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+// E2M1 code (sign in bit 3) of x * 2^-E, computed exactly in fp64.
+__device__ __forceinline__ uint32_t enc_e2m1_scaled(float x, int E)
+{
+    double a = __builtin_ldexp((double)__builtin_fabsf(x), -E);
+    uint32_t s = (__float_as_uint(x) >> 28) & 8u;
+    return s | enc_e2m1_mag(a);
+}
+
+// ---------------------------------------------------------------------------
+// fp64 exp of the draft softmax.  Cody-Waite: k = rint(x / ln 2) through the
+// rounded reciprocal, r = x - k ln2 with ln 2 split into a 32-bit head and a
+// tail (fdlibm's split), then e^r by its Taylor series to degree 13 in Horner
+// form with fused multiply-adds, then 2^k.  Below -708 the result is 0, so
+// every nonzero value is normal.
+// ---------------------------------------------------------------------------
+constexpr double kLn2Hi = 0x1.62e42feep-1;
+constexpr double kLn2Lo = 0x1.a39ef35793c76p-33;
+constexpr double kInvLn2 = 0x1.71547652b82fep+0;
+
+struct TaylorTable {
+    double c[14];
+    constexpr TaylorTable() : c()
+    {
+        double f = 1.0;
+        for (int j = 0; j < 14; j++) {
+            if (j)
+                f = f * (double)j;
+            c[j] = 1.0 / f;
+        }
+    }
+};
+constexpr TaylorTable kTaylor{};
+
+__device__ __forceinline__ double exp_draft(double x)
+{
+    if (x < -708.0)
+        return 0.0;
+    double k = __builtin_rint(x * kInvLn2);
+    double r = __builtin_fma(-k, kLn2Hi, x);
+    r = __builtin_fma(-k, kLn2Lo, r);
+    double p = kTaylor.c[13];
+#pragma unroll
+    for (int j = 12; j >= 0; j--)
+        p = __builtin_fma(p, r, kTaylor.c[j]);
+    return __builtin_ldexp(p, (int)k);
+}
+
+// Block-wide reductions for 256-thread blocks (4 waves of 64).
+__device__ __forceinline__ float wave_max_f32(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace da2

@@ -1,0 +1,345 @@
+// da2_host.cpp -- the C ABI of libda2: validation, workspace carving and the
+// launch sequence of the hot path (plan: prep Q/K -> draft -> rank ->
+// schedule; attention: prep V -> phased attention with fused restore).
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "da2_internal.h"
+#include "da2_device.h"
+
+using namespace da2;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+da2_status check_shape(const da2_shape *s)
+{
+    if (!s)
+        return DA2_ERR_INVALID_ARG;
+    if (s->batch < 1 || s->heads < 1 || s->frames < 1 || s->height < 8 || s->width < 8)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
+    if (s->height % 8 || s->width % 8)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
+    int64_t N = (int64_t)s->frames * s->height * s->width;
+    if (N / kBlk > kMaxRegions || (int64_t)s->batch * s->heads > 65535)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
+    if (s->stride_n < s->head_dim || s->stride_b < 0 || s->stride_h < 0)
+        return DA2_ERR_INVALID_ARG;
+    if (s->stride_n % 8 || s->stride_h % 8 || s->stride_b % 8)
+        return DA2_ERR_INVALID_ARG;
+    return DA2_OK;
+}
+
+void carve(da2_layout_s &L)
+{
+    const size_t BH = L.BH, N = L.N, R = L.R, d = L.d;
+    Workspace &W = L.ws;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    W.q8 = take(BH * N * d);
+    W.q4 = take(BH * N * d / 2);
+    W.q4s = take(BH * N * d / 32);
+    W.qs8 = take(BH * R * 4);
+    W.k8 = take(BH * N * d);
+    W.k4 = take(BH * N * d / 2);
+    W.k4s = take(BH * N * d / 32);
+    W.ks8 = take(BH * R * 4);
+    W.v8 = take(BH * N * d);
+    W.v4 = take(BH * N * d / 2);
+    W.v4s = take(BH * N * d / 32);
+    W.vs8 = take(BH * d * 4);
+    W.vamax = take(BH * d * 4);
+    W.qavg = take(BH * R * d * 8);
+    W.kavg = take(BH * R * d * 8);
+    W.qmax = take(BH * R * d * 4);
+    W.kmax = take(BH * R * d * 4);
+    W.la = take(BH * R * R * 8);
+    W.lm = take(BH * R * R * 8);
+    W.keys = take(BH * R * R * 4);
+    W.tier = take(BH * R * R);
+    W.sched = take(BH * R * R * 2);
+    W.cnt = take(BH * R * 2 * 4);
+    W.rank_state = take(BH * 2 * sizeof(RankState));
+    W.rank_hist = take(BH * 2 * 256 * 4);
+    W.rank_eq = take(BH * (size_t)L.nchunk * 2 * 4);
+    W.total = off;
+}
+
+da2_status launched()
+{
+    return hipGetLastError() == hipSuccess ? DA2_OK : DA2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *da2_status_string(da2_status s)
+{
+    switch (s) {
+    case DA2_OK: return "ok";
+    case DA2_ERR_INVALID_ARG: return "invalid argument";
+    case DA2_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case DA2_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case DA2_ERR_PLAN_MISMATCH: return "plan does not match these inputs";
+    case DA2_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
+{
+    if (!out)
+        return DA2_ERR_INVALID_ARG;
+    da2_status st = check_shape(shape);
+    if (st != DA2_OK)
+        return st;
+    da2_layout_s *L = (da2_layout_s *)calloc(1, sizeof(da2_layout_s));
+    if (!L)
+        return DA2_ERR_INVALID_ARG;
+    L->s = *shape;
+    L->N = shape->frames * shape->height * shape->width;
+    L->R = L->N / kBlk;
+    L->Ry = shape->height / 8;
+    L->Rx = shape->width / 8;
+    L->BH = shape->batch * shape->heads;
+    L->d = shape->head_dim;
+    L->nchunk = ((int64_t)L->R * L->R + 4095) / 4096;
+    carve(*L);
+    *out = L;
+    return DA2_OK;
+}
+
+void da2_layout_destroy(da2_layout_t *layout) { free(layout); }
+
+size_t da2_workspace_bytes(const da2_layout_t *layout) { return layout ? layout->ws.total : 0; }
+
+da2_status da2_plan_create(const da2_layout_t *layout, void *workspace, size_t workspace_bytes,
+                           da2_plan_t **out)
+{
+    if (!layout || !out)
+        return DA2_ERR_INVALID_ARG;
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < layout->ws.total)
+        return DA2_ERR_WORKSPACE;
+    da2_plan_s *P = (da2_plan_s *)calloc(1, sizeof(da2_plan_s));
+    if (!P)
+        return DA2_ERR_INVALID_ARG;
+    P->L = *layout;
+    P->ws = (char *)workspace;
+    P->ws_bytes = workspace_bytes;
+    *out = P;
+    return DA2_OK;
+}
+
+static void drop_events(da2_plan_s *P)
+{
+    if (P->ev) {
+        for (int i = 0; i < 2 * kMaxTimed; i++)
+            if (P->ev[i])
+                hipEventDestroy(P->ev[i]);
+        free(P->ev);
+    }
+    P->ev = nullptr;
+    P->nev = 0;
+    P->timing = 0;
+}
+
+void da2_plan_destroy(da2_plan_t *plan)
+{
+    if (!plan)
+        return;
+    drop_events(plan);
+    free(plan);
+}
+
+da2_status da2_plan_timing(da2_plan_t *P, int32_t enable)
+{
+    if (!P)
+        return DA2_ERR_INVALID_ARG;
+    drop_events(P);
+    if (!enable)
+        return DA2_OK;
+    P->ev = (hipEvent_t *)calloc(2 * kMaxTimed, sizeof(hipEvent_t));
+    if (!P->ev)
+        return DA2_ERR_INVALID_ARG;
+    P->timing = 1;
+    return DA2_OK;
+}
+
+da2_status da2_plan_timing_read(da2_plan_t *P, float *ms, int32_t max, int32_t *n)
+{
+    if (!P || !n || (max > 0 && !ms))
+        return DA2_ERR_INVALID_ARG;
+    int cnt = P->nev < max ? P->nev : max;
+    for (int i = 0; i < cnt; i++) {
+        if (hipEventSynchronize(P->ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms[i], P->ev[2 * i], P->ev[2 * i + 1]) != hipSuccess)
+            return DA2_ERR_HIP;
+    }
+    *n = P->nev;
+    return DA2_OK;
+}
+
+void da2_quotas(int64_t n, int32_t hi_bp, int32_t lo_bp, int64_t *t8, int64_t *tk)
+{
+    *t8 = ((int64_t)hi_bp * n + 5000) / 10000;
+    *tk = ((int64_t)(hi_bp + lo_bp) * n + 5000) / 10000;
+}
+
+da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budget *bud,
+                    hipStream_t stream)
+{
+    if (!P || !q || !k || !bud)
+        return DA2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k))
+        return DA2_ERR_INVALID_ARG;
+    if (bud->hi_bp < 0 || bud->lo_bp < 0 || bud->hi_bp + bud->lo_bp > 10000)
+        return DA2_ERR_INVALID_ARG;
+    if (!isfinite(bud->lambda) || bud->lambda < 0.0 || bud->lambda > 1.0)
+        return DA2_ERR_INVALID_ARG;
+    if (bud->scope != 0 && bud->scope != 1)
+        return DA2_ERR_INVALID_ARG;
+    const da2_layout_s &L = P->L;
+    const int64_t n = bud->scope == 0 ? (int64_t)L.R * L.R : (int64_t)L.R;
+    int64_t t8, tk;
+    da2_quotas(n, bud->hi_bp, bud->lo_bp, &t8, &tk);
+    P->ready = 0;
+    launch_prep_qk(L, q, 0, P->ws, stream);
+    launch_prep_qk(L, k, 1, P->ws, stream);
+    launch_draft(L, bud->lambda, P->ws, stream);
+    launch_rank(L, bud->scope, t8, tk, P->ws, stream);
+    launch_schedule(L, P->ws, stream);
+    da2_status st = launched();
+    if (st != DA2_OK)
+        return st;
+    P->q = q;
+    P->k = k;
+    P->ready = 1;
+    P->has_keys = 1;
+    return DA2_OK;
+}
+
+da2_status da2_plan_from_tier_map(da2_plan_t *P, const void *q, const void *k,
+                                  const uint8_t *tier_map, hipStream_t stream)
+{
+    if (!P || !q || !k || !tier_map)
+        return DA2_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k))
+        return DA2_ERR_INVALID_ARG;
+    const da2_layout_s &L = P->L;
+    P->ready = 0;
+    launch_prep_qk(L, q, 0, P->ws, stream);
+    launch_prep_qk(L, k, 1, P->ws, stream);
+    launch_import_tier(L, tier_map, P->ws, stream);
+    launch_schedule(L, P->ws, stream);
+    da2_status st = launched();
+    if (st != DA2_OK)
+        return st;
+    P->q = q;
+    P->k = k;
+    P->ready = 1;
+    P->has_keys = 0;
+    return DA2_OK;
+}
+
+da2_status da2_plan_tier_map(const da2_plan_t *P, uint8_t *dst, hipStream_t stream)
+{
+    if (!P || !dst)
+        return DA2_ERR_INVALID_ARG;
+    if (!P->ready)
+        return DA2_ERR_PLAN_MISMATCH;
+    const da2_layout_s &L = P->L;
+    hipError_t e = hipMemcpyAsync(dst, P->ws + L.ws.tier, (size_t)L.BH * L.R * L.R,
+                                  hipMemcpyDeviceToDevice, stream);
+    return e == hipSuccess ? DA2_OK : DA2_ERR_HIP;
+}
+
+da2_status da2_attention(da2_plan_t *P, const void *q, const void *k, const void *v, void *o,
+                         int32_t out_dtype, hipStream_t stream)
+{
+    if (!P || !q || !k || !v || !o)
+        return DA2_ERR_INVALID_ARG;
+    if (out_dtype != 0 && out_dtype != 1)
+        return DA2_ERR_INVALID_ARG;
+    if (!aligned16(v) || !aligned16(o))
+        return DA2_ERR_INVALID_ARG;
+    if (!P->ready || P->q != q || P->k != k)
+        return DA2_ERR_PLAN_MISMATCH;
+    const da2_layout_s &L = P->L;
+    launch_prep_v(L, v, P->ws, stream);
+    hipEvent_t *ev = nullptr;
+    if (P->timing && P->nev < kMaxTimed) {
+        ev = P->ev + 2 * P->nev;
+        for (int i = 0; i < 2; i++)
+            if (!ev[i] && hipEventCreate(&ev[i]) != hipSuccess)
+                return DA2_ERR_HIP;
+        hipEventRecord(ev[0], stream);
+    }
+    launch_attention(L, P->ws, o, out_dtype, stream);
+    if (ev) {
+        hipEventRecord(ev[1], stream);
+        P->nev++;
+    }
+    return launched();
+}
+
+size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which)
+{
+    if (!layout)
+        return 0;
+    const size_t BH = layout->BH, N = layout->N, R = layout->R, d = layout->d;
+    switch (which) {
+    case DA2_DBG_Q_FP8: case DA2_DBG_K_FP8: case DA2_DBG_V_FP8:
+    case DA2_DBG_Q_MX: case DA2_DBG_K_MX: case DA2_DBG_V_MX:
+        return BH * N * d;
+    case DA2_DBG_Q_FP8_SCALE: case DA2_DBG_K_FP8_SCALE:
+        return BH * R * 4;
+    case DA2_DBG_V_FP8_SCALE:
+        return BH * d * 4;
+    case DA2_DBG_Q_MX_SCALE: case DA2_DBG_K_MX_SCALE:
+        return BH * N * d / 32;
+    case DA2_DBG_V_MX_SCALE:
+        return BH * R * 2 * d;
+    case DA2_DBG_Q_AVG: case DA2_DBG_K_AVG:
+        return BH * R * d * 8;
+    case DA2_DBG_Q_MAX: case DA2_DBG_K_MAX:
+        return BH * R * d * 4;
+    case DA2_DBG_KEYS:
+        return BH * R * R * 4;
+    case DA2_DBG_SCHEDULE:
+        return BH * R * (R + 2) * 4;
+    default:
+        return 0;
+    }
+}
+
+da2_status da2_plan_debug(const da2_plan_t *P, int32_t which, void *dst, hipStream_t stream)
+{
+    if (!P || !dst || which < 0 || which >= DA2_DBG_COUNT)
+        return DA2_ERR_INVALID_ARG;
+    if (!P->ready)
+        return DA2_ERR_PLAN_MISMATCH;
+    launch_debug(P->L, which, P->ws, dst, stream);
+    return launched();
+}
+
+void da2_exp_constants(double *out)
+{
+    out[0] = kLn2Hi;
+    out[1] = kLn2Lo;
+    out[2] = kInvLn2;
+    for (int j = 0; j < 14; j++)
+        out[3 + j] = kTaylor.c[j];
+}
+
+}  // extern "C"

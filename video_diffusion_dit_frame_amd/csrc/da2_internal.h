@@ -1,0 +1,79 @@
+// da2_internal.h -- private types, workspace layout and device helpers of
+// libda2 (gfx950).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "da2.h"
+
+namespace da2 {
+
+constexpr int kBlk = 64;          // tokens per region: one 8x8 spatial cell
+constexpr int kMaxRegions = 8192; // R limit (keeps R*R in 32 bits, row scope in LDS)
+constexpr int kMaxTimed = 4096;   // attention calls recorded while timing
+
+// ---------------------------------------------------------------------------
+// Workspace: one region of caller memory carved into these buffers.
+// Packed operand layouts (per (b,h) slice "bh", per region a):
+//   Q fp8  : [bh][a][w=2][kc=d/64][lane=64][32 B]   B operand of S^T = K Q^T
+//   K fp8  : [bh][a][m=2][kc][lane][32 B]           A operand, key rows permuted
+//   *_mx   : same chunking, 16 B of E2M1 pairs per lane, one E8M0 byte per lane
+//   V fp8  : [bh][a][cb=d/32][lane][32 B]           A operand of O^T = V^T P^T
+//   V mx   : [bh][a][cb][lane][16 B] + E8M0 byte per lane
+// ---------------------------------------------------------------------------
+struct Workspace {
+    size_t q8, q4, q4s, qs8;
+    size_t k8, k4, k4s, ks8;
+    size_t v8, v4, v4s, vs8, vamax;
+    size_t qavg, kavg, qmax, kmax;
+    size_t la, lm, keys, tier;
+    size_t sched, cnt;
+    size_t rank_state, rank_hist, rank_eq;
+    size_t total;
+};
+
+struct RankState {      // one per (segment, target)
+    uint32_t prefix;    // selected key bits so far
+    uint32_t mask;      // which bits of prefix are fixed
+    uint32_t rank;      // 0-based rank still to find inside the prefix class
+    uint32_t active;    // 0 when the quota is zero
+};
+
+}  // namespace da2
+
+struct da2_layout_s {
+    da2_shape s;
+    int N, R, Ry, Rx, BH, d;
+    int64_t nchunk;           // rank chunks per head (head scope)
+    da2::Workspace ws;
+};
+
+struct da2_plan_s {
+    da2_layout_s L;
+    char *ws;
+    size_t ws_bytes;
+    const void *q, *k;        // inputs the plan was built on
+    int ready;                // operands + schedule present
+    int has_keys;             // draft keys present (da2_plan, not from tier map)
+    int timing;               // record events around the attention kernel
+    int nev;                  // recorded event pairs
+    hipEvent_t *ev;           // [2 * kMaxTimed] when timing is on
+};
+
+namespace da2 {
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the kernel translation units).
+// ---------------------------------------------------------------------------
+void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, hipStream_t st);
+void launch_prep_v(const da2_layout_s &L, const void *v, char *ws, hipStream_t st);
+void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st);
+void launch_rank(const da2_layout_s &L, int scope, int64_t t8, int64_t tk, char *ws,
+                 hipStream_t st);
+void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st);
+void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hipStream_t st);
+void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, hipStream_t st);
+void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st);
+
+}  // namespace da2

@@ -1,0 +1,314 @@
+// k_attn.hip -- phased mixed-precision block-sparse attention (DraftAttention2,
+// Sec. 3.3 "phased execution" and "cross-precision accumulation", App. B.3 /
+// B.4 shared normalization, App. C.1 empty rows) on gfx950 matrix cores.
+//
+// One workgroup = one query region (64 queries) of one (b, h); wave w owns
+// queries 32w .. 32w+31.  Both products use 32x32x64 f8f6f4 MFMAs in the
+// transposed form
+//     S^T = K Q^T      (A = key rows, B = queries, k = channels)
+//     O^T = V^T P^T    (A = channels, B = queries, k = keys)
+// so every lane holds one query: its softmax statistics never leave the lane
+// except for one exchange with the partner lane (l ^ 32) per tile.  Key rows
+// are stored permuted inside each region (see key_of_row) so that the S^T
+// accumulator hands each lane a whole 32-key group, which is exactly the B
+// operand chunk of the P^T V product and exactly one MX block of P.
+//
+// FP8 phase (tiles of the schedule's FP8 list, ascending): S from FP8 codes,
+// c8 = sQ sK log2(e)/sqrt(d); running max m per 64-key tile; e = 2^(S c8 + 8
+// - m) = 256 w; Z += e; P = e4m3(e); acc += P^T V8 (codes; V's per-channel
+// scale is left out).  Phase boundary: acc[c] *= sV[c] (the change of units).
+// MXFP4 phase: S from scaled MXFP4 MFMAs, c4 = log2(e)/sqrt(d); P gets one
+// E8M0 exponent per 32 keys (floor(log2 max) - 2 of the group's largest e);
+// acc += P^T V4 with both block scales applied by the MFMA.  Epilogue:
+// O = acc / Z (256 cancels), zero when no tile is kept; rows are written
+// straight to their original token positions (restore).
+#include "da2_internal.h"
+#include "da2_device.h"
+
+namespace da2 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+    const uint8_t *q8, *q4, *q4s;
+    const float *qs8;
+    const uint8_t *k8, *k4, *k4s;
+    const float *ks8;
+    const uint8_t *v8, *v4, *v4s;
+    const float *vs8;
+    const uint16_t *sched;
+    const int32_t *cnt;
+    void *out;
+    int64_t osb, osh, osn;
+    int out_f32;
+    int H, R, Ry, Rx, Hv, Wv;
+    float c4;  // log2(e) / sqrt(d)
+};
+
+__device__ __forceinline__ float pair_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ v8i load32(const uint8_t *p)
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    uint4 a = q[0], b = q[1];
+    v8i r;
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    return r;
+}
+
+__device__ __forceinline__ v8i load16(const uint8_t *p)
+{
+    uint4 a = *reinterpret_cast<const uint4 *>(p);
+    v8i r;
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void k_attn(const AttnArgs A)
+{
+    constexpr int KC = D / 64;   // 64-channel steps of QK^T
+    constexpr int CB = D / 32;   // 32-channel blocks of the output
+    const int a = blockIdx.x, bh = blockIdx.y;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hf = l >> 5;
+    const int R = A.R;
+    const int64_t qblk = (int64_t)bh * R + a;
+
+    // queries of this wave, both formats
+    v8i q8[KC], q4[KC];
+    int q4s[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; kc++) {
+        const int chunk = (w * KC + kc) * 64 + l;
+        q8[kc] = load32(A.q8 + qblk * (kBlk * D) + chunk * 32);
+        q4[kc] = load16(A.q4 + qblk * (kBlk * D / 2) + chunk * 16);
+        q4s[kc] = A.q4s[qblk * (2 * D) + chunk];
+    }
+    const float qs = A.qs8[qblk];
+    const int n8 = A.cnt[qblk * 2], n4 = A.cnt[qblk * 2 + 1];
+    const uint16_t *list = A.sched + qblk * R;
+
+    v16f acc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+        acc[cb] = (v16f){};
+    float m = -__builtin_huge_valf();
+    float z = 0.0f;
+
+    // ---------------- FP8 phase ----------------
+    for (int it = 0; it < n8; it++) {
+        const int kb = list[it];
+        const int64_t kblk = (int64_t)bh * R + kb;
+        const uint8_t *kp = A.k8 + kblk * (kBlk * D);
+        v16f s[2];
+#pragma unroll
+        for (int mm = 0; mm < 2; mm++) {
+            s[mm] = (v16f){};
+#pragma unroll
+            for (int kc = 0; kc < KC; kc++)
+                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    load32(kp + ((mm * KC + kc) * 64 + l) * 32), q8[kc], s[mm], 0, 0, 0, 0, 0, 0);
+        }
+        const float c8 = (qs * A.ks8[kblk]) * A.c4;
+        float mx = s[0][0];
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+        mx = pair_max(mx);
+        const float mnew = fmaxf(m, mx * c8);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        if (__any(alpha != 1.0f)) {
+            z *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] *= alpha;
+        }
+        m = mnew;
+        const float bias = 8.0f - mnew;
+        v8i p;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const int mm = q >> 2, r0 = 4 * (q & 3);
+            float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
+            float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
+            float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
+            float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
+            z += (e0 + e1) + (e2 + e3);
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
+            p[q] = wd;
+        }
+        const uint8_t *vp = A.v8 + kblk * (kBlk * D);
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+            acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                load32(vp + (cb * 64 + l) * 32), p, acc[cb], 0, 0, 0, 0, 0, 0);
+    }
+
+    // ---------------- phase boundary: FP8 value units -> real units ----------------
+    if (n8 > 0) {
+        const float *vs = A.vs8 + (int64_t)bh * D;
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+    }
+
+    // ---------------- MXFP4 phase ----------------
+    for (int it = n8; it < n8 + n4; it++) {
+        const int kb = list[it];
+        const int64_t kblk = (int64_t)bh * R + kb;
+        const uint8_t *kp = A.k4 + kblk * (kBlk * D / 2);
+        const uint8_t *ksp = A.k4s + kblk * (2 * D);
+        v16f s[2];
+#pragma unroll
+        for (int mm = 0; mm < 2; mm++) {
+            s[mm] = (v16f){};
+#pragma unroll
+            for (int kc = 0; kc < KC; kc++) {
+                const int chunk = (mm * KC + kc) * 64 + l;
+                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    load16(kp + chunk * 16), q4[kc], s[mm], 4, 4, 0, (int)ksp[chunk], 0, q4s[kc]);
+            }
+        }
+        const float c = A.c4;
+        float gm = s[0][0];
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            gm = fmaxf(gm, fmaxf(s[0][r], s[1][r]));
+        const float mx = pair_max(gm);
+        const float tm = mx * c;
+        const float mnew = fmaxf(m, tm);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        if (__any(alpha != 1.0f)) {
+            z *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] *= alpha;
+        }
+        m = mnew;
+        const float bias = 8.0f - mnew;
+        // E8M0 exponent of this lane's 32-key group: floor(log2(max e)) - 2.
+        // The group holding the running maximum has max e = 2^8 exactly
+        // (w = 1), so its exponent is fixed at 6 instead of being read from a
+        // rounded exp2 that may land just below the power of two.
+        int ef;
+        if (gm == mx && mnew == tm) {
+            ef = 127 + 6;
+        } else {
+            const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
+            ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
+            ef = ef < 0 ? 0 : ef;
+        }
+        const float pscale = ef ? __uint_as_float((uint32_t)ef << 23) : __uint_as_float(0x00400000u);
+        v8i p;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            // slots 8q .. 8q+7 of this lane's group; slot = 16*mm + r
+            const int mm = q >> 1, r0 = 8 * (q & 1);
+            float e[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
+                z += e[j];
+            }
+            uint32_t wd = 0;
+            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[0], e[1], pscale, 0);
+            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
+            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
+            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
+            p[q] = (int)wd;
+        }
+        p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
+        const uint8_t *vp = A.v4 + kblk * (kBlk * D / 2);
+        const uint8_t *vsp = A.v4s + kblk * (2 * D);
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++) {
+            const int chunk = cb * 64 + l;
+            acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                load16(vp + chunk * 16), p, acc[cb], 4, 4, 0, (int)vsp[chunk], 0, ef);
+        }
+    }
+
+    // ---------------- epilogue: normalize and restore token order ----------------
+    const float zt = pair_sum(z);
+    const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
+    const int i = 32 * w + (l & 31);
+    const int n = region_token(a, i, A.Ry, A.Rx, A.Hv, A.Wv);
+    const int b = bh / A.H, h = bh - b * A.H;
+    const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)n * A.osn;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int c0 = 32 * cb + 8 * g + 4 * hf;
+            float o0 = acc[cb][4 * g] * inv, o1 = acc[cb][4 * g + 1] * inv;
+            float o2 = acc[cb][4 * g + 2] * inv, o3 = acc[cb][4 * g + 3] * inv;
+            if (A.out_f32) {
+                *reinterpret_cast<float4 *>((float *)A.out + obase + c0) = make_float4(o0, o1, o2, o3);
+            } else {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+                pk.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
+                *reinterpret_cast<uint2 *>((uint16_t *)A.out + obase + c0) = pk;
+            }
+        }
+}
+
+}  // namespace
+
+void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hipStream_t st)
+{
+    const Workspace &W = L.ws;
+    AttnArgs A;
+    A.q8 = (const uint8_t *)(ws + W.q8);
+    A.q4 = (const uint8_t *)(ws + W.q4);
+    A.q4s = (const uint8_t *)(ws + W.q4s);
+    A.qs8 = (const float *)(ws + W.qs8);
+    A.k8 = (const uint8_t *)(ws + W.k8);
+    A.k4 = (const uint8_t *)(ws + W.k4);
+    A.k4s = (const uint8_t *)(ws + W.k4s);
+    A.ks8 = (const float *)(ws + W.ks8);
+    A.v8 = (const uint8_t *)(ws + W.v8);
+    A.v4 = (const uint8_t *)(ws + W.v4);
+    A.v4s = (const uint8_t *)(ws + W.v4s);
+    A.vs8 = (const float *)(ws + W.vs8);
+    A.sched = (const uint16_t *)(ws + W.sched);
+    A.cnt = (const int32_t *)(ws + W.cnt);
+    A.out = o;
+    A.osb = L.s.stride_b;
+    A.osh = L.s.stride_h;
+    A.osn = L.s.stride_n;
+    A.out_f32 = out_f32;
+    A.H = L.s.heads;
+    A.R = L.R;
+    A.Ry = L.Ry;
+    A.Rx = L.Rx;
+    A.Hv = L.s.height;
+    A.Wv = L.s.width;
+    A.c4 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
+    dim3 grid(L.R, L.BH);
+    if (L.d == 128)
+        k_attn<128><<<grid, 128, 0, st>>>(A);
+    else
+        k_attn<64><<<grid, 128, 0, st>>>(A);
+}
+
+}  // namespace da2

@@ -1,0 +1,576 @@
+// k_plan.hip -- draft scoring, ranking and scheduling (DraftAttention2,
+// Sec. 3.1 Eq. (2) and "joint allocation of sparsity and precision"; App. C.1
+// routing).
+//
+// Scores must be bit-identical run to run and against an fp64 reference, so
+// every floating-point step has a fixed order: logits are fused multiply-add
+// chains over channels 0..d-1 times 1/sqrt(d); row maxima (order-free);
+// exponentials by the shared Cody-Waite/Taylor exp; row sums strictly
+// sequential over key regions; p = e / Z; A = (1-lambda) p_avg + lambda p_max
+// with separate products; the ranking key is the bit pattern of fp32(A).
+//
+// Ranking (head scope) is an exact radix select on the 32-bit keys for the
+// T8-th and Tk-th largest (8-bit digits, four histogram passes), followed by
+// a pass that resolves equal keys by ascending pair index a*R+b with a
+// chunked prefix count.  Row scope does the same per query region inside one
+// workgroup.  The schedule lists, per query region, the FP8 key regions in
+// ascending order followed by the MXFP4 key regions in ascending order.
+#include "da2_internal.h"
+#include "da2_device.h"
+
+namespace da2 {
+namespace {
+
+constexpr int kChunk = 4096;   // keys per rank workgroup (256 threads x 16)
+
+// ---------------------------------------------------------------------------
+// Logits: La = avgQ avgK^T / sqrt(d), Lm = maxQ maxK^T / sqrt(d), fp64.
+// 64x64 output tile per workgroup, 4x4 per thread and branch; channels staged
+// through LDS 16 at a time; every accumulator is one fma chain in channel
+// order.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_logits(const double *__restrict__ qa,
+                                                const double *__restrict__ ka,
+                                                const float *__restrict__ qm,
+                                                const float *__restrict__ km, int R,
+                                                double inv_sqrt_d, double *__restrict__ La,
+                                                double *__restrict__ Lm)
+{
+    constexpr int CK = 16;
+    __shared__ double sqa[CK][64], ska[CK][64], sqm[CK][64], skm[CK][64];
+    const int b0 = blockIdx.x * 64, a0 = blockIdx.y * 64, bh = blockIdx.z;
+    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+    const double *qab = qa + (int64_t)bh * R * D, *kab = ka + (int64_t)bh * R * D;
+    const float *qmb = qm + (int64_t)bh * R * D, *kmb = km + (int64_t)bh * R * D;
+    double aa[4][4], am[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            aa[i][j] = 0.0;
+            am[i][j] = 0.0;
+        }
+    for (int c0 = 0; c0 < D; c0 += CK) {
+        // 64 rows x 16 channels per array; thread loads 4 elements per array
+        for (int e = t; e < 64 * CK; e += 256) {
+            int r = e / CK, c = e - r * CK;
+            int ga = a0 + r, gb = b0 + r;
+            sqa[c][r] = ga < R ? qab[(int64_t)ga * D + c0 + c] : 0.0;
+            sqm[c][r] = ga < R ? (double)qmb[(int64_t)ga * D + c0 + c] : 0.0;
+            ska[c][r] = gb < R ? kab[(int64_t)gb * D + c0 + c] : 0.0;
+            skm[c][r] = gb < R ? (double)kmb[(int64_t)gb * D + c0 + c] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int c = 0; c < CK; c++) {
+            double xa[4], ya[4], xm[4], ym[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                xa[i] = sqa[c][ty + 16 * i];
+                xm[i] = sqm[c][ty + 16 * i];
+                ya[i] = ska[c][tx + 16 * i];
+                ym[i] = skm[c][tx + 16 * i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    aa[i][j] = __builtin_fma(xa[i], ya[j], aa[i][j]);
+                    am[i][j] = __builtin_fma(xm[i], ym[j], am[i][j]);
+                }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        int ga = a0 + ty + 16 * i;
+        if (ga >= R)
+            continue;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            int gb = b0 + tx + 16 * j;
+            if (gb < R) {
+                int64_t o = ((int64_t)bh * R + ga) * R + gb;
+                La[o] = aa[i][j] * inv_sqrt_d;
+                Lm[o] = am[i][j] * inv_sqrt_d;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row softmax of both branches and the mixture, 64 query regions per
+// workgroup.  The exponentials overwrite the logits; the row sums run in one
+// thread per (row, branch), strictly in key order, chunk after chunk.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_softmix(double *__restrict__ La, double *__restrict__ Lm,
+                                                 int R, double lambda,
+                                                 uint32_t *__restrict__ keys)
+{
+    __shared__ double rmax[2][64], rsum[2][64];
+    __shared__ double ech[2][64][33];
+    const int a0 = blockIdx.x * 64, bh = blockIdx.y, t = threadIdx.x;
+    const int rows = min(64, R - a0);
+    // 1) row maxima: 4 threads per row, one branch at a time
+    {
+        const int r = t >> 2, q = t & 3;
+        for (int br = 0; br < 2; br++) {
+            double m = -__builtin_huge_val();
+            if (r < rows) {
+                const double *L = (br ? Lm : La) + ((int64_t)bh * R + a0 + r) * R;
+                for (int b = q; b < R; b += 4)
+                    m = fmax(m, L[b]);
+            }
+            m = fmax(m, __shfl_xor(m, 1, 64));
+            m = fmax(m, __shfl_xor(m, 2, 64));
+            if (q == 0)
+                rmax[br][r] = m;
+        }
+        if (t < 128)
+            rsum[t >> 6][t & 63] = 0.0;
+    }
+    __syncthreads();
+    // 2) exponentials chunk by chunk, then sequential sums
+    for (int b0 = 0; b0 < R; b0 += 32) {
+        const int cols = min(32, R - b0);
+        for (int e = t; e < 2 * 64 * 32; e += 256) {
+            int br = e >> 11, r = (e >> 5) & 63, c = e & 31;
+            if (r < rows && c < cols) {
+                double *L = (br ? Lm : La) + ((int64_t)bh * R + a0 + r) * R + b0 + c;
+                double v = exp_draft(*L - rmax[br][r]);
+                *L = v;
+                ech[br][r][c] = v;
+            }
+        }
+        __syncthreads();
+        if (t < 128) {
+            int br = t >> 6, r = t & 63;
+            if (r < rows) {
+                double z = rsum[br][r];
+                for (int c = 0; c < cols; c++)
+                    z += ech[br][r][c];
+                rsum[br][r] = z;
+            }
+        }
+        __syncthreads();
+    }
+    // 3) probabilities, mixture, keys
+    const double w0 = 1.0 - lambda;
+    for (int r = 0; r < rows; r++) {
+        const int64_t o = ((int64_t)bh * R + a0 + r) * R;
+        const double za = rsum[0][r], zm = rsum[1][r];
+        for (int b = t; b < R; b += 256) {
+            double pa = La[o + b] / za;
+            double pm = Lm[o + b] / zm;
+            double t0 = w0 * pa;
+            double t1 = lambda * pm;
+            double A = t0 + t1;
+            keys[o + b] = __float_as_uint((float)A);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Head-scope radix select.
+// ---------------------------------------------------------------------------
+__global__ void k_rank_init(RankState *__restrict__ st, uint32_t *__restrict__ hist, int nseg,
+                            int64_t t8, int64_t tk)
+{
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nseg * 2) {
+        int64_t T = (i & 1) ? tk : t8;
+        RankState s;
+        s.prefix = 0;
+        s.mask = 0;
+        s.rank = T > 0 ? (uint32_t)(T - 1) : 0u;
+        s.active = T > 0 ? 1u : 0u;
+        st[i] = s;
+    }
+    for (int j = i; j < nseg * 2 * 256; j += gridDim.x * blockDim.x)
+        hist[j] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_rank_hist(const uint32_t *__restrict__ keys,
+                                                   int64_t seglen, int64_t nchunk,
+                                                   const RankState *__restrict__ st,
+                                                   uint32_t *__restrict__ hist, int shift)
+{
+    __shared__ uint32_t h[2][256];
+    const int seg = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+    const int t = threadIdx.x;
+    h[0][t] = 0;
+    h[1][t] = 0;
+    const RankState s0 = st[seg * 2], s1 = st[seg * 2 + 1];
+    __syncthreads();
+    const uint32_t *kp = keys + (int64_t)seg * seglen;
+    for (int j = 0; j < kChunk / 256; j++) {
+        int64_t i = c0 + j * 256 + t;
+        if (i < seglen) {
+            uint32_t k = kp[i];
+            uint32_t dg = (k >> shift) & 255u;
+            if (s0.active && ((k ^ s0.prefix) & s0.mask) == 0)
+                atomicAdd(&h[0][dg], 1u);
+            if (s1.active && ((k ^ s1.prefix) & s1.mask) == 0)
+                atomicAdd(&h[1][dg], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t *g = hist + (int64_t)seg * 512;
+    if (h[0][t])
+        atomicAdd(&g[t], h[0][t]);
+    if (h[1][t])
+        atomicAdd(&g[256 + t], h[1][t]);
+}
+
+// One workgroup per segment: pick the digit holding the wanted rank (keys in
+// descending order), fix it in the prefix, clear the histogram.
+__global__ __launch_bounds__(256) void k_rank_select(RankState *__restrict__ st,
+                                                     uint32_t *__restrict__ hist, int shift)
+{
+    __shared__ uint32_t scan[256];
+    const int seg = blockIdx.x, t = threadIdx.x;
+    for (int tg = 0; tg < 2; tg++) {
+        RankState s = st[seg * 2 + tg];
+        uint32_t *g = hist + (int64_t)seg * 512 + tg * 256;
+        const int dg = 255 - t;  // thread t owns digit 255 - t (descending order)
+        uint32_t cnt = g[dg];
+        scan[t] = cnt;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            uint32_t v = t >= o ? scan[t - o] : 0u;
+            __syncthreads();
+            scan[t] += v;
+            __syncthreads();
+        }
+        uint32_t incl = scan[t], excl = incl - cnt;
+        if (s.active && excl <= s.rank && s.rank < incl) {
+            s.prefix |= (uint32_t)dg << shift;
+            s.mask |= 255u << shift;
+            s.rank -= excl;
+            st[seg * 2 + tg] = s;
+        }
+        __syncthreads();
+        g[dg] = 0;
+        __syncthreads();
+    }
+}
+
+// Count keys equal to each threshold per chunk.
+__global__ __launch_bounds__(256) void k_rank_eqcount(const uint32_t *__restrict__ keys,
+                                                      int64_t seglen, int64_t nchunk,
+                                                      const RankState *__restrict__ st,
+                                                      uint32_t *__restrict__ eq)
+{
+    const int seg = blockIdx.y, t = threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+    const RankState s0 = st[seg * 2], s1 = st[seg * 2 + 1];
+    const uint32_t *kp = keys + (int64_t)seg * seglen;
+    uint32_t n0 = 0, n1 = 0;
+    for (int j = 0; j < kChunk / 256; j++) {
+        int64_t i = c0 + j * 256 + t;
+        if (i < seglen) {
+            uint32_t k = kp[i];
+            n0 += (s0.active && k == s0.prefix);
+            n1 += (s1.active && k == s1.prefix);
+        }
+    }
+    __shared__ uint32_t r[2][4];
+    n0 = wave_sum_u32(n0);
+    n1 = wave_sum_u32(n1);
+    if ((t & 63) == 0) {
+        r[0][t >> 6] = n0;
+        r[1][t >> 6] = n1;
+    }
+    __syncthreads();
+    if (t < 2)
+        eq[((int64_t)seg * nchunk + blockIdx.x) * 2 + t] = r[t][0] + r[t][1] + r[t][2] + r[t][3];
+}
+
+// Final tier per key: above the threshold, or equal to it and among the first
+// `rank + 1` equal keys by pair index.
+__global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ keys,
+                                                   int64_t seglen, int64_t nchunk,
+                                                   const RankState *__restrict__ st,
+                                                   const uint32_t *__restrict__ eq,
+                                                   uint8_t *__restrict__ tier)
+{
+    __shared__ uint32_t base[2];
+    __shared__ uint32_t scan[2][256];
+    const int seg = blockIdx.y, t = threadIdx.x;
+    const int64_t ch = blockIdx.x;
+    const RankState s0 = st[seg * 2], s1 = st[seg * 2 + 1];
+    // equal keys in earlier chunks of this segment
+    if (t < 64) {
+        uint32_t p0 = 0, p1 = 0;
+        for (int64_t c = t; c < ch; c += 64) {
+            p0 += eq[((int64_t)seg * nchunk + c) * 2];
+            p1 += eq[((int64_t)seg * nchunk + c) * 2 + 1];
+        }
+        p0 = wave_sum_u32(p0);
+        p1 = wave_sum_u32(p1);
+        if (t == 0) {
+            base[0] = p0;
+            base[1] = p1;
+        }
+    }
+    // this thread owns 16 consecutive keys
+    const int64_t i0 = ch * kChunk + (int64_t)t * 16;
+    const uint32_t *kp = keys + (int64_t)seg * seglen;
+    uint32_t kv[16];
+    uint32_t e0 = 0, e1 = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        int64_t i = i0 + j;
+        kv[j] = i < seglen ? kp[i] : 0u;
+        e0 += (i < seglen && s0.active && kv[j] == s0.prefix);
+        e1 += (i < seglen && s1.active && kv[j] == s1.prefix);
+    }
+    scan[0][t] = e0;
+    scan[1][t] = e1;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        uint32_t v0 = t >= o ? scan[0][t - o] : 0u, v1 = t >= o ? scan[1][t - o] : 0u;
+        __syncthreads();
+        scan[0][t] += v0;
+        scan[1][t] += v1;
+        __syncthreads();
+    }
+    uint32_t r0 = base[0] + scan[0][t] - e0, r1 = base[1] + scan[1][t] - e1;
+    uint8_t *tp = tier + (int64_t)seg * seglen;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        int64_t i = i0 + j;
+        if (i >= seglen)
+            break;
+        uint32_t k = kv[j];
+        bool in8 = false, ink = false;
+        if (s0.active) {
+            if (k > s0.prefix)
+                in8 = true;
+            else if (k == s0.prefix) {
+                in8 = r0 <= s0.rank;
+                r0++;
+            }
+        }
+        if (s1.active) {
+            if (k > s1.prefix)
+                ink = true;
+            else if (k == s1.prefix) {
+                ink = r1 <= s1.rank;
+                r1++;
+            }
+        }
+        tp[i] = in8 ? 8 : (ink ? 4 : 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row scope: one workgroup per query region, keys of the row in LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rank_rows(const uint32_t *__restrict__ keys, int R,
+                                                   int64_t t8, int64_t tk,
+                                                   uint8_t *__restrict__ tier)
+{
+    extern __shared__ uint32_t row[];
+    __shared__ uint32_t hist[256], scan[256];
+    __shared__ RankState s[2];
+    const int64_t seg = blockIdx.x;
+    const int t = threadIdx.x;
+    for (int b = t; b < R; b += 256)
+        row[b] = keys[seg * R + b];
+    if (t < 2) {
+        int64_t T = t ? tk : t8;
+        s[t].prefix = 0;
+        s[t].mask = 0;
+        s[t].rank = T > 0 ? (uint32_t)(T - 1) : 0u;
+        s[t].active = T > 0;
+    }
+    __syncthreads();
+    for (int tg = 0; tg < 2; tg++) {
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            hist[t] = 0;
+            __syncthreads();
+            RankState cur = s[tg];
+            for (int b = t; b < R; b += 256) {
+                uint32_t k = row[b];
+                if (cur.active && ((k ^ cur.prefix) & cur.mask) == 0)
+                    atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            const int dg = 255 - t;
+            uint32_t cnt = hist[dg];
+            scan[t] = cnt;
+            __syncthreads();
+            for (int o = 1; o < 256; o <<= 1) {
+                uint32_t v = t >= o ? scan[t - o] : 0u;
+                __syncthreads();
+                scan[t] += v;
+                __syncthreads();
+            }
+            uint32_t incl = scan[t], excl = incl - cnt;
+            if (cur.active && excl <= cur.rank && cur.rank < incl) {
+                s[tg].prefix = cur.prefix | ((uint32_t)dg << shift);
+                s[tg].mask = cur.mask | (255u << shift);
+                s[tg].rank = cur.rank - excl;
+            }
+            __syncthreads();
+        }
+    }
+    // resolve ties in index order: thread t owns keys [t*per, (t+1)*per)
+    const int per = (R + 255) / 256;
+    const int bb = t * per;
+    uint32_t e0 = 0, e1 = 0;
+    for (int j = 0; j < per; j++) {
+        int b = bb + j;
+        if (b < R) {
+            e0 += (s[0].active && row[b] == s[0].prefix);
+            e1 += (s[1].active && row[b] == s[1].prefix);
+        }
+    }
+    __shared__ uint32_t sc2[2][256];
+    sc2[0][t] = e0;
+    sc2[1][t] = e1;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        uint32_t v0 = t >= o ? sc2[0][t - o] : 0u, v1 = t >= o ? sc2[1][t - o] : 0u;
+        __syncthreads();
+        sc2[0][t] += v0;
+        sc2[1][t] += v1;
+        __syncthreads();
+    }
+    uint32_t r0 = sc2[0][t] - e0, r1 = sc2[1][t] - e1;
+    for (int j = 0; j < per; j++) {
+        int b = bb + j;
+        if (b >= R)
+            break;
+        uint32_t k = row[b];
+        bool in8 = false, ink = false;
+        if (s[0].active) {
+            if (k > s[0].prefix)
+                in8 = true;
+            else if (k == s[0].prefix) {
+                in8 = r0 <= s[0].rank;
+                r0++;
+            }
+        }
+        if (s[1].active) {
+            if (k > s[1].prefix)
+                ink = true;
+            else if (k == s[1].prefix) {
+                ink = r1 <= s[1].rank;
+                r1++;
+            }
+        }
+        tier[seg * R + b] = in8 ? 8 : (ink ? 4 : 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Schedule: per query region, FP8 key regions ascending then MXFP4 ascending.
+// One wave per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tier, int R,
+                                                 uint16_t *__restrict__ sched,
+                                                 int32_t *__restrict__ cnt)
+{
+    const int64_t row = (int64_t)blockIdx.y * R + blockIdx.x;
+    const int l = threadIdx.x;
+    const uint8_t *tr = tier + row * R;
+    uint32_t n8 = 0, n4 = 0;
+    for (int b = l; b < R; b += 64) {
+        uint8_t v = tr[b];
+        n8 += v == 8;
+        n4 += v == 4;
+    }
+    n8 = wave_sum_u32(n8);
+    n4 = wave_sum_u32(n4);
+    uint16_t *out = sched + row * R;
+    uint32_t o8 = 0, o4 = n8;
+    for (int b0 = 0; b0 < R; b0 += 64) {
+        int b = b0 + l;
+        uint8_t v = b < R ? tr[b] : 0;
+        uint64_t m8 = __ballot(v == 8), m4 = __ballot(v == 4);
+        uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
+        if (v == 8)
+            out[o8 + __popcll(m8 & lt)] = (uint16_t)b;
+        if (v == 4)
+            out[o4 + __popcll(m4 & lt)] = (uint16_t)b;
+        o8 += __popcll(m8);
+        o4 += __popcll(m4);
+    }
+    if (l == 0) {
+        cnt[row * 2] = (int32_t)n8;
+        cnt[row * 2 + 1] = (int32_t)n4;
+    }
+}
+
+__global__ void k_copy_tier(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t n)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        uint8_t v = src[i];
+        dst[i] = (v == 8 || v == 4) ? v : 0;
+    }
+}
+
+}  // namespace
+
+void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st)
+{
+    const Workspace &W = L.ws;
+    const double inv_sqrt_d = 1.0 / __builtin_sqrt((double)L.d);
+    const int T = (L.R + 63) / 64;
+    dim3 g(T, T, L.BH);
+    double *La = (double *)(ws + W.la), *Lm = (double *)(ws + W.lm);
+    if (L.d == 128)
+        k_logits<128><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
+                                         (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
+                                         L.R, inv_sqrt_d, La, Lm);
+    else
+        k_logits<64><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
+                                        (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
+                                        L.R, inv_sqrt_d, La, Lm);
+    k_softmix<<<dim3(T, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, (uint32_t *)(ws + W.keys));
+}
+
+void launch_rank(const da2_layout_s &L, int scope, int64_t t8, int64_t tk, char *ws,
+                 hipStream_t st)
+{
+    const Workspace &W = L.ws;
+    const uint32_t *keys = (const uint32_t *)(ws + W.keys);
+    uint8_t *tier = (uint8_t *)(ws + W.tier);
+    if (scope == 1) {
+        k_rank_rows<<<(unsigned)((int64_t)L.BH * L.R), 256, sizeof(uint32_t) * L.R, st>>>(
+            keys, L.R, t8, tk, tier);
+        return;
+    }
+    RankState *rs = (RankState *)(ws + W.rank_state);
+    uint32_t *hist = (uint32_t *)(ws + W.rank_hist), *eq = (uint32_t *)(ws + W.rank_eq);
+    const int64_t seglen = (int64_t)L.R * L.R;
+    const int64_t nchunk = L.nchunk;
+    k_rank_init<<<(L.BH * 2 * 256 + 255) / 256, 256, 0, st>>>(rs, hist, L.BH, t8, tk);
+    dim3 g((unsigned)nchunk, L.BH);
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        k_rank_hist<<<g, 256, 0, st>>>(keys, seglen, nchunk, rs, hist, shift);
+        k_rank_select<<<L.BH, 256, 0, st>>>(rs, hist, shift);
+    }
+    k_rank_eqcount<<<g, 256, 0, st>>>(keys, seglen, nchunk, rs, eq);
+    k_rank_tier<<<g, 256, 0, st>>>(keys, seglen, nchunk, rs, eq, tier);
+}
+
+void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
+{
+    const Workspace &W = L.ws;
+    k_schedule<<<dim3(L.R, L.BH), 64, 0, st>>>((const uint8_t *)(ws + W.tier), L.R,
+                                                (uint16_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
+}
+
+void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st)
+{
+    int64_t n = (int64_t)L.BH * L.R * L.R;
+    k_copy_tier<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(src, (uint8_t *)(ws + L.ws.tier), n);
+}
+
+}  // namespace da2

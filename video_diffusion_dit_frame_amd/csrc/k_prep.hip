@@ -1,0 +1,282 @@
+// k_prep.hip -- fused operand preparation (DraftAttention2, Sec. 3.3 "fused
+// quantization and reordering"; App. C.2 spatial packing).
+//
+// k_prep_qk: one workgroup per (b, h, region).  Gathers the region's 64
+// tokens (one coalesced 16-byte load per chunk, strided input), and from the
+// same LDS copy emits the pooled descriptors of Eq. (1) (fp64 sum in region
+// order / 64, signed max), the FP8 E4M3 codes with one fp32 scale per block
+// (amax / 448, codes of x * (448 / amax)), and MXFP4 E2M1 codes with one E8M0
+// exponent per token and 32 channels -- all written directly in the MFMA
+// operand layouts the attention kernel loads.
+//
+// k_vamax + k_prep_v: V gets one FP8 scale per channel over all tokens (so
+// the attention accumulator changes units once, at the end of the FP8 phase)
+// and MXFP4 groups of 32 consecutive keys inside each region, packed as the
+// A operand of O^T = V^T P^T (the value transposition folded into packing).
+#include "da2_internal.h"
+#include "da2_device.h"
+
+namespace da2 {
+namespace {
+
+// Copy the 64 x D bf16 tile of region a into LDS (row i = region position i).
+template <int D>
+__device__ __forceinline__ void load_region(const uint16_t *__restrict__ x, int64_t sn, int a,
+                                            int Ry, int Rx, int Hv, int Wv, uint16_t *tile)
+{
+    constexpr int CH = D / 8;  // 16-byte chunks per token row
+    for (int ci = threadIdx.x; ci < kBlk * CH; ci += 256) {
+        int i = ci / CH, c8 = ci - i * CH;
+        int n = region_token(a, i, Ry, Rx, Hv, Wv);
+        uint4 v = *reinterpret_cast<const uint4 *>(x + (int64_t)n * sn + c8 * 8);
+        *reinterpret_cast<uint4 *>(tile + i * D + c8 * 8) = v;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x, int64_t sb,
+                                                 int64_t sh, int64_t sn, int H, int R, int Ry,
+                                                 int Rx, int Hv, int Wv, int is_key,
+                                                 uint8_t *__restrict__ op8, float *__restrict__ s8,
+                                                 uint8_t *__restrict__ op4,
+                                                 uint8_t *__restrict__ op4s,
+                                                 double *__restrict__ avg, float *__restrict__ mx)
+{
+    constexpr int KC = D / 64;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk * D];
+    __shared__ float red[4];
+    const int a = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
+    load_region<D>(xb, sn, a, Ry, Rx, Hv, Wv, tile);
+    __syncthreads();
+
+    const int t = threadIdx.x;
+    const int64_t blk = (int64_t)bh * R + a;
+    // pooled descriptors: channel t, tokens in region order
+    if (t < D) {
+        double s = 0.0;
+        float m = bf16_to_f32(tile[t]);
+        for (int i = 0; i < kBlk; i++) {
+            float v = bf16_to_f32(tile[i * D + t]);
+            s += (double)v;
+            if (v > m)
+                m = v;
+        }
+        avg[blk * D + t] = s / (double)kBlk;
+        mx[blk * D + t] = m;
+    }
+    // FP8 block scale
+    float am = 0.0f;
+    for (int e = t; e < kBlk * D; e += 256)
+        am = fmaxf(am, __builtin_fabsf(bf16_to_f32(tile[e])));
+    am = wave_max_f32(am);
+    if ((t & 63) == 0)
+        red[t >> 6] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float sc = 1.0f, inv = 0.0f;
+    if (am != 0.0f) {
+        sc = am / 448.0f;
+        inv = 448.0f / am;
+    }
+    if (t == 0)
+        s8[blk] = sc;
+
+    // operand chunks: t -> (half, kc, lane); 2*KC*64 = 2*D chunks per block
+    if (t < 2 * D) {
+        const int half = t / (KC * 64), kc = (t / 64) % KC, l = t & 63;
+        const int row = is_key ? key_of_row(l & 31, half) : 32 * half + (l & 31);
+        const int c0 = 64 * kc + 32 * (l >> 5);
+        const uint16_t *src = tile + row * D + c0;
+        float xv[32];
+        float ga = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            xv[j] = bf16_to_f32(src[j]);
+            ga = fmaxf(ga, __builtin_fabsf(xv[j]));
+        }
+        uint32_t w8[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                v |= (uint32_t)enc_e4m3(xv[4 * q + j] * inv) << (8 * j);
+            w8[q] = v;
+        }
+        uint4 *d8 = reinterpret_cast<uint4 *>(op8 + blk * (kBlk * D) + (int64_t)t * 32);
+        d8[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+        d8[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+        const int E = mx_exponent(ga);
+        uint32_t w4[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                v |= enc_e2m1_scaled(xv[8 * q + j], E) << (4 * j);
+            w4[q] = v;
+        }
+        *reinterpret_cast<uint4 *>(op4 + blk * (kBlk * D / 2) + (int64_t)t * 16) =
+            make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        op4s[blk * (2 * D) + t] = (uint8_t)(E + 127);
+    }
+}
+
+// Per-channel absolute maxima of V over all tokens (atomic max on the bit
+// pattern, which orders like the value for non-negative floats).
+template <int D>
+__global__ __launch_bounds__(256) void k_vamax(const uint16_t *__restrict__ x, int64_t sb,
+                                               int64_t sh, int64_t sn, int H, int N,
+                                               uint32_t *__restrict__ vamax)
+{
+    constexpr int CH = D / 8;           // chunks per token
+    constexpr int TPI = 256 / CH;       // tokens per iteration
+    constexpr int TOK = 256;            // tokens per workgroup
+    __shared__ float part[TPI][D];
+    const int bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
+    const int t = threadIdx.x, c8 = t % CH, ti = t / CH;
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int n0 = blockIdx.x * TOK;
+    for (int n = n0 + ti; n < min(n0 + TOK, N); n += TPI) {
+        uint4 v = *reinterpret_cast<const uint4 *>(xb + (int64_t)n * sn + c8 * 8);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            m[2 * j] = fmaxf(m[2 * j], __builtin_fabsf(bf16_to_f32((uint16_t)(w[j] & 0xffffu))));
+            m[2 * j + 1] = fmaxf(m[2 * j + 1], __builtin_fabsf(bf16_to_f32((uint16_t)(w[j] >> 16))));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        part[ti][c8 * 8 + j] = m[j];
+    __syncthreads();
+    if (t < D) {
+        float r = 0.0f;
+        for (int i = 0; i < TPI; i++)
+            r = fmaxf(r, part[i][t]);
+        atomicMax(&vamax[(int64_t)bh * D + t], __float_as_uint(r));
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, int64_t sb,
+                                                int64_t sh, int64_t sn, int H, int R, int Ry,
+                                                int Rx, int Hv, int Wv,
+                                                const uint32_t *__restrict__ vamax,
+                                                uint8_t *__restrict__ op8, float *__restrict__ s8,
+                                                uint8_t *__restrict__ op4,
+                                                uint8_t *__restrict__ op4s)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk * D];
+    const int a = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
+    load_region<D>(xb, sn, a, Ry, Rx, Hv, Wv, tile);
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int64_t blk = (int64_t)bh * R + a;
+    if (t < 2 * D) {
+        const int cb = t >> 6, l = t & 63;
+        const int c = 32 * cb + (l & 31), k0 = 32 * (l >> 5);
+        const float am = __uint_as_float(vamax[(int64_t)bh * D + c]);
+        float sc = 1.0f, inv = 0.0f;
+        if (am != 0.0f) {
+            sc = am / 448.0f;
+            inv = 448.0f / am;
+        }
+        if (a == 0 && l < 32)
+            s8[(int64_t)bh * D + c] = sc;
+        float xv[32];
+        float ga = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            xv[j] = bf16_to_f32(tile[(k0 + j) * D + c]);
+            ga = fmaxf(ga, __builtin_fabsf(xv[j]));
+        }
+        uint32_t w8[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                v |= (uint32_t)enc_e4m3(xv[4 * q + j] * inv) << (8 * j);
+            w8[q] = v;
+        }
+        uint4 *d8 = reinterpret_cast<uint4 *>(op8 + blk * (kBlk * D) + (int64_t)t * 32);
+        d8[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+        d8[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+        const int E = mx_exponent(ga);
+        uint32_t w4[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                v |= enc_e2m1_scaled(xv[8 * q + j], E) << (4 * j);
+            w4[q] = v;
+        }
+        *reinterpret_cast<uint4 *>(op4 + blk * (kBlk * D / 2) + (int64_t)t * 16) =
+            make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        op4s[blk * (2 * D) + t] = (uint8_t)(E + 127);
+    }
+}
+
+__global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = v;
+}
+
+}  // namespace
+
+void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, hipStream_t st)
+{
+    const Workspace &W = L.ws;
+    dim3 grid(L.R, L.BH);
+    const uint16_t *xp = static_cast<const uint16_t *>(x);
+    uint8_t *op8 = (uint8_t *)(ws + (is_key ? W.k8 : W.q8));
+    float *s8 = (float *)(ws + (is_key ? W.ks8 : W.qs8));
+    uint8_t *op4 = (uint8_t *)(ws + (is_key ? W.k4 : W.q4));
+    uint8_t *op4s = (uint8_t *)(ws + (is_key ? W.k4s : W.q4s));
+    double *avg = (double *)(ws + (is_key ? W.kavg : W.qavg));
+    float *mx = (float *)(ws + (is_key ? W.kmax : W.qmax));
+    const da2_shape &s = L.s;
+    if (L.d == 128)
+        k_prep_qk<128><<<grid, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
+                                             L.Ry, L.Rx, s.height, s.width, is_key, op8, s8, op4,
+                                             op4s, avg, mx);
+    else
+        k_prep_qk<64><<<grid, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
+                                            L.Ry, L.Rx, s.height, s.width, is_key, op8, s8, op4,
+                                            op4s, avg, mx);
+}
+
+void launch_prep_v(const da2_layout_s &L, const void *v, char *ws, hipStream_t st)
+{
+    const Workspace &W = L.ws;
+    const da2_shape &s = L.s;
+    const uint16_t *xp = static_cast<const uint16_t *>(v);
+    uint32_t *vamax = (uint32_t *)(ws + W.vamax);
+    int64_t n = (int64_t)L.BH * L.d;
+    k_fill_u32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(vamax, n, 0u);
+    dim3 g1((L.N + 255) / 256, L.BH), g2(L.R, L.BH);
+    uint8_t *op8 = (uint8_t *)(ws + W.v8), *op4 = (uint8_t *)(ws + W.v4),
+            *op4s = (uint8_t *)(ws + W.v4s);
+    float *s8 = (float *)(ws + W.vs8);
+    if (L.d == 128) {
+        k_vamax<128><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
+        k_prep_v<128><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
+                                          L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s);
+    } else {
+        k_vamax<64><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
+        k_prep_v<64><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
+                                         L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s);
+    }
+}
+
+}  // namespace da2

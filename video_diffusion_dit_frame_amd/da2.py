@@ -1,0 +1,234 @@
+"""Thin ctypes binding of libda2 (the C ABI in include/da2.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+library.  PyTorch supplies device memory (tensors) and streams.  Importing
+this module raises if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libda2.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "da2.h")
+
+DBG = {name: i for i, name in enumerate([
+    "Q_FP8", "Q_FP8_SCALE", "Q_MX", "Q_MX_SCALE", "K_FP8", "K_FP8_SCALE", "K_MX", "K_MX_SCALE",
+    "V_FP8", "V_FP8_SCALE", "V_MX", "V_MX_SCALE", "Q_AVG", "K_AVG", "Q_MAX", "K_MAX", "KEYS",
+    "SCHEDULE"])}
+
+
+class Da2Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+        self.status = status
+
+
+class Shape(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
+                ("frames", C.c_int32), ("height", C.c_int32), ("width", C.c_int32),
+                ("stride_b", C.c_int64), ("stride_h", C.c_int64), ("stride_n", C.c_int64)]
+
+
+class Budget(C.Structure):
+    _fields_ = [("hi_bp", C.c_int32), ("lo_bp", C.c_int32), ("lambda_", C.c_double),
+                ("scope", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libda2.so; raise when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libda2.so is not built (python -m video_diffusion_dit_frame_amd.build)")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.da2_layout_create.argtypes = [C.POINTER(Shape), C.POINTER(P)]
+        L.da2_layout_destroy.argtypes = [P]
+        L.da2_workspace_bytes.argtypes = [P]
+        L.da2_workspace_bytes.restype = sz
+        L.da2_plan_create.argtypes = [P, P, sz, C.POINTER(P)]
+        L.da2_plan_destroy.argtypes = [P]
+        L.da2_plan.argtypes = [P, P, P, C.POINTER(Budget), P]
+        L.da2_plan_from_tier_map.argtypes = [P, P, P, P, P]
+        L.da2_plan_tier_map.argtypes = [P, P, P]
+        L.da2_attention.argtypes = [P, P, P, P, P, i32, P]
+        L.da2_plan_debug.argtypes = [P, i32, P, P]
+        L.da2_plan_debug_bytes.argtypes = [P, i32]
+        L.da2_plan_debug_bytes.restype = sz
+        L.da2_status_string.argtypes = [C.c_int]
+        L.da2_status_string.restype = C.c_char_p
+        L.da2_exp_constants.argtypes = [P]
+        L.da2_plan_timing.argtypes = [P, i32]
+        L.da2_plan_timing.restype = C.c_int
+        L.da2_plan_timing_read.argtypes = [P, P, i32, C.POINTER(i32)]
+        L.da2_plan_timing_read.restype = C.c_int
+        L.da2_quotas.argtypes = [i64, i32, i32, C.POINTER(i64), C.POINTER(i64)]
+        for name in ("da2_layout_create", "da2_plan_create", "da2_plan", "da2_plan_from_tier_map",
+                     "da2_plan_tier_map", "da2_attention", "da2_plan_debug"):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/da2.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(da2_[a-z_]+)\s*\(", text)))
+
+
+def status_string(st: int) -> str:
+    return lib().da2_status_string(int(st)).decode()
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise Da2Error(st, what)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def exp_constants():
+    import numpy as np
+
+    out = np.empty(17, np.float64)
+    lib().da2_exp_constants(out.ctypes.data_as(C.c_void_p))
+    return out
+
+
+def quotas(n, hi_bp, lo_bp):
+    t8, tk = C.c_int64(), C.c_int64()
+    lib().da2_quotas(int(n), int(hi_bp), int(lo_bp), C.byref(t8), C.byref(tk))
+    return t8.value, tk.value
+
+
+class Layout:
+    """Region layout for one shape.  q/k/v/o are addressed with the given
+    element strides (channel stride 1)."""
+
+    def __init__(self, B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n):
+        self.B, self.H, self.d, self.F, self.Hv, self.Wv = B, H, d, F, Hv, Wv
+        self.N = F * Hv * Wv
+        self.R = self.N // 64
+        self.shape = Shape(B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n)
+        h = C.c_void_p()
+        _check(lib().da2_layout_create(C.byref(self.shape), C.byref(h)), "da2_layout_create")
+        self.handle = h
+
+    @classmethod
+    def for_tensor(cls, x: torch.Tensor, F, Hv, Wv, bhnd=True):
+        """x: a [B, H, N, d] view (bhnd) or a [B, N, H, d] view, channel-contiguous."""
+        if bhnd:
+            B, H, N, d = x.shape
+            sb, sh, sn, sc = x.stride()
+        else:
+            B, N, H, d = x.shape
+            sb, sn, sh, sc = x.stride()
+        assert sc == 1 and N == F * Hv * Wv
+        return cls(B, H, d, F, Hv, Wv, sb, sh, sn)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(lib().da2_workspace_bytes(self.handle))
+
+    def debug_bytes(self, which) -> int:
+        return int(lib().da2_plan_debug_bytes(self.handle, DBG[which] if isinstance(which, str) else which))
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.da2_layout_destroy(self.handle)
+            self.handle = None
+
+
+class Plan:
+    """A plan bound to a caller-owned device workspace."""
+
+    def __init__(self, layout: Layout, workspace: torch.Tensor = None):
+        self.layout = layout
+        if workspace is None:
+            workspace = torch.empty(layout.workspace_bytes, dtype=torch.uint8, device="cuda")
+        self.workspace = workspace
+        h = C.c_void_p()
+        _check(lib().da2_plan_create(layout.handle, C.c_void_p(workspace.data_ptr()),
+                                     workspace.numel() * workspace.element_size(), C.byref(h)),
+               "da2_plan_create")
+        self.handle = h
+
+    def plan(self, q, k, hi_bp, lo_bp, lam=0.2, scope=0, stream=None):
+        b = Budget(int(hi_bp), int(lo_bp), float(lam), int(scope))
+        _check(lib().da2_plan(self.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                              C.byref(b), _stream(stream)), "da2_plan")
+
+    def plan_from_tier_map(self, q, k, tier: torch.Tensor, stream=None):
+        assert tier.dtype == torch.uint8 and tier.is_contiguous()
+        L = self.layout
+        assert tier.numel() == L.B * L.H * L.R * L.R
+        _check(lib().da2_plan_from_tier_map(self.handle, C.c_void_p(q.data_ptr()),
+                                            C.c_void_p(k.data_ptr()), C.c_void_p(tier.data_ptr()),
+                                            _stream(stream)), "da2_plan_from_tier_map")
+
+    def tier_map(self, stream=None) -> torch.Tensor:
+        L = self.layout
+        out = torch.empty((L.B, L.H, L.R, L.R), dtype=torch.uint8, device="cuda")
+        _check(lib().da2_plan_tier_map(self.handle, C.c_void_p(out.data_ptr()), _stream(stream)),
+               "da2_plan_tier_map")
+        return out
+
+    def attention(self, q, k, v, o, stream=None):
+        if o.dtype == torch.float32:
+            od = 1
+        elif o.dtype == torch.bfloat16:
+            od = 0
+        else:
+            raise TypeError("output must be float32 or bfloat16")
+        _check(lib().da2_attention(self.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                                   C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), od,
+                                   _stream(stream)), "da2_attention")
+
+    def debug(self, which, stream=None) -> torch.Tensor:
+        w = DBG[which] if isinstance(which, str) else int(which)
+        n = self.layout.debug_bytes(w)
+        out = torch.empty(n, dtype=torch.uint8, device="cuda")
+        _check(lib().da2_plan_debug(self.handle, w, C.c_void_p(out.data_ptr()), _stream(stream)),
+               "da2_plan_debug")
+        return out
+
+    def timing(self, enable: bool):
+        """Record HIP events around the attention kernel of later calls."""
+        _check(lib().da2_plan_timing(self.handle, int(bool(enable))), "da2_plan_timing")
+
+    def timing_read(self):
+        """Per-call attention-kernel durations (ms) recorded since timing(True)."""
+        import numpy as np
+
+        n = C.c_int32()
+        _check(lib().da2_plan_timing_read(self.handle, None, 0, C.byref(n)), "da2_plan_timing_read")
+        out = np.empty(max(n.value, 1), np.float32)
+        _check(lib().da2_plan_timing_read(self.handle, out.ctypes.data_as(C.c_void_p), n.value,
+                                          C.byref(n)), "da2_plan_timing_read")
+        return out[:n.value]
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.da2_plan_destroy(self.handle)
+            self.handle = None
+
+
+def to_device_bf16(x_u16, device="cuda") -> torch.Tensor:
+    """uint16 bfloat16 bits (numpy) -> bfloat16 device tensor, same shape."""
+    import numpy as np
+
+    t = torch.from_numpy(np.ascontiguousarray(x_u16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
