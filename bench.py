@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Benchmark of the DraftAttention2 hot path on one MI355X.
+
+One step = the whole hot path on one layer of synthetic video-DiT
+activations: da2_plan (Q/K preparation, draft scoring, ranking, schedule)
+followed by da2_attention (V preparation, phased FP8/MXFP4 attention with the
+output written back in token order).  Inputs are resident in HBM before the
+timed region; Q/K/V use the [B, N, H, d] storage of DiT attention layers.
+
+Prints one JSON line.  value = dense-equivalent attention TFLOP/s of the
+complete step (4 B H N^2 d per step); roofline = the attention kernel against
+the tier-weighted MFMA peak (its achieved executed FLOP/s over
+(F8 + F4) / (F8/P8 + F4/P4)); cpu_baseline = the CPU oracle timed on a
+bounded sample and extrapolated to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense FP8 MFMA
+PEAK_FP4 = 10100.0   # TFLOP/s, MI355X dense FP4 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b-720p")
+    ap.add_argument("--budget", type=int, default=0, help="index into the workload's budget list")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, hi, lo):
+    """Time the oracle (as it stands) on one head: full plan, then tiered
+    attention on 1 and on 3 query regions (the difference isolates the
+    per-region cost from the per-head operand quantization); extrapolate to
+    all regions and heads."""
+    from oracle import oracle as O
+
+    qs, ks, vs = q[:1, :1].copy(), k[:1, :1].copy(), v[:1, :1].copy()
+    t0 = time.perf_counter()
+    pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam)
+    t_plan = time.perf_counter() - t0
+    R = w.R
+    sel1 = np.array([R // 2], np.int32)
+    sel3 = np.array([R // 4, R // 2, (3 * R) // 4], np.int32)
+    t0 = time.perf_counter()
+    O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=sel1)
+    t1 = time.perf_counter()
+    O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=sel3)
+    t3 = time.perf_counter() - t1
+    t1 = t1 - t0
+    per_region = max((t3 - t1) / 2.0, 1e-9)
+    per_head_fixed = max(t1 - per_region, 0.0)
+    t_head = t_plan + per_head_fixed + per_region * R
+    total = t_head * w.B * w.H
+    dense_flop = 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {
+        "value": dense_flop / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("1 of %d heads: full plan (%.2f s) + tiered attention on 1 and 3 query "
+                   "regions (%.2f s, %.2f s), extrapolated to %d regions x %d heads = %.0f s"
+                   % (w.B * w.H, t_plan, t1, t3, R, w.B * w.H, total)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this operator shards over (batch, head) with no "
+              "exchange, so a multi-GPU run is not part of this benchmark (got --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from video_diffusion_dit_frame_amd import configs, da2, synth
+
+    w = configs.WORKLOADS[args.workload]
+    hi, lo = w.budgets[args.budget]
+    dev = torch.device("cuda:0")
+    print("[bench] generating %s inputs (B=%d H=%d N=%d d=%d)" % (w.name, w.B, w.H, w.N, w.d),
+          file=sys.stderr, flush=True)
+    q, k, v = synth.make_qkv(w.B, w.H, w.F, w.Hv, w.Wv, w.d, w.seed, w.outliers)
+
+    def to_bnhd(x):
+        t = da2.to_device_bf16(x)                 # [B, H, N, d]
+        t = t.permute(0, 2, 1, 3).contiguous()    # [B, N, H, d] storage
+        return t.permute(0, 2, 1, 3)              # [B, H, N, d] view
+
+    qd, kd, vd = to_bnhd(q), to_bnhd(k), to_bnhd(v)
+    o = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+    L = da2.Layout.for_tensor(qd, w.F, w.Hv, w.Wv)
+    P = da2.Plan(L)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        P.plan(qd, kd, hi, lo, w.lam, 0, stream)
+        P.attention(qd, kd, vd, o, stream)
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    P.timing(True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        P.plan(qd, kd, hi, lo, w.lam, 0, stream)
+        ev[i][1].record(stream)
+        P.attention(qd, kd, vd, o, stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    plan_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    attn_call_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    kt = P.timing_read()
+    attn_kernel_ms = float(np.mean(kt)) if len(kt) else float("nan")
+    P.timing(False)
+    print("[bench] timed %d steps: %.3f ms/step (plan %.3f, attention call %.3f, kernel %.3f)"
+          % (args.steps, ms_step, plan_ms, attn_call_ms, attn_kernel_ms), file=sys.stderr, flush=True)
+
+    # work accounting (head-scope quotas, identical for every (b, h))
+    R = w.R
+    t8, tk = da2.quotas(R * R, hi, lo)
+    t4 = tk - t8
+    tile_flop = 4.0 * 64 * 64 * w.d
+    f8 = w.B * w.H * t8 * tile_flop
+    f4 = w.B * w.H * t4 * tile_flop
+    dense_flop = 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
+    t_attn = attn_kernel_ms * 1e-3
+    peak_eff = (f8 + f4) / (f8 / PEAK_FP8 + f4 / PEAK_FP4) if (f8 + f4) > 0 else PEAK_FP8
+    achieved = (f8 + f4) / t_attn / 1e12
+    util = (f8 / PEAK_FP8 + f4 / PEAK_FP4) / 1e12 / t_attn
+
+    out = {
+        "metric": "dense-equiv attention TFLOP/s + tier-weighted MFMA util, Wan-14B-720p layer",
+        "value": dense_flop / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3+mxfp4 (attention), f64 (draft scoring)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.d,
+                   "frames": w.F, "height": w.Hv, "width": w.Wv, "tokens": w.N, "regions": R,
+                   "budget_bp": {"fp8": hi, "mxfp4": lo}, "lambda": w.lam, "ranking": "head",
+                   "storage": "[B,N,H,d] bf16", "output": "bf16"},
+        "plan_ms": plan_ms,
+        "attention_call_ms": attn_call_ms,
+        "attention_kernel_ms": attn_kernel_ms,
+        "dense_equiv_tflops_attention_kernel": dense_flop / t_attn / 1e12,
+        "tier_weighted_mfma_util": util,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_eff, "unit": "TFLOP/s",
+                     "frac": achieved / peak_eff, "traffic": None,
+                     "kernel": "k_attn", "peak_basis": "tier-weighted FP8 5.0 / FP4 10.1 PFLOP/s"},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, hi, lo)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
