@@ -38,9 +38,9 @@ def run_plan(q, k, F, Hv, Wv, hi, lo, lam=0.2, scope=0, layout_bnhd=False):
     return P, qd, kd
 
 
-def run_attention(P, qd, kd, v, out_dtype=torch.float32):
+def run_attention(P, qd, kd, v, out_dtype=torch.float32, layout_bnhd=False):
     vd = dev(v)
-    if qd.stride(1) != qd.shape[2] * qd.shape[3]:  # [B,N,H,d] storage
+    if layout_bnhd:  # [B,N,H,d] storage
         vd = vd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
         B, H, N, d = vd.shape
         o = torch.empty((B, N, H, d), dtype=out_dtype, device="cuda").permute(0, 2, 1, 3)

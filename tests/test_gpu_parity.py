@@ -160,12 +160,12 @@ def test_attention_tier_families(which):
 
 def test_strided_layout_matches_contiguous():
     """[B, N, H, d] storage (the usual DiT layout) gives identical results."""
-    c = _case(RAGGED)
+    c = _case(MEDIUM)
     F, Hv, Wv = c["F"], c["Hv"], c["Wv"]
     P1, q1, k1 = G.run_plan(c["q"], c["k"], F, Hv, Wv, c["hi"], c["lo"])
     o1 = G.run_attention(P1, q1, k1, c["v"]).cpu().numpy()
     P2, q2, k2 = G.run_plan(c["q"], c["k"], F, Hv, Wv, c["hi"], c["lo"], layout_bnhd=True)
-    o2 = G.run_attention(P2, q2, k2, c["v"])
+    o2 = G.run_attention(P2, q2, k2, c["v"], layout_bnhd=True)
     assert o2.stride(1) == o2.shape[3]
     assert np.array_equal(P1.tier_map().cpu().numpy(), P2.tier_map().cpu().numpy())
     assert np.array_equal(o1, o2.cpu().numpy())

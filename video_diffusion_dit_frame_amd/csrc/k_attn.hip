@@ -31,8 +31,6 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 struct AttnArgs {
     const uint8_t *q8, *q4, *q4s;
     const float *qs8;
@@ -45,7 +43,7 @@ struct AttnArgs {
     void *out;
     int64_t osb, osh, osn;
     int out_f32;
-    int H, R, Ry, Rx, Hv, Wv;
+    int H, R, Ry, Rx, Hv, Wv, BH;
     float c4;  // log2(e) / sqrt(d)
 };
 
@@ -80,14 +78,84 @@ __device__ __forceinline__ v8i load16(const uint8_t *p)
     return r;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ v8i lds32(const uint8_t *p)
+{
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    uint4 a = q[0], b = q[1];
+    v8i r;
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    return r;
+}
+
+__device__ __forceinline__ v8i lds16(const uint8_t *p)
+{
+    uint4 a = *reinterpret_cast<const uint4 *>(p);
+    v8i r;
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
+// Copy `units` kilobytes from global src to LDS dst with direct-to-LDS loads;
+// wave w of the two copies units w, w+2, ...  Each unit is one instruction:
+// 64 lanes x 16 bytes landing at dst + lane * 16.
+__device__ __forceinline__ void copy_kb(const uint8_t *src, uint8_t *dst, int units, int w, int l)
+{
+    for (int u = w; u < units; u += 2)
+        __builtin_amdgcn_global_load_lds((const void *)(src + u * 1024 + l * 16),
+                                         (lds_void *)(dst + u * 1024), 16, 0, 0);
+}
+
+// Copy 4 bytes per active lane with one direct-to-LDS load (lane l -> dst + 4 l).
+__device__ __forceinline__ void copy_dword(const uint8_t *src, uint8_t *dst, int l)
+{
+    __builtin_amdgcn_global_load_lds((const void *)(src + l * 4), (lds_void *)dst, 4, 0, 0);
+}
+
+// LDS image of one kept tile.  FP8: K codes [0, 64D), V codes [64D, 128D).
+// MXFP4: K [0, 32D), V [32D, 64D), K exponents [64D, 66D), V [66D, 68D).
 template <int D>
-__global__ __launch_bounds__(128) void k_attn(const AttnArgs A)
+__device__ __forceinline__ void issue_tile(const AttnArgs &A, int64_t kblk, bool fp8, uint8_t *dst,
+                                           int w, int l)
+{
+    if (fp8) {
+        copy_kb(A.k8 + kblk * (kBlk * D), dst, kBlk * D / 1024, w, l);
+        copy_kb(A.v8 + kblk * (kBlk * D), dst + kBlk * D, kBlk * D / 1024, w, l);
+    } else {
+        copy_kb(A.k4 + kblk * (kBlk * D / 2), dst, kBlk * D / 2048, w, l);
+        copy_kb(A.v4 + kblk * (kBlk * D / 2), dst + 32 * D, kBlk * D / 2048, w, l);
+        // 2D bytes of exponents per operand (4 per lane): wave 0 copies K's, wave 1 V's
+        if (l * 4 < 2 * D) {
+            if (w == 0)
+                copy_dword(A.k4s + kblk * (2 * D), dst + 64 * D, l);
+            else
+                copy_dword(A.v4s + kblk * (2 * D), dst + 66 * D, l);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 {
     constexpr int KC = D / 64;   // 64-channel steps of QK^T
     constexpr int CB = D / 32;   // 32-channel blocks of the output
-    const int a = blockIdx.x, bh = blockIdx.y;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hf = l >> 5;
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2 * kBlk * D];
+
+    // XCD-aware work mapping: workgroups are dealt to the 8 XCDs round robin,
+    // so give XCD x the contiguous range of (b, h, query region) items
+    // [x * per, (x + 1) * per): one XCD works through a few heads at a time
+    // and its L2 keeps their key/value tiles.
     const int R = A.R;
+    const int total = A.BH * R;
+    const int per = (total + 7) / 8;
+    const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (item >= total)
+        return;
+    const int bh = item / R, a = item - bh * R;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hf = l >> 5;
     const int64_t qblk = (int64_t)bh * R + a;
 
     // queries of this wave, both formats
@@ -102,7 +170,9 @@ __global__ __launch_bounds__(128) void k_attn(const AttnArgs A)
     }
     const float qs = A.qs8[qblk];
     const int n8 = A.cnt[qblk * 2], n4 = A.cnt[qblk * 2 + 1];
+    const int n = n8 + n4;
     const uint16_t *list = A.sched + qblk * R;
+    const int64_t hbase = (int64_t)bh * R;
 
     v16f acc[CB];
 #pragma unroll
@@ -111,58 +181,146 @@ __global__ __launch_bounds__(128) void k_attn(const AttnArgs A)
     float m = -__builtin_huge_valf();
     float z = 0.0f;
 
-    // ---------------- FP8 phase ----------------
-    for (int it = 0; it < n8; it++) {
-        const int kb = list[it];
-        const int64_t kblk = (int64_t)bh * R + kb;
-        const uint8_t *kp = A.k8 + kblk * (kBlk * D);
-        v16f s[2];
-#pragma unroll
-        for (int mm = 0; mm < 2; mm++) {
-            s[mm] = (v16f){};
-#pragma unroll
-            for (int kc = 0; kc < KC; kc++)
-                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    load32(kp + ((mm * KC + kc) * 64 + l) * 32), q8[kc], s[mm], 0, 0, 0, 0, 0, 0);
+    int kb_next = n > 0 ? list[0] : 0;
+    if (n > 0)
+        issue_tile<D>(A, hbase + kb_next, n8 > 0, tiles[0], w, l);
+
+    for (int it = 0; it < n; it++) {
+        const int kb = kb_next;
+        // tile `it` has landed in LDS for every wave; the other buffer is free
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (it + 1 < n) {
+            kb_next = list[it + 1];
+            issue_tile<D>(A, hbase + kb_next, it + 1 < n8, tiles[(it + 1) & 1], w, l);
         }
-        const float c8 = (qs * A.ks8[kblk]) * A.c4;
-        float mx = s[0][0];
-#pragma unroll
-        for (int r = 0; r < 16; r++)
-            mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-        mx = pair_max(mx);
-        const float mnew = fmaxf(m, mx * c8);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        if (__any(alpha != 1.0f)) {
-            z *= alpha;
+        const uint8_t *tb = tiles[it & 1];
+        if (it == n8 && n8 > 0) {
+            // phase boundary: FP8 value units -> real units (per-channel V scale)
+            const float *vs = A.vs8 + (int64_t)bh * D;
 #pragma unroll
             for (int cb = 0; cb < CB; cb++)
-                acc[cb] *= alpha;
-        }
-        m = mnew;
-        const float bias = 8.0f - mnew;
-        v8i p;
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            const int mm = q >> 2, r0 = 4 * (q & 3);
-            float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
-            float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
-            float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
-            float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
-            z += (e0 + e1) + (e2 + e3);
-            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-            wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
-            p[q] = wd;
+                for (int r = 0; r < 16; r++)
+                    acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
         }
-        const uint8_t *vp = A.v8 + kblk * (kBlk * D);
+        v16f s[2];
+        if (it < n8) {
+            // ---------------- FP8 tile ----------------
 #pragma unroll
-        for (int cb = 0; cb < CB; cb++)
-            acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                load32(vp + (cb * 64 + l) * 32), p, acc[cb], 0, 0, 0, 0, 0, 0);
+            for (int mm = 0; mm < 2; mm++) {
+                s[mm] = (v16f){};
+#pragma unroll
+                for (int kc = 0; kc < KC; kc++)
+                    s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        lds32(tb + ((mm * KC + kc) * 64 + l) * 32), q8[kc], s[mm], 0, 0, 0, 0, 0, 0);
+            }
+            const float c8 = (qs * A.ks8[hbase + kb]) * A.c4;
+            float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+            for (int r = 1; r < 16; r++)
+                mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+            mx = pair_max(mx);
+            const float mnew = fmaxf(m, mx * c8);
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+            if (__any(alpha != 1.0f)) {
+                z *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CB; cb++)
+                    acc[cb] *= alpha;
+            }
+            m = mnew;
+            const float bias = 8.0f - mnew;
+            v8i p;
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                const int mm = q >> 2, r0 = 4 * (q & 3);
+                float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
+                float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
+                float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
+                float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
+                z += (e0 + e1) + (e2 + e3);
+                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+                wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
+                p[q] = wd;
+            }
+            const uint8_t *vp = tb + kBlk * D;
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    lds32(vp + (cb * 64 + l) * 32), p, acc[cb], 0, 0, 0, 0, 0, 0);
+        } else {
+            // ---------------- MXFP4 tile ----------------
+#pragma unroll
+            for (int mm = 0; mm < 2; mm++) {
+                s[mm] = (v16f){};
+#pragma unroll
+                for (int kc = 0; kc < KC; kc++) {
+                    const int chunk = (mm * KC + kc) * 64 + l;
+                    s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        lds16(tb + chunk * 16), q4[kc], s[mm], 4, 4, 0, (int)tb[64 * D + chunk], 0,
+                        q4s[kc]);
+                }
+            }
+            const float c = A.c4;
+            float gm = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+            for (int r = 1; r < 16; r++)
+                gm = fmaxf(gm, fmaxf(s[0][r], s[1][r]));
+            const float mx = pair_max(gm);
+            const float tm = mx * c;
+            const float mnew = fmaxf(m, tm);
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+            if (__any(alpha != 1.0f)) {
+                z *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CB; cb++)
+                    acc[cb] *= alpha;
+            }
+            m = mnew;
+            const float bias = 8.0f - mnew;
+            // E8M0 exponent of this lane's 32-key group: floor(log2(max e)) - 2.
+            // The group holding the running maximum has max e = 2^8 exactly
+            // (w = 1), so its exponent is fixed at 6 instead of being read
+            // from a rounded exp2 that may land just below the power of two.
+            int ef;
+            if (gm == mx && mnew == tm) {
+                ef = 127 + 6;
+            } else {
+                const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
+                ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
+                ef = ef < 0 ? 0 : ef;
+            }
+            const float pscale = ef ? __uint_as_float((uint32_t)ef << 23) : __uint_as_float(0x00400000u);
+            v8i p;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                // slots 8q .. 8q+7 of this lane's group; slot = 16*mm + r
+                const int mm = q >> 1, r0 = 8 * (q & 1);
+                float e[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
+                    z += e[j];
+                }
+                uint32_t wd = 0;
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[0], e[1], pscale, 0);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
+                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
+                p[q] = (int)wd;
+            }
+            p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++) {
+                const int chunk = cb * 64 + l;
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    lds16(tb + 32 * D + chunk * 16), p, acc[cb], 4, 4, 0, (int)tb[66 * D + chunk], 0, ef);
+            }
+        }
     }
-
-    // ---------------- phase boundary: FP8 value units -> real units ----------------
-    if (n8 > 0) {
+    if (n4 == 0 && n8 > 0) {
+        // phase boundary after the last FP8 tile when no MXFP4 tile follows
         const float *vs = A.vs8 + (int64_t)bh * D;
 #pragma unroll
         for (int cb = 0; cb < CB; cb++)
@@ -171,89 +329,13 @@ __global__ __launch_bounds__(128) void k_attn(const AttnArgs A)
                 acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
     }
 
-    // ---------------- MXFP4 phase ----------------
-    for (int it = n8; it < n8 + n4; it++) {
-        const int kb = list[it];
-        const int64_t kblk = (int64_t)bh * R + kb;
-        const uint8_t *kp = A.k4 + kblk * (kBlk * D / 2);
-        const uint8_t *ksp = A.k4s + kblk * (2 * D);
-        v16f s[2];
-#pragma unroll
-        for (int mm = 0; mm < 2; mm++) {
-            s[mm] = (v16f){};
-#pragma unroll
-            for (int kc = 0; kc < KC; kc++) {
-                const int chunk = (mm * KC + kc) * 64 + l;
-                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    load16(kp + chunk * 16), q4[kc], s[mm], 4, 4, 0, (int)ksp[chunk], 0, q4s[kc]);
-            }
-        }
-        const float c = A.c4;
-        float gm = s[0][0];
-#pragma unroll
-        for (int r = 0; r < 16; r++)
-            gm = fmaxf(gm, fmaxf(s[0][r], s[1][r]));
-        const float mx = pair_max(gm);
-        const float tm = mx * c;
-        const float mnew = fmaxf(m, tm);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        if (__any(alpha != 1.0f)) {
-            z *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-                acc[cb] *= alpha;
-        }
-        m = mnew;
-        const float bias = 8.0f - mnew;
-        // E8M0 exponent of this lane's 32-key group: floor(log2(max e)) - 2.
-        // The group holding the running maximum has max e = 2^8 exactly
-        // (w = 1), so its exponent is fixed at 6 instead of being read from a
-        // rounded exp2 that may land just below the power of two.
-        int ef;
-        if (gm == mx && mnew == tm) {
-            ef = 127 + 6;
-        } else {
-            const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
-            ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
-            ef = ef < 0 ? 0 : ef;
-        }
-        const float pscale = ef ? __uint_as_float((uint32_t)ef << 23) : __uint_as_float(0x00400000u);
-        v8i p;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            // slots 8q .. 8q+7 of this lane's group; slot = 16*mm + r
-            const int mm = q >> 1, r0 = 8 * (q & 1);
-            float e[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
-                z += e[j];
-            }
-            uint32_t wd = 0;
-            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[0], e[1], pscale, 0);
-            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
-            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
-            wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
-            p[q] = (int)wd;
-        }
-        p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
-        const uint8_t *vp = A.v4 + kblk * (kBlk * D / 2);
-        const uint8_t *vsp = A.v4s + kblk * (2 * D);
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++) {
-            const int chunk = cb * 64 + l;
-            acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                load16(vp + chunk * 16), p, acc[cb], 4, 4, 0, (int)vsp[chunk], 0, ef);
-        }
-    }
-
     // ---------------- epilogue: normalize and restore token order ----------------
     const float zt = pair_sum(z);
     const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
     const int i = 32 * w + (l & 31);
-    const int n = region_token(a, i, A.Ry, A.Rx, A.Hv, A.Wv);
+    const int tok = region_token(a, i, A.Ry, A.Rx, A.Hv, A.Wv);
     const int b = bh / A.H, h = bh - b * A.H;
-    const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)n * A.osn;
+    const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)tok * A.osn;
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
 #pragma unroll
@@ -303,8 +385,10 @@ void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hip
     A.Rx = L.Rx;
     A.Hv = L.s.height;
     A.Wv = L.s.width;
+    A.BH = L.BH;
     A.c4 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
-    dim3 grid(L.R, L.BH);
+    const int total = L.BH * L.R;
+    dim3 grid(8 * ((total + 7) / 8));
     if (L.d == 128)
         k_attn<128><<<grid, 128, 0, st>>>(A);
     else
