@@ -67,7 +67,7 @@ void carve(da2_layout_s &L)
     W.lm = take(BH * R * R * 8);
     W.keys = take(BH * R * R * 4);
     W.tier = take(BH * R * R);
-    W.sched = take(BH * R * R * 2);
+    W.sched = take(BH * R * R * 4);
     W.cnt = take(BH * R * 2 * 4);
     W.rank_state = take(BH * 2 * sizeof(RankState));
     W.rank_hist = take(BH * 2 * 256 * 4);

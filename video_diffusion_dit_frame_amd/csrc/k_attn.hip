@@ -38,7 +38,7 @@ struct AttnArgs {
     const float *ks8;
     const uint8_t *v8, *v4, *v4s;
     const float *vs8;
-    const uint16_t *sched;
+    const int32_t *sched;
     const int32_t *cnt;
     void *out;
     int64_t osb, osh, osn;
@@ -79,6 +79,19 @@ __device__ __forceinline__ v8i load16(const uint8_t *p)
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Loads from wave-uniform addresses through the constant address space, so
+// they become scalar loads that do not share the vector-memory counter the
+// tile prefetch waits on.
+__device__ __forceinline__ int sload_i32(const int32_t *p)
+{
+    return *(const __attribute__((address_space(4))) int32_t *)p;
+}
+
+__device__ __forceinline__ float sload_f32(const float *p)
+{
+    return *(const __attribute__((address_space(4))) float *)p;
+}
 
 __device__ __forceinline__ v8i lds32(const uint8_t *p)
 {
@@ -137,6 +150,131 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &A, int64_t kblk, bool
     }
 }
 
+// Rescale of the running statistics when a tile raises a row maximum;
+// skipped when no lane's maximum moved (the factor would be exactly 1).
+template <int CB>
+__device__ __forceinline__ void rescale(v16f (&acc)[CB], float &z, float alpha)
+{
+    if (__any(alpha != 1.0f)) {
+        z *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+            acc[cb] *= alpha;
+    }
+}
+
+// One FP8 tile from its LDS image.
+template <int D>
+__device__ __forceinline__ void tile_fp8(const uint8_t *tb, const v8i (&q8)[D / 64], float c8, int l,
+                                         v16f (&acc)[D / 32], float &m, float &z)
+{
+    constexpr int KC = D / 64, CB = D / 32;
+    v16f s[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; mm++) {
+        s[mm] = (v16f){};
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++)
+            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                lds32(tb + ((mm * KC + kc) * 64 + l) * 32), q8[kc], s[mm], 0, 0, 0, 0, 0, 0);
+    }
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; r++)
+        mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    mx = pair_max(mx);
+    const float mnew = fmaxf(m, mx * c8);
+    rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
+    m = mnew;
+    const float bias = 8.0f - mnew;
+    v8i p;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const int mm = q >> 2, r0 = 4 * (q & 3);
+        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
+        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
+        float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
+        float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
+        z += (e0 + e1) + (e2 + e3);
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
+        p[q] = wd;
+    }
+    const uint8_t *vp = tb + kBlk * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            lds32(vp + (cb * 64 + l) * 32), p, acc[cb], 0, 0, 0, 0, 0, 0);
+}
+
+// One MXFP4 tile from its LDS image.
+template <int D>
+__device__ __forceinline__ void tile_fp4(const uint8_t *tb, const v8i (&q4)[D / 64],
+                                         const int (&q4s)[D / 64], float c, int l,
+                                         v16f (&acc)[D / 32], float &m, float &z)
+{
+    constexpr int KC = D / 64, CB = D / 32;
+    v16f s[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; mm++) {
+        s[mm] = (v16f){};
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            const int chunk = (mm * KC + kc) * 64 + l;
+            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                lds16(tb + chunk * 16), q4[kc], s[mm], 4, 4, 0, (int)tb[64 * D + chunk], 0, q4s[kc]);
+        }
+    }
+    float gm = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; r++)
+        gm = fmaxf(gm, fmaxf(s[0][r], s[1][r]));
+    const float mx = pair_max(gm);
+    const float tm = mx * c;
+    const float mnew = fmaxf(m, tm);
+    rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
+    m = mnew;
+    const float bias = 8.0f - mnew;
+    // E8M0 exponent of this lane's 32-key group: floor(log2(max e)) - 2.  The
+    // group holding the running maximum has max e = 2^8 exactly (w = 1), so
+    // its exponent is fixed at 6 instead of being read from a rounded exp2
+    // that may land just below the power of two.
+    int ef;
+    if (gm == mx && mnew == tm) {
+        ef = 127 + 6;
+    } else {
+        const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
+        ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
+        ef = ef < 0 ? 0 : ef;
+    }
+    const float pscale = ef ? __uint_as_float((uint32_t)ef << 23) : __uint_as_float(0x00400000u);
+    v8i p;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        // slots 8q .. 8q+7 of this lane's group; slot = 16*mm + r
+        const int mm = q >> 1, r0 = 8 * (q & 1);
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
+            z += e[j];
+        }
+        uint32_t wd = 0;
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[0], e[1], pscale, 0);
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
+        p[q] = (int)wd;
+    }
+    p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+        const int chunk = cb * 64 + l;
+        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            lds16(tb + 32 * D + chunk * 16), p, acc[cb], 4, 4, 0, (int)tb[66 * D + chunk], 0, ef);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 {
@@ -171,7 +309,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     const float qs = A.qs8[qblk];
     const int n8 = A.cnt[qblk * 2], n4 = A.cnt[qblk * 2 + 1];
     const int n = n8 + n4;
-    const uint16_t *list = A.sched + qblk * R;
+    const int32_t *list = A.sched + qblk * R;
     const int64_t hbase = (int64_t)bh * R;
 
     v16f acc[CB];
@@ -181,152 +319,40 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     float m = -__builtin_huge_valf();
     float z = 0.0f;
 
-    int kb_next = n > 0 ? list[0] : 0;
+    // key regions are wave-uniform: keep them (and their FP8 scales) scalar
+    int kb_next = n > 0 ? sload_i32(list) : 0;
     if (n > 0)
         issue_tile<D>(A, hbase + kb_next, n8 > 0, tiles[0], w, l);
 
-    for (int it = 0; it < n; it++) {
+    int it = 0;
+    for (; it < n8; it++) {
         const int kb = kb_next;
-        // tile `it` has landed in LDS for every wave; the other buffer is free
+        const float c8 = (qs * sload_f32(A.ks8 + hbase + kb)) * A.c4;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (it + 1 < n) {
-            kb_next = list[it + 1];
+            kb_next = sload_i32(list + it + 1);
             issue_tile<D>(A, hbase + kb_next, it + 1 < n8, tiles[(it + 1) & 1], w, l);
         }
-        const uint8_t *tb = tiles[it & 1];
-        if (it == n8 && n8 > 0) {
-            // phase boundary: FP8 value units -> real units (per-channel V scale)
-            const float *vs = A.vs8 + (int64_t)bh * D;
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
-        }
-        v16f s[2];
-        if (it < n8) {
-            // ---------------- FP8 tile ----------------
-#pragma unroll
-            for (int mm = 0; mm < 2; mm++) {
-                s[mm] = (v16f){};
-#pragma unroll
-                for (int kc = 0; kc < KC; kc++)
-                    s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        lds32(tb + ((mm * KC + kc) * 64 + l) * 32), q8[kc], s[mm], 0, 0, 0, 0, 0, 0);
-            }
-            const float c8 = (qs * A.ks8[hbase + kb]) * A.c4;
-            float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-            for (int r = 1; r < 16; r++)
-                mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-            mx = pair_max(mx);
-            const float mnew = fmaxf(m, mx * c8);
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            if (__any(alpha != 1.0f)) {
-                z *= alpha;
-#pragma unroll
-                for (int cb = 0; cb < CB; cb++)
-                    acc[cb] *= alpha;
-            }
-            m = mnew;
-            const float bias = 8.0f - mnew;
-            v8i p;
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                const int mm = q >> 2, r0 = 4 * (q & 3);
-                float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
-                float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
-                float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
-                float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
-                z += (e0 + e1) + (e2 + e3);
-                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-                wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
-                p[q] = wd;
-            }
-            const uint8_t *vp = tb + kBlk * D;
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    lds32(vp + (cb * 64 + l) * 32), p, acc[cb], 0, 0, 0, 0, 0, 0);
-        } else {
-            // ---------------- MXFP4 tile ----------------
-#pragma unroll
-            for (int mm = 0; mm < 2; mm++) {
-                s[mm] = (v16f){};
-#pragma unroll
-                for (int kc = 0; kc < KC; kc++) {
-                    const int chunk = (mm * KC + kc) * 64 + l;
-                    s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        lds16(tb + chunk * 16), q4[kc], s[mm], 4, 4, 0, (int)tb[64 * D + chunk], 0,
-                        q4s[kc]);
-                }
-            }
-            const float c = A.c4;
-            float gm = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-            for (int r = 1; r < 16; r++)
-                gm = fmaxf(gm, fmaxf(s[0][r], s[1][r]));
-            const float mx = pair_max(gm);
-            const float tm = mx * c;
-            const float mnew = fmaxf(m, tm);
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            if (__any(alpha != 1.0f)) {
-                z *= alpha;
-#pragma unroll
-                for (int cb = 0; cb < CB; cb++)
-                    acc[cb] *= alpha;
-            }
-            m = mnew;
-            const float bias = 8.0f - mnew;
-            // E8M0 exponent of this lane's 32-key group: floor(log2(max e)) - 2.
-            // The group holding the running maximum has max e = 2^8 exactly
-            // (w = 1), so its exponent is fixed at 6 instead of being read
-            // from a rounded exp2 that may land just below the power of two.
-            int ef;
-            if (gm == mx && mnew == tm) {
-                ef = 127 + 6;
-            } else {
-                const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
-                ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
-                ef = ef < 0 ? 0 : ef;
-            }
-            const float pscale = ef ? __uint_as_float((uint32_t)ef << 23) : __uint_as_float(0x00400000u);
-            v8i p;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                // slots 8q .. 8q+7 of this lane's group; slot = 16*mm + r
-                const int mm = q >> 1, r0 = 8 * (q & 1);
-                float e[8];
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
-                    z += e[j];
-                }
-                uint32_t wd = 0;
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[0], e[1], pscale, 0);
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
-                wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
-                p[q] = (int)wd;
-            }
-            p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++) {
-                const int chunk = cb * 64 + l;
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    lds16(tb + 32 * D + chunk * 16), p, acc[cb], 4, 4, 0, (int)tb[66 * D + chunk], 0, ef);
-            }
-        }
+        tile_fp8<D>(tiles[it & 1], q8, c8, l, acc, m, z);
     }
-    if (n4 == 0 && n8 > 0) {
-        // phase boundary after the last FP8 tile when no MXFP4 tile follows
+    if (n8 > 0) {
+        // phase boundary: FP8 value units -> real units (per-channel V scale)
         const float *vs = A.vs8 + (int64_t)bh * D;
 #pragma unroll
         for (int cb = 0; cb < CB; cb++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+    }
+    for (; it < n; it++) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (it + 1 < n) {
+            kb_next = sload_i32(list + it + 1);
+            issue_tile<D>(A, hbase + kb_next, false, tiles[(it + 1) & 1], w, l);
+        }
+        tile_fp4<D>(tiles[it & 1], q4, q4s, A.c4, l, acc, m, z);
     }
 
     // ---------------- epilogue: normalize and restore token order ----------------
@@ -372,7 +398,7 @@ void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hip
     A.v4 = (const uint8_t *)(ws + W.v4);
     A.v4s = (const uint8_t *)(ws + W.v4s);
     A.vs8 = (const float *)(ws + W.vs8);
-    A.sched = (const uint16_t *)(ws + W.sched);
+    A.sched = (const int32_t *)(ws + W.sched);
     A.cnt = (const int32_t *)(ws + W.cnt);
     A.out = o;
     A.osb = L.s.stride_b;

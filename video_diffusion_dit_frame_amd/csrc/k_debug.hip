@@ -86,7 +86,7 @@ __global__ void k_unpack_v(const uint8_t *op8, const uint8_t *op4, const uint8_t
     }
 }
 
-__global__ void k_unpack_sched(const uint16_t *sched, const int32_t *cnt, int R, int64_t rows,
+__global__ void k_unpack_sched(const int32_t *sched, const int32_t *cnt, int R, int64_t rows,
                                int32_t *dst)
 {
     int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -159,7 +159,7 @@ void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, h
     case DA2_DBG_SCHEDULE: {
         const int64_t rows = (int64_t)L.BH * L.R;
         k_unpack_sched<<<grid(rows * (L.R + 2)), 256, 0, st>>>(
-            (const uint16_t *)(ws + W.sched), (const int32_t *)(ws + W.cnt), L.R, rows, (int32_t *)dst);
+            (const int32_t *)(ws + W.sched), (const int32_t *)(ws + W.cnt), L.R, rows, (int32_t *)dst);
         break;
     }
     default:

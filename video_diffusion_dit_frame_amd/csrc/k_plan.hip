@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256) void k_rank_rows(const uint32_t *__restrict__ 
 // One wave per row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tier, int R,
-                                                 uint16_t *__restrict__ sched,
+                                                 int32_t *__restrict__ sched,
                                                  int32_t *__restrict__ cnt)
 {
     const int64_t row = (int64_t)blockIdx.y * R + blockIdx.x;
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
     }
     n8 = wave_sum_u32(n8);
     n4 = wave_sum_u32(n4);
-    uint16_t *out = sched + row * R;
+    int32_t *out = sched + row * R;
     uint32_t o8 = 0, o4 = n8;
     for (int b0 = 0; b0 < R; b0 += 64) {
         int b = b0 + l;
@@ -494,9 +494,9 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
         uint64_t m8 = __ballot(v == 8), m4 = __ballot(v == 4);
         uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
         if (v == 8)
-            out[o8 + __popcll(m8 & lt)] = (uint16_t)b;
+            out[o8 + __popcll(m8 & lt)] = b;
         if (v == 4)
-            out[o4 + __popcll(m4 & lt)] = (uint16_t)b;
+            out[o4 + __popcll(m4 & lt)] = b;
         o8 += __popcll(m8);
         o4 += __popcll(m4);
     }
@@ -564,7 +564,7 @@ void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
     k_schedule<<<dim3(L.R, L.BH), 64, 0, st>>>((const uint8_t *)(ws + W.tier), L.R,
-                                                (uint16_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
+                                                (int32_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
 }
 
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st)
