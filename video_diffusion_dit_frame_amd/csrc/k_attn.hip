@@ -112,14 +112,18 @@ __device__ __forceinline__ v8i lds16(const uint8_t *p)
     return r;
 }
 
-// Copy `units` kilobytes from global src to LDS dst with direct-to-LDS loads;
+// Copy UNITS kilobytes from global src to LDS dst with direct-to-LDS loads;
 // wave w of the two copies units w, w+2, ...  Each unit is one instruction:
 // 64 lanes x 16 bytes landing at dst + lane * 16.
-__device__ __forceinline__ void copy_kb(const uint8_t *src, uint8_t *dst, int units, int w, int l)
+template <int UNITS>
+__device__ __forceinline__ void copy_kb(const uint8_t *src, uint8_t *dst, int w, int l)
 {
-    for (int u = w; u < units; u += 2)
+#pragma unroll
+    for (int j = 0; j < UNITS / 2; j++) {
+        const int u = 2 * j + w;
         __builtin_amdgcn_global_load_lds((const void *)(src + u * 1024 + l * 16),
                                          (lds_void *)(dst + u * 1024), 16, 0, 0);
+    }
 }
 
 // Copy 4 bytes per active lane with one direct-to-LDS load (lane l -> dst + 4 l).
@@ -135,11 +139,11 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &A, int64_t kblk, bool
                                            int w, int l)
 {
     if (fp8) {
-        copy_kb(A.k8 + kblk * (kBlk * D), dst, kBlk * D / 1024, w, l);
-        copy_kb(A.v8 + kblk * (kBlk * D), dst + kBlk * D, kBlk * D / 1024, w, l);
+        copy_kb<kBlk * D / 1024>(A.k8 + kblk * (kBlk * D), dst, w, l);
+        copy_kb<kBlk * D / 1024>(A.v8 + kblk * (kBlk * D), dst + kBlk * D, w, l);
     } else {
-        copy_kb(A.k4 + kblk * (kBlk * D / 2), dst, kBlk * D / 2048, w, l);
-        copy_kb(A.v4 + kblk * (kBlk * D / 2), dst + 32 * D, kBlk * D / 2048, w, l);
+        copy_kb<kBlk * D / 2048>(A.k4 + kblk * (kBlk * D / 2), dst, w, l);
+        copy_kb<kBlk * D / 2048>(A.v4 + kblk * (kBlk * D / 2), dst + 32 * D, w, l);
         // 2D bytes of exponents per operand (4 per lane): wave 0 copies K's, wave 1 V's
         if (l * 4 < 2 * D) {
             if (w == 0)
@@ -163,9 +167,55 @@ __device__ __forceinline__ void rescale(v16f (&acc)[CB], float &z, float alpha)
     }
 }
 
-// One FP8 tile from its LDS image.
+// Operands of one tile, read from its LDS image into registers before the
+// next tile's prefetch is issued (the compiler orders every LDS read after a
+// pending direct-to-LDS load, so reading first keeps the prefetch in flight
+// across the whole computation).
 template <int D>
-__device__ __forceinline__ void tile_fp8(const uint8_t *tb, const v8i (&q8)[D / 64], float c8, int l,
+struct TileRegs {
+    v8i k[2][D / 64];   // key operand per (key half, 64-channel step)
+    v8i v[D / 32];      // value operand per 32-channel block
+    int ks[2][D / 64];  // MXFP4 key exponents
+    int vs[D / 32];     // MXFP4 value exponents
+};
+
+template <int D>
+__device__ __forceinline__ void read_fp8(const uint8_t *tb, int l, TileRegs<D> &T)
+{
+    constexpr int KC = D / 64, CB = D / 32;
+#pragma unroll
+    for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++)
+            T.k[mm][kc] = lds32(tb + ((mm * KC + kc) * 64 + l) * 32);
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++)
+        T.v[cb] = lds32(tb + kBlk * D + (cb * 64 + l) * 32);
+}
+
+template <int D>
+__device__ __forceinline__ void read_fp4(const uint8_t *tb, int l, TileRegs<D> &T)
+{
+    constexpr int KC = D / 64, CB = D / 32;
+#pragma unroll
+    for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            const int chunk = (mm * KC + kc) * 64 + l;
+            T.k[mm][kc] = lds16(tb + chunk * 16);
+            T.ks[mm][kc] = tb[64 * D + chunk];
+        }
+#pragma unroll
+    for (int cb = 0; cb < CB; cb++) {
+        const int chunk = cb * 64 + l;
+        T.v[cb] = lds16(tb + 32 * D + chunk * 16);
+        T.vs[cb] = tb[66 * D + chunk];
+    }
+}
+
+// One FP8 tile.
+template <int D>
+__device__ __forceinline__ void tile_fp8(const TileRegs<D> &T, const v8i (&q8)[D / 64], float c8,
                                          v16f (&acc)[D / 32], float &m, float &z)
 {
     constexpr int KC = D / 64, CB = D / 32;
@@ -175,8 +225,8 @@ __device__ __forceinline__ void tile_fp8(const uint8_t *tb, const v8i (&q8)[D / 
         s[mm] = (v16f){};
 #pragma unroll
         for (int kc = 0; kc < KC; kc++)
-            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                lds32(tb + ((mm * KC + kc) * 64 + l) * 32), q8[kc], s[mm], 0, 0, 0, 0, 0, 0);
+            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.k[mm][kc], q8[kc], s[mm], 0, 0,
+                                                                   0, 0, 0, 0);
     }
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
@@ -200,18 +250,17 @@ __device__ __forceinline__ void tile_fp8(const uint8_t *tb, const v8i (&q8)[D / 
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
         p[q] = wd;
     }
-    const uint8_t *vp = tb + kBlk * D;
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
-        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            lds32(vp + (cb * 64 + l) * 32), p, acc[cb], 0, 0, 0, 0, 0, 0);
+        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.v[cb], p, acc[cb], 0, 0, 0, 0, 0,
+                                                                 0);
 }
 
-// One MXFP4 tile from its LDS image.
+// One MXFP4 tile.
 template <int D>
-__device__ __forceinline__ void tile_fp4(const uint8_t *tb, const v8i (&q4)[D / 64],
-                                         const int (&q4s)[D / 64], float c, int l,
-                                         v16f (&acc)[D / 32], float &m, float &z)
+__device__ __forceinline__ void tile_fp4(const TileRegs<D> &T, const v8i (&q4)[D / 64],
+                                         const int (&q4s)[D / 64], float c, v16f (&acc)[D / 32],
+                                         float &m, float &z)
 {
     constexpr int KC = D / 64, CB = D / 32;
     v16f s[2];
@@ -219,11 +268,9 @@ __device__ __forceinline__ void tile_fp4(const uint8_t *tb, const v8i (&q4)[D / 
     for (int mm = 0; mm < 2; mm++) {
         s[mm] = (v16f){};
 #pragma unroll
-        for (int kc = 0; kc < KC; kc++) {
-            const int chunk = (mm * KC + kc) * 64 + l;
-            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                lds16(tb + chunk * 16), q4[kc], s[mm], 4, 4, 0, (int)tb[64 * D + chunk], 0, q4s[kc]);
-        }
+        for (int kc = 0; kc < KC; kc++)
+            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.k[mm][kc], q4[kc], s[mm], 4, 4,
+                                                                   0, T.ks[mm][kc], 0, q4s[kc]);
     }
     float gm = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
@@ -268,11 +315,9 @@ __device__ __forceinline__ void tile_fp4(const uint8_t *tb, const v8i (&q4)[D / 
     }
     p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
 #pragma unroll
-    for (int cb = 0; cb < CB; cb++) {
-        const int chunk = cb * 64 + l;
-        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            lds16(tb + 32 * D + chunk * 16), p, acc[cb], 4, 4, 0, (int)tb[66 * D + chunk], 0, ef);
-    }
+    for (int cb = 0; cb < CB; cb++)
+        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.v[cb], p, acc[cb], 4, 4, 0,
+                                                                 T.vs[cb], 0, ef);
 }
 
 template <int D>
@@ -282,18 +327,21 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     constexpr int CB = D / 32;   // 32-channel blocks of the output
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2 * kBlk * D];
 
-    // XCD-aware work mapping: workgroups are dealt to the 8 XCDs round robin,
-    // so give XCD x the contiguous range of (b, h, query region) items
-    // [x * per, (x + 1) * per): one XCD works through a few heads at a time
-    // and its L2 keeps their key/value tiles.
+    // XCD-aware work mapping.  Workgroups are dealt to the 8 XCDs round robin
+    // (block L runs on XCD L % 8).  Every XCD walks the heads in the same
+    // order and takes its own contiguous eighth of each head's query regions,
+    // so all XCDs work on the same head at a time: that head's key/value
+    // tiles (about 31 MB for a 720p Wan layer) stay in the shared last-level
+    // cache, and each XCD's L2 serves spatially neighbouring query regions,
+    // whose kept key regions overlap.
     const int R = A.R;
-    const int total = A.BH * R;
-    const int per = (total + 7) / 8;
-    const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-    if (item >= total)
+    const int span = (R + 7) / 8;
+    const int xcd = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
+    const int bh = k / span;
+    const int a = xcd * span + (k - bh * span);
+    if (a >= R)
         return;
-    const int bh = item / R, a = item - bh * R;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, hf = l >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, hf = l >> 5;
     const int64_t qblk = (int64_t)bh * R + a;
 
     // queries of this wave, both formats
@@ -330,11 +378,13 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
         const float c8 = (qs * sload_f32(A.ks8 + hbase + kb)) * A.c4;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        TileRegs<D> T;
+        read_fp8<D>(tiles[it & 1], l, T);
         if (it + 1 < n) {
             kb_next = sload_i32(list + it + 1);
             issue_tile<D>(A, hbase + kb_next, it + 1 < n8, tiles[(it + 1) & 1], w, l);
         }
-        tile_fp8<D>(tiles[it & 1], q8, c8, l, acc, m, z);
+        tile_fp8<D>(T, q8, c8, acc, m, z);
     }
     if (n8 > 0) {
         // phase boundary: FP8 value units -> real units (per-channel V scale)
@@ -348,11 +398,13 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     for (; it < n; it++) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        TileRegs<D> T;
+        read_fp4<D>(tiles[it & 1], l, T);
         if (it + 1 < n) {
             kb_next = sload_i32(list + it + 1);
             issue_tile<D>(A, hbase + kb_next, false, tiles[(it + 1) & 1], w, l);
         }
-        tile_fp4<D>(tiles[it & 1], q4, q4s, A.c4, l, acc, m, z);
+        tile_fp4<D>(T, q4, q4s, A.c4, acc, m, z);
     }
 
     // ---------------- epilogue: normalize and restore token order ----------------
@@ -413,8 +465,7 @@ void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hip
     A.Wv = L.s.width;
     A.BH = L.BH;
     A.c4 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
-    const int total = L.BH * L.R;
-    dim3 grid(8 * ((total + 7) / 8));
+    dim3 grid(8 * ((L.R + 7) / 8) * L.BH);
     if (L.d == 128)
         k_attn<128><<<grid, 128, 0, st>>>(A);
     else
