@@ -42,10 +42,10 @@ def parse():
 
 
 def cpu_baseline(w, q, k, v, hi, lo):
-    """Time the oracle (as it stands) on one head: full plan, then tiered
-    attention on 1 and on 3 query regions (the difference isolates the
-    per-region cost from the per-head operand quantization); extrapolate to
-    all regions and heads."""
+    """Time the oracle (as it stands) on one head: the full plan, then tiered
+    attention on 1 query region and on 33 evenly spaced ones.  The per-head
+    fixed part (operand quantization) and the per-region part follow from the
+    two timings; the head total is extrapolated to all regions and heads."""
     from oracle import oracle as O
 
     qs, ks, vs = q[:1, :1].copy(), k[:1, :1].copy(), v[:1, :1].copy()
@@ -53,15 +53,16 @@ def cpu_baseline(w, q, k, v, hi, lo):
     pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam)
     t_plan = time.perf_counter() - t0
     R = w.R
+    n_many = 33
     sel1 = np.array([R // 2], np.int32)
-    sel3 = np.array([R // 4, R // 2, (3 * R) // 4], np.int32)
+    selm = np.array([(j * R) // n_many for j in range(n_many)], np.int32)
     t0 = time.perf_counter()
     O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=sel1)
-    t1 = time.perf_counter()
-    O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=sel3)
-    t3 = time.perf_counter() - t1
-    t1 = t1 - t0
-    per_region = max((t3 - t1) / 2.0, 1e-9)
+    t1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=selm)
+    tm = time.perf_counter() - t0
+    per_region = max((tm - t1) / (n_many - 1), 1e-9)
     per_head_fixed = max(t1 - per_region, 0.0)
     t_head = t_plan + per_head_fixed + per_region * R
     total = t_head * w.B * w.H
@@ -72,9 +73,11 @@ def cpu_baseline(w, q, k, v, hi, lo):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": ("1 of %d heads: full plan (%.2f s) + tiered attention on 1 and 3 query "
-                   "regions (%.2f s, %.2f s), extrapolated to %d regions x %d heads = %.0f s"
-                   % (w.B * w.H, t_plan, t1, t3, R, w.B * w.H, total)),
+        "sample": ("1 of %d heads: full plan (%.2f s), tiered attention on 1 and on %d query "
+                   "regions (%.2f s, %.2f s); per-head fixed %.2f s + %.4f s per region, "
+                   "extrapolated to %d regions x %d heads = %.0f s"
+                   % (w.B * w.H, t_plan, n_many, t1, tm, per_head_fixed, per_region, R,
+                      w.B * w.H, total)),
     }
 
 
