@@ -114,43 +114,56 @@ __device__ __forceinline__ v8i lds16(const uint8_t *p)
 
 // Copy UNITS kilobytes from global src to LDS dst with direct-to-LDS loads;
 // wave w of the two copies units w, w+2, ...  Each unit is one instruction:
-// 64 lanes x 16 bytes landing at dst + lane * 16.
+// 64 lanes x 16 bytes landing at dst + lane * 16.  The source address is a
+// wave-uniform base plus a 32-bit lane offset, so it needs no 64-bit vector
+// arithmetic.
 template <int UNITS>
-__device__ __forceinline__ void copy_kb(const uint8_t *src, uint8_t *dst, int w, int l)
+__device__ __forceinline__ void copy_kb(const uint8_t *src, uint8_t *dst, int w, uint32_t loff16)
 {
 #pragma unroll
     for (int j = 0; j < UNITS / 2; j++) {
         const int u = 2 * j + w;
-        __builtin_amdgcn_global_load_lds((const void *)(src + u * 1024 + l * 16),
+        __builtin_amdgcn_global_load_lds((const void *)((src + u * 1024) + loff16),
                                          (lds_void *)(dst + u * 1024), 16, 0, 0);
     }
 }
 
 // Copy 4 bytes per active lane with one direct-to-LDS load (lane l -> dst + 4 l).
-__device__ __forceinline__ void copy_dword(const uint8_t *src, uint8_t *dst, int l)
+__device__ __forceinline__ void copy_dword(const uint8_t *src, uint8_t *dst, uint32_t loff4)
 {
-    __builtin_amdgcn_global_load_lds((const void *)(src + l * 4), (lds_void *)dst, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void *)(src + loff4), (lds_void *)dst, 4, 0, 0);
 }
 
-// LDS image of one kept tile.  FP8: K codes [0, 64D), V codes [64D, 128D).
-// MXFP4: K [0, 32D), V [32D, 64D), K exponents [64D, 66D), V [66D, 68D).
-template <int D>
-__device__ __forceinline__ void issue_tile(const AttnArgs &A, int64_t kblk, bool fp8, uint8_t *dst,
-                                           int w, int l)
+// LDS images.  Keys and values travel in separate double-buffered streams:
+// the key operand of tile i+1 is needed while tile i's weights are formed
+// (its logits are computed one tile ahead, so the matrix core works while the
+// vector unit runs the softmax), the value operand of tile i only at the end
+// of tile i.  Per buffer (D = head dim):
+//   FP8 key    [0, 64D)  codes                    value [0, 64D) codes
+//   MXFP4 key  [0, 32D)  codes, [32D, 34D) E8M0   value [0, 32D) codes, [32D, 34D) E8M0
+template <int D, bool FP8>
+__device__ __forceinline__ void issue_k(const AttnArgs &A, int64_t kblk, uint8_t *dst, int w, int l)
 {
-    if (fp8) {
-        copy_kb<kBlk * D / 1024>(A.k8 + kblk * (kBlk * D), dst, w, l);
-        copy_kb<kBlk * D / 1024>(A.v8 + kblk * (kBlk * D), dst + kBlk * D, w, l);
+    const uint32_t lo = (uint32_t)l;
+    if (FP8) {
+        copy_kb<kBlk * D / 1024>(A.k8 + kblk * (kBlk * D), dst, w, lo * 16u);
     } else {
-        copy_kb<kBlk * D / 2048>(A.k4 + kblk * (kBlk * D / 2), dst, w, l);
-        copy_kb<kBlk * D / 2048>(A.v4 + kblk * (kBlk * D / 2), dst + 32 * D, w, l);
-        // 2D bytes of exponents per operand (4 per lane): wave 0 copies K's, wave 1 V's
-        if (l * 4 < 2 * D) {
-            if (w == 0)
-                copy_dword(A.k4s + kblk * (2 * D), dst + 64 * D, l);
-            else
-                copy_dword(A.v4s + kblk * (2 * D), dst + 66 * D, l);
-        }
+        copy_kb<kBlk * D / 2048>(A.k4 + kblk * (kBlk * D / 2), dst, w, lo * 16u);
+        if (w == 0 && l * 4 < 2 * D)
+            copy_dword(A.k4s + kblk * (2 * D), dst + 32 * D, lo * 4u);
+    }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void issue_v(const AttnArgs &A, int64_t kblk, uint8_t *dst, int w, int l)
+{
+    const uint32_t lo = (uint32_t)l;
+    if (FP8) {
+        copy_kb<kBlk * D / 1024>(A.v8 + kblk * (kBlk * D), dst, w, lo * 16u);
+    } else {
+        copy_kb<kBlk * D / 2048>(A.v4 + kblk * (kBlk * D / 2), dst, w, lo * 16u);
+        if (w == 1 && l * 4 < 2 * D)
+            copy_dword(A.v4s + kblk * (2 * D), dst + 32 * D, lo * 4u);
     }
 }
 
@@ -167,72 +180,98 @@ __device__ __forceinline__ void rescale(v16f (&acc)[CB], float &z, float alpha)
     }
 }
 
-// Operands of one tile, read from its LDS image into registers before the
-// next tile's prefetch is issued (the compiler orders every LDS read after a
-// pending direct-to-LDS load, so reading first keeps the prefetch in flight
-// across the whole computation).
+// Register operands of one tile.
 template <int D>
-struct TileRegs {
-    v8i k[2][D / 64];   // key operand per (key half, 64-channel step)
-    v8i v[D / 32];      // value operand per 32-channel block
-    int ks[2][D / 64];  // MXFP4 key exponents
-    int vs[D / 32];     // MXFP4 value exponents
+struct KRegs {
+    v8i k[2][D / 64];   // per (key half, 64-channel step)
+    int ks[2][D / 64];  // MXFP4 exponents
 };
 
 template <int D>
-__device__ __forceinline__ void read_fp8(const uint8_t *tb, int l, TileRegs<D> &T)
-{
-    constexpr int KC = D / 64, CB = D / 32;
-#pragma unroll
-    for (int mm = 0; mm < 2; mm++)
-#pragma unroll
-        for (int kc = 0; kc < KC; kc++)
-            T.k[mm][kc] = lds32(tb + ((mm * KC + kc) * 64 + l) * 32);
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-        T.v[cb] = lds32(tb + kBlk * D + (cb * 64 + l) * 32);
-}
+struct VRegs {
+    v8i v[D / 32];      // per 32-channel block
+    int vs[D / 32];     // MXFP4 exponents
+};
 
-template <int D>
-__device__ __forceinline__ void read_fp4(const uint8_t *tb, int l, TileRegs<D> &T)
+template <int D, bool FP8>
+__device__ __forceinline__ void read_k(const uint8_t *b, int l, KRegs<D> &K)
 {
-    constexpr int KC = D / 64, CB = D / 32;
+    constexpr int KC = D / 64;
 #pragma unroll
     for (int mm = 0; mm < 2; mm++)
 #pragma unroll
         for (int kc = 0; kc < KC; kc++) {
             const int chunk = (mm * KC + kc) * 64 + l;
-            T.k[mm][kc] = lds16(tb + chunk * 16);
-            T.ks[mm][kc] = tb[64 * D + chunk];
+            if (FP8) {
+                K.k[mm][kc] = lds32(b + chunk * 32);
+            } else {
+                K.k[mm][kc] = lds16(b + chunk * 16);
+                K.ks[mm][kc] = b[32 * D + chunk];
+            }
         }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void read_v(const uint8_t *b, int l, VRegs<D> &V)
+{
+    constexpr int CB = D / 32;
 #pragma unroll
     for (int cb = 0; cb < CB; cb++) {
         const int chunk = cb * 64 + l;
-        T.v[cb] = lds16(tb + 32 * D + chunk * 16);
-        T.vs[cb] = tb[66 * D + chunk];
+        if (FP8) {
+            V.v[cb] = lds32(b + chunk * 32);
+        } else {
+            V.v[cb] = lds16(b + chunk * 16);
+            V.vs[cb] = b[32 * D + chunk];
+        }
     }
 }
 
-// One FP8 tile.
-template <int D>
-__device__ __forceinline__ void tile_fp8(const TileRegs<D> &T, const v8i (&q8)[D / 64], float c8,
-                                         v16f (&acc)[D / 32], float &m, float &z)
+// Logits S^T = K Q^T of one tile (FP8 codes, or MXFP4 with block scales).
+template <int D, bool FP8>
+__device__ __forceinline__ void logits(const KRegs<D> &K, const v8i (&q8)[D / 64],
+                                       const v8i (&q4)[D / 64], const int (&q4s)[D / 64],
+                                       v16f (&s)[2])
 {
-    constexpr int KC = D / 64, CB = D / 32;
-    v16f s[2];
-#pragma unroll
-    for (int mm = 0; mm < 2; mm++) {
-        s[mm] = (v16f){};
+    constexpr int KC = D / 64;
+    s[0] = (v16f){};
+    s[1] = (v16f){};
+    if (FP8) {
 #pragma unroll
         for (int kc = 0; kc < KC; kc++)
-            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.k[mm][kc], q8[kc], s[mm], 0, 0,
-                                                                   0, 0, 0, 0);
-    }
-    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; r++)
-        mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-    mx = pair_max(mx);
+            for (int mm = 0; mm < 2; mm++)
+                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], q8[kc], s[mm], 0,
+                                                                       0, 0, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++)
+#pragma unroll
+            for (int mm = 0; mm < 2; mm++)
+                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    K.k[mm][kc], q4[kc], s[mm], 4, 4, 0, K.ks[mm][kc], 0, q4s[kc]);
+    }
+}
+
+// Largest of the 32 logits a lane holds: a tree of three-input maxima.
+__device__ __forceinline__ float lane_max(const v16f (&s)[2])
+{
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int r = 2 * j;
+        t[j] = fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1]));
+    }
+    return fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+}
+
+// FP8 weights of one tile: running max, e = 2^(S c8 + 8 - m) = 256 w,
+// Z += e, P = e4m3(e) as the B operand of P^T V.
+template <int CB>
+__device__ __forceinline__ v8i weights_fp8(const v16f (&s)[2], float c8, v16f (&acc)[CB], float &m,
+                                           float &z)
+{
+    float mx = pair_max(lane_max(s));
     const float mnew = fmaxf(m, mx * c8);
     rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
     m = mnew;
@@ -250,43 +289,25 @@ __device__ __forceinline__ void tile_fp8(const TileRegs<D> &T, const v8i (&q8)[D
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
         p[q] = wd;
     }
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.v[cb], p, acc[cb], 0, 0, 0, 0, 0,
-                                                                 0);
+    return p;
 }
 
-// One MXFP4 tile.
-template <int D>
-__device__ __forceinline__ void tile_fp4(const TileRegs<D> &T, const v8i (&q4)[D / 64],
-                                         const int (&q4s)[D / 64], float c, v16f (&acc)[D / 32],
-                                         float &m, float &z)
+// MXFP4 weights of one tile: as above with c = log2(e)/sqrt(d); each lane's
+// 32-key group gets the E8M0 exponent floor(log2(max e)) - 2 (returned in ef).
+template <int CB>
+__device__ __forceinline__ v8i weights_fp4(const v16f (&s)[2], float c, v16f (&acc)[CB], float &m,
+                                           float &z, int &ef)
 {
-    constexpr int KC = D / 64, CB = D / 32;
-    v16f s[2];
-#pragma unroll
-    for (int mm = 0; mm < 2; mm++) {
-        s[mm] = (v16f){};
-#pragma unroll
-        for (int kc = 0; kc < KC; kc++)
-            s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.k[mm][kc], q4[kc], s[mm], 4, 4,
-                                                                   0, T.ks[mm][kc], 0, q4s[kc]);
-    }
-    float gm = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; r++)
-        gm = fmaxf(gm, fmaxf(s[0][r], s[1][r]));
+    const float gm = lane_max(s);
     const float mx = pair_max(gm);
     const float tm = mx * c;
     const float mnew = fmaxf(m, tm);
     rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
     m = mnew;
     const float bias = 8.0f - mnew;
-    // E8M0 exponent of this lane's 32-key group: floor(log2(max e)) - 2.  The
-    // group holding the running maximum has max e = 2^8 exactly (w = 1), so
-    // its exponent is fixed at 6 instead of being read from a rounded exp2
-    // that may land just below the power of two.
-    int ef;
+    // The group holding the running maximum has max e = 2^8 exactly (w = 1),
+    // so its exponent is fixed at 6 instead of being read from a rounded
+    // exp2 that may land just below the power of two.
     if (gm == mx && mnew == tm) {
         ef = 127 + 6;
     } else {
@@ -314,18 +335,118 @@ __device__ __forceinline__ void tile_fp4(const TileRegs<D> &T, const v8i (&q4)[D
         p[q] = (int)wd;
     }
     p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(T.v[cb], p, acc[cb], 4, 4, 0,
-                                                                 T.vs[cb], 0, ef);
+    return p;
 }
+
+template <int D>
+struct Attn {
+    static constexpr int KC = D / 64;   // 64-channel steps of QK^T
+    static constexpr int CB = D / 32;   // 32-channel blocks of the output
+    const AttnArgs &A;
+    uint8_t (&kbuf)[2][kBlk * D];
+    uint8_t (&vbuf)[2][kBlk * D];
+    const int32_t *list;
+    int64_t hbase;
+    int n8, n, w, l;
+    float qs;
+    v8i q8[KC], q4[KC];
+    int q4s[KC];
+    v16f acc[CB];
+    float m, z;
+
+    // Key of tile j (kind NEXT8) from its buffer; issue its logits into s.
+    template <bool NEXT8>
+    __device__ __forceinline__ void key_logits(int j, v16f (&s)[2])
+    {
+        KRegs<D> K;
+        read_k<D, NEXT8>(kbuf[j & 1], l, K);
+        logits<D, NEXT8>(K, q8, q4, q4s, s);
+    }
+
+    // Wave-uniform values carried one tile ahead (scalar registers), so no
+    // scalar load is waited for inside a tile: key regions of the next key
+    // and value refills, and the FP8 logit scale of the current tile.
+    int kb_k, kb_v;
+    float c8;
+
+    template <bool FP8>
+    __device__ __forceinline__ void prefetch(int i)
+    {
+        // refill the buffers read last tile: key of tile i+2, value of tile i+1
+        if (i + 2 < n) {
+            const int64_t kb = hbase + kb_k;
+            if (FP8 && i + 2 < n8)
+                issue_k<D, true>(A, kb, kbuf[i & 1], w, l);
+            else
+                issue_k<D, false>(A, kb, kbuf[i & 1], w, l);
+        }
+        if (i + 1 < n) {
+            const int64_t kb = hbase + kb_v;
+            if (FP8 && i + 1 < n8)
+                issue_v<D, true>(A, kb, vbuf[(i + 1) & 1], w, l);
+            else
+                issue_v<D, false>(A, kb, vbuf[(i + 1) & 1], w, l);
+        }
+    }
+
+    // Tile i (kind FP8): its logits sc are ready.  Start tile i+1's logits
+    // into sn on the matrix core, then form tile i's weights on the vector
+    // unit and accumulate P^T V.
+    template <bool FP8>
+    __device__ __forceinline__ void step(int i, const v16f (&sc)[2], v16f (&sn)[2])
+    {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // LDS reads of this tile come before the refill is issued, so they
+        // never wait for it
+        VRegs<D> V;
+        read_v<D, FP8>(vbuf[i & 1], l, V);
+        KRegs<D> K;
+        const bool more = i + 1 < n, next8 = FP8 && i + 1 < n8;
+        if (more) {
+            if (next8)
+                read_k<D, true>(kbuf[(i + 1) & 1], l, K);
+            else
+                read_k<D, false>(kbuf[(i + 1) & 1], l, K);
+        }
+        prefetch<FP8>(i);
+        if (more) {
+            if (next8)
+                logits<D, true>(K, q8, q4, q4s, sn);
+            else
+                logits<D, false>(K, q8, q4, q4s, sn);
+        }
+        if (FP8) {
+            const v8i p = weights_fp8<CB>(sc, c8, acc, m, z);
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 0, 0, 0,
+                                                                         0, 0, 0);
+        } else {
+            int ef;
+            const v8i p = weights_fp4<CB>(sc, A.c4, acc, m, z, ef);
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 4, 4, 0,
+                                                                         V.vs[cb], 0, ef);
+        }
+        // scalars for the next tile, loaded after this tile's LDS reads were
+        // consumed (scalar and LDS loads share one completion counter)
+        if (next8)
+            c8 = (qs * sload_f32(A.ks8 + hbase + kb_v)) * A.c4;
+        kb_v = kb_k;
+        if (i + 3 < n)
+            kb_k = sload_i32(list + i + 3);
+    }
+};
 
 template <int D>
 __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 {
-    constexpr int KC = D / 64;   // 64-channel steps of QK^T
-    constexpr int CB = D / 32;   // 32-channel blocks of the output
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2 * kBlk * D];
+    constexpr int KC = D / 64;
+    constexpr int CB = D / 32;
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][kBlk * D];
 
     // XCD-aware work mapping.  Workgroups are dealt to the 8 XCDs round robin
     // (block L runs on XCD L % 8).  Every XCD walks the heads in the same
@@ -336,55 +457,77 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     // whose kept key regions overlap.
     const int R = A.R;
     const int span = (R + 7) / 8;
-    const int xcd = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
-    const int bh = k / span;
-    const int a = xcd * span + (k - bh * span);
+    const int xcd = (int)(blockIdx.x & 7), kk = (int)(blockIdx.x >> 3);
+    const int bh = kk / span;
+    const int a = xcd * span + (kk - bh * span);
     if (a >= R)
         return;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, hf = l >> 5;
     const int64_t qblk = (int64_t)bh * R + a;
 
+    Attn<D> S{A, kbuf, vbuf};
+    S.w = w;
+    S.l = l;
     // queries of this wave, both formats
-    v8i q8[KC], q4[KC];
-    int q4s[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; kc++) {
         const int chunk = (w * KC + kc) * 64 + l;
-        q8[kc] = load32(A.q8 + qblk * (kBlk * D) + chunk * 32);
-        q4[kc] = load16(A.q4 + qblk * (kBlk * D / 2) + chunk * 16);
-        q4s[kc] = A.q4s[qblk * (2 * D) + chunk];
+        S.q8[kc] = load32(A.q8 + qblk * (kBlk * D) + chunk * 32);
+        S.q4[kc] = load16(A.q4 + qblk * (kBlk * D / 2) + chunk * 16);
+        S.q4s[kc] = A.q4s[qblk * (2 * D) + chunk];
     }
-    const float qs = A.qs8[qblk];
-    const int n8 = A.cnt[qblk * 2], n4 = A.cnt[qblk * 2 + 1];
-    const int n = n8 + n4;
-    const int32_t *list = A.sched + qblk * R;
-    const int64_t hbase = (int64_t)bh * R;
-
-    v16f acc[CB];
+    S.qs = A.qs8[qblk];
+    const int n8 = sload_i32(A.cnt + qblk * 2), n = n8 + sload_i32(A.cnt + qblk * 2 + 1);
+    S.n8 = n8;
+    S.n = n;
+    S.list = A.sched + qblk * R;
+    S.hbase = (int64_t)bh * R;
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
-        acc[cb] = (v16f){};
-    float m = -__builtin_huge_valf();
-    float z = 0.0f;
+        S.acc[cb] = (v16f){};
+    S.m = -__builtin_huge_valf();
+    S.z = 0.0f;
 
-    // key regions are wave-uniform: keep them (and their FP8 scales) scalar
-    int kb_next = n > 0 ? sload_i32(list) : 0;
-    if (n > 0)
-        issue_tile<D>(A, hbase + kb_next, n8 > 0, tiles[0], w, l);
-
-    int it = 0;
-    for (; it < n8; it++) {
-        const int kb = kb_next;
-        const float c8 = (qs * sload_f32(A.ks8 + hbase + kb)) * A.c4;
+    v16f sa[2], sb[2];
+    if (n > 0) {
+        // prologue: key and value of tile 0, key of tile 1; logits of tile 0
+        const int64_t kb0 = S.hbase + sload_i32(S.list);
+        if (n8 > 0) {
+            issue_k<D, true>(A, kb0, kbuf[0], w, l);
+            issue_v<D, true>(A, kb0, vbuf[0], w, l);
+        } else {
+            issue_k<D, false>(A, kb0, kbuf[0], w, l);
+            issue_v<D, false>(A, kb0, vbuf[0], w, l);
+        }
+        if (n > 1) {
+            const int64_t kb1 = S.hbase + sload_i32(S.list + 1);
+            if (n8 > 1)
+                issue_k<D, true>(A, kb1, kbuf[1], w, l);
+            else
+                issue_k<D, false>(A, kb1, kbuf[1], w, l);
+        }
+        S.kb_v = n > 1 ? sload_i32(S.list + 1) : 0;
+        S.kb_k = n > 2 ? sload_i32(S.list + 2) : 0;
+        S.c8 = n8 > 0 ? (S.qs * sload_f32(A.ks8 + kb0)) * A.c4 : 0.0f;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        TileRegs<D> T;
-        read_fp8<D>(tiles[it & 1], l, T);
-        if (it + 1 < n) {
-            kb_next = sload_i32(list + it + 1);
-            issue_tile<D>(A, hbase + kb_next, it + 1 < n8, tiles[(it + 1) & 1], w, l);
+        if (n8 > 0)
+            S.template key_logits<true>(0, sa);
+        else
+            S.template key_logits<false>(0, sa);
+    }
+    // Tiles alternate between the two logit registers sets; the loops are
+    // unrolled by two so that no copy is needed between tiles.
+    int i = 0;
+    while (i < n8) {
+        S.template step<true>(i, sa, sb);
+        if (++i >= n8) {
+            sa[0] = sb[0];
+            sa[1] = sb[1];
+            break;
         }
-        tile_fp8<D>(T, q8, c8, acc, m, z);
+        S.template step<true>(i, sb, sa);
+        ++i;
     }
     if (n8 > 0) {
         // phase boundary: FP8 value units -> real units (per-channel V scale)
@@ -393,25 +536,21 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
         for (int cb = 0; cb < CB; cb++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
-                acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+                S.acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
     }
-    for (; it < n; it++) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        TileRegs<D> T;
-        read_fp4<D>(tiles[it & 1], l, T);
-        if (it + 1 < n) {
-            kb_next = sload_i32(list + it + 1);
-            issue_tile<D>(A, hbase + kb_next, false, tiles[(it + 1) & 1], w, l);
-        }
-        tile_fp4<D>(T, q4, q4s, A.c4, acc, m, z);
+    while (i < n) {
+        S.template step<false>(i, sa, sb);
+        if (++i >= n)
+            break;
+        S.template step<false>(i, sb, sa);
+        ++i;
     }
 
     // ---------------- epilogue: normalize and restore token order ----------------
-    const float zt = pair_sum(z);
+    const float zt = pair_sum(S.z);
     const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
-    const int i = 32 * w + (l & 31);
-    const int tok = region_token(a, i, A.Ry, A.Rx, A.Hv, A.Wv);
+    const int qi = 32 * w + (l & 31);
+    const int tok = region_token(a, qi, A.Ry, A.Rx, A.Hv, A.Wv);
     const int b = bh / A.H, h = bh - b * A.H;
     const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)tok * A.osn;
 #pragma unroll
@@ -419,8 +558,8 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 #pragma unroll
         for (int g = 0; g < 4; g++) {
             const int c0 = 32 * cb + 8 * g + 4 * hf;
-            float o0 = acc[cb][4 * g] * inv, o1 = acc[cb][4 * g + 1] * inv;
-            float o2 = acc[cb][4 * g + 2] * inv, o3 = acc[cb][4 * g + 3] * inv;
+            float o0 = S.acc[cb][4 * g] * inv, o1 = S.acc[cb][4 * g + 1] * inv;
+            float o2 = S.acc[cb][4 * g + 2] * inv, o3 = S.acc[cb][4 * g + 3] * inv;
             if (A.out_f32) {
                 *reinterpret_cast<float4 *>((float *)A.out + obase + c0) = make_float4(o0, o1, o2, o3);
             } else {
