@@ -451,17 +451,21 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     // XCD-aware work mapping.  Workgroups are dealt to the 8 XCDs round robin
     // (block L runs on XCD L % 8).  Every XCD walks the heads in the same
     // order and takes its own contiguous eighth of each head's query regions,
-    // so all XCDs work on the same head at a time: that head's key/value
+    // so all XCDs work on the same head at a time and that head's key/value
     // tiles (about 31 MB for a 720p Wan layer) stay in the shared last-level
-    // cache, and each XCD's L2 serves spatially neighbouring query regions,
-    // whose kept key regions overlap.
+    // cache.  Inside a head the query regions are taken frame-fastest: the
+    // regions at one spatial position in consecutive latent frames keep
+    // largely the same key regions, so the workgroups an XCD runs together
+    // share their key/value tiles through its L2.
     const int R = A.R;
     const int span = (R + 7) / 8;
     const int xcd = (int)(blockIdx.x & 7), kk = (int)(blockIdx.x >> 3);
     const int bh = kk / span;
-    const int a = xcd * span + (kk - bh * span);
-    if (a >= R)
+    const int j = xcd * span + (kk - bh * span);
+    if (j >= R)
         return;
+    const int RF = A.Ry * A.Rx, NF = R / RF;
+    const int a = (j % NF) * RF + j / NF;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, hf = l >> 5;
     const int64_t qblk = (int64_t)bh * R + a;
 
