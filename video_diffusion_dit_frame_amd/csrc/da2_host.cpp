@@ -65,6 +65,8 @@ void carve(da2_layout_s &L)
     W.kmax = take(BH * R * d * 4);
     W.la = take(BH * R * R * 8);
     W.lm = take(BH * R * R * 8);
+    W.rmax = take(BH * 2 * R * 8);
+    W.zsum = take(BH * 2 * R * 8);
     W.keys = take(BH * R * R * 4);
     W.tier = take(BH * R * R);
     W.sched = take(BH * R * R * 4);

@@ -27,7 +27,7 @@ struct Workspace {
     size_t k8, k4, k4s, ks8;
     size_t v8, v4, v4s, vs8, vamax;
     size_t qavg, kavg, qmax, kmax;
-    size_t la, lm, keys, tier;
+    size_t la, lm, rmax, zsum, keys, tier;
     size_t sched, cnt;
     size_t rank_state, rank_hist, rank_eq;
     size_t total;

@@ -4,7 +4,8 @@
 //
 // Scores must be bit-identical run to run and against an fp64 reference, so
 // every floating-point step has a fixed order: logits are fused multiply-add
-// chains over channels 0..d-1 times 1/sqrt(d); row maxima (order-free);
+// chains over channels 0..d-1 times 1/sqrt(d) (on the fp64 matrix core, whose
+// accumulation is exactly such a chain); row maxima (order-free);
 // exponentials by the shared Cody-Waite/Taylor exp; row sums strictly
 // sequential over key regions; p = e / Z; A = (1-lambda) p_avg + lambda p_max
 // with separate products; the ranking key is the bit pattern of fp32(A).
@@ -23,151 +24,213 @@ namespace {
 
 constexpr int kChunk = 4096;   // keys per rank workgroup (256 threads x 16)
 
+__global__ void k_fill_words(uint32_t *p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
-// Logits: La = avgQ avgK^T / sqrt(d), Lm = maxQ maxK^T / sqrt(d), fp64.
-// 64x64 output tile per workgroup, 4x4 per thread and branch; channels staged
-// through LDS 16 at a time; every accumulator is one fma chain in channel
-// order.
+// Logits: La = avgQ avgK^T / sqrt(d), Lm = maxQ maxK^T / sqrt(d), fp64, on the
+// fp64 matrix core.  v_mfma_f64_16x16x4f64 adds its four products to the
+// accumulator as four fused multiply-adds in ascending k (each rounded), so
+// feeding channels in ascending order makes every accumulator exactly the
+// fma chain over channels 0..d-1 that the scores are defined by.
+// Operand layouts of the instruction: A lane l = (row l%16, k l/16), B lane
+// l = (k l/16, column l%16), accumulator lane l register r = (row 4r + l/16,
+// column l%16).
+// One workgroup (4 waves, 2x2) computes a 128x128 tile of one branch; each
+// wave a 64x64 block as 4x4 accumulators.  Channels are staged through LDS
+// 32 at a time, transposed so that an operand is one conflict-free read.
 // ---------------------------------------------------------------------------
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+// Order-preserving map of (non-NaN) doubles to unsigned integers, so that an
+// integer atomic maximum is the floating-point maximum.  0 is below every
+// encoded value.
+__device__ __forceinline__ unsigned long long ord64(double x)
+{
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double unord64(unsigned long long e)
+{
+    const unsigned long long u = (e >> 63) ? (e & 0x7fffffffffffffffull) : ~e;
+    return __longlong_as_double((long long)u);
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_logits(const double *__restrict__ qa,
+__global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa,
                                                 const double *__restrict__ ka,
                                                 const float *__restrict__ qm,
                                                 const float *__restrict__ km, int R,
                                                 double inv_sqrt_d, double *__restrict__ La,
-                                                double *__restrict__ Lm)
+                                                double *__restrict__ Lm,
+                                                unsigned long long *__restrict__ rmax)
 {
-    constexpr int CK = 16;
-    __shared__ double sqa[CK][64], ska[CK][64], sqm[CK][64], skm[CK][64];
-    const int b0 = blockIdx.x * 64, a0 = blockIdx.y * 64, bh = blockIdx.z;
-    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-    const double *qab = qa + (int64_t)bh * R * D, *kab = ka + (int64_t)bh * R * D;
-    const float *qmb = qm + (int64_t)bh * R * D, *kmb = km + (int64_t)bh * R * D;
-    double aa[4][4], am[4][4];
+    constexpr int TM = 128, CK = 32, PITCH = TM + 4;
+    __shared__ double sq[CK][PITCH], sk[CK][PITCH];
+    const int b0 = blockIdx.x * TM, a0 = blockIdx.y * TM;
+    const int bh = blockIdx.z >> 1, maxb = blockIdx.z & 1;
+    const int t = threadIdx.x, l = t & 63, wv = t >> 6, wa = wv >> 1, wb = wv & 1;
+    v4d acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int g = 0; g < 4; g++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            aa[i][j] = 0.0;
-            am[i][j] = 0.0;
-        }
+        for (int h = 0; h < 4; h++)
+            acc[g][h] = (v4d){0.0, 0.0, 0.0, 0.0};
     for (int c0 = 0; c0 < D; c0 += CK) {
-        // 64 rows x 16 channels per array; thread loads 4 elements per array
-        for (int e = t; e < 64 * CK; e += 256) {
-            int r = e / CK, c = e - r * CK;
-            int ga = a0 + r, gb = b0 + r;
-            sqa[c][r] = ga < R ? qab[(int64_t)ga * D + c0 + c] : 0.0;
-            sqm[c][r] = ga < R ? (double)qmb[(int64_t)ga * D + c0 + c] : 0.0;
-            ska[c][r] = gb < R ? kab[(int64_t)gb * D + c0 + c] : 0.0;
-            skm[c][r] = gb < R ? (double)kmb[(int64_t)gb * D + c0 + c] : 0.0;
+        __syncthreads();
+        if (!maxb) {
+            // 128 rows x 32 channels of each operand, 16 bytes per thread
+            const double *qb = qa + (int64_t)bh * R * D, *kb = ka + (int64_t)bh * R * D;
+            for (int e = t; e < TM * CK / 2; e += 256) {
+                const int r = e / (CK / 2), c = 2 * (e % (CK / 2));
+                double2 x = make_double2(0.0, 0.0), y = make_double2(0.0, 0.0);
+                if (a0 + r < R)
+                    x = *reinterpret_cast<const double2 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
+                if (b0 + r < R)
+                    y = *reinterpret_cast<const double2 *>(kb + (int64_t)(b0 + r) * D + c0 + c);
+                sq[c][r] = x.x;
+                sq[c + 1][r] = x.y;
+                sk[c][r] = y.x;
+                sk[c + 1][r] = y.y;
+            }
+        } else {
+            const float *qb = qm + (int64_t)bh * R * D, *kb = km + (int64_t)bh * R * D;
+            for (int e = t; e < TM * CK / 4; e += 256) {
+                const int r = e / (CK / 4), c = 4 * (e % (CK / 4));
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (a0 + r < R)
+                    x = *reinterpret_cast<const float4 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
+                if (b0 + r < R)
+                    y = *reinterpret_cast<const float4 *>(kb + (int64_t)(b0 + r) * D + c0 + c);
+                sq[c][r] = x.x;
+                sq[c + 1][r] = x.y;
+                sq[c + 2][r] = x.z;
+                sq[c + 3][r] = x.w;
+                sk[c][r] = y.x;
+                sk[c + 1][r] = y.y;
+                sk[c + 2][r] = y.z;
+                sk[c + 3][r] = y.w;
+            }
         }
         __syncthreads();
-#pragma unroll 4
-        for (int c = 0; c < CK; c++) {
-            double xa[4], ya[4], xm[4], ym[4];
+#pragma unroll 2
+        for (int s4 = 0; s4 < CK; s4 += 4) {
+            const int c = s4 + (l >> 4), r = l & 15;
+            double av[4], bv[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                xa[i] = sqa[c][ty + 16 * i];
-                xm[i] = sqm[c][ty + 16 * i];
-                ya[i] = ska[c][tx + 16 * i];
-                ym[i] = skm[c][tx + 16 * i];
+            for (int g = 0; g < 4; g++) {
+                av[g] = sq[c][64 * wa + 16 * g + r];
+                bv[g] = sk[c][64 * wb + 16 * g + r];
             }
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+            for (int g = 0; g < 4; g++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    aa[i][j] = __builtin_fma(xa[i], ya[j], aa[i][j]);
-                    am[i][j] = __builtin_fma(xm[i], ym[j], am[i][j]);
+                for (int h = 0; h < 4; h++)
+                    acc[g][h] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[g], bv[h], acc[g][h], 0, 0, 0);
+        }
+    }
+    // Store key-major (L^T[b][a], so the row passes read a row of logits
+    // as a coalesced column sweep) and fold the row maxima into rmax with an
+    // order-preserving integer atomic maximum.
+    double *L = (maxb ? Lm : La) + (int64_t)bh * R * R;
+    unsigned long long *rm = rmax + ((int64_t)bh * 2 + maxb) * R;
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int i = a0 + 64 * wa + 16 * g + 4 * r + (l >> 4);
+            double mx = -__builtin_huge_val();
+#pragma unroll
+            for (int h = 0; h < 4; h++) {
+                const int j = b0 + 64 * wb + 16 * h + (l & 15);
+                const double v = acc[g][h][r] * inv_sqrt_d;
+                if (i < R && j < R) {
+                    L[(int64_t)j * R + i] = v;
+                    mx = fmax(mx, v);
                 }
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        int ga = a0 + ty + 16 * i;
-        if (ga >= R)
-            continue;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            int gb = b0 + tx + 16 * j;
-            if (gb < R) {
-                int64_t o = ((int64_t)bh * R + ga) * R + gb;
-                La[o] = aa[i][j] * inv_sqrt_d;
-                Lm[o] = am[i][j] * inv_sqrt_d;
             }
+            // lanes l and l ^ 1, 2, 4, 8 hold the same row
+            mx = fmax(mx, __shfl_xor(mx, 1, 16));
+            mx = fmax(mx, __shfl_xor(mx, 2, 16));
+            mx = fmax(mx, __shfl_xor(mx, 4, 16));
+            mx = fmax(mx, __shfl_xor(mx, 8, 16));
+            if ((l & 15) == 0 && i < R)
+                atomicMax(rm + i, ord64(mx));
         }
-    }
 }
 
 // ---------------------------------------------------------------------------
-// Row softmax of both branches and the mixture, 64 query regions per
-// workgroup.  The exponentials overwrite the logits; the row sums run in one
-// thread per (row, branch), strictly in key order, chunk after chunk.
+// Row sums of both branches' exponentials: one lane per (row, branch), the
+// key regions strictly in order (Z = (((e_0 + e_1) + e_2) + ...)).  The
+// logits are stored key-major, so each step of the sweep is one coalesced
+// load of 64 rows.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_softmix(double *__restrict__ La, double *__restrict__ Lm,
-                                                 int R, double lambda,
-                                                 uint32_t *__restrict__ keys)
+__global__ __launch_bounds__(64) void k_rowsum(const double *__restrict__ La,
+                                               const double *__restrict__ Lm, int R,
+                                               const unsigned long long *__restrict__ rmax,
+                                               double *__restrict__ zsum)
 {
-    __shared__ double rmax[2][64], rsum[2][64];
-    __shared__ double ech[2][64][33];
-    const int a0 = blockIdx.x * 64, bh = blockIdx.y, t = threadIdx.x;
-    const int rows = min(64, R - a0);
-    // 1) row maxima: 4 threads per row, one branch at a time
-    {
-        const int r = t >> 2, q = t & 3;
-        for (int br = 0; br < 2; br++) {
-            double m = -__builtin_huge_val();
-            if (r < rows) {
-                const double *L = (br ? Lm : La) + ((int64_t)bh * R + a0 + r) * R;
-                for (int b = q; b < R; b += 4)
-                    m = fmax(m, L[b]);
-            }
-            m = fmax(m, __shfl_xor(m, 1, 64));
-            m = fmax(m, __shfl_xor(m, 2, 64));
-            if (q == 0)
-                rmax[br][r] = m;
-        }
-        if (t < 128)
-            rsum[t >> 6][t & 63] = 0.0;
+    const int a = blockIdx.x * 64 + threadIdx.x, bh = blockIdx.y, br = blockIdx.z;
+    if (a >= R)
+        return;
+    const int64_t row = ((int64_t)bh * 2 + br) * R + a;
+    const double m = unord64(rmax[row]);
+    const double *L = (br ? Lm : La) + (int64_t)bh * R * R + a;
+    double z = 0.0;
+    for (int b = 0; b < R; b++)
+        z += exp_draft(L[(int64_t)b * R] - m);
+    zsum[row] = z;
+}
+
+// ---------------------------------------------------------------------------
+// Probabilities, mixture and ranking keys for a 64x64 tile of region pairs:
+// p = e / Z per branch (e recomputed bit-identically), A = (1 - lambda) p_avg
+// + lambda p_max with separate products, key = bits(fp32(A)).  Logits are
+// read key-major and the keys written query-major through an LDS transpose.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_keys(const double *__restrict__ La,
+                                              const double *__restrict__ Lm, int R, double lambda,
+                                              const unsigned long long *__restrict__ rmax,
+                                              const double *__restrict__ zsum,
+                                              uint32_t *__restrict__ keys)
+{
+    __shared__ uint32_t kt[64][65];
+    __shared__ double ma[64], mm[64], za[64], zm[64];
+    const int a0 = blockIdx.x * 64, b0 = blockIdx.y * 64, bh = blockIdx.z, t = threadIdx.x;
+    if (t < 64 && a0 + t < R) {
+        const int64_t r = (int64_t)bh * 2 * R + a0 + t;
+        ma[t] = unord64(rmax[r]);
+        mm[t] = unord64(rmax[r + R]);
+        za[t] = zsum[r];
+        zm[t] = zsum[r + R];
     }
     __syncthreads();
-    // 2) exponentials chunk by chunk, then sequential sums
-    for (int b0 = 0; b0 < R; b0 += 32) {
-        const int cols = min(32, R - b0);
-        for (int e = t; e < 2 * 64 * 32; e += 256) {
-            int br = e >> 11, r = (e >> 5) & 63, c = e & 31;
-            if (r < rows && c < cols) {
-                double *L = (br ? Lm : La) + ((int64_t)bh * R + a0 + r) * R + b0 + c;
-                double v = exp_draft(*L - rmax[br][r]);
-                *L = v;
-                ech[br][r][c] = v;
-            }
-        }
-        __syncthreads();
-        if (t < 128) {
-            int br = t >> 6, r = t & 63;
-            if (r < rows) {
-                double z = rsum[br][r];
-                for (int c = 0; c < cols; c++)
-                    z += ech[br][r][c];
-                rsum[br][r] = z;
-            }
-        }
-        __syncthreads();
-    }
-    // 3) probabilities, mixture, keys
     const double w0 = 1.0 - lambda;
-    for (int r = 0; r < rows; r++) {
-        const int64_t o = ((int64_t)bh * R + a0 + r) * R;
-        const double za = rsum[0][r], zm = rsum[1][r];
-        for (int b = t; b < R; b += 256) {
-            double pa = La[o + b] / za;
-            double pm = Lm[o + b] / zm;
-            double t0 = w0 * pa;
-            double t1 = lambda * pm;
-            double A = t0 + t1;
-            keys[o + b] = __float_as_uint((float)A);
+    const double *LA = La + (int64_t)bh * R * R, *LM = Lm + (int64_t)bh * R * R;
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int bb = e >> 6, aa = e & 63;
+        const int a = a0 + aa, b = b0 + bb;
+        if (a < R && b < R) {
+            const int64_t o = (int64_t)b * R + a;
+            const double pa = exp_draft(LA[o] - ma[aa]) / za[aa];
+            const double pm = exp_draft(LM[o] - mm[aa]) / zm[aa];
+            const double t0 = w0 * pa;
+            const double t1 = lambda * pm;
+            const double A = t0 + t1;
+            kt[aa][bb] = __float_as_uint((float)A);
         }
+    }
+    __syncthreads();
+    for (int e = t; e < 64 * 64; e += 256) {
+        const int aa = e >> 6, bb = e & 63;
+        const int a = a0 + aa, b = b0 + bb;
+        if (a < R && b < R)
+            keys[((int64_t)bh * R + a) * R + b] = kt[aa][bb];
     }
 }
 
@@ -521,18 +584,24 @@ void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st
 {
     const Workspace &W = L.ws;
     const double inv_sqrt_d = 1.0 / __builtin_sqrt((double)L.d);
-    const int T = (L.R + 63) / 64;
-    dim3 g(T, T, L.BH);
+    const int T = (L.R + 63) / 64, T2 = (L.R + 127) / 128;
     double *La = (double *)(ws + W.la), *Lm = (double *)(ws + W.lm);
+    unsigned long long *rmax = (unsigned long long *)(ws + W.rmax);
+    double *zsum = (double *)(ws + W.zsum);
+    const int64_t nmax = (int64_t)L.BH * 2 * L.R * 2;  // as 32-bit words
+    k_fill_words<<<(unsigned)((nmax + 255) / 256), 256, 0, st>>>((uint32_t *)rmax, nmax);
+    dim3 g(T2, T2, 2 * L.BH);
     if (L.d == 128)
         k_logits<128><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
                                          (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
-                                         L.R, inv_sqrt_d, La, Lm);
+                                         L.R, inv_sqrt_d, La, Lm, rmax);
     else
         k_logits<64><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
                                         (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
-                                        L.R, inv_sqrt_d, La, Lm);
-    k_softmix<<<dim3(T, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, (uint32_t *)(ws + W.keys));
+                                        L.R, inv_sqrt_d, La, Lm, rmax);
+    k_rowsum<<<dim3(T, L.BH, 2), 64, 0, st>>>(La, Lm, L.R, rmax, zsum);
+    k_keys<<<dim3(T, T, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
+                                             (uint32_t *)(ws + W.keys));
 }
 
 void launch_rank(const da2_layout_s &L, int scope, int64_t t8, int64_t tk, char *ws,
