@@ -165,26 +165,38 @@ __global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa
 }
 
 // ---------------------------------------------------------------------------
-// Row sums of both branches' exponentials: one lane per (row, branch), the
-// key regions strictly in order (Z = (((e_0 + e_1) + e_2) + ...)).  The
-// logits are stored key-major, so each step of the sweep is one coalesced
-// load of 64 rows.
+// Row sums of one branch's exponentials for 64 query regions: Z is added
+// strictly in key order (Z = (((e_0 + e_1) + e_2) + ...)).  Per chunk of 64
+// key regions all four waves form the exponentials (lane = query region,
+// coalesced reads of the key-major logits) into LDS, then wave 0 adds its
+// lane's 64 values in order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_rowsum(const double *__restrict__ La,
-                                               const double *__restrict__ Lm, int R,
-                                               const unsigned long long *__restrict__ rmax,
-                                               double *__restrict__ zsum)
+__global__ __launch_bounds__(256) void k_rowsum(const double *__restrict__ La,
+                                                const double *__restrict__ Lm, int R,
+                                                const unsigned long long *__restrict__ rmax,
+                                                double *__restrict__ zsum)
 {
-    const int a = blockIdx.x * 64 + threadIdx.x, bh = blockIdx.y, br = blockIdx.z;
-    if (a >= R)
-        return;
+    __shared__ double es[64][65];
+    const int a0 = blockIdx.x * 64, bh = blockIdx.y, br = blockIdx.z;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int a = a0 + lane;
     const int64_t row = ((int64_t)bh * 2 + br) * R + a;
-    const double m = unord64(rmax[row]);
+    const double m = a < R ? unord64(rmax[row]) : 0.0;
     const double *L = (br ? Lm : La) + (int64_t)bh * R * R + a;
     double z = 0.0;
-    for (int b = 0; b < R; b++)
-        z += exp_draft(L[(int64_t)b * R] - m);
-    zsum[row] = z;
+    for (int b0 = 0; b0 < R; b0 += 64) {
+        const int nb = R - b0 < 64 ? R - b0 : 64;
+#pragma unroll 4
+        for (int k = wv; k < nb; k += 4)
+            es[k][lane] = a < R ? exp_draft(L[(int64_t)(b0 + k) * R] - m) : 0.0;
+        __syncthreads();
+        if (wv == 0)
+            for (int k = 0; k < nb; k++)
+                z += es[k][lane];
+        __syncthreads();
+    }
+    if (wv == 0 && a < R)
+        zsum[row] = z;
 }
 
 // ---------------------------------------------------------------------------
@@ -599,7 +611,7 @@ void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st
         k_logits<64><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
                                         (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
                                         L.R, inv_sqrt_d, La, Lm, rmax);
-    k_rowsum<<<dim3(T, L.BH, 2), 64, 0, st>>>(La, Lm, L.R, rmax, zsum);
+    k_rowsum<<<dim3(T, L.BH, 2), 256, 0, st>>>(La, Lm, L.R, rmax, zsum);
     k_keys<<<dim3(T, T, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
                                              (uint32_t *)(ws + W.keys));
 }
