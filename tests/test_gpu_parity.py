@@ -189,3 +189,42 @@ def test_deterministic():
         outs.append((P.tier_map().cpu().numpy(), G.host(P.debug("KEYS"), np.uint32), o))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
+
+
+def _all_bf16(seed):
+    """Every finite bfloat16 bit pattern once per head: head 0 sorted by
+    magnitude (each block and MX group spans a narrow range, so codes near
+    the top of the grid dominate), head 1 in a seeded random order (wide
+    groups: small codes, subnormal FP8 codes and zeros)."""
+    u = np.arange(65536, dtype=np.uint32)
+    finite = ((u >> 7) & 0xFF) != 0xFF
+    vals = u[finite].astype(np.uint16)
+    mag = vals & np.uint16(0x7FFF)
+    srt = vals[np.lexsort((vals, mag))]
+    rnd = np.random.default_rng(seed).permutation(vals)
+    N, d = 1024, 64
+    x = np.zeros((1, 2, N * d), np.uint16)
+    x[0, 0, :srt.size] = srt
+    x[0, 1, :rnd.size] = rnd
+    return x.reshape(1, 2, N, d)
+
+
+def test_quantizers_exhaustive_bf16():
+    """FP8 and MXFP4 codes and scales of Q, K and V for every finite bf16
+    input value, bit-exact against the oracle's quantizers."""
+    F, Hv, Wv = 1, 32, 32
+    x = _all_bf16(7)
+    y = np.ascontiguousarray(x[:, ::-1])  # K: the two orders swapped between heads
+    P, qd, kd = G.run_plan(x, y, F, Hv, Wv, 1000, 3000)
+    G.run_attention(P, qd, kd, x)
+    for name, t in (("Q", x), ("K", y)):
+        o = O.quant_qk(t, F, Hv, Wv)
+        assert np.array_equal(G.host(P.debug(name + "_FP8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_MX"), np.uint8).reshape(o["c4"].shape), o["c4"]), name
+        assert np.array_equal(G.host(P.debug(name + "_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"]), name
+    o = O.quant_v(x, F, Hv, Wv)
+    assert np.array_equal(G.host(P.debug("V_FP8"), np.uint8).reshape(o["c8"].shape), o["c8"])
+    assert np.array_equal(G.host(P.debug("V_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"])
+    assert np.array_equal(G.host(P.debug("V_MX"), np.uint8).reshape(o["c4"].shape), o["c4"])
+    assert np.array_equal(G.host(P.debug("V_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"])
