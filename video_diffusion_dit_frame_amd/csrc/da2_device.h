@@ -37,39 +37,6 @@ __device__ __forceinline__ int key_of_row(int i, int m)
     return 32 * ((i >> 2) & 1) + 16 * m + 4 * (i >> 3) + (i & 3);
 }
 
-// ---------------------------------------------------------------------------
-// OCP FP8 E4M3 ("fn") encoder, round to nearest even, saturating at 448.
-// Works on the fp32 bit pattern: normals keep exponent and the top three
-// mantissa bits with an integer RNE on the rest; below 2^-6 the grid is
-// 2^-9, handled by an exact scale and rint.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint8_t enc_e4m3(float v)
-{
-    uint32_t u = __float_as_uint(v);
-    uint32_t s = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7fffffffu;
-    if (a >= 0x43e00000u)  // >= 448
-        return (uint8_t)(s | 0x7eu);
-    if (a < 0x3c800000u) {  // < 2^-6
-        float t = __uint_as_float(a) * 512.0f;
-        return (uint8_t)(s | (uint32_t)__builtin_rintf(t));
-    }
-    uint32_t m = a >> 20, rem = a & 0xfffffu;
-    m += (rem > 0x80000u) || (rem == 0x80000u && (m & 1u));
-    return (uint8_t)(s | (m - (120u << 3)));
-}
-
-// OCP E2M1 magnitude code of an exact non-negative value, nearest with ties to
-// the even code, saturating at 6: the grid 0, .5, 1, 1.5, 2, 3, 4, 6 has
-// midpoints .25 .75 1.25 1.75 2.5 3.5 5, and a tie goes up exactly when the
-// upper neighbour has the even code (.75, 1.75, 3.5).
-__device__ __forceinline__ uint32_t enc_e2m1_mag(double a)
-{
-    return (uint32_t)(a > 0.25) + (uint32_t)(a >= 0.75) + (uint32_t)(a > 1.25) +
-           (uint32_t)(a >= 1.75) + (uint32_t)(a > 2.5) + (uint32_t)(a >= 3.5) +
-           (uint32_t)(a > 5.0);
-}
-
 // floor(log2 x) for finite x > 0 (normal or subnormal fp32).
 __device__ __forceinline__ int floor_log2_f32(float x)
 {
@@ -90,12 +57,33 @@ __device__ __forceinline__ int mx_exponent(float amax)
     return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
-// E2M1 code (sign in bit 3) of x * 2^-E, computed exactly in fp64.
-__device__ __forceinline__ uint32_t enc_e2m1_scaled(float x, int E)
+// Four E4M3 codes (x0 in the low byte) from the hardware conversion: nearest
+// with ties to even, subnormals kept, sign kept on zero; inputs here never
+// exceed 448 by more than a rounding error, so no saturation is needed.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float x0, float x1, float x2, float x3)
 {
-    double a = __builtin_ldexp((double)__builtin_fabsf(x), -E);
-    uint32_t s = (__float_as_uint(x) >> 28) & 8u;
-    return s | enc_e2m1_mag(a);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+}
+
+// The fp32 value 2^E for an E8M0 exponent E in [-127, 127] (2^-127 is
+// subnormal).
+__device__ __forceinline__ float pow2_e8m0(int E)
+{
+    return E > -127 ? __uint_as_float((uint32_t)(E + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Eight E2M1 codes of x[j] / 2^E (x[0] in the low nibble) from the hardware
+// scaled conversion: the quotient by a power of two is exact, rounded to the
+// nearest code with ties to even, saturating at 6, sign kept on zero.
+__device__ __forceinline__ uint32_t pack_e2m1x8(const float *x, float scale)
+{
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], scale, 3);
+    return w;
 }
 
 // ---------------------------------------------------------------------------

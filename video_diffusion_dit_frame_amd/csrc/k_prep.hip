@@ -98,26 +98,18 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
         }
         uint32_t w8[8];
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                v |= (uint32_t)enc_e4m3(xv[4 * q + j] * inv) << (8 * j);
-            w8[q] = v;
-        }
+        for (int q = 0; q < 8; q++)
+            w8[q] = pack_e4m3x4(xv[4 * q] * inv, xv[4 * q + 1] * inv, xv[4 * q + 2] * inv,
+                                xv[4 * q + 3] * inv);
         uint4 *d8 = reinterpret_cast<uint4 *>(op8 + blk * (kBlk * D) + (int64_t)t * 32);
         d8[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
         d8[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
         const int E = mx_exponent(ga);
+        const float scale = pow2_e8m0(E);
         uint32_t w4[4];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                v |= enc_e2m1_scaled(xv[8 * q + j], E) << (4 * j);
-            w4[q] = v;
-        }
+        for (int q = 0; q < 4; q++)
+            w4[q] = pack_e2m1x8(xv + 8 * q, scale);
         *reinterpret_cast<uint4 *>(op4 + blk * (kBlk * D / 2) + (int64_t)t * 16) =
             make_uint4(w4[0], w4[1], w4[2], w4[3]);
         op4s[blk * (2 * D) + t] = (uint8_t)(E + 127);
@@ -199,26 +191,18 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
         }
         uint32_t w8[8];
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                v |= (uint32_t)enc_e4m3(xv[4 * q + j] * inv) << (8 * j);
-            w8[q] = v;
-        }
+        for (int q = 0; q < 8; q++)
+            w8[q] = pack_e4m3x4(xv[4 * q] * inv, xv[4 * q + 1] * inv, xv[4 * q + 2] * inv,
+                                xv[4 * q + 3] * inv);
         uint4 *d8 = reinterpret_cast<uint4 *>(op8 + blk * (kBlk * D) + (int64_t)t * 32);
         d8[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
         d8[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
         const int E = mx_exponent(ga);
+        const float scale = pow2_e8m0(E);
         uint32_t w4[4];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                v |= enc_e2m1_scaled(xv[8 * q + j], E) << (4 * j);
-            w4[q] = v;
-        }
+        for (int q = 0; q < 4; q++)
+            w4[q] = pack_e2m1x8(xv + 8 * q, scale);
         *reinterpret_cast<uint4 *>(op4 + blk * (kBlk * D / 2) + (int64_t)t * 16) =
             make_uint4(w4[0], w4[1], w4[2], w4[3]);
         op4s[blk * (2 * D) + t] = (uint8_t)(E + 127);
