@@ -134,8 +134,7 @@ __global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa
                     acc[g][h] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[g], bv[h], acc[g][h], 0, 0, 0);
         }
     }
-    // Store key-major (L^T[b][a], so the row passes read a row of logits
-    // as a coalesced column sweep) and fold the row maxima into rmax with an
+    // Store row-major and fold the row maxima into rmax with an
     // order-preserving integer atomic maximum.
     double *L = (maxb ? Lm : La) + (int64_t)bh * R * R;
     unsigned long long *rm = rmax + ((int64_t)bh * 2 + maxb) * R;
@@ -150,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa
                 const int j = b0 + 64 * wb + 16 * h + (l & 15);
                 const double v = acc[g][h][r] * inv_sqrt_d;
                 if (i < R && j < R) {
-                    L[(int64_t)j * R + i] = v;
+                    L[(int64_t)i * R + j] = v;
                     mx = fmax(mx, v);
                 }
             }
@@ -167,9 +166,9 @@ __global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa
 // ---------------------------------------------------------------------------
 // Row sums of one branch's exponentials for 64 query regions: Z is added
 // strictly in key order (Z = (((e_0 + e_1) + e_2) + ...)).  Per chunk of 64
-// key regions all four waves form the exponentials (lane = query region,
-// coalesced reads of the key-major logits) into LDS, then wave 0 adds its
-// lane's 64 values in order.
+// key regions all four waves form the exponentials (coalesced row reads)
+// into LDS, transposed, then wave 0 adds its lane's (row's) 64 values in
+// order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rowsum(const double *__restrict__ La,
                                                 const double *__restrict__ Lm, int R,
@@ -177,33 +176,36 @@ __global__ __launch_bounds__(256) void k_rowsum(const double *__restrict__ La,
                                                 double *__restrict__ zsum)
 {
     __shared__ double es[64][65];
+    __shared__ double mrow[64];
     const int a0 = blockIdx.x * 64, bh = blockIdx.y, br = blockIdx.z;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const int a = a0 + lane;
-    const int64_t row = ((int64_t)bh * 2 + br) * R + a;
-    const double m = a < R ? unord64(rmax[row]) : 0.0;
-    const double *L = (br ? Lm : La) + (int64_t)bh * R * R + a;
+    const int64_t rbase = ((int64_t)bh * 2 + br) * R + a0;
+    if (t < 64)
+        mrow[t] = a0 + t < R ? unord64(rmax[rbase + t]) : 0.0;
+    const double *L = (br ? Lm : La) + ((int64_t)bh * R + a0) * R;
     double z = 0.0;
+    __syncthreads();
     for (int b0 = 0; b0 < R; b0 += 64) {
-        const int nb = R - b0 < 64 ? R - b0 : 64;
+        const int b = b0 + lane;
 #pragma unroll 4
-        for (int k = wv; k < nb; k += 4)
-            es[k][lane] = a < R ? exp_draft(L[(int64_t)(b0 + k) * R] - m) : 0.0;
+        for (int r = wv; r < 64; r += 4)
+            es[lane][r] = (a0 + r < R && b < R) ? exp_draft(L[(int64_t)r * R + b] - mrow[r]) : 0.0;
         __syncthreads();
-        if (wv == 0)
+        if (wv == 0) {
+            const int nb = R - b0 < 64 ? R - b0 : 64;
             for (int k = 0; k < nb; k++)
                 z += es[k][lane];
+        }
         __syncthreads();
     }
-    if (wv == 0 && a < R)
-        zsum[row] = z;
+    if (wv == 0 && a0 + lane < R)
+        zsum[rbase + lane] = z;
 }
 
 // ---------------------------------------------------------------------------
-// Probabilities, mixture and ranking keys for a 64x64 tile of region pairs:
+// Probabilities, mixture and ranking keys, elementwise over region pairs:
 // p = e / Z per branch (e recomputed bit-identically), A = (1 - lambda) p_avg
-// + lambda p_max with separate products, key = bits(fp32(A)).  Logits are
-// read key-major and the keys written query-major through an LDS transpose.
+// + lambda p_max with separate products, key = bits(fp32(A)).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_keys(const double *__restrict__ La,
                                               const double *__restrict__ Lm, int R, double lambda,
@@ -211,39 +213,21 @@ __global__ __launch_bounds__(256) void k_keys(const double *__restrict__ La,
                                               const double *__restrict__ zsum,
                                               uint32_t *__restrict__ keys)
 {
-    __shared__ uint32_t kt[64][65];
-    __shared__ double ma[64], mm[64], za[64], zm[64];
-    const int a0 = blockIdx.x * 64, b0 = blockIdx.y * 64, bh = blockIdx.z, t = threadIdx.x;
-    if (t < 64 && a0 + t < R) {
-        const int64_t r = (int64_t)bh * 2 * R + a0 + t;
-        ma[t] = unord64(rmax[r]);
-        mm[t] = unord64(rmax[r + R]);
-        za[t] = zsum[r];
-        zm[t] = zsum[r + R];
-    }
-    __syncthreads();
+    const int a = blockIdx.y, bh = blockIdx.z;
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= R)
+        return;
+    const int64_t r = (int64_t)bh * 2 * R + a;
+    const double ma = unord64(rmax[r]), mm = unord64(rmax[r + R]);
+    const double za = zsum[r], zm = zsum[r + R];
+    const int64_t o = ((int64_t)bh * R + a) * R + b;
     const double w0 = 1.0 - lambda;
-    const double *LA = La + (int64_t)bh * R * R, *LM = Lm + (int64_t)bh * R * R;
-    for (int e = t; e < 64 * 64; e += 256) {
-        const int bb = e >> 6, aa = e & 63;
-        const int a = a0 + aa, b = b0 + bb;
-        if (a < R && b < R) {
-            const int64_t o = (int64_t)b * R + a;
-            const double pa = exp_draft(LA[o] - ma[aa]) / za[aa];
-            const double pm = exp_draft(LM[o] - mm[aa]) / zm[aa];
-            const double t0 = w0 * pa;
-            const double t1 = lambda * pm;
-            const double A = t0 + t1;
-            kt[aa][bb] = __float_as_uint((float)A);
-        }
-    }
-    __syncthreads();
-    for (int e = t; e < 64 * 64; e += 256) {
-        const int aa = e >> 6, bb = e & 63;
-        const int a = a0 + aa, b = b0 + bb;
-        if (a < R && b < R)
-            keys[((int64_t)bh * R + a) * R + b] = kt[aa][bb];
-    }
+    const double pa = exp_draft(La[o] - ma) / za;
+    const double pm = exp_draft(Lm[o] - mm) / zm;
+    const double t0 = w0 * pa;
+    const double t1 = lambda * pm;
+    const double A = t0 + t1;
+    keys[o] = __float_as_uint((float)A);
 }
 
 // ---------------------------------------------------------------------------
@@ -612,8 +596,8 @@ void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st
                                         (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
                                         L.R, inv_sqrt_d, La, Lm, rmax);
     k_rowsum<<<dim3(T, L.BH, 2), 256, 0, st>>>(La, Lm, L.R, rmax, zsum);
-    k_keys<<<dim3(T, T, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
-                                             (uint32_t *)(ws + W.keys));
+    k_keys<<<dim3((L.R + 255) / 256, L.R, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
+                                                               (uint32_t *)(ws + W.keys));
 }
 
 void launch_rank(const da2_layout_s &L, int scope, int64_t t8, int64_t tk, char *ws,
