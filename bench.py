@@ -38,7 +38,34 @@ def parse():
     ap.add_argument("--workload", default="wan14b-720p")
     ap.add_argument("--budget", type=int, default=0, help="index into the workload's budget list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain copy kernel of 1 GiB before the steps (reference for "
+                         "HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_wan14b-720p_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "video_diffusion_dit_frame_amd", "csrc", "k_attn.hip")
+
+
+def measured_traffic(workload, budget):
+    """HBM bytes per attention-kernel launch from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is none for this workload or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(ATTN_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload \
+            or rec.get("budget_index") != budget:
+        return None
+    return float(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(w, q, k, v, hi, lo):
@@ -105,6 +132,13 @@ def main():
         return t.permute(0, 2, 1, 3)              # [B, H, N, d] view
 
     qd, kd, vd = to_bnhd(q), to_bnhd(k), to_bnhd(v)
+    if args.calibrate_copy:
+        # a plain copy kernel: reads and writes exactly 2^30 bytes
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     o = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
     L = da2.Layout.for_tensor(qd, w.F, w.Hv, w.Wv)
     P = da2.Plan(L)
@@ -176,7 +210,7 @@ def main():
         "dense_equiv_tflops_attention_kernel": dense_flop / t_attn / 1e12,
         "tier_weighted_mfma_util": util,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_eff, "unit": "TFLOP/s",
-                     "frac": achieved / peak_eff, "traffic": None,
+                     "frac": achieved / peak_eff, "traffic": measured_traffic(w.name, args.budget),
                      "kernel": "k_attn", "peak_basis": "tier-weighted FP8 5.0 / FP4 10.1 PFLOP/s"},
     }
     if not args.no_cpu_baseline:
