@@ -228,3 +228,30 @@ def test_quantizers_exhaustive_bf16():
     assert np.array_equal(G.host(P.debug("V_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"])
     assert np.array_equal(G.host(P.debug("V_MX"), np.uint8).reshape(o["c4"].shape), o["c4"])
     assert np.array_equal(G.host(P.debug("V_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hi,lo", [(2500, 2500), (0, 0), (5000, 5000), (10000, 0), (0, 10000)])
+def test_degenerate_budgets_and_single_region(d, hi, lo):
+    """One region per head (R = 1) and a two-frame layer, at budgets that keep
+    nothing, everything, only FP8 or only MXFP4: tier maps bit-exact, outputs
+    within tolerance, rows without kept tiles exactly zero."""
+    for F, Hv, Wv in ((1, 8, 8), (2, 8, 16)):
+        q, k, v = G.inputs(1, 2, F, Hv, Wv, d, 31 + d + hi, True)
+        P, qd, kd = G.run_plan(q, k, F, Hv, Wv, hi, lo)
+        o = G.run_attention(P, qd, kd, v).cpu().numpy()
+        ref_plan = O.plan(q, k, F, Hv, Wv, hi, lo)
+        tier = P.tier_map().cpu().numpy()
+        assert np.array_equal(tier, ref_plan["tier"])
+        ref, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv)
+        if not (tier > 0).any():
+            assert (o == 0).all()
+            continue
+        G.check_kp(o, ref, allow, "F%d %dx%d d%d (%d,%d)" % (F, Hv, Wv, d, hi, lo))
+        perm = O.layout(F, Hv, Wv)
+        R = tier.shape[-1]
+        for b in range(tier.shape[0]):
+            for h in range(tier.shape[1]):
+                for a in range(R):
+                    if not (tier[b, h, a] > 0).any():
+                        assert (o[b, h, perm[a * 64:(a + 1) * 64]] == 0).all()
