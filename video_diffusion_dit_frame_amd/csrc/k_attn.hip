@@ -112,26 +112,51 @@ __device__ __forceinline__ v8i lds16(const uint8_t *p)
     return r;
 }
 
-// Copy UNITS kilobytes from global src to LDS dst with direct-to-LDS loads;
-// wave w of the two copies units w, w+2, ...  Each unit is one instruction:
-// 64 lanes x 16 bytes landing at dst + lane * 16.  The source address is a
-// wave-uniform base plus a 32-bit lane offset, so it needs no 64-bit vector
-// arithmetic.
+// Key/value operands of one head as buffer resources: a copy then addresses
+// its tile with one scalar offset and a fixed per-lane offset, with no
+// per-copy vector address arithmetic; reads past the head's bytes return 0.
+struct Src {
+    __amdgpu_buffer_rsrc_t k8, k4, k4s, v8, v4, v4s;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, 0x00020000);
+}
+
+template <int D>
+__device__ __forceinline__ Src head_sources(const AttnArgs &A, int64_t hbase, int R)
+{
+    Src s;
+    s.k8 = head_rsrc(A.k8 + hbase * (kBlk * D), (int64_t)R * kBlk * D);
+    s.k4 = head_rsrc(A.k4 + hbase * (kBlk * D / 2), (int64_t)R * kBlk * D / 2);
+    s.k4s = head_rsrc(A.k4s + hbase * (2 * D), (int64_t)R * 2 * D);
+    s.v8 = head_rsrc(A.v8 + hbase * (kBlk * D), (int64_t)R * kBlk * D);
+    s.v4 = head_rsrc(A.v4 + hbase * (kBlk * D / 2), (int64_t)R * kBlk * D / 2);
+    s.v4s = head_rsrc(A.v4s + hbase * (2 * D), (int64_t)R * 2 * D);
+    return s;
+}
+
+// Copy UNITS kilobytes at byte offset off of a resource to LDS dst with
+// direct-to-LDS buffer loads; wave w of the two copies units w, w+2, ...
+// Each unit is one instruction: 64 lanes x 16 bytes landing at dst + 16 l.
 template <int UNITS>
-__device__ __forceinline__ void copy_kb(const uint8_t *src, uint8_t *dst, int w, uint32_t loff16)
+__device__ __forceinline__ void copy_kb(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint8_t *dst, int w,
+                                        uint32_t loff16)
 {
 #pragma unroll
     for (int j = 0; j < UNITS / 2; j++) {
         const int u = 2 * j + w;
-        __builtin_amdgcn_global_load_lds((const void *)((src + u * 1024) + loff16),
-                                         (lds_void *)(dst + u * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + u * 1024), 16, loff16,
+                                                 off + u * 1024, 0, 0);
     }
 }
 
-// Copy 4 bytes per active lane with one direct-to-LDS load (lane l -> dst + 4 l).
-__device__ __forceinline__ void copy_dword(const uint8_t *src, uint8_t *dst, uint32_t loff4)
+// Copy 4 bytes per active lane (lane l -> dst + 4 l).
+__device__ __forceinline__ void copy_dword(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint8_t *dst,
+                                           uint32_t loff4)
 {
-    __builtin_amdgcn_global_load_lds((const void *)(src + loff4), (lds_void *)dst, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, loff4, off, 0, 0);
 }
 
 // LDS images.  Keys and values travel in separate double-buffered streams:
@@ -141,29 +166,30 @@ __device__ __forceinline__ void copy_dword(const uint8_t *src, uint8_t *dst, uin
 // of tile i.  Per buffer (D = head dim):
 //   FP8 key    [0, 64D)  codes                    value [0, 64D) codes
 //   MXFP4 key  [0, 32D)  codes, [32D, 34D) E8M0   value [0, 32D) codes, [32D, 34D) E8M0
+// kb is the key region inside the head.
 template <int D, bool FP8>
-__device__ __forceinline__ void issue_k(const AttnArgs &A, int64_t kblk, uint8_t *dst, int w, int l)
+__device__ __forceinline__ void issue_k(const Src &S, int kb, uint8_t *dst, int w, int l)
 {
     const uint32_t lo = (uint32_t)l;
     if (FP8) {
-        copy_kb<kBlk * D / 1024>(A.k8 + kblk * (kBlk * D), dst, w, lo * 16u);
+        copy_kb<kBlk * D / 1024>(S.k8, (uint32_t)kb * (kBlk * D), dst, w, lo * 16u);
     } else {
-        copy_kb<kBlk * D / 2048>(A.k4 + kblk * (kBlk * D / 2), dst, w, lo * 16u);
+        copy_kb<kBlk * D / 2048>(S.k4, (uint32_t)kb * (kBlk * D / 2), dst, w, lo * 16u);
         if (w == 0 && l * 4 < 2 * D)
-            copy_dword(A.k4s + kblk * (2 * D), dst + 32 * D, lo * 4u);
+            copy_dword(S.k4s, (uint32_t)kb * (2 * D), dst + 32 * D, lo * 4u);
     }
 }
 
 template <int D, bool FP8>
-__device__ __forceinline__ void issue_v(const AttnArgs &A, int64_t kblk, uint8_t *dst, int w, int l)
+__device__ __forceinline__ void issue_v(const Src &S, int kb, uint8_t *dst, int w, int l)
 {
     const uint32_t lo = (uint32_t)l;
     if (FP8) {
-        copy_kb<kBlk * D / 1024>(A.v8 + kblk * (kBlk * D), dst, w, lo * 16u);
+        copy_kb<kBlk * D / 1024>(S.v8, (uint32_t)kb * (kBlk * D), dst, w, lo * 16u);
     } else {
-        copy_kb<kBlk * D / 2048>(A.v4 + kblk * (kBlk * D / 2), dst, w, lo * 16u);
+        copy_kb<kBlk * D / 2048>(S.v4, (uint32_t)kb * (kBlk * D / 2), dst, w, lo * 16u);
         if (w == 1 && l * 4 < 2 * D)
-            copy_dword(A.v4s + kblk * (2 * D), dst + 32 * D, lo * 4u);
+            copy_dword(S.v4s, (uint32_t)kb * (2 * D), dst + 32 * D, lo * 4u);
     }
 }
 
@@ -347,6 +373,7 @@ struct Attn {
     uint8_t (&vbuf)[2][kBlk * D];
     const int32_t *list;
     int64_t hbase;
+    Src src;
     int n8, n, w, l;
     float qs;
     v8i q8[KC], q4[KC];
@@ -374,18 +401,16 @@ struct Attn {
     {
         // refill the buffers read last tile: key of tile i+2, value of tile i+1
         if (i + 2 < n) {
-            const int64_t kb = hbase + kb_k;
             if (FP8 && i + 2 < n8)
-                issue_k<D, true>(A, kb, kbuf[i & 1], w, l);
+                issue_k<D, true>(src, kb_k, kbuf[i & 1], w, l);
             else
-                issue_k<D, false>(A, kb, kbuf[i & 1], w, l);
+                issue_k<D, false>(src, kb_k, kbuf[i & 1], w, l);
         }
         if (i + 1 < n) {
-            const int64_t kb = hbase + kb_v;
             if (FP8 && i + 1 < n8)
-                issue_v<D, true>(A, kb, vbuf[(i + 1) & 1], w, l);
+                issue_v<D, true>(src, kb_v, vbuf[(i + 1) & 1], w, l);
             else
-                issue_v<D, false>(A, kb, vbuf[(i + 1) & 1], w, l);
+                issue_v<D, false>(src, kb_v, vbuf[(i + 1) & 1], w, l);
         }
     }
 
@@ -486,6 +511,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     S.n = n;
     S.list = A.sched + qblk * R;
     S.hbase = (int64_t)bh * R;
+    S.src = head_sources<D>(A, S.hbase, R);
 #pragma unroll
     for (int cb = 0; cb < CB; cb++)
         S.acc[cb] = (v16f){};
@@ -495,24 +521,24 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     v16f sa[2], sb[2];
     if (n > 0) {
         // prologue: key and value of tile 0, key of tile 1; logits of tile 0
-        const int64_t kb0 = S.hbase + sload_i32(S.list);
+        const int kb0 = sload_i32(S.list);
         if (n8 > 0) {
-            issue_k<D, true>(A, kb0, kbuf[0], w, l);
-            issue_v<D, true>(A, kb0, vbuf[0], w, l);
+            issue_k<D, true>(S.src, kb0, kbuf[0], w, l);
+            issue_v<D, true>(S.src, kb0, vbuf[0], w, l);
         } else {
-            issue_k<D, false>(A, kb0, kbuf[0], w, l);
-            issue_v<D, false>(A, kb0, vbuf[0], w, l);
+            issue_k<D, false>(S.src, kb0, kbuf[0], w, l);
+            issue_v<D, false>(S.src, kb0, vbuf[0], w, l);
         }
         if (n > 1) {
-            const int64_t kb1 = S.hbase + sload_i32(S.list + 1);
+            const int kb1 = sload_i32(S.list + 1);
             if (n8 > 1)
-                issue_k<D, true>(A, kb1, kbuf[1], w, l);
+                issue_k<D, true>(S.src, kb1, kbuf[1], w, l);
             else
-                issue_k<D, false>(A, kb1, kbuf[1], w, l);
+                issue_k<D, false>(S.src, kb1, kbuf[1], w, l);
         }
         S.kb_v = n > 1 ? sload_i32(S.list + 1) : 0;
         S.kb_k = n > 2 ? sload_i32(S.list + 2) : 0;
-        S.c8 = n8 > 0 ? (S.qs * sload_f32(A.ks8 + kb0)) * A.c4 : 0.0f;
+        S.c8 = n8 > 0 ? (S.qs * sload_f32(A.ks8 + S.hbase + kb0)) * A.c4 : 0.0f;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (n8 > 0)
