@@ -249,19 +249,23 @@ void or_draft_logits_head(const double *qa, const double *ka, const float *qm,
 /* ------------------------------------------------------------------ */
 /* O6 quotas: [DA2] Sec. 3.1 (T = T16 + T8 + T4), App. C.1 (integer     */
 /* quotas from precision fractions).  Budgets in basis points of n      */
-/* (n = R^2 for head scope, R for row scope), rounded half up.          */
+/* (n = R^2 for head scope, R for row scope); the cumulative counts     */
+/* T16, T16 + T8 and T16 + T8 + T4 are each rounded half up.            */
 /* ------------------------------------------------------------------ */
-void or_quotas(int64_t n, int32_t hi_bp, int32_t lo_bp, int64_t *T8, int64_t *Tk)
+void or_quotas(int64_t n, int32_t full_bp, int32_t hi_bp, int32_t lo_bp, int64_t *T16,
+               int64_t *T8c, int64_t *Tk)
 {
-    *T8 = ((int64_t)hi_bp * n + 5000) / 10000;
-    *Tk = ((int64_t)(hi_bp + lo_bp) * n + 5000) / 10000;
+    *T16 = ((int64_t)full_bp * n + 5000) / 10000;
+    *T8c = ((int64_t)(full_bp + hi_bp) * n + 5000) / 10000;
+    *Tk = ((int64_t)(full_bp + hi_bp + lo_bp) * n + 5000) / 10000;
 }
 
 /* ------------------------------------------------------------------ */
-/* O7 ranking: [DA2] Sec. 3.1 (ranking across the whole map of a head), */
-/* App. C.1 (ties by region-pair index), Sec. 3.2 (larger score ->      */
-/* higher precision).  Order = key descending, pair index ascending;    */
-/* rank < T8 -> tier 8, rank < Tk -> tier 4, else 0 (skip).             */
+/* O7 ranking: [DA2] Sec. 3.1 (ranking across the whole map of a head;  */
+/* larger masses to higher precision: the 16-bit path for the T16       */
+/* largest, 8-bit for the next T8, 4-bit for the next T4), App. C.1     */
+/* (ties by region-pair index).  Order = key descending, pair index     */
+/* ascending; rank < T16 -> 16, < T16+T8 -> 8, < Tk -> 4, else 0 (skip).*/
 /* scope 0: one ranking over all R^2 pairs; scope 1: one per query row. */
 /* ------------------------------------------------------------------ */
 static int cmp_u64(const void *x, const void *y)
@@ -270,7 +274,12 @@ static int cmp_u64(const void *x, const void *y)
     return (a > b) - (a < b);
 }
 
-void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T8, int64_t Tk,
+static uint8_t tier_of_rank(int64_t r, int64_t T16, int64_t T8c, int64_t Tk)
+{
+    return r < T16 ? 16 : (r < T8c ? 8 : (r < Tk ? 4 : 0));
+}
+
+void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T16, int64_t T8c, int64_t Tk,
                   uint8_t *tier)
 {
     int64_t n = (int64_t)R * R;
@@ -282,7 +291,7 @@ void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T8, int64_t Tk
         qsort(ord, (size_t)n, sizeof(uint64_t), cmp_u64);
         for (int64_t r = 0; r < n; r++) {
             uint32_t idx = (uint32_t)(ord[r] & 0xffffffffu);
-            tier[idx] = r < T8 ? 8 : (r < Tk ? 4 : 0);
+            tier[idx] = tier_of_rank(r, T16, T8c, Tk);
         }
         free(ord);
     } else {
@@ -293,7 +302,7 @@ void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T8, int64_t Tk
             qsort(ord, (size_t)R, sizeof(uint64_t), cmp_u64);
             for (int r = 0; r < R; r++) {
                 uint32_t b = (uint32_t)(ord[r] & 0xffffffffu);
-                tier[(size_t)a * R + b] = r < T8 ? 8 : (r < Tk ? 4 : 0);
+                tier[(size_t)a * R + b] = tier_of_rank(r, T16, T8c, Tk);
             }
         }
         free(ord);
@@ -306,7 +315,7 @@ void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T8, int64_t Tk
 /* keys and tier): avg [B,H,R,d] fp64 (Q then K arrays), mx f32.         */
 /* ------------------------------------------------------------------ */
 int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
-            const uint16_t *k, int32_t hi_bp, int32_t lo_bp, double lambda, int scope,
+            const uint16_t *k, int32_t full_bp, int32_t hi_bp, int32_t lo_bp, double lambda, int scope,
             uint32_t *keys, uint8_t *tier, double *qavg, double *kavg, float *qmx,
             float *kmx)
 {
@@ -316,8 +325,8 @@ int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
         free(perm);
         return -1;
     }
-    int64_t T8, Tk;
-    or_quotas(scope == 0 ? (int64_t)R * R : (int64_t)R, hi_bp, lo_bp, &T8, &Tk);
+    int64_t T16, T8c, Tk;
+    or_quotas(scope == 0 ? (int64_t)R * R : (int64_t)R, full_bp, hi_bp, lo_bp, &T16, &T8c, &Tk);
     double *qa = malloc(sizeof(double) * (size_t)R * d), *ka = malloc(sizeof(double) * (size_t)R * d);
     float *qm = malloc(sizeof(float) * (size_t)R * d), *km = malloc(sizeof(float) * (size_t)R * d);
     for (int bh = 0; bh < B * H; bh++) {
@@ -332,7 +341,7 @@ int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
     }
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < B * H; bh++)
-        or_rank_head(keys + (size_t)bh * R * R, R, scope, T8, Tk, tier + (size_t)bh * R * R);
+        or_rank_head(keys + (size_t)bh * R * R, R, scope, T16, T8c, Tk, tier + (size_t)bh * R * R);
     free(qa); free(ka); free(qm); free(km); free(perm);
     return 0;
 }
@@ -403,6 +412,25 @@ uint8_t or_e2m1_encode(double v)
     E = e - 1;
     int m = (int)ldexp(r, 1 - E) - 2;    /* r = (1 + m/2) 2^E */
     return sgn | (uint8_t)(((E + 1) << 1) | m);
+}
+
+/* bfloat16 rounding of a double (8 significant bits, exponent range of
+ * binary32 with its subnormals down to 2^-133), nearest with ties to even;
+ * returns the rounded value.  The weights it is used on are finite and at
+ * most 2^8, far below the bfloat16 maximum. */
+double or_bf16_round(double v)
+{
+    double a = fabs(v);
+    if (a == 0.0)
+        return v;
+    int e;
+    frexp(a, &e);
+    int E = e - 1;                       /* floor(log2 a) */
+    if (E < -126)
+        E = -126;                        /* subnormal spacing 2^-133 */
+    double q = ldexp(1.0, E - 7);
+    double r = rint(a / q) * q;          /* a / q exact: a power-of-two quotient */
+    return signbit(v) ? -r : r;
 }
 
 /* E8M0 exponent of an MX block: floor(log2 amax) - 2 (2 = exponent of the
@@ -556,9 +584,11 @@ int or_quant_v(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
 /* accumulator), App. B.3 (w = e^{s - h}, Z^q = sum of unquantized w),  */
 /* App. B.4 (O = sum(w_hat V_hat) / Z^q), App. C.1 (rows with no        */
 /* retained key return zero).                                           */
-/* Phases in descending precision: tier 16 (oracle-only, unquantized    */
-/* operands and weights), tier 8 (FP8), tier 4 (MXFP4); tiles ascending */
-/* inside a phase; running max updated once per 64-key tile.            */
+/* Phases in descending precision: tier 32 (oracle-only: unquantized    */
+/* operands and weights, for the invariants), tier 16 (the 16-bit path: */
+/* the bf16 inputs as they are, weights rounded to bf16 for P V), tier  */
+/* 8 (FP8), tier 4 (MXFP4); tiles ascending inside a phase; running max */
+/* updated once per 64-key tile.                                        */
 /* ------------------------------------------------------------------ */
 typedef struct {
     int N, d, R;
@@ -632,8 +662,10 @@ static void head_ops_free(head_ops *h)
 /* Weight quantizers for one 64-key tile, w[64] in key order. */
 static void quant_weights(int tier, const double *w, double *wq)
 {
-    if (tier == 16) {
+    if (tier == 32) {
         for (int j = 0; j < OR_BLK; j++) wq[j] = w[j];
+    } else if (tier == 16) {
+        for (int j = 0; j < OR_BLK; j++) wq[j] = or_bf16_round(w[j]);
     } else if (tier == 8) {
         for (int j = 0; j < OR_BLK; j++)
             wq[j] = ldexp(or_e4m3_value(or_e4m3_encode(ldexp(w[j], 8))), -8);
@@ -668,12 +700,12 @@ static void attention_row(const head_ops *h, const uint8_t *tier_row, int u,
     double m = -INFINITY, Z = 0.0;
     double *acc = calloc(d, sizeof(double));
     double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
-    static const int phases[3] = {16, 8, 4};
-    for (int ph = 0; ph < 3; ph++) {
+    static const int phases[4] = {32, 16, 8, 4};
+    for (int ph = 0; ph < 4; ph++) {
         int p = phases[ph];
-        const double *Q = p == 16 ? h->qf : (p == 8 ? h->q8 : h->q4);
-        const double *K = p == 16 ? h->kf : (p == 8 ? h->k8 : h->k4);
-        const double *V = p == 16 ? h->vf : (p == 8 ? h->v8 : h->v4);
+        const double *Q = p >= 16 ? h->qf : (p == 8 ? h->q8 : h->q4);
+        const double *K = p >= 16 ? h->kf : (p == 8 ? h->k8 : h->k4);
+        const double *V = p >= 16 ? h->vf : (p == 8 ? h->v8 : h->v4);
         for (int b = 0; b < R; b++) {
             if (tier_row[b] != p)
                 continue;
@@ -839,6 +871,10 @@ static float ulpf(float x)
 /* Quantized weight (in units of 256 w) of e for the FP8 tier. */
 static double q8_val(double e) { return or_e4m3_value(or_e4m3_encode(e)); }
 
+/* ... for the 16-bit tier: e in fp32 rounded to bf16 (binary32 -> bf16
+ * nearest even is one rounding of the double holding the fp32 value). */
+static double q16_val(double e) { return or_bf16_round(e); }
+
 /* ... and for the MXFP4 tier with block exponent Ep (same units). */
 static double q4_val(double e, int Ep) { return ldexp(or_e2m1_value(or_e2m1_encode(ldexp(e, -Ep))), Ep); }
 
@@ -856,20 +892,38 @@ static void attention_row_kp(const head_ops *h, const uint8_t *tier_row, int u,
 {
     int d = h->d, R = h->R, a = u / OR_BLK;
     const float c4 = (float)(1.4426950408889634 / sqrt((double)d));
-    const double kPV8 = ldexp(1.0, -10), kPV4 = ldexp(1.0, -20), kExp = ldexp(1.0, -21);
+    const double kPV8 = ldexp(1.0, -10), kPV4 = ldexp(1.0, -20), kPV16 = ldexp(1.0, -20);
+    const double kExp = ldexp(1.0, -21);
     float m = -INFINITY;
     double Z = 0.0;
     double *acc = calloc(d, sizeof(double)), *al = calloc(d, sizeof(double));
     float S[OR_BLK];
     double dS[OR_BLK];
-    static const int phases[2] = {8, 4};
-    for (int ph = 0; ph < 2; ph++) {
+    static const int phases[3] = {16, 8, 4};
+    for (int ph = 0; ph < 3; ph++) {
         int p = phases[ph];
         for (int b = 0; b < R; b++) {
             if (tier_row[b] != p)
                 continue;
             float cf;
-            if (p == 8) {
+            if (p == 16) {
+                /* bf16 products are exact in binary32; the matrix core sums
+                 * each 16-channel step exactly and accumulates the steps in
+                 * fp32: modelled as the exact dot rounded once, with the
+                 * accumulation rounding in the allowance */
+                cf = c4;
+                const double *qr = h->qf + (size_t)u * d;
+                for (int j = 0; j < OR_BLK; j++) {
+                    const double *kr = h->kf + ((size_t)b * OR_BLK + j) * d;
+                    double sx = 0.0, mag = 0.0;
+                    for (int c = 0; c < d; c++) {
+                        sx += qr[c] * kr[c];
+                        mag += fabs(qr[c] * kr[c]);
+                    }
+                    S[j] = (float)sx;
+                    dS[j] = ldexp(mag, -21) + 2.0 * ulpf(S[j]);
+                }
+            } else if (p == 8) {
                 cf = (h->s8q[a] * h->s8k[b]) * c4;
                 const uint8_t *qr = h->c8q + (size_t)u * d;
                 for (int j = 0; j < OR_BLK; j++) {
@@ -918,8 +972,20 @@ static void attention_row_kp(const head_ops *h, const uint8_t *tier_row, int u,
                 e[j] = (double)(float)exp2((double)t);
                 eta[j] = kExp + 0.6931471805599453 * (double)cf * (dS[j] + dSmax);
             }
-            const double *V = p == 8 ? h->v8 : h->v4;
-            if (p == 8) {
+            const double *V = p == 16 ? h->vf : (p == 8 ? h->v8 : h->v4);
+            if (p == 16) {
+                for (int j = 0; j < OR_BLK; j++) {
+                    double val = q16_val(e[j]);
+                    double lo = q16_val(e[j] * (1.0 - eta[j])), hi = q16_val(e[j] * (1.0 + eta[j]));
+                    double dv = fmax(hi - val, val - lo);
+                    const double *vv = V + ((size_t)b * OR_BLK + j) * d;
+                    Z += e[j];
+                    for (int c = 0; c < d; c++) {
+                        acc[c] += val * vv[c];
+                        al[c] += (dv + kPV16 * fabs(val)) * fabs(vv[c]);
+                    }
+                }
+            } else if (p == 8) {
                 /* scale of V is applied per channel: dequantized V already has it */
                 for (int j = 0; j < OR_BLK; j++) {
                     double val = q8_val(e[j]);
@@ -987,7 +1053,7 @@ static void attention_row_kp(const head_ops *h, const uint8_t *tier_row, int u,
     free(al);
 }
 
-/* Kernel-precision variant of or_attention (tiers 8 and 4 only; other values
+/* Kernel-precision variant of or_attention (tiers 16, 8 and 4; other values
  * skip).  allow: per-element bound on what the undetermined decisions and the
  * matrix-core accumulation of P V can move the result, same layout as out. */
 int or_attention_kp(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,

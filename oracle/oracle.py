@@ -54,9 +54,11 @@ def lib():
         L.or_exp.restype = f64
         L.or_draft_keys_head.argtypes = [P, P, P, P, C.c_int, C.c_int, f64, P, P]
         L.or_draft_logits_head.argtypes = [P, P, P, P, C.c_int, C.c_int, P, P]
-        L.or_quotas.argtypes = [i64, i32, i32, P, P]
-        L.or_rank_head.argtypes = [P, C.c_int, C.c_int, i64, i64, P]
-        L.or_plan.argtypes = [C.c_int] * 6 + [P, P, i32, i32, f64, C.c_int, P, P, P, P, P, P]
+        L.or_quotas.argtypes = [i64, i32, i32, i32, P, P, P]
+        L.or_bf16_round.argtypes = [f64]
+        L.or_bf16_round.restype = f64
+        L.or_rank_head.argtypes = [P, C.c_int, C.c_int, i64, i64, i64, P]
+        L.or_plan.argtypes = [C.c_int] * 6 + [P, P, i32, i32, i32, f64, C.c_int, P, P, P, P, P, P]
         L.or_plan.restype = C.c_int
         L.or_e4m3_value.argtypes = [C.c_int]
         L.or_e4m3_value.restype = f64
@@ -156,23 +158,33 @@ def draft_logits_head(qa, ka, qm, km):
     return La, Lm
 
 
+def quotas3(n, full_bp, hi_bp, lo_bp):
+    """Cumulative quotas (T16, T16 + T8, T16 + T8 + T4) of n pairs."""
+    t16, t8c, tk = C.c_int64(), C.c_int64(), C.c_int64()
+    lib().or_quotas(int(n), int(full_bp), int(hi_bp), int(lo_bp), C.byref(t16), C.byref(t8c),
+                    C.byref(tk))
+    return t16.value, t8c.value, tk.value
+
+
 def quotas(n, hi_bp, lo_bp):
-    t8 = C.c_int64()
-    tk = C.c_int64()
-    lib().or_quotas(int(n), int(hi_bp), int(lo_bp), C.byref(t8), C.byref(tk))
-    return t8.value, tk.value
+    """(T8, T8 + T4) with no 16-bit share."""
+    _, t8, tk = quotas3(n, 0, hi_bp, lo_bp)
+    return t8, tk
 
 
-def rank_head(keys: np.ndarray, T8, Tk, scope=0) -> np.ndarray:
+def rank_head(keys: np.ndarray, T8, Tk, scope=0, T16=0) -> np.ndarray:
+    """Tiers of one head's [R,R] keys; T8 and Tk are cumulative counts
+    (T16 + T8, T16 + T8 + T4)."""
     keys = np.ascontiguousarray(keys, np.uint32)
     R = keys.shape[0]
     tier = np.empty((R, R), np.uint8)
-    lib().or_rank_head(_p(keys), R, int(scope), int(T8), int(Tk), _p(tier))
+    lib().or_rank_head(_p(keys), R, int(scope), int(T16), int(T8), int(Tk), _p(tier))
     return tier
 
 
-def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False):
-    """Full plan for [B,H,N,d] inputs -> dict(keys [B,H,R,R] u32, tier u8, ...)."""
+def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False, full_bp=0):
+    """Full plan for [B,H,N,d] inputs -> dict(keys [B,H,R,R] u32, tier u8, ...).
+    full_bp: share of the 16-bit tier (basis points)."""
     q = _u16(q)
     k = _u16(k)
     B, H, N, d = q.shape
@@ -187,7 +199,7 @@ def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False):
         out["qmax"] = np.empty((B, H, R, d), np.float32)
         out["kmax"] = np.empty((B, H, R, d), np.float32)
         ptrs = [_p(out[n]) for n in ("qavg", "kavg", "qmax", "kmax")]
-    rc = lib().or_plan(B, H, F, Hv, Wv, d, _p(q), _p(k), int(hi_bp), int(lo_bp), float(lam),
+    rc = lib().or_plan(B, H, F, Hv, Wv, d, _p(q), _p(k), int(full_bp), int(hi_bp), int(lo_bp), float(lam),
                        int(scope), _p(keys), _p(tier), *ptrs)
     if rc:
         raise ValueError("bad shape")
@@ -195,6 +207,10 @@ def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False):
 
 
 # ---------------------------------------------------------------- formats
+def bf16_round(x: float) -> float:
+    return lib().or_bf16_round(float(x))
+
+
 def e4m3_value(code: int) -> float:
     return lib().or_e4m3_value(int(code))
 

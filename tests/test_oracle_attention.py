@@ -1,6 +1,6 @@
 """Pins of the oracle's tiered attention (CPU).
 
-* an oracle-only full-precision tier (16) over every tile equals dense
+* an oracle-only full-precision tier (32) over every tile equals dense
   softmax attention (textbook closed form, numpy);
 * with skipped tiles the full-precision result equals brute-force masked
   attention, rows with no kept key are zero (App. C.1), and the
@@ -56,7 +56,7 @@ def token_mask(orc, tier_rr):
 def test_full_tier_equals_dense(orc, qkv):
     q, k, v = qkv
     R = q.shape[2] // 64
-    tier = np.full((1, 2, R, R), 16, np.uint8)
+    tier = np.full((1, 2, R, R), 32, np.uint8)
     out = orc.attention(q, k, v, tier, F, HV, WV)
     for h in range(2):
         want, _ = dense_np(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]))
@@ -70,7 +70,7 @@ def test_full_tier_masked_equals_brute_force(orc, qkv):
     q, k, v = qkv
     R = q.shape[2] // 64
     rng = np.random.default_rng(4)
-    tier = np.where(rng.random((1, 2, R, R)) < 0.4, 16, 0).astype(np.uint8)
+    tier = np.where(rng.random((1, 2, R, R)) < 0.4, 32, 0).astype(np.uint8)
     tier[0, 0, 3, :] = 0  # an empty query region
     out = orc.attention(q, k, v, tier, F, HV, WV)
     for h in range(2):
@@ -86,8 +86,8 @@ def test_constant_values_give_constant_output(orc, qkv):
     v = np.full_like(q, 0x3FC0)  # 1.5
     R = q.shape[2] // 64
     rng = np.random.default_rng(8)
-    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 16, 0).astype(np.uint8)
-    tier[..., 0] = 16
+    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 32, 0).astype(np.uint8)
+    tier[..., 0] = 32
     out = orc.attention(q, k, v, tier, F, HV, WV)
     assert np.abs(out - 1.5).max() <= 1e-13
 
@@ -97,8 +97,8 @@ def test_sparsification_bound_eq4(orc, qkv):
     q, k, v = qkv
     R = q.shape[2] // 64
     rng = np.random.default_rng(12)
-    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 16, 0).astype(np.uint8)
-    tier[..., 0] = 16
+    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 32, 0).astype(np.uint8)
+    tier[..., 0] = 32
     out = orc.attention(q, k, v, tier, F, HV, WV)
     for h in range(2):
         Q, K, V = f64(q[0, h]), f64(k[0, h]), f64(v[0, h])
@@ -114,7 +114,7 @@ def test_frame_relabelling_invariance(orc, qkv):
     q, k, v = qkv
     R = q.shape[2] // 64
     rng = np.random.default_rng(2)
-    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 16, 0).astype(np.uint8)
+    tier = np.where(rng.random((1, 2, R, R)) < 0.5, 32, 0).astype(np.uint8)
     out = orc.attention(q, k, v, tier, F, HV, WV)
     # swap the two frames: token blocks and region ids move together
     N1 = HV * WV
@@ -146,19 +146,26 @@ def test_quantized_tile_loop_from_trace(orc, qkv, u):
     q, k, v = qkv
     R = q.shape[2] // 64
     rng = np.random.default_rng(u)
-    tier = rng.choice(np.array([0, 4, 8], np.uint8), size=(1, 2, R, R), p=[0.4, 0.35, 0.25])
+    tier = rng.choice(np.array([0, 4, 8, 16], np.uint8), size=(1, 2, R, R), p=[0.3, 0.3, 0.2, 0.2])
     tr = orc.attention_trace(q[0, 0], k[0, 0], v[0, 0], tier[0, 0], F, HV, WV, u)
     ops = _deq(orc, q, k, v)
+    perm = orc.layout(F, HV, WV)
+    full = {n: f64(x[0, 0])[perm] for n, x in (("q", q), ("k", k), ("v", v))}
     a = u // 64
     row = tier[0, 0, a]
-    # phase order: all FP8 tiles ascending, then all MXFP4 tiles ascending
-    order = [b for b in range(R) if row[b] == 8] + [b for b in range(R) if row[b] == 4]
+    # phase order: 16-bit tiles ascending, then FP8 ascending, then MXFP4 ascending
+    order = [b for p_ in (16, 8, 4) for b in range(R) if row[b] == p_]
     assert np.array_equal(tr["key"], np.concatenate([np.arange(b * 64, b * 64 + 64) for b in order]))
     assert np.array_equal(tr["tier"], np.repeat([row[b] for b in order], 64))
     p = tr["tier"]
-    Q = np.where(p[:, None] == 8, ops["q8"][u][None, :], ops["q4"][u][None, :])
-    K = np.where(p[:, None] == 8, ops["k8"][tr["key"]], ops["k4"][tr["key"]])
-    V = np.where(p[:, None] == 8, ops["v8"][tr["key"]], ops["v4"][tr["key"]])
+
+    def pick(name, idx):
+        return np.where(p[:, None] == 16, full[name][idx],
+                        np.where(p[:, None] == 8, ops[name + "8"][idx], ops[name + "4"][idx]))
+
+    Q = pick("q", np.full(p.size, u))
+    K = pick("k", tr["key"])
+    V = pick("v", tr["key"])
     s = (Q * K).sum(axis=1) / math.sqrt(D)
     assert np.allclose(tr["s"], s, rtol=1e-13, atol=1e-13)
     tile_max = tr["s"].reshape(-1, 64).max(axis=1)
@@ -170,7 +177,20 @@ def test_quantized_tile_loop_from_trace(orc, qkv, u):
     wq = tr["wq"].reshape(-1, 64)
     val8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
     for t in range(w.shape[0]):
-        if p[t * 64] == 8:
+        if p[t * 64] == 16:
+            # bfloat16 of each weight (w is exactly an fp32 value here only by
+            # chance, so compare against the nearest of the two bf16
+            # neighbours found by bracketing, ties to the even mantissa)
+            m_, e_ = np.frexp(w[t])
+            lo = np.floor(m_ * 256.0)
+            hi_ = lo + 1.0
+            d_lo, d_hi = m_ * 256.0 - lo, hi_ - m_ * 256.0
+            pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
+            ref = np.where(pick_hi, hi_, lo) * np.exp2(e_ - 8.0)
+            sub = w[t] < 2.0 ** -126  # bf16 subnormals: quantum 2^-133
+            ref = np.where(sub, np.rint(w[t] * 2.0 ** 133) * 2.0 ** -133, ref)
+            assert np.array_equal(wq[t], ref)
+        elif p[t * 64] == 8:
             codes = brute_nearest(w[t] * 256.0, val8[:127])
             assert np.array_equal(wq[t], val8[codes] / 256.0)
         else:
@@ -214,7 +234,7 @@ def test_zero_skip_error_within_quantization_envelope(orc, qkv):
     the B.4 terms built from actual reconstruction residuals."""
     q, k, v = qkv
     R = q.shape[2] // 64
-    for t in (8, 4):
+    for t in (16, 8, 4):
         tier = np.full((1, 2, R, R), t, np.uint8)
         for u in (17, 300):
             tr = orc.attention_trace(q[0, 0], k[0, 0], v[0, 0], tier[0, 0], F, HV, WV, u)
@@ -223,7 +243,7 @@ def test_zero_skip_error_within_quantization_envelope(orc, qkv):
             Kf = f64(k[0, 0])[perm][tr["key"]]
             Vf = f64(v[0, 0])[perm][tr["key"]]
             ops = _deq(orc, q, k, v)
-            V = ops["v%d" % t][tr["key"]]
+            V = Vf if t == 16 else ops["v%d" % t][tr["key"]]
             mf = tr["m"][-1]
             z = np.exp(Kf @ Qf / math.sqrt(D) - mf)
             Od = (z[:, None] * Vf).sum(0) / z.sum()

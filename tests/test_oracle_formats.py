@@ -135,3 +135,20 @@ def test_mx_exponent_closed_form(orc):
     for a in [1.0, 1.999, 3.0, 1e-3, 7e5]:
         E = orc.mx_exponent(a)
         assert 4.0 <= a * 2.0 ** -E < 8.0
+
+
+def test_bf16_round_matches_torch_cast(orc):
+    """The oracle's bfloat16 rounding of binary32 values equals PyTorch's
+    float32 -> bfloat16 conversion (nearest, ties to even): random bit
+    patterns across the normal and subnormal range, exact midpoints, and
+    values just beside them."""
+    rng = np.random.default_rng(4)
+    u = rng.integers(0, 0x7F800000, size=20000, dtype=np.uint32)           # finite positives
+    mid = (rng.integers(0, 0x7F7F, size=2000, dtype=np.uint32) << 16) | 0x8000  # exact ties
+    near = np.concatenate([mid - 1, mid + 1])
+    bits = np.concatenate([u, mid, near, np.array([1, 0x00400000, 0x007FFFFF, 0x00800000], np.uint32)])
+    bits = np.concatenate([bits, bits | 0x80000000])
+    x = bits.view(np.float32)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([orc.bf16_round(float(v)) for v in x])
+    assert np.array_equal(got, ref)

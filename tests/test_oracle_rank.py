@@ -82,3 +82,34 @@ def test_rank_larger_scores_get_higher_precision(orc):
     t = orc.rank_head(keys, T8, Tk, 0)
     assert A[t == 8].min() >= A[t == 4].max()
     assert A[t == 4].min() >= A[t == 0].max()
+
+
+@pytest.mark.parametrize("scope", [0, 1])
+def test_rank_three_tiers_matches_lexsort(orc, scope):
+    """16-bit, FP8 and MXFP4 tiers from one ranking: the T16 largest keys
+    (ties by ascending index) get 16, the next T8 get 8, the next T4 get 4."""
+    rng = np.random.default_rng(11 + scope)
+    R = 24
+    keys = rng.integers(0, 40, size=(R, R)).astype(np.uint32)  # many ties
+    n = R * R if scope == 0 else R
+    T16, T8c, Tk = orc.quotas3(n, 1200, 2000, 3500)
+    got = orc.rank_head(keys, T8c, Tk, scope, T16=T16)
+    rows = [np.arange(R * R)] if scope == 0 else [a * R + np.arange(R) for a in range(R)]
+    want = np.zeros(R * R, np.uint8)
+    for idx in rows:
+        k = keys.reshape(-1)[idx]
+        order = idx[np.lexsort((idx, -k.astype(np.int64)))]
+        want[order[:T16]] = 16
+        want[order[T16:T8c]] = 8
+        want[order[T8c:Tk]] = 4
+    assert np.array_equal(got.reshape(-1), want)
+    assert (got == 16).sum() == (T16 if scope == 0 else R * T16)
+
+
+def test_quotas_three_levels_pages_allocations(orc):
+    """Allocations the pages report (shares of 0/4/8/16-bit tiles): 85/0/7.5/7.5
+    and 13.4/64.9/21.6/0, on maps where the shares are whole pair counts."""
+    # 7.5% 16-bit, 7.5% 8-bit, no 4-bit, 85% skipped; R = 1260 (R^2 * 0.075 = 119070)
+    assert orc.quotas3(1260 * 1260, 750, 750, 0) == (119070, 238140, 238140)
+    # 0% 16-bit, 21.6% 8-bit, 64.9% 4-bit, 13.4% skipped; R = 100
+    assert orc.quotas3(100 * 100, 0, 2160, 6490) == (0, 2160, 8650)
