@@ -26,7 +26,7 @@
  *   - The output O uses the same element strides in its own element type
  *     (fp32 or bf16).
  *   - Tier maps are uint8 [B, H, R, R] (query region a, key region b) with
- *     values 8 (FP8), 4 (MXFP4) or 0 (skip).
+ *     values 16 (16-bit: bf16 operands), 8 (FP8), 4 (MXFP4) or 0 (skip).
  *   - All calls are asynchronous on the given HIP stream.  Nothing is
  *     synchronised except where stated.  Device buffers (inputs, outputs,
  *     the workspace) belong to the caller; the library allocates only the
@@ -63,10 +63,12 @@ typedef struct {
 
 typedef struct {
     int32_t hi_bp;   /* share of region pairs in the FP8 tier, basis points of n */
-    int32_t lo_bp;   /* share in the MXFP4 tier; hi_bp + lo_bp <= 10000 */
+    int32_t lo_bp;   /* share in the MXFP4 tier */
     double lambda;   /* weight of the max-pooled branch of the draft map, in [0, 1] */
     int32_t scope;   /* 0: one ranking per head over n = R*R pairs (the paper's);
                         1: one ranking per query region over n = R pairs */
+    int32_t full_bp; /* share in the 16-bit tier (bf16 operands, the paper's 16-bit
+                        path); full_bp + hi_bp + lo_bp <= 10000 */
 } da2_budget;
 
 typedef struct da2_layout_s da2_layout_t;
@@ -90,15 +92,17 @@ void da2_plan_destroy(da2_plan_t *plan);
  * Q/K operand preparation (Sec. 3.3): reorder, pool, quantize Q and K to FP8
  * (one fp32 scale per 64-token block) and MXFP4, score the draft map, rank
  * and assign tiers, and build the per-query-region schedule.  Quotas per
- * ranking: T8 = round_half_up(hi_bp*n/10^4), Tk = round_half_up((hi_bp +
- * lo_bp)*n/10^4), T4 = Tk - T8; ties between equal scores go to the smaller
- * pair index a*R+b.  q and k must stay unchanged until da2_attention on this
- * plan has run (stream order). */
+ * ranking, cumulative and each rounded half up: T16 = full_bp*n/10^4, T16 +
+ * T8 = (full_bp + hi_bp)*n/10^4, T16 + T8 + T4 = (full_bp + hi_bp +
+ * lo_bp)*n/10^4.  The T16 highest-scoring pairs get the 16-bit tier, the next
+ * T8 FP8, the next T4 MXFP4 (Sec. 3.1: larger draft mass, higher precision);
+ * ties between equal scores go to the smaller pair index a*R+b.  q and k must
+ * stay unchanged until da2_attention on this plan has run (stream order). */
 da2_status da2_plan(da2_plan_t *plan, const void *q, const void *k, const da2_budget *budget,
                     hipStream_t stream);
 
 /* Same as da2_plan but with a caller-supplied tier map (device, [B,H,R,R],
- * values in {0,4,8}; other values are treated as skip).  Pooling and draft
+ * values in {0,4,8,16}; other values are treated as skip).  Pooling and draft
  * scoring are not run. */
 da2_status da2_plan_from_tier_map(da2_plan_t *plan, const void *q, const void *k,
                                   const uint8_t *tier_map, hipStream_t stream);
@@ -108,8 +112,8 @@ da2_status da2_plan_tier_map(const da2_plan_t *plan, uint8_t *dst, hipStream_t s
 
 /* da2_attention: V preparation (FP8 with one fp32 scale per channel over all
  * tokens; MXFP4 along keys in groups of 32 inside each region) and the
- * phased mixed-precision attention over the plan's kept tiles, written to o
- * in the original token order.  out_dtype: 0 = bf16, 1 = fp32.  q and k must
+ * phased mixed-precision attention over the plan's kept tiles (16-bit phase,
+ * then FP8, then MXFP4; Sec. 3.3), written to o in the original token order.  out_dtype: 0 = bf16, 1 = fp32.  q and k must
  * be the pointers the plan was built on (DA2_ERR_PLAN_MISMATCH otherwise).
  * Rows whose query region keeps no tile are written as zero (App. C.1). */
 da2_status da2_attention(da2_plan_t *plan, const void *q, const void *k, const void *v, void *o,
@@ -122,8 +126,9 @@ da2_status da2_attention(da2_plan_t *plan, const void *q, const void *k, const v
  *   DA2_DBG_Q_MX_SCALE / K_...      : uint8 E8M0 [B,H,N,d/32];  V: [B,H,R,2,d]
  *   DA2_DBG_Q_AVG / K_AVG           : fp64 [B,H,R,d];  Q_MAX / K_MAX: fp32 [B,H,R,d]
  *   DA2_DBG_KEYS                    : uint32 [B,H,R,R] (bits of fp32 draft score)
- *   DA2_DBG_SCHEDULE                : int32 [B,H,R,2+R]: n8, n4, then FP8 key
- *                                     regions ascending, then MXFP4 ascending, then -1
+ *   DA2_DBG_SCHEDULE                : int32 [B,H,R,3+R]: n16, n8, n4, then the
+ *                                     16-bit key regions ascending, then FP8
+ *                                     ascending, then MXFP4 ascending, then -1
  * V entries are valid after da2_attention. */
 enum {
     DA2_DBG_Q_FP8 = 0, DA2_DBG_Q_FP8_SCALE, DA2_DBG_Q_MX, DA2_DBG_Q_MX_SCALE,
@@ -152,8 +157,10 @@ const char *da2_status_string(da2_status status);
 /* Constants of the fp64 exp used by the draft softmax: ln2 head, ln2 tail,
  * 1/ln2, then the 14 Taylor coefficients 1/j!, j = 0..13 (17 doubles). */
 void da2_exp_constants(double *out17);
-/* The quotas the ranking uses for n pairs: T8 and Tk = T8 + T4. */
-void da2_quotas(int64_t n, int32_t hi_bp, int32_t lo_bp, int64_t *t8, int64_t *tk);
+/* The cumulative quotas the ranking uses for n pairs: t16 = T16, t8 = T16 +
+ * T8, tk = T16 + T8 + T4. */
+void da2_quotas(int64_t n, int32_t full_bp, int32_t hi_bp, int32_t lo_bp, int64_t *t16,
+                int64_t *t8, int64_t *tk);
 
 #ifdef __cplusplus
 }

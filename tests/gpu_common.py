@@ -24,7 +24,7 @@ def host(t, dtype):
     return t.cpu().numpy().view(dtype)
 
 
-def run_plan(q, k, F, Hv, Wv, hi, lo, lam=0.2, scope=0, layout_bnhd=False):
+def run_plan(q, k, F, Hv, Wv, hi, lo, lam=0.2, scope=0, layout_bnhd=False, full=0):
     """Plan on the GPU.  Returns (plan, qd, kd) keeping the tensors alive."""
     from video_diffusion_dit_frame_amd import da2
 
@@ -34,7 +34,7 @@ def run_plan(q, k, F, Hv, Wv, hi, lo, lam=0.2, scope=0, layout_bnhd=False):
         kd = kd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     L = da2.Layout.for_tensor(qd, F, Hv, Wv)
     P = da2.Plan(L)
-    P.plan(qd, kd, hi, lo, lam, scope)
+    P.plan(qd, kd, hi, lo, lam, scope, full_bp=full)
     return P, qd, kd
 
 
@@ -52,19 +52,17 @@ def run_attention(P, qd, kd, v, out_dtype=torch.float32, layout_bnhd=False):
 
 
 def schedule_from_tier(tier):
-    """Expected schedule rows from a tier map: n8, n4, FP8 key regions
-    ascending, MXFP4 key regions ascending, -1 padding."""
+    """Expected schedule rows from a tier map: n16, n8, n4, the 16-bit key
+    regions ascending, FP8 ascending, MXFP4 ascending, -1 padding."""
     B, H, R, _ = tier.shape
-    out = np.full((B, H, R, R + 2), -1, np.int32)
+    out = np.full((B, H, R, R + 3), -1, np.int32)
     for b in range(B):
         for h in range(H):
             for a in range(R):
-                l8 = np.nonzero(tier[b, h, a] == 8)[0]
-                l4 = np.nonzero(tier[b, h, a] == 4)[0]
-                out[b, h, a, 0] = len(l8)
-                out[b, h, a, 1] = len(l4)
-                out[b, h, a, 2:2 + len(l8)] = l8
-                out[b, h, a, 2 + len(l8):2 + len(l8) + len(l4)] = l4
+                lists = [np.nonzero(tier[b, h, a] == p)[0] for p in (16, 8, 4)]
+                out[b, h, a, :3] = [len(x) for x in lists]
+                cat = np.concatenate(lists)
+                out[b, h, a, 3:3 + len(cat)] = cat
     return out
 
 

@@ -63,9 +63,11 @@ def test_workspace_and_plan_validation():
     assert L.da2_plan_create(lay, C.c_void_p((1 << 20) + 16), need, C.byref(p)) == WORKSPACE
     assert L.da2_plan_create(lay, fake, need, C.byref(p)) == OK
     q = C.c_void_p(1 << 24)
-    for hi, lo, lam, scope in [(-1, 0, 0.2, 0), (0, -5, 0.2, 0), (6000, 4001, 0.2, 0),
-                               (100, 100, 1.5, 0), (100, 100, float("nan"), 0), (100, 100, 0.2, 2)]:
-        b = da2.Budget(hi, lo, lam, scope)
+    for hi, lo, lam, scope, full in [(-1, 0, 0.2, 0, 0), (0, -5, 0.2, 0, 0), (6000, 4001, 0.2, 0, 0),
+                                     (100, 100, 1.5, 0, 0), (100, 100, float("nan"), 0, 0),
+                                     (100, 100, 0.2, 2, 0), (100, 100, 0.2, 0, -1),
+                                     (4000, 3000, 0.2, 0, 3001)]:
+        b = da2.Budget(hi, lo, lam, scope, full)
         assert L.da2_plan(p, q, q, C.byref(b), None) == INVALID
     b = da2.Budget(100, 100, 0.2, 0)
     assert L.da2_plan(p, C.c_void_p((1 << 24) + 2), q, C.byref(b), None) == INVALID  # misaligned
@@ -95,6 +97,8 @@ def test_quotas_agree_with_oracle(orc):
         hi = int(rng.integers(0, 10001))
         lo = int(rng.integers(0, 10001 - hi))
         assert da2.quotas(n, hi, lo) == orc.quotas(n, hi, lo)
+        full = int(rng.integers(0, 10001 - hi - lo))
+        assert da2.quotas3(n, full, hi, lo) == orc.quotas3(n, full, hi, lo)
 
 
 def test_debug_sizes():

@@ -39,7 +39,7 @@ def _check_heads(w, q, k, v, hi, lo, P, o32, o16, heads):
     perm = O.layout(w.F, w.Hv, w.Wv)
     keys = G.host(P.debug("KEYS"), np.uint32).reshape(B, H, R, R)
     tier = P.tier_map().cpu().numpy()
-    sched = G.host(P.debug("SCHEDULE"), np.int32).reshape(B, H, R, R + 2)
+    sched = G.host(P.debug("SCHEDULE"), np.int32).reshape(B, H, R, R + 3)
     regions = _sample_regions(R)
     rows = np.concatenate([perm[a * 64:(a + 1) * 64] for a in regions])
     for b, h in heads:

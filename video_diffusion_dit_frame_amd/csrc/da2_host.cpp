@@ -33,6 +33,10 @@ da2_status check_shape(const da2_shape *s)
         return DA2_ERR_INVALID_ARG;
     if (s->stride_n % 8 || s->stride_h % 8 || s->stride_b % 8)
         return DA2_ERR_INVALID_ARG;
+    // the 16-bit phase addresses one region's key rows (8 image rows) with
+    // 32-bit byte offsets from the region's first token
+    if ((((int64_t)7 * s->width + 7) * s->stride_n + s->head_dim) * 2 > INT32_MAX)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
     return DA2_OK;
 }
 
@@ -58,6 +62,7 @@ void carve(da2_layout_s &L)
     W.v4 = take(BH * N * d / 2);
     W.v4s = take(BH * N * d / 32);
     W.vs8 = take(BH * d * 4);
+    W.v16 = take(BH * N * d * 2);
     W.vamax = take(BH * d * 4);
     W.qavg = take(BH * R * d * 8);
     W.kavg = take(BH * R * d * 8);
@@ -70,10 +75,10 @@ void carve(da2_layout_s &L)
     W.keys = take(BH * R * R * 4);
     W.tier = take(BH * R * R);
     W.sched = take(BH * R * R * 4);
-    W.cnt = take(BH * R * 2 * 4);
-    W.rank_state = take(BH * 2 * sizeof(RankState));
-    W.rank_hist = take(BH * 2 * 256 * 4);
-    W.rank_eq = take(BH * (size_t)L.nchunk * 2 * 4);
+    W.cnt = take(BH * R * kTargets * 4);
+    W.rank_state = take(BH * kTargets * sizeof(RankState));
+    W.rank_hist = take(BH * kTargets * 256 * 4);
+    W.rank_eq = take(BH * (size_t)L.nchunk * kTargets * 4);
     W.total = off;
 }
 
@@ -192,10 +197,12 @@ da2_status da2_plan_timing_read(da2_plan_t *P, float *ms, int32_t max, int32_t *
     return DA2_OK;
 }
 
-void da2_quotas(int64_t n, int32_t hi_bp, int32_t lo_bp, int64_t *t8, int64_t *tk)
+void da2_quotas(int64_t n, int32_t full_bp, int32_t hi_bp, int32_t lo_bp, int64_t *t16,
+                int64_t *t8, int64_t *tk)
 {
-    *t8 = ((int64_t)hi_bp * n + 5000) / 10000;
-    *tk = ((int64_t)(hi_bp + lo_bp) * n + 5000) / 10000;
+    *t16 = ((int64_t)full_bp * n + 5000) / 10000;
+    *t8 = ((int64_t)(full_bp + hi_bp) * n + 5000) / 10000;
+    *tk = ((int64_t)(full_bp + hi_bp + lo_bp) * n + 5000) / 10000;
 }
 
 da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budget *bud,
@@ -205,7 +212,8 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
         return DA2_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k))
         return DA2_ERR_INVALID_ARG;
-    if (bud->hi_bp < 0 || bud->lo_bp < 0 || bud->hi_bp + bud->lo_bp > 10000)
+    if (bud->hi_bp < 0 || bud->lo_bp < 0 || bud->full_bp < 0 ||
+        (int64_t)bud->full_bp + bud->hi_bp + bud->lo_bp > 10000)
         return DA2_ERR_INVALID_ARG;
     if (!isfinite(bud->lambda) || bud->lambda < 0.0 || bud->lambda > 1.0)
         return DA2_ERR_INVALID_ARG;
@@ -213,13 +221,13 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
         return DA2_ERR_INVALID_ARG;
     const da2_layout_s &L = P->L;
     const int64_t n = bud->scope == 0 ? (int64_t)L.R * L.R : (int64_t)L.R;
-    int64_t t8, tk;
-    da2_quotas(n, bud->hi_bp, bud->lo_bp, &t8, &tk);
+    int64_t t16, t8, tk;
+    da2_quotas(n, bud->full_bp, bud->hi_bp, bud->lo_bp, &t16, &t8, &tk);
     P->ready = 0;
     launch_prep_qk(L, q, 0, P->ws, stream);
     launch_prep_qk(L, k, 1, P->ws, stream);
     launch_draft(L, bud->lambda, P->ws, stream);
-    launch_rank(L, bud->scope, t8, tk, P->ws, stream);
+    launch_rank(L, bud->scope, t16, t8, tk, P->ws, stream);
     launch_schedule(L, P->ws, stream);
     da2_status st = launched();
     if (st != DA2_OK)
@@ -228,6 +236,7 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
     P->k = k;
     P->ready = 1;
     P->has_keys = 1;
+    P->has16 = t16 > 0;
     return DA2_OK;
 }
 
@@ -251,6 +260,7 @@ da2_status da2_plan_from_tier_map(da2_plan_t *P, const void *q, const void *k,
     P->k = k;
     P->ready = 1;
     P->has_keys = 0;
+    P->has16 = 1;  // the imported map may hold 16-bit tiles
     return DA2_OK;
 }
 
@@ -278,7 +288,7 @@ da2_status da2_attention(da2_plan_t *P, const void *q, const void *k, const void
     if (!P->ready || P->q != q || P->k != k)
         return DA2_ERR_PLAN_MISMATCH;
     const da2_layout_s &L = P->L;
-    launch_prep_v(L, v, P->ws, stream);
+    launch_prep_v(L, v, P->has16, P->ws, stream);
     hipEvent_t *ev = nullptr;
     if (P->timing && P->nev < kMaxTimed) {
         ev = P->ev + 2 * P->nev;
@@ -287,7 +297,7 @@ da2_status da2_attention(da2_plan_t *P, const void *q, const void *k, const void
                 return DA2_ERR_HIP;
         hipEventRecord(ev[0], stream);
     }
-    launch_attention(L, P->ws, o, out_dtype, stream);
+    launch_attention(L, P->ws, q, k, o, out_dtype, stream);
     if (ev) {
         hipEventRecord(ev[1], stream);
         P->nev++;
@@ -319,7 +329,7 @@ size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which)
     case DA2_DBG_KEYS:
         return BH * R * R * 4;
     case DA2_DBG_SCHEDULE:
-        return BH * R * (R + 2) * 4;
+        return BH * R * (R + kTargets) * 4;
     default:
         return 0;
     }

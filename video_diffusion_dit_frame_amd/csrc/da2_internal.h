@@ -12,6 +12,7 @@ namespace da2 {
 constexpr int kBlk = 64;          // tokens per region: one 8x8 spatial cell
 constexpr int kMaxRegions = 8192; // R limit (keeps R*R in 32 bits, row scope in LDS)
 constexpr int kMaxTimed = 4096;   // attention calls recorded while timing
+constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
 
 // ---------------------------------------------------------------------------
 // Workspace: one region of caller memory carved into these buffers.
@@ -21,11 +22,13 @@ constexpr int kMaxTimed = 4096;   // attention calls recorded while timing
 //   *_mx   : same chunking, 16 B of E2M1 pairs per lane, one E8M0 byte per lane
 //   V fp8  : [bh][a][cb=d/32][lane][32 B]           A operand of O^T = V^T P^T
 //   V mx   : [bh][a][cb][lane][16 B] + E8M0 byte per lane
+//   V bf16 : [bh][a][cb][t=4][lane][16 B]           A operand of the 16-bit
+//            product: lane l holds channel 32cb + l%32, keys 32(l/32) + 8t .. +7
 // ---------------------------------------------------------------------------
 struct Workspace {
     size_t q8, q4, q4s, qs8;
     size_t k8, k4, k4s, ks8;
-    size_t v8, v4, v4s, vs8, vamax;
+    size_t v8, v4, v4s, vs8, vamax, v16;
     size_t qavg, kavg, qmax, kmax;
     size_t la, lm, rmax, zsum, keys, tier;
     size_t sched, cnt;
@@ -56,6 +59,7 @@ struct da2_plan_s {
     const void *q, *k;        // inputs the plan was built on
     int ready;                // operands + schedule present
     int has_keys;             // draft keys present (da2_plan, not from tier map)
+    int has16;                // the tier map may hold 16-bit tiles
     int timing;               // record events around the attention kernel
     int nev;                  // recorded event pairs
     hipEvent_t *ev;           // [2 * kMaxTimed] when timing is on
@@ -67,12 +71,13 @@ namespace da2 {
 // Launchers (defined in the kernel translation units).
 // ---------------------------------------------------------------------------
 void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, hipStream_t st);
-void launch_prep_v(const da2_layout_s &L, const void *v, char *ws, hipStream_t st);
+void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, hipStream_t st);
 void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st);
-void launch_rank(const da2_layout_s &L, int scope, int64_t t8, int64_t tk, char *ws,
+void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int64_t tk, char *ws,
                  hipStream_t st);
 void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st);
-void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hipStream_t st);
+void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
+                      int out_f32, hipStream_t st);
 void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, hipStream_t st);
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st);
 

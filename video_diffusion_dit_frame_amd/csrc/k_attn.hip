@@ -3,8 +3,8 @@
 // B.4 shared normalization, App. C.1 empty rows) on gfx950 matrix cores.
 //
 // One workgroup = one query region (64 queries) of one (b, h); wave w owns
-// queries 32w .. 32w+31.  Both products use 32x32x64 f8f6f4 MFMAs in the
-// transposed form
+// queries 32w .. 32w+31.  The quantized products use 32x32x64 f8f6f4 MFMAs,
+// the 16-bit ones 32x32x16 bf16 MFMAs, all in the transposed form
 //     S^T = K Q^T      (A = key rows, B = queries, k = channels)
 //     O^T = V^T P^T    (A = channels, B = queries, k = keys)
 // so every lane holds one query: its softmax statistics never leave the lane
@@ -13,6 +13,10 @@
 // accumulator hands each lane a whole 32-key group, which is exactly the B
 // operand chunk of the P^T V product and exactly one MX block of P.
 //
+// 16-bit phase (tiles of the schedule's 16-bit list, ascending): S from the
+// bf16 inputs as they are (exact products, fp32 sums), c4 = log2(e)/sqrt(d);
+// e = 2^(S c4 + 8 - m); Z += e; P = bf16(e) (nearest even); acc += P^T V in
+// real units.  Phase boundary, when FP8 tiles follow: acc[c] /= sV[c].
 // FP8 phase (tiles of the schedule's FP8 list, ascending): S from FP8 codes,
 // c8 = sQ sK log2(e)/sqrt(d); running max m per 64-key tile; e = 2^(S c8 + 8
 // - m) = 256 w; Z += e; P = e4m3(e); acc += P^T V8 (codes; V's per-channel
@@ -30,6 +34,8 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 struct AttnArgs {
     const uint8_t *q8, *q4, *q4s;
@@ -38,6 +44,9 @@ struct AttnArgs {
     const float *ks8;
     const uint8_t *v8, *v4, *v4s;
     const float *vs8;
+    const uint16_t *q, *k;  // bf16 inputs (16-bit phase)
+    const uint8_t *v16;     // bf16 value operand (16-bit phase)
+    int kspan;              // bytes from a region's first key row past its last
     const int32_t *sched;
     const int32_t *cnt;
     void *out;
@@ -46,6 +55,10 @@ struct AttnArgs {
     int H, R, Ry, Rx, Hv, Wv, BH;
     float c4;  // log2(e) / sqrt(d)
 };
+
+__device__ __forceinline__ v8bf as_bf16x8(v4u x) { return __builtin_bit_cast(v8bf, x); }
+
+__device__ __forceinline__ v4u lds_v4u(const uint8_t *p) { return *reinterpret_cast<const v4u *>(p); }
 
 __device__ __forceinline__ float pair_max(float x)
 {
@@ -463,6 +476,90 @@ struct Attn {
         if (i + 3 < n)
             kb_k = sload_i32(list + i + 3);
     }
+
+    // 16-bit phase over the n16 key regions of list16.  A tile's key image
+    // (64 key rows x D channels, bf16, gathered straight from K; chunk (m, s)
+    // holds for lane l key row key_of_row(l % 32, m), channels 16 s + 8 (l /
+    // 32) .. + 7) fills both key buffers, and its value image (the bf16
+    // operand written by the V preparation) both value buffers, so this phase
+    // is single-buffered; other workgroups on the CU cover its copies.
+    __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int a, int bh)
+    {
+        constexpr int KS = D / 16;   // 16-channel steps of QK^T
+        uint8_t *kall = &kbuf[0][0], *vall = &vbuf[0][0];
+        const int hf = l >> 5;
+        const int bb = bh / A.H, hh = bh - bb * A.H;
+        const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
+        // queries of this wave as B operands (lane l: query 32 w + l % 32,
+        // channels 16 s + 8 hf .. + 7 of step s)
+        v4u q16[KS];
+        {
+            const int qt = region_token(a, 32 * w + (l & 31), A.Ry, A.Rx, A.Hv, A.Wv);
+            const uint16_t *qr = A.q + hoff + (int64_t)qt * A.osn + 8 * hf;
+#pragma unroll
+            for (int s = 0; s < KS; s++)
+                q16[s] = *reinterpret_cast<const v4u *>(qr + 16 * s);
+        }
+        // wave w gathers the key rows of half m = w: a fixed byte offset from
+        // the key region's first token for every tile
+        const int kpos = key_of_row(l & 31, w);
+        const uint32_t koff =
+            (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * hf) * 2);
+        const uint16_t *kh = A.k + hoff;
+        const __amdgpu_buffer_rsrc_t vsrc =
+            head_rsrc(A.v16 + hbase * (kBlk * D * 2), (int64_t)A.R * kBlk * D * 2);
+        for (int i = 0; i < n16; i++) {
+            const int kb = sload_i32(list16 + i);
+            if (i > 0)
+                __syncthreads();   // every wave is done with the previous tile
+            const int t0 = region_token(kb, 0, A.Ry, A.Rx, A.Hv, A.Wv);
+            const __amdgpu_buffer_rsrc_t ksrc = head_rsrc((const uint8_t *)(kh + (int64_t)t0 * A.osn), A.kspan);
+#pragma unroll
+            for (int s = 0; s < KS; s++)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(kall + (w * KS + s) * 1024), 16,
+                                                         koff, 32 * s, 0, 0);
+            copy_kb<kBlk * D * 2 / 1024>(vsrc, (uint32_t)kb * (kBlk * D * 2), vall, w, (uint32_t)l * 16u);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            v16f sc[2];
+            sc[0] = (v16f){};
+            sc[1] = (v16f){};
+#pragma unroll
+            for (int s = 0; s < KS; s++)
+#pragma unroll
+                for (int mm = 0; mm < 2; mm++)
+                    sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(lds_v4u(kall + ((mm * KS + s) * 64 + l) * 16)), as_bf16x8(q16[s]), sc[mm],
+                        0, 0, 0);
+            const float c = A.c4;
+            const float mnew = fmaxf(m, pair_max(lane_max(sc)) * c);
+            rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
+            m = mnew;
+            const float bias = 8.0f - mnew;
+            // P^T chunk t: this lane's keys 32 hf + 8 t .. + 7 (slots 8 t ..)
+            v4u p[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int mm = t >> 1, r0 = 8 * (t & 1);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j], c, bias));
+                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j + 1], c, bias));
+                    z += e0 + e1;
+                    p[t][j] = (uint32_t)f32_to_bf16(e0) | ((uint32_t)f32_to_bf16(e1) << 16);
+                }
+            }
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+                for (int t = 0; t < 4; t++)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(lds_v4u(vall + ((cb * 4 + t) * 64 + l) * 16)), as_bf16x8(p[t]), acc[cb], 0,
+                        0, 0);
+        }
+        // the quantized phases refill these buffers
+        __syncthreads();
+    }
 };
 
 template <int D>
@@ -506,10 +603,12 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
         S.q4s[kc] = A.q4s[qblk * (2 * D) + chunk];
     }
     S.qs = A.qs8[qblk];
-    const int n8 = sload_i32(A.cnt + qblk * 2), n = n8 + sload_i32(A.cnt + qblk * 2 + 1);
+    const int n16 = sload_i32(A.cnt + qblk * kTargets);
+    const int n8 = sload_i32(A.cnt + qblk * kTargets + 1);
+    const int n = n8 + sload_i32(A.cnt + qblk * kTargets + 2);
     S.n8 = n8;
     S.n = n;
-    S.list = A.sched + qblk * R;
+    S.list = A.sched + qblk * R + n16;
     S.hbase = (int64_t)bh * R;
     S.src = head_sources<D>(A, S.hbase, R);
 #pragma unroll
@@ -517,6 +616,19 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
         S.acc[cb] = (v16f){};
     S.m = -__builtin_huge_valf();
     S.z = 0.0f;
+
+    if (n16 > 0) {
+        S.phase16(A.sched + qblk * R, n16, a, bh);
+        if (n8 > 0) {
+            // phase boundary: real units -> FP8 value units
+            const float *vs = A.vs8 + (int64_t)bh * D;
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    S.acc[cb][r] /= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+        }
+    }
 
     v16f sa[2], sb[2];
     if (n > 0) {
@@ -603,7 +715,8 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 
 }  // namespace
 
-void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hipStream_t st)
+void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
+                      int out_f32, hipStream_t st)
 {
     const Workspace &W = L.ws;
     AttnArgs A;
@@ -619,6 +732,10 @@ void launch_attention(const da2_layout_s &L, char *ws, void *o, int out_f32, hip
     A.v4 = (const uint8_t *)(ws + W.v4);
     A.v4s = (const uint8_t *)(ws + W.v4s);
     A.vs8 = (const float *)(ws + W.vs8);
+    A.q = (const uint16_t *)q;
+    A.k = (const uint16_t *)k;
+    A.v16 = (const uint8_t *)(ws + W.v16);
+    A.kspan = (int)(((int64_t)7 * L.s.width + 7) * L.s.stride_n + L.d) * 2;
     A.sched = (const int32_t *)(ws + W.sched);
     A.cnt = (const int32_t *)(ws + W.cnt);
     A.out = o;

@@ -90,17 +90,17 @@ __global__ void k_unpack_sched(const int32_t *sched, const int32_t *cnt, int R, 
                                int32_t *dst)
 {
     int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t W = R + 2;
+    const int64_t W = R + kTargets;
     if (e >= rows * W)
         return;
     const int64_t row = e / W;
     const int j = (int)(e % W);
-    const int n = cnt[row * 2] + cnt[row * 2 + 1];
+    const int n = cnt[row * kTargets] + cnt[row * kTargets + 1] + cnt[row * kTargets + 2];
     int32_t v;
-    if (j < 2)
-        v = cnt[row * 2 + j];
+    if (j < kTargets)
+        v = cnt[row * kTargets + j];
     else
-        v = (j - 2) < n ? (int32_t)sched[row * R + (j - 2)] : -1;
+        v = (j - kTargets) < n ? (int32_t)sched[row * R + (j - kTargets)] : -1;
     dst[e] = v;
 }
 
@@ -158,7 +158,7 @@ void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, h
         break;
     case DA2_DBG_SCHEDULE: {
         const int64_t rows = (int64_t)L.BH * L.R;
-        k_unpack_sched<<<grid(rows * (L.R + 2)), 256, 0, st>>>(
+        k_unpack_sched<<<grid(rows * (L.R + kTargets)), 256, 0, st>>>(
             (const int32_t *)(ws + W.sched), (const int32_t *)(ws + W.cnt), L.R, rows, (int32_t *)dst);
         break;
     }

@@ -11,11 +11,12 @@
 // with separate products; the ranking key is the bit pattern of fp32(A).
 //
 // Ranking (head scope) is an exact radix select on the 32-bit keys for the
-// T8-th and Tk-th largest (8-bit digits, four histogram passes), followed by
-// a pass that resolves equal keys by ascending pair index a*R+b with a
-// chunked prefix count.  Row scope does the same per query region inside one
-// workgroup.  The schedule lists, per query region, the FP8 key regions in
-// ascending order followed by the MXFP4 key regions in ascending order.
+// T16-th, (T16+T8)-th and (T16+T8+T4)-th largest (8-bit digits, four
+// histogram passes), followed by a pass that resolves equal keys by
+// ascending pair index a*R+b with a chunked prefix count.  Row scope does the
+// same per query region inside one workgroup.  The schedule lists, per query
+// region, the 16-bit key regions in ascending order, then the FP8 ones, then
+// the MXFP4 ones.
 #include "da2_internal.h"
 #include "da2_device.h"
 
@@ -231,14 +232,16 @@ __global__ __launch_bounds__(256) void k_keys(const double *__restrict__ La,
 }
 
 // ---------------------------------------------------------------------------
-// Head-scope radix select.
+// Head-scope radix select for the kTargets cumulative thresholds T16,
+// T16 + T8 and T16 + T8 + T4 at once.
 // ---------------------------------------------------------------------------
 __global__ void k_rank_init(RankState *__restrict__ st, uint32_t *__restrict__ hist, int nseg,
-                            int64_t t8, int64_t tk)
+                            int64_t t16, int64_t t8c, int64_t tk)
 {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < nseg * 2) {
-        int64_t T = (i & 1) ? tk : t8;
+    if (i < nseg * kTargets) {
+        const int tg = i % kTargets;
+        const int64_t T = tg == 0 ? t16 : (tg == 1 ? t8c : tk);
         RankState s;
         s.prefix = 0;
         s.mask = 0;
@@ -246,7 +249,7 @@ __global__ void k_rank_init(RankState *__restrict__ st, uint32_t *__restrict__ h
         s.active = T > 0 ? 1u : 0u;
         st[i] = s;
     }
-    for (int j = i; j < nseg * 2 * 256; j += gridDim.x * blockDim.x)
+    for (int j = i; j < nseg * kTargets * 256; j += gridDim.x * blockDim.x)
         hist[j] = 0;
 }
 
@@ -255,13 +258,16 @@ __global__ __launch_bounds__(256) void k_rank_hist(const uint32_t *__restrict__ 
                                                    const RankState *__restrict__ st,
                                                    uint32_t *__restrict__ hist, int shift)
 {
-    __shared__ uint32_t h[2][256];
+    __shared__ uint32_t h[kTargets][256];
     const int seg = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * kChunk;
     const int t = threadIdx.x;
-    h[0][t] = 0;
-    h[1][t] = 0;
-    const RankState s0 = st[seg * 2], s1 = st[seg * 2 + 1];
+    RankState s[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++) {
+        h[tg][t] = 0;
+        s[tg] = st[seg * kTargets + tg];
+    }
     __syncthreads();
     const uint32_t *kp = keys + (int64_t)seg * seglen;
     for (int j = 0; j < kChunk / 256; j++) {
@@ -269,18 +275,18 @@ __global__ __launch_bounds__(256) void k_rank_hist(const uint32_t *__restrict__ 
         if (i < seglen) {
             uint32_t k = kp[i];
             uint32_t dg = (k >> shift) & 255u;
-            if (s0.active && ((k ^ s0.prefix) & s0.mask) == 0)
-                atomicAdd(&h[0][dg], 1u);
-            if (s1.active && ((k ^ s1.prefix) & s1.mask) == 0)
-                atomicAdd(&h[1][dg], 1u);
+#pragma unroll
+            for (int tg = 0; tg < kTargets; tg++)
+                if (s[tg].active && ((k ^ s[tg].prefix) & s[tg].mask) == 0)
+                    atomicAdd(&h[tg][dg], 1u);
         }
     }
     __syncthreads();
-    uint32_t *g = hist + (int64_t)seg * 512;
-    if (h[0][t])
-        atomicAdd(&g[t], h[0][t]);
-    if (h[1][t])
-        atomicAdd(&g[256 + t], h[1][t]);
+    uint32_t *g = hist + (int64_t)seg * kTargets * 256;
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        if (h[tg][t])
+            atomicAdd(&g[tg * 256 + t], h[tg][t]);
 }
 
 // One workgroup per segment: pick the digit holding the wanted rank (keys in
@@ -290,9 +296,9 @@ __global__ __launch_bounds__(256) void k_rank_select(RankState *__restrict__ st,
 {
     __shared__ uint32_t scan[256];
     const int seg = blockIdx.x, t = threadIdx.x;
-    for (int tg = 0; tg < 2; tg++) {
-        RankState s = st[seg * 2 + tg];
-        uint32_t *g = hist + (int64_t)seg * 512 + tg * 256;
+    for (int tg = 0; tg < kTargets; tg++) {
+        RankState s = st[seg * kTargets + tg];
+        uint32_t *g = hist + ((int64_t)seg * kTargets + tg) * 256;
         const int dg = 255 - t;  // thread t owns digit 255 - t (descending order)
         uint32_t cnt = g[dg];
         scan[t] = cnt;
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(256) void k_rank_select(RankState *__restrict__ st,
             s.prefix |= (uint32_t)dg << shift;
             s.mask |= 255u << shift;
             s.rank -= excl;
-            st[seg * 2 + tg] = s;
+            st[seg * kTargets + tg] = s;
         }
         __syncthreads();
         g[dg] = 0;
@@ -324,30 +330,42 @@ __global__ __launch_bounds__(256) void k_rank_eqcount(const uint32_t *__restrict
 {
     const int seg = blockIdx.y, t = threadIdx.x;
     const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-    const RankState s0 = st[seg * 2], s1 = st[seg * 2 + 1];
+    RankState s[kTargets];
+    uint32_t n[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++) {
+        s[tg] = st[seg * kTargets + tg];
+        n[tg] = 0;
+    }
     const uint32_t *kp = keys + (int64_t)seg * seglen;
-    uint32_t n0 = 0, n1 = 0;
     for (int j = 0; j < kChunk / 256; j++) {
         int64_t i = c0 + j * 256 + t;
         if (i < seglen) {
             uint32_t k = kp[i];
-            n0 += (s0.active && k == s0.prefix);
-            n1 += (s1.active && k == s1.prefix);
+#pragma unroll
+            for (int tg = 0; tg < kTargets; tg++)
+                n[tg] += (s[tg].active && k == s[tg].prefix);
         }
     }
-    __shared__ uint32_t r[2][4];
-    n0 = wave_sum_u32(n0);
-    n1 = wave_sum_u32(n1);
-    if ((t & 63) == 0) {
-        r[0][t >> 6] = n0;
-        r[1][t >> 6] = n1;
+    __shared__ uint32_t r[kTargets][4];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++) {
+        n[tg] = wave_sum_u32(n[tg]);
+        if ((t & 63) == 0)
+            r[tg][t >> 6] = n[tg];
     }
     __syncthreads();
-    if (t < 2)
-        eq[((int64_t)seg * nchunk + blockIdx.x) * 2 + t] = r[t][0] + r[t][1] + r[t][2] + r[t][3];
+    if (t < kTargets)
+        eq[((int64_t)seg * nchunk + blockIdx.x) * kTargets + t] = r[t][0] + r[t][1] + r[t][2] + r[t][3];
 }
 
-// Final tier per key: above the threshold, or equal to it and among the first
+// Tier of a key from its membership in the cumulative top sets.
+__device__ __forceinline__ uint8_t tier_of(const bool (&in)[kTargets])
+{
+    return in[0] ? 16 : (in[1] ? 8 : (in[2] ? 4 : 0));
+}
+
+// Final tier per key: above a threshold, or equal to it and among the first
 // `rank + 1` equal keys by pair index.
 __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ keys,
                                                    int64_t seglen, int64_t nchunk,
@@ -355,48 +373,66 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
                                                    const uint32_t *__restrict__ eq,
                                                    uint8_t *__restrict__ tier)
 {
-    __shared__ uint32_t base[2];
-    __shared__ uint32_t scan[2][256];
+    __shared__ uint32_t base[kTargets];
+    __shared__ uint32_t scan[kTargets][256];
     const int seg = blockIdx.y, t = threadIdx.x;
     const int64_t ch = blockIdx.x;
-    const RankState s0 = st[seg * 2], s1 = st[seg * 2 + 1];
+    RankState s[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        s[tg] = st[seg * kTargets + tg];
     // equal keys in earlier chunks of this segment
     if (t < 64) {
-        uint32_t p0 = 0, p1 = 0;
-        for (int64_t c = t; c < ch; c += 64) {
-            p0 += eq[((int64_t)seg * nchunk + c) * 2];
-            p1 += eq[((int64_t)seg * nchunk + c) * 2 + 1];
-        }
-        p0 = wave_sum_u32(p0);
-        p1 = wave_sum_u32(p1);
-        if (t == 0) {
-            base[0] = p0;
-            base[1] = p1;
+        uint32_t p[kTargets];
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++)
+            p[tg] = 0;
+        for (int64_t c = t; c < ch; c += 64)
+#pragma unroll
+            for (int tg = 0; tg < kTargets; tg++)
+                p[tg] += eq[((int64_t)seg * nchunk + c) * kTargets + tg];
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++) {
+            p[tg] = wave_sum_u32(p[tg]);
+            if (t == 0)
+                base[tg] = p[tg];
         }
     }
     // this thread owns 16 consecutive keys
     const int64_t i0 = ch * kChunk + (int64_t)t * 16;
     const uint32_t *kp = keys + (int64_t)seg * seglen;
     uint32_t kv[16];
-    uint32_t e0 = 0, e1 = 0;
+    uint32_t e[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        e[tg] = 0;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         int64_t i = i0 + j;
         kv[j] = i < seglen ? kp[i] : 0u;
-        e0 += (i < seglen && s0.active && kv[j] == s0.prefix);
-        e1 += (i < seglen && s1.active && kv[j] == s1.prefix);
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++)
+            e[tg] += (i < seglen && s[tg].active && kv[j] == s[tg].prefix);
     }
-    scan[0][t] = e0;
-    scan[1][t] = e1;
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        scan[tg][t] = e[tg];
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
-        uint32_t v0 = t >= o ? scan[0][t - o] : 0u, v1 = t >= o ? scan[1][t - o] : 0u;
+        uint32_t v[kTargets];
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++)
+            v[tg] = t >= o ? scan[tg][t - o] : 0u;
         __syncthreads();
-        scan[0][t] += v0;
-        scan[1][t] += v1;
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++)
+            scan[tg][t] += v[tg];
         __syncthreads();
     }
-    uint32_t r0 = base[0] + scan[0][t] - e0, r1 = base[1] + scan[1][t] - e1;
+    uint32_t r[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        r[tg] = base[tg] + scan[tg][t] - e[tg];
     uint8_t *tp = tier + (int64_t)seg * seglen;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
@@ -404,24 +440,20 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
         if (i >= seglen)
             break;
         uint32_t k = kv[j];
-        bool in8 = false, ink = false;
-        if (s0.active) {
-            if (k > s0.prefix)
-                in8 = true;
-            else if (k == s0.prefix) {
-                in8 = r0 <= s0.rank;
-                r0++;
+        bool in[kTargets];
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++) {
+            in[tg] = false;
+            if (s[tg].active) {
+                if (k > s[tg].prefix)
+                    in[tg] = true;
+                else if (k == s[tg].prefix) {
+                    in[tg] = r[tg] <= s[tg].rank;
+                    r[tg]++;
+                }
             }
         }
-        if (s1.active) {
-            if (k > s1.prefix)
-                ink = true;
-            else if (k == s1.prefix) {
-                ink = r1 <= s1.rank;
-                r1++;
-            }
-        }
-        tp[i] = in8 ? 8 : (ink ? 4 : 0);
+        tp[i] = tier_of(in);
     }
 }
 
@@ -429,25 +461,25 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
 // Row scope: one workgroup per query region, keys of the row in LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rank_rows(const uint32_t *__restrict__ keys, int R,
-                                                   int64_t t8, int64_t tk,
+                                                   int64_t t16, int64_t t8c, int64_t tk,
                                                    uint8_t *__restrict__ tier)
 {
     extern __shared__ uint32_t row[];
     __shared__ uint32_t hist[256], scan[256];
-    __shared__ RankState s[2];
+    __shared__ RankState s[kTargets];
     const int64_t seg = blockIdx.x;
     const int t = threadIdx.x;
     for (int b = t; b < R; b += 256)
         row[b] = keys[seg * R + b];
-    if (t < 2) {
-        int64_t T = t ? tk : t8;
+    if (t < kTargets) {
+        const int64_t T = t == 0 ? t16 : (t == 1 ? t8c : tk);
         s[t].prefix = 0;
         s[t].mask = 0;
         s[t].rank = T > 0 ? (uint32_t)(T - 1) : 0u;
         s[t].active = T > 0;
     }
     __syncthreads();
-    for (int tg = 0; tg < 2; tg++) {
+    for (int tg = 0; tg < kTargets; tg++) {
         for (int shift = 24; shift >= 0; shift -= 8) {
             hist[t] = 0;
             __syncthreads();
@@ -480,55 +512,62 @@ __global__ __launch_bounds__(256) void k_rank_rows(const uint32_t *__restrict__ 
     // resolve ties in index order: thread t owns keys [t*per, (t+1)*per)
     const int per = (R + 255) / 256;
     const int bb = t * per;
-    uint32_t e0 = 0, e1 = 0;
+    uint32_t e[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        e[tg] = 0;
     for (int j = 0; j < per; j++) {
         int b = bb + j;
-        if (b < R) {
-            e0 += (s[0].active && row[b] == s[0].prefix);
-            e1 += (s[1].active && row[b] == s[1].prefix);
-        }
+        if (b < R)
+#pragma unroll
+            for (int tg = 0; tg < kTargets; tg++)
+                e[tg] += (s[tg].active && row[b] == s[tg].prefix);
     }
-    __shared__ uint32_t sc2[2][256];
-    sc2[0][t] = e0;
-    sc2[1][t] = e1;
+    __shared__ uint32_t sc2[kTargets][256];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        sc2[tg][t] = e[tg];
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
-        uint32_t v0 = t >= o ? sc2[0][t - o] : 0u, v1 = t >= o ? sc2[1][t - o] : 0u;
+        uint32_t v[kTargets];
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++)
+            v[tg] = t >= o ? sc2[tg][t - o] : 0u;
         __syncthreads();
-        sc2[0][t] += v0;
-        sc2[1][t] += v1;
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++)
+            sc2[tg][t] += v[tg];
         __syncthreads();
     }
-    uint32_t r0 = sc2[0][t] - e0, r1 = sc2[1][t] - e1;
+    uint32_t r[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        r[tg] = sc2[tg][t] - e[tg];
     for (int j = 0; j < per; j++) {
         int b = bb + j;
         if (b >= R)
             break;
         uint32_t k = row[b];
-        bool in8 = false, ink = false;
-        if (s[0].active) {
-            if (k > s[0].prefix)
-                in8 = true;
-            else if (k == s[0].prefix) {
-                in8 = r0 <= s[0].rank;
-                r0++;
+        bool in[kTargets];
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++) {
+            in[tg] = false;
+            if (s[tg].active) {
+                if (k > s[tg].prefix)
+                    in[tg] = true;
+                else if (k == s[tg].prefix) {
+                    in[tg] = r[tg] <= s[tg].rank;
+                    r[tg]++;
+                }
             }
         }
-        if (s[1].active) {
-            if (k > s[1].prefix)
-                ink = true;
-            else if (k == s[1].prefix) {
-                ink = r1 <= s[1].rank;
-                r1++;
-            }
-        }
-        tier[seg * R + b] = in8 ? 8 : (ink ? 4 : 0);
+        tier[seg * R + b] = tier_of(in);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Schedule: per query region, FP8 key regions ascending then MXFP4 ascending.
-// One wave per row.
+// Schedule: per query region, the 16-bit key regions ascending, then FP8
+// ascending, then MXFP4 ascending; counts n16, n8, n4.  One wave per row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tier, int R,
                                                  int32_t *__restrict__ sched,
@@ -537,31 +576,37 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
     const int64_t row = (int64_t)blockIdx.y * R + blockIdx.x;
     const int l = threadIdx.x;
     const uint8_t *tr = tier + row * R;
-    uint32_t n8 = 0, n4 = 0;
+    uint32_t n16 = 0, n8 = 0, n4 = 0;
     for (int b = l; b < R; b += 64) {
         uint8_t v = tr[b];
+        n16 += v == 16;
         n8 += v == 8;
         n4 += v == 4;
     }
+    n16 = wave_sum_u32(n16);
     n8 = wave_sum_u32(n8);
     n4 = wave_sum_u32(n4);
     int32_t *out = sched + row * R;
-    uint32_t o8 = 0, o4 = n8;
+    uint32_t o16 = 0, o8 = n16, o4 = n16 + n8;
     for (int b0 = 0; b0 < R; b0 += 64) {
         int b = b0 + l;
         uint8_t v = b < R ? tr[b] : 0;
-        uint64_t m8 = __ballot(v == 8), m4 = __ballot(v == 4);
+        uint64_t m16 = __ballot(v == 16), m8 = __ballot(v == 8), m4 = __ballot(v == 4);
         uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
+        if (v == 16)
+            out[o16 + __popcll(m16 & lt)] = b;
         if (v == 8)
             out[o8 + __popcll(m8 & lt)] = b;
         if (v == 4)
             out[o4 + __popcll(m4 & lt)] = b;
+        o16 += __popcll(m16);
         o8 += __popcll(m8);
         o4 += __popcll(m4);
     }
     if (l == 0) {
-        cnt[row * 2] = (int32_t)n8;
-        cnt[row * 2 + 1] = (int32_t)n4;
+        cnt[row * kTargets] = (int32_t)n16;
+        cnt[row * kTargets + 1] = (int32_t)n8;
+        cnt[row * kTargets + 2] = (int32_t)n4;
     }
 }
 
@@ -570,7 +615,7 @@ __global__ void k_copy_tier(const uint8_t *__restrict__ src, uint8_t *__restrict
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) {
         uint8_t v = src[i];
-        dst[i] = (v == 8 || v == 4) ? v : 0;
+        dst[i] = (v == 16 || v == 8 || v == 4) ? v : 0;
     }
 }
 
@@ -600,7 +645,7 @@ void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st
                                                                (uint32_t *)(ws + W.keys));
 }
 
-void launch_rank(const da2_layout_s &L, int scope, int64_t t8, int64_t tk, char *ws,
+void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int64_t tk, char *ws,
                  hipStream_t st)
 {
     const Workspace &W = L.ws;
@@ -608,14 +653,14 @@ void launch_rank(const da2_layout_s &L, int scope, int64_t t8, int64_t tk, char 
     uint8_t *tier = (uint8_t *)(ws + W.tier);
     if (scope == 1) {
         k_rank_rows<<<(unsigned)((int64_t)L.BH * L.R), 256, sizeof(uint32_t) * L.R, st>>>(
-            keys, L.R, t8, tk, tier);
+            keys, L.R, t16, t8c, tk, tier);
         return;
     }
     RankState *rs = (RankState *)(ws + W.rank_state);
     uint32_t *hist = (uint32_t *)(ws + W.rank_hist), *eq = (uint32_t *)(ws + W.rank_eq);
     const int64_t seglen = (int64_t)L.R * L.R;
     const int64_t nchunk = L.nchunk;
-    k_rank_init<<<(L.BH * 2 * 256 + 255) / 256, 256, 0, st>>>(rs, hist, L.BH, t8, tk);
+    k_rank_init<<<(L.BH * kTargets * 256 + 255) / 256, 256, 0, st>>>(rs, hist, L.BH, t16, t8c, tk);
     dim3 g((unsigned)nchunk, L.BH);
     for (int shift = 24; shift >= 0; shift -= 8) {
         k_rank_hist<<<g, 256, 0, st>>>(keys, seglen, nchunk, rs, hist, shift);

@@ -12,7 +12,9 @@
 // k_vamax + k_prep_v: V gets one FP8 scale per channel over all tokens (so
 // the attention accumulator changes units once, at the end of the FP8 phase)
 // and MXFP4 groups of 32 consecutive keys inside each region, packed as the
-// A operand of O^T = V^T P^T (the value transposition folded into packing).
+// A operand of O^T = V^T P^T (the value transposition folded into packing);
+// when the plan has 16-bit tiles, also the bf16 values in the A-operand
+// layout of the 16-bit product.
 #include "da2_internal.h"
 #include "da2_device.h"
 
@@ -161,7 +163,8 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
                                                 const uint32_t *__restrict__ vamax,
                                                 uint8_t *__restrict__ op8, float *__restrict__ s8,
                                                 uint8_t *__restrict__ op4,
-                                                uint8_t *__restrict__ op4s)
+                                                uint8_t *__restrict__ op4s,
+                                                uint16_t *__restrict__ op16)
 {
     __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk * D];
     const int a = blockIdx.x, bh = blockIdx.y;
@@ -206,6 +209,20 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
         *reinterpret_cast<uint4 *>(op4 + blk * (kBlk * D / 2) + (int64_t)t * 16) =
             make_uint4(w4[0], w4[1], w4[2], w4[3]);
         op4s[blk * (2 * D) + t] = (uint8_t)(E + 127);
+        if (op16) {
+            // bf16 A operand of the 16-bit product: chunk (cb, step q) holds,
+            // for lane l, channel c and the 8 keys 32 (l / 32) + 8 q .. + 7
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                uint32_t w16[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    w16[j] = (uint32_t)tile[(k0 + 8 * q + 2 * j) * D + c] |
+                             ((uint32_t)tile[(k0 + 8 * q + 2 * j + 1) * D + c] << 16);
+                *reinterpret_cast<uint4 *>(op16 + ((blk * (D / 32) + cb) * 4 + q) * 512 + l * 8) =
+                    make_uint4(w16[0], w16[1], w16[2], w16[3]);
+            }
+        }
     }
 }
 
@@ -240,7 +257,7 @@ void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, 
                                             op4s, avg, mx);
 }
 
-void launch_prep_v(const da2_layout_s &L, const void *v, char *ws, hipStream_t st)
+void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
     const da2_shape &s = L.s;
@@ -251,15 +268,18 @@ void launch_prep_v(const da2_layout_s &L, const void *v, char *ws, hipStream_t s
     dim3 g1((L.N + 255) / 256, L.BH), g2(L.R, L.BH);
     uint8_t *op8 = (uint8_t *)(ws + W.v8), *op4 = (uint8_t *)(ws + W.v4),
             *op4s = (uint8_t *)(ws + W.v4s);
+    uint16_t *op16 = with16 ? (uint16_t *)(ws + W.v16) : nullptr;
     float *s8 = (float *)(ws + W.vs8);
     if (L.d == 128) {
         k_vamax<128><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
         k_prep_v<128><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
-                                          L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s);
+                                          L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s,
+                                          op16);
     } else {
         k_vamax<64><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
         k_prep_v<64><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
-                                         L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s);
+                                         L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s,
+                                         op16);
     }
 }
 

@@ -36,7 +36,7 @@ class Shape(C.Structure):
 
 class Budget(C.Structure):
     _fields_ = [("hi_bp", C.c_int32), ("lo_bp", C.c_int32), ("lambda_", C.c_double),
-                ("scope", C.c_int32)]
+                ("scope", C.c_int32), ("full_bp", C.c_int32)]
 
 
 _lib = None
@@ -70,7 +70,7 @@ def lib():
         L.da2_plan_timing.restype = C.c_int
         L.da2_plan_timing_read.argtypes = [P, P, i32, C.POINTER(i32)]
         L.da2_plan_timing_read.restype = C.c_int
-        L.da2_quotas.argtypes = [i64, i32, i32, C.POINTER(i64), C.POINTER(i64)]
+        L.da2_quotas.argtypes = [i64, i32, i32, i32, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]
         for name in ("da2_layout_create", "da2_plan_create", "da2_plan", "da2_plan_from_tier_map",
                      "da2_plan_tier_map", "da2_attention", "da2_plan_debug"):
             getattr(L, name).restype = C.c_int
@@ -108,10 +108,18 @@ def exp_constants():
     return out
 
 
+def quotas3(n, full_bp, hi_bp, lo_bp):
+    """Cumulative quotas (T16, T16 + T8, T16 + T8 + T4) for n pairs."""
+    t16, t8, tk = C.c_int64(), C.c_int64(), C.c_int64()
+    lib().da2_quotas(int(n), int(full_bp), int(hi_bp), int(lo_bp), C.byref(t16), C.byref(t8),
+                     C.byref(tk))
+    return t16.value, t8.value, tk.value
+
+
 def quotas(n, hi_bp, lo_bp):
-    t8, tk = C.c_int64(), C.c_int64()
-    lib().da2_quotas(int(n), int(hi_bp), int(lo_bp), C.byref(t8), C.byref(tk))
-    return t8.value, tk.value
+    """(T8, T8 + T4) with no 16-bit share."""
+    _, t8, tk = quotas3(n, 0, hi_bp, lo_bp)
+    return t8, tk
 
 
 class Layout:
@@ -166,8 +174,8 @@ class Plan:
                "da2_plan_create")
         self.handle = h
 
-    def plan(self, q, k, hi_bp, lo_bp, lam=0.2, scope=0, stream=None):
-        b = Budget(int(hi_bp), int(lo_bp), float(lam), int(scope))
+    def plan(self, q, k, hi_bp, lo_bp, lam=0.2, scope=0, stream=None, full_bp=0):
+        b = Budget(int(hi_bp), int(lo_bp), float(lam), int(scope), int(full_bp))
         _check(lib().da2_plan(self.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
                               C.byref(b), _stream(stream)), "da2_plan")
 
