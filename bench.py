@@ -3,14 +3,14 @@
 
 One step = the whole hot path on one layer of synthetic video-DiT
 activations: da2_plan (Q/K preparation, draft scoring, ranking, schedule)
-followed by da2_attention (V preparation, phased FP8/MXFP4 attention with the
-output written back in token order).  Inputs are resident in HBM before the
+followed by da2_attention (V preparation, phased 16-bit/FP8/MXFP4 attention
+with the output written back in token order).  Inputs are resident in HBM before the
 timed region; Q/K/V use the [B, N, H, d] storage of DiT attention layers.
 
 Prints one JSON line.  value = dense-equivalent attention TFLOP/s of the
 complete step (4 B H N^2 d per step); roofline = the attention kernel against
 the tier-weighted MFMA peak (its achieved executed FLOP/s over
-(F8 + F4) / (F8/P8 + F4/P4)); cpu_baseline = the CPU oracle timed on a
+(F16 + F8 + F4) / (F16/P16 + F8/P8 + F4/P4)); cpu_baseline = the CPU oracle timed on a
 bounded sample and extrapolated to the same unit.
 """
 from __future__ import annotations
@@ -26,6 +26,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 MFMA
 PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense FP8 MFMA
 PEAK_FP4 = 10100.0   # TFLOP/s, MI355X dense FP4 MFMA
 
@@ -37,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b-720p")
     ap.add_argument("--budget", type=int, default=0, help="index into the workload's budget list")
+    ap.add_argument("--full-bp", type=int, default=0, help="16-bit share (basis points)")
+    ap.add_argument("--hi-bp", type=int, default=None, help="FP8 share, overriding --budget")
+    ap.add_argument("--lo-bp", type=int, default=None, help="MXFP4 share, overriding --budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain copy kernel of 1 GiB before the steps (reference for "
@@ -48,7 +52,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_wan14b-720p_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "video_diffusion_dit_frame_amd", "csrc", "k_attn.hip")
 
 
-def measured_traffic(workload, budget):
+def measured_traffic(workload, budget, full_bp):
     """HBM bytes per attention-kernel launch from the committed counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
     when there is none for this workload or the kernel source has changed
@@ -63,12 +67,12 @@ def measured_traffic(workload, budget):
     except OSError:
         return None
     if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload \
-            or rec.get("budget_index") != budget:
+            or rec.get("budget_bp") != budget or rec.get("full_bp", 0) != full_bp:
         return None
     return float(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, q, k, v, hi, lo):
+def cpu_baseline(w, q, k, v, hi, lo, full):
     """Time the oracle (as it stands) on one head: the full plan, then tiered
     attention on 1 query region and on 33 evenly spaced ones.  The per-head
     fixed part (operand quantization) and the per-region part follow from the
@@ -77,7 +81,7 @@ def cpu_baseline(w, q, k, v, hi, lo):
 
     qs, ks, vs = q[:1, :1].copy(), k[:1, :1].copy(), v[:1, :1].copy()
     t0 = time.perf_counter()
-    pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam)
+    pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam, full_bp=full)
     t_plan = time.perf_counter() - t0
     R = w.R
     n_many = 33
@@ -121,6 +125,9 @@ def main():
 
     w = configs.WORKLOADS[args.workload]
     hi, lo = w.budgets[args.budget]
+    hi = hi if args.hi_bp is None else args.hi_bp
+    lo = lo if args.lo_bp is None else args.lo_bp
+    full = args.full_bp
     dev = torch.device("cuda:0")
     print("[bench] generating %s inputs (B=%d H=%d N=%d d=%d)" % (w.name, w.B, w.H, w.N, w.d),
           file=sys.stderr, flush=True)
@@ -145,7 +152,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        P.plan(qd, kd, hi, lo, w.lam, 0, stream)
+        P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full)
         P.attention(qd, kd, vd, o, stream)
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
@@ -159,7 +166,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        P.plan(qd, kd, hi, lo, w.lam, 0, stream)
+        P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full)
         ev[i][1].record(stream)
         P.attention(qd, kd, vd, o, stream)
         ev[i][2].record(stream)
@@ -176,16 +183,18 @@ def main():
 
     # work accounting (head-scope quotas, identical for every (b, h))
     R = w.R
-    t8, tk = da2.quotas(R * R, hi, lo)
-    t4 = tk - t8
+    t16, t8c, tk = da2.quotas3(R * R, full, hi, lo)
     tile_flop = 4.0 * 64 * 64 * w.d
-    f8 = w.B * w.H * t8 * tile_flop
-    f4 = w.B * w.H * t4 * tile_flop
+    f16 = w.B * w.H * t16 * tile_flop
+    f8 = w.B * w.H * (t8c - t16) * tile_flop
+    f4 = w.B * w.H * (tk - t8c) * tile_flop
+    fx = f16 + f8 + f4
     dense_flop = 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
     t_attn = attn_kernel_ms * 1e-3
-    peak_eff = (f8 + f4) / (f8 / PEAK_FP8 + f4 / PEAK_FP4) if (f8 + f4) > 0 else PEAK_FP8
-    achieved = (f8 + f4) / t_attn / 1e12
-    util = (f8 / PEAK_FP8 + f4 / PEAK_FP4) / 1e12 / t_attn
+    wsum = f16 / PEAK_BF16 + f8 / PEAK_FP8 + f4 / PEAK_FP4
+    peak_eff = fx / wsum if fx > 0 else PEAK_FP8
+    achieved = fx / t_attn / 1e12
+    util = wsum / 1e12 / t_attn
 
     out = {
         "metric": "dense-equiv attention TFLOP/s + tier-weighted MFMA util, Wan-14B-720p layer",
@@ -198,11 +207,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3+mxfp4 (attention), f64 (draft scoring)",
+        "dtype": ("bf16+" if full else "") + "fp8_e4m3+mxfp4 (attention), f64 (draft scoring)",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.d,
                    "frames": w.F, "height": w.Hv, "width": w.Wv, "tokens": w.N, "regions": R,
-                   "budget_bp": {"fp8": hi, "mxfp4": lo}, "lambda": w.lam, "ranking": "head",
+                   "budget_bp": ({"bf16": full} if full else {}) | {"fp8": hi, "mxfp4": lo},
+                   "lambda": w.lam, "ranking": "head",
                    "storage": "[B,N,H,d] bf16", "output": "bf16"},
         "plan_ms": plan_ms,
         "attention_call_ms": attn_call_ms,
@@ -210,12 +220,14 @@ def main():
         "dense_equiv_tflops_attention_kernel": dense_flop / t_attn / 1e12,
         "tier_weighted_mfma_util": util,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_eff, "unit": "TFLOP/s",
-                     "frac": achieved / peak_eff, "traffic": measured_traffic(w.name, args.budget),
-                     "kernel": "k_attn", "peak_basis": "tier-weighted FP8 5.0 / FP4 10.1 PFLOP/s"},
+                     "frac": achieved / peak_eff,
+                     "traffic": measured_traffic(w.name, [hi, lo], full),
+                     "kernel": "k_attn",
+                     "peak_basis": "tier-weighted bf16 2.5 / FP8 5.0 / FP4 10.1 PFLOP/s"},
     }
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, hi, lo)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, hi, lo, full)
     print(json.dumps(out), flush=True)
 
 

@@ -377,6 +377,123 @@ __device__ __forceinline__ v8i weights_fp4(const v16f (&s)[2], float c, v16f (&a
     return p;
 }
 
+// Wait until at most n vector-memory operations of this wave are pending
+// (expcnt and lgkmcnt left alone).
+__device__ __forceinline__ constexpr int vm_wait(int n)
+{
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// 16-bit phase over the n16 key regions of list16.  A tile's key image (64
+// key rows x D channels, bf16, gathered straight from K: chunk (m, s) holds
+// for lane l key row key_of_row(l % 32, m), channels 16 s + 8 (l / 32) .. + 7)
+// fills the whole key buffer kall, its value image (the bf16 operand written
+// by the V preparation) the whole value buffer vall.  The two streams overlap
+// each other's use: the value copy of tile i runs under tile i's logits and
+// softmax, the key copy of tile i+1 under tile i's softmax and P^T V.  The
+// buffers are restrict-qualified so the compiler knows a copy into one never
+// feeds reads of the other.
+template <int D>
+__device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *__restrict__ kall,
+                                      uint8_t *__restrict__ vall, const int32_t *list16, int n16,
+                                      int a, int bh, int w, int l, int64_t hbase, v16f (&acc)[D / 32],
+                                      float &m, float &z)
+{
+    constexpr int KS = D / 16;                 // 16-channel steps of QK^T
+    constexpr int CB = D / 32;
+    constexpr int NK = KS;                     // key copies per wave and tile
+    const int hf = l >> 5;
+    const int bb = bh / A.H, hh = bh - bb * A.H;
+    const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
+    // queries of this wave as B operands (lane l: query 32 w + l % 32,
+    // channels 16 s + 8 hf .. + 7 of step s)
+    v4u q16[KS];
+    {
+        const int qt = region_token(a, 32 * w + (l & 31), A.Ry, A.Rx, A.Hv, A.Wv);
+        const uint16_t *qr = A.q + hoff + (int64_t)qt * A.osn + 8 * hf;
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+            q16[s] = *reinterpret_cast<const v4u *>(qr + 16 * s);
+    }
+    // wave w gathers the key rows of half m = w: a fixed byte offset from the
+    // key region's first token for every tile
+    const int kpos = key_of_row(l & 31, w);
+    const uint32_t koff = (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * hf) * 2);
+    const uint16_t *kh = A.k + hoff;
+    const __amdgpu_buffer_rsrc_t vsrc =
+        head_rsrc(A.v16 + hbase * (kBlk * D * 2), (int64_t)A.R * kBlk * D * 2);
+    auto issue_key = [&](int kb) {
+        const int t0 = region_token(kb, 0, A.Ry, A.Rx, A.Hv, A.Wv);
+        const __amdgpu_buffer_rsrc_t ksrc =
+            head_rsrc((const uint8_t *)(kh + (int64_t)t0 * A.osn), A.kspan);
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(kall + (w * KS + s) * 1024), 16,
+                                                     koff, 32 * s, 0, 0);
+    };
+    int kb = sload_i32(list16);
+    int kbn = n16 > 1 ? sload_i32(list16 + 1) : 0;
+    issue_key(kb);
+    for (int i = 0; i < n16; i++) {
+        // key image of tile i complete (both waves' halves); both waves are
+        // done with the value buffer
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        __syncthreads();
+        copy_kb<kBlk * D * 2 / 1024>(vsrc, (uint32_t)kb * (kBlk * D * 2), vall, w, (uint32_t)l * 16u);
+        v16f sc[2];
+        sc[0] = (v16f){};
+        sc[1] = (v16f){};
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+#pragma unroll
+            for (int mm = 0; mm < 2; mm++)
+                sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(lds_v4u(kall + ((mm * KS + s) * 64 + l) * 16)), as_bf16x8(q16[s]), sc[mm], 0,
+                    0, 0);
+        // both waves are done with the key buffer: refill it with tile i+1
+        __syncthreads();
+        const bool more = i + 1 < n16;
+        if (more)
+            issue_key(kbn);
+        const float c = A.c4;
+        const float mnew = fmaxf(m, pair_max(lane_max(sc)) * c);
+        rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
+        m = mnew;
+        const float bias = 8.0f - mnew;
+        // P^T chunk t: this lane's keys 32 hf + 8 t .. + 7 (slots 8 t ..)
+        v4u p[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const int mm = t >> 1, r0 = 8 * (t & 1);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j], c, bias));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j + 1], c, bias));
+                z += e0 + e1;
+                p[t][j] = (uint32_t)f32_to_bf16(e0) | ((uint32_t)f32_to_bf16(e1) << 16);
+            }
+        }
+        // value image of tile i complete: only the key copy may still run
+        if (more)
+            __builtin_amdgcn_s_waitcnt(vm_wait(NK));
+        else
+            __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        __syncthreads();
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(lds_v4u(vall + ((cb * 4 + t) * 64 + l) * 16)), as_bf16x8(p[t]), acc[cb], 0, 0,
+                    0);
+        kb = kbn;
+        if (i + 2 < n16)
+            kbn = sload_i32(list16 + i + 2);
+    }
+    // the quantized phases refill both buffers
+    __syncthreads();
+}
+
 template <int D>
 struct Attn {
     static constexpr int KC = D / 64;   // 64-channel steps of QK^T
@@ -477,88 +594,9 @@ struct Attn {
             kb_k = sload_i32(list + i + 3);
     }
 
-    // 16-bit phase over the n16 key regions of list16.  A tile's key image
-    // (64 key rows x D channels, bf16, gathered straight from K; chunk (m, s)
-    // holds for lane l key row key_of_row(l % 32, m), channels 16 s + 8 (l /
-    // 32) .. + 7) fills both key buffers, and its value image (the bf16
-    // operand written by the V preparation) both value buffers, so this phase
-    // is single-buffered; other workgroups on the CU cover its copies.
     __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int a, int bh)
     {
-        constexpr int KS = D / 16;   // 16-channel steps of QK^T
-        uint8_t *kall = &kbuf[0][0], *vall = &vbuf[0][0];
-        const int hf = l >> 5;
-        const int bb = bh / A.H, hh = bh - bb * A.H;
-        const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
-        // queries of this wave as B operands (lane l: query 32 w + l % 32,
-        // channels 16 s + 8 hf .. + 7 of step s)
-        v4u q16[KS];
-        {
-            const int qt = region_token(a, 32 * w + (l & 31), A.Ry, A.Rx, A.Hv, A.Wv);
-            const uint16_t *qr = A.q + hoff + (int64_t)qt * A.osn + 8 * hf;
-#pragma unroll
-            for (int s = 0; s < KS; s++)
-                q16[s] = *reinterpret_cast<const v4u *>(qr + 16 * s);
-        }
-        // wave w gathers the key rows of half m = w: a fixed byte offset from
-        // the key region's first token for every tile
-        const int kpos = key_of_row(l & 31, w);
-        const uint32_t koff =
-            (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * hf) * 2);
-        const uint16_t *kh = A.k + hoff;
-        const __amdgpu_buffer_rsrc_t vsrc =
-            head_rsrc(A.v16 + hbase * (kBlk * D * 2), (int64_t)A.R * kBlk * D * 2);
-        for (int i = 0; i < n16; i++) {
-            const int kb = sload_i32(list16 + i);
-            if (i > 0)
-                __syncthreads();   // every wave is done with the previous tile
-            const int t0 = region_token(kb, 0, A.Ry, A.Rx, A.Hv, A.Wv);
-            const __amdgpu_buffer_rsrc_t ksrc = head_rsrc((const uint8_t *)(kh + (int64_t)t0 * A.osn), A.kspan);
-#pragma unroll
-            for (int s = 0; s < KS; s++)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(kall + (w * KS + s) * 1024), 16,
-                                                         koff, 32 * s, 0, 0);
-            copy_kb<kBlk * D * 2 / 1024>(vsrc, (uint32_t)kb * (kBlk * D * 2), vall, w, (uint32_t)l * 16u);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            v16f sc[2];
-            sc[0] = (v16f){};
-            sc[1] = (v16f){};
-#pragma unroll
-            for (int s = 0; s < KS; s++)
-#pragma unroll
-                for (int mm = 0; mm < 2; mm++)
-                    sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(lds_v4u(kall + ((mm * KS + s) * 64 + l) * 16)), as_bf16x8(q16[s]), sc[mm],
-                        0, 0, 0);
-            const float c = A.c4;
-            const float mnew = fmaxf(m, pair_max(lane_max(sc)) * c);
-            rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
-            m = mnew;
-            const float bias = 8.0f - mnew;
-            // P^T chunk t: this lane's keys 32 hf + 8 t .. + 7 (slots 8 t ..)
-            v4u p[4];
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const int mm = t >> 1, r0 = 8 * (t & 1);
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j], c, bias));
-                    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j + 1], c, bias));
-                    z += e0 + e1;
-                    p[t][j] = (uint32_t)f32_to_bf16(e0) | ((uint32_t)f32_to_bf16(e1) << 16);
-                }
-            }
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-                for (int t = 0; t < 4; t++)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(lds_v4u(vall + ((cb * 4 + t) * 64 + l) * 16)), as_bf16x8(p[t]), acc[cb], 0,
-                        0, 0);
-        }
-        // the quantized phases refill these buffers
-        __syncthreads();
+        run16<D>(A, &kbuf[0][0], &vbuf[0][0], list16, n16, a, bh, w, l, hbase, acc, m, z);
     }
 };
 
