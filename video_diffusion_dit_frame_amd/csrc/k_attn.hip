@@ -116,12 +116,24 @@ __device__ __forceinline__ v8i lds32(const uint8_t *p)
     return r;
 }
 
+// A value the compiler may take from any register: the high half of a
+// 16-byte (FP4) matrix operand and the first packing target of a P word are
+// never read, so they need no instruction to set them.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wuninitialized"
+__device__ __forceinline__ int any_int()
+{
+    int x;
+    return x;
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ v8i lds16(const uint8_t *p)
 {
     uint4 a = *reinterpret_cast<const uint4 *>(p);
     v8i r;
     r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
-    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    r[4] = any_int(); r[5] = any_int(); r[6] = any_int(); r[7] = any_int();
     return r;
 }
 
@@ -251,6 +263,37 @@ __device__ __forceinline__ void read_k(const uint8_t *b, int l, KRegs<D> &K)
 }
 
 template <int D, bool FP8>
+__device__ __forceinline__ void read_k_half(const uint8_t *b, int l, int mm, KRegs<D> &K)
+{
+    constexpr int KC = D / 64;
+#pragma unroll
+    for (int kc = 0; kc < KC; kc++) {
+        const int chunk = (mm * KC + kc) * 64 + l;
+        if (FP8) {
+            K.k[mm][kc] = lds32(b + chunk * 32);
+        } else {
+            K.k[mm][kc] = lds16(b + chunk * 16);
+            K.ks[mm][kc] = b[32 * D + chunk];
+        }
+    }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void read_v_range(const uint8_t *b, int l, int c0, int c1, VRegs<D> &V)
+{
+#pragma unroll
+    for (int cb = c0; cb < c1; cb++) {
+        const int chunk = cb * 64 + l;
+        if (FP8) {
+            V.v[cb] = lds32(b + chunk * 32);
+        } else {
+            V.v[cb] = lds16(b + chunk * 16);
+            V.vs[cb] = b[32 * D + chunk];
+        }
+    }
+}
+
+template <int D, bool FP8>
 __device__ __forceinline__ void read_v(const uint8_t *b, int l, VRegs<D> &V)
 {
     constexpr int CB = D / 32;
@@ -292,89 +335,97 @@ __device__ __forceinline__ void logits(const KRegs<D> &K, const v8i (&q8)[D / 64
     }
 }
 
-// Largest of the 32 logits a lane holds: a tree of three-input maxima.
+// Largest of the 32 logits a lane holds: two independent chains of
+// three-input maxima, joined at the end.
 __device__ __forceinline__ float lane_max(const v16f (&s)[2])
 {
-    float t[8];
+    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+        a = fmaxf(fmaxf(a, s[0][r]), s[0][r + 1]);
+        b = fmaxf(fmaxf(b, s[1][r]), s[1][r + 1]);
+    }
+    return fmaxf(a, b);
+}
+
+// Running-max update of one tile: m = max(m, tile max * c), al = 2^(m_old -
+// m_new) (the factor the statistics of earlier tiles owe), Z *= al.  Returns
+// the bias 8 - m that puts the tile's weights in units of 2^-8.
+__device__ __forceinline__ float new_max(float tmax, float c, float &m, float &z, float &al)
+{
+    const float mnew = fmaxf(m, tmax * c);
+    al = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    z *= al;
+    return 8.0f - mnew;
+}
+
+// FP8 weight word Q of one tile (logits s[Q / 4][4 (Q % 4) .. + 3]):
+// e = 2^(S c8 + 8 - m) = 256 w, Z += e, P word Q = e4m3(e) (four keys) of the
+// B operand of P^T V.
+template <int Q>
+__device__ __forceinline__ void weight_word_fp8(const v16f (&s)[2], float c8, float bias, float &z, v8i &p)
+{
+    constexpr int mm = Q >> 2, r0 = 4 * (Q & 3);
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
+    const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
+    const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
+    z += (e0 + e1) + (e2 + e3);
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, any_int(), false);
+    p[Q] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
+}
+
+// MXFP4 block exponent of this lane's 32-key group: floor(log2(max e)) - 2,
+// where the group's largest logit is gm and the tile's is mx (tm = mx c).
+// The group holding the running maximum has max e = 2^8 exactly (w = 1), so
+// its exponent is fixed at 6 instead of being read from a rounded exp2 that
+// may land just below the power of two.
+__device__ __forceinline__ int fp4_exponent(float gm, float mx, float tm, float m, float c, float bias)
+{
+    if (gm == mx && m == tm)
+        return 127 + 6;
+    const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
+    const int ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
+    return ef < 0 ? 0 : ef;
+}
+
+// MXFP4 weight word Q of one tile (slots 8 Q .. 8 Q + 7 of the lane's 32-key
+// group, logits s[Q / 2][8 (Q % 2) .. + 7]), with c = log2(e)/sqrt(d) and the
+// group's scale 2^(ef - 127).
+template <int Q>
+__device__ __forceinline__ void weight_word_fp4(const v16f (&s)[2], float c, float bias, float pscale, float &z,
+                                                v8i &p)
+{
+    constexpr int mm = Q >> 1, r0 = 8 * (Q & 1);
+    float e[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const int r = 2 * j;
-        t[j] = fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1]));
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
+        z += e[j];
     }
-    return fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+    uint32_t wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((uint32_t)any_int(), e[0], e[1], pscale, 0);
+    wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
+    wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
+    p[Q] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
 }
 
-// FP8 weights of one tile: running max, e = 2^(S c8 + 8 - m) = 256 w,
-// Z += e, P = e4m3(e) as the B operand of P^T V.
-template <int CB>
-__device__ __forceinline__ v8i weights_fp8(const v16f (&s)[2], float c8, v16f (&acc)[CB], float &m,
-                                           float &z)
+// Logits of key half mm of one tile (S^T = K Q^T, FP8 codes, or MXFP4 with
+// block scales).
+template <int D, bool FP8>
+__device__ __forceinline__ void logits_half(const KRegs<D> &K, int mm, const v8i (&q8)[D / 64],
+                                            const v8i (&q4)[D / 64], const int (&q4s)[D / 64], v16f &s)
 {
-    float mx = pair_max(lane_max(s));
-    const float mnew = fmaxf(m, mx * c8);
-    rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
-    m = mnew;
-    const float bias = 8.0f - mnew;
-    v8i p;
+    constexpr int KC = D / 64;
+    s = (v16f){};
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-        const int mm = q >> 2, r0 = 4 * (q & 3);
-        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
-        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
-        float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
-        float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
-        z += (e0 + e1) + (e2 + e3);
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
-        p[q] = wd;
+    for (int kc = 0; kc < KC; kc++) {
+        if (FP8)
+            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], q8[kc], s, 0, 0, 0, 0, 0, 0);
+        else
+            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], q4[kc], s, 4, 4, 0, K.ks[mm][kc],
+                                                               0, q4s[kc]);
     }
-    return p;
-}
-
-// MXFP4 weights of one tile: as above with c = log2(e)/sqrt(d); each lane's
-// 32-key group gets the E8M0 exponent floor(log2(max e)) - 2 (returned in ef).
-template <int CB>
-__device__ __forceinline__ v8i weights_fp4(const v16f (&s)[2], float c, v16f (&acc)[CB], float &m,
-                                           float &z, int &ef)
-{
-    const float gm = lane_max(s);
-    const float mx = pair_max(gm);
-    const float tm = mx * c;
-    const float mnew = fmaxf(m, tm);
-    rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
-    m = mnew;
-    const float bias = 8.0f - mnew;
-    // The group holding the running maximum has max e = 2^8 exactly (w = 1),
-    // so its exponent is fixed at 6 instead of being read from a rounded
-    // exp2 that may land just below the power of two.
-    if (gm == mx && mnew == tm) {
-        ef = 127 + 6;
-    } else {
-        const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
-        ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
-        ef = ef < 0 ? 0 : ef;
-    }
-    const float pscale = ef ? __uint_as_float((uint32_t)ef << 23) : __uint_as_float(0x00400000u);
-    v8i p;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        // slots 8q .. 8q+7 of this lane's group; slot = 16*mm + r
-        const int mm = q >> 1, r0 = 8 * (q & 1);
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
-            z += e[j];
-        }
-        uint32_t wd = 0;
-        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[0], e[1], pscale, 0);
-        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
-        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
-        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
-        p[q] = (int)wd;
-    }
-    p[4] = 0; p[5] = 0; p[6] = 0; p[7] = 0;
-    return p;
 }
 
 // Wait until at most n vector-memory operations of this wave are pending
@@ -384,18 +435,25 @@ __device__ __forceinline__ constexpr int vm_wait(int n)
     return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// 1 KB chunk c of a 16-bit tile image held in two buffers of D/16 chunks.
+template <int D>
+__device__ __forceinline__ uint8_t *chunk16(uint8_t *b0, uint8_t *b1, int c)
+{
+    return (c < D / 16 ? b0 : b1) + (c % (D / 16)) * 1024;
+}
+
 // 16-bit phase over the n16 key regions of list16.  A tile's key image (64
 // key rows x D channels, bf16, gathered straight from K: chunk (m, s) holds
 // for lane l key row key_of_row(l % 32, m), channels 16 s + 8 (l / 32) .. + 7)
-// fills the whole key buffer kall, its value image (the bf16 operand written
-// by the V preparation) the whole value buffer vall.  The two streams overlap
-// each other's use: the value copy of tile i runs under tile i's logits and
-// softmax, the key copy of tile i+1 under tile i's softmax and P^T V.  The
-// buffers are restrict-qualified so the compiler knows a copy into one never
-// feeds reads of the other.
+// fills both key buffers (half m in buffer m), its value image (the bf16
+// operand written by the V preparation) both value buffers.  The two streams
+// overlap each other's use: the value copy of tile i runs under tile i's
+// logits and softmax, the key copy of tile i+1 under tile i's softmax and
+// P^T V.  Key and value buffers are distinct LDS variables, so the compiler
+// knows a copy into one never feeds reads of the other.
 template <int D>
-__device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *__restrict__ kall,
-                                      uint8_t *__restrict__ vall, const int32_t *list16, int n16,
+__device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
+                                      uint8_t *vb1, const int32_t *list16, int n16,
                                       int a, int bh, int w, int l, int64_t hbase, v16f (&acc)[D / 32],
                                       float &m, float &z)
 {
@@ -428,7 +486,7 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *__restrict__ k
             head_rsrc((const uint8_t *)(kh + (int64_t)t0 * A.osn), A.kspan);
 #pragma unroll
         for (int s = 0; s < KS; s++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(kall + (w * KS + s) * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)((w ? kb1 : kb0) + s * 1024), 16,
                                                      koff, 32 * s, 0, 0);
     };
     int kb = sload_i32(list16);
@@ -439,7 +497,14 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *__restrict__ k
         // done with the value buffer
         __builtin_amdgcn_s_waitcnt(vm_wait(0));
         __syncthreads();
-        copy_kb<kBlk * D * 2 / 1024>(vsrc, (uint32_t)kb * (kBlk * D * 2), vall, w, (uint32_t)l * 16u);
+#pragma unroll
+        for (int j = 0; j < kBlk * D * 2 / 2048; j++) {
+            // unit 2j + w lies in the first buffer exactly when j < D / 32
+            const int u = 2 * j + w;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vsrc, (lds_void *)((j < D / 32 ? vb0 : vb1) + (u % (D / 16)) * 1024), 16, (uint32_t)l * 16u,
+                (uint32_t)kb * (kBlk * D * 2) + u * 1024, 0, 0);
+        }
         v16f sc[2];
         sc[0] = (v16f){};
         sc[1] = (v16f){};
@@ -448,7 +513,7 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *__restrict__ k
 #pragma unroll
             for (int mm = 0; mm < 2; mm++)
                 sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(lds_v4u(kall + ((mm * KS + s) * 64 + l) * 16)), as_bf16x8(q16[s]), sc[mm], 0,
+                    as_bf16x8(lds_v4u(chunk16<D>(kb0, kb1, mm * KS + s) + l * 16)), as_bf16x8(q16[s]), sc[mm], 0,
                     0, 0);
         // both waves are done with the key buffer: refill it with tile i+1
         __syncthreads();
@@ -484,7 +549,7 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *__restrict__ k
 #pragma unroll
             for (int t = 0; t < 4; t++)
                 acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(lds_v4u(vall + ((cb * 4 + t) * 64 + l) * 16)), as_bf16x8(p[t]), acc[cb], 0, 0,
+                    as_bf16x8(lds_v4u(chunk16<D>(vb0, vb1, cb * 4 + t) + l * 16)), as_bf16x8(p[t]), acc[cb], 0, 0,
                     0);
         kb = kbn;
         if (i + 2 < n16)
@@ -494,109 +559,378 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *__restrict__ k
     __syncthreads();
 }
 
+// Instruction order inside one region of a step's main block: its LDS reads
+// first, then its matrix products spread through its vector instructions, so
+// the wave never waits for the matrix core to accept a product while it has
+// vector work to issue.
+__device__ __forceinline__ void region_pattern()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    }
+}
+
 template <int D>
 struct Attn {
     static constexpr int KC = D / 64;   // 64-channel steps of QK^T
     static constexpr int CB = D / 32;   // 32-channel blocks of the output
     const AttnArgs &A;
-    uint8_t (&kbuf)[2][kBlk * D];
-    uint8_t (&vbuf)[2][kBlk * D];
+    // key and value buffers, two of each; four distinct LDS variables, so
+    // that the compiler can tell a copy into one from a read of another
+    uint8_t *kb0, *kb1, *vb0, *vb1;
     const int32_t *list;
     int64_t hbase;
     Src src;
-    int n8, n, w, l;
+    int n8, n, w, l, hf, bh;
+    int64_t qblk;
     float qs;
     v8i q8[KC], q4[KC];
     int q4s[KC];
     v16f acc[CB];
     float m, z;
+    // Software pipeline state.  Step i forms the weights of tile i while the
+    // matrix core computes the logits of tile i+1 and P^T V of tile i-1, so
+    // the logits (S) and the weights (P, with the MXFP4 exponent e) live in
+    // two register sets each, used by steps of alternating parity.
+    v16f S0[2], S1[2];
+    v8i P0, P1;
+    int E0, E1;
+    float al;           // factor acc owes before the next P^T V (running-max change)
+    int kr0, kr1, kr2;  // key regions of tiles i, i+1, i+2 (wave-uniform)
+    float c8;           // FP8 logit scale of tile i
 
-    // Key of tile j (kind NEXT8) from its buffer; issue its logits into s.
-    template <bool NEXT8>
-    __device__ __forceinline__ void key_logits(int j, v16f (&s)[2])
+    __device__ __forceinline__ void vunits(bool to_fp8)
     {
-        KRegs<D> K;
-        read_k<D, NEXT8>(kbuf[j & 1], l, K);
-        logits<D, NEXT8>(K, q8, q4, q4s, s);
+        // change of value units: real <-> FP8 codes (per-channel V scale)
+        const float *vs = A.vs8 + (int64_t)bh * D;
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const float sv = vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
+                acc[cb][r] = to_fp8 ? acc[cb][r] / sv : acc[cb][r] * sv;
+            }
     }
 
-    // Wave-uniform values carried one tile ahead (scalar registers), so no
-    // scalar load is waited for inside a tile: key regions of the next key
-    // and value refills, and the FP8 logit scale of the current tile.
-    int kb_k, kb_v;
-    float c8;
-
-    template <bool FP8>
-    __device__ __forceinline__ void prefetch(int i)
+    // acc *= al before the next P^T V; with UNIT the FP8 -> real change of
+    // value units is applied as well (the product about to be added is the
+    // first MXFP4 one).
+    template <bool UNIT>
+    __device__ __forceinline__ void settle()
     {
-        // refill the buffers read last tile: key of tile i+2, value of tile i+1
-        if (i + 2 < n) {
-            if (FP8 && i + 2 < n8)
-                issue_k<D, true>(src, kb_k, kbuf[i & 1], w, l);
-            else
-                issue_k<D, false>(src, kb_k, kbuf[i & 1], w, l);
-        }
-        if (i + 1 < n) {
-            if (FP8 && i + 1 < n8)
-                issue_v<D, true>(src, kb_v, vbuf[(i + 1) & 1], w, l);
-            else
-                issue_v<D, false>(src, kb_v, vbuf[(i + 1) & 1], w, l);
-        }
-    }
-
-    // Tile i (kind FP8): its logits sc are ready.  Start tile i+1's logits
-    // into sn on the matrix core, then form tile i's weights on the vector
-    // unit and accumulate P^T V.
-    template <bool FP8>
-    __device__ __forceinline__ void step(int i, const v16f (&sc)[2], v16f (&sn)[2])
-    {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // LDS reads of this tile come before the refill is issued, so they
-        // never wait for it
-        VRegs<D> V;
-        read_v<D, FP8>(vbuf[i & 1], l, V);
-        KRegs<D> K;
-        const bool more = i + 1 < n, next8 = FP8 && i + 1 < n8;
-        if (more) {
-            if (next8)
-                read_k<D, true>(kbuf[(i + 1) & 1], l, K);
-            else
-                read_k<D, false>(kbuf[(i + 1) & 1], l, K);
-        }
-        prefetch<FP8>(i);
-        if (more) {
-            if (next8)
-                logits<D, true>(K, q8, q4, q4s, sn);
-            else
-                logits<D, false>(K, q8, q4, q4s, sn);
-        }
-        if (FP8) {
-            const v8i p = weights_fp8<CB>(sc, c8, acc, m, z);
+        if (UNIT) {
 #pragma unroll
             for (int cb = 0; cb < CB; cb++)
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 0, 0, 0,
-                                                                         0, 0, 0);
+                acc[cb] *= al;
+            vunits(false);
+        } else if (__any(al != 1.0f)) {
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] *= al;
+        }
+    }
+
+    template <bool FP8>
+    __device__ __forceinline__ void pv_range(const VRegs<D> &V, const v8i &p, int ef, int c0, int c1)
+    {
+        if (FP8) {
+#pragma unroll
+            for (int cb = c0; cb < c1; cb++)
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 0, 0, 0, 0, 0, 0);
         } else {
-            int ef;
-            const v8i p = weights_fp4<CB>(sc, A.c4, acc, m, z, ef);
+#pragma unroll
+            for (int cb = c0; cb < c1; cb++)
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 4, 4, 0,
+                                                                         V.vs[cb], 0, ef);
+        }
+    }
+
+    template <bool FP8>
+    __device__ __forceinline__ void pv(const VRegs<D> &V, const v8i &p, int ef)
+    {
+        if (FP8) {
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 0, 0, 0, 0, 0, 0);
+        } else {
 #pragma unroll
             for (int cb = 0; cb < CB; cb++)
                 acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 4, 4, 0,
                                                                          V.vs[cb], 0, ef);
         }
-        // scalars for the next tile, loaded after this tile's LDS reads were
-        // consumed (scalar and LDS loads share one completion counter)
-        if (next8)
-            c8 = (qs * sload_f32(A.ks8 + hbase + kb_v)) * A.c4;
-        kb_v = kb_k;
-        if (i + 3 < n)
-            kb_k = sload_i32(list + i + 3);
     }
 
-    __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int a, int bh)
+    // Step i, kinds KP (tile i-1), KCUR (tile i), KN (tile i+1) true for FP8.
+    // On entry sc holds the logits of tile i, pp / ep the weights of tile i-1
+    // (zero before the first tile), al the factor acc owes before their
+    // product.  The refills go first: K(i+2) into K(i)'s buffer kw and V(i)
+    // into V(i-2)'s buffer vw, both read for the last time in step i-1.  Then
+    // K(i+1) and V(i-1) are read from kr and vr, each half just before its
+    // products.  The four buffers are restrict-qualified so that the compiler
+    // knows a pending copy into one never feeds a read of another.  The last
+    // step computes logits of a stale key image, which are never used (kinds
+    // KN = KCUR there).
+    template <bool KP, bool KCUR, bool KN, bool UNIT>
+    __device__ __forceinline__ void step(int i, const v16f (&sc)[2], v16f (&sn)[2], const v8i &pp, int ep,
+                                         v8i &pc, int &ec, const uint8_t *__restrict__ kr,
+                                         uint8_t *__restrict__ kw, const uint8_t *__restrict__ vr,
+                                         uint8_t *__restrict__ vw)
     {
-        run16<D>(A, &kbuf[0][0], &vbuf[0][0], list16, n16, a, bh, w, l, hbase, acc, m, z);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        settle<UNIT>();
+        if (i + 2 < n) {
+            if (i + 2 < n8)
+                issue_k<D, true>(src, kr2, kw, w, l);
+            else
+                issue_k<D, false>(src, kr2, kw, w, l);
+        }
+        issue_v<D, KCUR>(src, kr0, vw, w, l);
+        // main block: weights of tile i on the vector unit, products of
+        // tiles i-1 and i+1 on the matrix core, in four regions fenced from
+        // each other.  Each region reads the operands of the next region's
+        // products from LDS, issues its own products (operands read by the
+        // region before) and forms a quarter of the weights in between:
+        //   R0: running max; read V blocks [0, CB/2)
+        //   R1: P^T V blocks [0, CB/2);  read V blocks [CB/2, CB); weights 1/4
+        //   R2: P^T V blocks [CB/2, CB); read K half 0;          weights 2/4
+        //   R3: logits half 0 (into the registers of the logits weights 1/4
+        //       and 2/4 consumed);        read K half 1;          weights 3/4
+        //   R4: logits half 1;                                    weights 4/4
+        float c, bias, pscale = 0.0f;
+        if (KCUR) {
+            c = c8;
+            bias = new_max(pair_max(lane_max(sc)), c, m, z, al);
+        } else {
+            c = A.c4;
+            const float gm = lane_max(sc);
+            const float mx = pair_max(gm);
+            bias = new_max(mx, c, m, z, al);
+            ec = fp4_exponent(gm, mx, mx * c, m, c, bias);
+            pscale = ec ? __uint_as_float((uint32_t)ec << 23) : __uint_as_float(0x00400000u);
+        }
+        VRegs<D> V;
+        KRegs<D> K;
+        read_v_range<D, KP>(vr, l, 0, CB / 2, V);
+        __builtin_amdgcn_sched_barrier(0);
+        // R1
+        pv_range<KP>(V, pp, ep, 0, CB / 2);
+        read_v_range<D, KP>(vr, l, CB / 2, CB, V);
+        if (KCUR) {
+            weight_word_fp8<0>(sc, c, bias, z, pc);
+            weight_word_fp8<1>(sc, c, bias, z, pc);
+        } else {
+            weight_word_fp4<0>(sc, c, bias, pscale, z, pc);
+        }
+        region_pattern();
+        __builtin_amdgcn_sched_barrier(0);
+        // R2
+        pv_range<KP>(V, pp, ep, CB / 2, CB);
+        read_k_half<D, KN>(kr, l, 0, K);
+        if (KCUR) {
+            weight_word_fp8<2>(sc, c, bias, z, pc);
+            weight_word_fp8<3>(sc, c, bias, z, pc);
+        } else {
+            weight_word_fp4<1>(sc, c, bias, pscale, z, pc);
+        }
+        region_pattern();
+        __builtin_amdgcn_sched_barrier(0);
+        // R3
+        logits_half<D, KN>(K, 0, q8, q4, q4s, sn[0]);
+        read_k_half<D, KN>(kr, l, 1, K);
+        if (KCUR) {
+            weight_word_fp8<4>(sc, c, bias, z, pc);
+            weight_word_fp8<5>(sc, c, bias, z, pc);
+        } else {
+            weight_word_fp4<2>(sc, c, bias, pscale, z, pc);
+        }
+        region_pattern();
+        __builtin_amdgcn_sched_barrier(0);
+        // R4
+        logits_half<D, KN>(K, 1, q8, q4, q4s, sn[1]);
+        if (KCUR) {
+            weight_word_fp8<6>(sc, c, bias, z, pc);
+            weight_word_fp8<7>(sc, c, bias, z, pc);
+        } else {
+            weight_word_fp4<3>(sc, c, bias, pscale, z, pc);
+            pc[4] = any_int(); pc[5] = any_int(); pc[6] = any_int(); pc[7] = any_int();
+        }
+        region_pattern();
+        // Z, the packed weights and the next logits are complete within the
+        // step: otherwise the compiler sinks their additions, conversions and
+        // products into the next step (keeping every weight of this tile live
+        // across the barrier, or serializing the next row maximum behind the
+        // products).
+        asm volatile("" ::"v"(z), "v"(pc), "v"(sn[0]), "v"(sn[1]));
+        // wave-uniform values of the next step, loaded without branches so
+        // that the main block stays one scheduling region (indices past the
+        // list are clamped; such values and the logit scale of an MXFP4 tile
+        // are never used)
+        kr0 = kr1;
+        kr1 = kr2;
+        kr2 = sload_i32(list + min(i + 3, n - 1));
+        c8 = (qs * sload_f32(A.ks8 + hbase + kr0)) * A.c4;
+    }
+
+    // Step i with the register sets and buffers of an even or an odd step.
+    template <bool KP, bool KCUR, bool KN, bool UNIT>
+    __device__ __forceinline__ void step_even(int i)
+    {
+        step<KP, KCUR, KN, UNIT>(i, S0, S1, P1, E1, P0, E0, kb1, kb0, vb1, vb0);
+    }
+
+    template <bool KP, bool KCUR, bool KN, bool UNIT>
+    __device__ __forceinline__ void step_odd(int i)
+    {
+        step<KP, KCUR, KN, UNIT>(i, S1, S0, P0, E0, P1, E1, kb0, kb1, vb0, vb1);
+    }
+
+    // Steps [i, end) of one kind.  Inside the loop an even step is always
+    // followed by an odd one, so only one logit set and one weight set are
+    // live between steps.
+    template <bool KP, bool KCUR, bool KN>
+    __device__ __forceinline__ void run_range(int &i, int end)
+    {
+        if (i < end && (i & 1)) {
+            step_odd<KP, KCUR, KN, false>(i);
+            ++i;
+        }
+        for (; i + 1 < end; i += 2) {
+            step_even<KP, KCUR, KN, false>(i);
+            step_odd<KP, KCUR, KN, false>(i + 1);
+        }
+        if (i < end) {
+            step_even<KP, KCUR, KN, false>(i);
+            ++i;
+        }
+    }
+
+    // Queries of this wave in one format, loaded when the first logits of
+    // that format are due, so that only one format occupies registers.
+    __device__ __forceinline__ void load_q8()
+    {
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++)
+            q8[kc] = load32(A.q8 + qblk * (kBlk * D) + ((w * KC + kc) * 64 + l) * 32);
+    }
+
+    __device__ __forceinline__ void load_q4()
+    {
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            const int chunk = (w * KC + kc) * 64 + l;
+            q4[kc] = load16(A.q4 + qblk * (kBlk * D / 2) + chunk * 16);
+            q4s[kc] = A.q4s[qblk * (2 * D) + chunk];
+        }
+    }
+
+    // The steps around the FP8 -> MXFP4 boundary, the first one odd when
+    // ODD: the last FP8 tile (its successor MXFP4), the first MXFP4 tile (its
+    // predecessor FP8), and the step that adds the first MXFP4 product (with
+    // the change of value units).
+    template <bool ODD>
+    __device__ __forceinline__ void boundary(int &i)
+    {
+        if (ODD) {
+            step_odd<true, true, false, false>(i++);
+            step_even<true, false, false, false>(i++);
+            if (i < n)
+                step_odd<false, false, false, true>(i++);
+        } else {
+            step_even<true, true, false, false>(i++);
+            step_odd<true, false, false, false>(i++);
+            if (i < n)
+                step_even<false, false, false, true>(i++);
+        }
+    }
+
+    // FP8 tiles [0, n8), then MXFP4 tiles [n8, n).
+    __device__ __forceinline__ void quantized_phases()
+    {
+        if (n == 0)
+            return;
+        if (n8 > 0)
+            load_q8();
+        else
+            load_q4();
+        // prologue: keys of tiles 0 and 1, logits of tile 0
+        kr0 = sload_i32(list);
+        kr1 = n > 1 ? sload_i32(list + 1) : 0;
+        kr2 = n > 2 ? sload_i32(list + 2) : 0;
+        if (n8 > 0)
+            issue_k<D, true>(src, kr0, kb0, w, l);
+        else
+            issue_k<D, false>(src, kr0, kb0, w, l);
+        if (n > 1) {
+            if (n8 > 1)
+                issue_k<D, true>(src, kr1, kb1, w, l);
+            else
+                issue_k<D, false>(src, kr1, kb1, w, l);
+        }
+        c8 = n8 > 0 ? (qs * sload_f32(A.ks8 + hbase + kr0)) * A.c4 : 0.0f;
+        // step 0 multiplies P = 0 into the value image of buffer 1: clear it
+        // so that no stale code can make a NaN
+#pragma unroll
+        for (int u = 0; u < kBlk * D / (128 * 16); u++)
+            *reinterpret_cast<v4u *>(vb1 + (u * 128 + threadIdx.x) * 16) = (v4u){};
+        P1 = (v8i){};
+        E1 = 127;
+        al = 1.0f;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        {
+            KRegs<D> K;
+            if (n8 > 0) {
+                read_k<D, true>(kb0, l, K);
+                logits<D, true>(K, q8, q4, q4s, S0);
+            } else {
+                read_k<D, false>(kb0, l, K);
+                logits<D, false>(K, q8, q4, q4s, S0);
+            }
+        }
+        int i = 0;
+        if (n8 > 0) {
+            // FP8 steps whose successor is FP8 (the last step counts as one
+            // when every tile is FP8)
+            run_range<true, true, true>(i, n8 == n ? n : n8 - 1);
+            if (n8 < n) {
+                load_q4();
+                if (i & 1)
+                    boundary<true>(i);
+                else
+                    boundary<false>(i);
+            }
+        }
+        run_range<false, false, false>(i, n);
+        // drain: P^T V of the last tile
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const bool last8 = n - 1 < n8;
+        VRegs<D> V;
+        const v8i pl = ((n - 1) & 1) ? P1 : P0;   // by value: a reference would keep both sets in memory
+        const int el = ((n - 1) & 1) ? E1 : E0;
+        if (last8) {
+            settle<false>();
+            read_v<D, true>(((n - 1) & 1) ? vb1 : vb0, l, V);
+            pv<true>(V, pl, el);
+            vunits(false);
+        } else {
+            if (n - 1 == n8 && n8 > 0)
+                settle<true>();
+            else
+                settle<false>();
+            read_v<D, false>(((n - 1) & 1) ? vb1 : vb0, l, V);
+            pv<false>(V, pl, el);
+        }
+    }
+
+    __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int a)
+    {
+        run16<D>(A, kb0, kb1, vb0, vb1, list16, n16, a, bh, w, l, hbase, acc, m, z);
     }
 };
 
@@ -605,8 +939,10 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 {
     constexpr int KC = D / 64;
     constexpr int CB = D / 32;
-    __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][kBlk * D];
-    __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t kb0[kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t kb1[kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb0[kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb1[kBlk * D];
 
     // XCD-aware work mapping.  Workgroups are dealt to the 8 XCDs round robin
     // (block L runs on XCD L % 8).  Every XCD walks the heads in the same
@@ -629,17 +965,12 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, hf = l >> 5;
     const int64_t qblk = (int64_t)bh * R + a;
 
-    Attn<D> S{A, kbuf, vbuf};
+    Attn<D> S{A, kb0, kb1, vb0, vb1};
     S.w = w;
     S.l = l;
-    // queries of this wave, both formats
-#pragma unroll
-    for (int kc = 0; kc < KC; kc++) {
-        const int chunk = (w * KC + kc) * 64 + l;
-        S.q8[kc] = load32(A.q8 + qblk * (kBlk * D) + chunk * 32);
-        S.q4[kc] = load16(A.q4 + qblk * (kBlk * D / 2) + chunk * 16);
-        S.q4s[kc] = A.q4s[qblk * (2 * D) + chunk];
-    }
+    S.hf = hf;
+    S.bh = bh;
+    S.qblk = qblk;
     S.qs = A.qs8[qblk];
     const int n16 = sload_i32(A.cnt + qblk * kTargets);
     const int n8 = sload_i32(A.cnt + qblk * kTargets + 1);
@@ -656,75 +987,11 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     S.z = 0.0f;
 
     if (n16 > 0) {
-        S.phase16(A.sched + qblk * R, n16, a, bh);
-        if (n8 > 0) {
-            // phase boundary: real units -> FP8 value units
-            const float *vs = A.vs8 + (int64_t)bh * D;
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    S.acc[cb][r] /= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
-        }
-    }
-
-    v16f sa[2], sb[2];
-    if (n > 0) {
-        // prologue: key and value of tile 0, key of tile 1; logits of tile 0
-        const int kb0 = sload_i32(S.list);
-        if (n8 > 0) {
-            issue_k<D, true>(S.src, kb0, kbuf[0], w, l);
-            issue_v<D, true>(S.src, kb0, vbuf[0], w, l);
-        } else {
-            issue_k<D, false>(S.src, kb0, kbuf[0], w, l);
-            issue_v<D, false>(S.src, kb0, vbuf[0], w, l);
-        }
-        if (n > 1) {
-            const int kb1 = sload_i32(S.list + 1);
-            if (n8 > 1)
-                issue_k<D, true>(S.src, kb1, kbuf[1], w, l);
-            else
-                issue_k<D, false>(S.src, kb1, kbuf[1], w, l);
-        }
-        S.kb_v = n > 1 ? sload_i32(S.list + 1) : 0;
-        S.kb_k = n > 2 ? sload_i32(S.list + 2) : 0;
-        S.c8 = n8 > 0 ? (S.qs * sload_f32(A.ks8 + S.hbase + kb0)) * A.c4 : 0.0f;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        S.phase16(A.sched + qblk * R, n16, a);
         if (n8 > 0)
-            S.template key_logits<true>(0, sa);
-        else
-            S.template key_logits<false>(0, sa);
+            S.vunits(true);   // phase boundary: real units -> FP8 value units
     }
-    // Tiles alternate between the two logit registers sets; the loops are
-    // unrolled by two so that no copy is needed between tiles.
-    int i = 0;
-    while (i < n8) {
-        S.template step<true>(i, sa, sb);
-        if (++i >= n8) {
-            sa[0] = sb[0];
-            sa[1] = sb[1];
-            break;
-        }
-        S.template step<true>(i, sb, sa);
-        ++i;
-    }
-    if (n8 > 0) {
-        // phase boundary: FP8 value units -> real units (per-channel V scale)
-        const float *vs = A.vs8 + (int64_t)bh * D;
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-            for (int r = 0; r < 16; r++)
-                S.acc[cb][r] *= vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
-    }
-    while (i < n) {
-        S.template step<false>(i, sa, sb);
-        if (++i >= n)
-            break;
-        S.template step<false>(i, sb, sa);
-        ++i;
-    }
+    S.quantized_phases();
 
     // ---------------- epilogue: normalize and restore token order ----------------
     const float zt = pair_sum(S.z);
