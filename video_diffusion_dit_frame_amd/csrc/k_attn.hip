@@ -126,6 +126,11 @@ __device__ __forceinline__ int any_int()
     int x;
     return x;
 }
+__device__ __forceinline__ v16f any_v16f()
+{
+    v16f x;
+    return x;
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ v8i lds16(const uint8_t *p)
@@ -310,29 +315,25 @@ __device__ __forceinline__ void read_v(const uint8_t *b, int l, VRegs<D> &V)
 }
 
 // Logits S^T = K Q^T of one tile (FP8 codes, or MXFP4 with block scales).
+// The query operand qv[kc] holds the FP8 codes of its 64 channels, or the
+// MXFP4 codes in dwords 0-3 and the E8M0 exponent in dword 4.
 template <int D, bool FP8>
-__device__ __forceinline__ void logits(const KRegs<D> &K, const v8i (&q8)[D / 64],
-                                       const v8i (&q4)[D / 64], const int (&q4s)[D / 64],
-                                       v16f (&s)[2])
+__device__ __forceinline__ void logits(const KRegs<D> &K, const v8i (&qv)[D / 64], v16f (&s)[2])
 {
     constexpr int KC = D / 64;
     s[0] = (v16f){};
     s[1] = (v16f){};
-    if (FP8) {
 #pragma unroll
-        for (int kc = 0; kc < KC; kc++)
+    for (int kc = 0; kc < KC; kc++)
 #pragma unroll
-            for (int mm = 0; mm < 2; mm++)
-                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], q8[kc], s[mm], 0,
-                                                                       0, 0, 0, 0, 0);
-    } else {
-#pragma unroll
-        for (int kc = 0; kc < KC; kc++)
-#pragma unroll
-            for (int mm = 0; mm < 2; mm++)
-                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    K.k[mm][kc], q4[kc], s[mm], 4, 4, 0, K.ks[mm][kc], 0, q4s[kc]);
-    }
+        for (int mm = 0; mm < 2; mm++) {
+            if (FP8)
+                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s[mm], 0, 0, 0, 0,
+                                                                       0, 0);
+            else
+                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s[mm], 4, 4, 0,
+                                                                       K.ks[mm][kc], 0, qv[kc][4]);
+        }
 }
 
 // Largest of the 32 logits a lane holds: two independent chains of
@@ -411,20 +412,19 @@ __device__ __forceinline__ void weight_word_fp4(const v16f (&s)[2], float c, flo
 }
 
 // Logits of key half mm of one tile (S^T = K Q^T, FP8 codes, or MXFP4 with
-// block scales).
+// block scales; query operand as in logits).
 template <int D, bool FP8>
-__device__ __forceinline__ void logits_half(const KRegs<D> &K, int mm, const v8i (&q8)[D / 64],
-                                            const v8i (&q4)[D / 64], const int (&q4s)[D / 64], v16f &s)
+__device__ __forceinline__ void logits_half(const KRegs<D> &K, int mm, const v8i (&qv)[D / 64], v16f &s)
 {
     constexpr int KC = D / 64;
     s = (v16f){};
 #pragma unroll
     for (int kc = 0; kc < KC; kc++) {
         if (FP8)
-            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], q8[kc], s, 0, 0, 0, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s, 0, 0, 0, 0, 0, 0);
         else
-            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], q4[kc], s, 4, 4, 0, K.ks[mm][kc],
-                                                               0, q4s[kc]);
+            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s, 4, 4, 0, K.ks[mm][kc],
+                                                               0, qv[kc][4]);
     }
 }
 
@@ -574,6 +574,8 @@ __device__ __forceinline__ void region_pattern()
     }
 }
 
+// One attention workgroup's state: two waves, one query region (wave w owns
+// queries 32 w .. 32 w + 31).
 template <int D>
 struct Attn {
     static constexpr int KC = D / 64;   // 64-channel steps of QK^T
@@ -582,14 +584,13 @@ struct Attn {
     // key and value buffers, two of each; four distinct LDS variables, so
     // that the compiler can tell a copy into one from a read of another
     uint8_t *kb0, *kb1, *vb0, *vb1;
-    const int32_t *list;
+    const int32_t *list;   // key regions of the tiles, in phase order
     int64_t hbase;
     Src src;
     int n8, n, w, l, hf, bh;
     int64_t qblk;
     float qs;
-    v8i q8[KC], q4[KC];
-    int q4s[KC];
+    v8i qv[KC];   // this wave's queries in the format of the next logits (see logits)
     v16f acc[CB];
     float m, z;
     // Software pipeline state.  Step i forms the weights of tile i while the
@@ -605,14 +606,19 @@ struct Attn {
 
     __device__ __forceinline__ void vunits(bool to_fp8)
     {
-        // change of value units: real <-> FP8 codes (per-channel V scale)
-        const float *vs = A.vs8 + (int64_t)bh * D;
+        // change of value units: real <-> FP8 codes (per-channel V scale).
+        // The scales are loaded where they are used (volatile): loaded once
+        // for both uses, they would stay in 64 registers through the phases.
+        const volatile float4 *vs = reinterpret_cast<const volatile float4 *>(A.vs8 + (int64_t)bh * D);
 #pragma unroll
         for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float sv = vs[32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3)];
-                acc[cb][r] = to_fp8 ? acc[cb][r] / sv : acc[cb][r] * sv;
+            for (int g = 0; g < 4; g++) {
+                const float4 sv = const_cast<const float4 &>(vs[(32 * cb + 8 * g + 4 * hf) / 4]);
+                const float f[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+                for (int t = 0; t < 4; t++)
+                    acc[cb][4 * g + t] = to_fp8 ? acc[cb][4 * g + t] / f[t] : acc[cb][4 * g + t] * f[t];
             }
     }
 
@@ -649,31 +655,14 @@ struct Attn {
         }
     }
 
-    template <bool FP8>
-    __device__ __forceinline__ void pv(const VRegs<D> &V, const v8i &p, int ef)
-    {
-        if (FP8) {
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 0, 0, 0, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 4, 4, 0,
-                                                                         V.vs[cb], 0, ef);
-        }
-    }
-
     // Step i, kinds KP (tile i-1), KCUR (tile i), KN (tile i+1) true for FP8.
     // On entry sc holds the logits of tile i, pp / ep the weights of tile i-1
     // (zero before the first tile), al the factor acc owes before their
-    // product.  The refills go first: K(i+2) into K(i)'s buffer kw and V(i)
-    // into V(i-2)'s buffer vw, both read for the last time in step i-1.  Then
-    // K(i+1) and V(i-1) are read from kr and vr, each half just before its
-    // products.  The four buffers are restrict-qualified so that the compiler
-    // knows a pending copy into one never feeds a read of another.  The last
-    // step computes logits of a stale key image, which are never used (kinds
-    // KN = KCUR there).
+    // product.  The refills go first: K(i+2)
+    // into K(i)'s buffer kw and V(i) into V(i-2)'s buffer vw, both read for
+    // the last time in step i-1.  Then K(i+1) and V(i-1) are read from kr and
+    // vr, each half just before its products.  The last step computes logits
+    // of a stale key image, which are never used (kinds KN = KCUR there).
     template <bool KP, bool KCUR, bool KN, bool UNIT>
     __device__ __forceinline__ void step(int i, const v16f (&sc)[2], v16f (&sn)[2], const v8i &pp, int ep,
                                          v8i &pc, int &ec, const uint8_t *__restrict__ kr,
@@ -690,11 +679,13 @@ struct Attn {
                 issue_k<D, false>(src, kr2, kw, w, l);
         }
         issue_v<D, KCUR>(src, kr0, vw, w, l);
-        // main block: weights of tile i on the vector unit, products of
-        // tiles i-1 and i+1 on the matrix core, in four regions fenced from
-        // each other.  Each region reads the operands of the next region's
-        // products from LDS, issues its own products (operands read by the
-        // region before) and forms a quarter of the weights in between:
+        VRegs<D> V;
+        KRegs<D> K;
+        // main block: weights of tile i on the vector unit, products of tiles
+        // i-1 and i+1 on the matrix core, in regions fenced from each other.
+        // Each region reads the operands of the next region's products from
+        // LDS, issues its own products (operands read by the region before)
+        // and forms a quarter of the weights:
         //   R0: running max; read V blocks [0, CB/2)
         //   R1: P^T V blocks [0, CB/2);  read V blocks [CB/2, CB); weights 1/4
         //   R2: P^T V blocks [CB/2, CB); read K half 0;          weights 2/4
@@ -713,8 +704,6 @@ struct Attn {
             ec = fp4_exponent(gm, mx, mx * c, m, c, bias);
             pscale = ec ? __uint_as_float((uint32_t)ec << 23) : __uint_as_float(0x00400000u);
         }
-        VRegs<D> V;
-        KRegs<D> K;
         read_v_range<D, KP>(vr, l, 0, CB / 2, V);
         __builtin_amdgcn_sched_barrier(0);
         // R1
@@ -740,7 +729,7 @@ struct Attn {
         region_pattern();
         __builtin_amdgcn_sched_barrier(0);
         // R3
-        logits_half<D, KN>(K, 0, q8, q4, q4s, sn[0]);
+        logits_half<D, KN>(K, 0, qv, sn[0]);
         read_k_half<D, KN>(kr, l, 1, K);
         if (KCUR) {
             weight_word_fp8<4>(sc, c, bias, z, pc);
@@ -751,7 +740,7 @@ struct Attn {
         region_pattern();
         __builtin_amdgcn_sched_barrier(0);
         // R4
-        logits_half<D, KN>(K, 1, q8, q4, q4s, sn[1]);
+        logits_half<D, KN>(K, 1, qv, sn[1]);
         if (KCUR) {
             weight_word_fp8<6>(sc, c, bias, z, pc);
             weight_word_fp8<7>(sc, c, bias, z, pc);
@@ -789,66 +778,45 @@ struct Attn {
         step<KP, KCUR, KN, UNIT>(i, S1, S0, P0, E0, P1, E1, kb0, kb1, vb0, vb1);
     }
 
-    // Steps [i, end) of one kind.  Inside the loop an even step is always
-    // followed by an odd one, so only one logit set and one weight set are
-    // live between steps.
-    template <bool KP, bool KCUR, bool KN>
-    __device__ __forceinline__ void run_range(int &i, int end)
+    template <bool ODD, bool KP, bool KCUR, bool KN, bool UNIT>
+    __device__ __forceinline__ void step_par(int i)
     {
-        if (i < end && (i & 1)) {
-            step_odd<KP, KCUR, KN, false>(i);
-            ++i;
-        }
-        for (; i + 1 < end; i += 2) {
-            step_even<KP, KCUR, KN, false>(i);
-            step_odd<KP, KCUR, KN, false>(i + 1);
-        }
-        if (i < end) {
-            step_even<KP, KCUR, KN, false>(i);
-            ++i;
-        }
+        if (ODD)
+            step_odd<KP, KCUR, KN, UNIT>(i);
+        else
+            step_even<KP, KCUR, KN, UNIT>(i);
     }
 
     // Queries of this wave in one format, loaded when the first logits of
-    // that format are due, so that only one format occupies registers.
+    // that format are due, into the one query operand set.
     __device__ __forceinline__ void load_q8()
     {
 #pragma unroll
         for (int kc = 0; kc < KC; kc++)
-            q8[kc] = load32(A.q8 + qblk * (kBlk * D) + ((w * KC + kc) * 64 + l) * 32);
+            qv[kc] = load32(A.q8 + qblk * (kBlk * D) + ((w * KC + kc) * 64 + l) * 32);
     }
 
+    // (volatile: a second load before the MXFP4 loop gives the loop its
+    // own short live range instead of one spanning the phase boundary)
     __device__ __forceinline__ void load_q4()
     {
 #pragma unroll
         for (int kc = 0; kc < KC; kc++) {
             const int chunk = (w * KC + kc) * 64 + l;
-            q4[kc] = load16(A.q4 + qblk * (kBlk * D / 2) + chunk * 16);
-            q4s[kc] = A.q4s[qblk * (2 * D) + chunk];
+            const uint4 c = const_cast<const uint4 &>(
+                *reinterpret_cast<const volatile uint4 *>(A.q4 + qblk * (kBlk * D / 2) + chunk * 16));
+            qv[kc][0] = c.x;
+            qv[kc][1] = c.y;
+            qv[kc][2] = c.z;
+            qv[kc][3] = c.w;
+            qv[kc][4] = *(const volatile uint8_t *)(A.q4s + qblk * (2 * D) + chunk);
         }
     }
 
-    // The steps around the FP8 -> MXFP4 boundary, the first one odd when
-    // ODD: the last FP8 tile (its successor MXFP4), the first MXFP4 tile (its
-    // predecessor FP8), and the step that adds the first MXFP4 product (with
-    // the change of value units).
-    template <bool ODD>
-    __device__ __forceinline__ void boundary(int &i)
-    {
-        if (ODD) {
-            step_odd<true, true, false, false>(i++);
-            step_even<true, false, false, false>(i++);
-            if (i < n)
-                step_odd<false, false, false, true>(i++);
-        } else {
-            step_even<true, true, false, false>(i++);
-            step_odd<true, false, false, false>(i++);
-            if (i < n)
-                step_even<false, false, false, true>(i++);
-        }
-    }
-
-    // FP8 tiles [0, n8), then MXFP4 tiles [n8, n).
+    // FP8 tiles [0, n8), then MXFP4 tiles [n8, n).  Step i uses the register
+    // sets and buffers of parity (i + off) % 2, with off = 1 - n8 % 2: the
+    // last FP8 step is then always even, so every step's sets and buffers are
+    // fixed at compile time (a lead-in step absorbs the choice).
     __device__ __forceinline__ void quantized_phases()
     {
         if (n == 0)
@@ -857,27 +825,32 @@ struct Attn {
             load_q8();
         else
             load_q4();
+        const bool off = !(n8 & 1);
         // prologue: keys of tiles 0 and 1, logits of tile 0
         kr0 = sload_i32(list);
         kr1 = n > 1 ? sload_i32(list + 1) : 0;
         kr2 = n > 2 ? sload_i32(list + 2) : 0;
+        uint8_t *k0 = off ? kb1 : kb0, *k1 = off ? kb0 : kb1;
         if (n8 > 0)
-            issue_k<D, true>(src, kr0, kb0, w, l);
+            issue_k<D, true>(src, kr0, k0, w, l);
         else
-            issue_k<D, false>(src, kr0, kb0, w, l);
+            issue_k<D, false>(src, kr0, k0, w, l);
         if (n > 1) {
             if (n8 > 1)
-                issue_k<D, true>(src, kr1, kb1, w, l);
+                issue_k<D, true>(src, kr1, k1, w, l);
             else
-                issue_k<D, false>(src, kr1, kb1, w, l);
+                issue_k<D, false>(src, kr1, k1, w, l);
         }
         c8 = n8 > 0 ? (qs * sload_f32(A.ks8 + hbase + kr0)) * A.c4 : 0.0f;
-        // step 0 multiplies P = 0 into the value image of buffer 1: clear it
-        // so that no stale code can make a NaN
+        // step 0 multiplies P = 0 into the value buffer of the other parity:
+        // clear it so that no stale code can make a NaN
+        uint8_t *vz = off ? vb0 : vb1;
 #pragma unroll
         for (int u = 0; u < kBlk * D / (128 * 16); u++)
-            *reinterpret_cast<v4u *>(vb1 + (u * 128 + threadIdx.x) * 16) = (v4u){};
+            *reinterpret_cast<v4u *>(vz + (u * 128 + threadIdx.x) * 16) = (v4u){};
+        P0 = (v8i){};
         P1 = (v8i){};
+        E0 = 127;
         E1 = 127;
         al = 1.0f;
         __builtin_amdgcn_s_waitcnt(0);
@@ -885,37 +858,61 @@ struct Attn {
         {
             KRegs<D> K;
             if (n8 > 0) {
-                read_k<D, true>(kb0, l, K);
-                logits<D, true>(K, q8, q4, q4s, S0);
+                read_k<D, true>(k0, l, K);
+                if (off)
+                    logits<D, true>(K, qv, S1);
+                else
+                    logits<D, true>(K, qv, S0);
             } else {
-                read_k<D, false>(kb0, l, K);
-                logits<D, false>(K, q8, q4, q4s, S0);
+                read_k<D, false>(k0, l, K);
+                logits<D, false>(K, qv, S1);   // n8 = 0: off
             }
         }
         int i = 0;
         if (n8 > 0) {
-            // FP8 steps whose successor is FP8 (the last step counts as one
-            // when every tile is FP8)
-            run_range<true, true, true>(i, n8 == n ? n : n8 - 1);
-            if (n8 < n) {
+            // FP8 steps whose successor is FP8, except the last FP8 step
+            if (off) {
+                step_odd<true, true, true, false>(0);
+                i = 1;
+            }
+            for (; i < n8 - 1; i += 2) {
+                step_even<true, true, true, false>(i);
+                step_odd<true, true, true, false>(i + 1);
+            }
+            // the last FP8 step (even), then the first MXFP4 step (odd) and
+            // the step adding the first MXFP4 product (even)
+            if (n8 == n) {
+                step_even<true, true, true, false>(i++);
+            } else {
                 load_q4();
-                if (i & 1)
-                    boundary<true>(i);
-                else
-                    boundary<false>(i);
+                step_even<true, true, false, false>(i++);
+                step_odd<true, false, false, false>(i++);
+                if (i < n)
+                    step_even<false, false, false, true>(i++);
             }
         }
-        run_range<false, false, false>(i, n);
-        // drain: P^T V of the last tile
+        // MXFP4 steps, starting odd
+        if (n8 > 0 && i + 1 < n)
+            load_q4();
+        for (; i + 1 < n; i += 2) {
+            step_odd<false, false, false, false>(i);
+            step_even<false, false, false, false>(i + 1);
+        }
+        if (i < n)
+            step_odd<false, false, false, false>(i);
+        // drain: P^T V of the last tile, and the change of value units when
+        // the last product added is an FP8 one, or when the first MXFP4
+        // product is the last
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         const bool last8 = n - 1 < n8;
+        const bool lodd = (n - 1 + (int)off) & 1;
         VRegs<D> V;
-        const v8i pl = ((n - 1) & 1) ? P1 : P0;   // by value: a reference would keep both sets in memory
-        const int el = ((n - 1) & 1) ? E1 : E0;
+        const v8i pl = lodd ? P1 : P0;   // by value: a reference would keep both sets in memory
+        const int el = lodd ? E1 : E0;
         if (last8) {
             settle<false>();
-            read_v<D, true>(((n - 1) & 1) ? vb1 : vb0, l, V);
+            read_v<D, true>(lodd ? vb1 : vb0, l, V);
             pv<true>(V, pl, el);
             vunits(false);
         } else {
@@ -923,22 +920,73 @@ struct Attn {
                 settle<true>();
             else
                 settle<false>();
-            read_v<D, false>(((n - 1) & 1) ? vb1 : vb0, l, V);
+            read_v<D, false>(lodd ? vb1 : vb0, l, V);
             pv<false>(V, pl, el);
         }
+    }
+
+    template <bool FP8>
+    __device__ __forceinline__ void pv(const VRegs<D> &V, const v8i &p, int ef)
+    {
+        pv_range<FP8>(V, p, ef, 0, CB);
     }
 
     __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int a)
     {
         run16<D>(A, kb0, kb1, vb0, vb1, list16, n16, a, bh, w, l, hbase, acc, m, z);
     }
+
+    // O = acc / Z for this wave's 32 queries of region a, written straight to
+    // their original token positions (the restore)
+    __device__ __forceinline__ void epilogue(int a)
+    {
+        const float zt = pair_sum(z);
+        const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
+        const int qi = 32 * w + (l & 31);
+        const int tok = region_token(a, qi, A.Ry, A.Rx, A.Hv, A.Wv);
+        const int b = bh / A.H, h = bh - b * A.H;
+        const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)tok * A.osn;
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int c0 = 32 * cb + 8 * g + 4 * hf;
+                float o0 = acc[cb][4 * g] * inv, o1 = acc[cb][4 * g + 1] * inv;
+                float o2 = acc[cb][4 * g + 2] * inv, o3 = acc[cb][4 * g + 3] * inv;
+                if (A.out_f32) {
+                    *reinterpret_cast<float4 *>((float *)A.out + obase + c0) = make_float4(o0, o1, o2, o3);
+                } else {
+                    uint2 pk;
+                    pk.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+                    pk.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
+                    *reinterpret_cast<uint2 *>((uint16_t *)A.out + obase + c0) = pk;
+                }
+            }
+    }
+
+    __device__ __forceinline__ void init(int w_, int bh_, int64_t qblk_)
+    {
+        w = w_;
+        l = threadIdx.x & 63;
+        hf = l >> 5;
+        bh = bh_;
+        qblk = qblk_;
+        qs = A.qs8[qblk_];
+        hbase = (int64_t)bh_ * A.R;
+        src = head_sources<D>(A, hbase, A.R);
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+            acc[cb] = (v16f){};
+        m = -__builtin_huge_valf();
+        z = 0.0f;
+    }
 };
 
+// One query region per workgroup: 16-bit phase (if any), then the FP8 and
+// MXFP4 phases.
 template <int D>
 __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 {
-    constexpr int KC = D / 64;
-    constexpr int CB = D / 32;
     __shared__ __attribute__((aligned(1024))) uint8_t kb0[kBlk * D];
     __shared__ __attribute__((aligned(1024))) uint8_t kb1[kBlk * D];
     __shared__ __attribute__((aligned(1024))) uint8_t vb0[kBlk * D];
@@ -962,60 +1010,23 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
         return;
     const int RF = A.Ry * A.Rx, NF = R / RF;
     const int a = (j % NF) * RF + j / NF;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, hf = l >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t qblk = (int64_t)bh * R + a;
 
     Attn<D> S{A, kb0, kb1, vb0, vb1};
-    S.w = w;
-    S.l = l;
-    S.hf = hf;
-    S.bh = bh;
-    S.qblk = qblk;
-    S.qs = A.qs8[qblk];
+    S.init(w, bh, qblk);
     const int n16 = sload_i32(A.cnt + qblk * kTargets);
     const int n8 = sload_i32(A.cnt + qblk * kTargets + 1);
-    const int n = n8 + sload_i32(A.cnt + qblk * kTargets + 2);
     S.n8 = n8;
-    S.n = n;
+    S.n = n8 + sload_i32(A.cnt + qblk * kTargets + 2);
     S.list = A.sched + qblk * R + n16;
-    S.hbase = (int64_t)bh * R;
-    S.src = head_sources<D>(A, S.hbase, R);
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-        S.acc[cb] = (v16f){};
-    S.m = -__builtin_huge_valf();
-    S.z = 0.0f;
-
     if (n16 > 0) {
         S.phase16(A.sched + qblk * R, n16, a);
         if (n8 > 0)
             S.vunits(true);   // phase boundary: real units -> FP8 value units
     }
     S.quantized_phases();
-
-    // ---------------- epilogue: normalize and restore token order ----------------
-    const float zt = pair_sum(S.z);
-    const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
-    const int qi = 32 * w + (l & 31);
-    const int tok = region_token(a, qi, A.Ry, A.Rx, A.Hv, A.Wv);
-    const int b = bh / A.H, h = bh - b * A.H;
-    const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)tok * A.osn;
-#pragma unroll
-    for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const int c0 = 32 * cb + 8 * g + 4 * hf;
-            float o0 = S.acc[cb][4 * g] * inv, o1 = S.acc[cb][4 * g + 1] * inv;
-            float o2 = S.acc[cb][4 * g + 2] * inv, o3 = S.acc[cb][4 * g + 3] * inv;
-            if (A.out_f32) {
-                *reinterpret_cast<float4 *>((float *)A.out + obase + c0) = make_float4(o0, o1, o2, o3);
-            } else {
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
-                pk.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
-                *reinterpret_cast<uint2 *>((uint16_t *)A.out + obase + c0) = pk;
-            }
-        }
+    S.epilogue(a);
 }
 
 }  // namespace
