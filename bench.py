@@ -74,7 +74,8 @@ def measured_traffic(workload, budget, full_bp):
 
 def cpu_baseline(w, q, k, v, hi, lo, full):
     """Time the oracle (as it stands) on one head: the full plan, then tiered
-    attention on 1 query region and on 33 evenly spaced ones.  The per-head
+    attention on 1 query region and on 401 evenly spaced ones (about 10 s of
+    CPU work on 16 host cores).  The per-head
     fixed part (operand quantization) and the per-region part follow from the
     two timings; the head total is extrapolated to all regions and heads."""
     from oracle import oracle as O
@@ -84,7 +85,7 @@ def cpu_baseline(w, q, k, v, hi, lo, full):
     pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam, full_bp=full)
     t_plan = time.perf_counter() - t0
     R = w.R
-    n_many = 33
+    n_many = 401
     sel1 = np.array([R // 2], np.int32)
     selm = np.array([(j * R) // n_many for j in range(n_many)], np.int32)
     t0 = time.perf_counter()
