@@ -692,15 +692,101 @@ typedef struct {
     double Z;
 } row_trace;
 
-static void attention_row(const head_ops *h, const uint8_t *tier_row, int u,
-                          double *out, row_trace *tr)
+/* Online-softmax state of one query row (App. B.4): running max m, sum Z
+ * of the unquantized weights, unnormalised output acc[d]. */
+typedef struct {
+    double m, Z;
+    double *acc;
+} row_acc;
+
+/* One tile of up to 64 keys at tier p: key j < nk has operand rows
+ * kt + j d and vt + j d; keys j >= nk (past the valid prefix keys, App. C.1)
+ * take no part: they add no weight and do not move the running max.  s, w
+ * and wq receive the tile's logits, weights and quantized weights (zero
+ * past nk; s is -inf there). */
+static void tile_exact(row_acc *st, int d, int p, const double *qu, const double *kt,
+                       const double *vt, int nk, double *s, double *w, double *wq)
+{
+    double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double tmax = -INFINITY;
+    for (int j = 0; j < OR_BLK; j++) {
+        s[j] = -INFINITY;
+        if (j >= nk)
+            continue;
+        const double *kv = kt + (size_t)j * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; c++)
+            dot += qu[c] * kv[c];
+        s[j] = dot * inv_sqrt_d;
+        if (s[j] > tmax) tmax = s[j];
+    }
+    double mn = tmax > st->m ? tmax : st->m;
+    double alpha = (st->m == -INFINITY) ? 0.0 : exp(st->m - mn);
+    st->Z *= alpha;
+    for (int c = 0; c < d; c++)
+        st->acc[c] *= alpha;
+    for (int j = 0; j < OR_BLK; j++) {
+        w[j] = j < nk ? exp(s[j] - mn) : 0.0;
+        st->Z += w[j];
+    }
+    quant_weights(p, w, wq);
+    for (int j = 0; j < nk; j++) {
+        const double *vv = vt + (size_t)j * d;
+        for (int c = 0; c < d; c++)
+            st->acc[c] += wq[j] * vv[c];
+    }
+    st->m = mn;
+}
+
+/* Text prefix of one head (App. C.1): Lp prefix tokens in their own order,
+ * of which the first nv are valid keys.  Prefix interactions are computed
+ * at tier pt (16: the 16-bit path; 32: unquantized, for the invariants). */
+typedef struct {
+    int Lp, nv, pt;
+    const double *qf, *kf, *vf; /* [Lp][d] */
+} prefix_ops;
+
+/* The prefix segment of a row: tiles of 64 consecutive prefix keys,
+ * ascending, the last one ragged.  Processed before the video tiles. */
+static void prefix_segment(row_acc *st, int d, const prefix_ops *px, const double *qu,
+                           row_trace *tr)
+{
+    double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
+    if (!px)
+        return;
+    for (int t = 0; OR_BLK * t < px->nv; t++) {
+        int nk = px->nv - OR_BLK * t < OR_BLK ? px->nv - OR_BLK * t : OR_BLK;
+        tile_exact(st, d, px->pt, qu, px->kf + (size_t)OR_BLK * t * d,
+                   px->vf + (size_t)OR_BLK * t * d, nk, s, w, wq);
+        if (tr) {
+            for (int j = 0; j < nk && tr->n < tr->cap; j++, tr->n++) {
+                tr->key[tr->n] = -1 - (OR_BLK * t + j);
+                tr->tier[tr->n] = px->pt;
+                tr->s[tr->n] = s[j];
+                tr->w[tr->n] = w[j];
+                tr->wq[tr->n] = wq[j];
+                tr->m[tr->n] = st->m;
+            }
+        }
+    }
+}
+
+static void finish_row(const row_acc *st, int d, double *out)
+{
+    for (int c = 0; c < d; c++)
+        out[c] = st->Z > 0.0 ? st->acc[c] / st->Z : 0.0;
+}
+
+/* Video query row u (reordered position): the prefix segment (if any), then
+ * the phases in descending precision over the kept video tiles. */
+static void attention_row(const head_ops *h, const prefix_ops *px, const uint8_t *tier_row,
+                          int u, double *out, row_trace *tr)
 {
     int d = h->d, R = h->R;
-    double inv_sqrt_d = 1.0 / sqrt((double)d);
-    double m = -INFINITY, Z = 0.0;
-    double *acc = calloc(d, sizeof(double));
+    row_acc st = {-INFINITY, 0.0, calloc(d, sizeof(double))};
     double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
     static const int phases[4] = {32, 16, 8, 4};
+    prefix_segment(&st, d, px, h->qf + (size_t)u * d, tr);
     for (int ph = 0; ph < 4; ph++) {
         int p = phases[ph];
         const double *Q = p >= 16 ? h->qf : (p == 8 ? h->q8 : h->q4);
@@ -709,31 +795,8 @@ static void attention_row(const head_ops *h, const uint8_t *tier_row, int u,
         for (int b = 0; b < R; b++) {
             if (tier_row[b] != p)
                 continue;
-            double tmax = -INFINITY;
-            for (int j = 0; j < OR_BLK; j++) {
-                const double *qu = Q + (size_t)u * d, *kv = K + ((size_t)b * OR_BLK + j) * d;
-                double dot = 0.0;
-                for (int c = 0; c < d; c++)
-                    dot += qu[c] * kv[c];
-                s[j] = dot * inv_sqrt_d;
-                if (s[j] > tmax) tmax = s[j];
-            }
-            double mn = tmax > m ? tmax : m;
-            double alpha = (m == -INFINITY) ? 0.0 : exp(m - mn);
-            Z *= alpha;
-            for (int c = 0; c < d; c++)
-                acc[c] *= alpha;
-            for (int j = 0; j < OR_BLK; j++) {
-                w[j] = exp(s[j] - mn);
-                Z += w[j];
-            }
-            quant_weights(p, w, wq);
-            for (int j = 0; j < OR_BLK; j++) {
-                const double *vv = V + ((size_t)b * OR_BLK + j) * d;
-                for (int c = 0; c < d; c++)
-                    acc[c] += wq[j] * vv[c];
-            }
-            m = mn;
+            tile_exact(&st, d, p, Q + (size_t)u * d, K + (size_t)b * OR_BLK * d,
+                       V + (size_t)b * OR_BLK * d, OR_BLK, s, w, wq);
             if (tr) {
                 for (int j = 0; j < OR_BLK && tr->n < tr->cap; j++, tr->n++) {
                     tr->key[tr->n] = b * OR_BLK + j;
@@ -741,16 +804,31 @@ static void attention_row(const head_ops *h, const uint8_t *tier_row, int u,
                     tr->s[tr->n] = s[j];
                     tr->w[tr->n] = w[j];
                     tr->wq[tr->n] = wq[j];
-                    tr->m[tr->n] = mn;
+                    tr->m[tr->n] = st.m;
                 }
             }
         }
     }
-    for (int c = 0; c < d; c++)
-        out[c] = Z > 0.0 ? acc[c] / Z : 0.0;
+    finish_row(&st, d, out);
     if (tr)
-        tr->Z = Z;
-    free(acc);
+        tr->Z = st.Z;
+    free(st.acc);
+}
+
+/* Prefix query row i (App. C.1: non-sparse attention): every valid prefix
+ * key, then every video region ascending, all at the prefix tier. */
+static void attention_prefix_row(const head_ops *h, const prefix_ops *px, int i, double *out)
+{
+    int d = h->d, R = h->R;
+    row_acc st = {-INFINITY, 0.0, calloc(d, sizeof(double))};
+    double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
+    const double *qu = px->qf + (size_t)i * d;
+    prefix_segment(&st, d, px, qu, NULL);
+    for (int b = 0; b < R; b++)
+        tile_exact(&st, d, px->pt, qu, h->kf + (size_t)b * OR_BLK * d,
+                   h->vf + (size_t)b * OR_BLK * d, OR_BLK, s, w, wq);
+    finish_row(&st, d, out);
+    free(st.acc);
 }
 
 /* q,k,v: [B,H,N,d] bf16; tier: [B,H,R,R] in {0,4,8,16}.
@@ -774,7 +852,7 @@ int or_attention(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
         for (int r = 0; r < nqb * OR_BLK; r++) {
             int j = r / OR_BLK, i = r % OR_BLK;
             int a = qblocks ? qblocks[j] : j;
-            attention_row(&h, tm + (size_t)a * R, a * OR_BLK + i,
+            attention_row(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i,
                           out + (((size_t)bh * nqb + j) * OR_BLK + i) * d, NULL);
         }
         head_ops_free(&h);
@@ -796,7 +874,7 @@ int64_t or_attention_trace(int F, int Hv, int Wv, int d, const uint16_t *q,
     head_ops h;
     head_ops_build(&h, q, k, v, N, d, perm);
     row_trace tr = {cap, 0, key, tr_tier, s, w, wq, m, 0.0};
-    attention_row(&h, tier + (size_t)(u / OR_BLK) * R, u, out, &tr);
+    attention_row(&h, NULL, tier + (size_t)(u / OR_BLK) * R, u, out, &tr);
     *Z = tr.Z;
     head_ops_free(&h);
     free(perm);
@@ -887,43 +965,156 @@ static int mx_pexp_from(float emax)
     return ef - 127;
 }
 
-static void attention_row_kp(const head_ops *h, const uint8_t *tier_row, int u,
-                             double *out, double *allow)
+/* Allowance constants: relative size of the matrix-core accumulation
+ * rounding of P^T V per tier, and of the hardware exp2's error. */
+static const double kPV8 = 0x1p-10, kPV4 = 0x1p-20, kPV16 = 0x1p-20;
+static const double kExp = 0x1p-21;
+
+/* Kernel-precision state of one query row: fp32 running max, fp64 sums. */
+typedef struct {
+    float m;
+    double Z;
+    double *acc, *al;
+} row_kp;
+
+/* Logits of one tile on the 16-bit path: bf16 products are exact in
+ * binary32; the matrix core sums each 16-channel step exactly and
+ * accumulates the steps in fp32: modelled as the exact dot rounded once,
+ * with the accumulation rounding in dS.  Keys j >= nk are masked (-inf). */
+static void kp_logits16(int d, const double *qr, const double *kt, int nk, float *S, double *dS)
+{
+    for (int j = 0; j < OR_BLK; j++) {
+        if (j >= nk) {
+            S[j] = -INFINITY;
+            dS[j] = 0.0;
+            continue;
+        }
+        const double *kr = kt + (size_t)j * d;
+        double sx = 0.0, mag = 0.0;
+        for (int c = 0; c < d; c++) {
+            sx += qr[c] * kr[c];
+            mag += fabs(qr[c] * kr[c]);
+        }
+        S[j] = (float)sx;
+        dS[j] = ldexp(mag, -21) + 2.0 * ulpf(S[j]);
+    }
+}
+
+/* The tile's softmax step as the kernel takes it: max of the logits, the
+ * new running max mn = max(m, max S * cf) in fp32, the rescale of Z, acc
+ * and the allowance by 2^(m - mn), then e = 2^(S cf + 8 - mn) and the
+ * relative uncertainty eta of each e. */
+typedef struct {
+    float mx, tm, mn, mold, bias;
+    double dSmax;
+} kp_step;
+
+static void kp_softmax(row_kp *st, int d, const float *S, const double *dS, float cf, double *e,
+                       double *eta, kp_step *t)
+{
+    float mx = S[0];
+    double dSmax = 0.0;
+    for (int j = 0; j < OR_BLK; j++) {
+        if (S[j] > mx) mx = S[j];
+        if (dS[j] > dSmax) dSmax = dS[j];
+    }
+    float tm = mx * cf;
+    float mn = fmaxf(st->m, tm);
+    double alpha = exp2((double)st->m - (double)mn);
+    st->Z *= alpha;
+    for (int c = 0; c < d; c++) {
+        st->acc[c] *= alpha;
+        st->al[c] *= alpha;
+    }
+    float bias = 8.0f - mn;
+    for (int j = 0; j < OR_BLK; j++) {
+        float tt = fmaf(S[j], cf, bias);
+        e[j] = (double)(float)exp2((double)tt);
+        eta[j] = kExp + 0.6931471805599453 * (double)cf * (dS[j] + dSmax);
+    }
+    t->mx = mx;
+    t->tm = tm;
+    t->mn = mn;
+    t->mold = st->m;
+    t->bias = bias;
+    t->dSmax = dSmax;
+}
+
+/* Accumulation for the element-wise weight formats (16-bit: bf16; FP8:
+ * E4M3): Z gets e, acc the quantized weight times V, the allowance the
+ * widest move of the weight within e (1 +- eta) plus the accumulation
+ * rounding. */
+static void kp_accumulate(row_kp *st, int d, double (*qv)(double), double kpv, const double *e,
+                          const double *eta, const double *vt, int nk)
+{
+    for (int j = 0; j < nk; j++) {
+        double val = qv(e[j]);
+        double lo = qv(e[j] * (1.0 - eta[j])), hi = qv(e[j] * (1.0 + eta[j]));
+        double dv = fmax(hi - val, val - lo);
+        const double *vv = vt + (size_t)j * d;
+        st->Z += e[j];
+        for (int c = 0; c < d; c++) {
+            st->acc[c] += val * vv[c];
+            st->al[c] += (dv + kpv * fabs(val)) * fabs(vv[c]);
+        }
+    }
+}
+
+/* One tile on the 16-bit path (video tile, prefix tile, or a prefix
+ * query's video tile). */
+static void kp_tile16(row_kp *st, int d, float c4, const double *qr, const double *kt,
+                      const double *vt, int nk)
+{
+    float S[OR_BLK];
+    double dS[OR_BLK], e[OR_BLK], eta[OR_BLK];
+    kp_step t;
+    kp_logits16(d, qr, kt, nk, S, dS);
+    kp_softmax(st, d, S, dS, c4, e, eta, &t);
+    kp_accumulate(st, d, q16_val, kPV16, e, eta, vt, nk);
+    st->m = t.mn;
+}
+
+static void kp_prefix_segment(row_kp *st, int d, float c4, const prefix_ops *px, const double *qr)
+{
+    if (!px)
+        return;
+    for (int t = 0; OR_BLK * t < px->nv; t++) {
+        int nk = px->nv - OR_BLK * t < OR_BLK ? px->nv - OR_BLK * t : OR_BLK;
+        kp_tile16(st, d, c4, qr, px->kf + (size_t)OR_BLK * t * d, px->vf + (size_t)OR_BLK * t * d, nk);
+    }
+}
+
+static void kp_finish(const row_kp *st, int d, double *out, double *allow)
+{
+    for (int c = 0; c < d; c++) {
+        out[c] = st->Z > 0.0 ? st->acc[c] / st->Z : 0.0;
+        allow[c] = st->Z > 0.0 ? st->al[c] / st->Z + 1e-6 * fabs(out[c]) : 0.0;
+    }
+}
+
+static void attention_row_kp(const head_ops *h, const prefix_ops *px, const uint8_t *tier_row,
+                             int u, double *out, double *allow)
 {
     int d = h->d, R = h->R, a = u / OR_BLK;
     const float c4 = (float)(1.4426950408889634 / sqrt((double)d));
-    const double kPV8 = ldexp(1.0, -10), kPV4 = ldexp(1.0, -20), kPV16 = ldexp(1.0, -20);
-    const double kExp = ldexp(1.0, -21);
-    float m = -INFINITY;
-    double Z = 0.0;
-    double *acc = calloc(d, sizeof(double)), *al = calloc(d, sizeof(double));
+    row_kp st = {-INFINITY, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double))};
     float S[OR_BLK];
-    double dS[OR_BLK];
+    double dS[OR_BLK], e[OR_BLK], eta[OR_BLK];
+    kp_step t;
     static const int phases[3] = {16, 8, 4};
+    kp_prefix_segment(&st, d, c4, px, h->qf + (size_t)u * d);
     for (int ph = 0; ph < 3; ph++) {
         int p = phases[ph];
         for (int b = 0; b < R; b++) {
             if (tier_row[b] != p)
                 continue;
-            float cf;
             if (p == 16) {
-                /* bf16 products are exact in binary32; the matrix core sums
-                 * each 16-channel step exactly and accumulates the steps in
-                 * fp32: modelled as the exact dot rounded once, with the
-                 * accumulation rounding in the allowance */
-                cf = c4;
-                const double *qr = h->qf + (size_t)u * d;
-                for (int j = 0; j < OR_BLK; j++) {
-                    const double *kr = h->kf + ((size_t)b * OR_BLK + j) * d;
-                    double sx = 0.0, mag = 0.0;
-                    for (int c = 0; c < d; c++) {
-                        sx += qr[c] * kr[c];
-                        mag += fabs(qr[c] * kr[c]);
-                    }
-                    S[j] = (float)sx;
-                    dS[j] = ldexp(mag, -21) + 2.0 * ulpf(S[j]);
-                }
-            } else if (p == 8) {
+                kp_tile16(&st, d, c4, h->qf + (size_t)u * d, h->kf + (size_t)b * OR_BLK * d,
+                          h->vf + (size_t)b * OR_BLK * d, OR_BLK);
+                continue;
+            }
+            float cf;
+            if (p == 8) {
                 cf = (h->s8q[a] * h->s8k[b]) * c4;
                 const uint8_t *qr = h->c8q + (size_t)u * d;
                 for (int j = 0; j < OR_BLK; j++) {
@@ -951,53 +1142,12 @@ static void attention_row_kp(const head_ops *h, const uint8_t *tier_row, int u,
                     dS[j] = ldexp(mag, -20) + 2.0 * ulpf(S[j]);
                 }
             }
-            float mx = S[0];
-            double dSmax = 0.0;
-            for (int j = 0; j < OR_BLK; j++) {
-                if (S[j] > mx) mx = S[j];
-                if (dS[j] > dSmax) dSmax = dS[j];
-            }
-            float tm = mx * cf;
-            float mn = fmaxf(m, tm);
-            double alpha = exp2((double)m - (double)mn);
-            Z *= alpha;
-            for (int c = 0; c < d; c++) {
-                acc[c] *= alpha;
-                al[c] *= alpha;
-            }
-            float bias = 8.0f - mn;
-            double e[OR_BLK], eta[OR_BLK];
-            for (int j = 0; j < OR_BLK; j++) {
-                float t = fmaf(S[j], cf, bias);
-                e[j] = (double)(float)exp2((double)t);
-                eta[j] = kExp + 0.6931471805599453 * (double)cf * (dS[j] + dSmax);
-            }
-            const double *V = p == 16 ? h->vf : (p == 8 ? h->v8 : h->v4);
-            if (p == 16) {
-                for (int j = 0; j < OR_BLK; j++) {
-                    double val = q16_val(e[j]);
-                    double lo = q16_val(e[j] * (1.0 - eta[j])), hi = q16_val(e[j] * (1.0 + eta[j]));
-                    double dv = fmax(hi - val, val - lo);
-                    const double *vv = V + ((size_t)b * OR_BLK + j) * d;
-                    Z += e[j];
-                    for (int c = 0; c < d; c++) {
-                        acc[c] += val * vv[c];
-                        al[c] += (dv + kPV16 * fabs(val)) * fabs(vv[c]);
-                    }
-                }
-            } else if (p == 8) {
+            kp_softmax(&st, d, S, dS, cf, e, eta, &t);
+            const double *V = p == 8 ? h->v8 : h->v4;
+            const double *vt = V + (size_t)b * OR_BLK * d;
+            if (p == 8) {
                 /* scale of V is applied per channel: dequantized V already has it */
-                for (int j = 0; j < OR_BLK; j++) {
-                    double val = q8_val(e[j]);
-                    double lo = q8_val(e[j] * (1.0 - eta[j])), hi = q8_val(e[j] * (1.0 + eta[j]));
-                    double dv = fmax(hi - val, val - lo);
-                    const double *vv = V + ((size_t)b * OR_BLK + j) * d;
-                    Z += e[j];
-                    for (int c = 0; c < d; c++) {
-                        acc[c] += val * vv[c];
-                        al[c] += (dv + kPV8 * fabs(val)) * fabs(vv[c]);
-                    }
-                }
+                kp_accumulate(&st, d, q8_val, kPV8, e, eta, vt, OR_BLK);
             } else {
                 for (int g = 0; g < 2; g++) {
                     float gm = S[32 * g], go = S[32 * (1 - g)];
@@ -1008,12 +1158,13 @@ static void attention_row_kp(const head_ops *h, const uint8_t *tier_row, int u,
                     double etag = 0.0;
                     for (int j = 0; j < 32; j++)
                         if (eta[32 * g + j] > etag) etag = eta[32 * g + j];
-                    int pinned = (gm == mx) && (mn == tm);
+                    int pinned = (gm == t.mx) && (t.mn == t.tm);
                     /* could the kernel have judged the pin differently? */
-                    double tol = 2.0 * dSmax;
+                    double tol = 2.0 * t.dSmax;
                     int pin_amb = (fabs((double)gm - (double)go) <= tol) ||
-                                  (fabs((double)tm - (double)m) <= (double)cf * tol + 4.0 * ulpf(tm));
-                    float emax = (float)exp2((double)fmaf(gm, cf, bias));
+                                  (fabs((double)t.tm - (double)t.mold) <=
+                                   (double)cf * tol + 4.0 * ulpf(t.tm));
+                    float emax = (float)exp2((double)fmaf(gm, cf, t.bias));
                     int Ep = pinned ? 6 : mx_pexp_from(emax);
                     /* exponents the kernel could have used for this group */
                     int cand[4], nc = 0;
@@ -1033,24 +1184,39 @@ static void attention_row_kp(const head_ops *h, const uint8_t *tier_row, int u,
                                 dv = fmax(dv, fabs(q4_val(ends[k2], cand[ci]) - val));
                             dv = fmax(dv, fabs(q4_val(e[j], cand[ci]) - val));
                         }
-                        const double *vv = V + ((size_t)b * OR_BLK + j) * d;
-                        Z += e[j];
+                        const double *vv = vt + (size_t)j * d;
+                        st.Z += e[j];
                         for (int c = 0; c < d; c++) {
-                            acc[c] += val * vv[c];
-                            al[c] += (dv + kPV4 * fabs(val)) * fabs(vv[c]);
+                            st.acc[c] += val * vv[c];
+                            st.al[c] += (dv + kPV4 * fabs(val)) * fabs(vv[c]);
                         }
                     }
                 }
             }
-            m = mn;
+            st.m = t.mn;
         }
     }
-    for (int c = 0; c < d; c++) {
-        out[c] = Z > 0.0 ? acc[c] / Z : 0.0;
-        allow[c] = Z > 0.0 ? al[c] / Z + 1e-6 * fabs(out[c]) : 0.0;
-    }
-    free(acc);
-    free(al);
+    kp_finish(&st, d, out, allow);
+    free(st.acc);
+    free(st.al);
+}
+
+/* Prefix query row i in the kernel's precision: all valid prefix keys, then
+ * all video regions ascending, on the 16-bit path. */
+static void attention_prefix_row_kp(const head_ops *h, const prefix_ops *px, int i, double *out,
+                                    double *allow)
+{
+    int d = h->d, R = h->R;
+    const float c4 = (float)(1.4426950408889634 / sqrt((double)d));
+    row_kp st = {-INFINITY, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double))};
+    const double *qr = px->qf + (size_t)i * d;
+    kp_prefix_segment(&st, d, c4, px, qr);
+    for (int b = 0; b < R; b++)
+        kp_tile16(&st, d, c4, qr, h->kf + (size_t)b * OR_BLK * d, h->vf + (size_t)b * OR_BLK * d,
+                  OR_BLK);
+    kp_finish(&st, d, out, allow);
+    free(st.acc);
+    free(st.al);
 }
 
 /* Kernel-precision variant of or_attention (tiers 16, 8 and 4; other values
@@ -1074,12 +1240,116 @@ int or_attention_kp(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *
             int j = r / OR_BLK, i = r % OR_BLK;
             int a = qblocks ? qblocks[j] : j;
             size_t o = (((size_t)bh * nqb + j) * OR_BLK + i) * d;
-            attention_row_kp(&h, tm + (size_t)a * R, a * OR_BLK + i, out + o, allow + o);
+            attention_row_kp(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i, out + o, allow + o);
         }
         head_ops_free(&h);
     }
     free(perm);
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Text prefix (App. C.1): video queries keep every valid prefix key    */
+/* outside the region budget, prefix queries attend to every valid key. */
+/* The prefix tensors qp, kp, vp are [B,H,Lp,d] bf16; valid[b] in      */
+/* [0, Lp] is the number of valid prefix keys of batch b (NULL: all).   */
+/* out: the video rows as in or_attention; outp: [B,H,Lp,d] prefix query */
+/* rows (NULL: not computed).  pt: tier of the prefix interactions (16  */
+/* or 32).  The _kp variant takes the kernel-precision decisions and    */
+/* always uses the 16-bit path for them.                                */
+/* ------------------------------------------------------------------ */
+static void prefix_ops_build(prefix_ops *px, const uint16_t *qp, const uint16_t *kp,
+                             const uint16_t *vp, int Lp, int nv, int d, int pt)
+{
+    size_t n = (size_t)Lp * d;
+    double *a[3];
+    const uint16_t *src[3] = {qp, kp, vp};
+    for (int t = 0; t < 3; t++) {
+        a[t] = malloc(sizeof(double) * (n ? n : 1));
+        for (size_t i = 0; i < n; i++)
+            a[t][i] = (double)bf16f(src[t][i]);
+    }
+    px->Lp = Lp;
+    px->nv = nv < 0 ? 0 : (nv > Lp ? Lp : nv);
+    px->pt = pt;
+    px->qf = a[0];
+    px->kf = a[1];
+    px->vf = a[2];
+}
+
+static void prefix_ops_free(prefix_ops *px)
+{
+    free((void *)px->qf);
+    free((void *)px->kf);
+    free((void *)px->vf);
+}
+
+static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+                      const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
+                      const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
+                      const uint8_t *tier, int nqb, const int32_t *qblocks, double *out,
+                      double *allow, double *outp, double *allowp)
+{
+    int N = F * Hv * Wv, R = N / OR_BLK;
+    int kp_mode = allow != NULL;
+    if (pt != 16 && pt != 32) return -1;
+    if (kp_mode && pt != 16) return -1;
+    int32_t *perm = malloc(sizeof(int32_t) * N);
+    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    if (!qblocks) nqb = R;
+    for (int bh = 0; bh < B * H; bh++) {
+        head_ops h;
+        prefix_ops px;
+        size_t off = (size_t)bh * N * d, poff = (size_t)bh * Lp * d;
+        head_ops_build(&h, q + off, k + off, v + off, N, d, perm);
+        prefix_ops_build(&px, qp + poff, kp + poff, vp + poff, Lp, valid ? valid[bh / H] : Lp, d, pt);
+        const uint8_t *tm = tier + (size_t)bh * R * R;
+#pragma omp parallel for schedule(dynamic, 8)
+        for (int r = 0; r < nqb * OR_BLK; r++) {
+            int j = r / OR_BLK, i = r % OR_BLK;
+            int a = qblocks ? qblocks[j] : j;
+            size_t o = (((size_t)bh * nqb + j) * OR_BLK + i) * d;
+            if (kp_mode)
+                attention_row_kp(&h, &px, tm + (size_t)a * R, a * OR_BLK + i, out + o, allow + o);
+            else
+                attention_row(&h, &px, tm + (size_t)a * R, a * OR_BLK + i, out + o, NULL);
+        }
+        if (outp) {
+#pragma omp parallel for schedule(dynamic, 4)
+            for (int i = 0; i < Lp; i++) {
+                size_t o = ((size_t)bh * Lp + i) * d;
+                if (kp_mode)
+                    attention_prefix_row_kp(&h, &px, i, outp + o, allowp + o);
+                else
+                    attention_prefix_row(&h, &px, i, outp + o);
+            }
+        }
+        prefix_ops_free(&px);
+        head_ops_free(&h);
+    }
+    free(perm);
+    return 0;
+}
+
+int or_attention_pfx(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+                     const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
+                     const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
+                     const uint8_t *tier, int nqb, const int32_t *qblocks, double *out,
+                     double *outp)
+{
+    return pfx_common(B, H, F, Hv, Wv, d, q, k, v, Lp, qp, kp, vp, valid, pt, tier, nqb, qblocks,
+                      out, NULL, outp, NULL);
+}
+
+int or_attention_kp_pfx(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+                        const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
+                        const uint16_t *kp, const uint16_t *vp, const int32_t *valid,
+                        const uint8_t *tier, int nqb, const int32_t *qblocks, double *out,
+                        double *allow, double *outp, double *allowp)
+{
+    if (!allow || (outp == NULL) != (allowp == NULL)) return -1;
+    return pfx_common(B, H, F, Hv, Wv, d, q, k, v, Lp, qp, kp, vp, valid, 16, tier, nqb, qblocks,
+                      out, allow, outp, allowp);
 }
 
 /* ------------------------------------------------------------------ */

@@ -83,6 +83,12 @@ def lib():
         L.or_attention_kp.restype = C.c_int
         L.or_mfma_fp8_dot64.argtypes = [P, P, C.c_float]
         L.or_mfma_fp8_dot64.restype = C.c_float
+        L.or_attention_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P, C.c_int,
+                                                       P, C.c_int, P, P, P]
+        L.or_attention_pfx.restype = C.c_int
+        L.or_attention_kp_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P,
+                                                          P, C.c_int, P, P, P, P, P]
+        L.or_attention_kp_pfx.restype = C.c_int
         L.or_dense.argtypes = [C.c_int] * 4 + [P, P, P, C.c_int, P, P]
         L.or_dense.restype = C.c_int
         _lib = L
@@ -308,6 +314,73 @@ def attention_kp(q, k, v, tier, F, Hv, Wv, qblocks=None):
     fo[:, :, perm, :] = out.reshape(B, H, N, d)
     fa[:, :, perm, :] = allow.reshape(B, H, N, d)
     return fo, fa
+
+
+def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks):
+    q, k, v, qp, kp, vp = (_u16(x) for x in (q, k, v, qp, kp, vp))
+    tier = np.ascontiguousarray(tier, np.uint8)
+    B, H, N, d = q.shape
+    Lp = qp.shape[2]
+    assert qp.shape == kp.shape == vp.shape == (B, H, Lp, d)
+    R = N // BLK
+    assert tier.shape == (B, H, R, R)
+    va = None if valid is None else np.ascontiguousarray(valid, np.int32)
+    assert va is None or va.shape == (B,)
+    qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
+    nq = R if qb is None else len(qb)
+    return q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R)
+
+
+def _restore(x, F, Hv, Wv):
+    B, H = x.shape[:2]
+    d = x.shape[-1]
+    N = F * Hv * Wv
+    full = np.empty((B, H, N, d), np.float64)
+    full[:, :, layout(F, Hv, Wv), :] = x.reshape(B, H, N, d)
+    return full
+
+
+def attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, pt=16, qblocks=None,
+                  prefix_rows=True):
+    """Tiered attention with a text prefix (App. C.1).  q, k, v: video
+    [B,H,N,d]; qp, kp, vp: prefix [B,H,Lp,d]; valid: [B] valid prefix keys
+    (None: all).  pt: precision of the prefix interactions (16 or 32).
+    Returns (video rows laid out as attention(), prefix rows [B,H,Lp,d] or
+    None)."""
+    q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R) = _pfx_args(
+        q, k, v, tier, qp, kp, vp, valid, qblocks)
+    out = np.empty((B, H, nq, BLK, d), np.float64)
+    outp = np.empty((B, H, Lp, d), np.float64) if prefix_rows else None
+    rc = lib().or_attention_pfx(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
+                                _p(vp), None if va is None else _p(va), pt, _p(tier), nq,
+                                None if qb is None else _p(qb), _p(out),
+                                None if outp is None else _p(outp))
+    assert rc == 0
+    if qblocks is None:
+        out = _restore(out, F, Hv, Wv)
+    return out, outp
+
+
+def attention_kp_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, qblocks=None,
+                     prefix_rows=True):
+    """Kernel-precision variant of attention_pfx (prefix on the 16-bit path).
+    Returns (out, allow, outp, allowp)."""
+    q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R) = _pfx_args(
+        q, k, v, tier, qp, kp, vp, valid, qblocks)
+    out = np.empty((B, H, nq, BLK, d), np.float64)
+    allow = np.empty_like(out)
+    outp = np.empty((B, H, Lp, d), np.float64) if prefix_rows else None
+    allowp = np.empty((B, H, Lp, d), np.float64) if prefix_rows else None
+    rc = lib().or_attention_kp_pfx(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
+                                   _p(vp), None if va is None else _p(va), _p(tier), nq,
+                                   None if qb is None else _p(qb), _p(out), _p(allow),
+                                   None if outp is None else _p(outp),
+                                   None if allowp is None else _p(allowp))
+    assert rc == 0
+    if qblocks is None:
+        out = _restore(out, F, Hv, Wv)
+        allow = _restore(allow, F, Hv, Wv)
+    return out, allow, outp, allowp
 
 
 def mfma_fp8_dot64(a_codes, b_codes, c_in=0.0) -> float:

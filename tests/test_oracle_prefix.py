@@ -1,0 +1,184 @@
+"""Pins of the oracle's text-prefix attention (CPU; DraftAttention2 App. C.1:
+prefix interactions lie outside the region budget, video queries keep every
+valid prefix key, prefix queries attend to every valid key).
+
+* with the oracle-only full-precision tier everywhere, video rows and prefix
+  rows both equal dense softmax attention over [valid prefix keys, video
+  keys] (textbook closed form, numpy), for ragged valid lengths;
+* with skipped video tiles, video rows equal brute-force masked attention
+  where every valid prefix key stays in the mask; a row whose region keeps
+  no video tile still attends to the prefix and is zero only when the
+  prefix has no valid key;
+* no output depends on prefix rows past the valid length (padding);
+* zero valid prefix keys reduce video rows exactly to the plain tiered
+  attention;
+* the 16-bit prefix path stays inside the bf16 weight-rounding envelope of
+  the full-precision one, and the kernel-precision variant agrees with the
+  fp64 tile loop.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from video_diffusion_dit_frame_amd import synth
+from video_diffusion_dit_frame_amd.synth import bf16_bits_to_f32
+from tests.test_oracle_attention import dense_np
+
+F, HV, WV = 2, 16, 16
+N = F * HV * WV
+R = N // 64
+LP = 150  # three prefix tiles, the last one ragged for every valid length
+
+
+def f64(x):
+    return bf16_bits_to_f32(x).astype(np.float64)
+
+
+@pytest.fixture(scope="module", params=[64, 128], ids=["d64", "d128"])
+def prob(request):
+    d = request.param
+    q, k, v = synth.make_qkv(2, 2, F, HV, WV, d, 310 + d, True)
+    qp, kp, vp = synth.make_prefix(2, 2, LP, d, 410 + d)
+    valid = np.array([LP, 71], np.int32)
+    return d, (q, k, v), (qp, kp, vp), valid
+
+
+def dense_joint(qrows, kp, vp, nv, k, v, vmask=None):
+    """Softmax attention of qrows over the first nv prefix keys and the video
+    keys (vmask [len(qrows), N]: which video keys each row keeps)."""
+    K = np.concatenate([kp[:nv], k])
+    V = np.concatenate([vp[:nv], v])
+    mask = None
+    if vmask is not None:
+        mask = np.concatenate([np.ones((len(qrows), nv), bool), vmask], axis=1)
+    return dense_np(qrows, K, V, mask)[0]
+
+
+def token_region(orc):
+    perm = orc.layout(F, HV, WV)
+    blk = np.empty(N, np.int64)
+    blk[perm] = np.arange(N) // 64
+    return blk
+
+
+def test_full_tier_prefix_equals_dense(orc, prob):
+    d, (q, k, v), (qp, kp, vp), valid = prob
+    tier = np.full((2, 2, R, R), 32, np.uint8)
+    out, outp = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid, pt=32)
+    for b in range(2):
+        nv = int(valid[b])
+        for h in range(2):
+            ref = dense_joint(f64(q[b, h]), f64(kp[b, h]), f64(vp[b, h]), nv, f64(k[b, h]),
+                              f64(v[b, h]))
+            assert np.abs(out[b, h] - ref).max() <= 1e-12
+            refp = dense_joint(f64(qp[b, h]), f64(kp[b, h]), f64(vp[b, h]), nv, f64(k[b, h]),
+                               f64(v[b, h]))
+            assert np.abs(outp[b, h] - refp).max() <= 1e-12
+
+
+def test_skipped_video_tiles_keep_prefix(orc, prob):
+    d, (q, k, v), (qp, kp, vp), valid = prob
+    rng = np.random.default_rng(3)
+    tier = np.where(rng.random((2, 2, R, R)) < 0.4, 32, 0).astype(np.uint8)
+    tier[:, :, 5, :] = 0          # region 5 keeps no video tile
+    valid = np.array([0, 71], np.int32)
+    out, outp = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid, pt=32)
+    blk = token_region(orc)
+    for b in range(2):
+        nv = int(valid[b])
+        for h in range(2):
+            vmask = tier[b, h][blk[:, None], blk[None, :]] > 0
+            ref = dense_joint(f64(q[b, h]), f64(kp[b, h]), f64(vp[b, h]), nv, f64(k[b, h]),
+                              f64(v[b, h]), vmask)
+            assert np.abs(out[b, h] - ref).max() <= 1e-12
+            rows5 = blk == 5
+            if nv == 0:
+                assert (out[b, h][rows5] == 0).all()
+            else:
+                assert np.abs(out[b, h][rows5]).max() > 0
+            # prefix queries ignore the tier map: dense over everything valid
+            refp = dense_joint(f64(qp[b, h]), f64(kp[b, h]), f64(vp[b, h]), nv, f64(k[b, h]),
+                               f64(v[b, h]))
+            assert np.abs(outp[b, h] - refp).max() <= 1e-12
+
+
+@pytest.mark.parametrize("pt", [16, 32])
+def test_padding_rows_do_not_matter(orc, prob, pt):
+    d, (q, k, v), (qp, kp, vp), valid = prob
+    rng = np.random.default_rng(9)
+    tier = rng.choice(np.array([0, 4, 8, 16], np.uint8), size=(2, 2, R, R))
+    out, outp = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid, pt=pt)
+    kp2, vp2 = kp.copy(), vp.copy()
+    for b in range(2):
+        nv = int(valid[b])
+        kp2[b, :, nv:] = synth.f32_to_bf16_bits(rng.standard_normal(kp2[b, :, nv:].shape) * 50)
+        vp2[b, :, nv:] = synth.f32_to_bf16_bits(rng.standard_normal(vp2[b, :, nv:].shape) * 50)
+    out2, outp2 = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp2, vp2, valid, pt=pt)
+    assert np.array_equal(out, out2) and np.array_equal(outp, outp2)
+
+
+def test_no_valid_prefix_reduces_to_plain(orc, prob):
+    d, (q, k, v), (qp, kp, vp), _ = prob
+    rng = np.random.default_rng(4)
+    tier = rng.choice(np.array([0, 4, 8, 16, 32], np.uint8), size=(2, 2, R, R))
+    plain = orc.attention(q, k, v, tier, F, HV, WV)
+    out, _ = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp,
+                               np.zeros(2, np.int32), pt=16, prefix_rows=False)
+    assert np.array_equal(plain, out)
+    t2 = np.where(tier == 32, 16, tier).astype(np.uint8)
+    plain_kp, plain_al = orc.attention_kp(q, k, v, t2, F, HV, WV)
+    okp, al, _, _ = orc.attention_kp_pfx(q, k, v, t2, F, HV, WV, qp, kp, vp,
+                                         np.zeros(2, np.int32), prefix_rows=False)
+    assert np.array_equal(plain_kp, okp) and np.array_equal(plain_al, al)
+
+
+def test_prefix_16bit_within_weight_rounding(orc, prob):
+    """All tiles at the 16-bit path vs full precision: every weight is
+    rounded to bf16 (8 significant bits: relative error <= 2^-8) and Z is
+    not, so each output moves by at most 2^-8 sum_j w_j |v_j| / Z."""
+    d, (q, k, v), (qp, kp, vp), valid = prob
+    t32 = np.full((2, 2, R, R), 32, np.uint8)
+    t16 = np.full((2, 2, R, R), 16, np.uint8)
+    o32, p32 = orc.attention_pfx(q, k, v, t32, F, HV, WV, qp, kp, vp, valid, pt=32)
+    o16, p16 = orc.attention_pfx(q, k, v, t16, F, HV, WV, qp, kp, vp, valid, pt=16)
+    for b in range(2):
+        nv = int(valid[b])
+        for h in range(2):
+            for rows, a32, a16 in ((f64(q[b, h]), o32[b, h], o16[b, h]),
+                                   (f64(qp[b, h]), p32[b, h], p16[b, h])):
+                K = np.concatenate([f64(kp[b, h])[:nv], f64(k[b, h])])
+                V = np.concatenate([f64(vp[b, h])[:nv], f64(v[b, h])])
+                _, P = dense_np(rows, K, V)
+                env = 2.0 ** -8 * (P @ np.abs(V)) * (1 + 1e-9) + 1e-14
+                assert (np.abs(a16 - a32) <= env).all()
+                assert np.abs(a16 - a32).max() > 0   # the rounding is there
+
+
+def test_kernel_precision_prefix_agrees(orc, prob):
+    """Kernel-precision decisions vs the fp64 tile loop.  Video rows: the
+    agreement asked of mixed tiers with outlier channels (FP8 code flips,
+    rel-L2 3e-3).  Prefix rows run the 16-bit path only, where a decision
+    can differ by one bf16 step of a weight (2^-8 of it): elementwise within
+    2^-8 sum_j w_j |v_j| / Z (the pin), and rel-L2 2e-4 as a sanity bound
+    (the prefix tokens share a direction in Q and K, so their logits reach
+    ~d and fp32 rounding of them decides more codes than on video tiles:
+    measured 1.3e-5 at d = 64, 5.4e-5 at d = 128)."""
+    d, (q, k, v), (qp, kp, vp), valid = prob
+    rng = np.random.default_rng(8)
+    tier = rng.choice(np.array([0, 4, 8, 16], np.uint8), size=(2, 2, R, R))
+    ex, exp_ = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid, pt=16)
+    kp_o, al, kp_p, alp = orc.attention_kp_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid)
+    assert (al >= 0).all() and (alp >= 0).all()
+    rl = np.linalg.norm(kp_o - ex) / np.linalg.norm(ex)
+    assert rl <= 3e-3, rl
+    rlp = np.linalg.norm(kp_p - exp_) / np.linalg.norm(exp_)
+    assert rlp <= 2e-4, rlp
+    for b in range(2):
+        nv = int(valid[b])
+        for h in range(2):
+            K = np.concatenate([f64(kp[b, h])[:nv], f64(k[b, h])])
+            V = np.concatenate([f64(vp[b, h])[:nv], f64(v[b, h])])
+            _, P = dense_np(f64(qp[b, h]), K, V)
+            env = 2.0 ** -8 * (P @ np.abs(V)) * 1.001 + 1e-12
+            assert (np.abs(kp_p[b, h] - exp_[b, h]) <= env).all()

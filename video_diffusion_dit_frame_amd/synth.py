@@ -87,3 +87,31 @@ def make_qkv(B, H, F, Hv, Wv, d, seed, outliers=True):
                         z[:, ch] *= np.float32(4.0)
                 out[t][b, h] = f32_to_bf16_bits(z)
     return tuple(out)
+
+
+def make_prefix(B, H, Lp, d, seed):
+    """Text-prefix tokens for joint text-video attention, (qp, kp, vp) as
+    uint16 bfloat16 bits, each [B, H, Lp, d].
+
+    Recipe: generator ``Generator(PCG64(seed))``; per (batch, head) one
+    shared direction ``mu ~ N(0, I_d)`` (text tokens of one prompt cluster),
+    then ``Q = z + mu``, ``K = z + mu``, ``V = z`` with fresh ``z ~ N(0, 1)``
+    per tensor, rounded to bfloat16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = [np.empty((B, H, Lp, d), dtype=np.uint16) for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            mu = rng.standard_normal(d, dtype=np.float32)
+            for t in range(3):
+                z = rng.standard_normal((Lp, d), dtype=np.float32)
+                if t < 2:
+                    z += mu
+                out[t][b, h] = f32_to_bf16_bits(z)
+    return tuple(out)
+
+
+def prefix_valid(B, Lp, seed):
+    """Valid prefix lengths per batch element (prompt lengths before the
+    padding), uniform in [1, Lp]; int32 [B]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(1, Lp + 1, size=B).astype(np.int32)
