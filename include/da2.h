@@ -59,6 +59,8 @@ typedef struct {
     int32_t batch, heads, head_dim;  /* B, H, d */
     int32_t frames, height, width;   /* F, H_v, W_v of the latent video */
     int64_t stride_b, stride_h, stride_n; /* element strides of Q/K/V/O */
+    int32_t prefix;                  /* Lp: text-prefix tokens per sequence (0: none;
+                                        at most 65536), see da2_attention_prefixed */
 } da2_shape;
 
 typedef struct {
@@ -113,11 +115,38 @@ da2_status da2_plan_tier_map(const da2_plan_t *plan, uint8_t *dst, hipStream_t s
 /* da2_attention: V preparation (FP8 with one fp32 scale per channel over all
  * tokens; MXFP4 along keys in groups of 32 inside each region) and the
  * phased mixed-precision attention over the plan's kept tiles (16-bit phase,
- * then FP8, then MXFP4; Sec. 3.3), written to o in the original token order.  out_dtype: 0 = bf16, 1 = fp32.  q and k must
- * be the pointers the plan was built on (DA2_ERR_PLAN_MISMATCH otherwise).
- * Rows whose query region keeps no tile are written as zero (App. C.1). */
+ * then FP8, then MXFP4; Sec. 3.3), written to o in the original token order.
+ * out_dtype: 0 = bf16, 1 = fp32.  q and k must be the pointers the plan was
+ * built on (DA2_ERR_PLAN_MISMATCH otherwise).  Rows whose query region keeps
+ * no tile are written as zero (App. C.1).  The video tokens only: a text
+ * prefix in the shape is ignored here (see da2_attention_prefixed). */
 da2_status da2_attention(da2_plan_t *plan, const void *q, const void *k, const void *v, void *o,
                          int32_t out_dtype, hipStream_t stream);
+
+/* da2_attention_prefixed: da2_attention for joint text-video attention
+ * (DraftAttention2 App. C.1: prefix interactions lie outside the region
+ * budget; video queries keep every valid prefix key, prefix queries use
+ * non-sparse attention).  Besides the video tensors q, k, v, o of
+ * da2_attention, the shape's Lp = prefix text tokens have their own bf16
+ * tensors qp, kp, vp and output op, [B,H,Lp,d] addressed with the same
+ * strides (for one joint tensor with the prefix first: qp = q_joint and
+ * q = q_joint + Lp*stride_n).  prefix_valid: device int32 [B], the number
+ * of valid prefix keys of each batch element (the first ones; values are
+ * clamped to [0, Lp]), or NULL for all Lp.  Prefix keys past the valid count
+ * are never read for the result (padding).
+ *   Video query rows: the plan's phases preceded by one segment over the
+ *   valid prefix keys in tiles of 64 (16-bit path: bf16 operands, weights
+ *   rounded to bf16); a row whose region keeps no video tile still attends
+ *   to the prefix, and is zero only when there is no valid prefix key.
+ *   Prefix query rows: every valid prefix key, then every video region in
+ *   order, all on the 16-bit path; all Lp rows are written.
+ * With prefix == 0 in the shape this is da2_attention (qp, kp, vp, op,
+ * prefix_valid are not used).  Otherwise qp, kp, vp and op must be non-null
+ * and 16-byte aligned (DA2_ERR_INVALID_ARG). */
+da2_status da2_attention_prefixed(da2_plan_t *plan, const void *q, const void *k, const void *v,
+                                  void *o, const void *qp, const void *kp, const void *vp, void *op,
+                                  const int32_t *prefix_valid, int32_t out_dtype,
+                                  hipStream_t stream);
 
 /* Debug exports in canonical layouts, for tests (device destination):
  *   DA2_DBG_Q_FP8 / K_FP8 / V_FP8   : uint8 codes [B,H,N,d], token axis in region order

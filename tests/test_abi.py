@@ -22,12 +22,12 @@ def test_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
-def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None):
+def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None, prefix=0):
     N = F * Hv * Wv
     sn = d if sn is None else sn
     sh = N * d if sh is None else sh
     sb = H * N * d if sb is None else sb
-    s = da2.Shape(B, H, d, F, Hv, Wv, sb, sh, sn)
+    s = da2.Shape(B, H, d, F, Hv, Wv, sb, sh, sn, prefix)
     h = C.c_void_p()
     st = da2.lib().da2_layout_create(C.byref(s), C.byref(h))
     return st, h
@@ -43,6 +43,11 @@ def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None):
     (dict(sn=60), INVALID),       # row stride below head_dim
     (dict(sn=68), INVALID),       # rows not 16-byte aligned
     (dict(F=200, Hv=128, Wv=128), SHAPE),  # too many regions
+    (dict(prefix=77), OK),
+    (dict(prefix=65536), OK),
+    (dict(prefix=-1), SHAPE),
+    (dict(prefix=65537), SHAPE),
+    (dict(prefix=40000, sn=65536), SHAPE),  # prefix rows past 32-bit byte offsets
 ])
 def test_layout_validation(kw, want):
     st, h = _layout(**kw)
@@ -79,6 +84,37 @@ def test_workspace_and_plan_validation():
     assert L.da2_plan_debug(p, 99, q, None) == INVALID
     L.da2_plan_destroy(p)
     L.da2_layout_destroy(lay)
+
+
+def test_prefix_workspace_and_validation():
+    """The text prefix adds one bf16 value image of ceil(Lp/64) tiles of 64
+    keys per (b, h); da2_attention_prefixed checks the prefix pointers before
+    the plan, and with no prefix in the shape is da2_attention."""
+    L = da2.lib()
+    st, lay0 = _layout(B=2, H=3, d=128)
+    st1, lay1 = _layout(B=2, H=3, d=128, prefix=130)
+    assert st == OK and st1 == OK
+    extra = L.da2_workspace_bytes(lay1) - L.da2_workspace_bytes(lay0)
+    img = 2 * 3 * 3 * 64 * 128 * 2
+    assert img <= extra <= img + 256
+    need = L.da2_workspace_bytes(lay1)
+    p = C.c_void_p()
+    assert L.da2_plan_create(lay1, C.c_void_p(1 << 20), need, C.byref(p)) == OK
+    q = C.c_void_p(1 << 24)
+    bad = C.c_void_p((1 << 24) + 8)
+    assert L.da2_attention_prefixed(p, q, q, q, q, None, q, q, q, None, 1, None) == INVALID
+    assert L.da2_attention_prefixed(p, q, q, q, q, q, q, q, None, None, 1, None) == INVALID
+    assert L.da2_attention_prefixed(p, q, q, q, q, q, bad, q, q, None, 1, None) == INVALID
+    assert L.da2_attention_prefixed(p, q, q, q, q, q, q, q, q, None, 3, None) == INVALID
+    assert L.da2_attention_prefixed(p, q, q, q, q, q, q, q, q, None, 1, None) == MISMATCH
+    L.da2_plan_destroy(p)
+    p0 = C.c_void_p()
+    assert L.da2_plan_create(lay0, C.c_void_p(1 << 20), need, C.byref(p0)) == OK
+    assert L.da2_attention_prefixed(p0, q, q, q, q, None, None, None, None, None, 1, None) == MISMATCH
+    assert L.da2_attention_prefixed(None, q, q, q, q, None, None, None, None, None, 1, None) == INVALID
+    L.da2_plan_destroy(p0)
+    L.da2_layout_destroy(lay0)
+    L.da2_layout_destroy(lay1)
 
 
 def test_status_strings():

@@ -37,6 +37,11 @@ da2_status check_shape(const da2_shape *s)
     // 32-bit byte offsets from the region's first token
     if ((((int64_t)7 * s->width + 7) * s->stride_n + s->head_dim) * 2 > INT32_MAX)
         return DA2_ERR_UNSUPPORTED_SHAPE;
+    // the prefix rows of one head are addressed the same way from its first
+    if (s->prefix < 0 || s->prefix > 65536)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
+    if (s->prefix > 0 && ((int64_t)(s->prefix - 1) * s->stride_n + s->head_dim) * 2 > INT32_MAX)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
     return DA2_OK;
 }
 
@@ -63,6 +68,7 @@ void carve(da2_layout_s &L)
     W.v4s = take(BH * N * d / 32);
     W.vs8 = take(BH * d * 4);
     W.v16 = take(BH * N * d * 2);
+    W.vp16 = take(BH * (size_t)L.ptiles * kBlk * d * 2);
     W.vamax = take(BH * d * 4);
     W.qavg = take(BH * R * d * 8);
     W.kavg = take(BH * R * d * 8);
@@ -122,6 +128,7 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
     L->BH = shape->batch * shape->heads;
     L->d = shape->head_dim;
     L->nchunk = ((int64_t)L->R * L->R + 4095) / 4096;
+    L->ptiles = (shape->prefix + kBlk - 1) / kBlk;
     carve(*L);
     *out = L;
     return DA2_OK;
@@ -276,8 +283,8 @@ da2_status da2_plan_tier_map(const da2_plan_t *P, uint8_t *dst, hipStream_t stre
     return e == hipSuccess ? DA2_OK : DA2_ERR_HIP;
 }
 
-da2_status da2_attention(da2_plan_t *P, const void *q, const void *k, const void *v, void *o,
-                         int32_t out_dtype, hipStream_t stream)
+static da2_status attend(da2_plan_s *P, const void *q, const void *k, const void *v, void *o,
+                         int32_t out_dtype, const PrefixIo *px, hipStream_t stream)
 {
     if (!P || !q || !k || !v || !o)
         return DA2_ERR_INVALID_ARG;
@@ -285,10 +292,16 @@ da2_status da2_attention(da2_plan_t *P, const void *q, const void *k, const void
         return DA2_ERR_INVALID_ARG;
     if (!aligned16(v) || !aligned16(o))
         return DA2_ERR_INVALID_ARG;
+    if (px && (!px->qp || !px->kp || !px->vp || !px->op || !aligned16(px->qp) ||
+               !aligned16(px->kp) || !aligned16(px->vp) || !aligned16(px->op)))
+        return DA2_ERR_INVALID_ARG;
     if (!P->ready || P->q != q || P->k != k)
         return DA2_ERR_PLAN_MISMATCH;
     const da2_layout_s &L = P->L;
-    launch_prep_v(L, v, P->has16, P->ws, stream);
+    // prefix queries attend to every region on the 16-bit path
+    launch_prep_v(L, v, P->has16 || px, P->ws, stream);
+    if (px)
+        launch_prep_vp(L, *px, P->ws, stream);
     hipEvent_t *ev = nullptr;
     if (P->timing && P->nev < kMaxTimed) {
         ev = P->ev + 2 * P->nev;
@@ -297,12 +310,31 @@ da2_status da2_attention(da2_plan_t *P, const void *q, const void *k, const void
                 return DA2_ERR_HIP;
         hipEventRecord(ev[0], stream);
     }
-    launch_attention(L, P->ws, q, k, o, out_dtype, stream);
+    launch_attention(L, P->ws, q, k, o, out_dtype, px, stream);
     if (ev) {
         hipEventRecord(ev[1], stream);
         P->nev++;
     }
     return launched();
+}
+
+da2_status da2_attention(da2_plan_t *P, const void *q, const void *k, const void *v, void *o,
+                         int32_t out_dtype, hipStream_t stream)
+{
+    return attend(P, q, k, v, o, out_dtype, nullptr, stream);
+}
+
+da2_status da2_attention_prefixed(da2_plan_t *P, const void *q, const void *k, const void *v,
+                                  void *o, const void *qp, const void *kp, const void *vp, void *op,
+                                  const int32_t *prefix_valid, int32_t out_dtype,
+                                  hipStream_t stream)
+{
+    if (!P)
+        return DA2_ERR_INVALID_ARG;
+    if (P->L.s.prefix == 0)
+        return attend(P, q, k, v, o, out_dtype, nullptr, stream);
+    PrefixIo px = {qp, kp, vp, op, prefix_valid};
+    return attend(P, q, k, v, o, out_dtype, &px, stream);
 }
 
 size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which)

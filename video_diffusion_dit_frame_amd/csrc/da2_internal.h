@@ -24,11 +24,14 @@ constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
 //   V mx   : [bh][a][cb][lane][16 B] + E8M0 byte per lane
 //   V bf16 : [bh][a][cb][t=4][lane][16 B]           A operand of the 16-bit
 //            product: lane l holds channel 32cb + l%32, keys 32(l/32) + 8t .. +7
+//   prefix V bf16 : [bh][tile][cb][t][lane][16 B]   the same for the text
+//            prefix, tile t holding prefix keys 64t .. 64t+63 (zero past the
+//            valid ones)
 // ---------------------------------------------------------------------------
 struct Workspace {
     size_t q8, q4, q4s, qs8;
     size_t k8, k4, k4s, ks8;
-    size_t v8, v4, v4s, vs8, vamax, v16;
+    size_t v8, v4, v4s, vs8, vamax, v16, vp16;
     size_t qavg, kavg, qmax, kmax;
     size_t la, lm, rmax, zsum, keys, tier;
     size_t sched, cnt;
@@ -49,6 +52,7 @@ struct da2_layout_s {
     da2_shape s;
     int N, R, Ry, Rx, BH, d;
     int64_t nchunk;           // rank chunks per head (head scope)
+    int ptiles;               // 64-key tiles of the text prefix (ceil(prefix / 64))
     da2::Workspace ws;
 };
 
@@ -67,17 +71,25 @@ struct da2_plan_s {
 
 namespace da2 {
 
+// Text-prefix inputs of one attention call (App. C.1).
+struct PrefixIo {
+    const void *qp, *kp, *vp;  // [B,H,Lp,d] bf16, the video strides
+    void *op;                  // prefix query rows of the output
+    const int32_t *valid;      // [B] valid prefix keys (device), or null
+};
+
 // ---------------------------------------------------------------------------
 // Launchers (defined in the kernel translation units).
 // ---------------------------------------------------------------------------
 void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, hipStream_t st);
 void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, hipStream_t st);
+void launch_prep_vp(const da2_layout_s &L, const PrefixIo &px, char *ws, hipStream_t st);
 void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st);
 void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int64_t tk, char *ws,
                  hipStream_t st);
 void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st);
 void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
-                      int out_f32, hipStream_t st);
+                      int out_f32, const PrefixIo *px, hipStream_t st);
 void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, hipStream_t st);
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st);
 

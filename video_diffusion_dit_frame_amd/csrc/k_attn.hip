@@ -47,6 +47,14 @@ struct AttnArgs {
     const uint16_t *q, *k;  // bf16 inputs (16-bit phase)
     const uint8_t *v16;     // bf16 value operand (16-bit phase)
     int kspan;              // bytes from a region's first key row past its last
+    // text prefix (App. C.1): Lp rows of Q/K/O at qp/kp/outp (same strides),
+    // their value images (ptiles tiles of 64 keys per head) and the valid
+    // counts per batch element (null: all Lp valid); Lp = 0: no prefix
+    const uint16_t *qp, *kp;
+    const uint8_t *vp16;
+    const int32_t *pvalid;
+    void *outp;
+    int Lp, ptiles, pkspan;
     const int32_t *sched;
     const int32_t *cnt;
     void *out;
@@ -442,56 +450,118 @@ __device__ __forceinline__ uint8_t *chunk16(uint8_t *b0, uint8_t *b1, int c)
     return (c < D / 16 ? b0 : b1) + (c % (D / 16)) * 1024;
 }
 
-// 16-bit phase over the n16 key regions of list16.  A tile's key image (64
-// key rows x D channels, bf16, gathered straight from K: chunk (m, s) holds
-// for lane l key row key_of_row(l % 32, m), channels 16 s + 8 (l / 32) .. + 7)
-// fills both key buffers (half m in buffer m), its value image (the bf16
-// operand written by the V preparation) both value buffers.  The two streams
-// overlap each other's use: the value copy of tile i runs under tile i's
-// logits and softmax, the key copy of tile i+1 under tile i's softmax and
-// P^T V.  Key and value buffers are distinct LDS variables, so the compiler
-// knows a copy into one never feeds reads of the other.
+// Key tiles of the 16-bit path.  A key source says which tile the i-th step
+// takes, copies that tile's key image (64 key rows x D channels, bf16,
+// gathered straight from K: chunk (m, s) holds for lane l key row
+// key_of_row(l % 32, m), channels 16 s + 8 (l / 32) .. + 7) into this wave's
+// half of the key buffers, and locates the value images (the bf16 operand
+// written by the V preparation, one 64 x D image per tile).
+//
+// Video regions of one head: the schedule's 16-bit list, or (DENSE) every
+// region in order.
+template <int D, bool DENSE>
+struct VideoKeys16 {
+    static constexpr bool kMasked = false;
+    const int32_t *list;
+    const uint16_t *kh;            // K of this head
+    const uint8_t *vbase;          // value images of the head's regions
+    int64_t vbytes;
+    uint32_t koff;                 // this lane's byte offset from a region's first token
+    int kspan, Ry, Rx, Hv, Wv;
+    int64_t osn;
+
+    __device__ __forceinline__ VideoKeys16(const AttnArgs &A, const int32_t *list_, int64_t hoff,
+                                           int64_t hbase, int w, int l)
+        : list(list_), kh(A.k + hoff), kspan(A.kspan), Ry(A.Ry), Rx(A.Rx), Hv(A.Hv), Wv(A.Wv),
+          osn(A.osn)
+    {
+        // wave w gathers the key rows of half m = w: a fixed byte offset from
+        // the key region's first token for every tile
+        const int kpos = key_of_row(l & 31, w);
+        koff = (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * (l >> 5)) * 2);
+        vbase = A.v16 + hbase * (kBlk * D * 2);
+        vbytes = (int64_t)A.R * kBlk * D * 2;
+    }
+    __device__ __forceinline__ int id(int i) const { return DENSE ? i : sload_i32(list + i); }
+    __device__ __forceinline__ int valid(int) const { return kBlk; }
+    __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
+    {
+        const int t0 = region_token(kb, 0, Ry, Rx, Hv, Wv);
+        const __amdgpu_buffer_rsrc_t ksrc = head_rsrc((const uint8_t *)(kh + (int64_t)t0 * osn), kspan);
+#pragma unroll
+        for (int s = 0; s < D / 16; s++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, koff, 32 * s, 0,
+                                                     0);
+    }
+};
+
+// Text-prefix keys of one head (App. C.1): tile t holds prefix keys
+// 64 t .. 64 t + 63, of which the first nv - 64 t are valid.  Rows past the
+// valid ones are read from the last valid row (their logits are masked, so
+// only the address matters); their value rows are zero in the value image.
 template <int D>
+struct PrefixKeys16 {
+    static constexpr bool kMasked = true;
+    __amdgpu_buffer_rsrc_t ksrc;   // prefix K rows of this head
+    const uint8_t *vbase;          // prefix value images of this head
+    int64_t vbytes;
+    int kpos, nv;
+    uint32_t lane_off;             // channel offset of this lane, bytes
+    int64_t osn;
+
+    __device__ __forceinline__ PrefixKeys16(const AttnArgs &A, int64_t hoff, int bh, int nv_, int w, int l)
+        : nv(nv_), osn(A.osn)
+    {
+        kpos = key_of_row(l & 31, w);
+        lane_off = (uint32_t)(16 * (l >> 5));
+        ksrc = head_rsrc((const uint8_t *)(A.kp + hoff), A.pkspan);
+        vbase = A.vp16 + (int64_t)bh * A.ptiles * (kBlk * D * 2);
+        vbytes = (int64_t)A.ptiles * kBlk * D * 2;
+    }
+    __device__ __forceinline__ int id(int i) const { return i; }
+    __device__ __forceinline__ int valid(int kb) const { return nv - kBlk * kb; }
+    __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
+    {
+        const int row = min(kBlk * kb + kpos, nv - 1);
+        const uint32_t off = (uint32_t)(row * osn * 2) + lane_off;
+#pragma unroll
+        for (int s = 0; s < D / 16; s++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, off, 32 * s, 0, 0);
+    }
+};
+
+// This wave's queries as B operands of the 16-bit logits (lane l: query row
+// qr, channels 16 s + 8 (l / 32) .. + 7 of step s).
+template <int D>
+__device__ __forceinline__ void load_q16(const uint16_t *qr, int l, v4u (&q16)[D / 16])
+{
+#pragma unroll
+    for (int s = 0; s < D / 16; s++)
+        q16[s] = *reinterpret_cast<const v4u *>(qr + 8 * (l >> 5) + 16 * s);
+}
+
+// 16-bit path over n tiles of a key source (ascending).  A tile's key image
+// fills both key buffers (half m in buffer m), its value image both value
+// buffers.  The two streams overlap each other's use: the value copy of tile
+// i runs under tile i's logits and softmax, the key copy of tile i+1 under
+// tile i's softmax and P^T V.  Key and value buffers are distinct LDS
+// variables, so the compiler knows a copy into one never feeds reads of the
+// other.  Semantics per tile: S from the bf16 operands as they are (exact
+// products, fp32 sums); masked keys get S = -inf; m = max(m, max S c4);
+// e = 2^(S c4 + 8 - m); Z += e; P = bf16(e) (nearest even); acc += P^T V.
+template <int D, class Keys>
 __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
-                                      uint8_t *vb1, const int32_t *list16, int n16,
-                                      int a, int bh, int w, int l, int64_t hbase, v16f (&acc)[D / 32],
-                                      float &m, float &z)
+                                      uint8_t *vb1, const Keys &K, int n16, const v4u (&q16)[D / 16],
+                                      int w, int l, v16f (&acc)[D / 32], float &m, float &z)
 {
     constexpr int KS = D / 16;                 // 16-channel steps of QK^T
     constexpr int CB = D / 32;
     constexpr int NK = KS;                     // key copies per wave and tile
     const int hf = l >> 5;
-    const int bb = bh / A.H, hh = bh - bb * A.H;
-    const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
-    // queries of this wave as B operands (lane l: query 32 w + l % 32,
-    // channels 16 s + 8 hf .. + 7 of step s)
-    v4u q16[KS];
-    {
-        const int qt = region_token(a, 32 * w + (l & 31), A.Ry, A.Rx, A.Hv, A.Wv);
-        const uint16_t *qr = A.q + hoff + (int64_t)qt * A.osn + 8 * hf;
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-            q16[s] = *reinterpret_cast<const v4u *>(qr + 16 * s);
-    }
-    // wave w gathers the key rows of half m = w: a fixed byte offset from the
-    // key region's first token for every tile
-    const int kpos = key_of_row(l & 31, w);
-    const uint32_t koff = (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * hf) * 2);
-    const uint16_t *kh = A.k + hoff;
-    const __amdgpu_buffer_rsrc_t vsrc =
-        head_rsrc(A.v16 + hbase * (kBlk * D * 2), (int64_t)A.R * kBlk * D * 2);
-    auto issue_key = [&](int kb) {
-        const int t0 = region_token(kb, 0, A.Ry, A.Rx, A.Hv, A.Wv);
-        const __amdgpu_buffer_rsrc_t ksrc =
-            head_rsrc((const uint8_t *)(kh + (int64_t)t0 * A.osn), A.kspan);
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)((w ? kb1 : kb0) + s * 1024), 16,
-                                                     koff, 32 * s, 0, 0);
-    };
-    int kb = sload_i32(list16);
-    int kbn = n16 > 1 ? sload_i32(list16 + 1) : 0;
-    issue_key(kb);
+    const __amdgpu_buffer_rsrc_t vsrc = head_rsrc(K.vbase, K.vbytes);
+    int kb = K.id(0);
+    int kbn = n16 > 1 ? K.id(1) : 0;
+    K.issue_key(kb, w ? kb1 : kb0);
     for (int i = 0; i < n16; i++) {
         // key image of tile i complete (both waves' halves); both waves are
         // done with the value buffer
@@ -519,7 +589,19 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *kb0, uint8_t *
         __syncthreads();
         const bool more = i + 1 < n16;
         if (more)
-            issue_key(kbn);
+            K.issue_key(kbn, w ? kb1 : kb0);
+        if (Keys::kMasked) {
+            // register r of half mm holds key 32 hf + 16 mm + r
+            const int nk = K.valid(kb);
+            if (nk < kBlk) {
+#pragma unroll
+                for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+                        if (32 * hf + 16 * mm + r >= nk)
+                            sc[mm][r] = -__builtin_huge_valf();
+            }
+        }
         const float c = A.c4;
         const float mnew = fmaxf(m, pair_max(lane_max(sc)) * c);
         rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
@@ -553,10 +635,45 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *kb0, uint8_t *
                     0);
         kb = kbn;
         if (i + 2 < n16)
-            kbn = sload_i32(list16 + i + 2);
+            kbn = K.id(i + 2);
     }
-    // the quantized phases refill both buffers
+    // the next segment or phase refills both buffers
     __syncthreads();
+}
+
+// O = acc / Z for this lane's query, written at element offset obase of the
+// output (this lane's channels 32 cb + 8 g + 4 hf .. + 3).
+template <int D>
+__device__ __forceinline__ void store_row(const AttnArgs &A, void *out, int64_t obase, const v16f (&acc)[D / 32],
+                                          float inv, int hf)
+{
+#pragma unroll
+    for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const int c0 = 32 * cb + 8 * g + 4 * hf;
+            float o0 = acc[cb][4 * g] * inv, o1 = acc[cb][4 * g + 1] * inv;
+            float o2 = acc[cb][4 * g + 2] * inv, o3 = acc[cb][4 * g + 3] * inv;
+            if (A.out_f32) {
+                *reinterpret_cast<float4 *>((float *)out + obase + c0) = make_float4(o0, o1, o2, o3);
+            } else {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+                pk.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
+                *reinterpret_cast<uint2 *>((uint16_t *)out + obase + c0) = pk;
+            }
+        }
+}
+
+// Valid prefix keys of batch element b: the caller's count clamped to
+// [0, Lp] (all Lp when no counts are given).
+__device__ __forceinline__ int prefix_valid(const AttnArgs &A, int b)
+{
+    if (A.Lp == 0)
+        return 0;
+    if (!A.pvalid)
+        return A.Lp;
+    return min(max(sload_i32(A.pvalid + b), 0), A.Lp);
 }
 
 // Instruction order inside one region of a step's main block: its LDS reads
@@ -931,9 +1048,20 @@ struct Attn {
         pv_range<FP8>(V, p, ef, 0, CB);
     }
 
-    __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int a)
+    // 16-bit segments of query region a: the text-prefix keys (np tiles, nv
+    // valid keys), then the schedule's 16-bit key regions
+    __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int np, int nv, int a)
     {
-        run16<D>(A, kb0, kb1, vb0, vb1, list16, n16, a, bh, w, l, hbase, acc, m, z);
+        const int bb = bh / A.H, hh = bh - bb * A.H;
+        const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
+        v4u q16[D / 16];
+        const int qt = region_token(a, 32 * w + (l & 31), A.Ry, A.Rx, A.Hv, A.Wv);
+        load_q16<D>(A.q + hoff + (int64_t)qt * A.osn, l, q16);
+        if (np > 0)
+            run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, hoff, bh, nv, w, l), np, q16, w, l, acc, m, z);
+        if (n16 > 0)
+            run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, false>(A, list16, hoff, hbase, w, l), n16, q16, w,
+                     l, acc, m, z);
     }
 
     // O = acc / Z for this wave's 32 queries of region a, written straight to
@@ -946,22 +1074,7 @@ struct Attn {
         const int tok = region_token(a, qi, A.Ry, A.Rx, A.Hv, A.Wv);
         const int b = bh / A.H, h = bh - b * A.H;
         const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)tok * A.osn;
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int c0 = 32 * cb + 8 * g + 4 * hf;
-                float o0 = acc[cb][4 * g] * inv, o1 = acc[cb][4 * g + 1] * inv;
-                float o2 = acc[cb][4 * g + 2] * inv, o3 = acc[cb][4 * g + 3] * inv;
-                if (A.out_f32) {
-                    *reinterpret_cast<float4 *>((float *)A.out + obase + c0) = make_float4(o0, o1, o2, o3);
-                } else {
-                    uint2 pk;
-                    pk.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
-                    pk.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
-                    *reinterpret_cast<uint2 *>((uint16_t *)A.out + obase + c0) = pk;
-                }
-            }
+        store_row<D>(A, A.out, obase, acc, inv, hf);
     }
 
     __device__ __forceinline__ void init(int w_, int bh_, int64_t qblk_)
@@ -1020,8 +1133,10 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     S.n8 = n8;
     S.n = n8 + sload_i32(A.cnt + qblk * kTargets + 2);
     S.list = A.sched + qblk * R + n16;
-    if (n16 > 0) {
-        S.phase16(A.sched + qblk * R, n16, a);
+    const int nv = prefix_valid(A, bh / A.H);
+    const int np = (nv + kBlk - 1) / kBlk;
+    if (n16 > 0 || np > 0) {
+        S.phase16(A.sched + qblk * R, n16, np, nv, a);
         if (n8 > 0)
             S.vunits(true);   // phase boundary: real units -> FP8 value units
     }
@@ -1029,10 +1144,57 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     S.epilogue(a);
 }
 
+// Text-prefix queries (App. C.1: non-sparse attention): one workgroup per 64
+// prefix query rows of one (b, h), wave w owning rows 32 w .. 32 w + 31;
+// every valid prefix key, then every video region in order, all on the
+// 16-bit path.  Rows past Lp (the last workgroup's tail) compute on a copy
+// of row Lp - 1 and are not written.
+template <int D>
+__device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
+                                            uint8_t *vb1, int pb, int bh, int w, int l)
+{
+    const int b = bh / A.H, h = bh - b * A.H;
+    const int64_t hoff = (int64_t)b * A.osb + (int64_t)h * A.osh;
+    const int row = kBlk * pb + 32 * w + (l & 31);
+    v4u q16[D / 16];
+    load_q16<D>(A.qp + hoff + (int64_t)min(row, A.Lp - 1) * A.osn, l, q16);
+    v16f acc[D / 32];
+#pragma unroll
+    for (int cb = 0; cb < D / 32; cb++)
+        acc[cb] = (v16f){};
+    float m = -__builtin_huge_valf(), z = 0.0f;
+    const int nv = prefix_valid(A, b);
+    const int np = (nv + kBlk - 1) / kBlk;
+    if (np > 0)
+        run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, hoff, bh, nv, w, l), np, q16, w, l, acc, m, z);
+    run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, true>(A, nullptr, hoff, (int64_t)bh * A.R, w, l), A.R, q16,
+             w, l, acc, m, z);
+    const float zt = pair_sum(z);
+    const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
+    if (row < A.Lp)
+        store_row<D>(A, A.outp, hoff + (int64_t)row * A.osn, acc, inv, l >> 5);
+}
+
+// Text-prefix queries (App. C.1: non-sparse attention): one workgroup per 64
+// prefix query rows of one (b, h), wave w owning rows 32 w .. 32 w + 31;
+// every valid prefix key, then every video region in order, all on the
+// 16-bit path.  Rows past Lp (the last workgroup's tail) compute on a copy
+// of row Lp - 1 and are not written.
+template <int D>
+__global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t kb0[kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t kb1[kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb0[kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb1[kBlk * D];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    prefix_rows<D>(A, kb0, kb1, vb0, vb1, (int)blockIdx.x, (int)blockIdx.y, w, (int)(threadIdx.x & 63));
+}
+
 }  // namespace
 
 void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
-                      int out_f32, hipStream_t st)
+                      int out_f32, const PrefixIo *px, hipStream_t st)
 {
     const Workspace &W = L.ws;
     AttnArgs A;
@@ -1067,11 +1229,26 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
     A.Wv = L.s.width;
     A.BH = L.BH;
     A.c4 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
+    A.Lp = px ? L.s.prefix : 0;
+    A.ptiles = L.ptiles;
+    A.qp = px ? (const uint16_t *)px->qp : nullptr;
+    A.kp = px ? (const uint16_t *)px->kp : nullptr;
+    A.vp16 = (const uint8_t *)(ws + W.vp16);
+    A.pvalid = px ? px->valid : nullptr;
+    A.outp = px ? px->op : nullptr;
+    A.pkspan = A.Lp > 0 ? (int)(((int64_t)(A.Lp - 1) * L.s.stride_n + L.d) * 2) : 0;
     dim3 grid(8 * ((L.R + 7) / 8) * L.BH);
     if (L.d == 128)
         k_attn<128><<<grid, 128, 0, st>>>(A);
     else
         k_attn<64><<<grid, 128, 0, st>>>(A);
+    if (A.Lp > 0) {
+        dim3 pgrid((A.Lp + kBlk - 1) / kBlk, L.BH);
+        if (L.d == 128)
+            k_attn_prefix<128><<<pgrid, 128, 0, st>>>(A);
+        else
+            k_attn_prefix<64><<<pgrid, 128, 0, st>>>(A);
+    }
 }
 
 }  // namespace da2

@@ -226,6 +226,39 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
     }
 }
 
+// Value image of the text prefix for the 16-bit path (App. C.1): the layout
+// of the regions' bf16 operand above, tile t holding prefix keys 64 t ..
+// 64 t + 63; keys past the valid count of their batch element are zero, so
+// their (zero) weights meet finite values.  Thread (cb, l) writes lane l of
+// channel block cb.
+template <int D>
+__global__ __launch_bounds__(2 * D) void k_prep_vp(const uint16_t *__restrict__ x, int64_t sb, int64_t sh,
+                                                   int64_t sn, int H, int Lp, int ptiles,
+                                                   const int32_t *__restrict__ valid,
+                                                   uint16_t *__restrict__ op16)
+{
+    const int t = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const int nv = valid ? min(max(valid[b], 0), Lp) : Lp;
+    const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
+    const int cb = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int c = 32 * cb + (l & 31), k0 = kBlk * t + 32 * (l >> 5);
+    const int64_t blk = (int64_t)bh * ptiles + t;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint32_t w16[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int key = k0 + 8 * q + 2 * j;
+            const uint32_t lo = key < nv ? xb[(int64_t)key * sn + c] : 0u;
+            const uint32_t hi = key + 1 < nv ? xb[(int64_t)(key + 1) * sn + c] : 0u;
+            w16[j] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4 *>(op16 + ((blk * (D / 32) + cb) * 4 + q) * 512 + l * 8) =
+            make_uint4(w16[0], w16[1], w16[2], w16[3]);
+    }
+}
+
 __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -281,6 +314,22 @@ void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, h
                                          L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s,
                                          op16);
     }
+}
+
+void launch_prep_vp(const da2_layout_s &L, const PrefixIo &px, char *ws, hipStream_t st)
+{
+    const da2_shape &s = L.s;
+    if (s.prefix <= 0)
+        return;
+    dim3 grid(L.ptiles, L.BH);
+    const uint16_t *xp = static_cast<const uint16_t *>(px.vp);
+    uint16_t *op16 = (uint16_t *)(ws + L.ws.vp16);
+    if (L.d == 128)
+        k_prep_vp<128><<<grid, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, s.prefix,
+                                             L.ptiles, px.valid, op16);
+    else
+        k_prep_vp<64><<<grid, 128, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, s.prefix,
+                                            L.ptiles, px.valid, op16);
 }
 
 }  // namespace da2

@@ -31,7 +31,8 @@ class Da2Error(RuntimeError):
 class Shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
                 ("frames", C.c_int32), ("height", C.c_int32), ("width", C.c_int32),
-                ("stride_b", C.c_int64), ("stride_h", C.c_int64), ("stride_n", C.c_int64)]
+                ("stride_b", C.c_int64), ("stride_h", C.c_int64), ("stride_n", C.c_int64),
+                ("prefix", C.c_int32)]
 
 
 class Budget(C.Structure):
@@ -60,6 +61,7 @@ def lib():
         L.da2_plan_from_tier_map.argtypes = [P, P, P, P, P]
         L.da2_plan_tier_map.argtypes = [P, P, P]
         L.da2_attention.argtypes = [P, P, P, P, P, i32, P]
+        L.da2_attention_prefixed.argtypes = [P, P, P, P, P, P, P, P, P, P, i32, P]
         L.da2_plan_debug.argtypes = [P, i32, P, P]
         L.da2_plan_debug_bytes.argtypes = [P, i32]
         L.da2_plan_debug_bytes.restype = sz
@@ -72,7 +74,8 @@ def lib():
         L.da2_plan_timing_read.restype = C.c_int
         L.da2_quotas.argtypes = [i64, i32, i32, i32, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]
         for name in ("da2_layout_create", "da2_plan_create", "da2_plan", "da2_plan_from_tier_map",
-                     "da2_plan_tier_map", "da2_attention", "da2_plan_debug"):
+                     "da2_plan_tier_map", "da2_attention", "da2_attention_prefixed",
+                     "da2_plan_debug"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -83,6 +86,14 @@ def header_functions():
     with open(HEADER) as f:
         text = f.read()
     return sorted(set(re.findall(r"\b(da2_[a-z_]+)\s*\(", text)))
+
+
+def _out_dtype(o) -> int:
+    if o.dtype == torch.float32:
+        return 1
+    if o.dtype == torch.bfloat16:
+        return 0
+    raise TypeError("output must be float32 or bfloat16")
 
 
 def status_string(st: int) -> str:
@@ -126,17 +137,18 @@ class Layout:
     """Region layout for one shape.  q/k/v/o are addressed with the given
     element strides (channel stride 1)."""
 
-    def __init__(self, B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n):
+    def __init__(self, B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix=0):
         self.B, self.H, self.d, self.F, self.Hv, self.Wv = B, H, d, F, Hv, Wv
         self.N = F * Hv * Wv
         self.R = self.N // 64
-        self.shape = Shape(B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n)
+        self.prefix = prefix
+        self.shape = Shape(B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix)
         h = C.c_void_p()
         _check(lib().da2_layout_create(C.byref(self.shape), C.byref(h)), "da2_layout_create")
         self.handle = h
 
     @classmethod
-    def for_tensor(cls, x: torch.Tensor, F, Hv, Wv, bhnd=True):
+    def for_tensor(cls, x: torch.Tensor, F, Hv, Wv, bhnd=True, prefix=0):
         """x: a [B, H, N, d] view (bhnd) or a [B, N, H, d] view, channel-contiguous."""
         if bhnd:
             B, H, N, d = x.shape
@@ -145,7 +157,7 @@ class Layout:
             B, N, H, d = x.shape
             sb, sn, sh, sc = x.stride()
         assert sc == 1 and N == F * Hv * Wv
-        return cls(B, H, d, F, Hv, Wv, sb, sh, sn)
+        return cls(B, H, d, F, Hv, Wv, sb, sh, sn, prefix)
 
     @property
     def workspace_bytes(self) -> int:
@@ -195,15 +207,21 @@ class Plan:
         return out
 
     def attention(self, q, k, v, o, stream=None):
-        if o.dtype == torch.float32:
-            od = 1
-        elif o.dtype == torch.bfloat16:
-            od = 0
-        else:
-            raise TypeError("output must be float32 or bfloat16")
         _check(lib().da2_attention(self.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
-                                   C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), od,
+                                   C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), _out_dtype(o),
                                    _stream(stream)), "da2_attention")
+
+    def attention_prefixed(self, q, k, v, o, qp, kp, vp, op, valid=None, stream=None):
+        """Joint text-video attention: video q/k/v/o plus the text prefix
+        qp/kp/vp/op ([B,H,Lp,d] views with the video strides); valid: device
+        int32 [B] valid prefix keys, or None for all."""
+        assert op.dtype == o.dtype
+        if valid is not None:
+            assert valid.dtype == torch.int32 and valid.is_cuda and valid.numel() == self.layout.B
+        ptr = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+        _check(lib().da2_attention_prefixed(self.handle, ptr(q), ptr(k), ptr(v), ptr(o), ptr(qp), ptr(kp),
+                                            ptr(vp), ptr(op), ptr(valid), _out_dtype(o), _stream(stream)),
+               "da2_attention_prefixed")
 
     def debug(self, which, stream=None) -> torch.Tensor:
         w = DBG[which] if isinstance(which, str) else int(which)
