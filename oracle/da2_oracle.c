@@ -815,20 +815,67 @@ static void attention_row(const head_ops *h, const prefix_ops *px, const uint8_t
     free(st.acc);
 }
 
-/* Prefix query row i (App. C.1: non-sparse attention): every valid prefix
- * key, then every video region ascending, all at the prefix tier. */
+/* Prefix query rows (App. C.1: non-sparse attention).  Their key sequence
+ * is every valid prefix key (tiles of 64, the last one ragged), then every
+ * video region ascending, all at the prefix tier.  The sequence is split
+ * into chunks of OR_PCHUNK consecutive tiles; each chunk is an online
+ * softmax of its own (running max from -inf), and the chunks' states are
+ * merged by the exact rescale of App. B.4's shared normalization:
+ * M = max m_c, Z = sum Z_c e^(m_c - M), acc = sum acc_c e^(m_c - M). */
+#define OR_PCHUNK 128
+
+static int prefix_tiles(const prefix_ops *px) { return (px->nv + OR_BLK - 1) / OR_BLK; }
+
+/* Tile t of prefix row i's key sequence: rows of K and V and the count of
+ * valid keys. */
+static int prefix_row_tile(const head_ops *h, const prefix_ops *px, int t, const double **kt,
+                           const double **vt)
+{
+    int np = prefix_tiles(px), d = h->d;
+    if (t < np) {
+        *kt = px->kf + (size_t)OR_BLK * t * d;
+        *vt = px->vf + (size_t)OR_BLK * t * d;
+        return px->nv - OR_BLK * t < OR_BLK ? px->nv - OR_BLK * t : OR_BLK;
+    }
+    *kt = h->kf + (size_t)(t - np) * OR_BLK * d;
+    *vt = h->vf + (size_t)(t - np) * OR_BLK * d;
+    return OR_BLK;
+}
+
 static void attention_prefix_row(const head_ops *h, const prefix_ops *px, int i, double *out)
 {
-    int d = h->d, R = h->R;
-    row_acc st = {-INFINITY, 0.0, calloc(d, sizeof(double))};
+    int d = h->d, T = prefix_tiles(px) + h->R;
+    int nc = (T + OR_PCHUNK - 1) / OR_PCHUNK;
     double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
     const double *qu = px->qf + (size_t)i * d;
-    prefix_segment(&st, d, px, qu, NULL);
-    for (int b = 0; b < R; b++)
-        tile_exact(&st, d, px->pt, qu, h->kf + (size_t)b * OR_BLK * d,
-                   h->vf + (size_t)b * OR_BLK * d, OR_BLK, s, w, wq);
-    finish_row(&st, d, out);
-    free(st.acc);
+    double *mc = malloc(sizeof(double) * nc), *zc = malloc(sizeof(double) * nc);
+    double *ac = calloc((size_t)nc * d, sizeof(double));
+    for (int c = 0; c < nc; c++) {
+        row_acc st = {-INFINITY, 0.0, ac + (size_t)c * d};
+        for (int t = c * OR_PCHUNK; t < T && t < (c + 1) * OR_PCHUNK; t++) {
+            const double *kt, *vt;
+            int nk = prefix_row_tile(h, px, t, &kt, &vt);
+            tile_exact(&st, d, px->pt, qu, kt, vt, nk, s, w, wq);
+        }
+        mc[c] = st.m;
+        zc[c] = st.Z;
+    }
+    double M = -INFINITY, Z = 0.0;
+    for (int c = 0; c < nc; c++)
+        if (mc[c] > M) M = mc[c];
+    for (int c = 0; c < d; c++)
+        out[c] = 0.0;
+    for (int c = 0; c < nc; c++) {
+        double f = exp(mc[c] - M);
+        Z += zc[c] * f;
+        for (int j = 0; j < d; j++)
+            out[j] += ac[(size_t)c * d + j] * f;
+    }
+    for (int j = 0; j < d; j++)
+        out[j] = Z > 0.0 ? out[j] / Z : 0.0;
+    free(mc);
+    free(zc);
+    free(ac);
 }
 
 /* q,k,v: [B,H,N,d] bf16; tier: [B,H,R,R] in {0,4,8,16}.
@@ -1201,22 +1248,48 @@ static void attention_row_kp(const head_ops *h, const prefix_ops *px, const uint
     free(st.al);
 }
 
-/* Prefix query row i in the kernel's precision: all valid prefix keys, then
- * all video regions ascending, on the 16-bit path. */
+/* Prefix query row i in the kernel's precision: the key sequence and its
+ * chunks as in attention_prefix_row, every tile on the 16-bit path; the
+ * merge takes 2^(m_c - M) of the chunks' fp32 running maxima (log2 units). */
 static void attention_prefix_row_kp(const head_ops *h, const prefix_ops *px, int i, double *out,
                                     double *allow)
 {
-    int d = h->d, R = h->R;
+    int d = h->d, T = prefix_tiles(px) + h->R;
+    int nc = (T + OR_PCHUNK - 1) / OR_PCHUNK;
     const float c4 = (float)(1.4426950408889634 / sqrt((double)d));
-    row_kp st = {-INFINITY, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double))};
     const double *qr = px->qf + (size_t)i * d;
-    kp_prefix_segment(&st, d, c4, px, qr);
-    for (int b = 0; b < R; b++)
-        kp_tile16(&st, d, c4, qr, h->kf + (size_t)b * OR_BLK * d, h->vf + (size_t)b * OR_BLK * d,
-                  OR_BLK);
-    kp_finish(&st, d, out, allow);
-    free(st.acc);
-    free(st.al);
+    float *mc = malloc(sizeof(float) * nc);
+    double *zc = malloc(sizeof(double) * nc);
+    double *ac = calloc((size_t)nc * d, sizeof(double)), *lc = calloc((size_t)nc * d, sizeof(double));
+    for (int c = 0; c < nc; c++) {
+        row_kp st = {-INFINITY, 0.0, ac + (size_t)c * d, lc + (size_t)c * d};
+        for (int t = c * OR_PCHUNK; t < T && t < (c + 1) * OR_PCHUNK; t++) {
+            const double *kt, *vt;
+            int nk = prefix_row_tile(h, px, t, &kt, &vt);
+            kp_tile16(&st, d, c4, qr, kt, vt, nk);
+        }
+        mc[c] = st.m;
+        zc[c] = st.Z;
+    }
+    float M = -INFINITY;
+    for (int c = 0; c < nc; c++)
+        M = fmaxf(M, mc[c]);
+    row_kp all = {M, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double))};
+    for (int c = 0; c < nc; c++) {
+        double f = exp2((double)mc[c] - (double)M);
+        all.Z += zc[c] * f;
+        for (int j = 0; j < d; j++) {
+            all.acc[j] += ac[(size_t)c * d + j] * f;
+            all.al[j] += lc[(size_t)c * d + j] * f;
+        }
+    }
+    kp_finish(&all, d, out, allow);
+    free(all.acc);
+    free(all.al);
+    free(mc);
+    free(zc);
+    free(ac);
+    free(lc);
 }
 
 /* Kernel-precision variant of or_attention (tiers 16, 8 and 4; other values

@@ -182,3 +182,31 @@ def test_kernel_precision_prefix_agrees(orc, prob):
             _, P = dense_np(f64(qp[b, h]), K, V)
             env = 2.0 ** -8 * (P @ np.abs(V)) * 1.001 + 1e-12
             assert (np.abs(kp_p[b, h] - exp_[b, h]) <= env).all()
+
+
+@pytest.mark.parametrize("nv", [70, 128])
+def test_chunked_prefix_rows_equal_dense(orc, nv):
+    """Prefix rows over more than one chunk of 128 tiles (2 prefix tiles +
+    128 video regions = 130 tiles: chunks of 128 and 2, the merge rescales
+    both): at full precision they equal dense softmax attention."""
+    F2, H2, W2, d, Lp = 2, 64, 64, 64, 128
+    q, k, v = synth.make_qkv(1, 1, F2, H2, W2, d, 512, True)
+    qp, kp, vp = synth.make_prefix(1, 1, Lp, d, 513)
+    R2 = F2 * H2 * W2 // 64
+    tier = np.full((1, 1, R2, R2), 32, np.uint8)
+    valid = np.array([nv], np.int32)
+    out, outp = orc.attention_pfx(q, k, v, tier, F2, H2, W2, qp, kp, vp, valid, pt=32,
+                                  qblocks=[0])
+    ref = dense_joint(f64(qp[0, 0]), f64(kp[0, 0]), f64(vp[0, 0]), nv, f64(k[0, 0]), f64(v[0, 0]))
+    assert np.abs(outp[0, 0] - ref).max() <= 1e-12
+    # the 16-bit path stays inside the weight-rounding envelope there too
+    _, outp16 = orc.attention_pfx(q, k, v, tier, F2, H2, W2, qp, kp, vp, valid, pt=16,
+                                  qblocks=[0])
+    K = np.concatenate([f64(kp[0, 0])[:nv], f64(k[0, 0])])
+    V = np.concatenate([f64(vp[0, 0])[:nv], f64(v[0, 0])])
+    _, P = dense_np(f64(qp[0, 0]), K, V)
+    env = 2.0 ** -8 * (P @ np.abs(V)) * (1 + 1e-9) + 1e-14
+    assert (np.abs(outp16[0, 0] - ref) <= env).all()
+    _, _, kpp, alp = orc.attention_kp_pfx(q, k, v, tier.clip(max=16), F2, H2, W2, qp, kp, vp, valid,
+                                          qblocks=[0])
+    assert (np.abs(kpp[0, 0] - outp16[0, 0]) <= env).all()
