@@ -7,8 +7,14 @@ followed by da2_attention (V preparation, phased 16-bit/FP8/MXFP4 attention
 with the output written back in token order).  Inputs are resident in HBM before the
 timed region; Q/K/V use the [B, N, H, d] storage of DiT attention layers.
 
+With --prefix Lp the layer is joint text-video attention (App. C.1 of the
+paper): a text prefix of Lp tokens (the first --prefix-valid of them valid)
+precedes the video tokens in the same [B, Lp + N, H, d] tensors, and the
+step's attention call is da2_attention_prefixed.
+
 Prints one JSON line.  value = dense-equivalent attention TFLOP/s of the
-complete step (4 B H N^2 d per step); roofline = the attention kernel against
+complete step (4 B H N^2 d per step; with a prefix, 4 B H (Lp + N)(nv + N) d
+over the nv valid prefix keys); roofline = the attention kernel against
 the tier-weighted MFMA peak (its achieved executed FLOP/s over
 (F16 + F8 + F4) / (F16/P16 + F8/P8 + F4/P4)); cpu_baseline = the CPU oracle timed on a
 bounded sample and extrapolated to the same unit.
@@ -41,6 +47,9 @@ def parse():
     ap.add_argument("--full-bp", type=int, default=0, help="16-bit share (basis points)")
     ap.add_argument("--hi-bp", type=int, default=None, help="FP8 share, overriding --budget")
     ap.add_argument("--lo-bp", type=int, default=None, help="MXFP4 share, overriding --budget")
+    ap.add_argument("--prefix", type=int, default=0, help="text-prefix tokens (joint attention)")
+    ap.add_argument("--prefix-valid", type=int, default=None,
+                    help="valid prefix keys per sequence (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain copy kernel of 1 GiB before the steps (reference for "
@@ -133,13 +142,20 @@ def main():
     print("[bench] generating %s inputs (B=%d H=%d N=%d d=%d)" % (w.name, w.B, w.H, w.N, w.d),
           file=sys.stderr, flush=True)
     q, k, v = synth.make_qkv(w.B, w.H, w.F, w.Hv, w.Wv, w.d, w.seed, w.outliers)
+    Lp = args.prefix
+    nv = Lp if args.prefix_valid is None else min(max(args.prefix_valid, 0), Lp)
+    if Lp:
+        qp, kp, vp = synth.make_prefix(w.B, w.H, Lp, w.d, w.seed + 7)
+        q, k, v = (np.concatenate([a, b], axis=2) for a, b in ((qp, q), (kp, k), (vp, v)))
+        del qp, kp, vp
 
     def to_bnhd(x):
-        t = da2.to_device_bf16(x)                 # [B, H, N, d]
-        t = t.permute(0, 2, 1, 3).contiguous()    # [B, N, H, d] storage
-        return t.permute(0, 2, 1, 3)              # [B, H, N, d] view
+        t = da2.to_device_bf16(x)                 # [B, H, Lp + N, d]
+        t = t.permute(0, 2, 1, 3).contiguous()    # [B, Lp + N, H, d] storage
+        return t.permute(0, 2, 1, 3)              # [B, H, Lp + N, d] view
 
-    qd, kd, vd = to_bnhd(q), to_bnhd(k), to_bnhd(v)
+    qj, kj, vj = to_bnhd(q), to_bnhd(k), to_bnhd(v)
+    qd, kd, vd = qj[:, :, Lp:], kj[:, :, Lp:], vj[:, :, Lp:]
     if args.calibrate_copy:
         # a plain copy kernel: reads and writes exactly 2^30 bytes
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -147,14 +163,23 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    o = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
-    L = da2.Layout.for_tensor(qd, w.F, w.Hv, w.Wv)
+    oj = torch.empty((w.B, Lp + w.N, w.H, w.d), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+    o = oj[:, :, Lp:]
+    L = da2.Layout.for_tensor(qd, w.F, w.Hv, w.Wv, prefix=Lp)
     P = da2.Plan(L)
     stream = torch.cuda.current_stream()
+    valid = torch.full((w.B,), nv, dtype=torch.int32, device=dev) if Lp else None
+
+    def attend():
+        if Lp:
+            P.attention_prefixed(qd, kd, vd, o, qj[:, :, :Lp], kj[:, :, :Lp], vj[:, :, :Lp],
+                                 oj[:, :, :Lp], valid, stream)
+        else:
+            P.attention(qd, kd, vd, o, stream)
 
     def step():
         P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full)
-        P.attention(qd, kd, vd, o, stream)
+        attend()
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -169,7 +194,7 @@ def main():
         ev[i][0].record(stream)
         P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full)
         ev[i][1].record(stream)
-        P.attention(qd, kd, vd, o, stream)
+        attend()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -189,8 +214,11 @@ def main():
     f16 = w.B * w.H * t16 * tile_flop
     f8 = w.B * w.H * (t8c - t16) * tile_flop
     f4 = w.B * w.H * (tk - t8c) * tile_flop
+    # prefix interactions run on the 16-bit path: video rows x valid prefix
+    # keys, and prefix rows x (valid prefix keys + video keys)
+    f16 += 4.0 * w.B * w.H * w.d * (float(w.N) * nv + float(Lp) * (nv + w.N))
     fx = f16 + f8 + f4
-    dense_flop = 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
+    dense_flop = 4.0 * w.B * w.H * float(Lp + w.N) * float(nv + w.N) * w.d
     t_attn = attn_kernel_ms * 1e-3
     wsum = f16 / PEAK_BF16 + f8 / PEAK_FP8 + f4 / PEAK_FP4
     peak_eff = fx / wsum if fx > 0 else PEAK_FP8
@@ -208,13 +236,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16+" if full else "") + "fp8_e4m3+mxfp4 (attention), f64 (draft scoring)",
+        "dtype": ("bf16+" if full or Lp else "") + "fp8_e4m3+mxfp4 (attention), f64 (draft scoring)",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.d,
                    "frames": w.F, "height": w.Hv, "width": w.Wv, "tokens": w.N, "regions": R,
                    "budget_bp": ({"bf16": full} if full else {}) | {"fp8": hi, "mxfp4": lo},
                    "lambda": w.lam, "ranking": "head",
-                   "storage": "[B,N,H,d] bf16", "output": "bf16"},
+                   "storage": "[B,N,H,d] bf16", "output": "bf16"}
+                  | ({"prefix": Lp, "prefix_valid": nv} if Lp else {}),
         "plan_ms": plan_ms,
         "attention_call_ms": attn_call_ms,
         "attention_kernel_ms": attn_kernel_ms,
@@ -222,11 +251,11 @@ def main():
         "tier_weighted_mfma_util": util,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_eff, "unit": "TFLOP/s",
                      "frac": achieved / peak_eff,
-                     "traffic": measured_traffic(w.name, [hi, lo], full),
+                     "traffic": None if Lp else measured_traffic(w.name, [hi, lo], full),
                      "kernel": "k_attn",
                      "peak_basis": "tier-weighted bf16 2.5 / FP8 5.0 / FP4 10.1 PFLOP/s"},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not Lp:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, hi, lo, full)
     print(json.dumps(out), flush=True)

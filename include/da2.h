@@ -60,7 +60,7 @@ typedef struct {
     int32_t frames, height, width;   /* F, H_v, W_v of the latent video */
     int64_t stride_b, stride_h, stride_n; /* element strides of Q/K/V/O */
     int32_t prefix;                  /* Lp: text-prefix tokens per sequence (0: none;
-                                        at most 65536), see da2_attention_prefixed */
+                                        at most 4096), see da2_attention_prefixed */
 } da2_shape;
 
 typedef struct {
@@ -139,7 +139,9 @@ da2_status da2_attention(da2_plan_t *plan, const void *q, const void *k, const v
  *   rounded to bf16); a row whose region keeps no video tile still attends
  *   to the prefix, and is zero only when there is no valid prefix key.
  *   Prefix query rows: every valid prefix key, then every video region in
- *   order, all on the 16-bit path; all Lp rows are written.
+ *   order, all on the 16-bit path, in chunks of 128 tiles (8192 keys), each
+ *   an online softmax of its own, merged by the exact rescale of the shared
+ *   normalization (App. B.4); all Lp rows are written.
  * With prefix == 0 in the shape this is da2_attention (qp, kp, vp, op,
  * prefix_valid are not used).  Otherwise qp, kp, vp and op must be non-null
  * and 16-byte aligned (DA2_ERR_INVALID_ARG). */

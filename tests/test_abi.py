@@ -44,10 +44,10 @@ def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None, prefix
     (dict(sn=68), INVALID),       # rows not 16-byte aligned
     (dict(F=200, Hv=128, Wv=128), SHAPE),  # too many regions
     (dict(prefix=77), OK),
-    (dict(prefix=65536), OK),
+    (dict(prefix=4096), OK),
     (dict(prefix=-1), SHAPE),
-    (dict(prefix=65537), SHAPE),
-    (dict(prefix=40000, sn=65536), SHAPE),  # prefix rows past 32-bit byte offsets
+    (dict(prefix=4097), SHAPE),
+    (dict(prefix=4096, sn=1 << 19), SHAPE),  # prefix rows past 32-bit byte offsets
 ])
 def test_layout_validation(kw, want):
     st, h = _layout(**kw)
@@ -87,16 +87,20 @@ def test_workspace_and_plan_validation():
 
 
 def test_prefix_workspace_and_validation():
-    """The text prefix adds one bf16 value image of ceil(Lp/64) tiles of 64
-    keys per (b, h); da2_attention_prefixed checks the prefix pointers before
-    the plan, and with no prefix in the shape is da2_attention."""
+    """The text prefix adds, per (b, h), one bf16 value image of ceil(Lp/64)
+    tiles of 64 keys and the prefix rows' chunk states (fp32 output and
+    (max, sum) per chunk of 128 tiles and row, rows padded to 64);
+    da2_attention_prefixed checks the prefix pointers before the plan, and
+    with no prefix in the shape is da2_attention."""
     L = da2.lib()
     st, lay0 = _layout(B=2, H=3, d=128)
     st1, lay1 = _layout(B=2, H=3, d=128, prefix=130)
     assert st == OK and st1 == OK
     extra = L.da2_workspace_bytes(lay1) - L.da2_workspace_bytes(lay0)
-    img = 2 * 3 * 3 * 64 * 128 * 2
-    assert img <= extra <= img + 256
+    BH, tiles, R = 6, 3, 8
+    chunks = -(-(tiles + R) // 128)
+    want = BH * tiles * 64 * 128 * 2 + BH * chunks * tiles * 64 * (128 * 4 + 8)
+    assert want <= extra <= want + 3 * 256
     need = L.da2_workspace_bytes(lay1)
     p = C.c_void_p()
     assert L.da2_plan_create(lay1, C.c_void_p(1 << 20), need, C.byref(p)) == OK

@@ -5,8 +5,9 @@ and every element within 5e-3 plus its allowance, video rows and prefix rows
 alike.  Inputs are joint [B, H, Lp + N, d] tensors with the prefix first, the
 video and prefix parts passed as views with the joint strides.  Cases cover
 ragged last prefix tiles, per-batch valid lengths (including zero and the
-full length), one prefix token, empty video rows, plans and tier maps with
-every phase, head dims 64 and 128, and bf16 output."""
+full length), one prefix token, empty video rows, prefix rows whose key
+sequence spans two chunks, plans and tier maps with every phase, head dims
+64 and 128, and bf16 output."""
 import numpy as np
 import pytest
 import torch
@@ -51,8 +52,13 @@ def run_prefixed(q, k, v, qp, kp, vp, F, Hv, Wv, tier=None, budget=None, valid=N
     return od.float().cpu().numpy(), opd.float().cpu().numpy(), tier_used
 
 
-def check(q, k, v, qp, kp, vp, F, Hv, Wv, tier, valid, o, op, what):
-    r, allow, rp, allowp = O.attention_kp_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid)
+def check(q, k, v, qp, kp, vp, F, Hv, Wv, tier, valid, o, op, what, qblocks=None):
+    r, allow, rp, allowp = O.attention_kp_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid,
+                                               qblocks=qblocks)
+    if qblocks is not None:
+        # the oracle's rows (j, i) are tokens perm[qblocks[j] * 64 + i]
+        tok = O.layout(F, Hv, Wv)[(np.asarray(qblocks)[:, None] * 64 + np.arange(64)).ravel()]
+        o = o[:, :, tok].reshape(r.shape)
     rl, ma = G.check_kp(o, r, allow, what + " video rows")
     rlp, map_ = G.check_kp(op, rp, allowp, what + " prefix rows")
     print("%s: video rel_l2 %.3e max_abs %.3e; prefix rel_l2 %.3e max_abs %.3e" % (what, rl, ma, rlp, map_))
@@ -64,6 +70,8 @@ WIDE = (1, 2, 3, 24, 40, 128, 77, [77], 32)
 EXACT = (2, 1, 2, 16, 24, 128, 128, None, 33)     # two whole prefix tiles, all valid
 ONE = (2, 1, 2, 16, 16, 64, 1, [1, 0], 34)        # one prefix token; none valid in batch 1
 ZERO = (2, 2, 2, 16, 16, 128, 96, [0, 95], 35)
+# 3 prefix tiles + 144 regions: prefix rows span two chunks of 128 tiles
+LONG = (1, 1, 2, 64, 72, 128, 190, [170], 36)
 
 
 def _inputs(c):
@@ -86,14 +94,17 @@ def _family(name, B, H, R, seed):
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("case", [SMALL, WIDE, EXACT, ONE, ZERO], ids=["small", "wide", "exact", "one", "zero"])
+@pytest.mark.parametrize("case", [SMALL, WIDE, EXACT, ONE, ZERO, LONG],
+                         ids=["small", "wide", "exact", "one", "zero", "long"])
 @pytest.mark.parametrize("family", ["mixed16", "quantized", "empty_rows"])
 def test_prefix_tier_families(case, family):
     B, H, F, Hv, Wv, d, Lp, valid, q, k, v, qp, kp, vp = _inputs(case)
     R = F * Hv * Wv // 64
     tier = _family(family, B, H, R, case[-1])
     o, op, _ = run_prefixed(q, k, v, qp, kp, vp, F, Hv, Wv, tier=tier, valid=valid)
-    check(q, k, v, qp, kp, vp, F, Hv, Wv, tier, valid, o, op, "%s/%s" % (family, case[:8]))
+    # long rows: video query regions sampled (first, last and one between)
+    qb = [0, R // 3, R - 1] if R > 100 else None
+    check(q, k, v, qp, kp, vp, F, Hv, Wv, tier, valid, o, op, "%s/%s" % (family, case[:8]), qb)
 
 
 @pytest.mark.parametrize("budget", [(0, 1500, 3000), (750, 750, 0)], ids=["8-4", "16-8"])

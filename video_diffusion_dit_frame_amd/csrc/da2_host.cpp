@@ -38,7 +38,7 @@ da2_status check_shape(const da2_shape *s)
     if ((((int64_t)7 * s->width + 7) * s->stride_n + s->head_dim) * 2 > INT32_MAX)
         return DA2_ERR_UNSUPPORTED_SHAPE;
     // the prefix rows of one head are addressed the same way from its first
-    if (s->prefix < 0 || s->prefix > 65536)
+    if (s->prefix < 0 || s->prefix > kMaxPrefix)
         return DA2_ERR_UNSUPPORTED_SHAPE;
     if (s->prefix > 0 && ((int64_t)(s->prefix - 1) * s->stride_n + s->head_dim) * 2 > INT32_MAX)
         return DA2_ERR_UNSUPPORTED_SHAPE;
@@ -69,6 +69,8 @@ void carve(da2_layout_s &L)
     W.vs8 = take(BH * d * 4);
     W.v16 = take(BH * N * d * 2);
     W.vp16 = take(BH * (size_t)L.ptiles * kBlk * d * 2);
+    W.pacc = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * d * 4);
+    W.pmz = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * 8);
     W.vamax = take(BH * d * 4);
     W.qavg = take(BH * R * d * 8);
     W.kavg = take(BH * R * d * 8);
@@ -129,6 +131,7 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
     L->d = shape->head_dim;
     L->nchunk = ((int64_t)L->R * L->R + 4095) / 4096;
     L->ptiles = (shape->prefix + kBlk - 1) / kBlk;
+    L->pchunks = L->ptiles ? (L->ptiles + L->R + kPrefixChunkTiles - 1) / kPrefixChunkTiles : 0;
     carve(*L);
     *out = L;
     return DA2_OK;

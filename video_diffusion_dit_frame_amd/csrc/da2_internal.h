@@ -13,6 +13,8 @@ constexpr int kBlk = 64;          // tokens per region: one 8x8 spatial cell
 constexpr int kMaxRegions = 8192; // R limit (keeps R*R in 32 bits, row scope in LDS)
 constexpr int kMaxTimed = 4096;   // attention calls recorded while timing
 constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
+constexpr int kPrefixChunkTiles = 128; // tiles per chunk of a prefix query row
+constexpr int kMaxPrefix = 4096;  // text-prefix tokens per sequence
 
 // ---------------------------------------------------------------------------
 // Workspace: one region of caller memory carved into these buffers.
@@ -27,11 +29,14 @@ constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
 //   prefix V bf16 : [bh][tile][cb][t][lane][16 B]   the same for the text
 //            prefix, tile t holding prefix keys 64t .. 64t+63 (zero past the
 //            valid ones)
+//   prefix partials : fp32 [bh][chunk][row][d] unnormalised outputs and
+//            float2 [bh][chunk][row] (running max, sum) of the prefix query
+//            rows' chunks, rows padded to ptiles*64
 // ---------------------------------------------------------------------------
 struct Workspace {
     size_t q8, q4, q4s, qs8;
     size_t k8, k4, k4s, ks8;
-    size_t v8, v4, v4s, vs8, vamax, v16, vp16;
+    size_t v8, v4, v4s, vs8, vamax, v16, vp16, pacc, pmz;
     size_t qavg, kavg, qmax, kmax;
     size_t la, lm, rmax, zsum, keys, tier;
     size_t sched, cnt;
@@ -53,6 +58,7 @@ struct da2_layout_s {
     int N, R, Ry, Rx, BH, d;
     int64_t nchunk;           // rank chunks per head (head scope)
     int ptiles;               // 64-key tiles of the text prefix (ceil(prefix / 64))
+    int pchunks;              // chunks of a prefix query row's key sequence (0: no prefix)
     da2::Workspace ws;
 };
 

@@ -55,6 +55,11 @@ struct AttnArgs {
     const int32_t *pvalid;
     void *outp;
     int Lp, ptiles, pkspan;
+    // prefix query rows: per (b, h), chunk and row (padded to ptiles * 64)
+    // the chunk's running max, sum and unnormalised output
+    float *pacc;
+    float2 *pmz;
+    int pchunks;
     const int32_t *sched;
     const int32_t *cnt;
     void *out;
@@ -457,12 +462,13 @@ __device__ __forceinline__ uint8_t *chunk16(uint8_t *b0, uint8_t *b1, int c)
 // half of the key buffers, and locates the value images (the bf16 operand
 // written by the V preparation, one 64 x D image per tile).
 //
-// Video regions of one head: the schedule's 16-bit list, or (DENSE) every
-// region in order.
+// Video regions of one head: the schedule's 16-bit list, or (DENSE) the
+// regions first, first + 1, ... in order.
 template <int D, bool DENSE>
 struct VideoKeys16 {
     static constexpr bool kMasked = false;
     const int32_t *list;
+    int first;
     const uint16_t *kh;            // K of this head
     const uint8_t *vbase;          // value images of the head's regions
     int64_t vbytes;
@@ -470,9 +476,9 @@ struct VideoKeys16 {
     int kspan, Ry, Rx, Hv, Wv;
     int64_t osn;
 
-    __device__ __forceinline__ VideoKeys16(const AttnArgs &A, const int32_t *list_, int64_t hoff,
+    __device__ __forceinline__ VideoKeys16(const AttnArgs &A, const int32_t *list_, int first_, int64_t hoff,
                                            int64_t hbase, int w, int l)
-        : list(list_), kh(A.k + hoff), kspan(A.kspan), Ry(A.Ry), Rx(A.Rx), Hv(A.Hv), Wv(A.Wv),
+        : list(list_), first(first_), kh(A.k + hoff), kspan(A.kspan), Ry(A.Ry), Rx(A.Rx), Hv(A.Hv), Wv(A.Wv),
           osn(A.osn)
     {
         // wave w gathers the key rows of half m = w: a fixed byte offset from
@@ -482,7 +488,7 @@ struct VideoKeys16 {
         vbase = A.v16 + hbase * (kBlk * D * 2);
         vbytes = (int64_t)A.R * kBlk * D * 2;
     }
-    __device__ __forceinline__ int id(int i) const { return DENSE ? i : sload_i32(list + i); }
+    __device__ __forceinline__ int id(int i) const { return DENSE ? first + i : sload_i32(list + i); }
     __device__ __forceinline__ int valid(int) const { return kBlk; }
     __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
     {
@@ -496,12 +502,14 @@ struct VideoKeys16 {
 };
 
 // Text-prefix keys of one head (App. C.1): tile t holds prefix keys
-// 64 t .. 64 t + 63, of which the first nv - 64 t are valid.  Rows past the
-// valid ones are read from the last valid row (their logits are masked, so
-// only the address matters); their value rows are zero in the value image.
+// 64 t .. 64 t + 63, of which the first nv - 64 t are valid; the steps take
+// tiles first, first + 1, ...  Rows past the valid ones are read from the
+// last valid row (their logits are masked, so only the address matters);
+// their value rows are zero in the value image.
 template <int D>
 struct PrefixKeys16 {
     static constexpr bool kMasked = true;
+    int first;
     __amdgpu_buffer_rsrc_t ksrc;   // prefix K rows of this head
     const uint8_t *vbase;          // prefix value images of this head
     int64_t vbytes;
@@ -509,8 +517,9 @@ struct PrefixKeys16 {
     uint32_t lane_off;             // channel offset of this lane, bytes
     int64_t osn;
 
-    __device__ __forceinline__ PrefixKeys16(const AttnArgs &A, int64_t hoff, int bh, int nv_, int w, int l)
-        : nv(nv_), osn(A.osn)
+    __device__ __forceinline__ PrefixKeys16(const AttnArgs &A, int first_, int64_t hoff, int bh, int nv_, int w,
+                                            int l)
+        : first(first_), nv(nv_), osn(A.osn)
     {
         kpos = key_of_row(l & 31, w);
         lane_off = (uint32_t)(16 * (l >> 5));
@@ -518,7 +527,7 @@ struct PrefixKeys16 {
         vbase = A.vp16 + (int64_t)bh * A.ptiles * (kBlk * D * 2);
         vbytes = (int64_t)A.ptiles * kBlk * D * 2;
     }
-    __device__ __forceinline__ int id(int i) const { return i; }
+    __device__ __forceinline__ int id(int i) const { return first + i; }
     __device__ __forceinline__ int valid(int kb) const { return nv - kBlk * kb; }
     __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
     {
@@ -1058,9 +1067,9 @@ struct Attn {
         const int qt = region_token(a, 32 * w + (l & 31), A.Ry, A.Rx, A.Hv, A.Wv);
         load_q16<D>(A.q + hoff + (int64_t)qt * A.osn, l, q16);
         if (np > 0)
-            run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, hoff, bh, nv, w, l), np, q16, w, l, acc, m, z);
+            run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, 0, hoff, bh, nv, w, l), np, q16, w, l, acc, m, z);
         if (n16 > 0)
-            run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, false>(A, list16, hoff, hbase, w, l), n16, q16, w,
+            run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, false>(A, list16, 0, hoff, hbase, w, l), n16, q16, w,
                      l, acc, m, z);
     }
 
@@ -1144,14 +1153,17 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     S.epilogue(a);
 }
 
-// Text-prefix queries (App. C.1: non-sparse attention): one workgroup per 64
-// prefix query rows of one (b, h), wave w owning rows 32 w .. 32 w + 31;
-// every valid prefix key, then every video region in order, all on the
-// 16-bit path.  Rows past Lp (the last workgroup's tail) compute on a copy
-// of row Lp - 1 and are not written.
+// Prefix query rows (App. C.1: non-sparse attention).  A row's key sequence
+// is its valid prefix tiles, then every video region in order, all on the
+// 16-bit path; it is cut into chunks of kPrefixChunkTiles consecutive tiles.
+// One workgroup takes 64 rows of one (b, h) (wave w owning rows 32 w ..
+// 32 w + 31) and one chunk, runs its own online softmax over the chunk and
+// leaves the chunk's state (running max m, sum Z, unnormalised output) for
+// the merge.  Rows past Lp (the last workgroup's tail) compute on a copy of
+// row Lp - 1 and are not written.
 template <int D>
 __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
-                                            uint8_t *vb1, int pb, int bh, int w, int l)
+                                            uint8_t *vb1, int pb, int bh, int c, int w, int l)
 {
     const int b = bh / A.H, h = bh - b * A.H;
     const int64_t hoff = (int64_t)b * A.osb + (int64_t)h * A.osh;
@@ -1165,21 +1177,30 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
     float m = -__builtin_huge_valf(), z = 0.0f;
     const int nv = prefix_valid(A, b);
     const int np = (nv + kBlk - 1) / kBlk;
-    if (np > 0)
-        run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, hoff, bh, nv, w, l), np, q16, w, l, acc, m, z);
-    run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, true>(A, nullptr, hoff, (int64_t)bh * A.R, w, l), A.R, q16,
-             w, l, acc, m, z);
+    const int t0 = c * kPrefixChunkTiles, t1 = min(t0 + kPrefixChunkTiles, np + A.R);
+    if (t0 < np)
+        run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, t0, hoff, bh, nv, w, l), min(t1, np) - t0, q16, w,
+                 l, acc, m, z);
+    const int r0 = max(t0, np) - np, r1 = t1 - np;
+    if (r1 > r0)
+        run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, true>(A, nullptr, r0, hoff, (int64_t)bh * A.R, w, l),
+                 r1 - r0, q16, w, l, acc, m, z);
     const float zt = pair_sum(z);
-    const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
-    if (row < A.Lp)
-        store_row<D>(A, A.outp, hoff + (int64_t)row * A.osn, acc, inv, l >> 5);
+    if (row < A.Lp) {
+        const int64_t slot = ((int64_t)bh * A.pchunks + c) * (A.ptiles * kBlk) + row;
+        float *dst = A.pacc + slot * D;
+        const int hf = l >> 5;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; cb++)
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+                *reinterpret_cast<float4 *>(dst + 32 * cb + 8 * g + 4 * hf) =
+                    make_float4(acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2], acc[cb][4 * g + 3]);
+        if (hf == 0)
+            A.pmz[slot] = make_float2(m, zt);
+    }
 }
 
-// Text-prefix queries (App. C.1: non-sparse attention): one workgroup per 64
-// prefix query rows of one (b, h), wave w owning rows 32 w .. 32 w + 31;
-// every valid prefix key, then every video region in order, all on the
-// 16-bit path.  Rows past Lp (the last workgroup's tail) compute on a copy
-// of row Lp - 1 and are not written.
 template <int D>
 __global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
 {
@@ -1188,7 +1209,50 @@ __global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
     __shared__ __attribute__((aligned(1024))) uint8_t vb0[kBlk * D];
     __shared__ __attribute__((aligned(1024))) uint8_t vb1[kBlk * D];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    prefix_rows<D>(A, kb0, kb1, vb0, vb1, (int)blockIdx.x, (int)blockIdx.y, w, (int)(threadIdx.x & 63));
+    prefix_rows<D>(A, kb0, kb1, vb0, vb1, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z, w,
+                   (int)(threadIdx.x & 63));
+}
+
+// Merge of a prefix row's chunks (App. B.4's shared normalization across
+// parts): M = max m_c, Z = sum Z_c 2^(m_c - M), O = sum acc_c 2^(m_c - M) / Z
+// (m in log2 units).  Thread: one row, 4 consecutive channels.
+template <int D>
+__global__ __launch_bounds__(256) void k_prefix_merge(const AttnArgs A)
+{
+    constexpr int TPR = D / 4;   // threads per row
+    const int bh = blockIdx.y;
+    const int row = blockIdx.x * (256 / TPR) + (int)threadIdx.x / TPR;
+    const int c0 = 4 * ((int)threadIdx.x % TPR);
+    if (row >= A.Lp)
+        return;
+    const int64_t rows = (int64_t)A.ptiles * kBlk;
+    const int64_t base = (int64_t)bh * A.pchunks * rows + row;
+    float M = -__builtin_huge_valf();
+    for (int c = 0; c < A.pchunks; c++)
+        M = fmaxf(M, A.pmz[base + c * rows].x);
+    float Z = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int c = 0; c < A.pchunks; c++) {
+        const float2 mz = A.pmz[base + c * rows];
+        const float f = __builtin_amdgcn_exp2f(mz.x - M);
+        const float4 a = *reinterpret_cast<const float4 *>(A.pacc + (base + c * rows) * D + c0);
+        Z += mz.y * f;
+        o.x += a.x * f;
+        o.y += a.y * f;
+        o.z += a.z * f;
+        o.w += a.w * f;
+    }
+    const float inv = Z > 0.0f ? 1.0f / Z : 0.0f;
+    const int b = bh / A.H, h = bh - b * A.H;
+    const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)row * A.osn + c0;
+    if (A.out_f32) {
+        *reinterpret_cast<float4 *>((float *)A.outp + obase) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    } else {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(o.x * inv) | ((uint32_t)f32_to_bf16(o.y * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(o.z * inv) | ((uint32_t)f32_to_bf16(o.w * inv) << 16);
+        *reinterpret_cast<uint2 *>((uint16_t *)A.outp + obase) = pk;
+    }
 }
 
 }  // namespace
@@ -1237,17 +1301,23 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
     A.pvalid = px ? px->valid : nullptr;
     A.outp = px ? px->op : nullptr;
     A.pkspan = A.Lp > 0 ? (int)(((int64_t)(A.Lp - 1) * L.s.stride_n + L.d) * 2) : 0;
+    A.pacc = (float *)(ws + W.pacc);
+    A.pmz = (float2 *)(ws + W.pmz);
+    A.pchunks = L.pchunks;
     dim3 grid(8 * ((L.R + 7) / 8) * L.BH);
     if (L.d == 128)
         k_attn<128><<<grid, 128, 0, st>>>(A);
     else
         k_attn<64><<<grid, 128, 0, st>>>(A);
     if (A.Lp > 0) {
-        dim3 pgrid((A.Lp + kBlk - 1) / kBlk, L.BH);
-        if (L.d == 128)
+        dim3 pgrid((A.Lp + kBlk - 1) / kBlk, L.BH, L.pchunks);
+        if (L.d == 128) {
             k_attn_prefix<128><<<pgrid, 128, 0, st>>>(A);
-        else
+            k_prefix_merge<128><<<dim3((A.Lp + 7) / 8, L.BH), 256, 0, st>>>(A);
+        } else {
             k_attn_prefix<64><<<pgrid, 128, 0, st>>>(A);
+            k_prefix_merge<64><<<dim3((A.Lp + 15) / 16, L.BH), 256, 0, st>>>(A);
+        }
     }
 }
 
