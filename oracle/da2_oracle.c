@@ -1326,8 +1326,9 @@ int or_attention_kp(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *
 /* outside the region budget, prefix queries attend to every valid key. */
 /* The prefix tensors qp, kp, vp are [B,H,Lp,d] bf16; valid[b] in      */
 /* [0, Lp] is the number of valid prefix keys of batch b (NULL: all).   */
-/* out: the video rows as in or_attention; outp: [B,H,Lp,d] prefix query */
-/* rows (NULL: not computed).  pt: tier of the prefix interactions (16  */
+/* out: the video rows as in or_attention; outp: [B,H,np,d] prefix query */
+/* rows prows[0..np) (prows NULL: all Lp rows, np = Lp; outp NULL: none). */
+/* pt: tier of the prefix interactions (16                              */
 /* or 32).  The _kp variant takes the kernel-precision decisions and    */
 /* always uses the 16-bit path for them.                                */
 /* ------------------------------------------------------------------ */
@@ -1360,8 +1361,9 @@ static void prefix_ops_free(prefix_ops *px)
 static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
                       const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
                       const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
-                      const uint8_t *tier, int nqb, const int32_t *qblocks, double *out,
-                      double *allow, double *outp, double *allowp)
+                      const uint8_t *tier, int nqb, const int32_t *qblocks, int nprow,
+                      const int32_t *prows, double *out, double *allow, double *outp,
+                      double *allowp)
 {
     int N = F * Hv * Wv, R = N / OR_BLK;
     int kp_mode = allow != NULL;
@@ -1388,9 +1390,11 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
                 attention_row(&h, &px, tm + (size_t)a * R, a * OR_BLK + i, out + o, NULL);
         }
         if (outp) {
-#pragma omp parallel for schedule(dynamic, 4)
-            for (int i = 0; i < Lp; i++) {
-                size_t o = ((size_t)bh * Lp + i) * d;
+            int n = prows ? nprow : Lp;
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int j = 0; j < n; j++) {
+                int i = prows ? prows[j] : j;
+                size_t o = ((size_t)bh * n + j) * d;
                 if (kp_mode)
                     attention_prefix_row_kp(&h, &px, i, outp + o, allowp + o);
                 else
@@ -1407,22 +1411,23 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
 int or_attention_pfx(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
                      const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
                      const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
-                     const uint8_t *tier, int nqb, const int32_t *qblocks, double *out,
-                     double *outp)
+                     const uint8_t *tier, int nqb, const int32_t *qblocks, int nprow,
+                     const int32_t *prows, double *out, double *outp)
 {
     return pfx_common(B, H, F, Hv, Wv, d, q, k, v, Lp, qp, kp, vp, valid, pt, tier, nqb, qblocks,
-                      out, NULL, outp, NULL);
+                      nprow, prows, out, NULL, outp, NULL);
 }
 
 int or_attention_kp_pfx(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
                         const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
                         const uint16_t *kp, const uint16_t *vp, const int32_t *valid,
-                        const uint8_t *tier, int nqb, const int32_t *qblocks, double *out,
-                        double *allow, double *outp, double *allowp)
+                        const uint8_t *tier, int nqb, const int32_t *qblocks, int nprow,
+                        const int32_t *prows, double *out, double *allow, double *outp,
+                        double *allowp)
 {
     if (!allow || (outp == NULL) != (allowp == NULL)) return -1;
     return pfx_common(B, H, F, Hv, Wv, d, q, k, v, Lp, qp, kp, vp, valid, 16, tier, nqb, qblocks,
-                      out, allow, outp, allowp);
+                      nprow, prows, out, allow, outp, allowp);
 }
 
 /* ------------------------------------------------------------------ */

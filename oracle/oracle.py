@@ -84,10 +84,10 @@ def lib():
         L.or_mfma_fp8_dot64.argtypes = [P, P, C.c_float]
         L.or_mfma_fp8_dot64.restype = C.c_float
         L.or_attention_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P, C.c_int,
-                                                       P, C.c_int, P, P, P]
+                                                       P, C.c_int, P, C.c_int, P, P, P]
         L.or_attention_pfx.restype = C.c_int
         L.or_attention_kp_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P,
-                                                          P, C.c_int, P, P, P, P, P]
+                                                          P, C.c_int, P, C.c_int, P, P, P, P, P]
         L.or_attention_kp_pfx.restype = C.c_int
         L.or_dense.argtypes = [C.c_int] * 4 + [P, P, P, C.c_int, P, P]
         L.or_dense.restype = C.c_int
@@ -340,20 +340,34 @@ def _restore(x, F, Hv, Wv):
     return full
 
 
+def _prows(prefix_rows, Lp):
+    """prefix_rows: True (all Lp rows), False (none) or row indices."""
+    if prefix_rows is True:
+        return Lp, None
+    if prefix_rows is False or prefix_rows is None:
+        return 0, None
+    pr = np.ascontiguousarray(prefix_rows, np.int32)
+    assert ((pr >= 0) & (pr < Lp)).all()
+    return len(pr), pr
+
+
 def attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, pt=16, qblocks=None,
                   prefix_rows=True):
     """Tiered attention with a text prefix (App. C.1).  q, k, v: video
     [B,H,N,d]; qp, kp, vp: prefix [B,H,Lp,d]; valid: [B] valid prefix keys
     (None: all).  pt: precision of the prefix interactions (16 or 32).
-    Returns (video rows laid out as attention(), prefix rows [B,H,Lp,d] or
+    prefix_rows: True (all), False (none) or the prefix query rows wanted.
+    Returns (video rows laid out as attention(), prefix rows [B,H,np,d] or
     None)."""
     q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R) = _pfx_args(
         q, k, v, tier, qp, kp, vp, valid, qblocks)
+    npr, pr = _prows(prefix_rows, Lp)
     out = np.empty((B, H, nq, BLK, d), np.float64)
-    outp = np.empty((B, H, Lp, d), np.float64) if prefix_rows else None
+    outp = np.empty((B, H, npr, d), np.float64) if prefix_rows is not False else None
     rc = lib().or_attention_pfx(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
                                 _p(vp), None if va is None else _p(va), pt, _p(tier), nq,
-                                None if qb is None else _p(qb), _p(out),
+                                None if qb is None else _p(qb), npr,
+                                None if pr is None else _p(pr), _p(out),
                                 None if outp is None else _p(outp))
     assert rc == 0
     if qblocks is None:
@@ -367,13 +381,15 @@ def attention_kp_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, qblocks=N
     Returns (out, allow, outp, allowp)."""
     q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R) = _pfx_args(
         q, k, v, tier, qp, kp, vp, valid, qblocks)
+    npr, pr = _prows(prefix_rows, Lp)
     out = np.empty((B, H, nq, BLK, d), np.float64)
     allow = np.empty_like(out)
-    outp = np.empty((B, H, Lp, d), np.float64) if prefix_rows else None
-    allowp = np.empty((B, H, Lp, d), np.float64) if prefix_rows else None
+    outp = np.empty((B, H, npr, d), np.float64) if prefix_rows is not False else None
+    allowp = np.empty((B, H, npr, d), np.float64) if prefix_rows is not False else None
     rc = lib().or_attention_kp_pfx(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
                                    _p(vp), None if va is None else _p(va), _p(tier), nq,
-                                   None if qb is None else _p(qb), _p(out), _p(allow),
+                                   None if qb is None else _p(qb), npr,
+                                   None if pr is None else _p(pr), _p(out), _p(allow),
                                    None if outp is None else _p(outp),
                                    None if allowp is None else _p(allowp))
     assert rc == 0

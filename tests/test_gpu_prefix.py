@@ -151,3 +151,50 @@ def test_plain_call_ignores_prefix():
     r, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv)
     G.check_kp(od.cpu().numpy(), r, allow, "plain call with prefix layout")
     del o
+
+
+def test_prefix_full_size_hunyuan():
+    """The HunyuanVideo-shaped layer (24 heads, 33 x 48 x 80 latent tokens)
+    with a 256-token text prefix of which 200 keys are valid, in the launch
+    configuration the benchmark times ([B, Lp + N, H, d] bf16 storage, the
+    prefix first, plan from the draft).  Sampled: head 7's plan bit-exact
+    against the oracle's, four of its video query regions and prefix rows
+    around the valid boundary against the kernel-precision oracle."""
+    from video_diffusion_dit_frame_amd import configs, da2
+
+    w = configs.WORKLOADS["hunyuan"]
+    hi, lo = w.budgets[0]
+    Lp, nv, head = 256, 200, 7
+    q, k, v = G.inputs(w.B, w.H, w.F, w.Hv, w.Wv, w.d, w.seed, w.outliers)
+    qp, kp, vp = synth.make_prefix(w.B, w.H, Lp, w.d, w.seed + 7)
+
+    def joint_bnhd(video, prefix):
+        t = G.dev(np.concatenate([prefix, video], axis=2))     # [B, H, Lp + N, d]
+        return t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+    qj, kj, vj = joint_bnhd(q, qp), joint_bnhd(k, kp), joint_bnhd(v, vp)
+    oj = torch.empty((w.B, Lp + w.N, w.H, w.d), dtype=torch.float32, device="cuda").permute(0, 2, 1, 3)
+    L = da2.Layout.for_tensor(qj[:, :, Lp:], w.F, w.Hv, w.Wv, prefix=Lp)
+    P = da2.Plan(L)
+    P.plan(qj[:, :, Lp:], kj[:, :, Lp:], hi, lo, w.lam)
+    valid = torch.full((w.B,), nv, dtype=torch.int32, device="cuda")
+    P.attention_prefixed(qj[:, :, Lp:], kj[:, :, Lp:], vj[:, :, Lp:], oj[:, :, Lp:], qj[:, :, :Lp],
+                         kj[:, :, :Lp], vj[:, :, :Lp], oj[:, :, :Lp], valid)
+    torch.cuda.synchronize()
+    R = w.R
+    sl = lambda x: np.ascontiguousarray(x[:, head:head + 1])
+    qh, kh, vh, qph, kph, vph = (sl(x) for x in (q, k, v, qp, kp, vp))
+    ref_plan = O.plan(qh, kh, w.F, w.Hv, w.Wv, hi, lo, w.lam)
+    tier = P.tier_map().cpu().numpy()[:, head:head + 1]
+    assert np.array_equal(tier, ref_plan["tier"])
+    regions = [0, R // 3, (2 * R) // 3, R - 1]
+    prows = [0, 1, 99, nv - 1, nv, Lp - 1]
+    o = oj[:, head:head + 1, Lp:].cpu().numpy()
+    op = oj[:, head:head + 1, :Lp].cpu().numpy()[:, :, prows]
+    r, allow, rp, allowp = O.attention_kp_pfx(qh, kh, vh, ref_plan["tier"], w.F, w.Hv, w.Wv, qph, kph,
+                                               vph, [nv], qblocks=regions, prefix_rows=prows)
+    tok = O.layout(w.F, w.Hv, w.Wv)[(np.asarray(regions)[:, None] * 64 + np.arange(64)).ravel()]
+    rl, ma = G.check_kp(o[:, :, tok].reshape(r.shape), r, allow, "hunyuan+prefix video rows")
+    rlp, map_ = G.check_kp(op, rp, allowp, "hunyuan+prefix prefix rows")
+    print("hunyuan + 256-token prefix (200 valid), head %d: video rel_l2 %.2e max_abs %.2e; "
+          "prefix rel_l2 %.2e max_abs %.2e" % (head, rl, ma, rlp, map_))

@@ -210,3 +210,17 @@ def test_chunked_prefix_rows_equal_dense(orc, nv):
     _, _, kpp, alp = orc.attention_kp_pfx(q, k, v, tier.clip(max=16), F2, H2, W2, qp, kp, vp, valid,
                                           qblocks=[0])
     assert (np.abs(kpp[0, 0] - outp16[0, 0]) <= env).all()
+
+
+def test_prefix_row_selection(orc, prob):
+    """A selection of prefix query rows returns exactly those rows of the
+    full computation, video rows unchanged."""
+    d, (q, k, v), (qp, kp, vp), valid = prob
+    tier = np.random.default_rng(2).choice(np.array([0, 4, 8, 16], np.uint8), size=(2, 2, R, R))
+    out, outp = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid)
+    sel = [149, 0, 70, 71]
+    out2, outp2 = orc.attention_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid, prefix_rows=sel)
+    assert np.array_equal(out, out2) and np.array_equal(outp[:, :, sel], outp2)
+    o3, a3, p3, ap3 = orc.attention_kp_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid, prefix_rows=sel)
+    o4, a4, p4, ap4 = orc.attention_kp_pfx(q, k, v, tier, F, HV, WV, qp, kp, vp, valid)
+    assert np.array_equal(p4[:, :, sel], p3) and np.array_equal(ap4[:, :, sel], ap3)
