@@ -67,52 +67,245 @@ static uint32_t f32bits(float f)
 }
 
 /* ------------------------------------------------------------------ */
-/* O1 layout: [DA2] App. C.2 and Sec. 3.3 (compact spatial packing).    */
-/* For H_v, W_v multiples of 8 and C = 64 the balanced, minimum-        */
-/* perimeter partition of each frame is the 8x8 grid.                   */
-/* perm[pos] = original token index of reordered position pos.         */
+/* O1 layout: [DA2] Sec. 3.3 (a ragged 2D partition of each frame with  */
+/* balanced token counts, the smallest total perimeter among candidate  */
+/* partitions, the minimum number of blocks and less than one block of  */
+/* padding per frame; every region packed into one block of C slots)    */
+/* and App. C.2 (R_f = ceil(H_v W_v / C)), with C = 64.                 */
+/*                                                                      */
+/* Candidates: the frame is cut into bands of whole rows, or of whole   */
+/* columns.  A band of h lines and length L is walked as a column snake */
+/* (its columns in order, each from the band's first line to its last   */
+/* for even columns and back for odd ones) and cut into k = ceil(hL/C)  */
+/* consecutive pieces of balanced sizes (the first hL mod k pieces one  */
+/* token larger).  A candidate must give exactly R_f regions, each of   */
+/* at least 48 tokens; the smallest total perimeter (edges between a    */
+/* region's token and a token outside it or the frame's border) wins.   */
+/* Ties: row bands before column bands, then fewer bands, then the      */
+/* smaller first band height (and so on).  Regions are numbered band by */
+/* band and along the snake inside a band; a region's tokens take its   */
+/* slots in raster order, and the slots after them are padding.  For    */
+/* H_v, W_v multiples of 8 this is the 8x8 grid, raster inside each     */
+/* square.                                                              */
 /* ------------------------------------------------------------------ */
+#define OR_MINFILL 48
+
+/* Piece label of every cell of one band (h lines x L), lab[line*L + col]. */
+static int band_pieces(int h, int L, int *lab)
+{
+    int n = h * L, k = (n + OR_BLK - 1) / OR_BLK;
+    int q = n / k, rem = n % k;
+    int piece = 0, used = 0;
+    for (int col = 0; col < L; col++)
+        for (int t = 0; t < h; t++) {
+            int line = (col % 2 == 0) ? t : h - 1 - t;
+            lab[line * L + col] = piece;
+            used++;
+            if (used == q + (piece < rem ? 1 : 0)) {
+                piece++;
+                used = 0;
+            }
+        }
+    return k;
+}
+
+/* Total perimeter of a band's pieces, or -1 if a piece is under 48. */
+static long band_perimeter(int h, int L)
+{
+    int n = h * L, k = (n + OR_BLK - 1) / OR_BLK;
+    if (n / k < OR_MINFILL)
+        return -1;
+    int *lab = malloc(sizeof(int) * n);
+    band_pieces(h, L, lab);
+    long per = 0;
+    for (int line = 0; line < h; line++)
+        for (int col = 0; col < L; col++) {
+            int me = lab[line * L + col];
+            int same = 0;
+            if (line > 0 && lab[(line - 1) * L + col] == me) same++;
+            if (line < h - 1 && lab[(line + 1) * L + col] == me) same++;
+            if (col > 0 && lab[line * L + col - 1] == me) same++;
+            if (col < L - 1 && lab[line * L + col + 1] == me) same++;
+            per += 4 - same;
+        }
+    free(lab);
+    return per;
+}
+
+/* Best band sequence of one orientation: E lines across, bands of length L,
+ * exactly Rf regions.  Returns the number of bands (heights in hs) and the
+ * perimeter in *per, or -1 when no candidate exists. */
+static int best_bands(int E, int L, int Rf, int32_t *hs, long *per)
+{
+    long *pb = malloc(sizeof(long) * (E + 1));
+    int *kb = malloc(sizeof(int) * (E + 1));
+    for (int h = 1; h <= E; h++) {
+        pb[h] = band_perimeter(h, L);
+        kb[h] = (h * L + OR_BLK - 1) / OR_BLK;
+    }
+    /* cost[e][r]: best (perimeter, bands) covering lines e..E-1 with r regions */
+    size_t S = (size_t)(E + 1) * (Rf + 1);
+    long *cost = malloc(sizeof(long) * S);
+    int *nb = malloc(sizeof(int) * S), *pick = malloc(sizeof(int) * S);
+    for (size_t i = 0; i < S; i++) { cost[i] = -1; nb[i] = 0; pick[i] = 0; }
+    cost[(size_t)E * (Rf + 1) + 0] = 0;
+    for (int e = E - 1; e >= 0; e--)
+        for (int r = 0; r <= Rf; r++) {
+            size_t me = (size_t)e * (Rf + 1) + r;
+            for (int h = 1; e + h <= E; h++) {
+                if (pb[h] < 0 || kb[h] > r) continue;
+                size_t nx = (size_t)(e + h) * (Rf + 1) + (r - kb[h]);
+                if (cost[nx] < 0) continue;
+                long c = pb[h] + cost[nx];
+                int n = 1 + nb[nx];
+                if (cost[me] < 0 || c < cost[me] || (c == cost[me] && n < nb[me])) {
+                    cost[me] = c;
+                    nb[me] = n;
+                    pick[me] = h;
+                }
+            }
+        }
+    int m = -1;
+    if (cost[Rf] >= 0) {
+        *per = cost[Rf];
+        m = 0;
+        for (int e = 0, r = Rf; e < E;) {
+            int h = pick[(size_t)e * (Rf + 1) + r];
+            hs[m++] = h;
+            r -= kb[h];
+            e += h;
+        }
+    }
+    free(pb); free(kb); free(cost); free(nb); free(pick);
+    return m;
+}
+
+/* The partition of an Hv x Wv frame: orientation (0: row bands, 1: column
+ * bands), band heights (capacity Hv + Wv) and total perimeter.  Returns the
+ * number of bands, or -1 when no candidate exists. */
+int or_partition_bands(int Hv, int Wv, int *orient, int32_t *bands, int64_t *perim)
+{
+    if (Hv <= 0 || Wv <= 0)
+        return -1;
+    int Rf = (Hv * Wv + OR_BLK - 1) / OR_BLK;
+    int32_t *h0 = malloc(sizeof(int32_t) * (Hv + Wv)), *h1 = malloc(sizeof(int32_t) * (Hv + Wv));
+    long p0 = 0, p1 = 0;
+    int m0 = best_bands(Hv, Wv, Rf, h0, &p0);
+    int m1 = best_bands(Wv, Hv, Rf, h1, &p1);
+    int m = -1;
+    if (m0 >= 0 && (m1 < 0 || p0 <= p1)) {
+        *orient = 0;
+        memcpy(bands, h0, sizeof(int32_t) * m0);
+        *perim = p0;
+        m = m0;
+    } else if (m1 >= 0) {
+        *orient = 1;
+        memcpy(bands, h1, sizeof(int32_t) * m1);
+        *perim = p1;
+        m = m1;
+    }
+    free(h0);
+    free(h1);
+    return m;
+}
+
+/* Slot table of one frame: tok[r*64 + i] = y*Wv + x of region r's slot i,
+ * -1 for padding; nvalid[r] = its token count.  Returns R_f or -1. */
+int or_partition(int Hv, int Wv, int32_t *tok, int32_t *nvalid)
+{
+    int orient;
+    int64_t per;
+    int32_t *bands = malloc(sizeof(int32_t) * (Hv + Wv));
+    int m = or_partition_bands(Hv, Wv, &orient, bands, &per);
+    if (m < 0) { free(bands); return -1; }
+    int Rf = (Hv * Wv + OR_BLK - 1) / OR_BLK;
+    int *reg = malloc(sizeof(int) * Hv * Wv);   /* region of each cell */
+    int L = orient ? Hv : Wv;
+    int base = 0, line0 = 0;
+    for (int b = 0; b < m; b++) {
+        int h = bands[b];
+        int *lab = malloc(sizeof(int) * h * L);
+        int k = band_pieces(h, L, lab);
+        for (int line = 0; line < h; line++)
+            for (int col = 0; col < L; col++) {
+                int y = orient ? col : line0 + line, x = orient ? line0 + line : col;
+                reg[y * Wv + x] = base + lab[line * L + col];
+            }
+        free(lab);
+        base += k;
+        line0 += h;
+    }
+    for (int r = 0; r < Rf; r++)
+        nvalid[r] = 0;
+    for (int i = 0; i < Rf * OR_BLK; i++)
+        tok[i] = -1;
+    for (int y = 0; y < Hv; y++)
+        for (int x = 0; x < Wv; x++) {
+            int r = reg[y * Wv + x];
+            tok[r * OR_BLK + nvalid[r]++] = y * Wv + x;
+        }
+    free(reg);
+    free(bands);
+    return Rf;
+}
+
+/* Regions of an F x Hv x Wv video (F R_f), or -1 when Hv x Wv has no
+ * partition. */
+int or_regions(int F, int Hv, int Wv)
+{
+    int orient;
+    int64_t per;
+    if (F <= 0) return -1;
+    int32_t *bands = malloc(sizeof(int32_t) * (Hv + Wv > 0 ? Hv + Wv : 1));
+    int m = or_partition_bands(Hv, Wv, &orient, bands, &per);
+    free(bands);
+    return m < 0 ? -1 : F * ((Hv * Wv + OR_BLK - 1) / OR_BLK);
+}
+
+/* perm[pos] (pos < F R_f 64) = original token index of reordered position
+ * pos, -1 for padding.  Region a = f R_f + r covers frame f's region r. */
 int or_layout(int F, int Hv, int Wv, int32_t *perm)
 {
-    if (F <= 0 || Hv <= 0 || Wv <= 0 || Hv % 8 || Wv % 8)
+    if (or_regions(F, Hv, Wv) < 0)
         return -1;
-    int Ry = Hv / 8, Rx = Wv / 8;
+    int Rf = (Hv * Wv + OR_BLK - 1) / OR_BLK;
+    int32_t *tok = malloc(sizeof(int32_t) * Rf * OR_BLK), *nv = malloc(sizeof(int32_t) * Rf);
+    or_partition(Hv, Wv, tok, nv);
     for (int f = 0; f < F; f++)
-        for (int ry = 0; ry < Ry; ry++)
-            for (int rx = 0; rx < Rx; rx++) {
-                int a = (f * Ry + ry) * Rx + rx;
-                for (int iy = 0; iy < 8; iy++)
-                    for (int ix = 0; ix < 8; ix++) {
-                        int pos = a * OR_BLK + iy * 8 + ix;
-                        int y = ry * 8 + iy, x = rx * 8 + ix;
-                        perm[pos] = (f * Hv + y) * Wv + x;
-                    }
-            }
+        for (int i = 0; i < Rf * OR_BLK; i++)
+            perm[(size_t)f * Rf * OR_BLK + i] = tok[i] < 0 ? -1 : f * Hv * Wv + tok[i];
+    free(tok);
+    free(nv);
     return 0;
 }
 
 /* ------------------------------------------------------------------ */
 /* O2 pooled descriptors: [DA2] Sec. 3.1 Eq. (1), App. C.1.             */
-/* X is one head, [N][d] bf16.  avg[a][c] = (sum over the region in     */
-/* region order, fp64) / n_a with n_a = 64; mx[a][c] = signed max,      */
-/* first occurrence kept on equal values.                               */
+/* X is one head, [N][d] bf16.  avg[a][c] = (sum over the region's n_a  */
+/* valid tokens in slot order, fp64) / n_a; mx[a][c] = signed max over  */
+/* the valid tokens, first occurrence kept on equal values.  Padding    */
+/* slots (perm -1) take no part.                                        */
 /* ------------------------------------------------------------------ */
 void or_pool_head(const uint16_t *X, int d, const int32_t *perm, int R,
                   double *avg, float *mx)
 {
-    for (int a = 0; a < R; a++)
+    for (int a = 0; a < R; a++) {
+        int na = 0;
+        while (na < OR_BLK && perm[a * OR_BLK + na] >= 0)
+            na++;
         for (int c = 0; c < d; c++) {
             double s = 0.0;
             float m = bf16f(X[(size_t)perm[a * OR_BLK] * d + c]);
-            for (int i = 0; i < OR_BLK; i++) {
+            for (int i = 0; i < na; i++) {
                 float v = bf16f(X[(size_t)perm[a * OR_BLK + i] * d + c]);
                 s += (double)v;
                 if (v > m)
                     m = v;
             }
-            avg[(size_t)a * d + c] = s / (double)OR_BLK;
+            avg[(size_t)a * d + c] = s / (double)na;
             mx[(size_t)a * d + c] = m;
         }
+    }
 }
 
 /* ------------------------------------------------------------------ */
@@ -319,12 +512,11 @@ int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
             uint32_t *keys, uint8_t *tier, double *qavg, double *kavg, float *qmx,
             float *kmx)
 {
-    int N = F * Hv * Wv, R = N / OR_BLK;
-    int32_t *perm = malloc(sizeof(int32_t) * N);
-    if (or_layout(F, Hv, Wv, perm)) {
-        free(perm);
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
+    if (R < 0)
         return -1;
-    }
+    int32_t *perm = malloc(sizeof(int32_t) * (size_t)R * OR_BLK);
+    or_layout(F, Hv, Wv, perm);
     int64_t T16, T8c, Tk;
     or_quotas(scope == 0 ? (int64_t)R * R : (int64_t)R, full_bp, hi_bp, lo_bp, &T16, &T8c, &Tk);
     double *qa = malloc(sizeof(double) * (size_t)R * d), *ka = malloc(sizeof(double) * (size_t)R * d);
@@ -468,15 +660,23 @@ static void fp8_scale(float amax, float *s, float *inv)
     }
 }
 
-void or_quant_qk_head(const uint16_t *X, int N, int d, const int32_t *perm,
+/* Value at reordered position pos, channel c: 0 for a padding slot. */
+static float xat(const uint16_t *X, const int32_t *perm, size_t pos, int d, int c)
+{
+    return perm[pos] < 0 ? 0.0f : bf16f(X[(size_t)perm[pos] * d + c]);
+}
+
+/* Q/K of one head over Np = R 64 reordered positions (padding slots hold
+ * zeros): c8 [Np][d] codes, s8 [R] scales, c4 [Np][d], e4 [Np][d/32]. */
+void or_quant_qk_head(const uint16_t *X, int Np, int d, const int32_t *perm,
                       uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
 {
-    int R = N / OR_BLK;
+    int R = Np / OR_BLK;
     for (int a = 0; a < R; a++) {
         float amax = 0.0f;
         for (int i = 0; i < OR_BLK; i++)
             for (int c = 0; c < d; c++) {
-                float v = fabsf(bf16f(X[(size_t)perm[a * OR_BLK + i] * d + c]));
+                float v = fabsf(xat(X, perm, (size_t)a * OR_BLK + i, d, c));
                 if (v > amax) amax = v;
             }
         float s, inv;
@@ -484,32 +684,33 @@ void or_quant_qk_head(const uint16_t *X, int N, int d, const int32_t *perm,
         s8[a] = s;
         for (int i = 0; i < OR_BLK; i++)
             for (int c = 0; c < d; c++) {
-                float v = bf16f(X[(size_t)perm[a * OR_BLK + i] * d + c]);
+                float v = xat(X, perm, (size_t)a * OR_BLK + i, d, c);
                 float prod = v * inv;
                 c8[((size_t)a * OR_BLK + i) * d + c] = or_e4m3_encode((double)prod);
             }
     }
-    for (int pos = 0; pos < N; pos++)
+    for (int pos = 0; pos < Np; pos++)
         for (int g = 0; g < d / 32; g++) {
             double amax = 0.0;
             for (int j = 0; j < 32; j++) {
-                double v = fabs((double)bf16f(X[(size_t)perm[pos] * d + 32 * g + j]));
+                double v = fabs((double)xat(X, perm, pos, d, 32 * g + j));
                 if (v > amax) amax = v;
             }
             int E = or_mx_exponent(amax);
             e4[(size_t)pos * (d / 32) + g] = (uint8_t)(E + 127);
             for (int j = 0; j < 32; j++) {
-                double v = (double)bf16f(X[(size_t)perm[pos] * d + 32 * g + j]);
+                double v = (double)xat(X, perm, pos, d, 32 * g + j);
                 c4[(size_t)pos * d + 32 * g + j] = or_e2m1_encode(ldexp(v, -E));
             }
         }
 }
 
-/* V: c8 [N][d] codes, s8 [d] scales, c4 [N][d] codes, e4 [R][2][d] exponents */
-void or_quant_v_head(const uint16_t *X, int N, int d, const int32_t *perm,
+/* V of one head (N tokens, Np positions): c8 [Np][d] codes, s8 [d] scales
+ * (amax over the N tokens), c4 [Np][d] codes, e4 [R][2][d] exponents */
+void or_quant_v_head(const uint16_t *X, int N, int Np, int d, const int32_t *perm,
                      uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
 {
-    int R = N / OR_BLK;
+    int R = Np / OR_BLK;
     for (int c = 0; c < d; c++) {
         float amax = 0.0f;
         for (int n = 0; n < N; n++) {
@@ -519,8 +720,8 @@ void or_quant_v_head(const uint16_t *X, int N, int d, const int32_t *perm,
         float s, inv;
         fp8_scale(amax, &s, &inv);
         s8[c] = s;
-        for (int pos = 0; pos < N; pos++) {
-            float v = bf16f(X[(size_t)perm[pos] * d + c]);
+        for (int pos = 0; pos < Np; pos++) {
+            float v = xat(X, perm, pos, d, c);
             float prod = v * inv;
             c8[(size_t)pos * d + c] = or_e4m3_encode((double)prod);
         }
@@ -531,33 +732,36 @@ void or_quant_v_head(const uint16_t *X, int N, int d, const int32_t *perm,
                 double amax = 0.0;
                 for (int j = 0; j < 32; j++) {
                     int pos = a * OR_BLK + 32 * g + j;
-                    double v = fabs((double)bf16f(X[(size_t)perm[pos] * d + c]));
+                    double v = fabs((double)xat(X, perm, pos, d, c));
                     if (v > amax) amax = v;
                 }
                 int E = or_mx_exponent(amax);
                 e4[((size_t)a * 2 + g) * d + c] = (uint8_t)(E + 127);
                 for (int j = 0; j < 32; j++) {
                     int pos = a * OR_BLK + 32 * g + j;
-                    double v = (double)bf16f(X[(size_t)perm[pos] * d + c]);
+                    double v = (double)xat(X, perm, pos, d, c);
                     c4[(size_t)pos * d + c] = or_e2m1_encode(ldexp(v, -E));
                 }
             }
 }
 
-/* Whole-problem quantization into canonical layouts:
- *   qk8 [B,H,N,d] codes, qks8 [B,H,R] scales, qk4 [B,H,N,d], qke4 [B,H,N,d/32]
- *   v8  [B,H,N,d],       vs8  [B,H,d],        v4  [B,H,N,d], ve4  [B,H,R,2,d] */
+/* Whole-problem quantization into canonical layouts (Np = R 64 positions,
+ * region order, padding slots included):
+ *   qk8 [B,H,Np,d] codes, qks8 [B,H,R] scales, qk4 [B,H,Np,d], qke4 [B,H,Np,d/32]
+ *   v8  [B,H,Np,d],       vs8  [B,H,d],        v4  [B,H,Np,d], ve4  [B,H,R,2,d] */
 int or_quant_qk(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
                 uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
 {
-    int N = F * Hv * Wv, R = N / OR_BLK;
-    int32_t *perm = malloc(sizeof(int32_t) * N);
-    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
+    if (R < 0) return -1;
+    size_t Np = (size_t)R * OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * Np);
+    or_layout(F, Hv, Wv, perm);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < B * H; bh++)
-        or_quant_qk_head(X + (size_t)bh * N * d, N, d, perm, c8 + (size_t)bh * N * d,
-                         s8 + (size_t)bh * R, c4 + (size_t)bh * N * d,
-                         e4 + (size_t)bh * N * (d / 32));
+        or_quant_qk_head(X + (size_t)bh * N * d, (int)Np, d, perm, c8 + (size_t)bh * Np * d,
+                         s8 + (size_t)bh * R, c4 + (size_t)bh * Np * d,
+                         e4 + (size_t)bh * Np * (d / 32));
     free(perm);
     return 0;
 }
@@ -565,13 +769,15 @@ int or_quant_qk(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
 int or_quant_v(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
                uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
 {
-    int N = F * Hv * Wv, R = N / OR_BLK;
-    int32_t *perm = malloc(sizeof(int32_t) * N);
-    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
+    if (R < 0) return -1;
+    size_t Np = (size_t)R * OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * Np);
+    or_layout(F, Hv, Wv, perm);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < B * H; bh++)
-        or_quant_v_head(X + (size_t)bh * N * d, N, d, perm, c8 + (size_t)bh * N * d,
-                        s8 + (size_t)bh * d, c4 + (size_t)bh * N * d,
+        or_quant_v_head(X + (size_t)bh * N * d, N, (int)Np, d, perm, c8 + (size_t)bh * Np * d,
+                        s8 + (size_t)bh * d, c4 + (size_t)bh * Np * d,
                         e4 + (size_t)bh * R * 2 * d);
     free(perm);
     return 0;
@@ -591,21 +797,31 @@ int or_quant_v(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
 /* updated once per 64-key tile.                                        */
 /* ------------------------------------------------------------------ */
 typedef struct {
-    int N, d, R;
+    int N, d, R;             /* N: reordered positions R 64 (padding included) */
     const int32_t *perm;
-    double *qf, *kf, *vf;    /* unquantized, reordered [N][d] */
+    int32_t *nv;             /* valid tokens of each region [R] (slots 0 .. nv-1) */
+    double *qf, *kf, *vf;    /* unquantized, reordered [N][d]; padding rows 0 */
     double *q8, *k8, *v8;    /* FP8 dequantized */
     double *q4, *k4, *v4;    /* MXFP4 dequantized */
     uint8_t *c8q, *c8k;      /* FP8 codes of Q and K, reordered [N][d] */
     float *s8q, *s8k;        /* their per-block scales [R] */
 } head_ops;
 
+/* q, k, v: one head, [Ntok][d] in token order; perm over Np = R 64
+ * positions (-1 for padding). */
 static void head_ops_build(head_ops *h, const uint16_t *q, const uint16_t *k,
-                           const uint16_t *v, int N, int d, const int32_t *perm)
+                           const uint16_t *v, int Ntok, int Np, int d, const int32_t *perm)
 {
-    int R = N / OR_BLK;
+    int N = Np, R = Np / OR_BLK;
     size_t nd = (size_t)N * d;
     h->N = N; h->d = d; h->R = R; h->perm = perm;
+    h->nv = malloc(sizeof(int32_t) * R);
+    for (int a = 0; a < R; a++) {
+        int n = 0;
+        while (n < OR_BLK && perm[a * OR_BLK + n] >= 0)
+            n++;
+        h->nv[a] = n;
+    }
     double **arrs[9] = {&h->qf, &h->kf, &h->vf, &h->q8, &h->k8, &h->v8, &h->q4, &h->k4, &h->v4};
     for (int i = 0; i < 9; i++)
         *arrs[i] = malloc(sizeof(double) * nd);
@@ -623,7 +839,7 @@ static void head_ops_build(head_ops *h, const uint16_t *q, const uint16_t *k,
     for (int t = 0; t < 3; t++) {
         for (int pos = 0; pos < N; pos++)
             for (int c = 0; c < d; c++)
-                full[t][(size_t)pos * d + c] = (double)bf16f(src[t][(size_t)perm[pos] * d + c]);
+                full[t][(size_t)pos * d + c] = (double)xat(src[t], perm, pos, d, c);
         if (t < 2) {
             or_quant_qk_head(src[t], N, d, perm, c8, s8, c4, e4);
             memcpy(t == 0 ? h->c8q : h->c8k, c8, nd);
@@ -635,7 +851,7 @@ static void head_ops_build(head_ops *h, const uint16_t *q, const uint16_t *k,
                     d4[t][i] = ldexp(or_e2m1_value(c4[i]), (int)e4[(size_t)pos * (d / 32) + c / 32] - 127);
                 }
         } else {
-            or_quant_v_head(src[t], N, d, perm, c8, s8, c4, e4);
+            or_quant_v_head(src[t], Ntok, N, d, perm, c8, s8, c4, e4);
             for (int pos = 0; pos < N; pos++)
                 for (int c = 0; c < d; c++) {
                     size_t i = (size_t)pos * d + c;
@@ -657,6 +873,7 @@ static void head_ops_free(head_ops *h)
     free(h->c8k);
     free(h->s8q);
     free(h->s8k);
+    free(h->nv);
 }
 
 /* Weight quantizers for one 64-key tile, w[64] in key order. */
@@ -796,9 +1013,9 @@ static void attention_row(const head_ops *h, const prefix_ops *px, const uint8_t
             if (tier_row[b] != p)
                 continue;
             tile_exact(&st, d, p, Q + (size_t)u * d, K + (size_t)b * OR_BLK * d,
-                       V + (size_t)b * OR_BLK * d, OR_BLK, s, w, wq);
+                       V + (size_t)b * OR_BLK * d, h->nv[b], s, w, wq);
             if (tr) {
-                for (int j = 0; j < OR_BLK && tr->n < tr->cap; j++, tr->n++) {
+                for (int j = 0; j < h->nv[b] && tr->n < tr->cap; j++, tr->n++) {
                     tr->key[tr->n] = b * OR_BLK + j;
                     tr->tier[tr->n] = p;
                     tr->s[tr->n] = s[j];
@@ -839,7 +1056,7 @@ static int prefix_row_tile(const head_ops *h, const prefix_ops *px, int t, const
     }
     *kt = h->kf + (size_t)(t - np) * OR_BLK * d;
     *vt = h->vf + (size_t)(t - np) * OR_BLK * d;
-    return OR_BLK;
+    return h->nv[t - np];
 }
 
 static void attention_prefix_row(const head_ops *h, const prefix_ops *px, int i, double *out)
@@ -886,21 +1103,27 @@ int or_attention(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
                  const uint16_t *k, const uint16_t *v, const uint8_t *tier, int nqb,
                  const int32_t *qblocks, double *out)
 {
-    int N = F * Hv * Wv, R = N / OR_BLK;
-    int32_t *perm = malloc(sizeof(int32_t) * N);
-    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
+    if (R < 0) return -1;
+    int Np = R * OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * Np);
+    or_layout(F, Hv, Wv, perm);
     if (!qblocks) nqb = R;
     for (int bh = 0; bh < B * H; bh++) {
         head_ops h;
         size_t off = (size_t)bh * N * d;
-        head_ops_build(&h, q + off, k + off, v + off, N, d, perm);
+        head_ops_build(&h, q + off, k + off, v + off, N, Np, d, perm);
         const uint8_t *tm = tier + (size_t)bh * R * R;
 #pragma omp parallel for schedule(dynamic, 8)
         for (int r = 0; r < nqb * OR_BLK; r++) {
             int j = r / OR_BLK, i = r % OR_BLK;
             int a = qblocks ? qblocks[j] : j;
-            attention_row(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i,
-                          out + (((size_t)bh * nqb + j) * OR_BLK + i) * d, NULL);
+            double *o = out + (((size_t)bh * nqb + j) * OR_BLK + i) * d;
+            if (i >= h.nv[a]) {   /* padding slot: no query */
+                memset(o, 0, sizeof(double) * d);
+                continue;
+            }
+            attention_row(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i, o, NULL);
         }
         head_ops_free(&h);
     }
@@ -915,11 +1138,13 @@ int64_t or_attention_trace(int F, int Hv, int Wv, int d, const uint16_t *q,
                            int u, int64_t cap, int32_t *key, int32_t *tr_tier, double *s,
                            double *w, double *wq, double *m, double *Z, double *out)
 {
-    int N = F * Hv * Wv, R = N / OR_BLK;
-    int32_t *perm = malloc(sizeof(int32_t) * N);
-    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
+    if (R < 0) return -1;
+    int Np = R * OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * Np);
+    or_layout(F, Hv, Wv, perm);
     head_ops h;
-    head_ops_build(&h, q, k, v, N, d, perm);
+    head_ops_build(&h, q, k, v, N, Np, d, perm);
     row_trace tr = {cap, 0, key, tr_tier, s, w, wq, m, 0.0};
     attention_row(&h, NULL, tier + (size_t)(u / OR_BLK) * R, u, out, &tr);
     *Z = tr.Z;
@@ -1155,9 +1380,10 @@ static void attention_row_kp(const head_ops *h, const prefix_ops *px, const uint
         for (int b = 0; b < R; b++) {
             if (tier_row[b] != p)
                 continue;
+            const int nk = h->nv[b];
             if (p == 16) {
                 kp_tile16(&st, d, c4, h->qf + (size_t)u * d, h->kf + (size_t)b * OR_BLK * d,
-                          h->vf + (size_t)b * OR_BLK * d, OR_BLK);
+                          h->vf + (size_t)b * OR_BLK * d, nk);
                 continue;
             }
             float cf;
@@ -1189,12 +1415,17 @@ static void attention_row_kp(const head_ops *h, const prefix_ops *px, const uint
                     dS[j] = ldexp(mag, -20) + 2.0 * ulpf(S[j]);
                 }
             }
+            /* padding slots of the key region take no part */
+            for (int j = nk; j < OR_BLK; j++) {
+                S[j] = -INFINITY;
+                dS[j] = 0.0;
+            }
             kp_softmax(&st, d, S, dS, cf, e, eta, &t);
             const double *V = p == 8 ? h->v8 : h->v4;
             const double *vt = V + (size_t)b * OR_BLK * d;
             if (p == 8) {
                 /* scale of V is applied per channel: dequantized V already has it */
-                kp_accumulate(&st, d, q8_val, kPV8, e, eta, vt, OR_BLK);
+                kp_accumulate(&st, d, q8_val, kPV8, e, eta, vt, nk);
             } else {
                 for (int g = 0; g < 2; g++) {
                     float gm = S[32 * g], go = S[32 * (1 - g)];
@@ -1299,20 +1530,27 @@ int or_attention_kp(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *
                     const uint16_t *k, const uint16_t *v, const uint8_t *tier, int nqb,
                     const int32_t *qblocks, double *out, double *allow)
 {
-    int N = F * Hv * Wv, R = N / OR_BLK;
-    int32_t *perm = malloc(sizeof(int32_t) * N);
-    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
+    if (R < 0) return -1;
+    int Np = R * OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * Np);
+    or_layout(F, Hv, Wv, perm);
     if (!qblocks) nqb = R;
     for (int bh = 0; bh < B * H; bh++) {
         head_ops h;
         size_t off = (size_t)bh * N * d;
-        head_ops_build(&h, q + off, k + off, v + off, N, d, perm);
+        head_ops_build(&h, q + off, k + off, v + off, N, Np, d, perm);
         const uint8_t *tm = tier + (size_t)bh * R * R;
 #pragma omp parallel for schedule(dynamic, 8)
         for (int r = 0; r < nqb * OR_BLK; r++) {
             int j = r / OR_BLK, i = r % OR_BLK;
             int a = qblocks ? qblocks[j] : j;
             size_t o = (((size_t)bh * nqb + j) * OR_BLK + i) * d;
+            if (i >= h.nv[a]) {   /* padding slot: no query */
+                memset(out + o, 0, sizeof(double) * d);
+                memset(allow + o, 0, sizeof(double) * d);
+                continue;
+            }
             attention_row_kp(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i, out + o, allow + o);
         }
         head_ops_free(&h);
@@ -1365,18 +1603,20 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
                       const int32_t *prows, double *out, double *allow, double *outp,
                       double *allowp)
 {
-    int N = F * Hv * Wv, R = N / OR_BLK;
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
     int kp_mode = allow != NULL;
     if (pt != 16 && pt != 32) return -1;
     if (kp_mode && pt != 16) return -1;
-    int32_t *perm = malloc(sizeof(int32_t) * N);
-    if (or_layout(F, Hv, Wv, perm)) { free(perm); return -1; }
+    if (R < 0) return -1;
+    int Np = R * OR_BLK;
+    int32_t *perm = malloc(sizeof(int32_t) * Np);
+    or_layout(F, Hv, Wv, perm);
     if (!qblocks) nqb = R;
     for (int bh = 0; bh < B * H; bh++) {
         head_ops h;
         prefix_ops px;
         size_t off = (size_t)bh * N * d, poff = (size_t)bh * Lp * d;
-        head_ops_build(&h, q + off, k + off, v + off, N, d, perm);
+        head_ops_build(&h, q + off, k + off, v + off, N, Np, d, perm);
         prefix_ops_build(&px, qp + poff, kp + poff, vp + poff, Lp, valid ? valid[bh / H] : Lp, d, pt);
         const uint8_t *tm = tier + (size_t)bh * R * R;
 #pragma omp parallel for schedule(dynamic, 8)
@@ -1384,6 +1624,12 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
             int j = r / OR_BLK, i = r % OR_BLK;
             int a = qblocks ? qblocks[j] : j;
             size_t o = (((size_t)bh * nqb + j) * OR_BLK + i) * d;
+            if (i >= h.nv[a]) {   /* padding slot: no query */
+                memset(out + o, 0, sizeof(double) * d);
+                if (kp_mode)
+                    memset(allow + o, 0, sizeof(double) * d);
+                continue;
+            }
             if (kp_mode)
                 attention_row_kp(&h, &px, tm + (size_t)a * R, a * OR_BLK + i, out + o, allow + o);
             else

@@ -48,6 +48,13 @@ def lib():
         i32, i64, f64 = C.c_int32, C.c_int64, C.c_double
         L.or_layout.argtypes = [C.c_int, C.c_int, C.c_int, P]
         L.or_layout.restype = C.c_int
+        L.or_regions.argtypes = [C.c_int, C.c_int, C.c_int]
+        L.or_regions.restype = C.c_int
+        L.or_partition.argtypes = [C.c_int, C.c_int, P, P]
+        L.or_partition.restype = C.c_int
+        L.or_partition_bands.argtypes = [C.c_int, C.c_int, C.POINTER(C.c_int), P,
+                                         C.POINTER(C.c_int64)]
+        L.or_partition_bands.restype = C.c_int
         L.or_pool_head.argtypes = [P, C.c_int, P, C.c_int, P, P]
         L.or_exp_constants.argtypes = [P]
         L.or_exp.argtypes = [f64]
@@ -107,11 +114,41 @@ def _u16(x):
 
 
 # ---------------------------------------------------------------- layout
+def regions(F, Hv, Wv) -> int:
+    """R = F R_f regions of the partition; raises when the frame has none."""
+    R = lib().or_regions(F, Hv, Wv)
+    if R < 0:
+        raise ValueError("no partition of a %d x %d frame" % (Hv, Wv))
+    return R
+
+
 def layout(F, Hv, Wv) -> np.ndarray:
-    perm = np.empty(F * Hv * Wv, dtype=np.int32)
-    if lib().or_layout(F, Hv, Wv, _p(perm)):
-        raise ValueError("H_v and W_v must be positive multiples of 8")
+    """perm [R 64]: original token of each reordered position, -1 for padding."""
+    perm = np.empty(regions(F, Hv, Wv) * BLK, dtype=np.int32)
+    lib().or_layout(F, Hv, Wv, _p(perm))
     return perm
+
+
+def partition(Hv, Wv):
+    """One frame's slot table: (tok [R_f, 64] int32 with y*Wv + x or -1,
+    nvalid [R_f])."""
+    Rf = -(-Hv * Wv // BLK)
+    tok = np.empty((Rf, BLK), np.int32)
+    nv = np.empty(Rf, np.int32)
+    if lib().or_partition(Hv, Wv, _p(tok), _p(nv)) < 0:
+        raise ValueError("no partition of a %d x %d frame" % (Hv, Wv))
+    return tok, nv
+
+
+def partition_bands(Hv, Wv):
+    """(orientation 0 rows / 1 columns, band heights, total perimeter)."""
+    o = C.c_int()
+    per = C.c_int64()
+    bands = np.empty(Hv + Wv, np.int32)
+    m = lib().or_partition_bands(Hv, Wv, C.byref(o), _p(bands), C.byref(per))
+    if m < 0:
+        raise ValueError("no partition of a %d x %d frame" % (Hv, Wv))
+    return o.value, bands[:m].copy(), per.value
 
 
 # ---------------------------------------------------------------- draft
@@ -119,7 +156,7 @@ def pool_head(X: np.ndarray, F, Hv, Wv):
     """X: [N, d] uint16 -> (avg [R, d] f64, max [R, d] f32)."""
     X = _u16(X)
     N, d = X.shape
-    R = N // BLK
+    R = regions(F, Hv, Wv)
     perm = layout(F, Hv, Wv)
     avg = np.empty((R, d), np.float64)
     mx = np.empty((R, d), np.float32)
@@ -194,7 +231,7 @@ def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False, ful
     q = _u16(q)
     k = _u16(k)
     B, H, N, d = q.shape
-    R = N // BLK
+    R = regions(F, Hv, Wv)
     keys = np.empty((B, H, R, R), np.uint32)
     tier = np.empty((B, H, R, R), np.uint8)
     out = {"keys": keys, "tier": tier}
@@ -242,47 +279,58 @@ def mx_exponent(amax: float) -> int:
 
 
 def quant_qk(X, F, Hv, Wv):
-    """-> dict(c8 [B,H,N,d] u8, s8 [B,H,R] f32, c4 [B,H,N,d] u8, e4 [B,H,N,d/32] u8),
-    token axis in reordered position order."""
+    """-> dict(c8 [B,H,Np,d] u8, s8 [B,H,R] f32, c4 [B,H,Np,d] u8, e4 [B,H,Np,d/32] u8),
+    position axis in reordered order (Np = 64 R, padding slots included)."""
     X = _u16(X)
     B, H, N, d = X.shape
-    R = N // BLK
-    o = {"c8": np.empty((B, H, N, d), np.uint8), "s8": np.empty((B, H, R), np.float32),
-         "c4": np.empty((B, H, N, d), np.uint8), "e4": np.empty((B, H, N, d // 32), np.uint8)}
+    R = regions(F, Hv, Wv)
+    Np = R * BLK
+    o = {"c8": np.empty((B, H, Np, d), np.uint8), "s8": np.empty((B, H, R), np.float32),
+         "c4": np.empty((B, H, Np, d), np.uint8), "e4": np.empty((B, H, Np, d // 32), np.uint8)}
     lib().or_quant_qk(B, H, F, Hv, Wv, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
                       _p(o["e4"]))
     return o
 
 
 def quant_v(X, F, Hv, Wv):
-    """-> dict(c8 [B,H,N,d], s8 [B,H,d], c4 [B,H,N,d], e4 [B,H,R,2,d])."""
+    """-> dict(c8 [B,H,Np,d], s8 [B,H,d], c4 [B,H,Np,d], e4 [B,H,R,2,d])."""
     X = _u16(X)
     B, H, N, d = X.shape
-    R = N // BLK
-    o = {"c8": np.empty((B, H, N, d), np.uint8), "s8": np.empty((B, H, d), np.float32),
-         "c4": np.empty((B, H, N, d), np.uint8), "e4": np.empty((B, H, R, 2, d), np.uint8)}
+    R = regions(F, Hv, Wv)
+    Np = R * BLK
+    o = {"c8": np.empty((B, H, Np, d), np.uint8), "s8": np.empty((B, H, d), np.float32),
+         "c4": np.empty((B, H, Np, d), np.uint8), "e4": np.empty((B, H, R, 2, d), np.uint8)}
     lib().or_quant_v(B, H, F, Hv, Wv, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
                      _p(o["e4"]))
     return o
 
 
 # ---------------------------------------------------------------- attention
+def _restore(x, F, Hv, Wv):
+    """[B,H,R,64,d] rows in reordered position order -> [B,H,N,d] in original
+    token order (padding slots dropped)."""
+    B, H = x.shape[:2]
+    d = x.shape[-1]
+    perm = layout(F, Hv, Wv)
+    keep = perm >= 0
+    full = np.empty((B, H, F * Hv * Wv, d), np.float64)
+    full[:, :, perm[keep], :] = x.reshape(B, H, -1, d)[:, :, keep]
+    return full
+
+
 def attention(q, k, v, tier, F, Hv, Wv, qblocks=None):
     """Tiered attention.  qblocks=None: all rows, returned [B,H,N,d] in original
     token order.  Otherwise [B,H,len(qblocks),64,d]; row (j,i) is original
-    token perm[qblocks[j]*64+i]."""
+    token perm[qblocks[j]*64+i] (zero for a padding slot)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     tier = np.ascontiguousarray(tier, np.uint8)
     B, H, N, d = q.shape
-    R = N // BLK
+    R = regions(F, Hv, Wv)
     assert tier.shape == (B, H, R, R)
     if qblocks is None:
         out = np.empty((B, H, R, BLK, d), np.float64)
         lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), R, None, _p(out))
-        perm = layout(F, Hv, Wv)
-        full = np.empty((B, H, N, d), np.float64)
-        full[:, :, perm, :] = out.reshape(B, H, N, d)
-        return full
+        return _restore(out, F, Hv, Wv)
     qb = np.ascontiguousarray(qblocks, np.int32)
     out = np.empty((B, H, len(qb), BLK, d), np.float64)
     lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), len(qb), _p(qb),
@@ -298,7 +346,7 @@ def attention_kp(q, k, v, tier, F, Hv, Wv, qblocks=None):
     q, k, v = _u16(q), _u16(k), _u16(v)
     tier = np.ascontiguousarray(tier, np.uint8)
     B, H, N, d = q.shape
-    R = N // BLK
+    R = regions(F, Hv, Wv)
     assert tier.shape == (B, H, R, R)
     nq = R if qblocks is None else len(qblocks)
     qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
@@ -308,12 +356,7 @@ def attention_kp(q, k, v, tier, F, Hv, Wv, qblocks=None):
                           None if qb is None else _p(qb), _p(out), _p(allow))
     if qblocks is not None:
         return out, allow
-    perm = layout(F, Hv, Wv)
-    fo = np.empty((B, H, N, d), np.float64)
-    fa = np.empty((B, H, N, d), np.float64)
-    fo[:, :, perm, :] = out.reshape(B, H, N, d)
-    fa[:, :, perm, :] = allow.reshape(B, H, N, d)
-    return fo, fa
+    return _restore(out, F, Hv, Wv), _restore(allow, F, Hv, Wv)
 
 
 def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks):
@@ -322,22 +365,13 @@ def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks):
     B, H, N, d = q.shape
     Lp = qp.shape[2]
     assert qp.shape == kp.shape == vp.shape == (B, H, Lp, d)
-    R = N // BLK
+    R = tier.shape[2]
     assert tier.shape == (B, H, R, R)
     va = None if valid is None else np.ascontiguousarray(valid, np.int32)
     assert va is None or va.shape == (B,)
     qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
     nq = R if qb is None else len(qb)
     return q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R)
-
-
-def _restore(x, F, Hv, Wv):
-    B, H = x.shape[:2]
-    d = x.shape[-1]
-    N = F * Hv * Wv
-    full = np.empty((B, H, N, d), np.float64)
-    full[:, :, layout(F, Hv, Wv), :] = x.reshape(B, H, N, d)
-    return full
 
 
 def _prows(prefix_rows, Lp):

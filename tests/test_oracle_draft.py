@@ -39,9 +39,11 @@ def test_layout_restore_inverts_reorder(orc):
     assert np.array_equal(restored, X)
 
 
-def test_layout_rejects_ragged(orc):
+def test_layout_rejects_frames_without_partition(orc):
+    """A frame whose every candidate leaves a region under 48 tokens (here a
+    single region of 5 x 7 = 35 tokens) has no partition."""
     with pytest.raises(ValueError):
-        orc.layout(1, 12, 16)
+        orc.layout(1, 5, 7)
 
 
 # ------------------------------------------------------------------ pooling
