@@ -16,9 +16,14 @@
  *
  * Conventions
  *   - Tokens of one (batch, head) are N = frames*height*width latent
- *     positions in (frame, y, x) raster order; height and width are
- *     multiples of 8; regions are the 8x8 cells, R = N/64 of them, numbered
- *     frame-major then raster; inside a region tokens are in raster order.
+ *     positions in (frame, y, x) raster order.  Each frame is partitioned
+ *     into R_f = ceil(height*width/64) connected regions of 48..64 tokens
+ *     (Sec. 3.3 ragged 2D partition, App. C.2), the same for every frame;
+ *     R = frames*R_f regions, numbered frame-major.  When height and width
+ *     are multiples of 8 the regions are the 8x8 cells in raster order.
+ *     Inside a region its tokens take slots 0..n_a-1 in raster order, and
+ *     slots n_a..63 are padding (App. C.1: n_a excludes padding).
+ *     da2_layout_regions and da2_layout_slots describe the partition.
  *   - Q, K, V are bfloat16 device arrays addressed as
  *     base + b*stride_b + h*stride_h + n*stride_n + c (element units, the
  *     channel index c is contiguous).  head_dim is 64 or 128.  Base pointers
@@ -49,7 +54,7 @@ extern "C" {
 typedef enum {
     DA2_OK = 0,
     DA2_ERR_INVALID_ARG = 1,       /* null pointer, bad budget, bad dtype, misalignment */
-    DA2_ERR_UNSUPPORTED_SHAPE = 2, /* head_dim not 64/128, height/width not multiples of 8, too large */
+    DA2_ERR_UNSUPPORTED_SHAPE = 2, /* head_dim not 64/128, no partition of the frame, too large */
     DA2_ERR_WORKSPACE = 3,         /* workspace smaller than da2_workspace_bytes() */
     DA2_ERR_PLAN_MISMATCH = 4,     /* q/k pointers differ from the ones the plan was built on, or no plan */
     DA2_ERR_HIP = 5                /* a kernel launch failed */
@@ -80,6 +85,15 @@ typedef struct da2_plan_s da2_plan_t;
  * and reused across layers and denoising steps).  Host only, no GPU work. */
 da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out);
 void da2_layout_destroy(da2_layout_t *layout);
+
+/* Regions of the layout: returns R = frames*R_f (0 for NULL) and writes R_f
+ * to *regions_per_frame when it is not NULL.  Host only. */
+int32_t da2_layout_regions(const da2_layout_t *layout, int32_t *regions_per_frame);
+
+/* The partition of one frame (host destination, int32 [R_f*64]): for slot i
+ * of region r, the token y*width + x it holds, or -1 for a padding slot.
+ * Region r of frame f is region f*R_f + r of the tier map.  Host only. */
+da2_status da2_layout_slots(const da2_layout_t *layout, int32_t *dst);
 
 /* Bytes of device workspace a plan on this layout needs (256-byte aligned
  * base required).  Holds packed operands, draft state, tier map, schedule. */
@@ -151,10 +165,11 @@ da2_status da2_attention_prefixed(da2_plan_t *plan, const void *q, const void *k
                                   hipStream_t stream);
 
 /* Debug exports in canonical layouts, for tests (device destination):
- *   DA2_DBG_Q_FP8 / K_FP8 / V_FP8   : uint8 codes [B,H,N,d], token axis in region order
+ *   (Np = 64 R reordered positions, region by region, padding slots included)
+ *   DA2_DBG_Q_FP8 / K_FP8 / V_FP8   : uint8 codes [B,H,Np,d]
  *   DA2_DBG_Q_FP8_SCALE / K_...     : fp32 [B,H,R];  V: fp32 [B,H,d]
- *   DA2_DBG_Q_MX / K_MX / V_MX      : uint8 E2M1 codes [B,H,N,d] (one per byte)
- *   DA2_DBG_Q_MX_SCALE / K_...      : uint8 E8M0 [B,H,N,d/32];  V: [B,H,R,2,d]
+ *   DA2_DBG_Q_MX / K_MX / V_MX      : uint8 E2M1 codes [B,H,Np,d] (one per byte)
+ *   DA2_DBG_Q_MX_SCALE / K_...      : uint8 E8M0 [B,H,Np,d/32];  V: [B,H,R,2,d]
  *   DA2_DBG_Q_AVG / K_AVG           : fp64 [B,H,R,d];  Q_MAX / K_MAX: fp32 [B,H,R,d]
  *   DA2_DBG_KEYS                    : uint32 [B,H,R,R] (bits of fp32 draft score)
  *   DA2_DBG_SCHEDULE                : int32 [B,H,R,3+R]: n16, n8, n4, then the

@@ -36,8 +36,10 @@ def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None, prefix
 @pytest.mark.parametrize("kw,want", [
     (dict(), OK),
     (dict(d=96), SHAPE),
-    (dict(Hv=12), SHAPE),
-    (dict(Wv=20), SHAPE),
+    (dict(Hv=12), OK),            # ragged partition
+    (dict(Wv=20), OK),
+    (dict(F=1, Hv=5, Wv=7), SHAPE),   # 35 tokens: no region of >= 48
+    (dict(Hv=0), SHAPE),
     (dict(F=0), SHAPE),
     (dict(B=0), SHAPE),
     (dict(sn=60), INVALID),       # row stride below head_dim
@@ -150,3 +152,15 @@ def test_debug_sizes():
     assert L.da2_plan_debug_bytes(lay, da2.DBG["V_MX_SCALE"]) == B * H * R * 2 * d
     assert L.da2_plan_debug_bytes(lay, 1234) == 0
     L.da2_layout_destroy(lay)
+
+
+@pytest.mark.parametrize("Hv,Wv", [(16, 24), (48, 80), (84, 48), (60, 60), (12, 16), (34, 60), (45, 80),
+                                   (30, 44), (20, 28), (17, 31), (9, 100), (7, 7), (8, 6), (68, 120),
+                                   (90, 160), (33, 47)])
+def test_partition_agrees_with_oracle(orc, Hv, Wv):
+    """The library's partition (host C++) and the oracle's (plain C) are
+    separate implementations of the same rule: slot tables bit-exact."""
+    lay = da2.Layout(1, 1, 64, 3, Hv, Wv, 3 * Hv * Wv * 64, 3 * Hv * Wv * 64, 64)
+    tok, nv = orc.partition(Hv, Wv)
+    assert lay.Rf == tok.shape[0] and lay.R == 3 * tok.shape[0]
+    assert np.array_equal(lay.slots(), tok)

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libda2.so")
 
-SOURCES = ["k_prep.hip", "k_plan.hip", "k_attn.hip", "k_debug.hip", "da2_host.cpp"]
+SOURCES = ["k_prep.hip", "k_plan.hip", "k_attn.hip", "k_debug.hip", "da2_host.cpp", "da2_partition.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

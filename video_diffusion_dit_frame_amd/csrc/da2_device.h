@@ -28,6 +28,25 @@ __device__ __forceinline__ int region_token(int a, int i, int Ry, int Rx, int Hv
     return (f * Hv + ry * 8 + (i >> 3)) * Wv + rx * 8 + (i & 7);
 }
 
+// Region geometry of a layout: the 8x8 grid (ftok null), or a ragged
+// partition given by its frame slot table (token y*Wv + x of each slot of
+// the frame's Rf regions, -1 for a padding slot; valid slots first).
+struct Geo {
+    int Ry, Rx, Hv, Wv, Rf;
+    const int32_t *ftok;
+};
+
+// Original token index of slot i of region a, or -1 for a padding slot.
+template <bool RAG>
+__device__ __forceinline__ int slot_token(const Geo &g, int a, int i)
+{
+    if (!RAG)
+        return region_token(a, i, g.Ry, g.Rx, g.Hv, g.Wv);
+    const int f = a / g.Rf, r = a - f * g.Rf;
+    const int t = g.ftok[r * 64 + i];
+    return t < 0 ? -1 : f * g.Hv * g.Wv + t;
+}
+
 // Logical key (0..63) held in row i (0..31) of the key operand of MFMA half m.
 // The 32x32 accumulator puts row i at register 4*(i/8) + i%4 of lane half
 // (i/4)%2; this permutation makes lane half hf own keys 32*hf .. 32*hf+31,
@@ -142,4 +161,10 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
     return v;
 }
 
+}  // namespace da2
+
+struct da2_layout_s;
+namespace da2 {
+// The region geometry of a layout whose workspace starts at ws.
+Geo layout_geo(const ::da2_layout_s &L, const char *ws);
 }  // namespace da2

@@ -20,14 +20,14 @@ da2_status check_shape(const da2_shape *s)
 {
     if (!s)
         return DA2_ERR_INVALID_ARG;
-    if (s->batch < 1 || s->heads < 1 || s->frames < 1 || s->height < 8 || s->width < 8)
+    if (s->batch < 1 || s->heads < 1 || s->frames < 1 || s->height < 1 || s->width < 1)
         return DA2_ERR_UNSUPPORTED_SHAPE;
     if (s->head_dim != 64 && s->head_dim != 128)
         return DA2_ERR_UNSUPPORTED_SHAPE;
-    if (s->height % 8 || s->width % 8)
+    if ((int64_t)s->height * s->width > 4096 * kBlk)
         return DA2_ERR_UNSUPPORTED_SHAPE;
-    int64_t N = (int64_t)s->frames * s->height * s->width;
-    if (N / kBlk > kMaxRegions || (int64_t)s->batch * s->heads > 65535)
+    const int64_t Rf = ((int64_t)s->height * s->width + kBlk - 1) / kBlk;
+    if ((int64_t)s->frames * Rf > kMaxRegions || (int64_t)s->batch * s->heads > 65535)
         return DA2_ERR_UNSUPPORTED_SHAPE;
     if (s->stride_n < s->head_dim || s->stride_b < 0 || s->stride_h < 0)
         return DA2_ERR_INVALID_ARG;
@@ -47,7 +47,8 @@ da2_status check_shape(const da2_shape *s)
 
 void carve(da2_layout_s &L)
 {
-    const size_t BH = L.BH, N = L.N, R = L.R, d = L.d;
+    // operand arrays hold every reordered position (padding slots included)
+    const size_t BH = L.BH, N = L.Np, R = L.R, d = L.d;
     Workspace &W = L.ws;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -71,6 +72,9 @@ void carve(da2_layout_s &L)
     W.vp16 = take(BH * (size_t)L.ptiles * kBlk * d * 2);
     W.pacc = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * d * 4);
     W.pmz = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * 8);
+    W.k16 = take(L.ragged ? BH * N * d * 2 : 0);
+    W.ftok = take(L.ragged ? (size_t)L.Rf * kBlk * 4 : 0);
+    W.nreg = take(L.ragged ? R * 4 : 0);
     W.vamax = take(BH * d * 4);
     W.qavg = take(BH * R * d * 8);
     W.kavg = take(BH * R * d * 8);
@@ -93,6 +97,35 @@ void carve(da2_layout_s &L)
 da2_status launched()
 {
     return hipGetLastError() == hipSuccess ? DA2_OK : DA2_ERR_HIP;
+}
+
+// Ragged layouts: the frame slot table and the valid-token count of every
+// region go to the workspace once per plan (the plan keeps the host copies
+// alive, so the asynchronous copies may complete later).
+da2_status upload_tables(da2_plan_s *P, hipStream_t stream)
+{
+    const da2_layout_s &L = P->L;
+    if (!L.ragged || P->tables_ready)
+        return DA2_OK;
+    if (!P->nreg) {
+        P->nreg = (int32_t *)malloc(sizeof(int32_t) * L.R);
+        if (!P->nreg)
+            return DA2_ERR_INVALID_ARG;
+        for (int a = 0; a < L.R; a++) {
+            const int32_t *t = L.ftok + (a % L.Rf) * kBlk;
+            int n = 0;
+            while (n < kBlk && t[n] >= 0)
+                n++;
+            P->nreg[a] = n;
+        }
+    }
+    if (hipMemcpyAsync(P->ws + L.ws.ftok, L.ftok, sizeof(int32_t) * L.Rf * kBlk, hipMemcpyHostToDevice,
+                       stream) != hipSuccess ||
+        hipMemcpyAsync(P->ws + L.ws.nreg, P->nreg, sizeof(int32_t) * L.R, hipMemcpyHostToDevice, stream) !=
+            hipSuccess)
+        return DA2_ERR_HIP;
+    P->tables_ready = 1;
+    return DA2_OK;
 }
 
 }  // namespace
@@ -124,9 +157,30 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
         return DA2_ERR_INVALID_ARG;
     L->s = *shape;
     L->N = shape->frames * shape->height * shape->width;
-    L->R = L->N / kBlk;
     L->Ry = shape->height / 8;
     L->Rx = shape->width / 8;
+    if (shape->height % 8 == 0 && shape->width % 8 == 0) {
+        // the 8x8 grid: slots follow from a closed form
+        L->Rf = L->Ry * L->Rx;
+    } else {
+        const int Rf = (shape->height * shape->width + kBlk - 1) / kBlk;
+        L->ftok = (int32_t *)malloc(sizeof(int32_t) * Rf * kBlk);
+        if (!L->ftok || partition_frame(shape->height, shape->width, L->ftok) != Rf) {
+            free(L->ftok);
+            free(L);
+            return DA2_ERR_UNSUPPORTED_SHAPE;
+        }
+        L->Rf = Rf;
+        L->ragged = 1;
+        for (int r = 0; r < Rf; r++) {
+            int n = 0;
+            while (n < kBlk && L->ftok[r * kBlk + n] >= 0)
+                n++;
+            L->pmax = L->pmax > kBlk - n ? L->pmax : kBlk - n;
+        }
+    }
+    L->R = shape->frames * L->Rf;
+    L->Np = L->R * kBlk;
     L->BH = shape->batch * shape->heads;
     L->d = shape->head_dim;
     L->nchunk = ((int64_t)L->R * L->R + 4095) / 4096;
@@ -137,9 +191,38 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
     return DA2_OK;
 }
 
-void da2_layout_destroy(da2_layout_t *layout) { free(layout); }
+void da2_layout_destroy(da2_layout_t *layout)
+{
+    if (layout)
+        free(layout->ftok);
+    free(layout);
+}
 
 size_t da2_workspace_bytes(const da2_layout_t *layout) { return layout ? layout->ws.total : 0; }
+
+int32_t da2_layout_regions(const da2_layout_t *layout, int32_t *regions_per_frame)
+{
+    if (!layout)
+        return 0;
+    if (regions_per_frame)
+        *regions_per_frame = layout->Rf;
+    return layout->R;
+}
+
+da2_status da2_layout_slots(const da2_layout_t *layout, int32_t *dst)
+{
+    if (!layout || !dst)
+        return DA2_ERR_INVALID_ARG;
+    const da2_layout_s &L = *layout;
+    if (L.ragged) {
+        memcpy(dst, L.ftok, sizeof(int32_t) * L.Rf * kBlk);
+        return DA2_OK;
+    }
+    for (int r = 0; r < L.Rf; r++)
+        for (int i = 0; i < kBlk; i++)
+            dst[r * kBlk + i] = ((r / L.Rx) * 8 + i / 8) * L.s.width + (r % L.Rx) * 8 + i % 8;
+    return DA2_OK;
+}
 
 da2_status da2_plan_create(const da2_layout_t *layout, void *workspace, size_t workspace_bytes,
                            da2_plan_t **out)
@@ -152,6 +235,15 @@ da2_status da2_plan_create(const da2_layout_t *layout, void *workspace, size_t w
     if (!P)
         return DA2_ERR_INVALID_ARG;
     P->L = *layout;
+    if (layout->ragged) {
+        const size_t bytes = sizeof(int32_t) * layout->Rf * kBlk;
+        P->L.ftok = (int32_t *)malloc(bytes);
+        if (!P->L.ftok) {
+            free(P);
+            return DA2_ERR_INVALID_ARG;
+        }
+        memcpy(P->L.ftok, layout->ftok, bytes);
+    }
     P->ws = (char *)workspace;
     P->ws_bytes = workspace_bytes;
     *out = P;
@@ -176,6 +268,8 @@ void da2_plan_destroy(da2_plan_t *plan)
     if (!plan)
         return;
     drop_events(plan);
+    free(plan->L.ftok);
+    free(plan->nreg);
     free(plan);
 }
 
@@ -234,6 +328,9 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
     int64_t t16, t8, tk;
     da2_quotas(n, bud->full_bp, bud->hi_bp, bud->lo_bp, &t16, &t8, &tk);
     P->ready = 0;
+    da2_status up = upload_tables(P, stream);
+    if (up != DA2_OK)
+        return up;
     launch_prep_qk(L, q, 0, P->ws, stream);
     launch_prep_qk(L, k, 1, P->ws, stream);
     launch_draft(L, bud->lambda, P->ws, stream);
@@ -259,6 +356,9 @@ da2_status da2_plan_from_tier_map(da2_plan_t *P, const void *q, const void *k,
         return DA2_ERR_INVALID_ARG;
     const da2_layout_s &L = P->L;
     P->ready = 0;
+    da2_status up = upload_tables(P, stream);
+    if (up != DA2_OK)
+        return up;
     launch_prep_qk(L, q, 0, P->ws, stream);
     launch_prep_qk(L, k, 1, P->ws, stream);
     launch_import_tier(L, tier_map, P->ws, stream);
@@ -344,7 +444,7 @@ size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which)
 {
     if (!layout)
         return 0;
-    const size_t BH = layout->BH, N = layout->N, R = layout->R, d = layout->d;
+    const size_t BH = layout->BH, N = layout->Np, R = layout->R, d = layout->d;
     switch (which) {
     case DA2_DBG_Q_FP8: case DA2_DBG_K_FP8: case DA2_DBG_V_FP8:
     case DA2_DBG_Q_MX: case DA2_DBG_K_MX: case DA2_DBG_V_MX:

@@ -15,6 +15,7 @@ constexpr int kMaxTimed = 4096;   // attention calls recorded while timing
 constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
 constexpr int kPrefixChunkTiles = 128; // tiles per chunk of a prefix query row
 constexpr int kMaxPrefix = 4096;  // text-prefix tokens per sequence
+constexpr int kMinFill = 48;      // fewest valid tokens of a region (at most 16 padding slots)
 
 // ---------------------------------------------------------------------------
 // Workspace: one region of caller memory carved into these buffers.
@@ -29,6 +30,12 @@ constexpr int kMaxPrefix = 4096;  // text-prefix tokens per sequence
 //   prefix V bf16 : [bh][tile][cb][t][lane][16 B]   the same for the text
 //            prefix, tile t holding prefix keys 64t .. 64t+63 (zero past the
 //            valid ones)
+//   K bf16 (ragged layouts) : [bh][a][m=2][s=d/16][lane][16 B]   the key
+//            image of the 16-bit products: chunk (m, s) holds for lane l key
+//            slot key_of_row(l%32, m), channels 16s + 8(l/32) .. +7
+//   frame slot table (ragged layouts) : int32 [R_f][64], token y*W_v + x of
+//            each slot of the frame's regions, -1 for padding; int32 [R]
+//            valid tokens of every region
 //   prefix partials : fp32 [bh][chunk][row][d] unnormalised outputs and
 //            float2 [bh][chunk][row] (running max, sum) of the prefix query
 //            rows' chunks, rows padded to ptiles*64
@@ -37,6 +44,8 @@ struct Workspace {
     size_t q8, q4, q4s, qs8;
     size_t k8, k4, k4s, ks8;
     size_t v8, v4, v4s, vs8, vamax, v16, vp16, pacc, pmz;
+    size_t k16;          // bf16 key image of ragged layouts (16-bit path)
+    size_t ftok, nreg;   // ragged layouts: frame slot table, valid tokens per region
     size_t qavg, kavg, qmax, kmax;
     size_t la, lm, rmax, zsum, keys, tier;
     size_t sched, cnt;
@@ -56,6 +65,11 @@ struct RankState {      // one per (segment, target)
 struct da2_layout_s {
     da2_shape s;
     int N, R, Ry, Rx, BH, d;
+    int Np;                   // reordered positions R*64 (padding slots included)
+    int Rf;                   // regions per frame
+    int ragged;               // 0: the 8x8 grid (closed form); 1: slot table
+    int pmax;                 // most padding slots of any region (0..16)
+    int32_t *ftok;            // ragged: frame slot table [Rf*64] (host, owned)
     int64_t nchunk;           // rank chunks per head (head scope)
     int ptiles;               // 64-key tiles of the text prefix (ceil(prefix / 64))
     int pchunks;              // chunks of a prefix query row's key sequence (0: no prefix)
@@ -63,7 +77,9 @@ struct da2_layout_s {
 };
 
 struct da2_plan_s {
-    da2_layout_s L;
+    da2_layout_s L;           // its ftok is the plan's own copy
+    int tables_ready;         // frame slot table uploaded to the workspace
+    int32_t *nreg;            // ragged: valid tokens of every region [R] (host)
     char *ws;
     size_t ws_bytes;
     const void *q, *k;        // inputs the plan was built on
@@ -88,6 +104,9 @@ struct PrefixIo {
 // Launchers (defined in the kernel translation units).
 // ---------------------------------------------------------------------------
 void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, hipStream_t st);
+// Spatial partition of one Hv x Wv frame (defined in da2_partition.cpp):
+// fills tok [Rf*64] (y*Wv + x or -1) and returns Rf, or -1 without one.
+int partition_frame(int Hv, int Wv, int32_t *tok);
 void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, hipStream_t st);
 void launch_prep_vp(const da2_layout_s &L, const PrefixIo &px, char *ws, hipStream_t st);
 void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st);

@@ -60,6 +60,11 @@ struct AttnArgs {
     float *pacc;
     float2 *pmz;
     int pchunks;
+    // region geometry; ragged layouts also give each region's valid tokens
+    // and the bf16 key image of the 16-bit products
+    Geo geo;
+    const int32_t *nreg;
+    const uint8_t *k16;
     const int32_t *sched;
     const int32_t *cnt;
     void *out;
@@ -463,41 +468,61 @@ __device__ __forceinline__ uint8_t *chunk16(uint8_t *b0, uint8_t *b1, int c)
 // written by the V preparation, one 64 x D image per tile).
 //
 // Video regions of one head: the schedule's 16-bit list, or (DENSE) the
-// regions first, first + 1, ... in order.
-template <int D, bool DENSE>
+// regions first, first + 1, ... in order.  On the 8x8 grid the key rows are
+// gathered straight from K (a fixed byte offset per lane from the region's
+// first token); a ragged layout copies the bf16 key image its K preparation
+// wrote and masks the region's padding slots.
+template <int D, bool DENSE, bool RAG>
 struct VideoKeys16 {
-    static constexpr bool kMasked = false;
+    static constexpr bool kMasked = RAG;
     const int32_t *list;
     int first;
     const uint16_t *kh;            // K of this head
     const uint8_t *vbase;          // value images of the head's regions
     int64_t vbytes;
-    uint32_t koff;                 // this lane's byte offset from a region's first token
-    int kspan, Ry, Rx, Hv, Wv;
+    const uint8_t *kimg;           // ragged: key images of the head's regions
+    const int32_t *nreg;           // ragged: valid tokens per region
+    uint32_t koff;                 // grid: this lane's byte offset from a region's first token;
+                                   // ragged: this lane's byte offset in a key-image chunk
+    int kspan, Ry, Rx, Hv, Wv, w;
     int64_t osn;
 
     __device__ __forceinline__ VideoKeys16(const AttnArgs &A, const int32_t *list_, int first_, int64_t hoff,
-                                           int64_t hbase, int w, int l)
-        : list(list_), first(first_), kh(A.k + hoff), kspan(A.kspan), Ry(A.Ry), Rx(A.Rx), Hv(A.Hv), Wv(A.Wv),
-          osn(A.osn)
+                                           int64_t hbase, int w_, int l)
+        : list(list_), first(first_), kh(A.k + hoff), nreg(A.nreg), kspan(A.kspan), Ry(A.Ry), Rx(A.Rx),
+          Hv(A.Hv), Wv(A.Wv), w(w_), osn(A.osn)
     {
-        // wave w gathers the key rows of half m = w: a fixed byte offset from
-        // the key region's first token for every tile
-        const int kpos = key_of_row(l & 31, w);
-        koff = (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * (l >> 5)) * 2);
+        if (RAG) {
+            koff = (uint32_t)l * 16u;
+        } else {
+            // wave w gathers the key rows of half m = w
+            const int kpos = key_of_row(l & 31, w_);
+            koff = (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * (l >> 5)) * 2);
+        }
         vbase = A.v16 + hbase * (kBlk * D * 2);
         vbytes = (int64_t)A.R * kBlk * D * 2;
+        kimg = A.k16 + hbase * (kBlk * D * 2);
     }
     __device__ __forceinline__ int id(int i) const { return DENSE ? first + i : sload_i32(list + i); }
-    __device__ __forceinline__ int valid(int) const { return kBlk; }
+    __device__ __forceinline__ int valid(int kb) const { return RAG ? sload_i32(nreg + kb) : kBlk; }
     __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
     {
-        const int t0 = region_token(kb, 0, Ry, Rx, Hv, Wv);
-        const __amdgpu_buffer_rsrc_t ksrc = head_rsrc((const uint8_t *)(kh + (int64_t)t0 * osn), kspan);
+        if (RAG) {
+            // chunks (w, s) of the region's key image: 1 KB each
+            const __amdgpu_buffer_rsrc_t ksrc = head_rsrc(kimg, vbytes);
 #pragma unroll
-        for (int s = 0; s < D / 16; s++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, koff, 32 * s, 0,
-                                                     0);
+            for (int s = 0; s < D / 16; s++)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, koff,
+                                                         (uint32_t)kb * (kBlk * D * 2) + (w * (D / 16) + s) * 1024,
+                                                         0, 0);
+        } else {
+            const int t0 = region_token(kb, 0, Ry, Rx, Hv, Wv);
+            const __amdgpu_buffer_rsrc_t ksrc = head_rsrc((const uint8_t *)(kh + (int64_t)t0 * osn), kspan);
+#pragma unroll
+            for (int s = 0; s < D / 16; s++)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, koff, 32 * s,
+                                                         0, 0);
+        }
     }
 };
 
@@ -700,9 +725,24 @@ __device__ __forceinline__ void region_pattern()
     }
 }
 
+// Padding slots of a ragged key region take no part: slots n .. 63 (at most
+// PMAX of them, n >= 48) are registers n - 48 .. 15 of logit half 1 on the
+// lanes of half 1 (slot 32 hf + 16 m + r is register r of half m).
+template <int PMAX>
+__device__ __forceinline__ void mask_padding(v16f &s1, int n, int hf)
+{
+    const bool upper = hf != 0;
+#pragma unroll
+    for (int r = 16 - PMAX; r < 16; r++) {
+        const bool pad = upper & (48 + r >= n);
+        s1[r] = pad ? -__builtin_huge_valf() : s1[r];
+    }
+}
+
 // One attention workgroup's state: two waves, one query region (wave w owns
-// queries 32 w .. 32 w + 31).
-template <int D>
+// queries 32 w .. 32 w + 31).  RAG: ragged layout (slot tables); PMAX: most
+// padding slots of a key region (0, 4 or 16).
+template <int D, bool RAG, int PMAX>
 struct Attn {
     static constexpr int KC = D / 64;   // 64-channel steps of QK^T
     static constexpr int CB = D / 32;   // 32-channel blocks of the output
@@ -728,6 +768,7 @@ struct Attn {
     int E0, E1;
     float al;           // factor acc owes before the next P^T V (running-max change)
     int kr0, kr1, kr2;  // key regions of tiles i, i+1, i+2 (wave-uniform)
+    int nk0;            // valid tokens of tile i's key region (PMAX > 0)
     float c8;           // FP8 logit scale of tile i
 
     __device__ __forceinline__ void vunits(bool to_fp8)
@@ -790,7 +831,7 @@ struct Attn {
     // vr, each half just before its products.  The last step computes logits
     // of a stale key image, which are never used (kinds KN = KCUR there).
     template <bool KP, bool KCUR, bool KN, bool UNIT>
-    __device__ __forceinline__ void step(int i, const v16f (&sc)[2], v16f (&sn)[2], const v8i &pp, int ep,
+    __device__ __forceinline__ void step(int i, v16f (&sc)[2], v16f (&sn)[2], const v8i &pp, int ep,
                                          v8i &pc, int &ec, const uint8_t *__restrict__ kr,
                                          uint8_t *__restrict__ kw, const uint8_t *__restrict__ vr,
                                          uint8_t *__restrict__ vw)
@@ -819,6 +860,8 @@ struct Attn {
         //       and 2/4 consumed);        read K half 1;          weights 3/4
         //   R4: logits half 1;                                    weights 4/4
         float c, bias, pscale = 0.0f;
+        if (PMAX > 0)
+            mask_padding<PMAX>(sc[1], nk0, hf);
         if (KCUR) {
             c = c8;
             bias = new_max(pair_max(lane_max(sc)), c, m, z, al);
@@ -889,6 +932,8 @@ struct Attn {
         kr1 = kr2;
         kr2 = sload_i32(list + min(i + 3, n - 1));
         c8 = (qs * sload_f32(A.ks8 + hbase + kr0)) * A.c4;
+        if (PMAX > 0)
+            nk0 = sload_i32(A.nreg + kr0);
     }
 
     // Step i with the register sets and buffers of an even or an odd step.
@@ -968,6 +1013,8 @@ struct Attn {
                 issue_k<D, false>(src, kr1, k1, w, l);
         }
         c8 = n8 > 0 ? (qs * sload_f32(A.ks8 + hbase + kr0)) * A.c4 : 0.0f;
+        if (PMAX > 0)
+            nk0 = sload_i32(A.nreg + kr0);
         // step 0 multiplies P = 0 into the value buffer of the other parity:
         // clear it so that no stale code can make a NaN
         uint8_t *vz = off ? vb0 : vb1;
@@ -1064,13 +1111,15 @@ struct Attn {
         const int bb = bh / A.H, hh = bh - bb * A.H;
         const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
         v4u q16[D / 16];
-        const int qt = region_token(a, 32 * w + (l & 31), A.Ry, A.Rx, A.Hv, A.Wv);
+        int qt = slot_token<RAG>(A.geo, a, 32 * w + (l & 31));
+        if (qt < 0)   // padding slot: any valid row (its output is not written)
+            qt = slot_token<RAG>(A.geo, a, 0);
         load_q16<D>(A.q + hoff + (int64_t)qt * A.osn, l, q16);
         if (np > 0)
             run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, 0, hoff, bh, nv, w, l), np, q16, w, l, acc, m, z);
         if (n16 > 0)
-            run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, false>(A, list16, 0, hoff, hbase, w, l), n16, q16, w,
-                     l, acc, m, z);
+            run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, false, RAG>(A, list16, 0, hoff, hbase, w, l), n16, q16,
+                     w, l, acc, m, z);
     }
 
     // O = acc / Z for this wave's 32 queries of region a, written straight to
@@ -1080,10 +1129,11 @@ struct Attn {
         const float zt = pair_sum(z);
         const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
         const int qi = 32 * w + (l & 31);
-        const int tok = region_token(a, qi, A.Ry, A.Rx, A.Hv, A.Wv);
+        const int tok = slot_token<RAG>(A.geo, a, qi);
         const int b = bh / A.H, h = bh - b * A.H;
         const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)tok * A.osn;
-        store_row<D>(A, A.out, obase, acc, inv, hf);
+        if (tok >= 0)
+            store_row<D>(A, A.out, obase, acc, inv, hf);
     }
 
     __device__ __forceinline__ void init(int w_, int bh_, int64_t qblk_)
@@ -1106,7 +1156,7 @@ struct Attn {
 
 // One query region per workgroup: 16-bit phase (if any), then the FP8 and
 // MXFP4 phases.
-template <int D>
+template <int D, bool RAG, int PMAX>
 __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t kb0[kBlk * D];
@@ -1130,12 +1180,12 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     const int j = xcd * span + (kk - bh * span);
     if (j >= R)
         return;
-    const int RF = A.Ry * A.Rx, NF = R / RF;
+    const int RF = A.geo.Rf, NF = R / RF;
     const int a = (j % NF) * RF + j / NF;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t qblk = (int64_t)bh * R + a;
 
-    Attn<D> S{A, kb0, kb1, vb0, vb1};
+    Attn<D, RAG, PMAX> S{A, kb0, kb1, vb0, vb1};
     S.init(w, bh, qblk);
     const int n16 = sload_i32(A.cnt + qblk * kTargets);
     const int n8 = sload_i32(A.cnt + qblk * kTargets + 1);
@@ -1161,7 +1211,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 // leaves the chunk's state (running max m, sum Z, unnormalised output) for
 // the merge.  Rows past Lp (the last workgroup's tail) compute on a copy of
 // row Lp - 1 and are not written.
-template <int D>
+template <int D, bool RAG>
 __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
                                             uint8_t *vb1, int pb, int bh, int c, int w, int l)
 {
@@ -1183,7 +1233,7 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
                  l, acc, m, z);
     const int r0 = max(t0, np) - np, r1 = t1 - np;
     if (r1 > r0)
-        run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, true>(A, nullptr, r0, hoff, (int64_t)bh * A.R, w, l),
+        run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, true, RAG>(A, nullptr, r0, hoff, (int64_t)bh * A.R, w, l),
                  r1 - r0, q16, w, l, acc, m, z);
     const float zt = pair_sum(z);
     if (row < A.Lp) {
@@ -1201,7 +1251,7 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
     }
 }
 
-template <int D>
+template <int D, bool RAG>
 __global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t kb0[kBlk * D];
@@ -1209,8 +1259,8 @@ __global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
     __shared__ __attribute__((aligned(1024))) uint8_t vb0[kBlk * D];
     __shared__ __attribute__((aligned(1024))) uint8_t vb1[kBlk * D];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    prefix_rows<D>(A, kb0, kb1, vb0, vb1, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z, w,
-                   (int)(threadIdx.x & 63));
+    prefix_rows<D, RAG>(A, kb0, kb1, vb0, vb1, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z, w,
+                        (int)(threadIdx.x & 63));
 }
 
 // Merge of a prefix row's chunks (App. B.4's shared normalization across
@@ -1304,18 +1354,42 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
     A.pacc = (float *)(ws + W.pacc);
     A.pmz = (float2 *)(ws + W.pmz);
     A.pchunks = L.pchunks;
+    A.geo = layout_geo(L, ws);
+    A.nreg = (const int32_t *)(ws + W.nreg);
+    A.k16 = (const uint8_t *)(ws + W.k16);
     dim3 grid(8 * ((L.R + 7) / 8) * L.BH);
+    // kernel variant: the 8x8 grid, or a ragged layout whose key regions
+    // have no padding, at most 4 or at most 16 padding slots
+    const int pm = !L.ragged ? -1 : (L.pmax == 0 ? 0 : (L.pmax <= 4 ? 4 : 16));
+#define DA2_ATTN(DD)                                                    \
+    do {                                                                \
+        if (pm < 0)                                                     \
+            k_attn<DD, false, 0><<<grid, 128, 0, st>>>(A);              \
+        else if (pm == 0)                                               \
+            k_attn<DD, true, 0><<<grid, 128, 0, st>>>(A);               \
+        else if (pm == 4)                                               \
+            k_attn<DD, true, 4><<<grid, 128, 0, st>>>(A);               \
+        else                                                            \
+            k_attn<DD, true, 16><<<grid, 128, 0, st>>>(A);              \
+    } while (0)
     if (L.d == 128)
-        k_attn<128><<<grid, 128, 0, st>>>(A);
+        DA2_ATTN(128);
     else
-        k_attn<64><<<grid, 128, 0, st>>>(A);
+        DA2_ATTN(64);
+#undef DA2_ATTN
     if (A.Lp > 0) {
         dim3 pgrid((A.Lp + kBlk - 1) / kBlk, L.BH, L.pchunks);
         if (L.d == 128) {
-            k_attn_prefix<128><<<pgrid, 128, 0, st>>>(A);
+            if (L.ragged)
+                k_attn_prefix<128, true><<<pgrid, 128, 0, st>>>(A);
+            else
+                k_attn_prefix<128, false><<<pgrid, 128, 0, st>>>(A);
             k_prefix_merge<128><<<dim3((A.Lp + 7) / 8, L.BH), 256, 0, st>>>(A);
         } else {
-            k_attn_prefix<64><<<pgrid, 128, 0, st>>>(A);
+            if (L.ragged)
+                k_attn_prefix<64, true><<<pgrid, 128, 0, st>>>(A);
+            else
+                k_attn_prefix<64, false><<<pgrid, 128, 0, st>>>(A);
             k_prefix_merge<64><<<dim3((A.Lp + 15) / 16, L.BH), 256, 0, st>>>(A);
         }
     }

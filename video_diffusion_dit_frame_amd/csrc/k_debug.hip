@@ -110,7 +110,7 @@ void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, h
 {
     const Workspace &W = L.ws;
     const int d = L.d;
-    const int64_t nd = (int64_t)L.BH * L.N * d;
+    const int64_t nd = (int64_t)L.BH * L.Np * d;
     auto grid = [](int64_t n) { return (unsigned)((n + 255) / 256); };
     uint8_t *o = (uint8_t *)dst;
     switch (which) {

@@ -21,28 +21,31 @@
 namespace da2 {
 namespace {
 
-// Copy the 64 x D bf16 tile of region a into LDS (row i = region position i).
-template <int D>
+// Copy the 64 x D bf16 tile of region a into LDS (row i = slot i; padding
+// slots of a ragged layout are zero rows).
+template <int D, bool RAG>
 __device__ __forceinline__ void load_region(const uint16_t *__restrict__ x, int64_t sn, int a,
-                                            int Ry, int Rx, int Hv, int Wv, uint16_t *tile)
+                                            const Geo &g, uint16_t *tile)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per token row
     for (int ci = threadIdx.x; ci < kBlk * CH; ci += 256) {
         int i = ci / CH, c8 = ci - i * CH;
-        int n = region_token(a, i, Ry, Rx, Hv, Wv);
-        uint4 v = *reinterpret_cast<const uint4 *>(x + (int64_t)n * sn + c8 * 8);
+        int n = slot_token<RAG>(g, a, i);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (n >= 0)
+            v = *reinterpret_cast<const uint4 *>(x + (int64_t)n * sn + c8 * 8);
         *reinterpret_cast<uint4 *>(tile + i * D + c8 * 8) = v;
     }
 }
 
-template <int D>
+template <int D, bool RAG>
 __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x, int64_t sb,
-                                                 int64_t sh, int64_t sn, int H, int R, int Ry,
-                                                 int Rx, int Hv, int Wv, int is_key,
-                                                 uint8_t *__restrict__ op8, float *__restrict__ s8,
-                                                 uint8_t *__restrict__ op4,
+                                                 int64_t sh, int64_t sn, int H, int R, Geo g,
+                                                 int is_key, uint8_t *__restrict__ op8,
+                                                 float *__restrict__ s8, uint8_t *__restrict__ op4,
                                                  uint8_t *__restrict__ op4s,
-                                                 double *__restrict__ avg, float *__restrict__ mx)
+                                                 double *__restrict__ avg, float *__restrict__ mx,
+                                                 uint16_t *__restrict__ op16)
 {
     constexpr int KC = D / 64;
     __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk * D];
@@ -50,23 +53,38 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
     const int a = blockIdx.x, bh = blockIdx.y;
     const int b = bh / H, h = bh - b * H;
     const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
-    load_region<D>(xb, sn, a, Ry, Rx, Hv, Wv, tile);
+    load_region<D, RAG>(xb, sn, a, g, tile);
+    // valid tokens of the region (App. C.1: n_a excludes padding); they fill
+    // the first slots
+    const int na = RAG ? __syncthreads_count(threadIdx.x < kBlk && slot_token<RAG>(g, a, threadIdx.x) >= 0)
+                       : kBlk;
     __syncthreads();
 
     const int t = threadIdx.x;
     const int64_t blk = (int64_t)bh * R + a;
-    // pooled descriptors: channel t, tokens in region order
+    // pooled descriptors: channel t, valid tokens in slot order
     if (t < D) {
         double s = 0.0;
         float m = bf16_to_f32(tile[t]);
-        for (int i = 0; i < kBlk; i++) {
+        for (int i = 0; i < na; i++) {
             float v = bf16_to_f32(tile[i * D + t]);
             s += (double)v;
             if (v > m)
                 m = v;
         }
-        avg[blk * D + t] = s / (double)kBlk;
+        avg[blk * D + t] = s / (double)na;
         mx[blk * D + t] = m;
+    }
+    // ragged layouts: the bf16 key image of the 16-bit products, chunk
+    // (m, s) holding for lane l slot key_of_row(l % 32, m), channels
+    // 16 s + 8 (l / 32) .. + 7
+    if (RAG && is_key) {
+        for (int u = t; u < 2 * (D / 16) * 64; u += 256) {
+            const int ms = u >> 6, l = u & 63, m = ms / (D / 16), st = ms - m * (D / 16);
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + key_of_row(l & 31, m) * D + 16 * st +
+                                                             8 * (l >> 5));
+            *reinterpret_cast<uint4 *>(op16 + blk * (kBlk * D) + (int64_t)u * 8) = v;
+        }
     }
     // FP8 block scale
     float am = 0.0f;
@@ -156,10 +174,9 @@ __global__ __launch_bounds__(256) void k_vamax(const uint16_t *__restrict__ x, i
     }
 }
 
-template <int D>
+template <int D, bool RAG>
 __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, int64_t sb,
-                                                int64_t sh, int64_t sn, int H, int R, int Ry,
-                                                int Rx, int Hv, int Wv,
+                                                int64_t sh, int64_t sn, int H, int R, Geo g,
                                                 const uint32_t *__restrict__ vamax,
                                                 uint8_t *__restrict__ op8, float *__restrict__ s8,
                                                 uint8_t *__restrict__ op4,
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
     const int a = blockIdx.x, bh = blockIdx.y;
     const int b = bh / H, h = bh - b * H;
     const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
-    load_region<D>(xb, sn, a, Ry, Rx, Hv, Wv, tile);
+    load_region<D, RAG>(xb, sn, a, g, tile);
     __syncthreads();
     const int t = threadIdx.x;
     const int64_t blk = (int64_t)bh * R + a;
@@ -268,6 +285,18 @@ __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v)
 
 }  // namespace
 
+Geo layout_geo(const da2_layout_s &L, const char *ws)
+{
+    Geo g;
+    g.Ry = L.Ry;
+    g.Rx = L.Rx;
+    g.Hv = L.s.height;
+    g.Wv = L.s.width;
+    g.Rf = L.Rf;
+    g.ftok = L.ragged ? (const int32_t *)(ws + L.ws.ftok) : nullptr;
+    return g;
+}
+
 void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
@@ -279,15 +308,24 @@ void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, 
     uint8_t *op4s = (uint8_t *)(ws + (is_key ? W.k4s : W.q4s));
     double *avg = (double *)(ws + (is_key ? W.kavg : W.qavg));
     float *mx = (float *)(ws + (is_key ? W.kmax : W.qmax));
+    uint16_t *op16 = (uint16_t *)(ws + W.k16);
     const da2_shape &s = L.s;
-    if (L.d == 128)
-        k_prep_qk<128><<<grid, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
-                                             L.Ry, L.Rx, s.height, s.width, is_key, op8, s8, op4,
-                                             op4s, avg, mx);
-    else
-        k_prep_qk<64><<<grid, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
-                                            L.Ry, L.Rx, s.height, s.width, is_key, op8, s8, op4,
-                                            op4s, avg, mx);
+    const Geo g = layout_geo(L, ws);
+#define DA2_PREP_QK(DD, RG)                                                                           \
+    k_prep_qk<DD, RG><<<grid, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R, g, is_key, \
+                                            op8, s8, op4, op4s, avg, mx, op16)
+    if (L.d == 128) {
+        if (L.ragged)
+            DA2_PREP_QK(128, true);
+        else
+            DA2_PREP_QK(128, false);
+    } else {
+        if (L.ragged)
+            DA2_PREP_QK(64, true);
+        else
+            DA2_PREP_QK(64, false);
+    }
+#undef DA2_PREP_QK
 }
 
 void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, hipStream_t st)
@@ -303,17 +341,24 @@ void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, h
             *op4s = (uint8_t *)(ws + W.v4s);
     uint16_t *op16 = with16 ? (uint16_t *)(ws + W.v16) : nullptr;
     float *s8 = (float *)(ws + W.vs8);
+    const Geo g = layout_geo(L, ws);
+#define DA2_PREP_V(DD, RG)                                                                              \
+    k_prep_v<DD, RG><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R, g, vamax, op8, \
+                                         s8, op4, op4s, op16)
     if (L.d == 128) {
         k_vamax<128><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
-        k_prep_v<128><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
-                                          L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s,
-                                          op16);
+        if (L.ragged)
+            DA2_PREP_V(128, true);
+        else
+            DA2_PREP_V(128, false);
     } else {
         k_vamax<64><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
-        k_prep_v<64><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R,
-                                         L.Ry, L.Rx, s.height, s.width, vamax, op8, s8, op4, op4s,
-                                         op16);
+        if (L.ragged)
+            DA2_PREP_V(64, true);
+        else
+            DA2_PREP_V(64, false);
     }
+#undef DA2_PREP_V
 }
 
 void launch_prep_vp(const da2_layout_s &L, const PrefixIo &px, char *ws, hipStream_t st)

@@ -53,6 +53,10 @@ def lib():
         P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
         L.da2_layout_create.argtypes = [C.POINTER(Shape), C.POINTER(P)]
         L.da2_layout_destroy.argtypes = [P]
+        L.da2_layout_regions.argtypes = [P, C.POINTER(i32)]
+        L.da2_layout_regions.restype = i32
+        L.da2_layout_slots.argtypes = [P, P]
+        L.da2_layout_slots.restype = C.c_int
         L.da2_workspace_bytes.argtypes = [P]
         L.da2_workspace_bytes.restype = sz
         L.da2_plan_create.argtypes = [P, P, sz, C.POINTER(P)]
@@ -140,12 +144,24 @@ class Layout:
     def __init__(self, B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix=0):
         self.B, self.H, self.d, self.F, self.Hv, self.Wv = B, H, d, F, Hv, Wv
         self.N = F * Hv * Wv
-        self.R = self.N // 64
         self.prefix = prefix
         self.shape = Shape(B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix)
         h = C.c_void_p()
         _check(lib().da2_layout_create(C.byref(self.shape), C.byref(h)), "da2_layout_create")
         self.handle = h
+        rf = C.c_int32()
+        self.R = int(lib().da2_layout_regions(h, C.byref(rf)))
+        self.Rf = rf.value
+        self.Np = 64 * self.R
+
+    def slots(self):
+        """One frame's partition: int32 [R_f, 64], token y*Wv + x of each slot
+        (-1: padding)."""
+        import numpy as np
+
+        out = np.empty((self.Rf, 64), np.int32)
+        _check(lib().da2_layout_slots(self.handle, out.ctypes.data_as(C.c_void_p)), "da2_layout_slots")
+        return out
 
     @classmethod
     def for_tensor(cls, x: torch.Tensor, F, Hv, Wv, bhnd=True, prefix=0):
