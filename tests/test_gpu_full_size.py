@@ -35,13 +35,15 @@ def _run_layout(w, q, k, v, hi, lo):
 
 def _check_heads(w, q, k, v, hi, lo, P, o32, o16, heads):
     B, H, N, d = q.shape
-    R = N // 64
+    R = w.R
     perm = O.layout(w.F, w.Hv, w.Wv)
     keys = G.host(P.debug("KEYS"), np.uint32).reshape(B, H, R, R)
     tier = P.tier_map().cpu().numpy()
     sched = G.host(P.debug("SCHEDULE"), np.int32).reshape(B, H, R, R + 3)
     regions = _sample_regions(R)
-    rows = np.concatenate([perm[a * 64:(a + 1) * 64] for a in regions])
+    slots = np.concatenate([perm[a * 64:(a + 1) * 64] for a in regions])
+    keep = slots >= 0                 # padding slots of ragged layouts hold no query
+    rows = slots[keep]
     for b, h in heads:
         qh, kh, vh = (np.ascontiguousarray(x[b:b + 1, h:h + 1]) for x in (q, k, v))
         ref_plan = O.plan(qh, kh, w.F, w.Hv, w.Wv, hi, lo, w.lam)
@@ -51,7 +53,8 @@ def _check_heads(w, q, k, v, hi, lo, P, o32, o16, heads):
         ref, allow = O.attention_kp(qh, kh, vh, ref_plan["tier"], w.F, w.Hv, w.Wv, qblocks=regions)
         idx = torch.from_numpy(rows.astype(np.int64)).cuda()
         got = o32[b, h].index_select(0, idx).cpu().numpy().astype(np.float64)
-        rl, ma = G.check_kp(got, ref.reshape(-1, d), allow.reshape(-1, d), "%s b%d h%d" % (w.name, b, h))
+        rl, ma = G.check_kp(got, ref.reshape(-1, d)[keep], allow.reshape(-1, d)[keep],
+                            "%s b%d h%d" % (w.name, b, h))
         # bf16 output: the fp32 result rounded to nearest even
         g16 = o16[b, h].index_select(0, idx).float().cpu().numpy()
         r16 = torch.from_numpy(got.astype(np.float32)).to(torch.bfloat16).float().numpy()
@@ -63,7 +66,9 @@ def _check_heads(w, q, k, v, hi, lo, P, o32, o16, heads):
 
 @pytest.mark.parametrize("name,heads", [("wan1.3b", [(0, 0), (0, 11)]),
                                         ("wan14b-720p", [(0, 0), (0, 39)]),
-                                        ("hunyuan", [(0, 7)])])
+                                        ("hunyuan", [(0, 7)]),
+                                        ("wan1.3b-480p", [(0, 0), (0, 11)]),
+                                        ("hunyuan-544p", [(0, 5)])])
 def test_layer_full_size(name, heads):
     w = configs.WORKLOADS[name]
     hi, lo = w.budgets[0]
