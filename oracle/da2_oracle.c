@@ -89,6 +89,7 @@ static uint32_t f32bits(float f)
 /* square.                                                              */
 /* ------------------------------------------------------------------ */
 #define OR_MINFILL 48
+#define OR_MEAN 1 /* tier of a block-mean tile (skip replaced by block means) */
 
 /* Piece label of every cell of one band (h lines x L), lab[line*L + col]. */
 static int band_pieces(int h, int L, int *lab)
@@ -509,7 +510,7 @@ void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T16, int64_t T
 /* ------------------------------------------------------------------ */
 int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
             const uint16_t *k, int32_t full_bp, int32_t hi_bp, int32_t lo_bp, double lambda, int scope,
-            uint32_t *keys, uint8_t *tier, double *qavg, double *kavg, float *qmx,
+            int skip_means, uint32_t *keys, uint8_t *tier, double *qavg, double *kavg, float *qmx,
             float *kmx)
 {
     int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
@@ -534,6 +535,11 @@ int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < B * H; bh++)
         or_rank_head(keys + (size_t)bh * R * R, R, scope, T16, T8c, Tk, tier + (size_t)bh * R * R);
+    /* skip replacement by block means: every pair outside the quotas */
+    if (skip_means)
+        for (size_t i = 0; i < (size_t)B * H * R * R; i++)
+            if (tier[i] == 0)
+                tier[i] = OR_MEAN;
     free(qa); free(ka); free(qm); free(km); free(perm);
     return 0;
 }
@@ -805,6 +811,7 @@ typedef struct {
     double *q4, *k4, *v4;    /* MXFP4 dequantized */
     uint8_t *c8q, *c8k;      /* FP8 codes of Q and K, reordered [N][d] */
     float *s8q, *s8k;        /* their per-block scales [R] */
+    double *qa, *ka, *va;    /* region means over the valid tokens [R][d] */
 } head_ops;
 
 /* q, k, v: one head, [Ntok][d] in token order; perm over Np = R 64
@@ -862,6 +869,13 @@ static void head_ops_build(head_ops *h, const uint16_t *q, const uint16_t *k,
         }
     }
     free(c8); free(c4); free(e4); free(s8);
+    double **means[3] = {&h->qa, &h->ka, &h->va};
+    float *mx = malloc(sizeof(float) * (size_t)R * d);
+    for (int t = 0; t < 3; t++) {
+        *means[t] = malloc(sizeof(double) * (size_t)R * d);
+        or_pool_head(src[t], d, perm, R, *means[t], mx);
+    }
+    free(mx);
 }
 
 static void head_ops_free(head_ops *h)
@@ -874,6 +888,20 @@ static void head_ops_free(head_ops *h)
     free(h->s8q);
     free(h->s8k);
     free(h->nv);
+    free(h->qa);
+    free(h->ka);
+    free(h->va);
+}
+
+/* Block-mean tile (a, b) ([Triage] abstract: a skipped tile replaced by its
+ * block means).  By bilinearity the mean of the tile's 64 x 64 scores is
+ * the score of the mean query and the mean key, q_a . k_b / sqrt(d) (the
+ * average-branch draft logit of Eq. 2, same fma chain); the tile's values
+ * are replaced by the key region's mean value v_b, and the tile counts its
+ * n_b valid keys. */
+static double mean_logit(const head_ops *h, int a, int b)
+{
+    return fma_chain(h->qa + (size_t)a * h->d, h->ka + (size_t)b * h->d, h->d) / sqrt((double)h->d);
 }
 
 /* Weight quantizers for one 64-key tile, w[64] in key order. */
@@ -1003,6 +1031,7 @@ static void attention_row(const head_ops *h, const prefix_ops *px, const uint8_t
     row_acc st = {-INFINITY, 0.0, calloc(d, sizeof(double))};
     double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
     static const int phases[4] = {32, 16, 8, 4};
+    const int a = u / OR_BLK;
     prefix_segment(&st, d, px, h->qf + (size_t)u * d, tr);
     for (int ph = 0; ph < 4; ph++) {
         int p = phases[ph];
@@ -1025,6 +1054,23 @@ static void attention_row(const head_ops *h, const prefix_ops *px, const uint8_t
                 }
             }
         }
+    }
+    /* block-mean tiles last, ascending (the lowest tier): one score per
+     * tile, unquantized */
+    for (int b = 0; b < R; b++) {
+        if (tier_row[b] != OR_MEAN)
+            continue;
+        double sb = mean_logit(h, a, b);
+        double mn = sb > st.m ? sb : st.m;
+        double alpha = (st.m == -INFINITY) ? 0.0 : exp(st.m - mn);
+        st.Z *= alpha;
+        for (int c = 0; c < d; c++)
+            st.acc[c] *= alpha;
+        double w = (double)h->nv[b] * exp(sb - mn);
+        st.Z += w;
+        for (int c = 0; c < d; c++)
+            st.acc[c] += w * h->va[(size_t)b * d + c];
+        st.m = mn;
     }
     finish_row(&st, d, out);
     if (tr)
@@ -1247,6 +1293,7 @@ typedef struct {
     float m;
     double Z;
     double *acc, *al;
+    double zrel;   /* relative uncertainty of Z (block-mean tiles), 0 otherwise */
 } row_kp;
 
 /* Logits of one tile on the 16-bit path: bf16 products are exact in
@@ -1360,8 +1407,55 @@ static void kp_finish(const row_kp *st, int d, double *out, double *allow)
 {
     for (int c = 0; c < d; c++) {
         out[c] = st->Z > 0.0 ? st->acc[c] / st->Z : 0.0;
-        allow[c] = st->Z > 0.0 ? st->al[c] / st->Z + 1e-6 * fabs(out[c]) : 0.0;
+        allow[c] = st->Z > 0.0 ? st->al[c] / st->Z + (1e-6 + st->zrel) * fabs(out[c]) : 0.0;
     }
+}
+
+/* Block-mean tiles in the kernel's arithmetic: the query region's tiles are
+ * gathered into one term before the row is finished -- t_b = fp32(s_b
+ * log2(e)), M = max t_b, z_a = sum n_b 2^(t_b - M), c_a = sum n_b 2^(t_b -
+ * M) v_b in fp32 -- and folded into the row's state as a key of logit M,
+ * weight z_a and value c_a / z_a.  Values here in fp64; the fp32 sums, the
+ * fp32 means and the hardware exp2 are bounded by (n + 8) 2^-23 of the
+ * terms' magnitude. */
+static void kp_mean_fold(row_kp *st, const head_ops *h, const uint8_t *tier_row, int a)
+{
+    int d = h->d, R = h->R, n = 0;
+    float M = -INFINITY;
+    for (int b = 0; b < R; b++)
+        if (tier_row[b] == OR_MEAN) {
+            float t = (float)(mean_logit(h, a, b) * 1.4426950408889634);
+            M = fmaxf(M, t);
+            n++;
+        }
+    if (n == 0)
+        return;
+    float mn = fmaxf(st->m, M);
+    double f = exp2((double)st->m - (double)mn);
+    st->Z *= f;
+    double zmean = 0.0, *mass = calloc(d, sizeof(double));
+    for (int c = 0; c < d; c++) {
+        st->acc[c] *= f;
+        st->al[c] *= f;
+    }
+    for (int b = 0; b < R; b++) {
+        if (tier_row[b] != OR_MEAN)
+            continue;
+        float t = (float)(mean_logit(h, a, b) * 1.4426950408889634);
+        double w = (double)h->nv[b] * exp2((double)t + 8.0 - (double)mn);
+        zmean += w;
+        for (int c = 0; c < d; c++) {
+            st->acc[c] += w * h->va[(size_t)b * d + c];
+            mass[c] += w * fabs(h->va[(size_t)b * d + c]);
+        }
+    }
+    st->Z += zmean;
+    double rel = (double)(n + 8) * 0x1p-23;
+    for (int c = 0; c < d; c++)
+        st->al[c] += rel * mass[c];
+    st->zrel = rel * zmean / st->Z;
+    st->m = mn;
+    free(mass);
 }
 
 static void attention_row_kp(const head_ops *h, const prefix_ops *px, const uint8_t *tier_row,
@@ -1369,7 +1463,7 @@ static void attention_row_kp(const head_ops *h, const prefix_ops *px, const uint
 {
     int d = h->d, R = h->R, a = u / OR_BLK;
     const float c4 = (float)(1.4426950408889634 / sqrt((double)d));
-    row_kp st = {-INFINITY, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double))};
+    row_kp st = {-INFINITY, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double)), 0.0};
     float S[OR_BLK];
     double dS[OR_BLK], e[OR_BLK], eta[OR_BLK];
     kp_step t;
@@ -1474,6 +1568,7 @@ static void attention_row_kp(const head_ops *h, const prefix_ops *px, const uint
             st.m = t.mn;
         }
     }
+    kp_mean_fold(&st, h, tier_row, a);
     kp_finish(&st, d, out, allow);
     free(st.acc);
     free(st.al);
@@ -1493,7 +1588,7 @@ static void attention_prefix_row_kp(const head_ops *h, const prefix_ops *px, int
     double *zc = malloc(sizeof(double) * nc);
     double *ac = calloc((size_t)nc * d, sizeof(double)), *lc = calloc((size_t)nc * d, sizeof(double));
     for (int c = 0; c < nc; c++) {
-        row_kp st = {-INFINITY, 0.0, ac + (size_t)c * d, lc + (size_t)c * d};
+        row_kp st = {-INFINITY, 0.0, ac + (size_t)c * d, lc + (size_t)c * d, 0.0};
         for (int t = c * OR_PCHUNK; t < T && t < (c + 1) * OR_PCHUNK; t++) {
             const double *kt, *vt;
             int nk = prefix_row_tile(h, px, t, &kt, &vt);
@@ -1505,7 +1600,7 @@ static void attention_prefix_row_kp(const head_ops *h, const prefix_ops *px, int
     float M = -INFINITY;
     for (int c = 0; c < nc; c++)
         M = fmaxf(M, mc[c]);
-    row_kp all = {M, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double))};
+    row_kp all = {M, 0.0, calloc(d, sizeof(double)), calloc(d, sizeof(double)), 0.0};
     for (int c = 0; c < nc; c++) {
         double f = exp2((double)mc[c] - (double)M);
         all.Z += zc[c] * f;

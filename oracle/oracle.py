@@ -65,7 +65,7 @@ def lib():
         L.or_bf16_round.argtypes = [f64]
         L.or_bf16_round.restype = f64
         L.or_rank_head.argtypes = [P, C.c_int, C.c_int, i64, i64, i64, P]
-        L.or_plan.argtypes = [C.c_int] * 6 + [P, P, i32, i32, i32, f64, C.c_int, P, P, P, P, P, P]
+        L.or_plan.argtypes = [C.c_int] * 6 + [P, P, i32, i32, i32, f64, C.c_int, C.c_int, P, P, P, P, P, P]
         L.or_plan.restype = C.c_int
         L.or_e4m3_value.argtypes = [C.c_int]
         L.or_e4m3_value.restype = f64
@@ -225,9 +225,11 @@ def rank_head(keys: np.ndarray, T8, Tk, scope=0, T16=0) -> np.ndarray:
     return tier
 
 
-def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False, full_bp=0):
+def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False, full_bp=0,
+         skip_means=False):
     """Full plan for [B,H,N,d] inputs -> dict(keys [B,H,R,R] u32, tier u8, ...).
-    full_bp: share of the 16-bit tier (basis points)."""
+    full_bp: share of the 16-bit tier (basis points); skip_means: pairs
+    outside the quotas become block-mean tiles (tier 1) instead of skipped."""
     q = _u16(q)
     k = _u16(k)
     B, H, N, d = q.shape
@@ -243,7 +245,7 @@ def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False, ful
         out["kmax"] = np.empty((B, H, R, d), np.float32)
         ptrs = [_p(out[n]) for n in ("qavg", "kavg", "qmax", "kmax")]
     rc = lib().or_plan(B, H, F, Hv, Wv, d, _p(q), _p(k), int(full_bp), int(hi_bp), int(lo_bp), float(lam),
-                       int(scope), _p(keys), _p(tier), *ptrs)
+                       int(scope), int(bool(skip_means)), _p(keys), _p(tier), *ptrs)
     if rc:
         raise ValueError("bad shape")
     return out

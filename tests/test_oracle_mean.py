@@ -1,0 +1,122 @@
+"""Pins of the oracle's block-mean tiles (CPU; [Triage] abstract: a skipped
+tile replaced by its block means; DraftAttention2 Eq. 1-2 pooled means).
+
+* a block-mean tile scores the whole tile with q_a . k_b / sqrt(d), the mean
+  of its 64 x 64 token scores (bilinearity), and counts its n_b keys with the
+  mean value v_b: brute force against a two-pass numpy formula over kept
+  full-precision keys plus one term per mean tile (1e-12), on a grid and on
+  a ragged layout (n_b < 64);
+* when every region's Q, K and V rows are constant, block-mean tiles equal
+  full-precision tiles;
+* the mean-tile score is the mean of the tile's token scores;
+* the plan's skip replacement turns exactly the pairs outside the quotas
+  into block-mean tiles; kernel-precision agreement with the fp64 loop.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from video_diffusion_dit_frame_amd import synth
+from video_diffusion_dit_frame_amd.synth import bf16_bits_to_f32, f32_to_bf16_bits
+
+MEAN = 1
+
+
+def f64(x):
+    return bf16_bits_to_f32(x).astype(np.float64)
+
+
+def region_of(orc, F, Hv, Wv):
+    perm = orc.layout(F, Hv, Wv)
+    R = perm.size // 64
+    blk = np.empty(F * Hv * Wv, np.int64)
+    blk[perm[perm >= 0]] = np.nonzero(perm >= 0)[0] // 64
+    return blk, R
+
+
+def brute(q, k, v, tier_rr, blk, R):
+    """Two-pass reference: full-precision keys of tier-32 pairs, plus for
+    every mean pair one term n_b e^(qbar_a . kbar_b / sqrt d) vbar_b."""
+    d = q.shape[1]
+    cnt = np.bincount(blk, minlength=R).astype(np.float64)
+    qa = np.stack([q[blk == a].sum(0) / cnt[a] for a in range(R)])
+    ka = np.stack([k[blk == a].sum(0) / cnt[a] for a in range(R)])
+    va = np.stack([v[blk == a].sum(0) / cnt[a] for a in range(R)])
+    out = np.zeros_like(q)
+    for u in range(q.shape[0]):
+        a = blk[u]
+        keep = tier_rr[a][blk] == 32
+        s_full = q[u] @ k[keep].T / math.sqrt(d)
+        mb = np.nonzero(tier_rr[a] == MEAN)[0]
+        s_mean = ka[mb] @ qa[a] / math.sqrt(d)
+        allm = np.concatenate([s_full, s_mean])
+        if allm.size == 0:
+            continue
+        m = allm.max()
+        w_full = np.exp(s_full - m)
+        w_mean = cnt[mb] * np.exp(s_mean - m)
+        Z = w_full.sum() + w_mean.sum()
+        out[u] = (w_full @ v[keep] + w_mean @ va[mb]) / Z
+    return out
+
+
+@pytest.mark.parametrize("F,Hv,Wv", [(2, 16, 16), (2, 20, 28)], ids=["grid", "ragged"])
+def test_mean_tiles_brute_force(orc, F, Hv, Wv):
+    q, k, v = synth.make_qkv(1, 1, F, Hv, Wv, 64, 71, True)
+    blk, R = region_of(orc, F, Hv, Wv)
+    rng = np.random.default_rng(2)
+    tier = rng.choice(np.array([0, MEAN, 32], np.uint8), size=(1, 1, R, R), p=[0.3, 0.4, 0.3])
+    tier[0, 0, 1, :] = MEAN      # a row of mean tiles only
+    tier[0, 0, 2, :] = 0         # an empty row
+    out = orc.attention(q, k, v, tier, F, Hv, Wv)
+    ref = brute(f64(q[0, 0]), f64(k[0, 0]), f64(v[0, 0]), tier[0, 0], blk, R)
+    assert np.abs(out[0, 0] - ref).max() <= 1e-12
+    assert (out[0, 0][blk == 2] == 0).all() and np.abs(out[0, 0][blk == 1]).max() > 0
+
+
+def test_constant_regions_mean_equals_full(orc):
+    F, Hv, Wv, d = 2, 16, 16, 64
+    q, k, v = synth.make_qkv(1, 1, F, Hv, Wv, d, 72, False)
+    blk, R = region_of(orc, F, Hv, Wv)
+    # one row per region, repeated over the region's tokens
+    for x in (q, k, v):
+        for a in range(R):
+            x[0, 0, blk == a] = x[0, 0, np.nonzero(blk == a)[0][0]]
+    rng = np.random.default_rng(3)
+    t32 = rng.choice(np.array([0, 32], np.uint8), size=(1, 1, R, R))
+    t1 = np.where(t32 == 32, MEAN, 0).astype(np.uint8)
+    o32 = orc.attention(q, k, v, t32, F, Hv, Wv)
+    o1 = orc.attention(q, k, v, t1, F, Hv, Wv)
+    assert np.abs(o32 - o1).max() <= 1e-12
+
+
+def test_mean_score_is_mean_of_tile_scores(orc):
+    F, Hv, Wv, d = 1, 16, 16, 64
+    q, k, _ = synth.make_qkv(1, 1, F, Hv, Wv, d, 73, True)
+    blk, R = region_of(orc, F, Hv, Wv)
+    Q, K = f64(q[0, 0]), f64(k[0, 0])
+    S = Q @ K.T / math.sqrt(d)
+    p = orc.plan(q, k, F, Hv, Wv, 1000, 1000, descriptors=True)
+    for a in range(R):
+        for b in range(R):
+            tile_mean = S[np.ix_(blk == a, blk == b)].mean()
+            pooled = p["qavg"][0, 0, a] @ p["kavg"][0, 0, b] / math.sqrt(d)
+            assert abs(tile_mean - pooled) <= 1e-12 * max(1.0, abs(tile_mean))
+
+
+def test_plan_skip_replacement(orc):
+    F, Hv, Wv, d = 2, 16, 24, 64
+    q, k, v = synth.make_qkv(1, 2, F, Hv, Wv, d, 74, True)
+    base = orc.plan(q, k, F, Hv, Wv, 1500, 2500)["tier"]
+    repl = orc.plan(q, k, F, Hv, Wv, 1500, 2500, skip_means=True)["tier"]
+    assert np.array_equal(repl, np.where(base == 0, MEAN, base))
+    ex = orc.attention(q, k, v, repl, F, Hv, Wv)
+    kp, al = orc.attention_kp(q, k, v, repl, F, Hv, Wv)
+    assert (al >= 0).all()
+    assert np.linalg.norm(kp - ex) / np.linalg.norm(ex) <= 3e-3
+    # only mean and 16-bit tiles: no FP8/MXFP4 code decisions, fp32-level agreement
+    t = np.where(repl == 4, 16, np.where(repl == 8, 16, repl)).astype(np.uint8)
+    ex = orc.attention(q, k, v, t, F, Hv, Wv)
+    kp, al = orc.attention_kp(q, k, v, t, F, Hv, Wv)
+    assert np.linalg.norm(kp - ex) / np.linalg.norm(ex) <= 1e-5
