@@ -31,7 +31,13 @@
  *   - The output O uses the same element strides in its own element type
  *     (fp32 or bf16).
  *   - Tier maps are uint8 [B, H, R, R] (query region a, key region b) with
- *     values 16 (16-bit: bf16 operands), 8 (FP8), 4 (MXFP4) or 0 (skip).
+ *     values 16 (16-bit: bf16 operands), 8 (FP8), 4 (MXFP4), 1 (block mean)
+ *     or 0 (skip).  A block-mean tile ("Triage: Skip, Skim, or Refine
+ *     Attention Tiles in Video Diffusion Transformers", abstract: a skipped
+ *     tile replaced by its block means) scores all its query-key pairs with
+ *     the mean of its scores, q_a . k_b / sqrt(d) over the valid-token means
+ *     (the average-branch draft logit of Eq. 2), and counts the key region's
+ *     n_b tokens with their mean value; it costs no tile product.
  *   - All calls are asynchronous on the given HIP stream.  Nothing is
  *     synchronised except where stated.  Device buffers (inputs, outputs,
  *     the workspace) belong to the caller; the library allocates only the
@@ -76,6 +82,8 @@ typedef struct {
                         1: one ranking per query region over n = R pairs */
     int32_t full_bp; /* share in the 16-bit tier (bf16 operands, the paper's 16-bit
                         path); full_bp + hi_bp + lo_bp <= 10000 */
+    int32_t skip_means; /* 0: pairs outside the quotas are skipped; 1: they become
+                           block-mean tiles (tier 1, see below) */
 } da2_budget;
 
 typedef struct da2_layout_s da2_layout_t;
@@ -118,8 +126,8 @@ da2_status da2_plan(da2_plan_t *plan, const void *q, const void *k, const da2_bu
                     hipStream_t stream);
 
 /* Same as da2_plan but with a caller-supplied tier map (device, [B,H,R,R],
- * values in {0,4,8,16}; other values are treated as skip).  Pooling and draft
- * scoring are not run. */
+ * values in {0,1,4,8,16}; other values are treated as skip).  The draft map
+ * and ranking are not run; the draft logits are (block-mean tiles use them). */
 da2_status da2_plan_from_tier_map(da2_plan_t *plan, const void *q, const void *k,
                                   const uint8_t *tier_map, hipStream_t stream);
 
@@ -129,7 +137,8 @@ da2_status da2_plan_tier_map(const da2_plan_t *plan, uint8_t *dst, hipStream_t s
 /* da2_attention: V preparation (FP8 with one fp32 scale per channel over all
  * tokens; MXFP4 along keys in groups of 32 inside each region) and the
  * phased mixed-precision attention over the plan's kept tiles (16-bit phase,
- * then FP8, then MXFP4; Sec. 3.3), written to o in the original token order.
+ * then FP8, then MXFP4; Sec. 3.3), then the block-mean tiles, written to o in
+ * the original token order.
  * out_dtype: 0 = bf16, 1 = fp32.  q and k must be the pointers the plan was
  * built on (DA2_ERR_PLAN_MISMATCH otherwise).  Rows whose query region keeps
  * no tile are written as zero (App. C.1).  The video tokens only: a text

@@ -74,7 +74,10 @@ def test_workspace_and_plan_validation():
                                      (100, 100, 1.5, 0, 0), (100, 100, float("nan"), 0, 0),
                                      (100, 100, 0.2, 2, 0), (100, 100, 0.2, 0, -1),
                                      (4000, 3000, 0.2, 0, 3001)]:
-        b = da2.Budget(hi, lo, lam, scope, full)
+        b = da2.Budget(hi, lo, lam, scope, full, 0)
+        assert L.da2_plan(p, q, q, C.byref(b), None) == INVALID
+    for bad_means in (-1, 2):
+        b = da2.Budget(100, 100, 0.2, 0, 0, bad_means)
         assert L.da2_plan(p, q, q, C.byref(b), None) == INVALID
     b = da2.Budget(100, 100, 0.2, 0)
     assert L.da2_plan(p, C.c_void_p((1 << 24) + 2), q, C.byref(b), None) == INVALID  # misaligned

@@ -73,6 +73,9 @@ void carve(da2_layout_s &L)
     W.pacc = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * d * 4);
     W.pmz = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * 8);
     W.k16 = take(L.ragged ? BH * N * d * 2 : 0);
+    W.vavg = take(BH * R * d * 4);
+    W.magg = take(BH * R * 8);
+    W.cagg = take(BH * R * d * 4);
     W.ftok = take(L.ragged ? (size_t)L.Rf * kBlk * 4 : 0);
     W.nreg = take(L.ragged ? R * 4 : 0);
     W.vamax = take(BH * d * 4);
@@ -323,6 +326,8 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
         return DA2_ERR_INVALID_ARG;
     if (bud->scope != 0 && bud->scope != 1)
         return DA2_ERR_INVALID_ARG;
+    if (bud->skip_means != 0 && bud->skip_means != 1)
+        return DA2_ERR_INVALID_ARG;
     const da2_layout_s &L = P->L;
     const int64_t n = bud->scope == 0 ? (int64_t)L.R * L.R : (int64_t)L.R;
     int64_t t16, t8, tk;
@@ -335,6 +340,8 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
     launch_prep_qk(L, k, 1, P->ws, stream);
     launch_draft(L, bud->lambda, P->ws, stream);
     launch_rank(L, bud->scope, t16, t8, tk, P->ws, stream);
+    if (bud->skip_means)
+        launch_skip_means(L, P->ws, stream);
     launch_schedule(L, P->ws, stream);
     da2_status st = launched();
     if (st != DA2_OK)
@@ -344,6 +351,7 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
     P->ready = 1;
     P->has_keys = 1;
     P->has16 = t16 > 0;
+    P->has_mean = bud->skip_means != 0;
     return DA2_OK;
 }
 
@@ -363,6 +371,9 @@ da2_status da2_plan_from_tier_map(da2_plan_t *P, const void *q, const void *k,
     launch_prep_qk(L, k, 1, P->ws, stream);
     launch_import_tier(L, tier_map, P->ws, stream);
     launch_schedule(L, P->ws, stream);
+    // the map may hold block-mean tiles: their scores are the draft's
+    // average-branch logits
+    launch_draft_logits(L, P->ws, stream);
     da2_status st = launched();
     if (st != DA2_OK)
         return st;
@@ -371,6 +382,7 @@ da2_status da2_plan_from_tier_map(da2_plan_t *P, const void *q, const void *k,
     P->ready = 1;
     P->has_keys = 0;
     P->has16 = 1;  // the imported map may hold 16-bit tiles
+    P->has_mean = 1;
     return DA2_OK;
 }
 
@@ -402,7 +414,7 @@ static da2_status attend(da2_plan_s *P, const void *q, const void *k, const void
         return DA2_ERR_PLAN_MISMATCH;
     const da2_layout_s &L = P->L;
     // prefix queries attend to every region on the 16-bit path
-    launch_prep_v(L, v, P->has16 || px, P->ws, stream);
+    launch_prep_v(L, v, P->has16 || px, P->has_mean, P->ws, stream);
     if (px)
         launch_prep_vp(L, *px, P->ws, stream);
     hipEvent_t *ev = nullptr;
@@ -413,7 +425,7 @@ static da2_status attend(da2_plan_s *P, const void *q, const void *k, const void
                 return DA2_ERR_HIP;
         hipEventRecord(ev[0], stream);
     }
-    launch_attention(L, P->ws, q, k, o, out_dtype, px, stream);
+    launch_attention(L, P->ws, q, k, o, out_dtype, px, P->has_mean, stream);
     if (ev) {
         hipEventRecord(ev[1], stream);
         P->nev++;

@@ -16,6 +16,7 @@ constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
 constexpr int kPrefixChunkTiles = 128; // tiles per chunk of a prefix query row
 constexpr int kMaxPrefix = 4096;  // text-prefix tokens per sequence
 constexpr int kMinFill = 48;      // fewest valid tokens of a region (at most 16 padding slots)
+constexpr uint8_t kMeanTier = 1;  // tier of a block-mean tile (skip replaced by block means)
 
 // ---------------------------------------------------------------------------
 // Workspace: one region of caller memory carved into these buffers.
@@ -45,6 +46,8 @@ struct Workspace {
     size_t k8, k4, k4s, ks8;
     size_t v8, v4, v4s, vs8, vamax, v16, vp16, pacc, pmz;
     size_t k16;          // bf16 key image of ragged layouts (16-bit path)
+    size_t vavg, magg, cagg;  // block-mean tiles: region mean values; per query region the
+                              // gathered term (max logit, weight) and its value sum
     size_t ftok, nreg;   // ragged layouts: frame slot table, valid tokens per region
     size_t qavg, kavg, qmax, kmax;
     size_t la, lm, rmax, zsum, keys, tier;
@@ -86,6 +89,7 @@ struct da2_plan_s {
     int ready;                // operands + schedule present
     int has_keys;             // draft keys present (da2_plan, not from tier map)
     int has16;                // the tier map may hold 16-bit tiles
+    int has_mean;             // the tier map may hold block-mean tiles
     int timing;               // record events around the attention kernel
     int nev;                  // recorded event pairs
     hipEvent_t *ev;           // [2 * kMaxTimed] when timing is on
@@ -107,14 +111,16 @@ void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, 
 // Spatial partition of one Hv x Wv frame (defined in da2_partition.cpp):
 // fills tok [Rf*64] (y*Wv + x or -1) and returns Rf, or -1 without one.
 int partition_frame(int Hv, int Wv, int32_t *tok);
-void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, hipStream_t st);
+void launch_prep_v(const da2_layout_s &L, const void *v, int with16, int with_mean, char *ws, hipStream_t st);
 void launch_prep_vp(const da2_layout_s &L, const PrefixIo &px, char *ws, hipStream_t st);
 void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st);
+void launch_draft_logits(const da2_layout_s &L, char *ws, hipStream_t st);
+void launch_skip_means(const da2_layout_s &L, char *ws, hipStream_t st);
 void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int64_t tk, char *ws,
                  hipStream_t st);
 void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st);
 void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
-                      int out_f32, const PrefixIo *px, hipStream_t st);
+                      int out_f32, const PrefixIo *px, int has_mean, hipStream_t st);
 void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, hipStream_t st);
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st);
 

@@ -65,6 +65,11 @@ struct AttnArgs {
     Geo geo;
     const int32_t *nreg;
     const uint8_t *k16;
+    // block-mean tiles (null when the plan has none): per query region the
+    // gathered term -- max logit M (log2 units) and weight z -- and its
+    // value sum [d]
+    const float2 *magg;
+    const float *cagg;
     const int32_t *sched;
     const int32_t *cnt;
     void *out;
@@ -1123,9 +1128,31 @@ struct Attn {
     }
 
     // O = acc / Z for this wave's 32 queries of region a, written straight to
-    // their original token positions (the restore)
+    // their original token positions (the restore).  The region's block-mean
+    // tiles enter first, as one key of logit M, weight z_a and value sum c_a.
     __device__ __forceinline__ void epilogue(int a)
     {
+        if (A.magg) {
+            const int64_t ra = (int64_t)bh * A.R + a;
+            const float2 mz = A.magg[ra];
+            if (mz.y > 0.0f) {
+                const float mnew = fmaxf(m, mz.x);
+                const float f = __builtin_amdgcn_exp2f(m - mnew), g = __builtin_amdgcn_exp2f(mz.x + 8.0f - mnew);
+                z = z * f + (hf ? 0.0f : mz.y * g);   // z is summed over the lane pair
+                const float *cv = A.cagg + ra * D + 4 * hf;
+#pragma unroll
+                for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+                    for (int gq = 0; gq < 4; gq++) {
+                        const float4 c4v = *reinterpret_cast<const float4 *>(cv + 32 * cb + 8 * gq);
+                        acc[cb][4 * gq] = acc[cb][4 * gq] * f + c4v.x * g;
+                        acc[cb][4 * gq + 1] = acc[cb][4 * gq + 1] * f + c4v.y * g;
+                        acc[cb][4 * gq + 2] = acc[cb][4 * gq + 2] * f + c4v.z * g;
+                        acc[cb][4 * gq + 3] = acc[cb][4 * gq + 3] * f + c4v.w * g;
+                    }
+                m = mnew;
+            }
+        }
         const float zt = pair_sum(z);
         const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
         const int qi = 32 * w + (l & 31);
@@ -1263,6 +1290,75 @@ __global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
                         (int)(threadIdx.x & 63));
 }
 
+// Block-mean tiles of one query region ([Triage] abstract: a skipped tile
+// replaced by its block means): tile (a, b) scores all its queries with the
+// mean of its token scores, the average-branch draft logit s_ab = q_a . k_b /
+// sqrt(d), and counts the key region's n_b tokens with their mean value v_b.
+// The region's mean tiles gather into one term: t_b = fp32(s_ab log2 e),
+// M = max t_b, z = sum n_b 2^(t_b - M), c = sum n_b 2^(t_b - M) v_b.  One
+// workgroup per (b, h, query region); thread t owns channel t.  Weights are
+// formed D key regions at a time and shared through LDS.
+template <int D>
+__global__ __launch_bounds__(D) void k_mean_agg(const uint8_t *__restrict__ tier, const double *__restrict__ la,
+                                                 const int32_t *__restrict__ nreg, int R,
+                                                 const float *__restrict__ vavg, float2 *__restrict__ magg,
+                                                 float *__restrict__ cagg)
+{
+    __shared__ float wt[D];
+    __shared__ float red[D / 64];
+    const int a = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const int64_t row = (int64_t)bh * R + a;
+    const uint8_t *trow = tier + row * R;
+    const double *lrow = la + row * R;
+    float M = -__builtin_huge_valf();
+    for (int b = t; b < R; b += D)
+        if (trow[b] == kMeanTier)
+            M = fmaxf(M, (float)(lrow[b] * 1.4426950408889634));
+    for (int o = 32; o > 0; o >>= 1)
+        M = fmaxf(M, __shfl_xor(M, o));
+    if ((t & 63) == 0)
+        red[t >> 6] = M;
+    __syncthreads();
+    M = red[0];
+#pragma unroll
+    for (int i = 1; i < D / 64; i++)
+        M = fmaxf(M, red[i]);
+    __syncthreads();
+    float z = 0.0f, c = 0.0f;
+    if (M > -__builtin_huge_valf()) {
+        for (int b0 = 0; b0 < R; b0 += D) {
+            const int b = b0 + t;
+            float w = 0.0f;
+            if (b < R && trow[b] == kMeanTier)
+                w = (float)(nreg ? nreg[b] : kBlk) *
+                    __builtin_amdgcn_exp2f((float)(lrow[b] * 1.4426950408889634) - M);
+            z += w;
+            wt[t] = w;
+            __syncthreads();
+            const int nb = min(D, R - b0);
+            for (int j = 0; j < nb; j++) {
+                const float wj = wt[j];
+                if (wj != 0.0f)
+                    c = __builtin_fmaf(wj, vavg[(row - a + b0 + j) * D + t], c);
+            }
+            __syncthreads();
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1)
+        z += __shfl_xor(z, o);
+    if ((t & 63) == 0)
+        red[t >> 6] = z;
+    __syncthreads();
+    if (t == 0) {
+        float zs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < D / 64; i++)
+            zs += red[i];
+        magg[row] = make_float2(M, zs);
+    }
+    cagg[row * D + t] = c;
+}
+
 // Merge of a prefix row's chunks (App. B.4's shared normalization across
 // parts): M = max m_c, Z = sum Z_c 2^(m_c - M), O = sum acc_c 2^(m_c - M) / Z
 // (m in log2 units).  Thread: one row, 4 consecutive channels.
@@ -1308,7 +1404,7 @@ __global__ __launch_bounds__(256) void k_prefix_merge(const AttnArgs A)
 }  // namespace
 
 void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
-                      int out_f32, const PrefixIo *px, hipStream_t st)
+                      int out_f32, const PrefixIo *px, int has_mean, hipStream_t st)
 {
     const Workspace &W = L.ws;
     AttnArgs A;
@@ -1357,6 +1453,22 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
     A.geo = layout_geo(L, ws);
     A.nreg = (const int32_t *)(ws + W.nreg);
     A.k16 = (const uint8_t *)(ws + W.k16);
+    A.magg = nullptr;
+    A.cagg = nullptr;
+    if (has_mean) {
+        A.magg = (const float2 *)(ws + W.magg);
+        A.cagg = (const float *)(ws + W.cagg);
+        const int32_t *nreg = L.ragged ? (const int32_t *)(ws + W.nreg) : nullptr;
+        dim3 mg(L.R, L.BH);
+        if (L.d == 128)
+            k_mean_agg<128><<<mg, 128, 0, st>>>((const uint8_t *)(ws + W.tier), (const double *)(ws + W.la),
+                                                nreg, L.R, (const float *)(ws + W.vavg), (float2 *)(ws + W.magg),
+                                                (float *)(ws + W.cagg));
+        else
+            k_mean_agg<64><<<mg, 64, 0, st>>>((const uint8_t *)(ws + W.tier), (const double *)(ws + W.la), nreg,
+                                              L.R, (const float *)(ws + W.vavg), (float2 *)(ws + W.magg),
+                                              (float *)(ws + W.cagg));
+    }
     dim3 grid(8 * ((L.R + 7) / 8) * L.BH);
     // kernel variant: the 8x8 grid, or a ragged layout whose key regions
     // have no padding, at most 4 or at most 16 padding slots

@@ -615,20 +615,35 @@ __global__ void k_copy_tier(const uint8_t *__restrict__ src, uint8_t *__restrict
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) {
         uint8_t v = src[i];
-        dst[i] = (v == 16 || v == 8 || v == 4) ? v : 0;
+        dst[i] = (v == 16 || v == 8 || v == 4 || v == kMeanTier) ? v : 0;
     }
 }
 
 }  // namespace
 
-void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st)
+// Skip replacement: every pair the ranking left out becomes a block-mean tile.
+__global__ void k_skip_means_kernel(uint8_t *__restrict__ tier, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n && tier[i] == 0)
+        tier[i] = kMeanTier;
+}
+
+void launch_skip_means(const da2_layout_s &L, char *ws, hipStream_t st)
+{
+    const int64_t n = (int64_t)L.BH * L.R * L.R;
+    k_skip_means_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((uint8_t *)(ws + L.ws.tier), n);
+}
+
+// The draft logits alone (both branches), e.g. for the block-mean tiles of
+// an imported tier map.
+void launch_draft_logits(const da2_layout_s &L, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
     const double inv_sqrt_d = 1.0 / __builtin_sqrt((double)L.d);
-    const int T = (L.R + 63) / 64, T2 = (L.R + 127) / 128;
+    const int T2 = (L.R + 127) / 128;
     double *La = (double *)(ws + W.la), *Lm = (double *)(ws + W.lm);
     unsigned long long *rmax = (unsigned long long *)(ws + W.rmax);
-    double *zsum = (double *)(ws + W.zsum);
     const int64_t nmax = (int64_t)L.BH * 2 * L.R * 2;  // as 32-bit words
     k_fill_words<<<(unsigned)((nmax + 255) / 256), 256, 0, st>>>((uint32_t *)rmax, nmax);
     dim3 g(T2, T2, 2 * L.BH);
@@ -640,6 +655,16 @@ void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st
         k_logits<64><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
                                         (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
                                         L.R, inv_sqrt_d, La, Lm, rmax);
+}
+
+void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st)
+{
+    const Workspace &W = L.ws;
+    const int T = (L.R + 63) / 64;
+    double *La = (double *)(ws + W.la), *Lm = (double *)(ws + W.lm);
+    unsigned long long *rmax = (unsigned long long *)(ws + W.rmax);
+    double *zsum = (double *)(ws + W.zsum);
+    launch_draft_logits(L, ws, st);
     k_rowsum<<<dim3(T, L.BH, 2), 256, 0, st>>>(La, Lm, L.R, rmax, zsum);
     k_keys<<<dim3((L.R + 255) / 256, L.R, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
                                                                (uint32_t *)(ws + W.keys));

@@ -177,6 +177,7 @@ __global__ __launch_bounds__(256) void k_vamax(const uint16_t *__restrict__ x, i
 template <int D, bool RAG>
 __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, int64_t sb,
                                                 int64_t sh, int64_t sn, int H, int R, Geo g,
+                                                float *__restrict__ vavg,
                                                 const uint32_t *__restrict__ vamax,
                                                 uint8_t *__restrict__ op8, float *__restrict__ s8,
                                                 uint8_t *__restrict__ op4,
@@ -188,9 +189,19 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
     const int b = bh / H, h = bh - b * H;
     const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
     load_region<D, RAG>(xb, sn, a, g, tile);
+    const int na = RAG ? __syncthreads_count(threadIdx.x < kBlk && slot_token<RAG>(g, a, threadIdx.x) >= 0)
+                       : kBlk;
     __syncthreads();
     const int t = threadIdx.x;
     const int64_t blk = (int64_t)bh * R + a;
+    // mean value of the region over its valid tokens (block-mean tiles):
+    // fp64 sum in slot order, divided by n_a, rounded to fp32
+    if (vavg && t < D) {
+        double sum = 0.0;
+        for (int i = 0; i < na; i++)
+            sum += (double)bf16_to_f32(tile[i * D + t]);
+        vavg[blk * D + t] = (float)(sum / (double)na);
+    }
     if (t < 2 * D) {
         const int cb = t >> 6, l = t & 63;
         const int c = 32 * cb + (l & 31), k0 = 32 * (l >> 5);
@@ -328,7 +339,7 @@ void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, 
 #undef DA2_PREP_QK
 }
 
-void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, hipStream_t st)
+void launch_prep_v(const da2_layout_s &L, const void *v, int with16, int with_mean, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
     const da2_shape &s = L.s;
@@ -341,10 +352,11 @@ void launch_prep_v(const da2_layout_s &L, const void *v, int with16, char *ws, h
             *op4s = (uint8_t *)(ws + W.v4s);
     uint16_t *op16 = with16 ? (uint16_t *)(ws + W.v16) : nullptr;
     float *s8 = (float *)(ws + W.vs8);
+    float *vavg = with_mean ? (float *)(ws + W.vavg) : nullptr;
     const Geo g = layout_geo(L, ws);
 #define DA2_PREP_V(DD, RG)                                                                              \
-    k_prep_v<DD, RG><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R, g, vamax, op8, \
-                                         s8, op4, op4s, op16)
+    k_prep_v<DD, RG><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R, g, vavg, vamax, \
+                                         op8, s8, op4, op4s, op16)
     if (L.d == 128) {
         k_vamax<128><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
         if (L.ragged)

@@ -37,7 +37,7 @@ class Shape(C.Structure):
 
 class Budget(C.Structure):
     _fields_ = [("hi_bp", C.c_int32), ("lo_bp", C.c_int32), ("lambda_", C.c_double),
-                ("scope", C.c_int32), ("full_bp", C.c_int32)]
+                ("scope", C.c_int32), ("full_bp", C.c_int32), ("skip_means", C.c_int32)]
 
 
 _lib = None
@@ -202,8 +202,8 @@ class Plan:
                "da2_plan_create")
         self.handle = h
 
-    def plan(self, q, k, hi_bp, lo_bp, lam=0.2, scope=0, stream=None, full_bp=0):
-        b = Budget(int(hi_bp), int(lo_bp), float(lam), int(scope), int(full_bp))
+    def plan(self, q, k, hi_bp, lo_bp, lam=0.2, scope=0, stream=None, full_bp=0, skip_means=False):
+        b = Budget(int(hi_bp), int(lo_bp), float(lam), int(scope), int(full_bp), int(bool(skip_means)))
         _check(lib().da2_plan(self.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
                               C.byref(b), _stream(stream)), "da2_plan")
 
