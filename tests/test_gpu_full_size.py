@@ -90,3 +90,28 @@ def test_budget_sweep_full_size(sweep_inputs, point):
     hi, lo = w.budgets[point]
     P, o32, o16 = _run_layout(w, q, k, v, hi, lo)
     _check_heads(w, q, k, v, hi, lo, P, o32, o16, [(1, 17)])
+
+
+def test_maximum_region_count():
+    """The largest layout the library accepts: 8192 regions per head (32
+    frames of 128 x 128 tokens, R^2 = 67M region pairs).  Draft keys and the
+    tier map of the head bit-exact against the oracle, four query regions
+    against the kernel-precision oracle."""
+    F, Hv, Wv, d = 32, 128, 128, 64
+    hi, lo = 500, 1500
+    q, k, v = G.inputs(1, 1, F, Hv, Wv, d, 8192, True)
+    P, qd, kd = G.run_plan(q, k, F, Hv, Wv, hi, lo)
+    o = G.run_attention(P, qd, kd, v).cpu().numpy()
+    R = P.layout.R
+    assert R == 8192
+    ref_plan = O.plan(q, k, F, Hv, Wv, hi, lo)
+    keys = G.host(P.debug("KEYS"), np.uint32).reshape(ref_plan["keys"].shape)
+    assert np.array_equal(keys, ref_plan["keys"])
+    tier = P.tier_map().cpu().numpy()
+    assert np.array_equal(tier, ref_plan["tier"])
+    regions = _sample_regions(R)
+    ref, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv, qblocks=regions)
+    perm = O.layout(F, Hv, Wv)
+    rows = np.concatenate([perm[a * 64:(a + 1) * 64] for a in regions])
+    rl, ma = G.check_kp(o[0, 0, rows], ref.reshape(-1, d), allow.reshape(-1, d), "R = 8192")
+    print("R = 8192: rel_l2 %.2e max_abs %.2e vs kernel-precision oracle" % (rl, ma))
