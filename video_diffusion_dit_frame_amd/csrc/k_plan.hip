@@ -17,6 +17,8 @@
 // same per query region inside one workgroup.  The schedule lists, per query
 // region, the 16-bit key regions in ascending order, then the FP8 ones, then
 // the MXFP4 ones.
+#include <type_traits>
+
 #include "da2_internal.h"
 #include "da2_device.h"
 
@@ -43,7 +45,8 @@ __global__ void k_fill_words(uint32_t *p, int64_t n)
 // column l%16).
 // One workgroup (4 waves, 2x2) computes a 128x128 tile of one branch; each
 // wave a 64x64 block as 4x4 accumulators.  Channels are staged through LDS
-// 32 at a time, transposed so that an operand is one conflict-free read.
+// 32 at a time, transposed so that an operand is one conflict-free read;
+// the next stage's global loads are in flight while a stage's products run.
 // ---------------------------------------------------------------------------
 typedef double v4d __attribute__((ext_vector_type(4)));
 
@@ -62,63 +65,92 @@ __device__ __forceinline__ double unord64(unsigned long long e)
     return __longlong_as_double((long long)u);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa,
-                                                const double *__restrict__ ka,
-                                                const float *__restrict__ qm,
-                                                const float *__restrict__ km, int R,
-                                                double inv_sqrt_d, double *__restrict__ La,
-                                                double *__restrict__ Lm,
-                                                unsigned long long *__restrict__ rmax)
+// One stage (CK channels of 128 rows of each operand) of one branch, held in
+// registers between its global load and its store to LDS, so that the loads
+// of stage s + 1 are in flight while the products of stage s run.
+template <int D, bool MAXB>
+struct LogitStage {
+    static constexpr int TM = 128, CK = 32;
+    static constexpr int NV = MAXB ? TM * CK / 4 / 256 : TM * CK / 2 / 256;  // vectors per thread
+    typename std::conditional<MAXB, float4, double2>::type x[NV], y[NV];
+
+    __device__ __forceinline__ void load(const void *qb_, const void *kb_, int a0, int b0, int R, int c0, int t)
+    {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int e = t + 256 * i;
+            if (MAXB) {
+                const float *qb = (const float *)qb_, *kb = (const float *)kb_;
+                const int r = e / (CK / 4), c = 4 * (e % (CK / 4));
+                float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), yv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (a0 + r < R)
+                    xv = *reinterpret_cast<const float4 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
+                if (b0 + r < R)
+                    yv = *reinterpret_cast<const float4 *>(kb + (int64_t)(b0 + r) * D + c0 + c);
+                x[i] = *reinterpret_cast<decltype(&x[i])>(&xv);
+                y[i] = *reinterpret_cast<decltype(&y[i])>(&yv);
+            } else {
+                const double *qb = (const double *)qb_, *kb = (const double *)kb_;
+                const int r = e / (CK / 2), c = 2 * (e % (CK / 2));
+                double2 xv = make_double2(0.0, 0.0), yv = make_double2(0.0, 0.0);
+                if (a0 + r < R)
+                    xv = *reinterpret_cast<const double2 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
+                if (b0 + r < R)
+                    yv = *reinterpret_cast<const double2 *>(kb + (int64_t)(b0 + r) * D + c0 + c);
+                x[i] = *reinterpret_cast<decltype(&x[i])>(&xv);
+                y[i] = *reinterpret_cast<decltype(&y[i])>(&yv);
+            }
+        }
+    }
+
+    template <int PITCH>
+    __device__ __forceinline__ void store(double (*sq)[PITCH], double (*sk)[PITCH], int t) const
+    {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int e = t + 256 * i;
+            if (MAXB) {
+                const int r = e / (CK / 4), c = 4 * (e % (CK / 4));
+                const float4 xv = *reinterpret_cast<const float4 *>(&x[i]);
+                const float4 yv = *reinterpret_cast<const float4 *>(&y[i]);
+                sq[c][r] = xv.x; sq[c + 1][r] = xv.y; sq[c + 2][r] = xv.z; sq[c + 3][r] = xv.w;
+                sk[c][r] = yv.x; sk[c + 1][r] = yv.y; sk[c + 2][r] = yv.z; sk[c + 3][r] = yv.w;
+            } else {
+                const int r = e / (CK / 2), c = 2 * (e % (CK / 2));
+                const double2 xv = *reinterpret_cast<const double2 *>(&x[i]);
+                const double2 yv = *reinterpret_cast<const double2 *>(&y[i]);
+                sq[c][r] = xv.x; sq[c + 1][r] = xv.y;
+                sk[c][r] = yv.x; sk[c + 1][r] = yv.y;
+            }
+        }
+    }
+};
+
+template <int D, bool MAXB>
+__device__ __forceinline__ void logits_tile(const double *__restrict__ qa, const double *__restrict__ ka,
+                                            const float *__restrict__ qm, const float *__restrict__ km, int R,
+                                            double inv_sqrt_d, double *__restrict__ La, double *__restrict__ Lm,
+                                            unsigned long long *__restrict__ rmax, int bh, int a0, int b0,
+                                            double (*sq)[132], double (*sk)[132])
 {
-    constexpr int TM = 128, CK = 32, PITCH = TM + 4;
-    __shared__ double sq[CK][PITCH], sk[CK][PITCH];
-    const int b0 = blockIdx.x * TM, a0 = blockIdx.y * TM;
-    const int bh = blockIdx.z >> 1, maxb = blockIdx.z & 1;
+    constexpr int CK = 32;
     const int t = threadIdx.x, l = t & 63, wv = t >> 6, wa = wv >> 1, wb = wv & 1;
+    const void *qb = MAXB ? (const void *)(qm + (int64_t)bh * R * D) : (const void *)(qa + (int64_t)bh * R * D);
+    const void *kb = MAXB ? (const void *)(km + (int64_t)bh * R * D) : (const void *)(ka + (int64_t)bh * R * D);
     v4d acc[4][4];
 #pragma unroll
     for (int g = 0; g < 4; g++)
 #pragma unroll
         for (int h = 0; h < 4; h++)
             acc[g][h] = (v4d){0.0, 0.0, 0.0, 0.0};
+    LogitStage<D, MAXB> st;
+    st.load(qb, kb, a0, b0, R, 0, t);
     for (int c0 = 0; c0 < D; c0 += CK) {
         __syncthreads();
-        if (!maxb) {
-            // 128 rows x 32 channels of each operand, 16 bytes per thread
-            const double *qb = qa + (int64_t)bh * R * D, *kb = ka + (int64_t)bh * R * D;
-            for (int e = t; e < TM * CK / 2; e += 256) {
-                const int r = e / (CK / 2), c = 2 * (e % (CK / 2));
-                double2 x = make_double2(0.0, 0.0), y = make_double2(0.0, 0.0);
-                if (a0 + r < R)
-                    x = *reinterpret_cast<const double2 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
-                if (b0 + r < R)
-                    y = *reinterpret_cast<const double2 *>(kb + (int64_t)(b0 + r) * D + c0 + c);
-                sq[c][r] = x.x;
-                sq[c + 1][r] = x.y;
-                sk[c][r] = y.x;
-                sk[c + 1][r] = y.y;
-            }
-        } else {
-            const float *qb = qm + (int64_t)bh * R * D, *kb = km + (int64_t)bh * R * D;
-            for (int e = t; e < TM * CK / 4; e += 256) {
-                const int r = e / (CK / 4), c = 4 * (e % (CK / 4));
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (a0 + r < R)
-                    x = *reinterpret_cast<const float4 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
-                if (b0 + r < R)
-                    y = *reinterpret_cast<const float4 *>(kb + (int64_t)(b0 + r) * D + c0 + c);
-                sq[c][r] = x.x;
-                sq[c + 1][r] = x.y;
-                sq[c + 2][r] = x.z;
-                sq[c + 3][r] = x.w;
-                sk[c][r] = y.x;
-                sk[c + 1][r] = y.y;
-                sk[c + 2][r] = y.z;
-                sk[c + 3][r] = y.w;
-            }
-        }
+        st.template store<132>(sq, sk, t);
         __syncthreads();
+        if (c0 + CK < D)
+            st.load(qb, kb, a0, b0, R, c0 + CK, t);
 #pragma unroll 2
         for (int s4 = 0; s4 < CK; s4 += 4) {
             const int c = s4 + (l >> 4), r = l & 15;
@@ -137,8 +169,8 @@ __global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa
     }
     // Store row-major and fold the row maxima into rmax with an
     // order-preserving integer atomic maximum.
-    double *L = (maxb ? Lm : La) + (int64_t)bh * R * R;
-    unsigned long long *rm = rmax + ((int64_t)bh * 2 + maxb) * R;
+    double *L = (MAXB ? Lm : La) + (int64_t)bh * R * R;
+    unsigned long long *rm = rmax + ((int64_t)bh * 2 + MAXB) * R;
 #pragma unroll
     for (int g = 0; g < 4; g++)
 #pragma unroll
@@ -162,6 +194,24 @@ __global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa
             if ((l & 15) == 0 && i < R)
                 atomicMax(rm + i, ord64(mx));
         }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa,
+                                                const double *__restrict__ ka,
+                                                const float *__restrict__ qm,
+                                                const float *__restrict__ km, int R,
+                                                double inv_sqrt_d, double *__restrict__ La,
+                                                double *__restrict__ Lm,
+                                                unsigned long long *__restrict__ rmax)
+{
+    __shared__ double sq[32][132], sk[32][132];
+    const int b0 = blockIdx.x * 128, a0 = blockIdx.y * 128;
+    const int bh = blockIdx.z >> 1, maxb = blockIdx.z & 1;
+    if (maxb)
+        logits_tile<D, true>(qa, ka, qm, km, R, inv_sqrt_d, La, Lm, rmax, bh, a0, b0, sq, sk);
+    else
+        logits_tile<D, false>(qa, ka, qm, km, R, inv_sqrt_d, La, Lm, rmax, bh, a0, b0, sq, sk);
 }
 
 // ---------------------------------------------------------------------------
