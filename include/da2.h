@@ -3,16 +3,19 @@
  *
  * The operation (DraftAttention2: Fast Video Diffusion with Low-Resolution-
  * Guided Mixed-Precision Attention, Sec. 3.1 and App. C.1): for every head,
- * pool Q and K over 8x8 spatial regions of each latent frame (Eq. 1), build
+ * pool Q and K over the spatial regions of each latent frame (Eq. 1), build
  * the mixed average/max draft attention map over region pairs (Eq. 2), rank
- * all R^2 region pairs of the head, and give the top T8 pairs the 8-bit tier
- * (FP8 E4M3), the next T4 the 4-bit tier (MXFP4 E2M1 with E8M0 scales per 32
- * values) and skip the rest.  Attention (Sec. 3.3 "phased execution",
- * "cross-precision accumulation"; App. B.3/B.4) then evaluates every kept
- * 64x64 tile at full resolution with its tier's precision, FP8 phase first,
- * MXFP4 phase second, sharing one online softmax and one output accumulator,
- * and writes the output in the original token order ("DraftAttention: Fast
- * Video Diffusion via Low-Resolution Attention Guidance", abstract).
+ * all R^2 region pairs of the head, and give the top T16 pairs the 16-bit
+ * tier (bf16 operands), the next T8 the 8-bit tier (FP8 E4M3), the next T4
+ * the 4-bit tier (MXFP4 E2M1 with E8M0 scales per 32 values) and skip the
+ * rest (or replace them by block means).  Attention (Sec. 3.3 "phased
+ * execution", "cross-precision accumulation"; App. B.3/B.4) then evaluates
+ * every kept 64x64 tile at full resolution with its tier's precision, phase
+ * by phase in descending precision, sharing one online softmax and one
+ * output accumulator, and writes the output in the original token order
+ * ("DraftAttention: Fast Video Diffusion via Low-Resolution Attention
+ * Guidance", abstract).  Text-prefix tokens of joint text-video attention
+ * (App. C.1) are handled by da2_attention_prefixed.
  *
  * Conventions
  *   - Tokens of one (batch, head) are N = frames*height*width latent

@@ -1,7 +1,7 @@
 /*
  * da2_oracle.c -- plain, slow, obviously correct CPU oracle for the
  * DraftAttention2 hot path (low-resolution-guided, block-sparse, mixed
- * FP8 / MXFP4 / skip attention for video diffusion transformers).
+ * 16-bit / FP8 / MXFP4 / skip attention for video diffusion transformers).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code,
@@ -19,25 +19,37 @@
  *   [DA1]  "DraftAttention: Fast Video Diffusion via Low-Resolution Attention
  *           Guidance" -- abstract (reorder, block-sparse attention, restore
  *           the original order).
+ *   [Triage] "Triage: Skip, Skim, or Refine Attention Tiles in Video
+ *           Diffusion Transformers" -- abstract (a skipped tile replaced by
+ *           its block means).
  * Number formats: OCP 8-bit floating point (E4M3, "fn" variant: no inf,
  * max 448) and OCP Microscaling v1.0 (E2M1 elements, E8M0 scale, blocks of
  * 32), as fixed for this path in place of the paper's INT8/NVFP4 paths.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - token order of the input is (frame, y, x) raster;
- *   - regions are the 8x8 grid of every frame (C = 64 tokens, no padding),
- *     region order frame-major then raster, raster order inside a region;
- *   - pooled sums run over the 64 tokens in region order, in fp64;
+ *   - the partition of a frame: bands of whole rows or columns walked as
+ *     column snakes and cut into ceil(hL/64) balanced pieces of >= 48
+ *     tokens, the admissible candidate of smallest total perimeter with
+ *     R_f = ceil(HW/64) regions; valid tokens take slots in raster order,
+ *     padding slots follow (the 8x8 grid when the sides are multiples of 8);
+ *   - pooled sums run over the n_a valid tokens in slot order, in fp64;
  *   - logits are fixed-order fma chains over channels 0..d-1 times 1/sqrt(d);
  *   - exp of the draft softmax is a Cody-Waite reduction (fdlibm's split of
  *     ln 2) followed by a degree-13 Taylor polynomial in Horner form;
  *   - row sums of the draft softmax are sequential over key regions;
  *   - ranking key is the bit pattern of fp32(A); ties by ascending pair index;
- *   - quotas: T8 = round-half-up(hi_bp * n / 10^4), Tk likewise for hi+lo;
+ *   - quotas: cumulative counts T16, T16+T8, T16+T8+T4, each rounded half up;
  *   - FP8 Q/K scale per 64-token block, FP8 V scale per channel over all
  *     tokens, MXFP4 groups along channels for Q/K and along keys for V;
  *   - attention weights are quantized per 64-key tile relative to the
- *     running max: FP8 as e4m3(w * 2^8) * 2^-8, MXFP4 per 32 keys.
+ *     running max: 16-bit path bf16(w), FP8 e4m3(w * 2^8) * 2^-8, MXFP4 per
+ *     32 keys; phases 16 -> 8 -> 4, then block-mean tiles (the tile's mean
+ *     score q_a . k_b / sqrt(d), its mean value, n_b keys);
+ *   - a text prefix: video rows take the valid prefix keys first on the
+ *     16-bit path, in tiles of 64; prefix rows take every valid prefix key and
+ *     every video region on the 16-bit path, in chunks of 128 tiles merged
+ *     by the exact rescale.
  * Parity: every exported function is pinned by a CPU test against closed
  * forms, brute force or a library routine (see the test suite).
  */
