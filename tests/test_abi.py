@@ -167,3 +167,30 @@ def test_partition_agrees_with_oracle(orc, Hv, Wv):
     tok, nv = orc.partition(Hv, Wv)
     assert lay.Rf == tok.shape[0] and lay.R == 3 * tok.shape[0]
     assert np.array_equal(lay.slots(), tok)
+
+
+def test_partition_agrees_with_oracle_random_shapes(orc):
+    """Seeded sweep over 200 frame shapes, half with sides 1..140 and half
+    with sides 1..24 (where many frames have no partition): the library
+    rejects a frame exactly when the oracle finds no partition, and
+    otherwise both give the same slot table."""
+    rng = np.random.default_rng(20261203)
+    rejected = 0
+    for i in range(200):
+        hi = 141 if i % 2 == 0 else 25
+        Hv, Wv = (int(x) for x in rng.integers(1, hi, size=2))
+        s = da2.Shape(1, 1, 64, 1, Hv, Wv, Hv * Wv * 64, Hv * Wv * 64, 64, 0)
+        h = C.c_void_p()
+        st = da2.lib().da2_layout_create(C.byref(s), C.byref(h))
+        try:
+            tok, _ = orc.partition(Hv, Wv)
+        except ValueError:
+            assert st == SHAPE, (Hv, Wv)
+            rejected += 1
+            continue
+        assert st == OK, (Hv, Wv, st)
+        out = np.empty_like(tok)
+        assert da2.lib().da2_layout_slots(h, out.ctypes.data_as(C.c_void_p)) == OK
+        da2.lib().da2_layout_destroy(h)
+        assert np.array_equal(out, tok), (Hv, Wv)
+    assert 0 < rejected < 200
