@@ -91,6 +91,7 @@ void carve(da2_layout_s &L)
     W.tier = take(BH * R * R);
     W.sched = take(BH * R * R * 4);
     W.cnt = take(BH * R * kTargets * 4);
+    W.qord = take(BH * R * 4);
     W.rank_state = take(BH * kTargets * sizeof(RankState));
     W.rank_hist = take(BH * kTargets * 256 * 4);
     W.rank_eq = take(BH * (size_t)L.nchunk * kTargets * 4);

@@ -52,6 +52,7 @@ struct Workspace {
     size_t qavg, kavg, qmax, kmax;
     size_t la, lm, rmax, zsum, keys, tier;
     size_t sched, cnt;
+    size_t qord;         // attention work order: query region of each workgroup slot
     size_t rank_state, rank_hist, rank_eq;
     size_t total;
 };

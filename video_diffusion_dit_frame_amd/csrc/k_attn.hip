@@ -72,6 +72,7 @@ struct AttnArgs {
     const float *cagg;
     const int32_t *sched;
     const int32_t *cnt;
+    const int32_t *qord;  // [bh][j]: query region of work slot j
     void *out;
     int64_t osb, osh, osn;
     int out_f32;
@@ -1193,13 +1194,12 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 
     // XCD-aware work mapping.  Workgroups are dealt to the 8 XCDs round robin
     // (block L runs on XCD L % 8).  Every XCD walks the heads in the same
-    // order and takes its own contiguous eighth of each head's query regions,
-    // so all XCDs work on the same head at a time and that head's key/value
-    // tiles (about 31 MB for a 720p Wan layer) stay in the shared last-level
-    // cache.  Inside a head the query regions are taken frame-fastest: the
-    // regions at one spatial position in consecutive latent frames keep
-    // largely the same key regions, so the workgroups an XCD runs together
-    // share their key/value tiles through its L2.
+    // order and takes its own contiguous eighth (work slots j) of each head's
+    // query regions, so all XCDs work on the same head at a time and that
+    // head's key/value tiles (about 31 MB for a 720p Wan layer) stay in the
+    // shared last-level cache.  The plan's work order maps a slot to its
+    // query region (k_qorder: the share's regions are frame-fastest, ranked
+    // by kept tile count).
     const int R = A.R;
     const int span = (R + 7) / 8;
     const int xcd = (int)(blockIdx.x & 7), kk = (int)(blockIdx.x >> 3);
@@ -1207,8 +1207,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     const int j = xcd * span + (kk - bh * span);
     if (j >= R)
         return;
-    const int RF = A.geo.Rf, NF = R / RF;
-    const int a = (j % NF) * RF + j / NF;
+    const int a = sload_i32(A.qord + (int64_t)bh * R + j);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t qblk = (int64_t)bh * R + a;
 
@@ -1426,6 +1425,7 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
     A.kspan = (int)(((int64_t)7 * L.s.width + 7) * L.s.stride_n + L.d) * 2;
     A.sched = (const int32_t *)(ws + W.sched);
     A.cnt = (const int32_t *)(ws + W.cnt);
+    A.qord = (const int32_t *)(ws + W.qord);
     A.out = o;
     A.osb = L.s.stride_b;
     A.osh = L.s.stride_h;

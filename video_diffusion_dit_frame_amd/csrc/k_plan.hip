@@ -660,6 +660,43 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
     }
 }
 
+// Attention work order.  The attention kernel deals its workgroups to the 8
+// XCDs round robin; XCD x takes work slots j = x*span .. x*span + span - 1
+// (span = ceil(R/8)) of every head.  The slots of a share start as its query
+// regions in frame-fastest order (regions at one spatial position in
+// consecutive latent frames keep largely the same key regions) and are then
+// ranked by kept tile count, largest first, ties in that order.  Workgroups
+// an XCD runs together then walk ascending key lists of similar length from
+// about the same time, so more of their tile reads hit its L2; the longest
+// workgroups of the last head also start first.  One workgroup per (share,
+// head); a share holds at most ceil(kMaxRegions / 8) regions.
+constexpr int kMaxShare = (kMaxRegions + 7) / 8;
+
+__global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt, int R, int RF,
+                                                int32_t *__restrict__ qord)
+{
+    __shared__ int32_t len[kMaxShare];
+    const int span = (R + 7) / 8, j0 = (int)blockIdx.x * span, bh = (int)blockIdx.y;
+    const int n = min(span, R - j0), NF = R / RF;
+    const int64_t row0 = (int64_t)bh * R;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const int j = j0 + i, a = (j % NF) * RF + j / NF;
+        const int32_t *c = cnt + (row0 + a) * kTargets;
+        len[i] = c[0] + c[1] + c[2];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const int me = len[i];
+        int r = 0;
+        for (int k = 0; k < n; k++) {
+            const int o = len[k];
+            r += (o > me) | ((o == me) & (k < i));
+        }
+        const int j = j0 + i;
+        qord[row0 + j0 + r] = (j % NF) * RF + j / NF;
+    }
+}
+
 __global__ void k_copy_tier(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t n)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -750,6 +787,8 @@ void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
     const Workspace &W = L.ws;
     k_schedule<<<dim3(L.R, L.BH), 64, 0, st>>>((const uint8_t *)(ws + W.tier), L.R,
                                                 (int32_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
+    k_qorder<<<dim3(8, L.BH), 256, 0, st>>>((const int32_t *)(ws + W.cnt), L.R, L.Rf,
+                                            (int32_t *)(ws + W.qord));
 }
 
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st)
