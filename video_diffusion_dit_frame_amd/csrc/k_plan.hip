@@ -219,8 +219,22 @@ __global__ __launch_bounds__(256, 2) void k_logits(const double *__restrict__ qa
 // strictly in key order (Z = (((e_0 + e_1) + e_2) + ...)).  Per chunk of 64
 // key regions all four waves form the exponentials (coalesced row reads)
 // into LDS, transposed, then wave 0 adds its lane's (row's) 64 values in
-// order.
+// order.  The next chunk's 16 logits per lane are loaded into registers
+// before the current chunk's exponentials, so the row reads stay in flight
+// through the exponentials and the in-order sum.
 // ---------------------------------------------------------------------------
+constexpr int kRowsumRows = 64 / 4;  // logits per lane per chunk
+
+__device__ __forceinline__ void rowsum_load(const double *__restrict__ L, int R, int a0, int b,
+                                            int wv, double (&x)[kRowsumRows])
+{
+#pragma unroll
+    for (int i = 0; i < kRowsumRows; i++) {
+        const int r = wv + 4 * i;
+        x[i] = (a0 + r < R && b < R) ? L[(int64_t)r * R + b] : 0.0;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_rowsum(const double *__restrict__ La,
                                                 const double *__restrict__ Lm, int R,
                                                 const unsigned long long *__restrict__ rmax,
@@ -234,13 +248,19 @@ __global__ __launch_bounds__(256) void k_rowsum(const double *__restrict__ La,
     if (t < 64)
         mrow[t] = a0 + t < R ? unord64(rmax[rbase + t]) : 0.0;
     const double *L = (br ? Lm : La) + ((int64_t)bh * R + a0) * R;
+    double cur[kRowsumRows], nxt[kRowsumRows] = {};
+    rowsum_load(L, R, a0, lane, wv, cur);
     double z = 0.0;
     __syncthreads();
     for (int b0 = 0; b0 < R; b0 += 64) {
         const int b = b0 + lane;
-#pragma unroll 4
-        for (int r = wv; r < 64; r += 4)
-            es[lane][r] = (a0 + r < R && b < R) ? exp_draft(L[(int64_t)r * R + b] - mrow[r]) : 0.0;
+        if (b0 + 64 < R)
+            rowsum_load(L, R, a0, b + 64, wv, nxt);
+#pragma unroll
+        for (int i = 0; i < kRowsumRows; i++) {
+            const int r = wv + 4 * i;
+            es[lane][r] = (a0 + r < R && b < R) ? exp_draft(cur[i] - mrow[r]) : 0.0;
+        }
         __syncthreads();
         if (wv == 0) {
             const int nb = R - b0 < 64 ? R - b0 : 64;
@@ -248,6 +268,9 @@ __global__ __launch_bounds__(256) void k_rowsum(const double *__restrict__ La,
                 z += es[k][lane];
         }
         __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kRowsumRows; i++)
+            cur[i] = nxt[i];
     }
     if (wv == 0 && a0 + lane < R)
         zsum[rbase + lane] = z;
@@ -256,29 +279,45 @@ __global__ __launch_bounds__(256) void k_rowsum(const double *__restrict__ La,
 // ---------------------------------------------------------------------------
 // Probabilities, mixture and ranking keys, elementwise over region pairs:
 // p = e / Z per branch (e recomputed bit-identically), A = (1 - lambda) p_avg
-// + lambda p_max with separate products, key = bits(fp32(A)).
+// + lambda p_max with separate products, key = bits(fp32(A)).  One workgroup
+// per query region; each thread loads kKeysUnroll pairs' logits before
+// forming their keys, to keep enough reads in flight.
 // ---------------------------------------------------------------------------
+constexpr int kKeysUnroll = 4;
+
 __global__ __launch_bounds__(256) void k_keys(const double *__restrict__ La,
                                               const double *__restrict__ Lm, int R, double lambda,
                                               const unsigned long long *__restrict__ rmax,
                                               const double *__restrict__ zsum,
                                               uint32_t *__restrict__ keys)
 {
-    const int a = blockIdx.y, bh = blockIdx.z;
-    const int b = blockIdx.x * 256 + threadIdx.x;
-    if (b >= R)
-        return;
+    const int a = blockIdx.x, bh = blockIdx.y;
     const int64_t r = (int64_t)bh * 2 * R + a;
     const double ma = unord64(rmax[r]), mm = unord64(rmax[r + R]);
     const double za = zsum[r], zm = zsum[r + R];
-    const int64_t o = ((int64_t)bh * R + a) * R + b;
+    const int64_t row = ((int64_t)bh * R + a) * R;
     const double w0 = 1.0 - lambda;
-    const double pa = exp_draft(La[o] - ma) / za;
-    const double pm = exp_draft(Lm[o] - mm) / zm;
-    const double t0 = w0 * pa;
-    const double t1 = lambda * pm;
-    const double A = t0 + t1;
-    keys[o] = __float_as_uint((float)A);
+    for (int b0 = threadIdx.x; b0 < R; b0 += 256 * kKeysUnroll) {
+        double xa[kKeysUnroll], xm[kKeysUnroll];
+#pragma unroll
+        for (int u = 0; u < kKeysUnroll; u++) {
+            const int b = b0 + 256 * u;
+            xa[u] = b < R ? La[row + b] : 0.0;
+            xm[u] = b < R ? Lm[row + b] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kKeysUnroll; u++) {
+            const int b = b0 + 256 * u;
+            if (b < R) {
+                const double pa = exp_draft(xa[u] - ma) / za;
+                const double pm = exp_draft(xm[u] - mm) / zm;
+                const double t0 = w0 * pa;
+                const double t1 = lambda * pm;
+                const double A = t0 + t1;
+                keys[row + b] = __float_as_uint((float)A);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -753,8 +792,8 @@ void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st
     double *zsum = (double *)(ws + W.zsum);
     launch_draft_logits(L, ws, st);
     k_rowsum<<<dim3(T, L.BH, 2), 256, 0, st>>>(La, Lm, L.R, rmax, zsum);
-    k_keys<<<dim3((L.R + 255) / 256, L.R, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
-                                                               (uint32_t *)(ws + W.keys));
+    k_keys<<<dim3(L.R, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
+                                            (uint32_t *)(ws + W.keys));
 }
 
 void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int64_t tk, char *ws,
