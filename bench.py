@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--prefix", type=int, default=0, help="text-prefix tokens (joint attention)")
     ap.add_argument("--prefix-valid", type=int, default=None,
                     help="valid prefix keys per sequence (default: all)")
+    ap.add_argument("--skip-means", action="store_true",
+                    help="replace skipped tiles by block-mean tiles (tier 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain copy kernel of 1 GiB before the steps (reference for "
@@ -177,8 +179,10 @@ def main():
         else:
             P.attention(qd, kd, vd, o, stream)
 
+    sm = args.skip_means
+
     def step():
-        P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full)
+        P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full, skip_means=sm)
         attend()
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
@@ -192,7 +196,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full)
+        P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full, skip_means=sm)
         ev[i][1].record(stream)
         attend()
         ev[i][2].record(stream)
@@ -243,7 +247,8 @@ def main():
                    "budget_bp": ({"bf16": full} if full else {}) | {"fp8": hi, "mxfp4": lo},
                    "lambda": w.lam, "ranking": "head",
                    "storage": "[B,N,H,d] bf16", "output": "bf16"}
-                  | ({"prefix": Lp, "prefix_valid": nv} if Lp else {}),
+                  | ({"prefix": Lp, "prefix_valid": nv} if Lp else {})
+                  | ({"skip_means": True} if sm else {}),
         "plan_ms": plan_ms,
         "attention_call_ms": attn_call_ms,
         "attention_kernel_ms": attn_kernel_ms,
@@ -251,11 +256,11 @@ def main():
         "tier_weighted_mfma_util": util,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_eff, "unit": "TFLOP/s",
                      "frac": achieved / peak_eff,
-                     "traffic": None if Lp else measured_traffic(w.name, [hi, lo], full),
+                     "traffic": None if Lp or sm else measured_traffic(w.name, [hi, lo], full),
                      "kernel": "k_attn",
                      "peak_basis": "tier-weighted bf16 2.5 / FP8 5.0 / FP4 10.1 PFLOP/s"},
     }
-    if not args.no_cpu_baseline and not Lp:
+    if not args.no_cpu_baseline and not Lp and not sm:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, hi, lo, full)
     print(json.dumps(out), flush=True)

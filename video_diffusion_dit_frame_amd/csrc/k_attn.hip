@@ -1289,73 +1289,109 @@ __global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
                         (int)(threadIdx.x & 63));
 }
 
-// Block-mean tiles of one query region ([Triage] abstract: a skipped tile
+// Block-mean tiles of a query region ([Triage] abstract: a skipped tile
 // replaced by its block means): tile (a, b) scores all its queries with the
 // mean of its token scores, the average-branch draft logit s_ab = q_a . k_b /
 // sqrt(d), and counts the key region's n_b tokens with their mean value v_b.
 // The region's mean tiles gather into one term: t_b = fp32(s_ab log2 e),
-// M = max t_b, z = sum n_b 2^(t_b - M), c = sum n_b 2^(t_b - M) v_b.  One
-// workgroup per (b, h, query region); thread t owns channel t.  Weights are
-// formed D key regions at a time and shared through LDS.
+// M = max t_b, z = sum n_b 2^(t_b - M), c = sum n_b 2^(t_b - M) v_b, each
+// sum in key order.  One workgroup per (b, h) and kMeanRows consecutive
+// query regions; thread t owns channel t.  Per chunk of D key regions thread
+// t forms the weights of key region b0 + t for every row into LDS, then each
+// mean value is read once and applied to all the rows.
+constexpr int kMeanRows = 16;
+
 template <int D>
 __global__ __launch_bounds__(D) void k_mean_agg(const uint8_t *__restrict__ tier, const double *__restrict__ la,
                                                  const int32_t *__restrict__ nreg, int R,
                                                  const float *__restrict__ vavg, float2 *__restrict__ magg,
                                                  float *__restrict__ cagg)
 {
-    __shared__ float wt[D];
-    __shared__ float red[D / 64];
-    const int a = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-    const int64_t row = (int64_t)bh * R + a;
-    const uint8_t *trow = tier + row * R;
-    const double *lrow = la + row * R;
-    float M = -__builtin_huge_valf();
-    for (int b = t; b < R; b += D)
-        if (trow[b] == kMeanTier)
-            M = fmaxf(M, (float)(lrow[b] * 1.4426950408889634));
-    for (int o = 32; o > 0; o >>= 1)
-        M = fmaxf(M, __shfl_xor(M, o));
-    if ((t & 63) == 0)
-        red[t >> 6] = M;
-    __syncthreads();
-    M = red[0];
+    __shared__ __attribute__((aligned(16))) float wt[D][kMeanRows];
+    __shared__ float red[kMeanRows][D / 64];
+    const int a0 = blockIdx.x * kMeanRows, bh = blockIdx.y, t = threadIdx.x;
+    const int nq = min(kMeanRows, R - a0);
+    const int64_t row0 = (int64_t)bh * R + a0;
+    constexpr double kL2e = 1.4426950408889634;
+    float M[kMeanRows];
 #pragma unroll
-    for (int i = 1; i < D / 64; i++)
-        M = fmaxf(M, red[i]);
-    __syncthreads();
-    float z = 0.0f, c = 0.0f;
-    if (M > -__builtin_huge_valf()) {
-        for (int b0 = 0; b0 < R; b0 += D) {
-            const int b = b0 + t;
-            float w = 0.0f;
-            if (b < R && trow[b] == kMeanTier)
-                w = (float)(nreg ? nreg[b] : kBlk) *
-                    __builtin_amdgcn_exp2f((float)(lrow[b] * 1.4426950408889634) - M);
-            z += w;
-            wt[t] = w;
-            __syncthreads();
-            const int nb = min(D, R - b0);
-            for (int j = 0; j < nb; j++) {
-                const float wj = wt[j];
-                if (wj != 0.0f)
-                    c = __builtin_fmaf(wj, vavg[(row - a + b0 + j) * D + t], c);
-            }
-            __syncthreads();
+    for (int q = 0; q < kMeanRows; q++) {
+        float m = -__builtin_huge_valf();
+        if (q < nq) {
+            const uint8_t *trow = tier + (row0 + q) * R;
+            const double *lrow = la + (row0 + q) * R;
+            for (int b = t; b < R; b += D)
+                if (trow[b] == kMeanTier)
+                    m = fmaxf(m, (float)(lrow[b] * kL2e));
         }
+        for (int o = 32; o > 0; o >>= 1)
+            m = fmaxf(m, __shfl_xor(m, o));
+        if ((t & 63) == 0)
+            red[q][t >> 6] = m;
     }
-    for (int o = 32; o > 0; o >>= 1)
-        z += __shfl_xor(z, o);
-    if ((t & 63) == 0)
-        red[t >> 6] = z;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kMeanRows; q++) {
+        M[q] = red[q][0];
+#pragma unroll
+        for (int i = 1; i < D / 64; i++)
+            M[q] = fmaxf(M[q], red[q][i]);
+    }
+    __syncthreads();
+    float z[kMeanRows], c[kMeanRows];
+#pragma unroll
+    for (int q = 0; q < kMeanRows; q++) {
+        z[q] = 0.0f;
+        c[q] = 0.0f;
+    }
+    const float *vhead = vavg + (int64_t)bh * R * D + t;
+    for (int b0 = 0; b0 < R; b0 += D) {
+        const int b = b0 + t;
+        const float nb = b < R ? (float)(nreg ? nreg[b] : kBlk) : 0.0f;
+#pragma unroll
+        for (int q = 0; q < kMeanRows; q++) {
+            float w = 0.0f;
+            if (q < nq && b < R && tier[(row0 + q) * R + b] == kMeanTier)
+                w = nb * __builtin_amdgcn_exp2f((float)(la[(row0 + q) * R + b] * kL2e) - M[q]);
+            z[q] += w;
+            wt[t][q] = w;
+        }
+        __syncthreads();
+        const int n = min(D, R - b0);
+#pragma unroll 4
+        for (int j = 0; j < n; j++) {
+            const float v = vhead[(int64_t)(b0 + j) * D];
+            // an absent tile has weight 0 and leaves c unchanged (v is finite)
+#pragma unroll
+            for (int q = 0; q < kMeanRows; q++)
+                c[q] = __builtin_fmaf(wt[j][q], v, c[q]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < kMeanRows; q++) {
+        float zz = z[q];
+        for (int o = 32; o > 0; o >>= 1)
+            zz += __shfl_xor(zz, o);
+        if ((t & 63) == 0)
+            red[q][t >> 6] = zz;
+    }
     __syncthreads();
     if (t == 0) {
-        float zs = 0.0f;
 #pragma unroll
-        for (int i = 0; i < D / 64; i++)
-            zs += red[i];
-        magg[row] = make_float2(M, zs);
+        for (int q = 0; q < kMeanRows; q++) {
+            float zs = 0.0f;
+#pragma unroll
+            for (int i = 0; i < D / 64; i++)
+                zs += red[q][i];
+            if (q < nq)
+                magg[row0 + q] = make_float2(M[q], zs);
+        }
     }
-    cagg[row * D + t] = c;
+#pragma unroll
+    for (int q = 0; q < kMeanRows; q++)
+        if (q < nq)
+            cagg[(row0 + q) * D + t] = c[q];
 }
 
 // Merge of a prefix row's chunks (App. B.4's shared normalization across
@@ -1459,7 +1495,7 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
         A.magg = (const float2 *)(ws + W.magg);
         A.cagg = (const float *)(ws + W.cagg);
         const int32_t *nreg = L.ragged ? (const int32_t *)(ws + W.nreg) : nullptr;
-        dim3 mg(L.R, L.BH);
+        dim3 mg((L.R + kMeanRows - 1) / kMeanRows, L.BH);
         if (L.d == 128)
             k_mean_agg<128><<<mg, 128, 0, st>>>((const uint8_t *)(ws + W.tier), (const double *)(ws + W.la),
                                                 nreg, L.R, (const float *)(ws + W.vavg), (float2 *)(ws + W.magg),
