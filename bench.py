@@ -218,9 +218,11 @@ def main():
     f16 = w.B * w.H * t16 * tile_flop
     f8 = w.B * w.H * (t8c - t16) * tile_flop
     f4 = w.B * w.H * (tk - t8c) * tile_flop
-    # prefix interactions run on the 16-bit path: video rows x valid prefix
-    # keys, and prefix rows x (valid prefix keys + video keys)
-    f16 += 4.0 * w.B * w.H * w.d * (float(w.N) * nv + float(Lp) * (nv + w.N))
+    # prefix interactions run on the 16-bit path.  The attention kernel
+    # (k_attn, the timed one) does the video rows x valid prefix keys; the
+    # prefix rows x (valid prefix keys + video keys) run in k_attn_prefix,
+    # outside the timed kernel and outside this roofline.
+    f16 += 4.0 * w.B * w.H * w.d * float(w.N) * nv
     fx = f16 + f8 + f4
     dense_flop = 4.0 * w.B * w.H * float(Lp + w.N) * float(nv + w.N) * w.d
     t_attn = attn_kernel_ms * 1e-3

@@ -202,7 +202,9 @@ size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which);
 
 /* Kernel timing of the attention kernel itself (measurement aid).
  * da2_plan_timing(plan, 1) starts recording a pair of HIP events around the
- * attention kernel of every later da2_attention call on this plan (up to
+ * attention kernel (k_attn alone: not the value preparation, the block-mean
+ * gather or the prefix query rows) of every later da2_attention or
+ * da2_attention_prefixed call on this plan (up to
  * 4096 calls; older pairs are kept, further calls are not recorded);
  * da2_plan_timing(plan, 0) stops and discards them.  da2_plan_timing_read
  * waits for the recorded events and writes up to `max` per-call durations in

@@ -424,13 +424,10 @@ static da2_status attend(da2_plan_s *P, const void *q, const void *k, const void
         for (int i = 0; i < 2; i++)
             if (!ev[i] && hipEventCreate(&ev[i]) != hipSuccess)
                 return DA2_ERR_HIP;
-        hipEventRecord(ev[0], stream);
     }
-    launch_attention(L, P->ws, q, k, o, out_dtype, px, P->has_mean, stream);
-    if (ev) {
-        hipEventRecord(ev[1], stream);
+    launch_attention(L, P->ws, q, k, o, out_dtype, px, P->has_mean, ev, stream);
+    if (ev)
         P->nev++;
-    }
     return launched();
 }
 

@@ -120,8 +120,9 @@ void launch_skip_means(const da2_layout_s &L, char *ws, hipStream_t st);
 void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int64_t tk, char *ws,
                  hipStream_t st);
 void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st);
+// ev: null, or two events recorded right before and right after the k_attn launch
 void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
-                      int out_f32, const PrefixIo *px, int has_mean, hipStream_t st);
+                      int out_f32, const PrefixIo *px, int has_mean, hipEvent_t *ev, hipStream_t st);
 void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, hipStream_t st);
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st);
 

@@ -1439,7 +1439,7 @@ __global__ __launch_bounds__(256) void k_prefix_merge(const AttnArgs A)
 }  // namespace
 
 void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void *k, void *o,
-                      int out_f32, const PrefixIo *px, int has_mean, hipStream_t st)
+                      int out_f32, const PrefixIo *px, int has_mean, hipEvent_t *ev, hipStream_t st)
 {
     const Workspace &W = L.ws;
     AttnArgs A;
@@ -1520,10 +1520,14 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
         else                                                            \
             k_attn<DD, true, 16><<<grid, 128, 0, st>>>(A);              \
     } while (0)
+    if (ev)
+        hipEventRecord(ev[0], st);
     if (L.d == 128)
         DA2_ATTN(128);
     else
         DA2_ATTN(64);
+    if (ev)
+        hipEventRecord(ev[1], st);
 #undef DA2_ATTN
     if (A.Lp > 0) {
         dim3 pgrid((A.Lp + kBlk - 1) / kBlk, L.BH, L.pchunks);
