@@ -358,18 +358,42 @@ __global__ __launch_bounds__(256) void k_rank_hist(const uint32_t *__restrict__ 
         s[tg] = st[seg * kTargets + tg];
     }
     __syncthreads();
+    // all of the thread's keys are loaded first; each thread then counts
+    // runs of equal digits itself and adds a run with one LDS atomic (the
+    // leading digits of nearby keys mostly agree)
     const uint32_t *kp = keys + (int64_t)seg * seglen;
-    for (int j = 0; j < kChunk / 256; j++) {
-        int64_t i = c0 + j * 256 + t;
-        if (i < seglen) {
-            uint32_t k = kp[i];
-            uint32_t dg = (k >> shift) & 255u;
+    constexpr int J = kChunk / 256;
+    uint32_t kv[J];
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        const int64_t i = c0 + j * 256 + t;
+        kv[j] = i < seglen ? kp[i] : 0u;
+    }
+    uint32_t last[kTargets], run[kTargets];
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++) {
+        last[tg] = 0u;
+        run[tg] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        if (c0 + j * 256 + t < seglen) {
+            const uint32_t k = kv[j];
+            const uint32_t dg = (k >> shift) & 255u;
 #pragma unroll
             for (int tg = 0; tg < kTargets; tg++)
-                if (s[tg].active && ((k ^ s[tg].prefix) & s[tg].mask) == 0)
-                    atomicAdd(&h[tg][dg], 1u);
+                if (s[tg].active && ((k ^ s[tg].prefix) & s[tg].mask) == 0) {
+                    if (run[tg] != 0u && dg != last[tg])
+                        atomicAdd(&h[tg][last[tg]], run[tg]);
+                    run[tg] = (run[tg] != 0u && dg == last[tg]) ? run[tg] + 1u : 1u;
+                    last[tg] = dg;
+                }
         }
     }
+#pragma unroll
+    for (int tg = 0; tg < kTargets; tg++)
+        if (run[tg] != 0u)
+            atomicAdd(&h[tg][last[tg]], run[tg]);
     __syncthreads();
     uint32_t *g = hist + (int64_t)seg * kTargets * 256;
 #pragma unroll
@@ -427,13 +451,19 @@ __global__ __launch_bounds__(256) void k_rank_eqcount(const uint32_t *__restrict
         n[tg] = 0;
     }
     const uint32_t *kp = keys + (int64_t)seg * seglen;
-    for (int j = 0; j < kChunk / 256; j++) {
-        int64_t i = c0 + j * 256 + t;
-        if (i < seglen) {
-            uint32_t k = kp[i];
+    constexpr int J = kChunk / 256;
+    uint32_t kv[J];
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        const int64_t i = c0 + j * 256 + t;
+        kv[j] = i < seglen ? kp[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        if (c0 + j * 256 + t < seglen) {
 #pragma unroll
             for (int tg = 0; tg < kTargets; tg++)
-                n[tg] += (s[tg].active && k == s[tg].prefix);
+                n[tg] += (s[tg].active && kv[j] == s[tg].prefix);
         }
     }
     __shared__ uint32_t r[kTargets][4];
