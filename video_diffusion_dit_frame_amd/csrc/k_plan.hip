@@ -494,6 +494,8 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
 {
     __shared__ uint32_t base[kTargets];
     __shared__ uint32_t scan[kTargets][256];
+    __shared__ uint32_t kl[kChunk];  // the chunk's keys, staged by coalesced reads
+    __shared__ uint8_t tl[kChunk];   // their tiers, written back by coalesced stores
     const int seg = blockIdx.y, t = threadIdx.x;
     const int64_t ch = blockIdx.x;
     RankState s[kTargets];
@@ -517,9 +519,16 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
                 base[tg] = p[tg];
         }
     }
-    // this thread owns 16 consecutive keys
-    const int64_t i0 = ch * kChunk + (int64_t)t * 16;
+    const int64_t c0 = ch * kChunk;
     const uint32_t *kp = keys + (int64_t)seg * seglen;
+#pragma unroll
+    for (int j = 0; j < kChunk / 256; j++) {
+        const int64_t i = c0 + j * 256 + t;
+        kl[j * 256 + t] = i < seglen ? kp[i] : 0u;
+    }
+    __syncthreads();
+    // this thread owns 16 consecutive keys
+    const int64_t i0 = c0 + (int64_t)t * 16;
     uint32_t kv[16];
     uint32_t e[kTargets];
 #pragma unroll
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
 #pragma unroll
     for (int j = 0; j < 16; j++) {
         int64_t i = i0 + j;
-        kv[j] = i < seglen ? kp[i] : 0u;
+        kv[j] = kl[t * 16 + j];
 #pragma unroll
         for (int tg = 0; tg < kTargets; tg++)
             e[tg] += (i < seglen && s[tg].active && kv[j] == s[tg].prefix);
@@ -572,7 +581,14 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
                 }
             }
         }
-        tp[i] = tier_of(in);
+        tl[t * 16 + j] = tier_of(in);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kChunk / 256; j++) {
+        const int64_t i = c0 + j * 256 + t;
+        if (i < seglen)
+            tp[i] = tl[j * 256 + t];
     }
 }
 
@@ -692,9 +708,24 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
                                                  int32_t *__restrict__ sched,
                                                  int32_t *__restrict__ cnt)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t rowl[kMaxRegions];
     const int64_t row = (int64_t)blockIdx.y * R + blockIdx.x;
     const int l = threadIdx.x;
-    const uint8_t *tr = tier + row * R;
+    const uint8_t *tg = tier + row * R;
+    // stage the row in LDS: dword reads when the row starts on a dword
+    int b4 = 0;
+    if ((reinterpret_cast<uintptr_t>(tg) & 3) == 0) {
+        const uint32_t *t4 = reinterpret_cast<const uint32_t *>(tg);
+        const int nw = R >> 2;
+#pragma unroll 4
+        for (int w = l; w < nw; w += 64)
+            reinterpret_cast<uint32_t *>(rowl)[w] = t4[w];
+        b4 = nw << 2;
+    }
+    for (int b = b4 + l; b < R; b += 64)
+        rowl[b] = tg[b];
+    __syncthreads();
+    const uint8_t *tr = rowl;
     uint32_t n16 = 0, n8 = 0, n4 = 0;
     for (int b = l; b < R; b += 64) {
         uint8_t v = tr[b];
