@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
                                                    uint8_t *__restrict__ tier)
 {
     __shared__ uint32_t base[kTargets];
-    __shared__ uint32_t scan[kTargets][256];
+    __shared__ uint32_t wsum[kTargets][4];
     __shared__ uint32_t kl[kChunk];  // the chunk's keys, staged by coalesced reads
     __shared__ uint8_t tl[kChunk];   // their tiers, written back by coalesced stores
     const int seg = blockIdx.y, t = threadIdx.x;
@@ -542,25 +542,33 @@ __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ 
         for (int tg = 0; tg < kTargets; tg++)
             e[tg] += (i < seglen && s[tg].active && kv[j] == s[tg].prefix);
     }
+    // exclusive scan of the equal-key counts over the threads: inside each
+    // wave by lane shuffles, then across the four waves through LDS
+    const int lane = t & 63, wv = t >> 6;
+    uint32_t x[kTargets];
 #pragma unroll
     for (int tg = 0; tg < kTargets; tg++)
-        scan[tg][t] = e[tg];
+        x[tg] = e[tg];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++) {
+            const uint32_t y = __shfl_up(x[tg], o, 64);
+            x[tg] += lane >= o ? y : 0u;
+        }
+    if (lane == 63)
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++)
+            wsum[tg][wv] = x[tg];
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        uint32_t v[kTargets];
-#pragma unroll
-        for (int tg = 0; tg < kTargets; tg++)
-            v[tg] = t >= o ? scan[tg][t - o] : 0u;
-        __syncthreads();
-#pragma unroll
-        for (int tg = 0; tg < kTargets; tg++)
-            scan[tg][t] += v[tg];
-        __syncthreads();
-    }
     uint32_t r[kTargets];
 #pragma unroll
-    for (int tg = 0; tg < kTargets; tg++)
-        r[tg] = base[tg] + scan[tg][t] - e[tg];
+    for (int tg = 0; tg < kTargets; tg++) {
+        uint32_t off = 0;
+        for (int w = 0; w < wv; w++)
+            off += wsum[tg][w];
+        r[tg] = base[tg] + off + x[tg] - e[tg];
+    }
     uint8_t *tp = tier + (int64_t)seg * seglen;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
