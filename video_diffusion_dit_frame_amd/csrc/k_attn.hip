@@ -1294,21 +1294,22 @@ __global__ __launch_bounds__(128, 2) void k_attn_prefix(const AttnArgs A)
 // mean of its token scores, the average-branch draft logit s_ab = q_a . k_b /
 // sqrt(d), and counts the key region's n_b tokens with their mean value v_b.
 // The region's mean tiles gather into one term: t_b = fp32(s_ab log2 e),
-// M = max t_b, z = sum n_b 2^(t_b - M), c = sum n_b 2^(t_b - M) v_b, each
-// sum in key order.  One workgroup per (b, h) and kMeanRows consecutive
-// query regions; thread t owns channel t.  Per chunk of D key regions thread
-// t forms the weights of key region b0 + t for every row into LDS, then each
-// mean value is read once and applied to all the rows.
+// M = max t_b, z = sum n_b 2^(t_b - M), c = sum n_b 2^(t_b - M) v_b, c
+// summed in key order.  One 64-thread workgroup per (b, h) and kMeanRows
+// consecutive query regions; thread t owns D / 64 consecutive channels.  Per
+// chunk of 64 key regions thread t forms the weights of key region b0 + t
+// for every row into LDS, then each mean value is read once and applied to
+// all the rows.
 constexpr int kMeanRows = 16;
 
 template <int D>
-__global__ __launch_bounds__(D) void k_mean_agg(const uint8_t *__restrict__ tier, const double *__restrict__ la,
-                                                 const int32_t *__restrict__ nreg, int R,
-                                                 const float *__restrict__ vavg, float2 *__restrict__ magg,
-                                                 float *__restrict__ cagg)
+__global__ __launch_bounds__(64) void k_mean_agg(const uint8_t *__restrict__ tier, const double *__restrict__ la,
+                                                  const int32_t *__restrict__ nreg, int R,
+                                                  const float *__restrict__ vavg, float2 *__restrict__ magg,
+                                                  float *__restrict__ cagg)
 {
-    __shared__ __attribute__((aligned(16))) float wt[D][kMeanRows];
-    __shared__ float red[kMeanRows][D / 64];
+    constexpr int CPT = D / 64;   // channels per thread
+    __shared__ __attribute__((aligned(16))) float wt[64][kMeanRows];
     const int a0 = blockIdx.x * kMeanRows, bh = blockIdx.y, t = threadIdx.x;
     const int nq = min(kMeanRows, R - a0);
     const int64_t row0 = (int64_t)bh * R + a0;
@@ -1320,32 +1321,24 @@ __global__ __launch_bounds__(D) void k_mean_agg(const uint8_t *__restrict__ tier
         if (q < nq) {
             const uint8_t *trow = tier + (row0 + q) * R;
             const double *lrow = la + (row0 + q) * R;
-            for (int b = t; b < R; b += D)
+            for (int b = t; b < R; b += 64)
                 if (trow[b] == kMeanTier)
                     m = fmaxf(m, (float)(lrow[b] * kL2e));
         }
         for (int o = 32; o > 0; o >>= 1)
             m = fmaxf(m, __shfl_xor(m, o));
-        if ((t & 63) == 0)
-            red[q][t >> 6] = m;
+        M[q] = m;
     }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kMeanRows; q++) {
-        M[q] = red[q][0];
-#pragma unroll
-        for (int i = 1; i < D / 64; i++)
-            M[q] = fmaxf(M[q], red[q][i]);
-    }
-    __syncthreads();
-    float z[kMeanRows], c[kMeanRows];
+    float z[kMeanRows], c[kMeanRows][CPT];
 #pragma unroll
     for (int q = 0; q < kMeanRows; q++) {
         z[q] = 0.0f;
-        c[q] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < CPT; u++)
+            c[q][u] = 0.0f;
     }
-    const float *vhead = vavg + (int64_t)bh * R * D + t;
-    for (int b0 = 0; b0 < R; b0 += D) {
+    const float *vhead = vavg + (int64_t)bh * R * D + t * CPT;
+    for (int b0 = 0; b0 < R; b0 += 64) {
         const int b = b0 + t;
         const float nb = b < R ? (float)(nreg ? nreg[b] : kBlk) : 0.0f;
 #pragma unroll
@@ -1357,14 +1350,23 @@ __global__ __launch_bounds__(D) void k_mean_agg(const uint8_t *__restrict__ tier
             wt[t][q] = w;
         }
         __syncthreads();
-        const int n = min(D, R - b0);
+        const int n = min(64, R - b0);
 #pragma unroll 4
         for (int j = 0; j < n; j++) {
-            const float v = vhead[(int64_t)(b0 + j) * D];
+            float v[CPT];
+            if (CPT == 2) {
+                const float2 v2 = *reinterpret_cast<const float2 *>(vhead + (int64_t)(b0 + j) * D);
+                v[0] = v2.x;
+                v[CPT - 1] = v2.y;
+            } else {
+                v[0] = vhead[(int64_t)(b0 + j) * D];
+            }
             // an absent tile has weight 0 and leaves c unchanged (v is finite)
 #pragma unroll
             for (int q = 0; q < kMeanRows; q++)
-                c[q] = __builtin_fmaf(wt[j][q], v, c[q]);
+#pragma unroll
+                for (int u = 0; u < CPT; u++)
+                    c[q][u] = __builtin_fmaf(wt[j][q], v[u], c[q][u]);
         }
         __syncthreads();
     }
@@ -1373,25 +1375,17 @@ __global__ __launch_bounds__(D) void k_mean_agg(const uint8_t *__restrict__ tier
         float zz = z[q];
         for (int o = 32; o > 0; o >>= 1)
             zz += __shfl_xor(zz, o);
-        if ((t & 63) == 0)
-            red[q][t >> 6] = zz;
-    }
-    __syncthreads();
-    if (t == 0) {
-#pragma unroll
-        for (int q = 0; q < kMeanRows; q++) {
-            float zs = 0.0f;
-#pragma unroll
-            for (int i = 0; i < D / 64; i++)
-                zs += red[q][i];
-            if (q < nq)
-                magg[row0 + q] = make_float2(M[q], zs);
-        }
+        if (t == 0 && q < nq)
+            magg[row0 + q] = make_float2(M[q], zz);
     }
 #pragma unroll
     for (int q = 0; q < kMeanRows; q++)
-        if (q < nq)
-            cagg[(row0 + q) * D + t] = c[q];
+        if (q < nq) {
+            if (CPT == 2)
+                *reinterpret_cast<float2 *>(cagg + (row0 + q) * D + t * CPT) = make_float2(c[q][0], c[q][CPT - 1]);
+            else
+                cagg[(row0 + q) * D + t] = c[q][0];
+        }
 }
 
 // Merge of a prefix row's chunks (App. B.4's shared normalization across
@@ -1497,7 +1491,7 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
         const int32_t *nreg = L.ragged ? (const int32_t *)(ws + W.nreg) : nullptr;
         dim3 mg((L.R + kMeanRows - 1) / kMeanRows, L.BH);
         if (L.d == 128)
-            k_mean_agg<128><<<mg, 128, 0, st>>>((const uint8_t *)(ws + W.tier), (const double *)(ws + W.la),
+            k_mean_agg<128><<<mg, 64, 0, st>>>((const uint8_t *)(ws + W.tier), (const double *)(ws + W.la),
                                                 nreg, L.R, (const float *)(ws + W.vavg), (float2 *)(ws + W.magg),
                                                 (float *)(ws + W.cagg));
         else
