@@ -55,6 +55,11 @@ def lib():
         L.or_partition_bands.argtypes = [C.c_int, C.c_int, C.POINTER(C.c_int), P,
                                          C.POINTER(C.c_int64)]
         L.or_partition_bands.restype = C.c_int
+        L.or_partition_c.argtypes = [C.c_int, C.c_int, C.c_int, P, P]
+        L.or_partition_c.restype = C.c_int
+        L.or_partition_bands_c.argtypes = [C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int), P, P,
+                                           C.POINTER(C.c_int64)]
+        L.or_partition_bands_c.restype = C.c_int
         L.or_pool_head.argtypes = [P, C.c_int, P, C.c_int, P, P]
         L.or_exp_constants.argtypes = [P]
         L.or_exp.argtypes = [f64]
@@ -86,16 +91,9 @@ def lib():
         L.or_attention_trace.argtypes = [C.c_int] * 4 + [P, P, P, P, C.c_int, i64,
                                                          P, P, P, P, P, P, P, P]
         L.or_attention_trace.restype = i64
-        L.or_attention_kp.argtypes = [C.c_int] * 6 + [P, P, P, P, C.c_int, P, P, P]
-        L.or_attention_kp.restype = C.c_int
-        L.or_mfma_fp8_dot64.argtypes = [P, P, C.c_float]
-        L.or_mfma_fp8_dot64.restype = C.c_float
         L.or_attention_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P, C.c_int,
                                                        P, C.c_int, P, C.c_int, P, P, P]
         L.or_attention_pfx.restype = C.c_int
-        L.or_attention_kp_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P,
-                                                          P, C.c_int, P, C.c_int, P, P, P, P, P]
-        L.or_attention_kp_pfx.restype = C.c_int
         L.or_dense.argtypes = [C.c_int] * 4 + [P, P, P, C.c_int, P, P]
         L.or_dense.restype = C.c_int
         _lib = L
@@ -149,6 +147,29 @@ def partition_bands(Hv, Wv):
     if m < 0:
         raise ValueError("no partition of a %d x %d frame" % (Hv, Wv))
     return o.value, bands[:m].copy(), per.value
+
+
+def partition_c(Hv, Wv, cap):
+    """The same partition for block capacity cap: (tok [R_f, cap], nvalid)."""
+    Rf = -(-Hv * Wv // cap)
+    tok = np.empty((Rf, cap), np.int32)
+    nv = np.empty(Rf, np.int32)
+    if lib().or_partition_c(Hv, Wv, cap, _p(tok), _p(nv)) < 0:
+        raise ValueError("no partition of a %d x %d frame" % (Hv, Wv))
+    return tok, nv
+
+
+def partition_bands_c(Hv, Wv, cap):
+    """(orientation, band heights, pieces per band, total perimeter) for
+    block capacity cap."""
+    o = C.c_int()
+    per = C.c_int64()
+    bands = np.empty(Hv + Wv, np.int32)
+    pieces = np.empty(Hv + Wv, np.int32)
+    m = lib().or_partition_bands_c(Hv, Wv, cap, C.byref(o), _p(bands), _p(pieces), C.byref(per))
+    if m < 0:
+        raise ValueError("no partition of a %d x %d frame" % (Hv, Wv))
+    return o.value, bands[:m].copy(), pieces[:m].copy(), per.value
 
 
 # ---------------------------------------------------------------- draft
@@ -340,27 +361,6 @@ def attention(q, k, v, tier, F, Hv, Wv, qblocks=None):
     return out
 
 
-def attention_kp(q, k, v, tier, F, Hv, Wv, qblocks=None):
-    """Tiered attention with the weight-quantization decisions taken in the
-    kernel's precision.  Returns (out, allow), each laid out like
-    attention(); allow bounds the effect of undetermined decisions and of
-    the matrix-core accumulation of P V."""
-    q, k, v = _u16(q), _u16(k), _u16(v)
-    tier = np.ascontiguousarray(tier, np.uint8)
-    B, H, N, d = q.shape
-    R = regions(F, Hv, Wv)
-    assert tier.shape == (B, H, R, R)
-    nq = R if qblocks is None else len(qblocks)
-    qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
-    out = np.empty((B, H, nq, BLK, d), np.float64)
-    allow = np.empty((B, H, nq, BLK, d), np.float64)
-    lib().or_attention_kp(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), nq,
-                          None if qb is None else _p(qb), _p(out), _p(allow))
-    if qblocks is not None:
-        return out, allow
-    return _restore(out, F, Hv, Wv), _restore(allow, F, Hv, Wv)
-
-
 def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks):
     q, k, v, qp, kp, vp = (_u16(x) for x in (q, k, v, qp, kp, vp))
     tier = np.ascontiguousarray(tier, np.uint8)
@@ -409,37 +409,6 @@ def attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, pt=16, qbloc
     if qblocks is None:
         out = _restore(out, F, Hv, Wv)
     return out, outp
-
-
-def attention_kp_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, qblocks=None,
-                     prefix_rows=True):
-    """Kernel-precision variant of attention_pfx (prefix on the 16-bit path).
-    Returns (out, allow, outp, allowp)."""
-    q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R) = _pfx_args(
-        q, k, v, tier, qp, kp, vp, valid, qblocks)
-    npr, pr = _prows(prefix_rows, Lp)
-    out = np.empty((B, H, nq, BLK, d), np.float64)
-    allow = np.empty_like(out)
-    outp = np.empty((B, H, npr, d), np.float64) if prefix_rows is not False else None
-    allowp = np.empty((B, H, npr, d), np.float64) if prefix_rows is not False else None
-    rc = lib().or_attention_kp_pfx(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
-                                   _p(vp), None if va is None else _p(va), _p(tier), nq,
-                                   None if qb is None else _p(qb), npr,
-                                   None if pr is None else _p(pr), _p(out), _p(allow),
-                                   None if outp is None else _p(outp),
-                                   None if allowp is None else _p(allowp))
-    assert rc == 0
-    if qblocks is None:
-        out = _restore(out, F, Hv, Wv)
-        allow = _restore(allow, F, Hv, Wv)
-    return out, allow, outp, allowp
-
-
-def mfma_fp8_dot64(a_codes, b_codes, c_in=0.0) -> float:
-    a = np.ascontiguousarray(a_codes, np.uint8)
-    b = np.ascontiguousarray(b_codes, np.uint8)
-    assert a.size == 64 and b.size == 64
-    return float(lib().or_mfma_fp8_dot64(_p(a), _p(b), float(c_in)))
 
 
 def attention_trace(q, k, v, tier, F, Hv, Wv, u, cap=None):

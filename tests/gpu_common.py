@@ -71,23 +71,22 @@ def rel_l2(x, ref):
     return np.linalg.norm(x - ref) / den if den > 0 else np.linalg.norm(x)
 
 
-def check_kp(got, ref, allow, what=""):
-    """Parity against the kernel-precision oracle: rel-L2 <= 1e-3 overall and
-    every element within 5e-3 plus its allowance (undetermined decisions and
-    matrix-core accumulation bounds)."""
+def report(got, ref, what="", dense=None):
+    """Print the comparison with the oracle (and with dense fp64 attention on
+    sampled rows) before it is asserted, so a failing case still shows its
+    numbers."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    rl = rel_l2(got, ref)
-    diff = np.abs(got - ref)
-    excess = diff - (ATOL_MAX + allow)
-    ma = diff.max() if got.size else 0.0
-    assert rl <= RTOL_L2, "%s rel_l2=%.3e (max_abs %.3e)" % (what, rl, ma)
-    assert (excess <= 0).all(), "%s element beyond 5e-3 + allowance by %.3e (max_abs %.3e, rel_l2 %.3e)" % (
-        what, excess.max(), ma, rl)
-    return rl, ma
+    d = np.abs(got - ref)
+    msg = "%s: vs oracle rel_l2 %.3e max_abs %.3e" % (what, rel_l2(got, ref), d.max() if d.size else 0.0)
+    if dense is not None:
+        msg += " | vs dense fp64 rel_l2 %.3e" % rel_l2(np.asarray(dense[0], np.float64), dense[1])
+    print(msg, flush=True)
 
 
 def check_close(got, ref, what=""):
+    """Parity of the attention output with the oracle: rel-L2 <= 1e-3 over
+    the compared rows and every element within 5e-3."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     rl = rel_l2(got, ref)

@@ -1,8 +1,7 @@
 """GPU parity of block-mean tiles ([Triage] abstract: a skipped tile replaced
 by its block means; scored with the average-branch draft logit of
 DraftAttention2 Eq. 2 and weighted by the key region's token count) against
-the kernel-precision oracle (rel-L2 <= 1e-3, every element within 5e-3 plus
-its allowance): plans with skip replacement (tier maps bit-exact), tier maps
+the oracle (rel-L2 <= 1e-3, every element within 5e-3): plans with skip replacement (tier maps bit-exact), tier maps
 mixing block-mean tiles with every other tier, rows of block-mean tiles only,
 a ragged layout, a text prefix, and the Wan-14B-720p layer at full size.  The
 error against dense fp64 attention with and without skip replacement is
@@ -43,8 +42,8 @@ def test_plan_with_skip_replacement(c):
     tier = P.tier_map().cpu().numpy()
     assert np.array_equal(tier, ref_plan["tier"])
     assert (tier == MEAN).any()
-    r, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv)
-    rl, ma = G.check_kp(o, r, allow, "skip replacement")
+    r = O.attention(q, k, v, tier, F, Hv, Wv)
+    rl, ma = G.check_close(o, r, "skip replacement")
     # the same plan without replacement, both against dense fp64
     P0 = da2.Plan(da2.Layout.for_tensor(qd, F, Hv, Wv))
     P0.plan(qd, kd, hi, lo)
@@ -79,8 +78,8 @@ def test_mean_tier_families(c, family):
     P = da2.Plan(da2.Layout.for_tensor(qd, F, Hv, Wv))
     P.plan_from_tier_map(qd, kd, torch.from_numpy(tier).cuda())
     o = G.run_attention(P, qd, kd, v).cpu().numpy()
-    r, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv)
-    G.check_kp(o, r, allow, family)
+    r = O.attention(q, k, v, tier, F, Hv, Wv)
+    G.check_close(o, r, family)
 
 
 def test_mean_tiles_with_prefix():
@@ -91,9 +90,9 @@ def test_mean_tiles_with_prefix():
     R = O.regions(F, Hv, Wv)
     tier = _families(1, 2, R, 10)["all"]
     o, op, _ = run_prefixed(q, k, v, qp, kp, vp, F, Hv, Wv, tier=tier, valid=[77])
-    r, allow, rp, allowp = O.attention_kp_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, [77])
-    G.check_kp(o, r, allow, "mean + prefix video rows")
-    G.check_kp(op, rp, allowp, "mean + prefix prefix rows")
+    r, rp = O.attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, [77])
+    G.check_close(o, r, "mean + prefix video rows")
+    G.check_close(op, rp, "mean + prefix prefix rows")
 
 
 def test_skip_replacement_full_size():
@@ -122,9 +121,9 @@ def test_skip_replacement_full_size():
         qh, kh, vh = sl(q), sl(k), sl(v)
         ref_plan = O.plan(qh, kh, w.F, w.Hv, w.Wv, hi, lo, w.lam, skip_means=True)
         assert np.array_equal(tier[:, h:h + 1], ref_plan["tier"])
-        r, allow = O.attention_kp(qh, kh, vh, ref_plan["tier"], w.F, w.Hv, w.Wv, qblocks=regions)
+        r = O.attention(qh, kh, vh, ref_plan["tier"], w.F, w.Hv, w.Wv, qblocks=regions)
         got = o[0, h].index_select(0, torch.from_numpy(rows.astype(np.int64)).cuda()).cpu().numpy()
-        rl, ma = G.check_kp(got, r.reshape(-1, w.d), allow.reshape(-1, w.d), "wan14b skip replacement h%d" % h)
+        rl, ma = G.check_close(got, r.reshape(-1, w.d), "wan14b skip replacement h%d" % h)
         dn = O.dense(qh, kh, vh, rows[::16])[0, 0]
         print("wan14b-720p h%d skip replacement: rel_l2 %.2e vs oracle; %.3f vs dense fp64"
               % (h, rl, G.rel_l2(got[::16], dn)))

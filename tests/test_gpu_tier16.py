@@ -1,8 +1,7 @@
 """GPU parity of the 16-bit tier (the paper's 16-bit path, bf16 operands):
 three-level plans bit-exact against the oracle (draft keys, tier map with
 T16 / T8 / T4 quotas, schedule) and the phased attention with a 16-bit phase
-against the kernel-precision oracle (rel-L2 <= 1e-3, every element within
-5e-3 plus its allowance), for plan tier maps at the paper's allocations and
+against the oracle (rel-L2 <= 1e-3, every element within 5e-3), for plan tier maps at the paper's allocations and
 for synthetic tier families that exercise every phase order and boundary.
 """
 import numpy as np
@@ -53,11 +52,11 @@ def test_three_tier_plan_and_attention(which, budget):
     assert ((tier == 4).sum(axis=(2, 3)) == tk - t8c).all()
     sch = G.host(P.debug("SCHEDULE"), np.int32).reshape(tier.shape[:3] + (-1,))
     assert np.array_equal(sch, G.schedule_from_tier(tier))
-    r, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv)
-    rl, ma = G.check_kp(o, r, allow, "budget %s" % (budget,))
+    r = O.attention(q, k, v, tier, F, Hv, Wv)
+    rl, ma = G.check_close(o, r, "budget %s" % (budget,))
     rows = np.arange(0, q.shape[2], 97, dtype=np.int32)
     dn = O.dense(q, k, v, rows)
-    print("16/8/4 = %s: rel_l2 %.3e max_abs %.3e vs kernel-precision oracle; rel_l2 %.3e vs dense fp64"
+    print("16/8/4 = %s: rel_l2 %.3e max_abs %.3e vs oracle; rel_l2 %.3e vs dense fp64"
           % (budget, rl, ma, G.rel_l2(o[:, :, rows], dn)))
 
 
@@ -99,8 +98,8 @@ def test_tier16_families(which):
         assert np.array_equal(P.tier_map().cpu().numpy(), tier)
         sch = G.host(P.debug("SCHEDULE"), np.int32).reshape(tier.shape[:3] + (-1,))
         assert np.array_equal(sch, G.schedule_from_tier(tier)), name
-        ref, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv)
-        G.check_kp(got, ref, allow, name)
+        ref = O.attention(q, k, v, tier, F, Hv, Wv)
+        G.check_close(got, ref, name)
         if name == "empty_rows":
             dead = O.layout(F, Hv, Wv).reshape(R, 64)[::3].reshape(-1)
             assert (got[:, :, dead] == 0).all()
@@ -137,5 +136,5 @@ def test_tier16_single_region_and_two_frames(d, full, hi, lo):
         ref_plan = O.plan(q, k, F, Hv, Wv, hi, lo, full_bp=full)
         tier = P.tier_map().cpu().numpy()
         assert np.array_equal(tier, ref_plan["tier"])
-        ref, allow = O.attention_kp(q, k, v, tier, F, Hv, Wv)
-        G.check_kp(o, ref, allow, "F%d %dx%d d%d (%d,%d,%d)" % (F, Hv, Wv, d, full, hi, lo))
+        ref = O.attention(q, k, v, tier, F, Hv, Wv)
+        G.check_close(o, ref, "F%d %dx%d d%d (%d,%d,%d)" % (F, Hv, Wv, d, full, hi, lo))

@@ -39,11 +39,14 @@ def test_layout_restore_inverts_reorder(orc):
     assert np.array_equal(restored, X)
 
 
-def test_layout_rejects_frames_without_partition(orc):
-    """A frame whose every candidate leaves a region under 48 tokens (here a
-    single region of 5 x 7 = 35 tokens) has no partition."""
-    with pytest.raises(ValueError):
-        orc.layout(1, 5, 7)
+def test_small_frame_is_one_region(orc):
+    """A frame of fewer than 64 tokens is one region (R_f = 1) holding all of
+    them in raster order, the remaining slots padding (5 x 7 = 35 tokens)."""
+    perm = orc.layout(2, 5, 7)
+    assert perm.size == 2 * 64
+    for f in range(2):
+        blk = perm[64 * f:64 * f + 64]
+        assert np.array_equal(blk[:35], 35 * f + np.arange(35)) and (blk[35:] == -1).all()
 
 
 # ------------------------------------------------------------------ pooling

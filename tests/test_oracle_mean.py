@@ -10,7 +10,7 @@ tile replaced by its block means; DraftAttention2 Eq. 1-2 pooled means).
   full-precision tiles;
 * the mean-tile score is the mean of the tile's token scores;
 * the plan's skip replacement turns exactly the pairs outside the quotas
-  into block-mean tiles; kernel-precision agreement with the fp64 loop.
+  into block-mean tiles.
 """
 import math
 
@@ -111,12 +111,3 @@ def test_plan_skip_replacement(orc):
     base = orc.plan(q, k, F, Hv, Wv, 1500, 2500)["tier"]
     repl = orc.plan(q, k, F, Hv, Wv, 1500, 2500, skip_means=True)["tier"]
     assert np.array_equal(repl, np.where(base == 0, MEAN, base))
-    ex = orc.attention(q, k, v, repl, F, Hv, Wv)
-    kp, al = orc.attention_kp(q, k, v, repl, F, Hv, Wv)
-    assert (al >= 0).all()
-    assert np.linalg.norm(kp - ex) / np.linalg.norm(ex) <= 3e-3
-    # only mean and 16-bit tiles: no FP8/MXFP4 code decisions, fp32-level agreement
-    t = np.where(repl == 4, 16, np.where(repl == 8, 16, repl)).astype(np.uint8)
-    ex = orc.attention(q, k, v, t, F, Hv, Wv)
-    kp, al = orc.attention_kp(q, k, v, t, F, Hv, Wv)
-    assert np.linalg.norm(kp - ex) / np.linalg.norm(ex) <= 1e-5

@@ -1,22 +1,27 @@
 // da2_partition.cpp -- the spatial partition of a latent frame into regions of
 // at most C = 64 tokens (DraftAttention2, Sec. 3.3: a ragged 2D partition with
-// balanced token counts, the smallest total perimeter among candidate
-// partitions, the minimum number of blocks and less than one block of
-// padding per frame; App. C.2: R_f = ceil(H_v W_v / C)).
+// balanced token counts across regions, the smallest total perimeter among
+// candidate partitions, the minimum number of blocks and less than one block
+// of padding per frame; App. C.2: R_f = ceil(H_v W_v / C)).
 //
-// Candidate family: bands of whole rows (or of whole columns) across the
-// frame.  A band of h lines and length L is walked as a column snake --
-// column by column, down even columns and up odd ones -- and cut into
-// k = ceil(h L / C) consecutive pieces, the first (h L mod k) of them one
-// token larger than the rest; every piece is connected.  A candidate is
-// admissible when it gives exactly R_f regions and no piece is under 48
-// tokens.  Among admissible candidates the smallest total perimeter (region
-// edges against another region or the frame border) is taken; ties prefer
-// row bands, then fewer bands, then a smaller first band height (then the
-// next, and so on).  A dynamic program over (lines covered, regions used)
-// finds it.  Regions are numbered band by band and along the snake; each
-// region's tokens take its slots in raster order, the remaining slots are
-// padding.  For H_v, W_v multiples of 8 the result is the 8x8 grid.
+// Balance: with n = H_v W_v, q = floor(n / R_f) and r = n mod R_f, every
+// region holds q tokens or (when r > 0) q + 1.  Candidate family: bands of
+// whole rows (or of whole columns) across the frame.  A band of h lines and
+// length L is walked as a column snake -- column by column, down even
+// columns and up odd ones -- and cut into k consecutive pieces, the first
+// (hL - kq) of them q + 1 tokens long and the rest q; a band can take k
+// pieces when kq <= hL <= k(q + r?1:0).  Bands adding up to R_f pieces give
+// a balanced partition (one band of all lines always does).  The smallest
+// total perimeter (region edges against another region or the frame border)
+// is taken; ties prefer row bands, then fewer bands, then a smaller first
+// band height, then fewer pieces in it (then the next band, and so on).  A
+// dynamic program over (lines covered, regions used) finds it.  Regions are
+// numbered band by band and along the snake; each region's tokens take its
+// slots in raster order, the remaining slots are padding.  For H_v, W_v
+// multiples of 8 the result is the 8x8 grid.
+//
+// The attention kernels handle at most 16 padding slots per region, so a
+// frame whose regions hold fewer than 48 tokens (q < 48) is refused here.
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -27,16 +32,12 @@
 namespace da2 {
 namespace {
 
-struct Band {
-    int pieces;        // regions of the band
-    long perimeter;    // summed perimeter of its pieces, -1 when inadmissible
-};
-
-// Piece of each cell of an h x L band (cell (line, col) at line * L + col).
-std::vector<int> snake_pieces(int h, int L)
+// Piece of each cell of an h x L band cut into k pieces of q or q + 1 tokens
+// (cell (line, col) at line * L + col).
+std::vector<int> snake_pieces(int h, int L, int k, int q)
 {
-    const int n = h * L, k = (n + kBlk - 1) / kBlk, q = n / k, big = n % k;
-    std::vector<int> lab(n);
+    const int big = h * L - k * q;
+    std::vector<int> lab(h * L);
     int piece = 0, filled = 0;
     for (int col = 0; col < L; col++)
         for (int t = 0; t < h; t++) {
@@ -50,13 +51,9 @@ std::vector<int> snake_pieces(int h, int L)
     return lab;
 }
 
-Band measure_band(int h, int L)
+long band_perimeter(int h, int L, int k, int q)
 {
-    const int n = h * L, k = (n + kBlk - 1) / kBlk;
-    Band b{k, -1};
-    if (n / k < kMinFill)
-        return b;
-    const std::vector<int> lab = snake_pieces(h, L);
+    const std::vector<int> lab = snake_pieces(h, L, k, q);
     long per = 0;
     for (int line = 0; line < h; line++)
         for (int col = 0; col < L; col++) {
@@ -66,55 +63,67 @@ Band measure_band(int h, int L)
             per += (col == 0 || lab[line * L + col - 1] != me);
             per += (col == L - 1 || lab[line * L + col + 1] != me);
         }
-    b.perimeter = per;
-    return b;
+    return per;
 }
+
+struct BandChoice {
+    int h, k;
+    long perimeter;
+};
 
 struct Choice {
     long perimeter = -1;
-    int bands = 0;
-    std::vector<int> heights;
+    std::vector<int> heights, pieces;
 };
 
-// Best composition of E lines into bands of length L giving Rf regions.
-Choice best_composition(int E, int L, int Rf)
+// Best composition of E lines into bands of length L giving Rf regions of q
+// (or q + 1 when big) tokens.
+Choice best_composition(int E, int L, int Rf, int q, bool big)
 {
-    std::vector<Band> band(E + 1);
-    for (int h = 1; h <= E; h++)
-        band[h] = measure_band(h, L);
-    // state (e, r): lines e .. E-1 still to cover with r regions
+    // every band that can be cut: height h, pieces k, perimeter
+    std::vector<std::vector<BandChoice>> opts(E + 1);
+    for (int h = 1; h <= E; h++) {
+        const long n = (long)h * L;
+        const long kmax = n / q, kmin = big ? (n + q) / (q + 1) : kmax;
+        for (long k = kmin; k <= kmax && k <= Rf; k++)
+            if (k >= 1 && k * q <= n && n <= k * (q + (big ? 1 : 0)))
+                opts[h].push_back({h, (int)k, band_perimeter(h, L, (int)k, q)});
+    }
+    // state (e, t): lines e .. E-1 still to cover with t regions
     const size_t W = (size_t)Rf + 1;
     std::vector<long> cost((size_t)(E + 1) * W, -1);
-    std::vector<int> nb((size_t)(E + 1) * W, 0), first((size_t)(E + 1) * W, 0);
+    std::vector<int> nb((size_t)(E + 1) * W, 0), fh((size_t)(E + 1) * W, 0), fk((size_t)(E + 1) * W, 0);
     cost[(size_t)E * W] = 0;
     for (int e = E - 1; e >= 0; e--)
-        for (int r = 0; r <= Rf; r++) {
-            const size_t me = (size_t)e * W + r;
-            for (int h = 1; h <= E - e; h++) {
-                if (band[h].perimeter < 0 || band[h].pieces > r)
-                    continue;
-                const size_t rest = (size_t)(e + h) * W + (r - band[h].pieces);
-                if (cost[rest] < 0)
-                    continue;
-                const long c = band[h].perimeter + cost[rest];
-                const int n = nb[rest] + 1;
-                if (cost[me] < 0 || c < cost[me] || (c == cost[me] && n < nb[me])) {
-                    cost[me] = c;
-                    nb[me] = n;
-                    first[me] = h;
+        for (int t = 0; t <= Rf; t++) {
+            const size_t me = (size_t)e * W + t;
+            for (int h = 1; h <= E - e; h++)
+                for (const BandChoice &o : opts[h]) {
+                    if (o.k > t)
+                        continue;
+                    const size_t rest = (size_t)(e + h) * W + (t - o.k);
+                    if (cost[rest] < 0)
+                        continue;
+                    const long c = o.perimeter + cost[rest];
+                    const int n = nb[rest] + 1;
+                    if (cost[me] < 0 || c < cost[me] || (c == cost[me] && n < nb[me])) {
+                        cost[me] = c;
+                        nb[me] = n;
+                        fh[me] = h;
+                        fk[me] = o.k;
+                    }
                 }
-            }
         }
     Choice ch;
     if (cost[Rf] < 0)
         return ch;
     ch.perimeter = cost[Rf];
-    ch.bands = nb[Rf];
-    for (int e = 0, r = Rf; e < E;) {
-        const int h = first[(size_t)e * W + r];
-        ch.heights.push_back(h);
-        r -= band[h].pieces;
-        e += h;
+    for (int e = 0, t = Rf; e < E;) {
+        const size_t me = (size_t)e * W + t;
+        ch.heights.push_back(fh[me]);
+        ch.pieces.push_back(fk[me]);
+        t -= fk[me];
+        e += fh[me];
     }
     return ch;
 }
@@ -125,9 +134,12 @@ int partition_frame(int Hv, int Wv, int32_t *tok)
 {
     if (Hv < 1 || Wv < 1)
         return -1;
-    const int Rf = (Hv * Wv + kBlk - 1) / kBlk;
-    const Choice rows = best_composition(Hv, Wv, Rf);
-    const Choice cols = best_composition(Wv, Hv, Rf);
+    const int n = Hv * Wv, Rf = (n + kBlk - 1) / kBlk, q = n / Rf;
+    const bool big = n % Rf != 0;
+    if (q < kMinFill)
+        return -1;
+    const Choice rows = best_composition(Hv, Wv, Rf, q, big);
+    const Choice cols = best_composition(Wv, Hv, Rf, q, big);
     bool by_rows;
     if (rows.perimeter >= 0 && (cols.perimeter < 0 || rows.perimeter <= cols.perimeter))
         by_rows = true;
@@ -137,22 +149,23 @@ int partition_frame(int Hv, int Wv, int32_t *tok)
         return -1;
     const Choice &ch = by_rows ? rows : cols;
     const int L = by_rows ? Wv : Hv;
-    std::vector<int> region(Hv * Wv);
+    std::vector<int> region(n);
     int base = 0, line0 = 0;
-    for (int h : ch.heights) {
-        const std::vector<int> lab = snake_pieces(h, L);
+    for (size_t b = 0; b < ch.heights.size(); b++) {
+        const int h = ch.heights[b], k = ch.pieces[b];
+        const std::vector<int> lab = snake_pieces(h, L, k, q);
         for (int line = 0; line < h; line++)
             for (int col = 0; col < L; col++) {
                 const int y = by_rows ? line0 + line : col, x = by_rows ? col : line0 + line;
                 region[y * Wv + x] = base + lab[line * L + col];
             }
-        base += (h * L + kBlk - 1) / kBlk;
+        base += k;
         line0 += h;
     }
     std::vector<int> fill(Rf, 0);
     for (int i = 0; i < Rf * kBlk; i++)
         tok[i] = -1;
-    for (int t = 0; t < Hv * Wv; t++) {
+    for (int t = 0; t < n; t++) {
         const int r = region[t];
         tok[r * kBlk + fill[r]++] = t;   // raster order inside the region
     }
