@@ -22,9 +22,11 @@
  *   [Triage] "Triage: Skip, Skim, or Refine Attention Tiles in Video
  *           Diffusion Transformers" -- abstract (a skipped tile replaced by
  *           its block means).
- * Number formats: OCP 8-bit floating point (E4M3, "fn" variant: no inf,
- * max 448) and OCP Microscaling v1.0 (E2M1 elements, E8M0 scale, blocks of
- * 32), as fixed for this path in place of the paper's INT8/NVFP4 paths.
+ * Number formats: the 8-bit path takes INT8 for Q K^T ([DA2] App. C.1) with
+ * the uniform nearest-integer quantizer of App. B.2, and OCP 8-bit floating
+ * point (E4M3, "fn" variant: no inf, max 448) for P V; the 4-bit path takes
+ * OCP Microscaling v1.0 (E2M1 elements, E8M0 scale, blocks of 32) in place of
+ * the paper's NVFP4.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - token order of the input is (frame, y, x) raster;
@@ -41,11 +43,16 @@
  *   - row sums of the draft softmax are sequential over key regions;
  *   - ranking key is the bit pattern of fp32(A); ties by ascending pair index;
  *   - quotas: cumulative counts T16, T16+T8, T16+T8+T4, each rounded half up;
- *   - FP8 Q/K scale per 64-token block, FP8 V scale per channel over all
- *     tokens, MXFP4 groups along channels for Q/K and along keys for V;
- *   - attention weights are quantized per 64-key tile relative to the
- *     running max: 16-bit path bf16(w), FP8 e4m3(w * 2^8) * 2^-8, MXFP4 per
- *     32 keys; phases 16 -> 8 -> 4, then block-mean tiles (the tile's mean
+ *   - INT8 Q/K step amax/127 per 64-token block (code = nearest integer of
+ *     x 127/amax, ties to even, the product in fp32), FP8 V scale per channel
+ *     over all tokens, MXFP4 groups along channels for Q/K and along keys
+ *     for V;
+ *   - attention weights are taken per 64-key tile relative to the running
+ *     max: the 16-bit path keeps them unquantized (App. B's bound charges
+ *     quantization error to the 4- and 8-bit paths only), FP8
+ *     e4m3(w * 2^8) * 2^-8, MXFP4 per 32 keys (E8M0 exponent: the smallest
+ *     X with max w 2^-X <= 6); phases 16 -> 8 -> 4, then
+ *     block-mean tiles (the tile's mean
  *     score q_a . k_b / sqrt(d), its mean value, n_b keys);
  *   - a text prefix: video rows take the valid prefix keys first on the
  *     16-bit path, in tiles of 64; prefix rows take every valid prefix key and
@@ -706,11 +713,32 @@ int or_mx_exponent(double amax)
     return E;
 }
 
+/* E8M0 exponent of an MX block of attention weights: the smallest X with
+ * amax 2^-X <= 6, so the block maximum is never clipped -- the power-of-two
+ * counterpart of the NVFP4 block scale amax / 6 that [DA2] App. C.1 names
+ * for the probability-value product.  (The operand rule above clips block
+ * maxima in [6, 8) 2^X to 6; a weight block holding the running maximum has
+ * amax = 1 exactly, where that rule jumps from 1 to 0.75 under any rounding
+ * below 1.)  amax = 0 -> -127; clamped to the E8M0 range. */
+int or_mx_exponent_w(double amax)
+{
+    if (amax == 0.0)
+        return -127;
+    int e;
+    double m = frexp(amax, &e);           /* amax = m 2^e, m in [0.5, 1) */
+    int E = (e - 1) - 2 + (2.0 * m > 1.5 ? 1 : 0);
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
+    return E;
+}
+
 /* ------------------------------------------------------------------ */
 /* O8/O9 operand quantization: [DA2] Sec. 3.3 (fused quantization and   */
 /* reordering).  All outputs are in reordered token order pos.          */
-/*  Q/K FP8 : one fp32 scale per 64-token block: s = amax/448 (fp32     */
-/*            division), code = e4m3(fp32(x * (448/amax))).              */
+/*  Q/K INT8: one fp32 step per 64-token block: s = amax/127 (fp32      */
+/*            division), code = nearest integer (ties to even) of        */
+/*            fp32(x * fp32(127/amax)): App. B.2's uniform quantizer     */
+/*            with no clipping ([DA2] App. C.1: INT8 for Q K^T).         */
 /*  Q/K MX  : per token, per 32 channels: E8M0 + E2M1 codes of x 2^-E.  */
 /*  V FP8   : one fp32 scale per channel over all N tokens.             */
 /*  V MX    : per channel, per 32 consecutive keys of a block.          */
@@ -733,8 +761,33 @@ static float xat(const uint16_t *X, const int32_t *perm, size_t pos, int d, int 
     return perm[pos] < 0 ? 0.0f : bf16f(X[(size_t)perm[pos] * d + c]);
 }
 
+/* INT8 step of a Q/K block: amax/127; an all-zero block takes step 1 and
+ * zero codes. */
+static void int8_scale(float amax, float *s, float *inv)
+{
+    if (amax == 0.0f) {
+        *s = 1.0f;
+        *inv = 0.0f;
+    } else {
+        *s = amax / 127.0f;
+        *inv = 127.0f / amax;
+    }
+}
+
+/* Nearest integer of an fp32 value, ties to even, within [-127, 127]
+ * (|x| <= 127 up to the product's rounding, so the clamp never changes a
+ * code that the rounding alone would not). */
+static uint8_t int8_code(float x)
+{
+    double r = nearbyint((double)x);
+    if (r > 127.0) r = 127.0;
+    if (r < -127.0) r = -127.0;
+    return (uint8_t)(int8_t)r;
+}
+
 /* Q/K of one head over Np = R 64 reordered positions (padding slots hold
- * zeros): c8 [Np][d] codes, s8 [R] scales, c4 [Np][d], e4 [Np][d/32]. */
+ * zeros): c8 [Np][d] INT8 codes (two's complement bytes), s8 [R] steps,
+ * c4 [Np][d], e4 [Np][d/32]. */
 void or_quant_qk_head(const uint16_t *X, int Np, int d, const int32_t *perm,
                       uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
 {
@@ -747,13 +800,13 @@ void or_quant_qk_head(const uint16_t *X, int Np, int d, const int32_t *perm,
                 if (v > amax) amax = v;
             }
         float s, inv;
-        fp8_scale(amax, &s, &inv);
+        int8_scale(amax, &s, &inv);
         s8[a] = s;
         for (int i = 0; i < OR_BLK; i++)
             for (int c = 0; c < d; c++) {
                 float v = xat(X, perm, (size_t)a * OR_BLK + i, d, c);
                 float prod = v * inv;
-                c8[((size_t)a * OR_BLK + i) * d + c] = or_e4m3_encode((double)prod);
+                c8[((size_t)a * OR_BLK + i) * d + c] = int8_code(prod);
             }
     }
     for (int pos = 0; pos < Np; pos++)
@@ -859,8 +912,9 @@ int or_quant_v(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
 /* retained key return zero).                                           */
 /* Phases in descending precision: tier 32 (oracle-only: unquantized    */
 /* operands and weights, for the invariants), tier 16 (the 16-bit path: */
-/* the bf16 inputs as they are, weights rounded to bf16 for P V), tier  */
-/* 8 (FP8), tier 4 (MXFP4); tiles ascending inside a phase; running max */
+/* the bf16 inputs as they are, weights unquantized), tier 8 (INT8      */
+/* Q K^T, FP8 P V), tier 4 (MXFP4); tiles ascending inside a phase;     */
+/* running max                                                          */
 /* updated once per 64-key tile.                                        */
 /* ------------------------------------------------------------------ */
 typedef struct {
@@ -868,9 +922,9 @@ typedef struct {
     const int32_t *perm;
     int32_t *nv;             /* valid tokens of each region [R] (slots 0 .. nv-1) */
     double *qf, *kf, *vf;    /* unquantized, reordered [N][d]; padding rows 0 */
-    double *q8, *k8, *v8;    /* FP8 dequantized */
+    double *q8, *k8, *v8;    /* 8-bit path dequantized: INT8 Q/K, FP8 V */
     double *q4, *k4, *v4;    /* MXFP4 dequantized */
-    uint8_t *c8q, *c8k;      /* FP8 codes of Q and K, reordered [N][d] */
+    uint8_t *c8q, *c8k;      /* INT8 codes of Q and K, reordered [N][d] */
     float *s8q, *s8k;        /* their per-block scales [R] */
     double *qa, *ka, *va;    /* region means over the valid tokens [R][d] */
 } head_ops;
@@ -915,7 +969,7 @@ static void head_ops_build(head_ops *h, const uint16_t *q, const uint16_t *k,
             for (int pos = 0; pos < N; pos++)
                 for (int c = 0; c < d; c++) {
                     size_t i = (size_t)pos * d + c;
-                    d8[t][i] = or_e4m3_value(c8[i]) * (double)s8[pos / OR_BLK];
+                    d8[t][i] = (double)(int8_t)c8[i] * (double)s8[pos / OR_BLK];
                     d4[t][i] = ldexp(or_e2m1_value(c4[i]), (int)e4[(size_t)pos * (d / 32) + c / 32] - 127);
                 }
         } else {
@@ -965,24 +1019,77 @@ static double mean_logit(const head_ops *h, int a, int b)
     return fma_chain(h->qa + (size_t)a * h->d, h->ka + (size_t)b * h->d, h->d) / sqrt((double)h->d);
 }
 
-/* Weight quantizers for one 64-key tile, w[64] in key order. */
-static void quant_weights(int tier, const double *w, double *wq)
+/* Relative precision band of a weight code decision.  The GPU path forms
+ * each weight in fp32 from fp32 logits; its relative error stays below
+ * 2^-16 wherever the weight is above 2^-60 (log2-domain error about
+ * (|t| + |S c|) 2^-23 for |t|, |S c| <= 60, plus one ulp of exp2).  A code
+ * whose value changes when w moves by that band has two correct results. */
+#define OR_AMB_REL 0x1p-16
+
+/* Alternative of one element's code inside the band: the largest change of
+ * the quantized value over w (1 - delta) and w (1 + delta). */
+static double band_alt_e4m3(double x, double q)
 {
+    double a = or_e4m3_value(or_e4m3_encode(x * (1.0 - OR_AMB_REL)));
+    double b = or_e4m3_value(or_e4m3_encode(x * (1.0 + OR_AMB_REL)));
+    double da = fabs(a - q), db = fabs(b - q);
+    return da > db ? da : db;
+}
+
+static double band_alt_e2m1(double x, double q)
+{
+    double a = or_e2m1_value(or_e2m1_encode(x * (1.0 - OR_AMB_REL)));
+    double b = or_e2m1_value(or_e2m1_encode(x * (1.0 + OR_AMB_REL)));
+    double da = fabs(a - q), db = fabs(b - q);
+    return da > db ? da : db;
+}
+
+/* Weight quantizers for one 64-key tile, w[64] in key order.  wa (may be
+ * NULL) receives, per key, how far its quantized weight can move when the
+ * decisions it depends on are taken anywhere in the precision band: its own
+ * code, and for MXFP4 also the block exponent. */
+static void quant_weights(int tier, const double *w, double *wq, double *wa)
+{
+    if (wa)
+        for (int j = 0; j < OR_BLK; j++) wa[j] = 0.0;
     if (tier == 32) {
         for (int j = 0; j < OR_BLK; j++) wq[j] = w[j];
     } else if (tier == 16) {
-        for (int j = 0; j < OR_BLK; j++) wq[j] = or_bf16_round(w[j]);
+        /* the 16-bit path: weights unquantized (App. B's error bound has no
+         * term for it) */
+        for (int j = 0; j < OR_BLK; j++) wq[j] = w[j];
     } else if (tier == 8) {
-        for (int j = 0; j < OR_BLK; j++)
-            wq[j] = ldexp(or_e4m3_value(or_e4m3_encode(ldexp(w[j], 8))), -8);
+        for (int j = 0; j < OR_BLK; j++) {
+            double x = ldexp(w[j], 8), q = or_e4m3_value(or_e4m3_encode(x));
+            wq[j] = ldexp(q, -8);
+            if (wa)
+                wa[j] = ldexp(band_alt_e4m3(x, q), -8);
+        }
     } else {
         for (int g = 0; g < 2; g++) {
             double amax = 0.0;
             for (int j = 0; j < 32; j++)
                 if (fabs(w[32 * g + j]) > amax) amax = fabs(w[32 * g + j]);
-            int E = or_mx_exponent(amax);
-            for (int j = 0; j < 32; j++)
-                wq[32 * g + j] = ldexp(or_e2m1_value(or_e2m1_encode(ldexp(w[32 * g + j], -E))), E);
+            int E = or_mx_exponent_w(amax);
+            int Elo = or_mx_exponent_w(amax * (1.0 - OR_AMB_REL));
+            int Ehi = or_mx_exponent_w(amax * (1.0 + OR_AMB_REL));
+            for (int j = 0; j < 32; j++) {
+                double x = ldexp(w[32 * g + j], -E), q = or_e2m1_value(or_e2m1_encode(x));
+                wq[32 * g + j] = ldexp(q, E);
+                if (!wa)
+                    continue;
+                double d = ldexp(band_alt_e2m1(x, q), E);
+                int Ea[2] = {Elo, Ehi};
+                for (int t = 0; t < 2; t++) {
+                    if (Ea[t] == E)
+                        continue;
+                    double xa = ldexp(w[32 * g + j], -Ea[t]);
+                    double qa = ldexp(or_e2m1_value(or_e2m1_encode(xa)), Ea[t]);
+                    double da = fabs(qa - wq[32 * g + j]) + ldexp(band_alt_e2m1(xa, ldexp(qa, -Ea[t])), Ea[t]);
+                    if (da > d) d = da;
+                }
+                wa[32 * g + j] = d;
+            }
         }
     }
 }
@@ -999,10 +1106,13 @@ typedef struct {
 } row_trace;
 
 /* Online-softmax state of one query row (App. B.4): running max m, sum Z
- * of the unquantized weights, unnormalised output acc[d]. */
+ * of the unquantized weights, unnormalised output acc[d]; amb[d] (NULL when
+ * not asked for) the same sum over the band movements wa of the weights
+ * times |v|. */
 typedef struct {
     double m, Z;
     double *acc;
+    double *amb;
 } row_acc;
 
 /* One tile of up to 64 keys at tier p: key j < nk has operand rows
@@ -1013,6 +1123,7 @@ typedef struct {
 static void tile_exact(row_acc *st, int d, int p, const double *qu, const double *kt,
                        const double *vt, int nk, double *s, double *w, double *wq)
 {
+    double wa[OR_BLK];
     double inv_sqrt_d = 1.0 / sqrt((double)d);
     double tmax = -INFINITY;
     for (int j = 0; j < OR_BLK; j++) {
@@ -1031,15 +1142,21 @@ static void tile_exact(row_acc *st, int d, int p, const double *qu, const double
     st->Z *= alpha;
     for (int c = 0; c < d; c++)
         st->acc[c] *= alpha;
+    if (st->amb)
+        for (int c = 0; c < d; c++)
+            st->amb[c] *= alpha;
     for (int j = 0; j < OR_BLK; j++) {
         w[j] = j < nk ? exp(s[j] - mn) : 0.0;
         st->Z += w[j];
     }
-    quant_weights(p, w, wq);
+    quant_weights(p, w, wq, st->amb ? wa : NULL);
     for (int j = 0; j < nk; j++) {
         const double *vv = vt + (size_t)j * d;
         for (int c = 0; c < d; c++)
             st->acc[c] += wq[j] * vv[c];
+        if (st->amb)
+            for (int c = 0; c < d; c++)
+                st->amb[c] += wa[j] * fabs(vv[c]);
     }
     st->m = mn;
 }
@@ -1077,19 +1194,22 @@ static void prefix_segment(row_acc *st, int d, const prefix_ops *px, const doubl
     }
 }
 
-static void finish_row(const row_acc *st, int d, double *out)
+static void finish_row(const row_acc *st, int d, double *out, double *amb)
 {
     for (int c = 0; c < d; c++)
         out[c] = st->Z > 0.0 ? st->acc[c] / st->Z : 0.0;
+    if (amb)
+        for (int c = 0; c < d; c++)
+            amb[c] = st->Z > 0.0 ? st->amb[c] / st->Z : 0.0;
 }
 
 /* Video query row u (reordered position): the prefix segment (if any), then
  * the phases in descending precision over the kept video tiles. */
 static void attention_row(const head_ops *h, const prefix_ops *px, const uint8_t *tier_row,
-                          int u, double *out, row_trace *tr)
+                          int u, double *out, row_trace *tr, double *amb)
 {
     int d = h->d, R = h->R;
-    row_acc st = {-INFINITY, 0.0, calloc(d, sizeof(double))};
+    row_acc st = {-INFINITY, 0.0, calloc(d, sizeof(double)), amb ? calloc(d, sizeof(double)) : NULL};
     double s[OR_BLK], w[OR_BLK], wq[OR_BLK];
     static const int phases[4] = {32, 16, 8, 4};
     const int a = u / OR_BLK;
@@ -1127,16 +1247,20 @@ static void attention_row(const head_ops *h, const prefix_ops *px, const uint8_t
         st.Z *= alpha;
         for (int c = 0; c < d; c++)
             st.acc[c] *= alpha;
+        if (st.amb)
+            for (int c = 0; c < d; c++)
+                st.amb[c] *= alpha;
         double w = (double)h->nv[b] * exp(sb - mn);
         st.Z += w;
         for (int c = 0; c < d; c++)
             st.acc[c] += w * h->va[(size_t)b * d + c];
         st.m = mn;
     }
-    finish_row(&st, d, out);
+    finish_row(&st, d, out, amb);
     if (tr)
         tr->Z = st.Z;
     free(st.acc);
+    free(st.amb);
 }
 
 /* Prefix query rows (App. C.1: non-sparse attention).  Their key sequence
@@ -1175,7 +1299,7 @@ static void attention_prefix_row(const head_ops *h, const prefix_ops *px, int i,
     double *mc = malloc(sizeof(double) * nc), *zc = malloc(sizeof(double) * nc);
     double *ac = calloc((size_t)nc * d, sizeof(double));
     for (int c = 0; c < nc; c++) {
-        row_acc st = {-INFINITY, 0.0, ac + (size_t)c * d};
+        row_acc st = {-INFINITY, 0.0, ac + (size_t)c * d, NULL};
         for (int t = c * OR_PCHUNK; t < T && t < (c + 1) * OR_PCHUNK; t++) {
             const double *kt, *vt;
             int nk = prefix_row_tile(h, px, t, &kt, &vt);
@@ -1208,7 +1332,7 @@ static void attention_prefix_row(const head_ops *h, const prefix_ops *px, int i,
  * perm[qblocks[j]*64 + i] (restore is done by the caller's indexing). */
 int or_attention(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
                  const uint16_t *k, const uint16_t *v, const uint8_t *tier, int nqb,
-                 const int32_t *qblocks, double *out)
+                 const int32_t *qblocks, double *out, double *amb)
 {
     int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
     if (R < 0) return -1;
@@ -1225,12 +1349,15 @@ int or_attention(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
         for (int r = 0; r < nqb * OR_BLK; r++) {
             int j = r / OR_BLK, i = r % OR_BLK;
             int a = qblocks ? qblocks[j] : j;
-            double *o = out + (((size_t)bh * nqb + j) * OR_BLK + i) * d;
+            size_t ro = (((size_t)bh * nqb + j) * OR_BLK + i) * d;
+            double *o = out + ro;
             if (i >= h.nv[a]) {   /* padding slot: no query */
                 memset(o, 0, sizeof(double) * d);
+                if (amb)
+                    memset(amb + ro, 0, sizeof(double) * d);
                 continue;
             }
-            attention_row(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i, o, NULL);
+            attention_row(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i, o, NULL, amb ? amb + ro : NULL);
         }
         head_ops_free(&h);
     }
@@ -1253,7 +1380,7 @@ int64_t or_attention_trace(int F, int Hv, int Wv, int d, const uint16_t *q,
     head_ops h;
     head_ops_build(&h, q, k, v, N, Np, d, perm);
     row_trace tr = {cap, 0, key, tr_tier, s, w, wq, m, 0.0};
-    attention_row(&h, NULL, tier + (size_t)(u / OR_BLK) * R, u, out, &tr);
+    attention_row(&h, NULL, tier + (size_t)(u / OR_BLK) * R, u, out, &tr, NULL);
     *Z = tr.Z;
     head_ops_free(&h);
     free(perm);
@@ -1300,7 +1427,7 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
                       const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
                       const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
                       const uint8_t *tier, int nqb, const int32_t *qblocks, int nprow,
-                      const int32_t *prows, double *out, double *outp)
+                      const int32_t *prows, double *out, double *outp, double *amb)
 {
     int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
     if (pt != 16 && pt != 32) return -1;
@@ -1323,9 +1450,11 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
             size_t o = (((size_t)bh * nqb + j) * OR_BLK + i) * d;
             if (i >= h.nv[a]) {   /* padding slot: no query */
                 memset(out + o, 0, sizeof(double) * d);
+                if (amb)
+                    memset(amb + o, 0, sizeof(double) * d);
                 continue;
             }
-            attention_row(&h, &px, tm + (size_t)a * R, a * OR_BLK + i, out + o, NULL);
+            attention_row(&h, &px, tm + (size_t)a * R, a * OR_BLK + i, out + o, NULL, amb ? amb + o : NULL);
         }
         if (outp) {
             int n = prows ? nprow : Lp;
@@ -1347,10 +1476,10 @@ int or_attention_pfx(int B, int H, int F, int Hv, int Wv, int d, const uint16_t 
                      const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
                      const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
                      const uint8_t *tier, int nqb, const int32_t *qblocks, int nprow,
-                     const int32_t *prows, double *out, double *outp)
+                     const int32_t *prows, double *out, double *outp, double *amb)
 {
     return pfx_common(B, H, F, Hv, Wv, d, q, k, v, Lp, qp, kp, vp, valid, pt, tier, nqb, qblocks,
-                      nprow, prows, out, outp);
+                      nprow, prows, out, outp, amb);
 }
 
 /* ------------------------------------------------------------------ */

@@ -82,17 +82,19 @@ def lib():
         L.or_e2m1_encode.restype = C.c_uint8
         L.or_mx_exponent.argtypes = [f64]
         L.or_mx_exponent.restype = C.c_int
+        L.or_mx_exponent_w.argtypes = [f64]
+        L.or_mx_exponent_w.restype = C.c_int
         L.or_quant_qk.argtypes = [C.c_int] * 6 + [P, P, P, P, P]
         L.or_quant_qk.restype = C.c_int
         L.or_quant_v.argtypes = [C.c_int] * 6 + [P, P, P, P, P]
         L.or_quant_v.restype = C.c_int
-        L.or_attention.argtypes = [C.c_int] * 6 + [P, P, P, P, C.c_int, P, P]
+        L.or_attention.argtypes = [C.c_int] * 6 + [P, P, P, P, C.c_int, P, P, P]
         L.or_attention.restype = C.c_int
         L.or_attention_trace.argtypes = [C.c_int] * 4 + [P, P, P, P, C.c_int, i64,
                                                          P, P, P, P, P, P, P, P]
         L.or_attention_trace.restype = i64
         L.or_attention_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P, C.c_int,
-                                                       P, C.c_int, P, C.c_int, P, P, P]
+                                                       P, C.c_int, P, C.c_int, P, P, P, P]
         L.or_attention_pfx.restype = C.c_int
         L.or_dense.argtypes = [C.c_int] * 4 + [P, P, P, C.c_int, P, P]
         L.or_dense.restype = C.c_int
@@ -301,6 +303,11 @@ def mx_exponent(amax: float) -> int:
     return lib().or_mx_exponent(float(amax))
 
 
+def mx_exponent_w(amax: float) -> int:
+    """E8M0 exponent of a block of attention weights (no clipping)."""
+    return lib().or_mx_exponent_w(float(amax))
+
+
 def quant_qk(X, F, Hv, Wv):
     """-> dict(c8 [B,H,Np,d] u8, s8 [B,H,R] f32, c4 [B,H,Np,d] u8, e4 [B,H,Np,d/32] u8),
     position axis in reordered order (Np = 64 R, padding slots included)."""
@@ -341,24 +348,28 @@ def _restore(x, F, Hv, Wv):
     return full
 
 
-def attention(q, k, v, tier, F, Hv, Wv, qblocks=None):
+def attention(q, k, v, tier, F, Hv, Wv, qblocks=None, amb=False):
     """Tiered attention.  qblocks=None: all rows, returned [B,H,N,d] in original
     token order.  Otherwise [B,H,len(qblocks),64,d]; row (j,i) is original
-    token perm[qblocks[j]*64+i] (zero for a padding slot)."""
+    token perm[qblocks[j]*64+i] (zero for a padding slot).  amb=True also
+    returns, laid out alike, the bound on how far each output can move when
+    every weight-code decision inside the precision band (OR_AMB_REL) is
+    taken either way: (out, amb)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     tier = np.ascontiguousarray(tier, np.uint8)
     B, H, N, d = q.shape
     R = regions(F, Hv, Wv)
     assert tier.shape == (B, H, R, R)
-    if qblocks is None:
-        out = np.empty((B, H, R, BLK, d), np.float64)
-        lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), R, None, _p(out))
-        return _restore(out, F, Hv, Wv)
-    qb = np.ascontiguousarray(qblocks, np.int32)
-    out = np.empty((B, H, len(qb), BLK, d), np.float64)
-    lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), len(qb), _p(qb),
-                       _p(out))
-    return out
+    qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
+    nq = R if qb is None else len(qb)
+    out = np.empty((B, H, nq, BLK, d), np.float64)
+    ab = np.empty((B, H, nq, BLK, d), np.float64) if amb else None
+    lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), nq,
+                       None if qb is None else _p(qb), _p(out), None if ab is None else _p(ab))
+    if qb is None:
+        out = _restore(out, F, Hv, Wv)
+        ab = None if ab is None else _restore(ab, F, Hv, Wv)
+    return (out, ab) if amb else out
 
 
 def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks):
@@ -388,27 +399,31 @@ def _prows(prefix_rows, Lp):
 
 
 def attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, pt=16, qblocks=None,
-                  prefix_rows=True):
+                  prefix_rows=True, amb=False):
     """Tiered attention with a text prefix (App. C.1).  q, k, v: video
     [B,H,N,d]; qp, kp, vp: prefix [B,H,Lp,d]; valid: [B] valid prefix keys
     (None: all).  pt: precision of the prefix interactions (16 or 32).
     prefix_rows: True (all), False (none) or the prefix query rows wanted.
     Returns (video rows laid out as attention(), prefix rows [B,H,np,d] or
-    None)."""
+    None), and with amb=True also the video rows' band bound (prefix rows
+    take only unquantized weights)."""
     q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R) = _pfx_args(
         q, k, v, tier, qp, kp, vp, valid, qblocks)
     npr, pr = _prows(prefix_rows, Lp)
     out = np.empty((B, H, nq, BLK, d), np.float64)
     outp = np.empty((B, H, npr, d), np.float64) if prefix_rows is not False else None
+    ab = np.empty((B, H, nq, BLK, d), np.float64) if amb else None
     rc = lib().or_attention_pfx(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
                                 _p(vp), None if va is None else _p(va), pt, _p(tier), nq,
                                 None if qb is None else _p(qb), npr,
                                 None if pr is None else _p(pr), _p(out),
-                                None if outp is None else _p(outp))
+                                None if outp is None else _p(outp),
+                                None if ab is None else _p(ab))
     assert rc == 0
     if qblocks is None:
         out = _restore(out, F, Hv, Wv)
-    return out, outp
+        ab = None if ab is None else _restore(ab, F, Hv, Wv)
+    return (out, outp, ab) if amb else (out, outp)
 
 
 def attention_trace(q, k, v, tier, F, Hv, Wv, u, cap=None):

@@ -133,7 +133,7 @@ def _deq(orc, q, k, v):
     oq, ok, ov = orc.quant_qk(q, F, HV, WV), orc.quant_qk(k, F, HV, WV), orc.quant_v(v, F, HV, WV)
     out = {}
     for name, o in (("q", oq), ("k", ok)):
-        out[name + "8"] = val8[o["c8"][0, 0]] * np.repeat(o["s8"][0, 0], 64)[:, None]
+        out[name + "8"] = o["c8"][0, 0].view(np.int8).astype(np.float64) * np.repeat(o["s8"][0, 0], 64)[:, None]
         out[name + "4"] = val4[o["c4"][0, 0]] * np.exp2(np.repeat(o["e4"][0, 0].astype(np.int64) - 127, 32, axis=1))
     out["v8"] = val8[ov["c8"][0, 0]] * ov["s8"][0, 0][None, :]
     e = ov["e4"][0, 0].astype(np.int64) - 127  # [R,2,d]
@@ -178,25 +178,18 @@ def test_quantized_tile_loop_from_trace(orc, qkv, u):
     val8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
     for t in range(w.shape[0]):
         if p[t * 64] == 16:
-            # bfloat16 of each weight (w is exactly an fp32 value here only by
-            # chance, so compare against the nearest of the two bf16
-            # neighbours found by bracketing, ties to the even mantissa)
-            m_, e_ = np.frexp(w[t])
-            lo = np.floor(m_ * 256.0)
-            hi_ = lo + 1.0
-            d_lo, d_hi = m_ * 256.0 - lo, hi_ - m_ * 256.0
-            pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
-            ref = np.where(pick_hi, hi_, lo) * np.exp2(e_ - 8.0)
-            sub = w[t] < 2.0 ** -126  # bf16 subnormals: quantum 2^-133
-            ref = np.where(sub, np.rint(w[t] * 2.0 ** 133) * 2.0 ** -133, ref)
-            assert np.array_equal(wq[t], ref)
+            # the 16-bit path does not quantize its weights
+            assert np.array_equal(wq[t], w[t])
         elif p[t * 64] == 8:
             codes = brute_nearest(w[t] * 256.0, val8[:127])
             assert np.array_equal(wq[t], val8[codes] / 256.0)
         else:
             for g in range(2):
                 wg = w[t, 32 * g:32 * g + 32]
-                E = int(np.clip(np.frexp(wg.max())[1] - 1 - 2, -127, 127))
+                # smallest E with max w 2^-E <= 6 (no block maximum clipped)
+                E = -127
+                while wg.max() * 2.0 ** -E > 6.0:
+                    E += 1
                 codes = brute_nearest(wg * 2.0 ** -E, E2M1_POS)
                 assert np.array_equal(wq[t, 32 * g:32 * g + 32], E2M1_POS[codes] * 2.0 ** E)
     # shared normalization (B.3/B.4): every weight rescaled to the final max
@@ -254,3 +247,83 @@ def test_zero_skip_error_within_quantization_envelope(orc, qkv):
                    + np.linalg.norm((wr[:, None] * (V - Vf)).sum(0))
                    + np.linalg.norm(((wqr - wr)[:, None] * V).sum(0))) / Z
             assert np.linalg.norm(tr["out"] - Od) <= env * (1 + 1e-9) + 1e-13
+
+
+AMB_REL = 2.0 ** -16
+
+
+def _band_move(x, q, table):
+    """Largest change of the nearest-code value of x over x (1 -+ delta);
+    table: the format's non-negative values (brute-force nearest)."""
+    a = table[brute_nearest(np.array([x * (1 - AMB_REL)]), table)[0]]
+    b = table[brute_nearest(np.array([x * (1 + AMB_REL)]), table)[0]]
+    return max(abs(a - q), abs(b - q))
+
+
+def _w_exponent(a):
+    X = -127
+    while a * 2.0 ** -X > 6.0:
+        X += 1
+    return X
+
+
+@pytest.mark.parametrize("seed,u", [(5, 207), (200, 214), (200, 5), (451, 97)])
+def test_band_bound_from_trace(orc, qkv, seed, u):
+    """The band bound (how far an output can move when every weight code
+    within the kernel's precision band goes either way) recomputed from the
+    trace with brute-force code searches: per key the largest move of its
+    quantized weight over w (1 -+ 2^-16), for MXFP4 also under the block
+    exponents of max w (1 -+ 2^-16); summed with |v| at the final max."""
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    rng = np.random.default_rng(seed)
+    tier = rng.choice(np.array([0, 4, 8, 16], np.uint8), size=(1, 2, R, R), p=[0.3, 0.3, 0.2, 0.2])
+    tr = orc.attention_trace(q[0, 0], k[0, 0], v[0, 0], tier[0, 0], F, HV, WV, u)
+    out, amb = orc.attention(q, k, v, tier, F, HV, WV, qblocks=[u // 64], amb=True)
+    ops = _deq(orc, q, k, v)
+    perm = orc.layout(F, HV, WV)
+    Vf = f64(v[0, 0])[perm]
+    val8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()[:127]
+    w = tr["w"].reshape(-1, 64)
+    p = tr["tier"].reshape(-1, 64)[:, 0]
+    move = np.zeros_like(w)
+    for t in range(w.shape[0]):
+        if p[t] == 8:
+            for j in range(64):
+                x = w[t, j] * 256
+                qv = val8[brute_nearest(np.array([x]), val8)[0]]
+                move[t, j] = _band_move(x, qv, val8) / 256
+        elif p[t] == 4:
+            for g in range(2):
+                wg = w[t, 32 * g:32 * g + 32]
+                E = _w_exponent(wg.max())
+                alts = {_w_exponent(wg.max() * (1 - AMB_REL)), _w_exponent(wg.max() * (1 + AMB_REL))} - {E}
+                for j in range(32):
+                    x = wg[j] * 2.0 ** -E
+                    qv = E2M1_POS[brute_nearest(np.array([x]), E2M1_POS)[0]]
+                    m = _band_move(x, qv, E2M1_POS) * 2.0 ** E
+                    for Ea in alts:
+                        xa = wg[j] * 2.0 ** -Ea
+                        qa = E2M1_POS[brute_nearest(np.array([xa]), E2M1_POS)[0]]
+                        m = max(m, abs(qa * 2.0 ** Ea - qv * 2.0 ** E) + _band_move(xa, qa, E2M1_POS) * 2.0 ** Ea)
+                    move[t, 32 * g + j] = m
+    keys = tr["key"]
+    V = np.where(tr["tier"][:, None] == 8, ops["v8"][keys],
+                 np.where(tr["tier"][:, None] == 4, ops["v4"][keys], Vf[keys]))
+    scale = np.exp(tr["m"] - tr["m"][-1])
+    want = ((move.reshape(-1) * scale)[:, None] * np.abs(V)).sum(axis=0) / tr["Z"]
+    got = amb[0, 0, 0, u % 64]
+    assert np.allclose(got, want, rtol=1e-9, atol=1e-15)
+    assert np.array_equal(out[0, 0, 0, u % 64], tr["out"])
+    # rows chosen to hold an ambiguous decision, and one that holds none
+    assert (got.max() > 0) == (u != 5)
+
+
+def test_band_bound_zero_without_quantized_weights(orc, qkv):
+    """16-bit, full-precision and skipped tiles quantize no weight."""
+    q, k, v = qkv
+    R = q.shape[2] // 64
+    rng = np.random.default_rng(3)
+    tier = rng.choice(np.array([0, 16, 32], np.uint8), size=(1, 2, R, R))
+    _, amb = orc.attention(q, k, v, tier, F, HV, WV, amb=True)
+    assert (amb == 0).all()

@@ -137,6 +137,25 @@ def test_mx_exponent_closed_form(orc):
         assert 4.0 <= a * 2.0 ** -E < 8.0
 
 
+def test_weight_mx_exponent_is_smallest_unclipped(orc):
+    """Attention-weight blocks: the smallest X with amax 2^-X <= 6, found by
+    brute force; amax = 1 (a block holding the running maximum) and values
+    just below it share X = -2, so rounding below 1 never moves the scale."""
+    rng = np.random.default_rng(2)
+    vals = np.concatenate([2.0 ** np.arange(-120, 1, dtype=np.float64), 0.75 * 2.0 ** np.arange(-100, 1.0),
+                           rng.uniform(0, 1, 3000), np.exp(-rng.uniform(0, 80, 2000))])
+    for a in vals:
+        X = -127
+        while a * 2.0 ** -X > 6.0:
+            X += 1
+        assert orc.mx_exponent_w(a) == X, a
+        if X > -127:
+            assert a * 2.0 ** -(X - 1) > 6.0
+    assert orc.mx_exponent_w(0.0) == -127
+    assert orc.mx_exponent_w(1.0) == -2 and orc.mx_exponent_w(1.0 - 1e-7) == -2
+    assert orc.mx_exponent_w(0.75) == -3 and orc.mx_exponent_w(0.75 + 1e-9) == -2
+
+
 def test_bf16_round_matches_torch_cast(orc):
     """The oracle's bfloat16 rounding of binary32 values equals PyTorch's
     float32 -> bfloat16 conversion (nearest, ties to even): random bit

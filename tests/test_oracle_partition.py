@@ -290,7 +290,7 @@ def test_pooling_and_quantization_over_valid_tokens(orc, Hv, Wv):
         assert np.array_equal(avg[a], G.sum(axis=0) / len(valid))
         assert np.array_equal(mx[a], G.max(axis=0).astype(np.float32))
         amax = np.float32(np.abs(G).max())
-        assert qq["s8"][0, 0, a] == np.float32(amax / np.float32(448.0))
+        assert qq["s8"][0, 0, a] == np.float32(amax / np.float32(127.0))
         pad = slice(a * 64 + len(valid), (a + 1) * 64)
         assert (qq["c8"][0, 0, pad] == 0).all() and (qq["c4"][0, 0, pad] == 0).all()
 

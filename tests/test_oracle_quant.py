@@ -1,11 +1,13 @@
 """Pins of the oracle's operand quantization (CPU).
 
-Q/K: FP8 with one fp32 scale per 64-token block (amax/448), MXFP4 per token
-and 32 channels.  V: FP8 with one scale per channel over all tokens, MXFP4 per
-channel and 32 consecutive keys of a block.  Every rule is recomputed here
-with numpy/torch (independent of the oracle's C code): fp32 division and
-product via numpy float32, codes via torch's float8 cast or a brute-force
-nearest search, exponents via frexp.
+Q/K: INT8 with one fp32 step per 64-token block (amax/127; the uniform
+nearest-integer quantizer of DraftAttention2 App. B.2, used for Q K^T by the
+8-bit path of App. C.1), MXFP4 per token and 32 channels.  V: FP8 with one
+scale per channel over all tokens, MXFP4 per channel and 32 consecutive keys
+of a block.  Every rule is recomputed here with numpy/torch (independent of
+the oracle's C code): fp32 division and product via numpy float32, codes via
+numpy's round-half-even, torch's float8 cast or a brute-force nearest search,
+exponents via frexp.
 """
 import numpy as np
 import pytest
@@ -22,6 +24,12 @@ def _inputs(F=2, Hv=16, Wv=16, d=64, B=1, H=2, seed=21, outliers=True):
 
 def torch_e4m3(x32):
     return torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def int8_codes(prod32):
+    """Nearest integer, ties to even, as two's complement bytes."""
+    r = np.clip(np.rint(prod32.astype(np.float64)), -127, 127)
+    return r.astype(np.int8).view(np.uint8)
 
 
 def mx_exp(amax):
@@ -43,11 +51,14 @@ def test_quant_qk_rules(orc):
     B, H, N, d = X.shape
     G = X.reshape(B, H, N // 64, 64 * d)
     amax = np.abs(G).max(axis=-1)
-    s = (amax / np.float32(448.0)).astype(np.float32)
-    inv = (np.float32(448.0) / amax).astype(np.float32)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    inv = (np.float32(127.0) / amax).astype(np.float32)
     assert np.array_equal(o["s8"], s)
     prod = (G * inv[..., None]).astype(np.float32)
-    assert np.array_equal(o["c8"].reshape(G.shape), torch_e4m3(prod).reshape(G.shape))
+    assert np.array_equal(o["c8"].reshape(G.shape), int8_codes(prod).reshape(G.shape))
+    # the extreme codes are reached: the block's largest |x| maps to +-127
+    c = o["c8"].view(np.int8).reshape(G.shape)
+    assert (np.abs(c).max(axis=-1) == 127).all()
     # MX: per token, 32 channels
     T = X.reshape(B, H, N, d // 32, 32).astype(np.float64)
     E = mx_exp(np.abs(T).max(axis=-1))
@@ -85,8 +96,8 @@ def test_quant_zero_block_and_power_of_two(orc):
     X[0, 0, perm[64:], :] = 0x4000
     o = orc.quant_qk(X, F, Hv, Wv)
     assert o["s8"][0, 0, 0] == 1.0 and (o["c8"][0, 0, :64] == 0).all()
-    assert o["s8"][0, 0, 1] == np.float32(2.0) / np.float32(448.0)
-    assert (o["c8"][0, 0, 64:] == 0x7E).all()  # x * 448/amax = 448 exactly
+    assert o["s8"][0, 0, 1] == np.float32(2.0) / np.float32(127.0)
+    assert (o["c8"][0, 0, 64:] == 127).all()  # x * 127/amax = 127 exactly
     assert (o["e4"][0, 0, :64] == 0).all() and (o["c4"][0, 0, :64] == 0).all()
     # amax = 2 -> E = 1 - 2 = -1, 2 * 2^1 = 4 -> code 6
     assert (o["e4"][0, 0, 64:] == 126).all() and (o["c4"][0, 0, 64:] == 6).all()
@@ -116,9 +127,13 @@ def test_quant_error_within_half_step(orc, which):
     B, H, N, d = Xr.shape
     val8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
     if which == "qk":
+        # uniform quantizer: every value within half a step (App. B.2), up to
+        # the fp32 rounding of the step and of x * 127/amax
         s = np.repeat(o["s8"], 64, axis=2)[..., None].astype(np.float64)
-    else:
-        s = o["s8"][:, :, None, :].astype(np.float64)
+        deq = o["c8"].view(np.int8).astype(np.float64) * s
+        assert (np.abs(deq - Xr) <= s * (0.5 + 2.0 ** -16)).all()
+        return
+    s = o["s8"][:, :, None, :].astype(np.float64)
     deq = val8[o["c8"]] * s
     # relative spacing of e4m3 is at most 2^-3; subnormal step 2^-9 * s
     err = np.abs(deq - Xr)
