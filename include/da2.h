@@ -6,8 +6,9 @@
  * pool Q and K over the spatial regions of each latent frame (Eq. 1), build
  * the mixed average/max draft attention map over region pairs (Eq. 2), rank
  * all R^2 region pairs of the head, and give the top T16 pairs the 16-bit
- * tier (bf16 operands), the next T8 the 8-bit tier (FP8 E4M3), the next T4
- * the 4-bit tier (MXFP4 E2M1 with E8M0 scales per 32 values) and skip the
+ * tier (bf16 operands, unquantized weights), the next T8 the 8-bit tier (INT8
+ * Q K^T, FP8 E4M3 weights and values), the next T4 the 4-bit tier (MXFP4
+ * E2M1 with E8M0 scales per 32 values) and skip the
  * rest (or replace them by block means).  Attention (Sec. 3.3 "phased
  * execution", "cross-precision accumulation"; App. B.3/B.4) then evaluates
  * every kept 64x64 tile at full resolution with its tier's precision, phase
@@ -34,7 +35,7 @@
  *   - The output O uses the same element strides in its own element type
  *     (fp32 or bf16).
  *   - Tier maps are uint8 [B, H, R, R] (query region a, key region b) with
- *     values 16 (16-bit: bf16 operands), 8 (FP8), 4 (MXFP4), 1 (block mean)
+ *     values 16 (16-bit: bf16 operands), 8 (8-bit), 4 (MXFP4), 1 (block mean)
  *     or 0 (skip).  A block-mean tile ("Triage: Skip, Skim, or Refine
  *     Attention Tiles in Video Diffusion Transformers", abstract: a skipped
  *     tile replaced by its block means) scores all its query-key pairs with
@@ -78,7 +79,7 @@ typedef struct {
 } da2_shape;
 
 typedef struct {
-    int32_t hi_bp;   /* share of region pairs in the FP8 tier, basis points of n */
+    int32_t hi_bp;   /* share of region pairs in the 8-bit tier, basis points of n */
     int32_t lo_bp;   /* share in the MXFP4 tier */
     double lambda;   /* weight of the max-pooled branch of the draft map, in [0, 1] */
     int32_t scope;   /* 0: one ranking per head over n = R*R pairs (the paper's);
@@ -116,13 +117,14 @@ da2_status da2_plan_create(const da2_layout_t *layout, void *workspace, size_t w
 void da2_plan_destroy(da2_plan_t *plan);
 
 /* da2_plan: draft-guided tier planning (Sec. 3.1, App. C.1) plus the fused
- * Q/K operand preparation (Sec. 3.3): reorder, pool, quantize Q and K to FP8
- * (one fp32 scale per 64-token block) and MXFP4, score the draft map, rank
+ * Q/K operand preparation (Sec. 3.3): reorder, pool, quantize Q and K to INT8
+ * (App. B.2's uniform quantizer: one fp32 step amax/127 per 64-token block,
+ * codes the nearest integers, ties to even) and MXFP4, score the draft map, rank
  * and assign tiers, and build the per-query-region schedule.  Quotas per
  * ranking, cumulative and each rounded half up: T16 = full_bp*n/10^4, T16 +
  * T8 = (full_bp + hi_bp)*n/10^4, T16 + T8 + T4 = (full_bp + hi_bp +
  * lo_bp)*n/10^4.  The T16 highest-scoring pairs get the 16-bit tier, the next
- * T8 FP8, the next T4 MXFP4 (Sec. 3.1: larger draft mass, higher precision);
+ * T8 the 8-bit tier, the next T4 MXFP4 (Sec. 3.1: larger draft mass, higher precision);
  * ties between equal scores go to the smaller pair index a*R+b.  q and k must
  * stay unchanged until da2_attention on this plan has run (stream order). */
 da2_status da2_plan(da2_plan_t *plan, const void *q, const void *k, const da2_budget *budget,
@@ -140,7 +142,7 @@ da2_status da2_plan_tier_map(const da2_plan_t *plan, uint8_t *dst, hipStream_t s
 /* da2_attention: V preparation (FP8 with one fp32 scale per channel over all
  * tokens; MXFP4 along keys in groups of 32 inside each region) and the
  * phased mixed-precision attention over the plan's kept tiles (16-bit phase,
- * then FP8, then MXFP4; Sec. 3.3), then the block-mean tiles, written to o in
+ * then 8-bit, then MXFP4; Sec. 3.3), then the block-mean tiles, written to o in
  * the original token order.
  * out_dtype: 0 = bf16, 1 = fp32.  q and k must be the pointers the plan was
  * built on (DA2_ERR_PLAN_MISMATCH otherwise).  Rows whose query region keeps
@@ -162,7 +164,7 @@ da2_status da2_attention(da2_plan_t *plan, const void *q, const void *k, const v
  * are never read for the result (padding).
  *   Video query rows: the plan's phases preceded by one segment over the
  *   valid prefix keys in tiles of 64 (16-bit path: bf16 operands, weights
- *   rounded to bf16); a row whose region keeps no video tile still attends
+ *   unquantized); a row whose region keeps no video tile still attends
  *   to the prefix, and is zero only when there is no valid prefix key.
  *   Prefix query rows: every valid prefix key, then every video region in
  *   order, all on the 16-bit path, in chunks of 128 tiles (8192 keys), each
@@ -178,19 +180,20 @@ da2_status da2_attention_prefixed(da2_plan_t *plan, const void *q, const void *k
 
 /* Debug exports in canonical layouts, for tests (device destination):
  *   (Np = 64 R reordered positions, region by region, padding slots included)
- *   DA2_DBG_Q_FP8 / K_FP8 / V_FP8   : uint8 codes [B,H,Np,d]
- *   DA2_DBG_Q_FP8_SCALE / K_...     : fp32 [B,H,R];  V: fp32 [B,H,d]
+ *   DA2_DBG_Q_I8 / K_I8             : INT8 codes (two's complement bytes) [B,H,Np,d]
+ *   DA2_DBG_Q_I8_SCALE / K_...      : fp32 steps [B,H,R]
+ *   DA2_DBG_V_FP8 / V_FP8_SCALE     : E4M3 codes [B,H,Np,d];  fp32 [B,H,d]
  *   DA2_DBG_Q_MX / K_MX / V_MX      : uint8 E2M1 codes [B,H,Np,d] (one per byte)
  *   DA2_DBG_Q_MX_SCALE / K_...      : uint8 E8M0 [B,H,Np,d/32];  V: [B,H,R,2,d]
  *   DA2_DBG_Q_AVG / K_AVG           : fp64 [B,H,R,d];  Q_MAX / K_MAX: fp32 [B,H,R,d]
  *   DA2_DBG_KEYS                    : uint32 [B,H,R,R] (bits of fp32 draft score)
  *   DA2_DBG_SCHEDULE                : int32 [B,H,R,3+R]: n16, n8, n4, then the
- *                                     16-bit key regions ascending, then FP8
+ *                                     16-bit key regions ascending, then 8-bit
  *                                     ascending, then MXFP4 ascending, then -1
  * V entries are valid after da2_attention. */
 enum {
-    DA2_DBG_Q_FP8 = 0, DA2_DBG_Q_FP8_SCALE, DA2_DBG_Q_MX, DA2_DBG_Q_MX_SCALE,
-    DA2_DBG_K_FP8, DA2_DBG_K_FP8_SCALE, DA2_DBG_K_MX, DA2_DBG_K_MX_SCALE,
+    DA2_DBG_Q_I8 = 0, DA2_DBG_Q_I8_SCALE, DA2_DBG_Q_MX, DA2_DBG_Q_MX_SCALE,
+    DA2_DBG_K_I8, DA2_DBG_K_I8_SCALE, DA2_DBG_K_MX, DA2_DBG_K_MX_SCALE,
     DA2_DBG_V_FP8, DA2_DBG_V_FP8_SCALE, DA2_DBG_V_MX, DA2_DBG_V_MX_SCALE,
     DA2_DBG_Q_AVG, DA2_DBG_K_AVG, DA2_DBG_Q_MAX, DA2_DBG_K_MAX,
     DA2_DBG_KEYS, DA2_DBG_SCHEDULE, DA2_DBG_COUNT

@@ -150,7 +150,7 @@ def test_debug_sizes():
     st, lay = _layout(B=2, H=3, d=128, F=1, Hv=16, Wv=24)
     L = da2.lib()
     B, H, d, N, R = 2, 3, 128, 384, 6
-    assert L.da2_plan_debug_bytes(lay, da2.DBG["Q_FP8"]) == B * H * N * d
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["Q_I8"]) == B * H * N * d
     assert L.da2_plan_debug_bytes(lay, da2.DBG["KEYS"]) == B * H * R * R * 4
     assert L.da2_plan_debug_bytes(lay, da2.DBG["V_MX_SCALE"]) == B * H * R * 2 * d
     assert L.da2_plan_debug_bytes(lay, 1234) == 0

@@ -49,11 +49,11 @@ def _check_heads(w, q, k, v, hi, lo, P, o32, o16, heads):
         assert np.array_equal(keys[b:b + 1, h:h + 1], ref_plan["keys"]), (b, h)
         assert np.array_equal(tier[b:b + 1, h:h + 1], ref_plan["tier"]), (b, h)
         assert np.array_equal(sched[b:b + 1, h:h + 1], G.schedule_from_tier(ref_plan["tier"])), (b, h)
-        ref = O.attention(qh, kh, vh, ref_plan["tier"], w.F, w.Hv, w.Wv, qblocks=regions)
+        ref, amb = O.attention(qh, kh, vh, ref_plan["tier"], w.F, w.Hv, w.Wv, qblocks=regions, amb=True)
         idx = torch.from_numpy(rows.astype(np.int64)).cuda()
         got = o32[b, h].index_select(0, idx).cpu().numpy().astype(np.float64)
         rl, ma = G.check_close(got, ref.reshape(-1, d)[keep],
-                            "%s b%d h%d" % (w.name, b, h))
+                               "%s b%d h%d" % (w.name, b, h), amb=amb.reshape(-1, d)[keep])
         # bf16 output: the fp32 result rounded to nearest even
         g16 = o16[b, h].index_select(0, idx).float().cpu().numpy()
         r16 = torch.from_numpy(got.astype(np.float32)).to(torch.bfloat16).float().numpy()
@@ -109,8 +109,8 @@ def test_maximum_region_count():
     tier = P.tier_map().cpu().numpy()
     assert np.array_equal(tier, ref_plan["tier"])
     regions = _sample_regions(R)
-    ref = O.attention(q, k, v, tier, F, Hv, Wv, qblocks=regions)
+    ref, amb = O.attention(q, k, v, tier, F, Hv, Wv, qblocks=regions, amb=True)
     perm = O.layout(F, Hv, Wv)
     rows = np.concatenate([perm[a * 64:(a + 1) * 64] for a in regions])
-    rl, ma = G.check_close(o[0, 0, rows], ref.reshape(-1, d), "R = 8192")
+    rl, ma = G.check_close(o[0, 0, rows], ref.reshape(-1, d), "R = 8192", amb=amb.reshape(-1, d))
     print("R = 8192: rel_l2 %.2e max_abs %.2e vs oracle" % (rl, ma))

@@ -42,8 +42,8 @@ def test_operands_bit_exact(case):
     P, F, Hv, Wv = case["P"], case["F"], case["Hv"], case["Wv"]
     for name, x in (("Q", case["q"]), ("K", case["k"])):
         o = O.quant_qk(x, F, Hv, Wv)
-        assert np.array_equal(G.host(P.debug(name + "_FP8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
-        assert np.array_equal(G.host(P.debug(name + "_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_I8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_I8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
         assert np.array_equal(G.host(P.debug(name + "_MX"), np.uint8).reshape(o["c4"].shape), o["c4"]), name
         assert np.array_equal(G.host(P.debug(name + "_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"]), name
     o = O.quant_v(case["v"], F, Hv, Wv)
@@ -81,11 +81,12 @@ def test_schedule_exact(case):
 
 def test_attention_matches_oracle(case):
     c = case
-    ref = O.attention(c["q"], c["k"], c["v"], c["oracle_plan"]["tier"], c["F"], c["Hv"], c["Wv"])
+    ref, amb = O.attention(c["q"], c["k"], c["v"], c["oracle_plan"]["tier"], c["F"], c["Hv"], c["Wv"],
+                           amb=True)
     rows = np.arange(0, c["q"].shape[2], 97, dtype=np.int32)
     dn = O.dense(c["q"], c["k"], c["v"], rows)
     G.report(c["o"], ref, "plan tier map", dense=(c["o"][:, :, rows], dn))
-    G.check_close(c["o"], ref, "plan tier map")
+    G.check_close(c["o"], ref, "plan tier map", amb=amb)
 
 
 def test_row_scope_tier_map():
@@ -144,11 +145,11 @@ def test_attention_tier_families(which):
         P.attention(qd, kd, vd, o)
         got = o.cpu().numpy()
         assert np.array_equal(P.tier_map().cpu().numpy(), tier)
-        ref = O.attention(c["q"], c["k"], c["v"], tier, F, Hv, Wv)
+        ref, amb = O.attention(c["q"], c["k"], c["v"], tier, F, Hv, Wv, amb=True)
         if name == "skip_all":
             assert (got == 0).all()
             continue
-        G.check_close(got, ref, name)
+        G.check_close(got, ref, name, amb=amb)
         if name == "empty_rows":
             perm = O.layout(F, Hv, Wv)
             dead = perm.reshape(R, 64)[::3].reshape(-1)
@@ -216,8 +217,8 @@ def test_quantizers_exhaustive_bf16():
     G.run_attention(P, qd, kd, x)
     for name, t in (("Q", x), ("K", y)):
         o = O.quant_qk(t, F, Hv, Wv)
-        assert np.array_equal(G.host(P.debug(name + "_FP8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
-        assert np.array_equal(G.host(P.debug(name + "_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_I8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_I8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
         assert np.array_equal(G.host(P.debug(name + "_MX"), np.uint8).reshape(o["c4"].shape), o["c4"]), name
         assert np.array_equal(G.host(P.debug(name + "_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"]), name
     o = O.quant_v(x, F, Hv, Wv)
@@ -240,11 +241,11 @@ def test_degenerate_budgets_and_single_region(d, hi, lo):
         ref_plan = O.plan(q, k, F, Hv, Wv, hi, lo)
         tier = P.tier_map().cpu().numpy()
         assert np.array_equal(tier, ref_plan["tier"])
-        ref = O.attention(q, k, v, tier, F, Hv, Wv)
+        ref, amb = O.attention(q, k, v, tier, F, Hv, Wv, amb=True)
         if not (tier > 0).any():
             assert (o == 0).all()
             continue
-        G.check_close(o, ref, "F%d %dx%d d%d (%d,%d)" % (F, Hv, Wv, d, hi, lo))
+        G.check_close(o, ref, "F%d %dx%d d%d (%d,%d)" % (F, Hv, Wv, d, hi, lo), amb=amb)
         perm = O.layout(F, Hv, Wv)
         R = tier.shape[-1]
         for b in range(tier.shape[0]):

@@ -1,7 +1,7 @@
 """Workloads: video-DiT attention layers (8x8 spatial regions, 64 tokens).
 
 Each entry: batch B, heads H, head_dim d, latent frames F x height Hv x width
-Wv (tokens N = F*Hv*Wv in raster order), and budgets as (FP8, MXFP4) shares
+Wv (tokens N = F*Hv*Wv in raster order), and budgets as (8-bit, MXFP4) shares
 of the R^2 region pairs in basis points; the rest is skipped.
 """
 from dataclasses import dataclass, field

@@ -85,6 +85,31 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float x0, float x1, float x2, fl
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
+// Four INT8 codes: the nearest integers of x (ties to even), two's
+// complement bytes, x0 in the low byte.  Callers pass |x| <= 127 up to one
+// fp32 rounding; the clamp keeps any such value on the code the rounding
+// names.
+__device__ __forceinline__ int i8_code(float x)
+{
+    return (int)__builtin_rintf(fminf(fmaxf(x, -127.0f), 127.0f));
+}
+
+__device__ __forceinline__ uint32_t pack_i8x4(float x0, float x1, float x2, float x3)
+{
+    return ((uint32_t)i8_code(x0) & 0xffu) | (((uint32_t)i8_code(x1) & 0xffu) << 8) |
+           (((uint32_t)i8_code(x2) & 0xffu) << 16) | ((uint32_t)i8_code(x3) << 24);
+}
+
+// Two E4M3 codes (bytes 2 hi and 2 hi + 1 of c) as their values in bf16, low
+// half first.  Exact: an E4M3 value has at most 4 significant bits and lies
+// in the bf16 range, so the top half of its fp32 pattern is the value.
+__device__ __forceinline__ uint32_t fp8_pair_bf16(uint32_t c, int hi)
+{
+    const float a = hi ? __builtin_amdgcn_cvt_f32_fp8((int)c, 2) : __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+    const float b = hi ? __builtin_amdgcn_cvt_f32_fp8((int)c, 3) : __builtin_amdgcn_cvt_f32_fp8((int)c, 1);
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
 // The fp32 value 2^E for an E8M0 exponent E in [-127, 127] (2^-127 is
 // subnormal).
 __device__ __forceinline__ float pow2_e8m0(int E)

@@ -73,6 +73,7 @@ void carve(da2_layout_s &L)
     W.pacc = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * d * 4);
     W.pmz = take(BH * (size_t)L.pchunks * L.ptiles * kBlk * 8);
     W.k16 = take(L.ragged ? BH * N * d * 2 : 0);
+    W.v8b = take(BH * N * d * 2);
     W.vavg = take(BH * R * d * 4);
     W.magg = take(BH * R * 8);
     W.cagg = take(BH * R * d * 4);
@@ -456,10 +457,10 @@ size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which)
         return 0;
     const size_t BH = layout->BH, N = layout->Np, R = layout->R, d = layout->d;
     switch (which) {
-    case DA2_DBG_Q_FP8: case DA2_DBG_K_FP8: case DA2_DBG_V_FP8:
+    case DA2_DBG_Q_I8: case DA2_DBG_K_I8: case DA2_DBG_V_FP8:
     case DA2_DBG_Q_MX: case DA2_DBG_K_MX: case DA2_DBG_V_MX:
         return BH * N * d;
-    case DA2_DBG_Q_FP8_SCALE: case DA2_DBG_K_FP8_SCALE:
+    case DA2_DBG_Q_I8_SCALE: case DA2_DBG_K_I8_SCALE:
         return BH * R * 4;
     case DA2_DBG_V_FP8_SCALE:
         return BH * d * 4;

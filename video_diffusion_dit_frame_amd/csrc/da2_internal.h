@@ -21,8 +21,10 @@ constexpr uint8_t kMeanTier = 1;  // tier of a block-mean tile (skip replaced by
 // ---------------------------------------------------------------------------
 // Workspace: one region of caller memory carved into these buffers.
 // Packed operand layouts (per (b,h) slice "bh", per region a):
-//   Q fp8  : [bh][a][w=2][kc=d/64][lane=64][32 B]   B operand of S^T = K Q^T
-//   K fp8  : [bh][a][m=2][kc][lane][32 B]           A operand, key rows permuted
+//   Q int8 : [bh][a][w=2][kc=d/64][lane=64][32 B]   B operand of S^T = K Q^T:
+//            lane l holds row 32 w + l % 32, channels 64 kc + 32 (l / 32) .. +31
+//   K int8 : [bh][a][m=2][kc][lane][32 B]           A operand, key rows permuted
+//            (lane l: slot key_of_row(l % 32, m), the same channels)
 //   *_mx   : same chunking, 16 B of E2M1 pairs per lane, one E8M0 byte per lane
 //   V fp8  : [bh][a][cb=d/32][lane][32 B]           A operand of O^T = V^T P^T
 //   V mx   : [bh][a][cb][lane][16 B] + E8M0 byte per lane
@@ -34,6 +36,9 @@ constexpr uint8_t kMeanTier = 1;  // tier of a block-mean tile (skip replaced by
 //   K bf16 (ragged layouts) : [bh][a][m=2][s=d/16][lane][16 B]   the key
 //            image of the 16-bit products: chunk (m, s) holds for lane l key
 //            slot key_of_row(l%32, m), channels 16s + 8(l/32) .. +7
+//   V fp8 values : the layout of V bf16, holding the value of every FP8
+//            value code (unscaled) as bf16 (exact: E4M3 has 4 significant
+//            bits); the value operand of the 8-bit tier's P^T V
 //   frame slot table (ragged layouts) : int32 [R_f][64], token y*W_v + x of
 //            each slot of the frame's regions, -1 for padding; int32 [R]
 //            valid tokens of every region
@@ -46,6 +51,7 @@ struct Workspace {
     size_t k8, k4, k4s, ks8;
     size_t v8, v4, v4s, vs8, vamax, v16, vp16, pacc, pmz;
     size_t k16;          // bf16 key image of ragged layouts (16-bit path)
+    size_t v8b;          // bf16 image of the FP8 value codes (8-bit tier P^T V)
     size_t vavg, magg, cagg;  // block-mean tiles: region mean values; per query region the
                               // gathered term (max logit, weight) and its value sum
     size_t ftok, nreg;   // ragged layouts: frame slot table, valid tokens per region

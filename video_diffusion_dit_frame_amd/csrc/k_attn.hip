@@ -3,46 +3,65 @@
 // B.4 shared normalization, App. C.1 empty rows) on gfx950 matrix cores.
 //
 // One workgroup = one query region (64 queries) of one (b, h); wave w owns
-// queries 32w .. 32w+31.  The quantized products use 32x32x64 f8f6f4 MFMAs,
-// the 16-bit ones 32x32x16 bf16 MFMAs, all in the transposed form
+// queries 32w .. 32w+31.  Every product runs in the transposed form
 //     S^T = K Q^T      (A = key rows, B = queries, k = channels)
 //     O^T = V^T P^T    (A = channels, B = queries, k = keys)
 // so every lane holds one query: its softmax statistics never leave the lane
 // except for one exchange with the partner lane (l ^ 32) per tile.  Key rows
-// are stored permuted inside each region (see key_of_row) so that the S^T
+// are stored permuted inside each region (key_of_row) so that the S^T
 // accumulator hands each lane a whole 32-key group, which is exactly the B
 // operand chunk of the P^T V product and exactly one MX block of P.
 //
-// 16-bit phase (tiles of the schedule's 16-bit list, ascending): S from the
-// bf16 inputs as they are (exact products, fp32 sums), c4 = log2(e)/sqrt(d);
-// e = 2^(S c4 + 8 - m); Z += e; P = bf16(e) (nearest even); acc += P^T V in
-// real units.  Phase boundary, when FP8 tiles follow: acc[c] /= sV[c].
-// FP8 phase (tiles of the schedule's FP8 list, ascending): S from FP8 codes,
-// c8 = sQ sK log2(e)/sqrt(d); running max m per 64-key tile; e = 2^(S c8 + 8
-// - m) = 256 w; Z += e; P = e4m3(e); acc += P^T V8 (codes; V's per-channel
-// scale is left out).  Phase boundary: acc[c] *= sV[c] (the change of units).
-// MXFP4 phase: S from scaled MXFP4 MFMAs, c4 = log2(e)/sqrt(d); P gets one
-// E8M0 exponent per 32 keys (floor(log2 max) - 2 of the group's largest e);
-// acc += P^T V4 with both block scales applied by the MFMA.  Epilogue:
-// O = acc / Z (256 cancels), zero when no tile is kept; rows are written
-// straight to their original token positions (restore).
+// Phases, each over its tiles in ascending key region (one running max per
+// 64-key tile, one normalizer Z of the unquantized weights, one output
+// accumulator; App. B.3/B.4):
+//   16-bit: S from the bf16 inputs as they are; w unquantized (App. B's
+//           error bound has no term for this path), carried into P^T V as
+//           two bf16 products, P = hi + lo, hi = bf16(w), lo = bf16(w - hi).
+//   8-bit:  S from INT8 codes of Q and K on the integer matrix core (exact
+//           int32 sums); P = e4m3(256 w) (the 256 applied by the scaled
+//           conversion) times the FP8 codes of V.  That product runs on the
+//           bf16 matrix core over the exact bf16 values of both codes: the
+//           gfx950 FP8 matrix instructions keep only about 13 bits of each
+//           product group below its largest product.  V's per-channel scale
+//           and the 256 are the accumulator's units inside the phase,
+//           changed once at each boundary.
+//   MXFP4:  S from scaled MXFP4 products; P gets one E8M0 exponent per 32
+//           keys (the smallest X with max w 2^-X <= 6); acc += P^T V4.
+// Epilogue: O = acc / Z, zero when no tile is kept; rows are written straight
+// to their original token positions (restore).
+//
+// Softmax arithmetic.  A logit is w = 2^(S c - M) with c the tile's scale
+// (log2 units per unit of the product) and M the row's running maximum.  M
+// is kept as an unevaluated sum mh + ml.  Every product's accumulator starts
+// at -R, R = mh / c in product units, so the matrix core returns D = S - R
+// with a rounding relative to the small difference, not to S (logits of
+// video DiTs carry a large per-query constant); the first tile of a row is
+// multiplied twice, the first time to find R.  Then t = fma(D, c, b) with a
+// per-row bias b = R c - M computed in double-float arithmetic (or, for a row
+// whose maximum this tile raises, the new maximum), and w = 2^t <= 1.
 #include "da2_internal.h"
 #include "da2_device.h"
 
 namespace da2 {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
     const uint8_t *q8, *q4, *q4s;
     const float *qs8;
-    const uint8_t *k8, *k4, *k4s;
+    const uint8_t *k4, *k4s;
     const float *ks8;
-    const uint8_t *v8, *v4, *v4s;
+    const uint8_t *k8;      // INT8 key operand tiles (8-bit tier logits)
+    const uint8_t *v8b;     // bf16 values of the FP8 value codes (16-bit value layout)
+    const uint8_t *v4, *v4s;
     const float *vs8;
     const uint16_t *q, *k;  // bf16 inputs (16-bit phase)
     const uint8_t *v16;     // bf16 value operand (16-bit phase)
@@ -77,7 +96,7 @@ struct AttnArgs {
     int64_t osb, osh, osn;
     int out_f32;
     int H, R, Ry, Rx, Hv, Wv, BH;
-    float c4;  // log2(e) / sqrt(d)
+    float c4h, c4l;  // log2(e) / sqrt(d) as an unevaluated sum
 };
 
 __device__ __forceinline__ v8bf as_bf16x8(v4u x) { return __builtin_bit_cast(v8bf, x); }
@@ -96,25 +115,6 @@ __device__ __forceinline__ float pair_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ v8i load32(const uint8_t *p)
-{
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-    uint4 a = q[0], b = q[1];
-    v8i r;
-    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
-    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
-    return r;
-}
-
-__device__ __forceinline__ v8i load16(const uint8_t *p)
-{
-    uint4 a = *reinterpret_cast<const uint4 *>(p);
-    v8i r;
-    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
-    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
-    return r;
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Loads from wave-uniform addresses through the constant address space, so
@@ -130,29 +130,14 @@ __device__ __forceinline__ float sload_f32(const float *p)
     return *(const __attribute__((address_space(4))) float *)p;
 }
 
-__device__ __forceinline__ v8i lds32(const uint8_t *p)
-{
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-    uint4 a = q[0], b = q[1];
-    v8i r;
-    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
-    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
-    return r;
-}
-
 // A value the compiler may take from any register: the high half of a
-// 16-byte (FP4) matrix operand and the first packing target of a P word are
-// never read, so they need no instruction to set them.
+// 16-byte (FP4) matrix operand is never read, so it needs no instruction to
+// set it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wuninitialized"
 __device__ __forceinline__ int any_int()
 {
     int x;
-    return x;
-}
-__device__ __forceinline__ v16f any_v16f()
-{
-    v16f x;
     return x;
 }
 #pragma clang diagnostic pop
@@ -166,29 +151,166 @@ __device__ __forceinline__ v8i lds16(const uint8_t *p)
     return r;
 }
 
+// A product accumulator holding -R in every element (the lane's query).
+__device__ __forceinline__ v16f splat_neg(float R)
+{
+    v16f x;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+        x[r] = -R;
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Softmax statistics of one query row (this lane's), log2 units.
+// ---------------------------------------------------------------------------
+struct Row {
+    float mh, ml;   // running maximum M = mh + ml; mh = -inf before the first tile
+    float z;        // sum of the unquantized weights 2^(S c - M)
+};
+
+// Scale of a tile's products in log2 units, c = ch + cl, and 1 / ch (rough).
+struct Scale {
+    float ch, cl, inv;
+};
+
+__device__ __forceinline__ Scale scale_c4(const AttnArgs &A)
+{
+    return Scale{A.c4h, A.c4l, __builtin_amdgcn_rcpf(A.c4h)};
+}
+
+// c = sq sk c4 for FP8 codes: the product of the two block scales is exact as
+// a + ae; c keeps the terms of (a + ae)(c4h + c4l) down to the fp32 rounding
+// of the small ones.
+__device__ __forceinline__ Scale scale_fp8(float sq, float sk, const AttnArgs &A)
+{
+    const float a = sq * sk, ae = __builtin_fmaf(sq, sk, -a);
+    const float h = a * A.c4h;
+    const float l = __builtin_fmaf(a, A.c4h, -h) + __builtin_fmaf(a, A.c4l, ae * A.c4h);
+    return Scale{h, l, __builtin_amdgcn_rcpf(h)};
+}
+
+// Product offset of a row for a tile of scale c: R = M / c (0 before the
+// first tile; the first tile finds its own R).
+__device__ __forceinline__ float row_offset(const Row &r, const Scale &c)
+{
+    return r.mh == -__builtin_huge_valf() ? 0.0f : r.mh * c.inv;
+}
+
+// Running-max update of one tile whose products were offset by R and whose
+// largest D = S - R over valid keys is dm.  B = R c - M is formed exactly
+// enough to be small and precise (p + pe = R ch exactly).  A row whose
+// maximum the tile raises takes M' = R c + fl(dm ch) (so the tile's largest
+// weight is 2^(tiny) ~ 1) and owes its earlier statistics al = 2^(M - M');
+// the others keep M.  Returns the bias b of t = fma(D, ch, b); raised tells
+// whether M moved.
+__device__ __forceinline__ float tile_update(Row &r, const Scale &c, float R, float dm, float &al, bool &raised)
+{
+    const float p = R * c.ch, pe = __builtin_fmaf(R, c.ch, -p);
+    const float B = ((p - r.mh) + pe) + __builtin_fmaf(R, c.cl, -r.ml);   // +inf before the first tile
+    const float tm = __builtin_fmaf(dm, c.ch, B);
+    raised = tm > 0.0f;
+    float b = B;
+    al = 1.0f;
+    if (raised) {
+        const float u = dm * c.ch;
+        // M' = p + u + (pe + R cl), renormalised
+        const float s = p + u, bb = s - p;
+        const float err = (p - (s - bb)) + (u - bb);
+        const float lo = err + __builtin_fmaf(R, c.cl, pe);
+        const float hi = s + lo;
+        r.ml = lo - (hi - s);
+        r.mh = hi;
+        al = __builtin_amdgcn_exp2f(-tm);   // 0 before the first tile
+        b = -u;
+    }
+    r.z *= al;
+    return b;
+}
+
+// Largest of the 32 logits a lane holds: two independent chains of
+// three-input maxima, joined at the end.
+__device__ __forceinline__ float lane_max(const v16f (&s)[2])
+{
+    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+        a = fmaxf(fmaxf(a, s[0][r]), s[0][r + 1]);
+        b = fmaxf(fmaxf(b, s[1][r]), s[1][r + 1]);
+    }
+    return fmaxf(a, b);
+}
+
+// Rescale of the running statistics when a tile raises a row maximum;
+// skipped when no lane's maximum moved (the factor would be exactly 1).
+template <int CB>
+__device__ __forceinline__ void rescale(v16f (&acc)[CB], float al)
+{
+    if (__any(al != 1.0f)) {
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++)
+            acc[cb] *= al;
+    }
+}
+
+// Two bf16 values (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
+// Four E4M3 codes of 256 e (the scale 2^-8 of the conversion divides).
+__device__ __forceinline__ int pk_fp8_256(float e0, float e1, float e2, float e3)
+{
+    v2s w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, e0, e1, 0x1p-8f, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, e2, e3, 0x1p-8f, true);
+    return __builtin_bit_cast(int, w);
+}
+
+// MXFP4 block exponent (biased) of this lane's 32-key group, whose largest
+// logit is gm: the smallest X with max e 2^-X <= 6 (the block maximum is
+// never clipped, as with an NVFP4 scale of amax / 6).  With max e = m 2^k,
+// m in [1, 2): X = k - 2, plus 1 when m > 1.5.  Zero and subnormal maxima
+// take the smallest exponent.
+__device__ __forceinline__ int fp4_exponent(float gm, float c, float bias)
+{
+    const uint32_t u = __float_as_uint(__builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias)));
+    const int ef = (int)(u >> 23) - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+    return ef < 0 ? 0 : ef;
+}
+
+// MXFP4 weight word Q of one tile (slots 8 Q .. 8 Q + 7 of the lane's 32-key
+// group, logits s[Q / 2][8 (Q % 2) .. + 7]), with the group's scale
+// 2^(ef - 127).
+template <int Q>
+__device__ __forceinline__ void weight_word_fp4(const v16f (&s)[2], float c, float bias, float pscale, float &z,
+                                                v8i &p)
+{
+    constexpr int mm = Q >> 1, r0 = 8 * (Q & 1);
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
+        z += e[j];
+    }
+    uint32_t wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((uint32_t)any_int(), e[0], e[1], pscale, 0);
+    wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
+    wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
+    p[Q] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
+}
+
+// ---------------------------------------------------------------------------
+// Copies of key/value tiles into LDS.
+// ---------------------------------------------------------------------------
 // Key/value operands of one head as buffer resources: a copy then addresses
 // its tile with one scalar offset and a fixed per-lane offset, with no
 // per-copy vector address arithmetic; reads past the head's bytes return 0.
-struct Src {
-    __amdgpu_buffer_rsrc_t k8, k4, k4s, v8, v4, v4s;
-};
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t *base, int64_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, 0x00020000);
-}
-
-template <int D>
-__device__ __forceinline__ Src head_sources(const AttnArgs &A, int64_t hbase, int R)
-{
-    Src s;
-    s.k8 = head_rsrc(A.k8 + hbase * (kBlk * D), (int64_t)R * kBlk * D);
-    s.k4 = head_rsrc(A.k4 + hbase * (kBlk * D / 2), (int64_t)R * kBlk * D / 2);
-    s.k4s = head_rsrc(A.k4s + hbase * (2 * D), (int64_t)R * 2 * D);
-    s.v8 = head_rsrc(A.v8 + hbase * (kBlk * D), (int64_t)R * kBlk * D);
-    s.v4 = head_rsrc(A.v4 + hbase * (kBlk * D / 2), (int64_t)R * kBlk * D / 2);
-    s.v4s = head_rsrc(A.v4s + hbase * (2 * D), (int64_t)R * 2 * D);
-    return s;
 }
 
 // Copy UNITS kilobytes at byte offset off of a resource to LDS dst with
@@ -213,243 +335,88 @@ __device__ __forceinline__ void copy_dword(__amdgpu_buffer_rsrc_t rs, uint32_t o
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 4, loff4, off, 0, 0);
 }
 
-// LDS images.  Keys and values travel in separate double-buffered streams:
-// the key operand of tile i+1 is needed while tile i's weights are formed
-// (its logits are computed one tile ahead, so the matrix core works while the
-// vector unit runs the softmax), the value operand of tile i only at the end
-// of tile i.  Per buffer (D = head dim):
-//   FP8 key    [0, 64D)  codes                    value [0, 64D) codes
-//   MXFP4 key  [0, 32D)  codes, [32D, 34D) E8M0   value [0, 32D) codes, [32D, 34D) E8M0
-// kb is the key region inside the head.
-template <int D, bool FP8>
-__device__ __forceinline__ void issue_k(const Src &S, int kb, uint8_t *dst, int w, int l)
+// MXFP4 key and value tiles of one head.
+struct Src {
+    __amdgpu_buffer_rsrc_t k4, k4s, v4, v4s;
+};
+
+template <int D>
+__device__ __forceinline__ Src head_sources(const AttnArgs &A, int64_t hbase, int R)
 {
-    const uint32_t lo = (uint32_t)l;
-    if (FP8) {
-        copy_kb<kBlk * D / 1024>(S.k8, (uint32_t)kb * (kBlk * D), dst, w, lo * 16u);
-    } else {
-        copy_kb<kBlk * D / 2048>(S.k4, (uint32_t)kb * (kBlk * D / 2), dst, w, lo * 16u);
-        if (w == 0 && l * 4 < 2 * D)
-            copy_dword(S.k4s, (uint32_t)kb * (2 * D), dst + 32 * D, lo * 4u);
-    }
+    Src s;
+    s.k4 = head_rsrc(A.k4 + hbase * (kBlk * D / 2), (int64_t)R * kBlk * D / 2);
+    s.k4s = head_rsrc(A.k4s + hbase * (2 * D), (int64_t)R * 2 * D);
+    s.v4 = head_rsrc(A.v4 + hbase * (kBlk * D / 2), (int64_t)R * kBlk * D / 2);
+    s.v4s = head_rsrc(A.v4s + hbase * (2 * D), (int64_t)R * 2 * D);
+    return s;
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void issue_v(const Src &S, int kb, uint8_t *dst, int w, int l)
+// LDS images of the MXFP4 phase, in separate double-buffered key and value
+// streams (D = head dim): key [0, 32D) codes, [32D, 34D) E8M0; value the same.
+template <int D>
+__device__ __forceinline__ void issue_k4(const Src &S, int kb, uint8_t *dst, int w, int l)
 {
-    const uint32_t lo = (uint32_t)l;
-    if (FP8) {
-        copy_kb<kBlk * D / 1024>(S.v8, (uint32_t)kb * (kBlk * D), dst, w, lo * 16u);
-    } else {
-        copy_kb<kBlk * D / 2048>(S.v4, (uint32_t)kb * (kBlk * D / 2), dst, w, lo * 16u);
-        if (w == 1 && l * 4 < 2 * D)
-            copy_dword(S.v4s, (uint32_t)kb * (2 * D), dst + 32 * D, lo * 4u);
-    }
+    copy_kb<kBlk * D / 2048>(S.k4, (uint32_t)kb * (kBlk * D / 2), dst, w, (uint32_t)l * 16u);
+    if (w == 0 && l * 4 < 2 * D)
+        copy_dword(S.k4s, (uint32_t)kb * (2 * D), dst + 32 * D, (uint32_t)l * 4u);
 }
 
-// Rescale of the running statistics when a tile raises a row maximum;
-// skipped when no lane's maximum moved (the factor would be exactly 1).
-template <int CB>
-__device__ __forceinline__ void rescale(v16f (&acc)[CB], float &z, float alpha)
+template <int D>
+__device__ __forceinline__ void issue_v4(const Src &S, int kb, uint8_t *dst, int w, int l)
 {
-    if (__any(alpha != 1.0f)) {
-        z *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++)
-            acc[cb] *= alpha;
-    }
+    copy_kb<kBlk * D / 2048>(S.v4, (uint32_t)kb * (kBlk * D / 2), dst, w, (uint32_t)l * 16u);
+    if (w == 1 && l * 4 < 2 * D)
+        copy_dword(S.v4s, (uint32_t)kb * (2 * D), dst + 32 * D, (uint32_t)l * 4u);
 }
 
-// Register operands of one tile.
+// Register operands of one MXFP4 tile.
 template <int D>
 struct KRegs {
-    v8i k[2][D / 64];   // per (key half, 64-channel step)
-    int ks[2][D / 64];  // MXFP4 exponents
+    v8i k[2][D / 64];   // per (key half, 64-channel step); codes in dwords 0-3
+    int ks[2][D / 64];  // E8M0 exponents
 };
 
 template <int D>
 struct VRegs {
     v8i v[D / 32];      // per 32-channel block
-    int vs[D / 32];     // MXFP4 exponents
+    int vs[D / 32];
 };
 
-template <int D, bool FP8>
-__device__ __forceinline__ void read_k(const uint8_t *b, int l, KRegs<D> &K)
+template <int D>
+__device__ __forceinline__ void read_k4(const uint8_t *b, int l, int mm, KRegs<D> &K)
 {
-    constexpr int KC = D / 64;
 #pragma unroll
-    for (int mm = 0; mm < 2; mm++)
-#pragma unroll
-        for (int kc = 0; kc < KC; kc++) {
-            const int chunk = (mm * KC + kc) * 64 + l;
-            if (FP8) {
-                K.k[mm][kc] = lds32(b + chunk * 32);
-            } else {
-                K.k[mm][kc] = lds16(b + chunk * 16);
-                K.ks[mm][kc] = b[32 * D + chunk];
-            }
-        }
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ void read_k_half(const uint8_t *b, int l, int mm, KRegs<D> &K)
-{
-    constexpr int KC = D / 64;
-#pragma unroll
-    for (int kc = 0; kc < KC; kc++) {
-        const int chunk = (mm * KC + kc) * 64 + l;
-        if (FP8) {
-            K.k[mm][kc] = lds32(b + chunk * 32);
-        } else {
-            K.k[mm][kc] = lds16(b + chunk * 16);
-            K.ks[mm][kc] = b[32 * D + chunk];
-        }
+    for (int kc = 0; kc < D / 64; kc++) {
+        const int chunk = (mm * (D / 64) + kc) * 64 + l;
+        K.k[mm][kc] = lds16(b + chunk * 16);
+        K.ks[mm][kc] = b[32 * D + chunk];
     }
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void read_v_range(const uint8_t *b, int l, int c0, int c1, VRegs<D> &V)
+template <int D>
+__device__ __forceinline__ void read_v4(const uint8_t *b, int l, int c0, int c1, VRegs<D> &V)
 {
 #pragma unroll
     for (int cb = c0; cb < c1; cb++) {
         const int chunk = cb * 64 + l;
-        if (FP8) {
-            V.v[cb] = lds32(b + chunk * 32);
-        } else {
-            V.v[cb] = lds16(b + chunk * 16);
-            V.vs[cb] = b[32 * D + chunk];
-        }
+        V.v[cb] = lds16(b + chunk * 16);
+        V.vs[cb] = b[32 * D + chunk];
     }
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ void read_v(const uint8_t *b, int l, VRegs<D> &V)
+// Logits of key half mm of an MXFP4 tile (S^T = K Q^T with block scales),
+// accumulator starting at neg (-R).  The query operand qv[kc] holds the MXFP4
+// codes in dwords 0-3 and the E8M0 exponent in dword 4.
+template <int D>
+__device__ __forceinline__ v16f logits4_half(const KRegs<D> &K, int mm, const v8i (&qv)[D / 64], const v16f &neg)
 {
-    constexpr int CB = D / 32;
+    v16f s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][0], qv[0], neg, 4, 4, 0, K.ks[mm][0], 0,
+                                                            qv[0][4]);
 #pragma unroll
-    for (int cb = 0; cb < CB; cb++) {
-        const int chunk = cb * 64 + l;
-        if (FP8) {
-            V.v[cb] = lds32(b + chunk * 32);
-        } else {
-            V.v[cb] = lds16(b + chunk * 16);
-            V.vs[cb] = b[32 * D + chunk];
-        }
-    }
-}
-
-// Logits S^T = K Q^T of one tile (FP8 codes, or MXFP4 with block scales).
-// The query operand qv[kc] holds the FP8 codes of its 64 channels, or the
-// MXFP4 codes in dwords 0-3 and the E8M0 exponent in dword 4.
-template <int D, bool FP8>
-__device__ __forceinline__ void logits(const KRegs<D> &K, const v8i (&qv)[D / 64], v16f (&s)[2])
-{
-    constexpr int KC = D / 64;
-    s[0] = (v16f){};
-    s[1] = (v16f){};
-#pragma unroll
-    for (int kc = 0; kc < KC; kc++)
-#pragma unroll
-        for (int mm = 0; mm < 2; mm++) {
-            if (FP8)
-                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s[mm], 0, 0, 0, 0,
-                                                                       0, 0);
-            else
-                s[mm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s[mm], 4, 4, 0,
-                                                                       K.ks[mm][kc], 0, qv[kc][4]);
-        }
-}
-
-// Largest of the 32 logits a lane holds: two independent chains of
-// three-input maxima, joined at the end.
-__device__ __forceinline__ float lane_max(const v16f (&s)[2])
-{
-    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-        a = fmaxf(fmaxf(a, s[0][r]), s[0][r + 1]);
-        b = fmaxf(fmaxf(b, s[1][r]), s[1][r + 1]);
-    }
-    return fmaxf(a, b);
-}
-
-// Running-max update of one tile: m = max(m, tile max * c), al = 2^(m_old -
-// m_new) (the factor the statistics of earlier tiles owe), Z *= al.  Returns
-// the bias 8 - m that puts the tile's weights in units of 2^-8.
-__device__ __forceinline__ float new_max(float tmax, float c, float &m, float &z, float &al)
-{
-    const float mnew = fmaxf(m, tmax * c);
-    al = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
-    z *= al;
-    return 8.0f - mnew;
-}
-
-// FP8 weight word Q of one tile (logits s[Q / 4][4 (Q % 4) .. + 3]):
-// e = 2^(S c8 + 8 - m) = 256 w, Z += e, P word Q = e4m3(e) (four keys) of the
-// B operand of P^T V.
-template <int Q>
-__device__ __forceinline__ void weight_word_fp8(const v16f (&s)[2], float c8, float bias, float &z, v8i &p)
-{
-    constexpr int mm = Q >> 2, r0 = 4 * (Q & 3);
-    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 0], c8, bias));
-    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 1], c8, bias));
-    const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 2], c8, bias));
-    const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + 3], c8, bias));
-    z += (e0 + e1) + (e2 + e3);
-    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, any_int(), false);
-    p[Q] = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wd, true);
-}
-
-// MXFP4 block exponent of this lane's 32-key group: floor(log2(max e)) - 2,
-// where the group's largest logit is gm and the tile's is mx (tm = mx c).
-// The group holding the running maximum has max e = 2^8 exactly (w = 1), so
-// its exponent is fixed at 6 instead of being read from a rounded exp2 that
-// may land just below the power of two.
-__device__ __forceinline__ int fp4_exponent(float gm, float mx, float tm, float m, float c, float bias)
-{
-    if (gm == mx && m == tm)
-        return 127 + 6;
-    const float emax = __builtin_amdgcn_exp2f(__builtin_fmaf(gm, c, bias));
-    const int ef = (int)((__float_as_uint(emax) >> 23) & 0xffu) - 2;
-    return ef < 0 ? 0 : ef;
-}
-
-// MXFP4 weight word Q of one tile (slots 8 Q .. 8 Q + 7 of the lane's 32-key
-// group, logits s[Q / 2][8 (Q % 2) .. + 7]), with c = log2(e)/sqrt(d) and the
-// group's scale 2^(ef - 127).
-template <int Q>
-__device__ __forceinline__ void weight_word_fp4(const v16f (&s)[2], float c, float bias, float pscale, float &z,
-                                                v8i &p)
-{
-    constexpr int mm = Q >> 1, r0 = 8 * (Q & 1);
-    float e[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mm][r0 + j], c, bias));
-        z += e[j];
-    }
-    uint32_t wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((uint32_t)any_int(), e[0], e[1], pscale, 0);
-    wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[2], e[3], pscale, 1);
-    wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[4], e[5], pscale, 2);
-    p[Q] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, e[6], e[7], pscale, 3);
-}
-
-// Logits of key half mm of one tile (S^T = K Q^T, FP8 codes, or MXFP4 with
-// block scales; query operand as in logits).
-template <int D, bool FP8>
-__device__ __forceinline__ void logits_half(const KRegs<D> &K, int mm, const v8i (&qv)[D / 64], v16f &s)
-{
-    constexpr int KC = D / 64;
-    s = (v16f){};
-#pragma unroll
-    for (int kc = 0; kc < KC; kc++) {
-        if (FP8)
-            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s, 0, 0, 0, 0, 0, 0);
-        else
-            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s, 4, 4, 0, K.ks[mm][kc],
-                                                               0, qv[kc][4]);
-    }
+    for (int kc = 1; kc < D / 64; kc++)
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(K.k[mm][kc], qv[kc], s, 4, 4, 0, K.ks[mm][kc], 0,
+                                                           qv[kc][4]);
+    return s;
 }
 
 // Wait until at most n vector-memory operations of this wave are pending
@@ -466,56 +433,58 @@ __device__ __forceinline__ uint8_t *chunk16(uint8_t *b0, uint8_t *b1, int c)
     return (c < D / 16 ? b0 : b1) + (c % (D / 16)) * 1024;
 }
 
-// Key tiles of the 16-bit path.  A key source says which tile the i-th step
-// takes, copies that tile's key image (64 key rows x D channels, bf16,
-// gathered straight from K: chunk (m, s) holds for lane l key row
+// ---------------------------------------------------------------------------
+// Key sources of the tiles that run on the bf16 matrix core.  A key source
+// says which tile the i-th step takes, copies that tile's key image (64 key
+// rows x D channels as bf16: chunk (m, s) holds for lane l key row
 // key_of_row(l % 32, m), channels 16 s + 8 (l / 32) .. + 7) into this wave's
-// half of the key buffers, and locates the value images (the bf16 operand
-// written by the V preparation, one 64 x D image per tile).
-//
-// Video regions of one head: the schedule's 16-bit list, or (DENSE) the
-// regions first, first + 1, ... in order.  On the 8x8 grid the key rows are
-// gathered straight from K (a fixed byte offset per lane from the region's
-// first token); a ragged layout copies the bf16 key image its K preparation
-// wrote and masks the region's padding slots.
-template <int D, bool DENSE, bool RAG>
-struct VideoKeys16 {
+// half of the key buffers, and tells how many of its keys are valid.
+// ---------------------------------------------------------------------------
+// Video regions of one head: the schedule's list, or (DENSE) the regions
+// first, first + 1, ... in order.  IMG: copy a prepared key image (the FP8
+// tier's code values, or a ragged layout's 16-bit keys); otherwise (16-bit
+// tier on the 8x8 grid) the rows are gathered straight from K at a fixed
+// byte offset per lane from the region's first token.  RAG: mask the
+// region's padding slots.
+template <int D, bool DENSE, bool IMG, bool RAG>
+struct VideoKeys {
     static constexpr bool kMasked = RAG;
+    static constexpr int kCopies = D / 16;   // copies per wave and tile
     const int32_t *list;
     int first;
     const uint16_t *kh;            // K of this head
-    const uint8_t *vbase;          // value images of the head's regions
+    const uint8_t *kimg;           // key images of the head's regions
+    const uint8_t *vbase;          // 16-bit value images of the head's regions
     int64_t vbytes;
-    const uint8_t *kimg;           // ragged: key images of the head's regions
     const int32_t *nreg;           // ragged: valid tokens per region
-    uint32_t koff;                 // grid: this lane's byte offset from a region's first token;
-                                   // ragged: this lane's byte offset in a key-image chunk
+    uint32_t koff;                 // image: this lane's byte offset in a chunk; grid: from a region's first token
     int kspan, Ry, Rx, Hv, Wv, w;
-    int64_t osn;
+    int64_t osn, ibytes;
 
-    __device__ __forceinline__ VideoKeys16(const AttnArgs &A, const int32_t *list_, int first_, int64_t hoff,
-                                           int64_t hbase, int w_, int l)
+    __device__ __forceinline__ VideoKeys(const AttnArgs &A, const uint8_t *img, const int32_t *list_, int first_,
+                                         int64_t hoff, int64_t hbase, int w_, int l)
         : list(list_), first(first_), kh(A.k + hoff), nreg(A.nreg), kspan(A.kspan), Ry(A.Ry), Rx(A.Rx),
           Hv(A.Hv), Wv(A.Wv), w(w_), osn(A.osn)
     {
-        if (RAG) {
+        if (IMG) {
             koff = (uint32_t)l * 16u;
         } else {
             // wave w gathers the key rows of half m = w
             const int kpos = key_of_row(l & 31, w_);
             koff = (uint32_t)((((kpos >> 3) * A.Wv + (kpos & 7)) * A.osn + 8 * (l >> 5)) * 2);
         }
+        kimg = img ? img + hbase * (kBlk * D * 2) : nullptr;
+        ibytes = (int64_t)A.R * kBlk * D * 2;
         vbase = A.v16 + hbase * (kBlk * D * 2);
-        vbytes = (int64_t)A.R * kBlk * D * 2;
-        kimg = A.k16 + hbase * (kBlk * D * 2);
+        vbytes = ibytes;
     }
     __device__ __forceinline__ int id(int i) const { return DENSE ? first + i : sload_i32(list + i); }
     __device__ __forceinline__ int valid(int kb) const { return RAG ? sload_i32(nreg + kb) : kBlk; }
     __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
     {
-        if (RAG) {
+        if (IMG) {
             // chunks (w, s) of the region's key image: 1 KB each
-            const __amdgpu_buffer_rsrc_t ksrc = head_rsrc(kimg, vbytes);
+            const __amdgpu_buffer_rsrc_t ksrc = head_rsrc(kimg, ibytes);
 #pragma unroll
             for (int s = 0; s < D / 16; s++)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, koff,
@@ -538,8 +507,9 @@ struct VideoKeys16 {
 // last valid row (their logits are masked, so only the address matters);
 // their value rows are zero in the value image.
 template <int D>
-struct PrefixKeys16 {
+struct PrefixKeys {
     static constexpr bool kMasked = true;
+    static constexpr int kCopies = D / 16;
     int first;
     __amdgpu_buffer_rsrc_t ksrc;   // prefix K rows of this head
     const uint8_t *vbase;          // prefix value images of this head
@@ -548,8 +518,8 @@ struct PrefixKeys16 {
     uint32_t lane_off;             // channel offset of this lane, bytes
     int64_t osn;
 
-    __device__ __forceinline__ PrefixKeys16(const AttnArgs &A, int first_, int64_t hoff, int bh, int nv_, int w,
-                                            int l)
+    __device__ __forceinline__ PrefixKeys(const AttnArgs &A, int first_, int64_t hoff, int bh, int nv_, int w,
+                                          int l)
         : first(first_), nv(nv_), osn(A.osn)
     {
         kpos = key_of_row(l & 31, w);
@@ -570,8 +540,42 @@ struct PrefixKeys16 {
     }
 };
 
-// This wave's queries as B operands of the 16-bit logits (lane l: query row
-// qr, channels 16 s + 8 (l / 32) .. + 7 of step s).
+// INT8 key tiles of the schedule's video regions of one head (the 8-bit
+// tier): the prepared operand of region kb, [m][kc][lane][32 B] (lane l: slot
+// key_of_row(l % 32, m), channels 64 kc + 32 (l / 32) .. + 31); wave w copies
+// half m = w into its key buffer.
+template <int D, bool RAG>
+struct Int8Keys {
+    static constexpr bool kMasked = RAG;
+    static constexpr int kCopies = D / 32;
+    const int32_t *list;
+    const int32_t *nreg;
+    const uint8_t *vbase;          // bf16 values of the FP8 value codes of the head's regions
+    int64_t vbytes;
+    __amdgpu_buffer_rsrc_t ksrc;
+    uint32_t loff;
+    int w;
+
+    __device__ __forceinline__ Int8Keys(const AttnArgs &A, const int32_t *list_, int64_t hbase, int w_, int l)
+        : list(list_), nreg(A.nreg), loff((uint32_t)l * 16u), w(w_)
+    {
+        ksrc = head_rsrc(A.k8 + hbase * (kBlk * D), (int64_t)A.R * kBlk * D);
+        vbase = A.v8b + hbase * (kBlk * D * 2);
+        vbytes = (int64_t)A.R * kBlk * D * 2;
+    }
+    __device__ __forceinline__ int id(int i) const { return sload_i32(list + i); }
+    __device__ __forceinline__ int valid(int kb) const { return RAG ? sload_i32(nreg + kb) : kBlk; }
+    __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
+    {
+#pragma unroll
+        for (int s = 0; s < kCopies; s++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, loff,
+                                                     (uint32_t)kb * (kBlk * D) + (w * kCopies + s) * 1024, 0, 0);
+    }
+};
+
+// This wave's queries as B operands of the bf16 logits (lane l: query row qr,
+// channels 16 s + 8 (l / 32) .. + 7 of step s).
 template <int D>
 __device__ __forceinline__ void load_q16(const uint16_t *qr, int l, v4u (&q16)[D / 16])
 {
@@ -580,86 +584,183 @@ __device__ __forceinline__ void load_q16(const uint16_t *qr, int l, v4u (&q16)[D
         q16[s] = *reinterpret_cast<const v4u *>(qr + 8 * (l >> 5) + 16 * s);
 }
 
-// 16-bit path over n tiles of a key source (ascending).  A tile's key image
-// fills both key buffers (half m in buffer m), its value image both value
-// buffers.  The two streams overlap each other's use: the value copy of tile
-// i runs under tile i's logits and softmax, the key copy of tile i+1 under
-// tile i's softmax and P^T V.  Key and value buffers are distinct LDS
-// variables, so the compiler knows a copy into one never feeds reads of the
-// other.  Semantics per tile: S from the bf16 operands as they are (exact
-// products, fp32 sums); masked keys get S = -inf; m = max(m, max S c4);
-// e = 2^(S c4 + 8 - m); Z += e; P = bf16(e) (nearest even); acc += P^T V.
-template <int D, class Keys>
-__device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
-                                      uint8_t *vb1, const Keys &K, int n16, const v4u (&q16)[D / 16],
-                                      int w, int l, v16f (&acc)[D / 32], float &m, float &z)
+// This wave's INT8 query codes as B operands of the integer logits, in
+// entries 0 .. D/32 - 1 of the operand array: entry 2 kc + j holds bytes
+// 16 j .. 16 j + 15 of chunk (w, kc, lane), the same split as the key tiles.
+template <int D>
+__device__ __forceinline__ void load_q8(const uint8_t *q8blk, int w, int l, v4u (&q)[D / 16])
 {
-    constexpr int KS = D / 16;                 // 16-channel steps of QK^T
+#pragma unroll
+    for (int kc = 0; kc < D / 64; kc++) {
+        const uint8_t *p = q8blk + ((w * (D / 64) + kc) * 64 + l) * 32;
+        q[2 * kc] = *reinterpret_cast<const v4u *>(p);
+        q[2 * kc + 1] = *reinterpret_cast<const v4u *>(p + 16);
+    }
+}
+
+// bf16 logits of one tile from the key image in kb0 / kb1, accumulators
+// starting at neg.
+template <int D>
+__device__ __forceinline__ void logits16(uint8_t *kb0, uint8_t *kb1, const v4u (&q16)[D / 16], int l,
+                                         const v16f &neg, v16f (&sc)[2])
+{
+    constexpr int KS = D / 16;
+#pragma unroll
+    for (int mm = 0; mm < 2; mm++)
+        sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(lds_v4u(chunk16<D>(kb0, kb1, mm * KS) + l * 16)), as_bf16x8(q16[0]), neg, 0, 0, 0);
+#pragma unroll
+    for (int s = 1; s < KS; s++)
+#pragma unroll
+        for (int mm = 0; mm < 2; mm++)
+            sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(lds_v4u(chunk16<D>(kb0, kb1, mm * KS + s) + l * 16)), as_bf16x8(q16[s]), sc[mm], 0, 0,
+                0);
+}
+
+// Integer logits of one 8-bit tile (half m of the key tile in buffer m), the
+// accumulators starting at -R (an integer, |R| <= 2^22, so every sum, at
+// most 127^2 D in size, stays exact in the fp32 it is converted to).
+template <int D>
+__device__ __forceinline__ void logits8(const uint8_t *kb0, const uint8_t *kb1, const v4u (&q)[D / 16], int l,
+                                        int negR, v16f (&sc)[2])
+{
+    v16i s[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            s[mm][r] = negR;
+#pragma unroll
+    for (int e = 0; e < D / 32; e++)
+#pragma unroll
+        for (int mm = 0; mm < 2; mm++) {
+            const v4i k = __builtin_bit_cast(v4i, lds_v4u((mm ? kb1 : kb0) + ((e >> 1) * 64 + l) * 32 + 16 * (e & 1)));
+            s[mm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k, __builtin_bit_cast(v4i, q[e]), s[mm], 0, 0, 0);
+        }
+#pragma unroll
+    for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+        for (int r = 0; r < 16; r++)
+            sc[mm][r] = (float)s[mm][r];
+}
+
+// Keys of a tile past its valid count take no part (register r of half mm
+// holds key 32 hf + 16 mm + r).
+__device__ __forceinline__ void mask_keys(v16f (&sc)[2], int nk, int hf)
+{
+    if (nk < kBlk) {
+#pragma unroll
+        for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (32 * hf + 16 * mm + r >= nk)
+                    sc[mm][r] = -__builtin_huge_valf();
+    }
+}
+
+// Tiles whose P^T V runs on the bf16 matrix core: the 16-bit tier (TIER 16:
+// logits from the bf16 inputs, P = w as the pair hi + lo of bf16 values,
+// real units) or the 8-bit tier (TIER 8: integer logits from the INT8 codes,
+// c = sq sk c4 per tile, P = e4m3(256 w) as bf16 times the exact bf16 values
+// of the FP8 value codes, units 256 / sV).  n tiles of a key source,
+// ascending; q holds the query operand (bf16 rows, or the INT8 codes).  A
+// tile's key operand fills both key buffers (half m in buffer m), its value
+// image both value buffers.  The value copy of tile i runs under tile i's
+// logits and softmax, the key copy of tile i+1 under tile i's softmax and
+// P^T V.  Key and value buffers are distinct LDS variables, so the compiler
+// knows a copy into one never feeds reads of the other.
+template <int D, int TIER, class Keys>
+__device__ __forceinline__ void run_bf16(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
+                                         uint8_t *vb1, const Keys &K, int n, const v4u (&q)[D / 16], float qs,
+                                         int64_t hbase, int w, int l, v16f (&acc)[D / 32], Row &row)
+{
     constexpr int CB = D / 32;
-    constexpr int NK = KS;                     // key copies per wave and tile
+    constexpr int NK = Keys::kCopies;              // key copies per wave and tile
+    constexpr int VB = kBlk * D * 2;               // value image of a tile
     const int hf = l >> 5;
     const __amdgpu_buffer_rsrc_t vsrc = head_rsrc(K.vbase, K.vbytes);
+    const Scale c4 = scale_c4(A);
     int kb = K.id(0);
-    int kbn = n16 > 1 ? K.id(1) : 0;
+    int kbn = n > 1 ? K.id(1) : 0;
     K.issue_key(kb, w ? kb1 : kb0);
-    for (int i = 0; i < n16; i++) {
-        // key image of tile i complete (both waves' halves); both waves are
+    for (int i = 0; i < n; i++) {
+        // key operand of tile i complete (both waves' halves); both waves are
         // done with the value buffer
         __builtin_amdgcn_s_waitcnt(vm_wait(0));
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kBlk * D * 2 / 2048; j++) {
+        for (int j = 0; j < VB / 2048; j++) {
             // unit 2j + w lies in the first buffer exactly when j < D / 32
             const int u = 2 * j + w;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 vsrc, (lds_void *)((j < D / 32 ? vb0 : vb1) + (u % (D / 16)) * 1024), 16, (uint32_t)l * 16u,
-                (uint32_t)kb * (kBlk * D * 2) + u * 1024, 0, 0);
+                (uint32_t)kb * VB + u * 1024, 0, 0);
         }
+        const Scale c = TIER == 16 ? c4 : scale_fp8(qs, sload_f32(A.ks8 + hbase + kb), A);
+        const int nk = Keys::kMasked ? K.valid(kb) : kBlk;
         v16f sc[2];
-        sc[0] = (v16f){};
-        sc[1] = (v16f){};
-#pragma unroll
-        for (int s = 0; s < KS; s++)
-#pragma unroll
-            for (int mm = 0; mm < 2; mm++)
-                sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(lds_v4u(chunk16<D>(kb0, kb1, mm * KS + s) + l * 16)), as_bf16x8(q16[s]), sc[mm], 0,
-                    0, 0);
+        float R;
+        if (__builtin_amdgcn_readfirstlane(row.mh == -__builtin_huge_valf() ? 1 : 0)) {
+            // first tile of the row: find its offset from a first product
+            if (TIER == 16)
+                logits16<D>(kb0, kb1, q, l, v16f{}, sc);
+            else
+                logits8<D>(kb0, kb1, q, l, 0, sc);
+            if (Keys::kMasked)
+                mask_keys(sc, nk, hf);
+            R = pair_max(lane_max(sc));
+        } else {
+            R = row_offset(row, c);
+            if (TIER == 8)   // an integer offset within the exact range of the sums
+                R = __builtin_rintf(fminf(fmaxf(R, -0x1p22f), 0x1p22f));
+        }
+        if (TIER == 16)
+            logits16<D>(kb0, kb1, q, l, splat_neg(R), sc);
+        else
+            logits8<D>(kb0, kb1, q, l, -(int)R, sc);
         // both waves are done with the key buffer: refill it with tile i+1
         __syncthreads();
-        const bool more = i + 1 < n16;
+        const bool more = i + 1 < n;
         if (more)
             K.issue_key(kbn, w ? kb1 : kb0);
-        if (Keys::kMasked) {
-            // register r of half mm holds key 32 hf + 16 mm + r
-            const int nk = K.valid(kb);
-            if (nk < kBlk) {
-#pragma unroll
-                for (int mm = 0; mm < 2; mm++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        if (32 * hf + 16 * mm + r >= nk)
-                            sc[mm][r] = -__builtin_huge_valf();
-            }
-        }
-        const float c = A.c4;
-        const float mnew = fmaxf(m, pair_max(lane_max(sc)) * c);
-        rescale<CB>(acc, z, __builtin_amdgcn_exp2f(m - mnew));
-        m = mnew;
-        const float bias = 8.0f - mnew;
-        // P^T chunk t: this lane's keys 32 hf + 8 t .. + 7 (slots 8 t ..)
-        v4u p[4];
+        if (Keys::kMasked)
+            mask_keys(sc, nk, hf);
+        float al;
+        bool raised;
+        const float bias = tile_update(row, c, R, pair_max(lane_max(sc)), al, raised);
+        rescale<CB>(acc, al);
+        float z = 0.0f;
+        // P^T chunk t: this lane's keys 32 hf + 8 t .. + 7 (slots 8 t ..);
+        // the 16-bit tier's residual chunk in pl
+        v4u ph[4], pl[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             const int mm = t >> 1, r0 = 8 * (t & 1);
+            float e[8];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j], c, bias));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + 2 * j + 1], c, bias));
-                z += e0 + e1;
-                p[t][j] = (uint32_t)f32_to_bf16(e0) | ((uint32_t)f32_to_bf16(e1) << 16);
+            for (int j = 0; j < 8; j++) {
+                e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + j], c.ch, bias));
+                z += e[j];
+            }
+            if (TIER == 16) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t h = pk_bf16(e[2 * j], e[2 * j + 1]);
+                    ph[t][j] = h;
+                    pl[t][j] = pk_bf16(e[2 * j] - __uint_as_float(h << 16),
+                                       e[2 * j + 1] - __uint_as_float(h & 0xffff0000u));
+                }
+            } else {
+                const uint32_t w0 = (uint32_t)pk_fp8_256(e[0], e[1], e[2], e[3]);
+                const uint32_t w1 = (uint32_t)pk_fp8_256(e[4], e[5], e[6], e[7]);
+                ph[t][0] = fp8_pair_bf16(w0, 0);
+                ph[t][1] = fp8_pair_bf16(w0, 1);
+                ph[t][2] = fp8_pair_bf16(w1, 0);
+                ph[t][3] = fp8_pair_bf16(w1, 1);
             }
         }
+        row.z += z;
         // value image of tile i complete: only the key copy may still run
         if (more)
             __builtin_amdgcn_s_waitcnt(vm_wait(NK));
@@ -669,15 +770,17 @@ __device__ __forceinline__ void run16(const AttnArgs &A, uint8_t *kb0, uint8_t *
 #pragma unroll
         for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(lds_v4u(chunk16<D>(vb0, vb1, cb * 4 + t) + l * 16)), as_bf16x8(p[t]), acc[cb], 0, 0,
-                    0);
+            for (int t = 0; t < 4; t++) {
+                const v8bf vv = as_bf16x8(lds_v4u(chunk16<D>(vb0, vb1, cb * 4 + t) + l * 16));
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(ph[t]), acc[cb], 0, 0, 0);
+                if (TIER == 16)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(pl[t]), acc[cb], 0, 0, 0);
+            }
         kb = kbn;
-        if (i + 2 < n16)
+        if (i + 2 < n)
             kbn = K.id(i + 2);
     }
-    // the next segment or phase refills both buffers
+    // the next segment or phase refills the buffers
     __syncthreads();
 }
 
@@ -756,32 +859,35 @@ struct Attn {
     // key and value buffers, two of each; four distinct LDS variables, so
     // that the compiler can tell a copy into one from a read of another
     uint8_t *kb0, *kb1, *vb0, *vb1;
-    const int32_t *list;   // key regions of the tiles, in phase order
+    const int32_t *list;   // key regions of the MXFP4 tiles, ascending
     int64_t hbase;
     Src src;
-    int n8, n, w, l, hf, bh;
+    int n, w, l, hf, bh;
     int64_t qblk;
     float qs;
-    v8i qv[KC];   // this wave's queries in the format of the next logits (see logits)
+    v8i qv[KC];   // this wave's queries: MXFP4 codes (dwords 0-3) and exponent (dword 4)
     v16f acc[CB];
-    float m, z;
-    // Software pipeline state.  Step i forms the weights of tile i while the
-    // matrix core computes the logits of tile i+1 and P^T V of tile i-1, so
-    // the logits (S) and the weights (P, with the MXFP4 exponent e) live in
-    // two register sets each, used by steps of alternating parity.
+    Row row;
+    // Software pipeline state of the MXFP4 phase.  Step i forms the weights
+    // of tile i while the matrix core computes the logits of tile i+1 and
+    // P^T V of tile i-1, so the logits (S) and the weights (P, with the MXFP4
+    // exponent e) live in two register sets each, used by steps of
+    // alternating parity.
     v16f S0[2], S1[2];
     v8i P0, P1;
     int E0, E1;
+    v16f negR;          // -R, the accumulator start of the next logits
+    float R;            // offset of the logits held in the current set
     float al;           // factor acc owes before the next P^T V (running-max change)
     int kr0, kr1, kr2;  // key regions of tiles i, i+1, i+2 (wave-uniform)
     int nk0;            // valid tokens of tile i's key region (PMAX > 0)
-    float c8;           // FP8 logit scale of tile i
 
+    // change of value units around the 8-bit phase: real <-> 256 / sV (the
+    // FP8 value codes and the 256 of the weight codes).  The scales are
+    // loaded where they are used (volatile): loaded once for both uses, they
+    // would stay in 64 registers through the phases.
     __device__ __forceinline__ void vunits(bool to_fp8)
     {
-        // change of value units: real <-> FP8 codes (per-channel V scale).
-        // The scales are loaded where they are used (volatile): loaded once
-        // for both uses, they would stay in 64 registers through the phases.
         const volatile float4 *vs = reinterpret_cast<const volatile float4 *>(A.vs8 + (int64_t)bh * D);
 #pragma unroll
         for (int cb = 0; cb < CB; cb++)
@@ -790,68 +896,47 @@ struct Attn {
                 const float4 sv = const_cast<const float4 &>(vs[(32 * cb + 8 * g + 4 * hf) / 4]);
                 const float f[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-                for (int t = 0; t < 4; t++)
-                    acc[cb][4 * g + t] = to_fp8 ? acc[cb][4 * g + t] / f[t] : acc[cb][4 * g + t] * f[t];
+                for (int t = 0; t < 4; t++) {
+                    const float u = f[t] * 0x1p-8f;
+                    acc[cb][4 * g + t] = to_fp8 ? acc[cb][4 * g + t] / u : acc[cb][4 * g + t] * u;
+                }
             }
     }
 
-    // acc *= al before the next P^T V; with UNIT the FP8 -> real change of
-    // value units is applied as well (the product about to be added is the
-    // first MXFP4 one).
-    template <bool UNIT>
+    // acc *= al before the next P^T V
     __device__ __forceinline__ void settle()
     {
-        if (UNIT) {
-#pragma unroll
-            for (int cb = 0; cb < CB; cb++)
-                acc[cb] *= al;
-            vunits(false);
-        } else if (__any(al != 1.0f)) {
+        if (__any(al != 1.0f)) {
 #pragma unroll
             for (int cb = 0; cb < CB; cb++)
                 acc[cb] *= al;
         }
     }
 
-    template <bool FP8>
     __device__ __forceinline__ void pv_range(const VRegs<D> &V, const v8i &p, int ef, int c0, int c1)
     {
-        if (FP8) {
 #pragma unroll
-            for (int cb = c0; cb < c1; cb++)
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 0, 0, 0, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int cb = c0; cb < c1; cb++)
-                acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 4, 4, 0,
-                                                                         V.vs[cb], 0, ef);
-        }
+        for (int cb = c0; cb < c1; cb++)
+            acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(V.v[cb], p, acc[cb], 4, 4, 0, V.vs[cb], 0, ef);
     }
 
-    // Step i, kinds KP (tile i-1), KCUR (tile i), KN (tile i+1) true for FP8.
-    // On entry sc holds the logits of tile i, pp / ep the weights of tile i-1
-    // (zero before the first tile), al the factor acc owes before their
-    // product.  The refills go first: K(i+2)
-    // into K(i)'s buffer kw and V(i) into V(i-2)'s buffer vw, both read for
-    // the last time in step i-1.  Then K(i+1) and V(i-1) are read from kr and
-    // vr, each half just before its products.  The last step computes logits
-    // of a stale key image, which are never used (kinds KN = KCUR there).
-    template <bool KP, bool KCUR, bool KN, bool UNIT>
-    __device__ __forceinline__ void step(int i, v16f (&sc)[2], v16f (&sn)[2], const v8i &pp, int ep,
-                                         v8i &pc, int &ec, const uint8_t *__restrict__ kr,
-                                         uint8_t *__restrict__ kw, const uint8_t *__restrict__ vr,
-                                         uint8_t *__restrict__ vw)
+    // MXFP4 step i.  On entry sc holds the logits of tile i (offset R), pp /
+    // ep the weights of tile i-1 (zero before the first tile), al the factor
+    // acc owes before their product.  The refills go first: K(i+2) into
+    // K(i)'s buffer kw and V(i) into V(i-2)'s buffer vw, both read for the
+    // last time in step i-1.  Then K(i+1) and V(i-1) are read from kr and vr,
+    // each half just before its products.  The last step computes logits of a
+    // stale key image, which are never used.
+    __device__ __forceinline__ void step(int i, v16f (&sc)[2], v16f (&sn)[2], const v8i &pp, int ep, v8i &pc,
+                                         int &ec, const uint8_t *__restrict__ kr, uint8_t *__restrict__ kw,
+                                         const uint8_t *__restrict__ vr, uint8_t *__restrict__ vw)
     {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        settle<UNIT>();
-        if (i + 2 < n) {
-            if (i + 2 < n8)
-                issue_k<D, true>(src, kr2, kw, w, l);
-            else
-                issue_k<D, false>(src, kr2, kw, w, l);
-        }
-        issue_v<D, KCUR>(src, kr0, vw, w, l);
+        settle();
+        if (i + 2 < n)
+            issue_k4<D>(src, kr2, kw, w, l);
+        issue_v4<D>(src, kr0, vw, w, l);
         VRegs<D> V;
         KRegs<D> K;
         // main block: weights of tile i on the vector unit, products of tiles
@@ -859,122 +944,74 @@ struct Attn {
         // Each region reads the operands of the next region's products from
         // LDS, issues its own products (operands read by the region before)
         // and forms a quarter of the weights:
-        //   R0: running max; read V blocks [0, CB/2)
+        //   R0: running max; offset of the next logits; read V [0, CB/2)
         //   R1: P^T V blocks [0, CB/2);  read V blocks [CB/2, CB); weights 1/4
         //   R2: P^T V blocks [CB/2, CB); read K half 0;          weights 2/4
         //   R3: logits half 0 (into the registers of the logits weights 1/4
         //       and 2/4 consumed);        read K half 1;          weights 3/4
         //   R4: logits half 1;                                    weights 4/4
-        float c, bias, pscale = 0.0f;
         if (PMAX > 0)
             mask_padding<PMAX>(sc[1], nk0, hf);
-        if (KCUR) {
-            c = c8;
-            bias = new_max(pair_max(lane_max(sc)), c, m, z, al);
-        } else {
-            c = A.c4;
-            const float gm = lane_max(sc);
-            const float mx = pair_max(gm);
-            bias = new_max(mx, c, m, z, al);
-            ec = fp4_exponent(gm, mx, mx * c, m, c, bias);
-            pscale = ec ? __uint_as_float((uint32_t)ec << 23) : __uint_as_float(0x00400000u);
+        const Scale c = scale_c4(A);
+        const float gm = lane_max(sc);
+        const float dm = pair_max(gm);
+        bool raised;
+        const float bias = tile_update(row, c, R, dm, al, raised);
+        ec = fp4_exponent(gm, c.ch, bias);
+        const float pscale = ec ? __uint_as_float((uint32_t)ec << 23) : __uint_as_float(0x00400000u);
+        // the next logits start at -R' (R' = M / c), refreshed when a maximum moved
+        if (__any(raised)) {
+            R = row_offset(row, c);
+            negR = splat_neg(R);
         }
-        read_v_range<D, KP>(vr, l, 0, CB / 2, V);
+        read_v4<D>(vr, l, 0, CB / 2, V);
         __builtin_amdgcn_sched_barrier(0);
         // R1
-        pv_range<KP>(V, pp, ep, 0, CB / 2);
-        read_v_range<D, KP>(vr, l, CB / 2, CB, V);
-        if (KCUR) {
-            weight_word_fp8<0>(sc, c, bias, z, pc);
-            weight_word_fp8<1>(sc, c, bias, z, pc);
-        } else {
-            weight_word_fp4<0>(sc, c, bias, pscale, z, pc);
-        }
+        pv_range(V, pp, ep, 0, CB / 2);
+        read_v4<D>(vr, l, CB / 2, CB, V);
+        float z = 0.0f;
+        weight_word_fp4<0>(sc, c.ch, bias, pscale, z, pc);
         region_pattern();
         __builtin_amdgcn_sched_barrier(0);
         // R2
-        pv_range<KP>(V, pp, ep, CB / 2, CB);
-        read_k_half<D, KN>(kr, l, 0, K);
-        if (KCUR) {
-            weight_word_fp8<2>(sc, c, bias, z, pc);
-            weight_word_fp8<3>(sc, c, bias, z, pc);
-        } else {
-            weight_word_fp4<1>(sc, c, bias, pscale, z, pc);
-        }
+        pv_range(V, pp, ep, CB / 2, CB);
+        read_k4<D>(kr, l, 0, K);
+        weight_word_fp4<1>(sc, c.ch, bias, pscale, z, pc);
         region_pattern();
         __builtin_amdgcn_sched_barrier(0);
         // R3
-        logits_half<D, KN>(K, 0, qv, sn[0]);
-        read_k_half<D, KN>(kr, l, 1, K);
-        if (KCUR) {
-            weight_word_fp8<4>(sc, c, bias, z, pc);
-            weight_word_fp8<5>(sc, c, bias, z, pc);
-        } else {
-            weight_word_fp4<2>(sc, c, bias, pscale, z, pc);
-        }
+        sn[0] = logits4_half<D>(K, 0, qv, negR);
+        read_k4<D>(kr, l, 1, K);
+        weight_word_fp4<2>(sc, c.ch, bias, pscale, z, pc);
         region_pattern();
         __builtin_amdgcn_sched_barrier(0);
         // R4
-        logits_half<D, KN>(K, 1, qv, sn[1]);
-        if (KCUR) {
-            weight_word_fp8<6>(sc, c, bias, z, pc);
-            weight_word_fp8<7>(sc, c, bias, z, pc);
-        } else {
-            weight_word_fp4<3>(sc, c, bias, pscale, z, pc);
-            pc[4] = any_int(); pc[5] = any_int(); pc[6] = any_int(); pc[7] = any_int();
-        }
+        sn[1] = logits4_half<D>(K, 1, qv, negR);
+        weight_word_fp4<3>(sc, c.ch, bias, pscale, z, pc);
+        pc[4] = any_int(); pc[5] = any_int(); pc[6] = any_int(); pc[7] = any_int();
         region_pattern();
+        row.z += z;
         // Z, the packed weights and the next logits are complete within the
         // step: otherwise the compiler sinks their additions, conversions and
         // products into the next step (keeping every weight of this tile live
         // across the barrier, or serializing the next row maximum behind the
         // products).
-        asm volatile("" ::"v"(z), "v"(pc), "v"(sn[0]), "v"(sn[1]));
+        asm volatile("" ::"v"(row.z), "v"(pc), "v"(sn[0]), "v"(sn[1]));
         // wave-uniform values of the next step, loaded without branches so
         // that the main block stays one scheduling region (indices past the
-        // list are clamped; such values and the logit scale of an MXFP4 tile
-        // are never used)
+        // list are clamped; such values are never used)
         kr0 = kr1;
         kr1 = kr2;
         kr2 = sload_i32(list + min(i + 3, n - 1));
-        c8 = (qs * sload_f32(A.ks8 + hbase + kr0)) * A.c4;
         if (PMAX > 0)
             nk0 = sload_i32(A.nreg + kr0);
     }
 
-    // Step i with the register sets and buffers of an even or an odd step.
-    template <bool KP, bool KCUR, bool KN, bool UNIT>
-    __device__ __forceinline__ void step_even(int i)
-    {
-        step<KP, KCUR, KN, UNIT>(i, S0, S1, P1, E1, P0, E0, kb1, kb0, vb1, vb0);
-    }
+    __device__ __forceinline__ void step_even(int i) { step(i, S0, S1, P1, E1, P0, E0, kb1, kb0, vb1, vb0); }
+    __device__ __forceinline__ void step_odd(int i) { step(i, S1, S0, P0, E0, P1, E1, kb0, kb1, vb0, vb1); }
 
-    template <bool KP, bool KCUR, bool KN, bool UNIT>
-    __device__ __forceinline__ void step_odd(int i)
-    {
-        step<KP, KCUR, KN, UNIT>(i, S1, S0, P0, E0, P1, E1, kb0, kb1, vb0, vb1);
-    }
-
-    template <bool ODD, bool KP, bool KCUR, bool KN, bool UNIT>
-    __device__ __forceinline__ void step_par(int i)
-    {
-        if (ODD)
-            step_odd<KP, KCUR, KN, UNIT>(i);
-        else
-            step_even<KP, KCUR, KN, UNIT>(i);
-    }
-
-    // Queries of this wave in one format, loaded when the first logits of
-    // that format are due, into the one query operand set.
-    __device__ __forceinline__ void load_q8()
-    {
-#pragma unroll
-        for (int kc = 0; kc < KC; kc++)
-            qv[kc] = load32(A.q8 + qblk * (kBlk * D) + ((w * KC + kc) * 64 + l) * 32);
-    }
-
-    // (volatile: a second load before the MXFP4 loop gives the loop its
-    // own short live range instead of one spanning the phase boundary)
+    // (volatile: the load right before the MXFP4 loop gives the loop its own
+    // short live range)
     __device__ __forceinline__ void load_q4()
     {
 #pragma unroll
@@ -987,46 +1024,30 @@ struct Attn {
             qv[kc][2] = c.z;
             qv[kc][3] = c.w;
             qv[kc][4] = *(const volatile uint8_t *)(A.q4s + qblk * (2 * D) + chunk);
+            qv[kc][5] = any_int(); qv[kc][6] = any_int(); qv[kc][7] = any_int();
         }
     }
 
-    // FP8 tiles [0, n8), then MXFP4 tiles [n8, n).  Step i uses the register
-    // sets and buffers of parity (i + off) % 2, with off = 1 - n8 % 2: the
-    // last FP8 step is then always even, so every step's sets and buffers are
-    // fixed at compile time (a lead-in step absorbs the choice).
-    __device__ __forceinline__ void quantized_phases()
+    // MXFP4 tiles [0, n), step i with the register sets and buffers of parity
+    // i % 2.
+    __device__ __forceinline__ void fp4_phase()
     {
         if (n == 0)
             return;
-        if (n8 > 0)
-            load_q8();
-        else
-            load_q4();
-        const bool off = !(n8 & 1);
-        // prologue: keys of tiles 0 and 1, logits of tile 0
+        load_q4();
         kr0 = sload_i32(list);
         kr1 = n > 1 ? sload_i32(list + 1) : 0;
         kr2 = n > 2 ? sload_i32(list + 2) : 0;
-        uint8_t *k0 = off ? kb1 : kb0, *k1 = off ? kb0 : kb1;
-        if (n8 > 0)
-            issue_k<D, true>(src, kr0, k0, w, l);
-        else
-            issue_k<D, false>(src, kr0, k0, w, l);
-        if (n > 1) {
-            if (n8 > 1)
-                issue_k<D, true>(src, kr1, k1, w, l);
-            else
-                issue_k<D, false>(src, kr1, k1, w, l);
-        }
-        c8 = n8 > 0 ? (qs * sload_f32(A.ks8 + hbase + kr0)) * A.c4 : 0.0f;
+        issue_k4<D>(src, kr0, kb0, w, l);
+        if (n > 1)
+            issue_k4<D>(src, kr1, kb1, w, l);
         if (PMAX > 0)
             nk0 = sload_i32(A.nreg + kr0);
         // step 0 multiplies P = 0 into the value buffer of the other parity:
         // clear it so that no stale code can make a NaN
-        uint8_t *vz = off ? vb0 : vb1;
 #pragma unroll
         for (int u = 0; u < kBlk * D / (128 * 16); u++)
-            *reinterpret_cast<v4u *>(vz + (u * 128 + threadIdx.x) * 16) = (v4u){};
+            *reinterpret_cast<v4u *>(vb1 + (u * 128 + threadIdx.x) * 16) = (v4u){};
         P0 = (v8i){};
         P1 = (v8i){};
         E0 = 127;
@@ -1036,96 +1057,73 @@ struct Attn {
         __syncthreads();
         {
             KRegs<D> K;
-            if (n8 > 0) {
-                read_k<D, true>(k0, l, K);
-                if (off)
-                    logits<D, true>(K, qv, S1);
-                else
-                    logits<D, true>(K, qv, S0);
+            read_k4<D>(kb0, l, 0, K);
+            read_k4<D>(kb0, l, 1, K);
+            const Scale c = scale_c4(A);
+            if (__builtin_amdgcn_readfirstlane(row.mh == -__builtin_huge_valf() ? 1 : 0)) {
+                // first tile of the row: find its offset from a first product
+                const v16f zero = {};
+                S0[0] = logits4_half<D>(K, 0, qv, zero);
+                S0[1] = logits4_half<D>(K, 1, qv, zero);
+                if (PMAX > 0)
+                    mask_padding<PMAX>(S0[1], nk0, hf);
+                R = pair_max(lane_max(S0));
             } else {
-                read_k<D, false>(k0, l, K);
-                logits<D, false>(K, qv, S1);   // n8 = 0: off
+                R = row_offset(row, c);
             }
+            negR = splat_neg(R);
+            S0[0] = logits4_half<D>(K, 0, qv, negR);
+            S0[1] = logits4_half<D>(K, 1, qv, negR);
         }
         int i = 0;
-        if (n8 > 0) {
-            // FP8 steps whose successor is FP8, except the last FP8 step
-            if (off) {
-                step_odd<true, true, true, false>(0);
-                i = 1;
-            }
-            for (; i < n8 - 1; i += 2) {
-                step_even<true, true, true, false>(i);
-                step_odd<true, true, true, false>(i + 1);
-            }
-            // the last FP8 step (even), then the first MXFP4 step (odd) and
-            // the step adding the first MXFP4 product (even)
-            if (n8 == n) {
-                step_even<true, true, true, false>(i++);
-            } else {
-                load_q4();
-                step_even<true, true, false, false>(i++);
-                step_odd<true, false, false, false>(i++);
-                if (i < n)
-                    step_even<false, false, false, true>(i++);
-            }
-        }
-        // MXFP4 steps, starting odd
-        if (n8 > 0 && i + 1 < n)
-            load_q4();
         for (; i + 1 < n; i += 2) {
-            step_odd<false, false, false, false>(i);
-            step_even<false, false, false, false>(i + 1);
+            step_even(i);
+            step_odd(i + 1);
         }
         if (i < n)
-            step_odd<false, false, false, false>(i);
-        // drain: P^T V of the last tile, and the change of value units when
-        // the last product added is an FP8 one, or when the first MXFP4
-        // product is the last
+            step_even(i);
+        // drain: P^T V of the last tile
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        const bool last8 = n - 1 < n8;
-        const bool lodd = (n - 1 + (int)off) & 1;
+        const bool lodd = (n - 1) & 1;
         VRegs<D> V;
         const v8i pl = lodd ? P1 : P0;   // by value: a reference would keep both sets in memory
         const int el = lodd ? E1 : E0;
-        if (last8) {
-            settle<false>();
-            read_v<D, true>(lodd ? vb1 : vb0, l, V);
-            pv<true>(V, pl, el);
-            vunits(false);
-        } else {
-            if (n - 1 == n8 && n8 > 0)
-                settle<true>();
-            else
-                settle<false>();
-            read_v<D, false>(lodd ? vb1 : vb0, l, V);
-            pv<false>(V, pl, el);
-        }
+        settle();
+        read_v4<D>(lodd ? vb1 : vb0, l, 0, CB, V);
+        pv_range(V, pl, el, 0, CB);
+        __syncthreads();
     }
 
-    template <bool FP8>
-    __device__ __forceinline__ void pv(const VRegs<D> &V, const v8i &p, int ef)
-    {
-        pv_range<FP8>(V, p, ef, 0, CB);
-    }
-
-    // 16-bit segments of query region a: the text-prefix keys (np tiles, nv
-    // valid keys), then the schedule's 16-bit key regions
-    __device__ __forceinline__ void phase16(const int32_t *list16, int n16, int np, int nv, int a)
+    // Phases whose P^T V runs on the bf16 matrix core: the text-prefix keys
+    // (np tiles, nv valid keys) and the schedule's 16-bit key regions, then
+    // its 8-bit key regions.
+    __device__ __forceinline__ void bf16_phases(const int32_t *list16, int n16, const int32_t *list8, int n8, int np,
+                                                int nv, int a)
     {
         const int bb = bh / A.H, hh = bh - bb * A.H;
         const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
         v4u q16[D / 16];
-        int qt = slot_token<RAG>(A.geo, a, 32 * w + (l & 31));
-        if (qt < 0)   // padding slot: any valid row (its output is not written)
-            qt = slot_token<RAG>(A.geo, a, 0);
-        load_q16<D>(A.q + hoff + (int64_t)qt * A.osn, l, q16);
-        if (np > 0)
-            run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, 0, hoff, bh, nv, w, l), np, q16, w, l, acc, m, z);
-        if (n16 > 0)
-            run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, false, RAG>(A, list16, 0, hoff, hbase, w, l), n16, q16,
-                     w, l, acc, m, z);
+        if (np > 0 || n16 > 0) {
+            int qt = slot_token<RAG>(A.geo, a, 32 * w + (l & 31));
+            if (qt < 0)   // padding slot: any valid row (its output is not written)
+                qt = slot_token<RAG>(A.geo, a, 0);
+            load_q16<D>(A.q + hoff + (int64_t)qt * A.osn, l, q16);
+            if (np > 0)
+                run_bf16<D, 16>(A, kb0, kb1, vb0, vb1, PrefixKeys<D>(A, 0, hoff, bh, nv, w, l), np, q16, qs, hbase, w,
+                                l, acc, row);
+            if (n16 > 0)
+                run_bf16<D, 16>(A, kb0, kb1, vb0, vb1,
+                                VideoKeys<D, false, RAG, RAG>(A, A.k16, list16, 0, hoff, hbase, w, l), n16, q16, qs,
+                                hbase, w, l, acc, row);
+        }
+        if (n8 > 0) {
+            vunits(true);
+            load_q8<D>(A.q8 + qblk * (kBlk * D), w, l, q16);
+            run_bf16<D, 8>(A, kb0, kb1, vb0, vb1, Int8Keys<D, RAG>(A, list8, hbase, w, l), n8, q16, qs, hbase, w, l,
+                           acc, row);
+            vunits(false);
+        }
     }
 
     // O = acc / Z for this wave's 32 queries of region a, written straight to
@@ -1137,9 +1135,9 @@ struct Attn {
             const int64_t ra = (int64_t)bh * A.R + a;
             const float2 mz = A.magg[ra];
             if (mz.y > 0.0f) {
-                const float mnew = fmaxf(m, mz.x);
-                const float f = __builtin_amdgcn_exp2f(m - mnew), g = __builtin_amdgcn_exp2f(mz.x + 8.0f - mnew);
-                z = z * f + (hf ? 0.0f : mz.y * g);   // z is summed over the lane pair
+                const float mnew = fmaxf(row.mh, mz.x);
+                const float f = __builtin_amdgcn_exp2f(row.mh - mnew), g = __builtin_amdgcn_exp2f(mz.x - mnew);
+                row.z = row.z * f + (hf ? 0.0f : mz.y * g);   // z is summed over the lane pair
                 const float *cv = A.cagg + ra * D + 4 * hf;
 #pragma unroll
                 for (int cb = 0; cb < CB; cb++)
@@ -1151,10 +1149,10 @@ struct Attn {
                         acc[cb][4 * gq + 2] = acc[cb][4 * gq + 2] * f + c4v.z * g;
                         acc[cb][4 * gq + 3] = acc[cb][4 * gq + 3] * f + c4v.w * g;
                     }
-                m = mnew;
+                row.mh = mnew;
             }
         }
-        const float zt = pair_sum(z);
+        const float zt = pair_sum(row.z);
         const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
         const int qi = 32 * w + (l & 31);
         const int tok = slot_token<RAG>(A.geo, a, qi);
@@ -1177,13 +1175,14 @@ struct Attn {
 #pragma unroll
         for (int cb = 0; cb < CB; cb++)
             acc[cb] = (v16f){};
-        m = -__builtin_huge_valf();
-        z = 0.0f;
+        row.mh = -__builtin_huge_valf();
+        row.ml = 0.0f;
+        row.z = 0.0f;
     }
 };
 
-// One query region per workgroup: 16-bit phase (if any), then the FP8 and
-// MXFP4 phases.
+// One query region per workgroup: 16-bit phase (text prefix, then 16-bit
+// tiles), 8-bit phase, MXFP4 phase, epilogue.
 template <int D, bool RAG, int PMAX>
 __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
 {
@@ -1215,17 +1214,14 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     S.init(w, bh, qblk);
     const int n16 = sload_i32(A.cnt + qblk * kTargets);
     const int n8 = sload_i32(A.cnt + qblk * kTargets + 1);
-    S.n8 = n8;
-    S.n = n8 + sload_i32(A.cnt + qblk * kTargets + 2);
-    S.list = A.sched + qblk * R + n16;
+    S.n = sload_i32(A.cnt + qblk * kTargets + 2);
+    const int32_t *list16 = A.sched + qblk * R;
+    S.list = list16 + n16 + n8;
     const int nv = prefix_valid(A, bh / A.H);
     const int np = (nv + kBlk - 1) / kBlk;
-    if (n16 > 0 || np > 0) {
-        S.phase16(A.sched + qblk * R, n16, np, nv, a);
-        if (n8 > 0)
-            S.vunits(true);   // phase boundary: real units -> FP8 value units
-    }
-    S.quantized_phases();
+    if (n16 > 0 || n8 > 0 || np > 0)
+        S.bf16_phases(list16, n16, list16 + n16, n8, np, nv, a);
+    S.fp4_phase();
     S.epilogue(a);
 }
 
@@ -1243,6 +1239,7 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
 {
     const int b = bh / A.H, h = bh - b * A.H;
     const int64_t hoff = (int64_t)b * A.osb + (int64_t)h * A.osh;
+    const int64_t hbase = (int64_t)bh * A.R;
     const int row = kBlk * pb + 32 * w + (l & 31);
     v4u q16[D / 16];
     load_q16<D>(A.qp + hoff + (int64_t)min(row, A.Lp - 1) * A.osn, l, q16);
@@ -1250,18 +1247,19 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
 #pragma unroll
     for (int cb = 0; cb < D / 32; cb++)
         acc[cb] = (v16f){};
-    float m = -__builtin_huge_valf(), z = 0.0f;
+    Row st{-__builtin_huge_valf(), 0.0f, 0.0f};
     const int nv = prefix_valid(A, b);
     const int np = (nv + kBlk - 1) / kBlk;
     const int t0 = c * kPrefixChunkTiles, t1 = min(t0 + kPrefixChunkTiles, np + A.R);
     if (t0 < np)
-        run16<D>(A, kb0, kb1, vb0, vb1, PrefixKeys16<D>(A, t0, hoff, bh, nv, w, l), min(t1, np) - t0, q16, w,
-                 l, acc, m, z);
+        run_bf16<D, 16>(A, kb0, kb1, vb0, vb1, PrefixKeys<D>(A, t0, hoff, bh, nv, w, l), min(t1, np) - t0, q16, 0.0f,
+                        hbase, w, l, acc, st);
     const int r0 = max(t0, np) - np, r1 = t1 - np;
     if (r1 > r0)
-        run16<D>(A, kb0, kb1, vb0, vb1, VideoKeys16<D, true, RAG>(A, nullptr, r0, hoff, (int64_t)bh * A.R, w, l),
-                 r1 - r0, q16, w, l, acc, m, z);
-    const float zt = pair_sum(z);
+        run_bf16<D, 16>(A, kb0, kb1, vb0, vb1,
+                        VideoKeys<D, true, RAG, RAG>(A, A.k16, nullptr, r0, hoff, hbase, w, l), r1 - r0, q16, 0.0f,
+                        hbase, w, l, acc, st);
+    const float zt = pair_sum(st.z);
     if (row < A.Lp) {
         const int64_t slot = ((int64_t)bh * A.pchunks + c) * (A.ptiles * kBlk) + row;
         float *dst = A.pacc + slot * D;
@@ -1273,7 +1271,7 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
                 *reinterpret_cast<float4 *>(dst + 32 * cb + 8 * g + 4 * hf) =
                     make_float4(acc[cb][4 * g], acc[cb][4 * g + 1], acc[cb][4 * g + 2], acc[cb][4 * g + 3]);
         if (hf == 0)
-            A.pmz[slot] = make_float2(m, zt);
+            A.pmz[slot] = make_float2(st.mh, zt);
     }
 }
 
@@ -1441,11 +1439,11 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
     A.q4 = (const uint8_t *)(ws + W.q4);
     A.q4s = (const uint8_t *)(ws + W.q4s);
     A.qs8 = (const float *)(ws + W.qs8);
-    A.k8 = (const uint8_t *)(ws + W.k8);
     A.k4 = (const uint8_t *)(ws + W.k4);
     A.k4s = (const uint8_t *)(ws + W.k4s);
     A.ks8 = (const float *)(ws + W.ks8);
-    A.v8 = (const uint8_t *)(ws + W.v8);
+    A.k8 = (const uint8_t *)(ws + W.k8);
+    A.v8b = (const uint8_t *)(ws + W.v8b);
     A.v4 = (const uint8_t *)(ws + W.v4);
     A.v4s = (const uint8_t *)(ws + W.v4s);
     A.vs8 = (const float *)(ws + W.vs8);
@@ -1468,7 +1466,12 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
     A.Hv = L.s.height;
     A.Wv = L.s.width;
     A.BH = L.BH;
-    A.c4 = (float)(1.4426950408889634 / __builtin_sqrt((double)L.d));
+    {
+        // log2(e) / sqrt(d) as an unevaluated sum of two floats
+        const double c4 = 1.4426950408889634 / __builtin_sqrt((double)L.d);
+        A.c4h = (float)c4;
+        A.c4l = (float)(c4 - (double)A.c4h);
+    }
     A.Lp = px ? L.s.prefix : 0;
     A.ptiles = L.ptiles;
     A.qp = px ? (const uint16_t *)px->qp : nullptr;

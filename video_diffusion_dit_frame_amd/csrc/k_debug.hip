@@ -114,10 +114,10 @@ void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, h
     auto grid = [](int64_t n) { return (unsigned)((n + 255) / 256); };
     uint8_t *o = (uint8_t *)dst;
     switch (which) {
-    case DA2_DBG_Q_FP8: case DA2_DBG_Q_MX: case DA2_DBG_Q_MX_SCALE:
-    case DA2_DBG_K_FP8: case DA2_DBG_K_MX: case DA2_DBG_K_MX_SCALE: {
-        const int is_key = which >= DA2_DBG_K_FP8;
-        const int kind = (which - (is_key ? DA2_DBG_K_FP8 : DA2_DBG_Q_FP8));  // 0 fp8, 2 mx, 3 mx scale
+    case DA2_DBG_Q_I8: case DA2_DBG_Q_MX: case DA2_DBG_Q_MX_SCALE:
+    case DA2_DBG_K_I8: case DA2_DBG_K_MX: case DA2_DBG_K_MX_SCALE: {
+        const int is_key = which >= DA2_DBG_K_I8;
+        const int kind = (which - (is_key ? DA2_DBG_K_I8 : DA2_DBG_Q_I8));  // 0 int8, 2 mx, 3 mx scale
         const int wk = kind == 0 ? 0 : (kind == 2 ? 1 : 2);
         const int64_t total = wk == 2 ? nd / 32 : nd;
         k_unpack_qk<<<grid(total), 256, 0, st>>>(
@@ -132,10 +132,10 @@ void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, h
                                                 (const uint8_t *)(ws + W.v4s), wk, d, total, o);
         break;
     }
-    case DA2_DBG_Q_FP8_SCALE:
+    case DA2_DBG_Q_I8_SCALE:
         hipMemcpyAsync(dst, ws + W.qs8, sizeof(float) * L.BH * L.R, hipMemcpyDeviceToDevice, st);
         break;
-    case DA2_DBG_K_FP8_SCALE:
+    case DA2_DBG_K_I8_SCALE:
         hipMemcpyAsync(dst, ws + W.ks8, sizeof(float) * L.BH * L.R, hipMemcpyDeviceToDevice, st);
         break;
     case DA2_DBG_V_FP8_SCALE:

@@ -4,10 +4,11 @@
 // k_prep_qk: one workgroup per (b, h, region).  Gathers the region's 64
 // tokens (one coalesced 16-byte load per chunk, strided input), and from the
 // same LDS copy emits the pooled descriptors of Eq. (1) (fp64 sum in region
-// order / 64, signed max), the FP8 E4M3 codes with one fp32 scale per block
-// (amax / 448, codes of x * (448 / amax)), and MXFP4 E2M1 codes with one E8M0
-// exponent per token and 32 channels -- all written directly in the MFMA
-// operand layouts the attention kernel loads.
+// order / 64, signed max), the INT8 codes of the 8-bit path's Q K^T (App.
+// C.1) with one fp32 step per block (App. B.2's uniform quantizer: step
+// amax / 127, codes the nearest integers of x * (127 / amax)), and MXFP4 E2M1
+// codes with one E8M0 exponent per token and 32 channels -- all written
+// directly in the MFMA operand layouts the attention kernel loads.
 //
 // k_vamax + k_prep_v: V gets one FP8 scale per channel over all tokens (so
 // the attention accumulator changes units once, at the end of the FP8 phase)
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
             *reinterpret_cast<uint4 *>(op16 + blk * (kBlk * D) + (int64_t)u * 8) = v;
         }
     }
-    // FP8 block scale
+    // INT8 block step
     float am = 0.0f;
     for (int e = t; e < kBlk * D; e += 256)
         am = fmaxf(am, __builtin_fabsf(bf16_to_f32(tile[e])));
@@ -97,8 +98,8 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
     am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     float sc = 1.0f, inv = 0.0f;
     if (am != 0.0f) {
-        sc = am / 448.0f;
-        inv = 448.0f / am;
+        sc = am / 127.0f;
+        inv = 127.0f / am;
     }
     if (t == 0)
         s8[blk] = sc;
@@ -119,8 +120,7 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
         uint32_t w8[8];
 #pragma unroll
         for (int q = 0; q < 8; q++)
-            w8[q] = pack_e4m3x4(xv[4 * q] * inv, xv[4 * q + 1] * inv, xv[4 * q + 2] * inv,
-                                xv[4 * q + 3] * inv);
+            w8[q] = pack_i8x4(xv[4 * q] * inv, xv[4 * q + 1] * inv, xv[4 * q + 2] * inv, xv[4 * q + 3] * inv);
         uint4 *d8 = reinterpret_cast<uint4 *>(op8 + blk * (kBlk * D) + (int64_t)t * 32);
         d8[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
         d8[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
                                                 uint8_t *__restrict__ op8, float *__restrict__ s8,
                                                 uint8_t *__restrict__ op4,
                                                 uint8_t *__restrict__ op4s,
-                                                uint16_t *__restrict__ op16)
+                                                uint16_t *__restrict__ op16, uint16_t *__restrict__ op8b)
 {
     __shared__ __attribute__((aligned(16))) uint16_t tile[kBlk * D];
     const int a = blockIdx.x, bh = blockIdx.y;
@@ -228,6 +228,14 @@ __global__ __launch_bounds__(256) void k_prep_v(const uint16_t *__restrict__ x, 
         uint4 *d8 = reinterpret_cast<uint4 *>(op8 + blk * (kBlk * D) + (int64_t)t * 32);
         d8[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
         d8[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+        // the values of the FP8 codes as bf16 (exact), in the layout of the
+        // bf16 operand below: the value operand of the FP8 tier's products on
+        // the bf16 matrix core
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            *reinterpret_cast<uint4 *>(op8b + ((blk * (D / 32) + cb) * 4 + q) * 512 + l * 8) =
+                make_uint4(fp8_pair_bf16(w8[2 * q], 0), fp8_pair_bf16(w8[2 * q], 1), fp8_pair_bf16(w8[2 * q + 1], 0),
+                           fp8_pair_bf16(w8[2 * q + 1], 1));
         const int E = mx_exponent(ga);
         const float scale = pow2_e8m0(E);
         uint32_t w4[4];
@@ -351,12 +359,13 @@ void launch_prep_v(const da2_layout_s &L, const void *v, int with16, int with_me
     uint8_t *op8 = (uint8_t *)(ws + W.v8), *op4 = (uint8_t *)(ws + W.v4),
             *op4s = (uint8_t *)(ws + W.v4s);
     uint16_t *op16 = with16 ? (uint16_t *)(ws + W.v16) : nullptr;
+    uint16_t *op8b = (uint16_t *)(ws + W.v8b);
     float *s8 = (float *)(ws + W.vs8);
     float *vavg = with_mean ? (float *)(ws + W.vavg) : nullptr;
     const Geo g = layout_geo(L, ws);
 #define DA2_PREP_V(DD, RG)                                                                              \
     k_prep_v<DD, RG><<<g2, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R, g, vavg, vamax, \
-                                         op8, s8, op4, op4s, op16)
+                                         op8, s8, op4, op4s, op16, op8b)
     if (L.d == 128) {
         k_vamax<128><<<g1, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.N, vamax);
         if (L.ragged)

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libda2.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "da2.h")
 
 DBG = {name: i for i, name in enumerate([
-    "Q_FP8", "Q_FP8_SCALE", "Q_MX", "Q_MX_SCALE", "K_FP8", "K_FP8_SCALE", "K_MX", "K_MX_SCALE",
+    "Q_I8", "Q_I8_SCALE", "Q_MX", "Q_MX_SCALE", "K_I8", "K_I8_SCALE", "K_MX", "K_MX_SCALE",
     "V_FP8", "V_FP8_SCALE", "V_MX", "V_MX_SCALE", "Q_AVG", "K_AVG", "Q_MAX", "K_MAX", "KEYS",
     "SCHEDULE"])}
 
