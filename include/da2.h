@@ -215,6 +215,26 @@ size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which);
 da2_status da2_plan_timing(da2_plan_t *plan, int32_t enable);
 da2_status da2_plan_timing_read(da2_plan_t *plan, float *ms, int32_t max, int32_t *n);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * da2_plan followed by da2_attention in one call, on a workspace inside the
+ * library instead of a caller's -- a static device array of
+ * DA2_NOALLOC_BYTES on every GPU the library runs on, held until the process
+ * ends.  The caller passes the layout, Q, K, V, the budget and the output as
+ * for da2_plan and da2_attention (same rules, same result); the layout must
+ * stay alive until the call's work on the stream has completed (its host
+ * tables are copied asynchronously).  Returns DA2_ERR_WORKSPACE, before any
+ * GPU work, when da2_workspace_bytes(layout) exceeds DA2_NOALLOC_BYTES, and
+ * DA2_ERR_HIP when the array's device address cannot be obtained.  The call
+ * allocates nothing: no hipMalloc or hipFree, no host heap.  Every call on
+ * one GPU shares that GPU's array, which keeps the last call's contents
+ * (every byte a call reads it first writes on the same stream): calls that
+ * overlap on one GPU -- on different streams or from different threads --
+ * race. */
+#define DA2_NOALLOC_BYTES ((size_t)32 << 20)
+da2_status da2_forward_noalloc(const da2_layout_t *layout, const void *q, const void *k, const void *v,
+                               void *o, const da2_budget *budget, int32_t out_dtype, hipStream_t stream);
+
 /* Host-side helpers (no GPU work). */
 const char *da2_status_string(da2_status status);
 /* Constants of the fp64 exp used by the draft softmax: ln2 head, ln2 tail,

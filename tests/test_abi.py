@@ -194,3 +194,23 @@ def test_partition_agrees_with_oracle_random_shapes(orc):
         da2.lib().da2_layout_destroy(h)
         assert np.array_equal(out, tok), (Hv, Wv)
     assert 0 < rejected < 200
+
+
+def test_noalloc_refuses_a_workspace_beyond_its_array():
+    """da2_forward_noalloc returns DA2_ERR_WORKSPACE, before any GPU work,
+    when the layout needs more than DA2_NOALLOC_BYTES; a layout within it
+    is in range (its run is a GPU test)."""
+    L = da2.lib()
+    cap = da2.noalloc_bytes()
+    assert cap == 32 << 20
+    st, big = _layout(B=1, H=40, d=128, F=21, Hv=48, Wv=80)   # a Wan-14B 720p layer
+    assert st == OK
+    assert L.da2_workspace_bytes(big) > cap
+    b = da2.Budget(1000, 3000, 0.2, 0, 0, 0)
+    dummy = C.c_void_p(1 << 20)   # never dereferenced: the size check comes first
+    assert L.da2_forward_noalloc(big, dummy, dummy, dummy, dummy, C.byref(b), 1, None) == WORKSPACE
+    assert L.da2_forward_noalloc(None, dummy, dummy, dummy, dummy, C.byref(b), 1, None) == INVALID
+    L.da2_layout_destroy(big)
+    st, small = _layout(B=1, H=2, d=128, F=2, Hv=64, Wv=72)
+    assert st == OK and L.da2_workspace_bytes(small) <= cap
+    L.da2_layout_destroy(small)

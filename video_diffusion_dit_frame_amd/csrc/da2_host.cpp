@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "da2_internal.h"
 #include "da2_device.h"
 
@@ -185,6 +187,21 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
         }
     }
     L->R = shape->frames * L->Rf;
+    if (L->ragged) {
+        L->nreg = (int32_t *)malloc(sizeof(int32_t) * L->R);
+        if (!L->nreg) {
+            free(L->ftok);
+            free(L);
+            return DA2_ERR_INVALID_ARG;
+        }
+        for (int a = 0; a < L->R; a++) {
+            const int32_t *t = L->ftok + (a % L->Rf) * kBlk;
+            int n = 0;
+            while (n < kBlk && t[n] >= 0)
+                n++;
+            L->nreg[a] = n;
+        }
+    }
     L->Np = L->R * kBlk;
     L->BH = shape->batch * shape->heads;
     L->d = shape->head_dim;
@@ -198,8 +215,10 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
 
 void da2_layout_destroy(da2_layout_t *layout)
 {
-    if (layout)
+    if (layout) {
         free(layout->ftok);
+        free(layout->nreg);
+    }
     free(layout);
 }
 
@@ -240,6 +259,7 @@ da2_status da2_plan_create(const da2_layout_t *layout, void *workspace, size_t w
     if (!P)
         return DA2_ERR_INVALID_ARG;
     P->L = *layout;
+    P->L.nreg = nullptr;   // the plan keeps its own count table (upload_tables)
     if (layout->ragged) {
         const size_t bytes = sizeof(int32_t) * layout->Rf * kBlk;
         P->L.ftok = (int32_t *)malloc(bytes);
@@ -498,6 +518,58 @@ void da2_exp_constants(double *out)
     out[2] = kInvLn2;
     for (int j = 0; j < 14; j++)
         out[3 + j] = kTaylor.c[j];
+}
+
+// ---------------------------------------------------------------------------
+// Workspace inside the library, for callers that cannot allocate.  The array
+// is file-scope device memory: in host code its name is only a stand-in, so
+// every host use goes through the device address hipGetSymbolAddress returns,
+// taken once per device with that device current and kept per device.
+// ---------------------------------------------------------------------------
+namespace {
+__device__ __align__(256) char scratch[DA2_NOALLOC_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+char *scratch_dev[kMaxDevices];   // device address of scratch per device (null: not taken yet)
+
+char *scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        scratch_dev[dev] = (char *)p;
+    }
+    return scratch_dev[dev];
+}
+}  // namespace
+
+da2_status da2_forward_noalloc(const da2_layout_t *layout, const void *q, const void *k, const void *v,
+                               void *o, const da2_budget *budget, int32_t out_dtype, hipStream_t stream)
+{
+    if (!layout)
+        return DA2_ERR_INVALID_ARG;
+    if (layout->ws.total > DA2_NOALLOC_BYTES)
+        return DA2_ERR_WORKSPACE;
+    char *ws = scratch_address();
+    if (!ws)
+        return DA2_ERR_HIP;
+    // a plan on the stack over the caller's layout: the layout's own host
+    // tables serve the uploads, so nothing is allocated
+    da2_plan_s P;
+    memset(&P, 0, sizeof(P));
+    P.L = *layout;
+    P.nreg = layout->nreg;
+    P.ws = ws;
+    P.ws_bytes = DA2_NOALLOC_BYTES;
+    da2_status st = da2_plan(&P, q, k, budget, stream);
+    if (st != DA2_OK)
+        return st;
+    return da2_attention(&P, q, k, v, o, out_dtype, stream);
 }
 
 }  // extern "C"

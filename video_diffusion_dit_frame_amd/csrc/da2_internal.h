@@ -80,6 +80,8 @@ struct da2_layout_s {
     int ragged;               // 0: the 8x8 grid (closed form); 1: slot table
     int pmax;                 // most padding slots of any region (0..16)
     int32_t *ftok;            // ragged: frame slot table [Rf*64] (host, owned)
+    int32_t *nreg;            // ragged: valid tokens of every region [R] (host, owned by
+                              // the layout; a plan's copy of the layout does not use it)
     int64_t nchunk;           // rank chunks per head (head scope)
     int ptiles;               // 64-key tiles of the text prefix (ceil(prefix / 64))
     int pchunks;              // chunks of a prefix query row's key sequence (0: no prefix)

@@ -77,9 +77,10 @@ def lib():
         L.da2_plan_timing_read.argtypes = [P, P, i32, C.POINTER(i32)]
         L.da2_plan_timing_read.restype = C.c_int
         L.da2_quotas.argtypes = [i64, i32, i32, i32, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]
+        L.da2_forward_noalloc.argtypes = [P, P, P, P, P, C.POINTER(Budget), i32, P]
         for name in ("da2_layout_create", "da2_plan_create", "da2_plan", "da2_plan_from_tier_map",
                      "da2_plan_tier_map", "da2_attention", "da2_attention_prefixed",
-                     "da2_plan_debug"):
+                     "da2_plan_debug", "da2_forward_noalloc"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -266,6 +267,23 @@ class Plan:
         if getattr(self, "handle", None) and _lib is not None:
             _lib.da2_plan_destroy(self.handle)
             self.handle = None
+
+
+def noalloc_bytes() -> int:
+    """DA2_NOALLOC_BYTES of include/da2.h: the library's own workspace per GPU."""
+    with open(HEADER) as f:
+        m = re.search(r"#define DA2_NOALLOC_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def forward_noalloc(layout: Layout, q, k, v, o, hi_bp, lo_bp, lam=0.2, scope=0, stream=None, full_bp=0,
+                    skip_means=False):
+    """da2_forward_noalloc: plan + attention on the library's own workspace
+    (for callers that cannot allocate device memory)."""
+    b = Budget(int(hi_bp), int(lo_bp), float(lam), int(scope), int(full_bp), int(bool(skip_means)))
+    _check(lib().da2_forward_noalloc(layout.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                                     C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), C.byref(b),
+                                     _out_dtype(o), _stream(stream)), "da2_forward_noalloc")
 
 
 def to_device_bf16(x_u16, device="cuda") -> torch.Tensor:
