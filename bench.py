@@ -3,7 +3,7 @@
 
 One step = the whole hot path on one layer of synthetic video-DiT
 activations: da2_plan (Q/K preparation, draft scoring, ranking, schedule)
-followed by da2_attention (V preparation, phased 16-bit/FP8/MXFP4 attention
+followed by da2_attention (V preparation, phased 16-bit/8-bit/MXFP4 attention
 with the output written back in token order).  Inputs are resident in HBM before the
 timed region; Q/K/V use the [B, N, H, d] storage of DiT attention layers.
 
@@ -242,7 +242,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16+" if full or Lp else "") + "fp8_e4m3+mxfp4 (attention), f64 (draft scoring)",
+        "dtype": ("bf16+" if full or Lp else "") + "int8+fp8_e4m3+mxfp4 (attention), f64 (draft scoring)",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.d,
                    "frames": w.F, "height": w.Hv, "width": w.Wv, "tokens": w.N, "regions": R,

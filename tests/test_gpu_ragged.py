@@ -80,8 +80,8 @@ def test_operands_bit_exact(case):
     P, F, Hv, Wv = case["P"], case["F"], case["Hv"], case["Wv"]
     for name, x in (("Q", case["q"]), ("K", case["k"])):
         o = O.quant_qk(x, F, Hv, Wv)
-        assert np.array_equal(G.host(P.debug(name + "_FP8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
-        assert np.array_equal(G.host(P.debug(name + "_FP8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_I8"), np.uint8).reshape(o["c8"].shape), o["c8"]), name
+        assert np.array_equal(G.host(P.debug(name + "_I8_SCALE"), np.float32).reshape(o["s8"].shape), o["s8"]), name
         assert np.array_equal(G.host(P.debug(name + "_MX"), np.uint8).reshape(o["c4"].shape), o["c4"]), name
         assert np.array_equal(G.host(P.debug(name + "_MX_SCALE"), np.uint8).reshape(o["e4"].shape), o["e4"]), name
     o = O.quant_v(case["v"], F, Hv, Wv)
