@@ -105,9 +105,10 @@ __device__ __forceinline__ uint32_t pack_i8x4(float x0, float x1, float x2, floa
 // in the bf16 range, so the top half of its fp32 pattern is the value.
 __device__ __forceinline__ uint32_t fp8_pair_bf16(uint32_t c, int hi)
 {
-    const float a = hi ? __builtin_amdgcn_cvt_f32_fp8((int)c, 2) : __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
-    const float b = hi ? __builtin_amdgcn_cvt_f32_fp8((int)c, 3) : __builtin_amdgcn_cvt_f32_fp8((int)c, 1);
-    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c, 1.0f, true)
+                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c, 1.0f, false);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // The fp32 value 2^E for an E8M0 exponent E in [-127, 127] (2^-127 is

@@ -565,11 +565,12 @@ struct Int8Keys {
     }
     __device__ __forceinline__ int id(int i) const { return sload_i32(list + i); }
     __device__ __forceinline__ int valid(int kb) const { return RAG ? sload_i32(nreg + kb) : kBlk; }
+    // wave w copies half m = w of region kb's tile to dst + w * (half bytes)
     __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
     {
 #pragma unroll
         for (int s = 0; s < kCopies; s++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, loff,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + (w * kCopies + s) * 1024), 16, loff,
                                                      (uint32_t)kb * (kBlk * D) + (w * kCopies + s) * 1024, 0, 0);
     }
 };
@@ -618,13 +619,13 @@ __device__ __forceinline__ void logits16(uint8_t *kb0, uint8_t *kb1, const v4u (
                 0);
 }
 
-// Integer logits of one 8-bit tile (half m of the key tile in buffer m), the
+// Integer logits of one 8-bit tile (half m of the key tile at kb + m 32 D), the
 // accumulators starting at -R (an integer, |R| <= 2^22, so every sum, at
 // most 127^2 D in size, stays exact in the fp32 it is converted to).
 template <int D>
-__device__ __forceinline__ void logits8(const uint8_t *kb0, const uint8_t *kb1, const v4u (&q)[D / 16], int l,
-                                        int negR, v16f (&sc)[2])
+__device__ __forceinline__ void logits8(const uint8_t *kb, const v4u (&q)[D / 16], int l, int negR, v16f (&sc)[2])
 {
+    const uint8_t *kb0 = kb, *kb1 = kb + 32 * D;   // halves m = 0, 1
     v16i s[2];
 #pragma unroll
     for (int mm = 0; mm < 2; mm++)
@@ -659,33 +660,29 @@ __device__ __forceinline__ void mask_keys(v16f (&sc)[2], int nk, int hf)
     }
 }
 
-// Tiles whose P^T V runs on the bf16 matrix core: the 16-bit tier (TIER 16:
-// logits from the bf16 inputs, P = w as the pair hi + lo of bf16 values,
-// real units) or the 8-bit tier (TIER 8: integer logits from the INT8 codes,
-// c = sq sk c4 per tile, P = e4m3(256 w) as bf16 times the exact bf16 values
-// of the FP8 value codes, units 256 / sV).  n tiles of a key source,
-// ascending; q holds the query operand (bf16 rows, or the INT8 codes).  A
-// tile's key operand fills both key buffers (half m in buffer m), its value
-// image both value buffers.  The value copy of tile i runs under tile i's
-// logits and softmax, the key copy of tile i+1 under tile i's softmax and
-// P^T V.  Key and value buffers are distinct LDS variables, so the compiler
-// knows a copy into one never feeds reads of the other.
-template <int D, int TIER, class Keys>
-__device__ __forceinline__ void run_bf16(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0,
-                                         uint8_t *vb1, const Keys &K, int n, const v4u (&q)[D / 16], float qs,
-                                         int64_t hbase, int w, int l, v16f (&acc)[D / 32], Row &row)
+// Tiles of the 16-bit tier on the bf16 matrix core: logits from the bf16
+// inputs, P = w as the pair hi + lo of bf16 values, real units.  n tiles of
+// a key source, ascending; q holds the query rows.  A tile's key image fills
+// both key buffers (half m in buffer m), its value image both value buffers.
+// The value copy of tile i runs under tile i's logits and softmax, the key
+// copy of tile i+1 under tile i's softmax and P^T V.  Key and value buffers
+// are distinct LDS variables, so the compiler knows a copy into one never
+// feeds reads of the other.
+template <int D, class Keys>
+__device__ __forceinline__ void run_bf16(uint8_t *kb0, uint8_t *kb1, uint8_t *vb0, uint8_t *vb1, const Keys &K,
+                                         int n, const v4u (&q)[D / 16], const Scale &c, int w, int l,
+                                         v16f (&acc)[D / 32], Row &row)
 {
     constexpr int CB = D / 32;
     constexpr int NK = Keys::kCopies;              // key copies per wave and tile
     constexpr int VB = kBlk * D * 2;               // value image of a tile
     const int hf = l >> 5;
     const __amdgpu_buffer_rsrc_t vsrc = head_rsrc(K.vbase, K.vbytes);
-    const Scale c4 = scale_c4(A);
     int kb = K.id(0);
     int kbn = n > 1 ? K.id(1) : 0;
     K.issue_key(kb, w ? kb1 : kb0);
     for (int i = 0; i < n; i++) {
-        // key operand of tile i complete (both waves' halves); both waves are
+        // key image of tile i complete (both waves' halves); both waves are
         // done with the value buffer
         __builtin_amdgcn_s_waitcnt(vm_wait(0));
         __syncthreads();
@@ -697,28 +694,19 @@ __device__ __forceinline__ void run_bf16(const AttnArgs &A, uint8_t *kb0, uint8_
                 vsrc, (lds_void *)((j < D / 32 ? vb0 : vb1) + (u % (D / 16)) * 1024), 16, (uint32_t)l * 16u,
                 (uint32_t)kb * VB + u * 1024, 0, 0);
         }
-        const Scale c = TIER == 16 ? c4 : scale_fp8(qs, sload_f32(A.ks8 + hbase + kb), A);
         const int nk = Keys::kMasked ? K.valid(kb) : kBlk;
         v16f sc[2];
         float R;
         if (__builtin_amdgcn_readfirstlane(row.mh == -__builtin_huge_valf() ? 1 : 0)) {
             // first tile of the row: find its offset from a first product
-            if (TIER == 16)
-                logits16<D>(kb0, kb1, q, l, v16f{}, sc);
-            else
-                logits8<D>(kb0, kb1, q, l, 0, sc);
+            logits16<D>(kb0, kb1, q, l, v16f{}, sc);
             if (Keys::kMasked)
                 mask_keys(sc, nk, hf);
             R = pair_max(lane_max(sc));
         } else {
             R = row_offset(row, c);
-            if (TIER == 8)   // an integer offset within the exact range of the sums
-                R = __builtin_rintf(fminf(fmaxf(R, -0x1p22f), 0x1p22f));
         }
-        if (TIER == 16)
-            logits16<D>(kb0, kb1, q, l, splat_neg(R), sc);
-        else
-            logits8<D>(kb0, kb1, q, l, -(int)R, sc);
+        logits16<D>(kb0, kb1, q, l, splat_neg(R), sc);
         // both waves are done with the key buffer: refill it with tile i+1
         __syncthreads();
         const bool more = i + 1 < n;
@@ -730,34 +718,23 @@ __device__ __forceinline__ void run_bf16(const AttnArgs &A, uint8_t *kb0, uint8_
         bool raised;
         const float bias = tile_update(row, c, R, pair_max(lane_max(sc)), al, raised);
         rescale<CB>(acc, al);
-        float z = 0.0f;
-        // P^T chunk t: this lane's keys 32 hf + 8 t .. + 7 (slots 8 t ..);
-        // the 16-bit tier's residual chunk in pl
+        // P^T chunk t: this lane's keys 32 hf + 8 t .. + 7 (slots 8 t ..), as
+        // hi and residual lo
         v4u ph[4], pl[4];
+        float z = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             const int mm = t >> 1, r0 = 8 * (t & 1);
             float e[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
+            for (int j = 0; j < 8; j++)
                 e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + j], c.ch, bias));
-                z += e[j];
-            }
-            if (TIER == 16) {
+            z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint32_t h = pk_bf16(e[2 * j], e[2 * j + 1]);
-                    ph[t][j] = h;
-                    pl[t][j] = pk_bf16(e[2 * j] - __uint_as_float(h << 16),
-                                       e[2 * j + 1] - __uint_as_float(h & 0xffff0000u));
-                }
-            } else {
-                const uint32_t w0 = (uint32_t)pk_fp8_256(e[0], e[1], e[2], e[3]);
-                const uint32_t w1 = (uint32_t)pk_fp8_256(e[4], e[5], e[6], e[7]);
-                ph[t][0] = fp8_pair_bf16(w0, 0);
-                ph[t][1] = fp8_pair_bf16(w0, 1);
-                ph[t][2] = fp8_pair_bf16(w1, 0);
-                ph[t][3] = fp8_pair_bf16(w1, 1);
+            for (int j = 0; j < 4; j++) {
+                const uint32_t h = pk_bf16(e[2 * j], e[2 * j + 1]);
+                ph[t][j] = h;
+                pl[t][j] = pk_bf16(e[2 * j] - __uint_as_float(h << 16), e[2 * j + 1] - __uint_as_float(h & 0xffff0000u));
             }
         }
         row.z += z;
@@ -773,14 +750,194 @@ __device__ __forceinline__ void run_bf16(const AttnArgs &A, uint8_t *kb0, uint8_
             for (int t = 0; t < 4; t++) {
                 const v8bf vv = as_bf16x8(lds_v4u(chunk16<D>(vb0, vb1, cb * 4 + t) + l * 16));
                 acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(ph[t]), acc[cb], 0, 0, 0);
-                if (TIER == 16)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(pl[t]), acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, as_bf16x8(pl[t]), acc[cb], 0, 0, 0);
             }
         kb = kbn;
         if (i + 2 < n)
             kbn = K.id(i + 2);
     }
     // the next segment or phase refills the buffers
+    __syncthreads();
+}
+
+template <int N>
+struct Par {
+    static constexpr int value = N;
+};
+
+// Tiles of the 8-bit tier, software pipelined: integer logits from the INT8
+// codes on the integer matrix core (c = sq sk c4 per tile), P = e4m3(256 w) as
+// bf16 times the exact bf16 values of the FP8 value codes on the bf16 matrix
+// core (units 256 / sV).  n tiles of the schedule's list, ascending.
+//   Step i forms the weights of tile i on the vector unit while the matrix
+// cores compute P^T V of tile i-1 and the logits of tile i+1.  The INT8 key
+// tile (both halves) sits in kb0; the value images of even tiles go to the
+// pair (vb0, vb1), of odd tiles to (kb1, xb).  Step i copies V(i) into its
+// pair (last read by step i-1), reads K(i+1) from kb0 and issues its logits,
+// then, once both waves are done reading kb0, copies K(i+2): every copy has
+// about a step to land.
+template <int D, bool RAG>
+__device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0, uint8_t *vb1,
+                                       uint8_t *xb, const int32_t *lst, int n, const v4u (&q)[D / 16], float qs,
+                                       int64_t hbase, int w, int l, v16f (&acc)[D / 32], Row &row)
+{
+    constexpr int CB = D / 32;
+    constexpr int VB = kBlk * D * 2;               // value image of a tile
+    const int hf = l >> 5;
+    const Int8Keys<D, RAG> K(A, lst, hbase, w, l);
+    const __amdgpu_buffer_rsrc_t vsrc = head_rsrc(K.vbase, K.vbytes);
+    v16f Sa[2], Sb[2];   // logits of tiles of alternating parity
+    v4u P[4];            // bf16 weights of the previous tile, then of this one
+    float R, al = 1.0f;
+    int kr0 = sload_i32(lst), kr1 = n > 1 ? sload_i32(lst + 1) : 0, kr2 = n > 2 ? sload_i32(lst + 2) : 0;
+    int nk0 = RAG ? sload_i32(A.nreg + kr0) : kBlk;
+
+    auto issue_value = [&](int kbv, uint8_t *b0, uint8_t *b1) {
+#pragma unroll
+        for (int j = 0; j < VB / 2048; j++) {
+            // unit 2j + w lies in the first buffer exactly when j < D / 32
+            const int u = 2 * j + w;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vsrc, (lds_void *)((j < D / 32 ? b0 : b1) + (u % (D / 16)) * 1024), 16, (uint32_t)l * 16u,
+                (uint32_t)kbv * VB + u * 1024, 0, 0);
+        }
+    };
+    // integer logits of the tile in kb0, accumulators starting at -Ri
+    auto logits = [&](int Ri, v16f (&sn)[2]) {
+        v16i s[2];
+        v16i neg;
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            neg[j] = -Ri;
+#pragma unroll
+        for (int e = 0; e < D / 32; e++) {
+            v4i k[2];
+#pragma unroll
+            for (int mm = 0; mm < 2; mm++)
+                k[mm] = __builtin_bit_cast(v4i, lds_v4u(kb0 + mm * 32 * D + ((e >> 1) * 64 + l) * 32 + 16 * (e & 1)));
+#pragma unroll
+            for (int mm = 0; mm < 2; mm++)
+                s[mm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k[mm], __builtin_bit_cast(v4i, q[e]), e ? s[mm] : neg, 0,
+                                                             0, 0);
+        }
+#pragma unroll
+        for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                sn[mm][r] = (float)s[mm][r];
+    };
+    // R' = M / c rounded to an integer within the exact range of the sums
+    auto offset = [&](const Scale &c) {
+        return __builtin_rintf(fminf(fmaxf(row_offset(row, c), -0x1p22f), 0x1p22f));
+    };
+    // P^T V of the previous tile (weights P) from the pair (v0, v1)
+    auto pv = [&](uint8_t *v0, uint8_t *v1) {
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++) {
+            v4u vv[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                vv[t] = lds_v4u(chunk16<D>(v0, v1, cb * 4 + t) + l * 16);
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv[t]), as_bf16x8(P[t]), acc[cb], 0, 0, 0);
+        }
+    };
+    auto settle = [&]() {
+        if (__any(al != 1.0f)) {
+#pragma unroll
+            for (int cb = 0; cb < CB; cb++)
+                acc[cb] *= al;
+        }
+    };
+    // step i of parity PAR: sc the logits of tile i (offset R), P the
+    // weights of tile i-1, al the factor acc owes before their product
+    auto step = [&](auto par, int i, v16f (&sc)[2], v16f (&sn)[2]) {
+        constexpr int PAR = decltype(par)::value;
+        uint8_t *vw0 = PAR ? kb1 : vb0, *vw1 = PAR ? xb : vb1;   // pair of tile i
+        uint8_t *vr0 = PAR ? vb0 : kb1, *vr1 = PAR ? vb1 : xb;   // pair of tile i-1
+        // K(i+1) and V(i-1) complete; both waves are done with step i-1
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        __syncthreads();
+        settle();
+        issue_value(kr0, vw0, vw1);
+        if (RAG)
+            mask_keys(sc, nk0, hf);
+        // running max of tile i; the offset and logits of tile i+1
+        const Scale c = scale_fp8(qs, sload_f32(A.ks8 + hbase + kr0), A);
+        bool raised;
+        float al_i;
+        const float bias = tile_update(row, c, R, pair_max(lane_max(sc)), al_i, raised);
+        float Rn = 0.0f;
+        if (i + 1 < n) {
+            Rn = offset(scale_fp8(qs, sload_f32(A.ks8 + hbase + kr1), A));
+            logits((int)Rn, sn);
+        }
+        // both waves are done reading kb0: refill it with tile i+2
+        __syncthreads();
+        if (i + 2 < n)
+            K.issue_key(kr2, kb0);
+        // P^T V of tile i-1 on the matrix core, then the weights of tile i
+        if (i > 0)
+            pv(vr0, vr1);
+        float z = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const int mm = t >> 1, r0 = 8 * (t & 1);
+            float e[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + j], c.ch, bias));
+            z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            const uint32_t w0 = (uint32_t)pk_fp8_256(e[0], e[1], e[2], e[3]);
+            const uint32_t w1 = (uint32_t)pk_fp8_256(e[4], e[5], e[6], e[7]);
+            P[t][0] = fp8_pair_bf16(w0, 0);
+            P[t][1] = fp8_pair_bf16(w0, 1);
+            P[t][2] = fp8_pair_bf16(w1, 0);
+            P[t][3] = fp8_pair_bf16(w1, 1);
+        }
+        row.z += z;
+        al = al_i;
+        R = Rn;
+        kr0 = kr1;
+        kr1 = kr2;
+        kr2 = sload_i32(lst + min(i + 3, n - 1));
+        if (RAG)
+            nk0 = sload_i32(A.nreg + kr0);
+    };
+
+    // prologue: the logits of tile 0 (a fresh row first finds its offset)
+    K.issue_key(kr0, kb0);
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(row.mh == -__builtin_huge_valf() ? 1 : 0)) {
+        logits(0, Sa);
+        if (RAG)
+            mask_keys(Sa, nk0, hf);
+        R = pair_max(lane_max(Sa));
+    } else {
+        R = offset(scale_fp8(qs, sload_f32(A.ks8 + hbase + kr0), A));
+    }
+    logits((int)R, Sa);
+    __syncthreads();
+    if (n > 1)
+        K.issue_key(kr1, kb0);
+    int i = 0;
+    for (; i + 1 < n; i += 2) {
+        step(Par<0>{}, i, Sa, Sb);
+        step(Par<1>{}, i + 1, Sb, Sa);
+    }
+    if (i < n)
+        step(Par<0>{}, i, Sa, Sb);
+    // drain: P^T V of the last tile
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __syncthreads();
+    settle();
+    if ((n - 1) & 1)
+        pv(kb1, xb);
+    else
+        pv(vb0, vb1);
+    // the next phase refills the buffers
     __syncthreads();
 }
 
@@ -856,9 +1013,10 @@ struct Attn {
     static constexpr int KC = D / 64;   // 64-channel steps of QK^T
     static constexpr int CB = D / 32;   // 32-channel blocks of the output
     const AttnArgs &A;
-    // key and value buffers, two of each; four distinct LDS variables, so
-    // that the compiler can tell a copy into one from a read of another
-    uint8_t *kb0, *kb1, *vb0, *vb1;
+    // key and value buffers, two of each, and a fifth buffer (the 8-bit
+    // tier's second value pair is kb1 + xb); distinct LDS variables, so that
+    // the compiler can tell a copy into one from a read of another
+    uint8_t *kb0, *kb1, *vb0, *vb1, *xb;
     const int32_t *list;   // key regions of the MXFP4 tiles, ascending
     int64_t hbase;
     Src src;
@@ -959,9 +1117,12 @@ struct Attn {
         const float bias = tile_update(row, c, R, dm, al, raised);
         ec = fp4_exponent(gm, c.ch, bias);
         const float pscale = ec ? __uint_as_float((uint32_t)ec << 23) : __uint_as_float(0x00400000u);
-        // the next logits start at -R' (R' = M / c), refreshed when a maximum moved
+        // the next logits start at -R' (R' = M / c), refreshed when a maximum
+        // moved (a branch: the empty asm keeps the compiler from turning the
+        // refresh into sixteen selects on every step)
         if (__any(raised)) {
             R = row_offset(row, c);
+            asm volatile("" ::: "memory");
             negR = splat_neg(R);
         }
         read_v4<D>(vr, l, 0, CB / 2, V);
@@ -1110,18 +1271,16 @@ struct Attn {
                 qt = slot_token<RAG>(A.geo, a, 0);
             load_q16<D>(A.q + hoff + (int64_t)qt * A.osn, l, q16);
             if (np > 0)
-                run_bf16<D, 16>(A, kb0, kb1, vb0, vb1, PrefixKeys<D>(A, 0, hoff, bh, nv, w, l), np, q16, qs, hbase, w,
-                                l, acc, row);
+                run_bf16<D>(kb0, kb1, vb0, vb1, PrefixKeys<D>(A, 0, hoff, bh, nv, w, l), np, q16, scale_c4(A), w, l,
+                            acc, row);
             if (n16 > 0)
-                run_bf16<D, 16>(A, kb0, kb1, vb0, vb1,
-                                VideoKeys<D, false, RAG, RAG>(A, A.k16, list16, 0, hoff, hbase, w, l), n16, q16, qs,
-                                hbase, w, l, acc, row);
+                run_bf16<D>(kb0, kb1, vb0, vb1, VideoKeys<D, false, RAG, RAG>(A, A.k16, list16, 0, hoff, hbase, w, l),
+                            n16, q16, scale_c4(A), w, l, acc, row);
         }
         if (n8 > 0) {
             vunits(true);
             load_q8<D>(A.q8 + qblk * (kBlk * D), w, l, q16);
-            run_bf16<D, 8>(A, kb0, kb1, vb0, vb1, Int8Keys<D, RAG>(A, list8, hbase, w, l), n8, q16, qs, hbase, w, l,
-                           acc, row);
+            run_i8<D, RAG>(A, kb0, kb1, vb0, vb1, xb, list8, n8, q16, qs, hbase, w, l, acc, row);
             vunits(false);
         }
     }
@@ -1190,6 +1349,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     __shared__ __attribute__((aligned(1024))) uint8_t kb1[kBlk * D];
     __shared__ __attribute__((aligned(1024))) uint8_t vb0[kBlk * D];
     __shared__ __attribute__((aligned(1024))) uint8_t vb1[kBlk * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t xb[kBlk * D];
 
     // XCD-aware work mapping.  Workgroups are dealt to the 8 XCDs round robin
     // (block L runs on XCD L % 8).  Every XCD walks the heads in the same
@@ -1210,7 +1370,7 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t qblk = (int64_t)bh * R + a;
 
-    Attn<D, RAG, PMAX> S{A, kb0, kb1, vb0, vb1};
+    Attn<D, RAG, PMAX> S{A, kb0, kb1, vb0, vb1, xb};
     S.init(w, bh, qblk);
     const int n16 = sload_i32(A.cnt + qblk * kTargets);
     const int n8 = sload_i32(A.cnt + qblk * kTargets + 1);
@@ -1252,13 +1412,12 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
     const int np = (nv + kBlk - 1) / kBlk;
     const int t0 = c * kPrefixChunkTiles, t1 = min(t0 + kPrefixChunkTiles, np + A.R);
     if (t0 < np)
-        run_bf16<D, 16>(A, kb0, kb1, vb0, vb1, PrefixKeys<D>(A, t0, hoff, bh, nv, w, l), min(t1, np) - t0, q16, 0.0f,
-                        hbase, w, l, acc, st);
+        run_bf16<D>(kb0, kb1, vb0, vb1, PrefixKeys<D>(A, t0, hoff, bh, nv, w, l), min(t1, np) - t0, q16,
+                    scale_c4(A), w, l, acc, st);
     const int r0 = max(t0, np) - np, r1 = t1 - np;
     if (r1 > r0)
-        run_bf16<D, 16>(A, kb0, kb1, vb0, vb1,
-                        VideoKeys<D, true, RAG, RAG>(A, A.k16, nullptr, r0, hoff, hbase, w, l), r1 - r0, q16, 0.0f,
-                        hbase, w, l, acc, st);
+        run_bf16<D>(kb0, kb1, vb0, vb1, VideoKeys<D, true, RAG, RAG>(A, A.k16, nullptr, r0, hoff, hbase, w, l),
+                    r1 - r0, q16, scale_c4(A), w, l, acc, st);
     const float zt = pair_sum(st.z);
     if (row < A.Lp) {
         const int64_t slot = ((int64_t)bh * A.pchunks + c) * (A.ptiles * kBlk) + row;
