@@ -15,9 +15,19 @@ step's attention call is da2_attention_prefixed.
 Prints one JSON line.  value = dense-equivalent attention TFLOP/s of the
 complete step (4 B H N^2 d per step; with a prefix, 4 B H (Lp + N)(nv + N) d
 over the nv valid prefix keys); roofline = the attention kernel against
-the tier-weighted MFMA peak (its achieved executed FLOP/s over
-(F16 + F8 + F4) / (F16/P16 + F8/P8 + F4/P4)); cpu_baseline = the CPU oracle timed on a
-bounded sample and extrapolated to the same unit.
+the MFMA peak weighted by where each product runs (16-bit tier: bf16; 8-bit
+tier: Q K^T on INT8, P V on bf16; MXFP4 tier: FP4), i.e. its achieved
+algorithmic FLOP/s over F / sum(F_part / P_part); cpu_baseline = the CPU
+oracle timed on a bounded sample and extrapolated to the same unit.  The
+same CPU leg checks the GPU result: one extra call with an fp32 output
+after the timed steps, compared on the sampled query regions of head 0
+with the oracle (rel-L2, max-abs, max-abs beyond the oracle's band bound)
+and, on sampled rows, with dense fp64 attention ("accuracy").
+
+--sweep runs the workload's budget points in turn (default workload: the
+Wan-14B CFG pair at B = 2), one JSON line per point.  --cold-l2 writes
+1 GiB before every timed step, so every step starts with cold caches, and
+times the steps with events that exclude the flush.
 """
 from __future__ import annotations
 
@@ -33,7 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16 MFMA
-PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense FP8 MFMA
+PEAK_INT8 = 5000.0   # TOPS, MI355X dense INT8 MFMA
 PEAK_FP4 = 10100.0   # TFLOP/s, MI355X dense FP4 MFMA
 
 
@@ -56,6 +66,10 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain copy kernel of 1 GiB before the steps (reference for "
                          "HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="every budget point of the workload (default sweep-wan14b-cfg), one line each")
+    ap.add_argument("--cold-l2", action="store_true",
+                    help="flush the caches with a 1 GiB write before every timed step")
     return ap.parse_args()
 
 
@@ -83,17 +97,25 @@ def measured_traffic(workload, budget, full_bp):
     return float(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, q, k, v, hi, lo, full):
-    """Time the oracle (as it stands) on one head: the full plan, then tiered
-    attention on 1 query region and on 401 evenly spaced ones (about 10 s of
-    CPU work on 16 host cores).  The per-head
-    fixed part (operand quantization) and the per-region part follow from the
-    two timings; the head total is extrapolated to all regions and heads."""
+N_ACC_REGIONS = 16   # query regions of head 0 compared with the oracle
+N_ACC_DENSE = 64     # of their rows compared with dense fp64 attention
+
+
+def cpu_baseline(w, q, k, v, hi, lo, full, sm, gpu_head0, tier_head0):
+    """The CPU leg: time the oracle (as it stands) on one head -- the full
+    plan, then tiered attention on 1 query region and on 401 evenly spaced
+    ones (about 10 s of CPU work on 16 host cores).  The per-head fixed part
+    (operand quantization) and the per-region part follow from the two
+    timings; the head total is extrapolated to all regions and heads.  The
+    same leg compares the GPU result of head 0 (gpu_head0: fp32 [N, d] in
+    token order, tier_head0: its tier map) with the oracle on
+    N_ACC_REGIONS query regions and with dense fp64 attention on
+    N_ACC_DENSE of their rows.  Returns (cpu_baseline, accuracy)."""
     from oracle import oracle as O
 
     qs, ks, vs = q[:1, :1].copy(), k[:1, :1].copy(), v[:1, :1].copy()
     t0 = time.perf_counter()
-    pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam, full_bp=full)
+    pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam, full_bp=full, skip_means=sm)
     t_plan = time.perf_counter() - t0
     R = w.R
     n_many = 401
@@ -103,7 +125,7 @@ def cpu_baseline(w, q, k, v, hi, lo, full):
     O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=sel1)
     t1 = time.perf_counter() - t0
     t0 = time.perf_counter()
-    O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=selm)
+    ref_m = O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=selm)
     tm = time.perf_counter() - t0
     per_region = max((tm - t1) / (n_many - 1), 1e-9)
     per_head_fixed = max(t1 - per_region, 0.0)
@@ -111,7 +133,7 @@ def cpu_baseline(w, q, k, v, hi, lo, full):
     total = t_head * w.B * w.H
     dense_flop = 4.0 * w.B * w.H * float(w.N) ** 2 * w.d
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {
+    base = {
         "value": dense_flop / total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
@@ -122,28 +144,38 @@ def cpu_baseline(w, q, k, v, hi, lo, full):
                    % (w.B * w.H, t_plan, n_many, t1, tm, per_head_fixed, per_region, R,
                       w.B * w.H, total)),
     }
+    # accuracy of the GPU result on sampled query regions of head 0
+    acc_regions = np.array([(j * R) // N_ACC_REGIONS for j in range(N_ACC_REGIONS)], np.int32)
+    ref, amb = O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=acc_regions, amb=True)
+    perm = O.layout(w.F, w.Hv, w.Wv)
+    tok = perm[(acc_regions[:, None] * 64 + np.arange(64)).ravel()]
+    keep = tok >= 0
+    ref = ref.reshape(-1, w.d)[keep]
+    amb = amb.reshape(-1, w.d)[keep]
+    got = gpu_head0[tok[keep]].astype(np.float64)
+    err = np.abs(got - ref)
+    rows = tok[keep][np.linspace(0, keep.sum() - 1, N_ACC_DENSE).astype(np.int64)]
+    dn = O.dense(qs, ks, vs, rows.astype(np.int32))[0, 0]
+    gd = gpu_head0[rows].astype(np.float64)
+
+    def rel(a, b):
+        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+    accuracy = {
+        "head": [0, 0],
+        "tier_map_bit_exact": bool(np.array_equal(tier_head0, pl["tier"][0, 0])),
+        "vs_oracle": {"rows": int(keep.sum()), "query_regions": N_ACC_REGIONS, "rel_l2": rel(got, ref),
+                      "max_abs": float(err.max()), "max_abs_beyond_band": float((err - amb).max())},
+        "vs_dense_fp64": {"rows": N_ACC_DENSE, "rel_l2": rel(gd, dn), "max_abs": float(np.abs(gd - dn).max())},
+        "output": "fp32 (one extra call after the timed steps)",
+    }
+    return base, accuracy
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this operator shards over (batch, head) with no "
-              "exchange, so a multi-GPU run is not part of this benchmark (got --gpus %d)"
-              % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    import torch
-
-    from video_diffusion_dit_frame_amd import configs, da2, synth
-
-    w = configs.WORKLOADS[args.workload]
-    hi, lo = w.budgets[args.budget]
-    hi = hi if args.hi_bp is None else args.hi_bp
-    lo = lo if args.lo_bp is None else args.lo_bp
-    full = args.full_bp
+def measure(args, w, hi, lo, full, q, k, v, torch, da2, synth):
+    """One workload point: warmup, timed steps, roofline, CPU leg.  Returns
+    the JSON record."""
     dev = torch.device("cuda:0")
-    print("[bench] generating %s inputs (B=%d H=%d N=%d d=%d)" % (w.name, w.B, w.H, w.N, w.d),
-          file=sys.stderr, flush=True)
-    q, k, v = synth.make_qkv(w.B, w.H, w.F, w.Hv, w.Wv, w.d, w.seed, w.outliers)
     Lp = args.prefix
     nv = Lp if args.prefix_valid is None else min(max(args.prefix_valid, 0), Lp)
     if Lp:
@@ -171,13 +203,13 @@ def main():
     P = da2.Plan(L)
     stream = torch.cuda.current_stream()
     valid = torch.full((w.B,), nv, dtype=torch.int32, device=dev) if Lp else None
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.cold_l2 else None
 
-    def attend():
+    def attend(out=o, outp=oj[:, :, :Lp]):
         if Lp:
-            P.attention_prefixed(qd, kd, vd, o, qj[:, :, :Lp], kj[:, :, :Lp], vj[:, :, :Lp],
-                                 oj[:, :, :Lp], valid, stream)
+            P.attention_prefixed(qd, kd, vd, out, qj[:, :, :Lp], kj[:, :, :Lp], vj[:, :, :Lp], outp, valid, stream)
         else:
-            P.attention(qd, kd, vd, o, stream)
+            P.attention(qd, kd, vd, out, stream)
 
     sm = args.skip_means
 
@@ -185,7 +217,8 @@ def main():
         P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full, skip_means=sm)
         attend()
 
-    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    print("[bench] %s budget (bf16 %d, 8-bit %d, MXFP4 %d): warmup %d"
+          % (w.name, full, hi, lo, args.warmup), file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -195,6 +228,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))   # 1 GiB written: caches cold for the step
         ev[i][0].record(stream)
         P.plan(qd, kd, hi, lo, w.lam, 0, stream, full_bp=full, skip_means=sm)
         ev[i][1].record(stream)
@@ -205,6 +240,9 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     plan_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     attn_call_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    if flush is not None:
+        # the flush is not part of the step: time the steps by their events
+        ms_step = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
     kt = P.timing_read()
     attn_kernel_ms = float(np.mean(kt)) if len(kt) else float("nan")
     P.timing(False)
@@ -226,8 +264,9 @@ def main():
     fx = f16 + f8 + f4
     dense_flop = 4.0 * w.B * w.H * float(Lp + w.N) * float(nv + w.N) * w.d
     t_attn = attn_kernel_ms * 1e-3
-    wsum = f16 / PEAK_BF16 + f8 / PEAK_FP8 + f4 / PEAK_FP4
-    peak_eff = fx / wsum if fx > 0 else PEAK_FP8
+    # where each product runs: 8-bit tier Q K^T on INT8, its P V on bf16
+    wsum = f16 / PEAK_BF16 + 0.5 * f8 / PEAK_INT8 + 0.5 * f8 / PEAK_BF16 + f4 / PEAK_FP4
+    peak_eff = fx / wsum if fx > 0 else PEAK_INT8
     achieved = fx / t_attn / 1e12
     util = wsum / 1e12 / t_attn
 
@@ -246,9 +285,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.d,
                    "frames": w.F, "height": w.Hv, "width": w.Wv, "tokens": w.N, "regions": R,
-                   "budget_bp": ({"bf16": full} if full else {}) | {"fp8": hi, "mxfp4": lo},
+                   "budget_bp": ({"bf16": full} if full else {}) | {"8bit": hi, "mxfp4": lo},
                    "lambda": w.lam, "ranking": "head",
-                   "storage": "[B,N,H,d] bf16", "output": "bf16"}
+                   "storage": "[B,N,H,d] bf16", "output": "bf16",
+                   "caches": "cold (1 GiB written before every step)" if flush is not None else "warm"}
                   | ({"prefix": Lp, "prefix_valid": nv} if Lp else {})
                   | ({"skip_means": True} if sm else {}),
         "plan_ms": plan_ms,
@@ -258,14 +298,50 @@ def main():
         "tier_weighted_mfma_util": util,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak_eff, "unit": "TFLOP/s",
                      "frac": achieved / peak_eff,
-                     "traffic": None if Lp or sm else measured_traffic(w.name, [hi, lo], full),
+                     "traffic": None if Lp or sm or flush is not None
+                     else measured_traffic(w.name, [hi, lo], full),
                      "kernel": "k_attn",
-                     "peak_basis": "tier-weighted bf16 2.5 / FP8 5.0 / FP4 10.1 PFLOP/s"},
+                     "peak_basis": "bf16 2.5 PFLOP/s for the 16-bit tier and the 8-bit tier's P V, "
+                                   "INT8 5.0 POPS for the 8-bit tier's Q K^T, FP4 10.1 for MXFP4, "
+                                   "weighted by algorithmic flops"},
     }
-    if not args.no_cpu_baseline and not Lp and not sm:
-        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, hi, lo, full)
-    print(json.dumps(out), flush=True)
+    if not args.no_cpu_baseline and not Lp:
+        # one more call with an fp32 output, for the CPU leg's accuracy check
+        o32 = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.float32, device=dev).permute(0, 2, 1, 3)
+        attend(o32)
+        torch.cuda.synchronize()
+        gpu_head0 = o32[0, 0].cpu().numpy()
+        tier_head0 = P.tier_map()[0, 0].cpu().numpy()
+        del o32
+        print("[bench] CPU leg: oracle baseline and accuracy", file=sys.stderr, flush=True)
+        out["cpu_baseline"], out["accuracy"] = cpu_baseline(w, q, k, v, hi, lo, full, sm, gpu_head0, tier_head0)
+    del P, L, qj, kj, vj, oj, flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this operator shards over (batch, head) with no "
+              "exchange, so a multi-GPU run is not part of this benchmark (got --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from video_diffusion_dit_frame_amd import configs, da2, synth
+
+    name = "sweep-wan14b-cfg" if args.sweep and args.workload == "wan14b-720p" else args.workload
+    w = configs.WORKLOADS[name]
+    print("[bench] generating %s inputs (B=%d H=%d N=%d d=%d)" % (w.name, w.B, w.H, w.N, w.d),
+          file=sys.stderr, flush=True)
+    q, k, v = synth.make_qkv(w.B, w.H, w.F, w.Hv, w.Wv, w.d, w.seed, w.outliers)
+    points = list(w.budgets) if args.sweep else [w.budgets[args.budget]]
+    for hi, lo in points:
+        hi = hi if args.hi_bp is None or args.sweep else args.hi_bp
+        lo = lo if args.lo_bp is None or args.sweep else args.lo_bp
+        out = measure(args, w, hi, lo, args.full_bp, q, k, v, torch, da2, synth)
+        print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
