@@ -30,8 +30,9 @@
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - token order of the input is (frame, y, x) raster;
- *   - the partition of a frame: R_f = ceil(HW/64) regions of
- *     floor(HW/R_f) or ceil(HW/R_f) tokens (balanced across the frame);
+ *   - the partition of a frame: R_f = ceil(HW/C) regions of
+ *     floor(HW/R_f) or ceil(HW/R_f) tokens (balanced across the frame),
+ *     C the block capacity (64 by default; App. C.2's study uses 128);
  *     candidates are bands of whole rows or columns walked as column
  *     snakes and cut into consecutive pieces; the smallest total perimeter
  *     wins; valid tokens take slots in raster order, padding slots follow
@@ -43,6 +44,10 @@
  *   - row sums of the draft softmax are sequential over key regions;
  *   - ranking key is the bit pattern of fp32(A); ties by ascending pair index;
  *   - quotas: cumulative counts T16, T16+T8, T16+T8+T4, each rounded half up;
+ *   - regions of capacity C > 64 run as C/64 tiles of 64 positions in slot
+ *     order, every tile of a region pair taking the pair's tier; the
+ *     quantization blocks below stay 64 tokens; block-mean tiles only at
+ *     C = 64;
  *   - INT8 Q/K step amax/127 per 64-token block (code = nearest integer of
  *     x 127/amax, ties to even, the product in fp32), FP8 V scale per channel
  *     over all tokens, MXFP4 groups along channels for Q/K and along keys
@@ -66,7 +71,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define OR_BLK 64 /* tokens per region: an 8x8 square */
+#define OR_BLK 64 /* tokens per tile (and per region at the default capacity C = 64) */
 
 /* ------------------------------------------------------------------ */
 /* bf16 and IEEE helpers                                               */
@@ -318,31 +323,34 @@ int or_partition(int Hv, int Wv, int32_t *tok, int32_t *nvalid)
     return or_partition_c(Hv, Wv, OR_BLK, tok, nvalid);
 }
 
-/* Regions of an F x Hv x Wv video (F R_f), or -1 when Hv x Wv has no
- * partition. */
-int or_regions(int F, int Hv, int Wv)
+/* Regions of an F x Hv x Wv video at block capacity C (F R_f with
+ * R_f = ceil(Hv Wv / C), App. C.2), or -1 when Hv x Wv has no partition. */
+int or_regions(int F, int Hv, int Wv, int C)
 {
     int orient;
     int64_t per;
-    if (F <= 0) return -1;
+    if (F <= 0 || C < 1) return -1;
     int32_t *bands = malloc(sizeof(int32_t) * (Hv + Wv > 0 ? Hv + Wv : 1));
-    int m = or_partition_bands(Hv, Wv, &orient, bands, &per);
+    int32_t *pieces = malloc(sizeof(int32_t) * (Hv + Wv > 0 ? Hv + Wv : 1));
+    int m = or_partition_bands_c(Hv, Wv, C, &orient, bands, pieces, &per);
     free(bands);
-    return m < 0 ? -1 : F * ((Hv * Wv + OR_BLK - 1) / OR_BLK);
+    free(pieces);
+    return m < 0 ? -1 : F * ((Hv * Wv + C - 1) / C);
 }
 
-/* perm[pos] (pos < F R_f 64) = original token index of reordered position
- * pos, -1 for padding.  Region a = f R_f + r covers frame f's region r. */
-int or_layout(int F, int Hv, int Wv, int32_t *perm)
+/* perm[pos] (pos < F R_f C) = original token index of reordered position
+ * pos, -1 for padding.  Region a = f R_f + r covers frame f's region r and
+ * positions a C .. a C + C - 1; its tokens take the first of them. */
+int or_layout(int F, int Hv, int Wv, int C, int32_t *perm)
 {
-    if (or_regions(F, Hv, Wv) < 0)
+    if (or_regions(F, Hv, Wv, C) < 0)
         return -1;
-    int Rf = (Hv * Wv + OR_BLK - 1) / OR_BLK;
-    int32_t *tok = malloc(sizeof(int32_t) * Rf * OR_BLK), *nv = malloc(sizeof(int32_t) * Rf);
-    or_partition(Hv, Wv, tok, nv);
+    int Rf = (Hv * Wv + C - 1) / C;
+    int32_t *tok = malloc(sizeof(int32_t) * Rf * C), *nv = malloc(sizeof(int32_t) * Rf);
+    or_partition_c(Hv, Wv, C, tok, nv);
     for (int f = 0; f < F; f++)
-        for (int i = 0; i < Rf * OR_BLK; i++)
-            perm[(size_t)f * Rf * OR_BLK + i] = tok[i] < 0 ? -1 : f * Hv * Wv + tok[i];
+        for (int i = 0; i < Rf * C; i++)
+            perm[(size_t)f * Rf * C + i] = tok[i] < 0 ? -1 : f * Hv * Wv + tok[i];
     free(tok);
     free(nv);
     return 0;
@@ -350,23 +358,23 @@ int or_layout(int F, int Hv, int Wv, int32_t *perm)
 
 /* ------------------------------------------------------------------ */
 /* O2 pooled descriptors: [DA2] Sec. 3.1 Eq. (1), App. C.1.             */
-/* X is one head, [N][d] bf16.  avg[a][c] = (sum over the region's n_a  */
-/* valid tokens in slot order, fp64) / n_a; mx[a][c] = signed max over  */
-/* the valid tokens, first occurrence kept on equal values.  Padding    */
-/* slots (perm -1) take no part.                                        */
+/* X is one head, [N][d] bf16; regions of C slots.  avg[a][c] = (sum    */
+/* over the region's n_a valid tokens in slot order, fp64) / n_a;       */
+/* mx[a][c] = signed max over the valid tokens, first occurrence kept   */
+/* on equal values.  Padding slots (perm -1) take no part.              */
 /* ------------------------------------------------------------------ */
-void or_pool_head(const uint16_t *X, int d, const int32_t *perm, int R,
+void or_pool_head(const uint16_t *X, int d, const int32_t *perm, int R, int C,
                   double *avg, float *mx)
 {
     for (int a = 0; a < R; a++) {
         int na = 0;
-        while (na < OR_BLK && perm[a * OR_BLK + na] >= 0)
+        while (na < C && perm[(size_t)a * C + na] >= 0)
             na++;
         for (int c = 0; c < d; c++) {
             double s = 0.0;
-            float m = bf16f(X[(size_t)perm[a * OR_BLK] * d + c]);
+            float m = bf16f(X[(size_t)perm[(size_t)a * C] * d + c]);
             for (int i = 0; i < na; i++) {
-                float v = bf16f(X[(size_t)perm[a * OR_BLK + i] * d + c]);
+                float v = bf16f(X[(size_t)perm[(size_t)a * C + i] * d + c]);
                 s += (double)v;
                 if (v > m)
                     m = v;
@@ -572,28 +580,30 @@ void or_rank_head(const uint32_t *keys, int R, int scope, int64_t T16, int64_t T
 }
 
 /* ------------------------------------------------------------------ */
-/* Plan for a whole [B,H] problem: pooling, keys, ranking.               */
+/* Plan for a whole [B,H] problem: pooling, keys, ranking, over the R   */
+/* regions of block capacity C.                                         */
 /* q, k: [B,H,N,d] contiguous bf16.  Outputs (each may be NULL except    */
 /* keys and tier): avg [B,H,R,d] fp64 (Q then K arrays), mx f32.         */
+/* Block-mean replacement (skip_means) is defined for C = 64 only.       */
 /* ------------------------------------------------------------------ */
-int or_plan(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+int or_plan(int B, int H, int F, int Hv, int Wv, int C, int d, const uint16_t *q,
             const uint16_t *k, int32_t full_bp, int32_t hi_bp, int32_t lo_bp, double lambda, int scope,
             int skip_means, uint32_t *keys, uint8_t *tier, double *qavg, double *kavg, float *qmx,
             float *kmx)
 {
-    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
-    if (R < 0)
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv, C);
+    if (R < 0 || (skip_means && C != OR_BLK))
         return -1;
-    int32_t *perm = malloc(sizeof(int32_t) * (size_t)R * OR_BLK);
-    or_layout(F, Hv, Wv, perm);
+    int32_t *perm = malloc(sizeof(int32_t) * (size_t)R * C);
+    or_layout(F, Hv, Wv, C, perm);
     int64_t T16, T8c, Tk;
     or_quotas(scope == 0 ? (int64_t)R * R : (int64_t)R, full_bp, hi_bp, lo_bp, &T16, &T8c, &Tk);
     double *qa = malloc(sizeof(double) * (size_t)R * d), *ka = malloc(sizeof(double) * (size_t)R * d);
     float *qm = malloc(sizeof(float) * (size_t)R * d), *km = malloc(sizeof(float) * (size_t)R * d);
     for (int bh = 0; bh < B * H; bh++) {
         const uint16_t *qh = q + (size_t)bh * N * d, *kh = k + (size_t)bh * N * d;
-        or_pool_head(qh, d, perm, R, qa, qm);
-        or_pool_head(kh, d, perm, R, ka, km);
+        or_pool_head(qh, d, perm, R, C, qa, qm);
+        or_pool_head(kh, d, perm, R, C, ka, km);
         if (qavg) memcpy(qavg + (size_t)bh * R * d, qa, sizeof(double) * (size_t)R * d);
         if (kavg) memcpy(kavg + (size_t)bh * R * d, ka, sizeof(double) * (size_t)R * d);
         if (qmx) memcpy(qmx + (size_t)bh * R * d, qm, sizeof(float) * (size_t)R * d);
@@ -865,40 +875,41 @@ void or_quant_v_head(const uint16_t *X, int N, int Np, int d, const int32_t *per
             }
 }
 
-/* Whole-problem quantization into canonical layouts (Np = R 64 positions,
- * region order, padding slots included):
- *   qk8 [B,H,Np,d] codes, qks8 [B,H,R] scales, qk4 [B,H,Np,d], qke4 [B,H,Np,d/32]
- *   v8  [B,H,Np,d],       vs8  [B,H,d],        v4  [B,H,Np,d], ve4  [B,H,R,2,d] */
-int or_quant_qk(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
+/* Whole-problem quantization into canonical layouts (Np = R C positions
+ * of the R regions of capacity C, region order, padding slots included;
+ * T = Np / 64 tiles of 64 positions):
+ *   qk8 [B,H,Np,d] codes, qks8 [B,H,T] scales, qk4 [B,H,Np,d], qke4 [B,H,Np,d/32]
+ *   v8  [B,H,Np,d],       vs8  [B,H,d],        v4  [B,H,Np,d], ve4  [B,H,T,2,d] */
+int or_quant_qk(int B, int H, int F, int Hv, int Wv, int C, int d, const uint16_t *X,
                 uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
 {
-    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
-    if (R < 0) return -1;
-    size_t Np = (size_t)R * OR_BLK;
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv, C);
+    if (R < 0 || C % OR_BLK) return -1;
+    size_t Np = (size_t)R * C;
     int32_t *perm = malloc(sizeof(int32_t) * Np);
-    or_layout(F, Hv, Wv, perm);
+    or_layout(F, Hv, Wv, C, perm);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < B * H; bh++)
         or_quant_qk_head(X + (size_t)bh * N * d, (int)Np, d, perm, c8 + (size_t)bh * Np * d,
-                         s8 + (size_t)bh * R, c4 + (size_t)bh * Np * d,
+                         s8 + (size_t)bh * (Np / OR_BLK), c4 + (size_t)bh * Np * d,
                          e4 + (size_t)bh * Np * (d / 32));
     free(perm);
     return 0;
 }
 
-int or_quant_v(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *X,
+int or_quant_v(int B, int H, int F, int Hv, int Wv, int C, int d, const uint16_t *X,
                uint8_t *c8, float *s8, uint8_t *c4, uint8_t *e4)
 {
-    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
-    if (R < 0) return -1;
-    size_t Np = (size_t)R * OR_BLK;
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv, C);
+    if (R < 0 || C % OR_BLK) return -1;
+    size_t Np = (size_t)R * C;
     int32_t *perm = malloc(sizeof(int32_t) * Np);
-    or_layout(F, Hv, Wv, perm);
+    or_layout(F, Hv, Wv, C, perm);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int bh = 0; bh < B * H; bh++)
         or_quant_v_head(X + (size_t)bh * N * d, N, (int)Np, d, perm, c8 + (size_t)bh * Np * d,
                         s8 + (size_t)bh * d, c4 + (size_t)bh * Np * d,
-                        e4 + (size_t)bh * R * 2 * d);
+                        e4 + (size_t)bh * (Np / OR_BLK) * 2 * d);
     free(perm);
     return 0;
 }
@@ -988,7 +999,7 @@ static void head_ops_build(head_ops *h, const uint16_t *q, const uint16_t *k,
     float *mx = malloc(sizeof(float) * (size_t)R * d);
     for (int t = 0; t < 3; t++) {
         *means[t] = malloc(sizeof(double) * (size_t)R * d);
-        or_pool_head(src[t], d, perm, R, *means[t], mx);
+        or_pool_head(src[t], d, perm, R, OR_BLK, *means[t], mx);
     }
     free(mx);
 }
@@ -1326,25 +1337,57 @@ static void attention_prefix_row(const head_ops *h, const prefix_ops *px, int i,
     free(ac);
 }
 
-/* q,k,v: [B,H,N,d] bf16; tier: [B,H,R,R] in {0,4,8,16}.
- * qblocks: nqb query regions evaluated for every (b,h) (NULL -> all R).
+/* Tiles of a layout of block capacity C (a multiple of 64): region a's C
+ * positions are the C / 64 tiles a C/64 .. a C/64 + C/64 - 1, and a region
+ * pair's tier holds for each of its tile pairs.  The phases visit a row's
+ * kept tiles ascending, i.e. key regions ascending and the tiles of one
+ * region in slot order.  tile_tiers writes one head's [T,T] tile tiers
+ * from its [R,R] region tiers (T = R C/64); for C = 64 they are the same. */
+static const uint8_t *tile_tiers(const uint8_t *tier, int R, int tpr, uint8_t **buf)
+{
+    if (tpr == 1)
+        return tier;
+    int T = R * tpr;
+    if (!*buf)
+        *buf = malloc((size_t)T * T);
+    for (int at = 0; at < T; at++)
+        for (int bt = 0; bt < T; bt++)
+            (*buf)[(size_t)at * T + bt] = tier[(size_t)(at / tpr) * R + bt / tpr];
+    return *buf;
+}
+
+/* Block-mean tiles are defined for C = 64 only. */
+static int tiers_valid(const uint8_t *tier, size_t n, int C)
+{
+    if (C == OR_BLK)
+        return 1;
+    for (size_t i = 0; i < n; i++)
+        if (tier[i] == OR_MEAN)
+            return 0;
+    return 1;
+}
+
+/* q,k,v: [B,H,N,d] bf16; tier: [B,H,R,R] in {0,4,8,16} over the R regions
+ * of block capacity C (a multiple of 64).  qblocks: nqb query tiles (64
+ * positions each) evaluated for every (b,h) (NULL -> all T = R C/64).
  * out: [B,H,nqb,64,d] fp64, row (j,i) belongs to original token
  * perm[qblocks[j]*64 + i] (restore is done by the caller's indexing). */
-int or_attention(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+int or_attention(int B, int H, int F, int Hv, int Wv, int C, int d, const uint16_t *q,
                  const uint16_t *k, const uint16_t *v, const uint8_t *tier, int nqb,
                  const int32_t *qblocks, double *out, double *amb)
 {
-    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
-    if (R < 0) return -1;
-    int Np = R * OR_BLK;
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv, C);
+    if (R < 0 || C % OR_BLK || !tiers_valid(tier, (size_t)B * H * R * R, C)) return -1;
+    int tpr = C / OR_BLK, T = R * tpr, Np = R * C;
     int32_t *perm = malloc(sizeof(int32_t) * Np);
-    or_layout(F, Hv, Wv, perm);
-    if (!qblocks) nqb = R;
+    uint8_t *tbuf = NULL;
+    or_layout(F, Hv, Wv, C, perm);
+    if (!qblocks) nqb = T;
     for (int bh = 0; bh < B * H; bh++) {
         head_ops h;
         size_t off = (size_t)bh * N * d;
         head_ops_build(&h, q + off, k + off, v + off, N, Np, d, perm);
-        const uint8_t *tm = tier + (size_t)bh * R * R;
+        const uint8_t *tm = tile_tiers(tier + (size_t)bh * R * R, R, tpr, &tbuf);
 #pragma omp parallel for schedule(dynamic, 8)
         for (int r = 0; r < nqb * OR_BLK; r++) {
             int j = r / OR_BLK, i = r % OR_BLK;
@@ -1357,33 +1400,37 @@ int or_attention(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
                     memset(amb + ro, 0, sizeof(double) * d);
                 continue;
             }
-            attention_row(&h, NULL, tm + (size_t)a * R, a * OR_BLK + i, o, NULL, amb ? amb + ro : NULL);
+            attention_row(&h, NULL, tm + (size_t)a * T, a * OR_BLK + i, o, NULL, amb ? amb + ro : NULL);
         }
         head_ops_free(&h);
     }
     free(perm);
+    free(tbuf);
     return 0;
 }
 
 /* Trace of one query row (reordered position u) of one head.  Returns the
  * number of processed keys (may exceed cap; only cap entries are written). */
-int64_t or_attention_trace(int F, int Hv, int Wv, int d, const uint16_t *q,
+int64_t or_attention_trace(int F, int Hv, int Wv, int C, int d, const uint16_t *q,
                            const uint16_t *k, const uint16_t *v, const uint8_t *tier,
                            int u, int64_t cap, int32_t *key, int32_t *tr_tier, double *s,
                            double *w, double *wq, double *m, double *Z, double *out)
 {
-    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
-    if (R < 0) return -1;
-    int Np = R * OR_BLK;
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv, C);
+    if (R < 0 || C % OR_BLK || !tiers_valid(tier, (size_t)R * R, C)) return -1;
+    int tpr = C / OR_BLK, T = R * tpr, Np = R * C;
     int32_t *perm = malloc(sizeof(int32_t) * Np);
-    or_layout(F, Hv, Wv, perm);
+    uint8_t *tbuf = NULL;
+    or_layout(F, Hv, Wv, C, perm);
     head_ops h;
     head_ops_build(&h, q, k, v, N, Np, d, perm);
+    const uint8_t *tm = tile_tiers(tier, R, tpr, &tbuf);
     row_trace tr = {cap, 0, key, tr_tier, s, w, wq, m, 0.0};
-    attention_row(&h, NULL, tier + (size_t)(u / OR_BLK) * R, u, out, &tr, NULL);
+    attention_row(&h, NULL, tm + (size_t)(u / OR_BLK) * T, u, out, &tr, NULL);
     *Z = tr.Z;
     head_ops_free(&h);
     free(perm);
+    free(tbuf);
     return tr.n;
 }
 
@@ -1423,26 +1470,27 @@ static void prefix_ops_free(prefix_ops *px)
     free((void *)px->vf);
 }
 
-static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+static int pfx_common(int B, int H, int F, int Hv, int Wv, int C, int d, const uint16_t *q,
                       const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
                       const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
                       const uint8_t *tier, int nqb, const int32_t *qblocks, int nprow,
                       const int32_t *prows, double *out, double *outp, double *amb)
 {
-    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv);
+    int N = F * Hv * Wv, R = or_regions(F, Hv, Wv, C);
     if (pt != 16 && pt != 32) return -1;
-    if (R < 0) return -1;
-    int Np = R * OR_BLK;
+    if (R < 0 || C % OR_BLK || !tiers_valid(tier, (size_t)B * H * R * R, C)) return -1;
+    int tpr = C / OR_BLK, T = R * tpr, Np = R * C;
     int32_t *perm = malloc(sizeof(int32_t) * Np);
-    or_layout(F, Hv, Wv, perm);
-    if (!qblocks) nqb = R;
+    uint8_t *tbuf = NULL;
+    or_layout(F, Hv, Wv, C, perm);
+    if (!qblocks) nqb = T;
     for (int bh = 0; bh < B * H; bh++) {
         head_ops h;
         prefix_ops px;
         size_t off = (size_t)bh * N * d, poff = (size_t)bh * Lp * d;
         head_ops_build(&h, q + off, k + off, v + off, N, Np, d, perm);
         prefix_ops_build(&px, qp + poff, kp + poff, vp + poff, Lp, valid ? valid[bh / H] : Lp, d, pt);
-        const uint8_t *tm = tier + (size_t)bh * R * R;
+        const uint8_t *tm = tile_tiers(tier + (size_t)bh * R * R, R, tpr, &tbuf);
 #pragma omp parallel for schedule(dynamic, 8)
         for (int r = 0; r < nqb * OR_BLK; r++) {
             int j = r / OR_BLK, i = r % OR_BLK;
@@ -1454,7 +1502,7 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
                     memset(amb + o, 0, sizeof(double) * d);
                 continue;
             }
-            attention_row(&h, &px, tm + (size_t)a * R, a * OR_BLK + i, out + o, NULL, amb ? amb + o : NULL);
+            attention_row(&h, &px, tm + (size_t)a * T, a * OR_BLK + i, out + o, NULL, amb ? amb + o : NULL);
         }
         if (outp) {
             int n = prows ? nprow : Lp;
@@ -1469,16 +1517,17 @@ static int pfx_common(int B, int H, int F, int Hv, int Wv, int d, const uint16_t
         head_ops_free(&h);
     }
     free(perm);
+    free(tbuf);
     return 0;
 }
 
-int or_attention_pfx(int B, int H, int F, int Hv, int Wv, int d, const uint16_t *q,
+int or_attention_pfx(int B, int H, int F, int Hv, int Wv, int C, int d, const uint16_t *q,
                      const uint16_t *k, const uint16_t *v, int Lp, const uint16_t *qp,
                      const uint16_t *kp, const uint16_t *vp, const int32_t *valid, int pt,
                      const uint8_t *tier, int nqb, const int32_t *qblocks, int nprow,
                      const int32_t *prows, double *out, double *outp, double *amb)
 {
-    return pfx_common(B, H, F, Hv, Wv, d, q, k, v, Lp, qp, kp, vp, valid, pt, tier, nqb, qblocks,
+    return pfx_common(B, H, F, Hv, Wv, C, d, q, k, v, Lp, qp, kp, vp, valid, pt, tier, nqb, qblocks,
                       nprow, prows, out, outp, amb);
 }
 

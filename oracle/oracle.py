@@ -46,9 +46,9 @@ def lib():
         L = C.CDLL(_LIB)
         P = C.c_void_p
         i32, i64, f64 = C.c_int32, C.c_int64, C.c_double
-        L.or_layout.argtypes = [C.c_int, C.c_int, C.c_int, P]
+        L.or_layout.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P]
         L.or_layout.restype = C.c_int
-        L.or_regions.argtypes = [C.c_int, C.c_int, C.c_int]
+        L.or_regions.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int]
         L.or_regions.restype = C.c_int
         L.or_partition.argtypes = [C.c_int, C.c_int, P, P]
         L.or_partition.restype = C.c_int
@@ -60,7 +60,7 @@ def lib():
         L.or_partition_bands_c.argtypes = [C.c_int, C.c_int, C.c_int, C.POINTER(C.c_int), P, P,
                                            C.POINTER(C.c_int64)]
         L.or_partition_bands_c.restype = C.c_int
-        L.or_pool_head.argtypes = [P, C.c_int, P, C.c_int, P, P]
+        L.or_pool_head.argtypes = [P, C.c_int, P, C.c_int, C.c_int, P, P]
         L.or_exp_constants.argtypes = [P]
         L.or_exp.argtypes = [f64]
         L.or_exp.restype = f64
@@ -70,7 +70,7 @@ def lib():
         L.or_bf16_round.argtypes = [f64]
         L.or_bf16_round.restype = f64
         L.or_rank_head.argtypes = [P, C.c_int, C.c_int, i64, i64, i64, P]
-        L.or_plan.argtypes = [C.c_int] * 6 + [P, P, i32, i32, i32, f64, C.c_int, C.c_int, P, P, P, P, P, P]
+        L.or_plan.argtypes = [C.c_int] * 7 + [P, P, i32, i32, i32, f64, C.c_int, C.c_int, P, P, P, P, P, P]
         L.or_plan.restype = C.c_int
         L.or_e4m3_value.argtypes = [C.c_int]
         L.or_e4m3_value.restype = f64
@@ -84,16 +84,16 @@ def lib():
         L.or_mx_exponent.restype = C.c_int
         L.or_mx_exponent_w.argtypes = [f64]
         L.or_mx_exponent_w.restype = C.c_int
-        L.or_quant_qk.argtypes = [C.c_int] * 6 + [P, P, P, P, P]
+        L.or_quant_qk.argtypes = [C.c_int] * 7 + [P, P, P, P, P]
         L.or_quant_qk.restype = C.c_int
-        L.or_quant_v.argtypes = [C.c_int] * 6 + [P, P, P, P, P]
+        L.or_quant_v.argtypes = [C.c_int] * 7 + [P, P, P, P, P]
         L.or_quant_v.restype = C.c_int
-        L.or_attention.argtypes = [C.c_int] * 6 + [P, P, P, P, C.c_int, P, P, P]
+        L.or_attention.argtypes = [C.c_int] * 7 + [P, P, P, P, C.c_int, P, P, P]
         L.or_attention.restype = C.c_int
-        L.or_attention_trace.argtypes = [C.c_int] * 4 + [P, P, P, P, C.c_int, i64,
+        L.or_attention_trace.argtypes = [C.c_int] * 5 + [P, P, P, P, C.c_int, i64,
                                                          P, P, P, P, P, P, P, P]
         L.or_attention_trace.restype = i64
-        L.or_attention_pfx.argtypes = [C.c_int] * 6 + [P, P, P, C.c_int, P, P, P, P, C.c_int,
+        L.or_attention_pfx.argtypes = [C.c_int] * 7 + [P, P, P, C.c_int, P, P, P, P, C.c_int,
                                                        P, C.c_int, P, C.c_int, P, P, P, P]
         L.or_attention_pfx.restype = C.c_int
         L.or_dense.argtypes = [C.c_int] * 4 + [P, P, P, C.c_int, P, P]
@@ -114,18 +114,19 @@ def _u16(x):
 
 
 # ---------------------------------------------------------------- layout
-def regions(F, Hv, Wv) -> int:
-    """R = F R_f regions of the partition; raises when the frame has none."""
-    R = lib().or_regions(F, Hv, Wv)
+def regions(F, Hv, Wv, cap=BLK) -> int:
+    """R = F R_f regions of the partition at block capacity cap; raises when
+    the frame has none."""
+    R = lib().or_regions(F, Hv, Wv, cap)
     if R < 0:
         raise ValueError("no partition of a %d x %d frame" % (Hv, Wv))
     return R
 
 
-def layout(F, Hv, Wv) -> np.ndarray:
-    """perm [R 64]: original token of each reordered position, -1 for padding."""
-    perm = np.empty(regions(F, Hv, Wv) * BLK, dtype=np.int32)
-    lib().or_layout(F, Hv, Wv, _p(perm))
+def layout(F, Hv, Wv, cap=BLK) -> np.ndarray:
+    """perm [R cap]: original token of each reordered position, -1 for padding."""
+    perm = np.empty(regions(F, Hv, Wv, cap) * cap, dtype=np.int32)
+    lib().or_layout(F, Hv, Wv, cap, _p(perm))
     return perm
 
 
@@ -175,15 +176,16 @@ def partition_bands_c(Hv, Wv, cap):
 
 
 # ---------------------------------------------------------------- draft
-def pool_head(X: np.ndarray, F, Hv, Wv):
-    """X: [N, d] uint16 -> (avg [R, d] f64, max [R, d] f32)."""
+def pool_head(X: np.ndarray, F, Hv, Wv, cap=BLK):
+    """X: [N, d] uint16 -> (avg [R, d] f64, max [R, d] f32) over the R
+    regions of capacity cap."""
     X = _u16(X)
     N, d = X.shape
-    R = regions(F, Hv, Wv)
-    perm = layout(F, Hv, Wv)
+    R = regions(F, Hv, Wv, cap)
+    perm = layout(F, Hv, Wv, cap)
     avg = np.empty((R, d), np.float64)
     mx = np.empty((R, d), np.float32)
-    lib().or_pool_head(_p(X), d, _p(perm), R, _p(avg), _p(mx))
+    lib().or_pool_head(_p(X), d, _p(perm), R, cap, _p(avg), _p(mx))
     return avg, mx
 
 
@@ -249,14 +251,15 @@ def rank_head(keys: np.ndarray, T8, Tk, scope=0, T16=0) -> np.ndarray:
 
 
 def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False, full_bp=0,
-         skip_means=False):
-    """Full plan for [B,H,N,d] inputs -> dict(keys [B,H,R,R] u32, tier u8, ...).
-    full_bp: share of the 16-bit tier (basis points); skip_means: pairs
-    outside the quotas become block-mean tiles (tier 1) instead of skipped."""
+         skip_means=False, cap=BLK):
+    """Full plan for [B,H,N,d] inputs -> dict(keys [B,H,R,R] u32, tier u8, ...)
+    over the R regions of block capacity cap.  full_bp: share of the 16-bit
+    tier (basis points); skip_means: pairs outside the quotas become
+    block-mean tiles (tier 1) instead of skipped (cap = 64 only)."""
     q = _u16(q)
     k = _u16(k)
     B, H, N, d = q.shape
-    R = regions(F, Hv, Wv)
+    R = regions(F, Hv, Wv, cap)
     keys = np.empty((B, H, R, R), np.uint32)
     tier = np.empty((B, H, R, R), np.uint8)
     out = {"keys": keys, "tier": tier}
@@ -267,7 +270,7 @@ def plan(q, k, F, Hv, Wv, hi_bp, lo_bp, lam=0.2, scope=0, descriptors=False, ful
         out["qmax"] = np.empty((B, H, R, d), np.float32)
         out["kmax"] = np.empty((B, H, R, d), np.float32)
         ptrs = [_p(out[n]) for n in ("qavg", "kavg", "qmax", "kmax")]
-    rc = lib().or_plan(B, H, F, Hv, Wv, d, _p(q), _p(k), int(full_bp), int(hi_bp), int(lo_bp), float(lam),
+    rc = lib().or_plan(B, H, F, Hv, Wv, cap, d, _p(q), _p(k), int(full_bp), int(hi_bp), int(lo_bp), float(lam),
                        int(scope), int(bool(skip_means)), _p(keys), _p(tier), *ptrs)
     if rc:
         raise ValueError("bad shape")
@@ -308,71 +311,76 @@ def mx_exponent_w(amax: float) -> int:
     return lib().or_mx_exponent_w(float(amax))
 
 
-def quant_qk(X, F, Hv, Wv):
-    """-> dict(c8 [B,H,Np,d] u8, s8 [B,H,R] f32, c4 [B,H,Np,d] u8, e4 [B,H,Np,d/32] u8),
-    position axis in reordered order (Np = 64 R, padding slots included)."""
+def quant_qk(X, F, Hv, Wv, cap=BLK):
+    """-> dict(c8 [B,H,Np,d] u8, s8 [B,H,T] f32, c4 [B,H,Np,d] u8, e4 [B,H,Np,d/32] u8),
+    position axis in reordered order (Np = cap R, padding slots included; T =
+    Np / 64 tiles)."""
     X = _u16(X)
     B, H, N, d = X.shape
-    R = regions(F, Hv, Wv)
-    Np = R * BLK
-    o = {"c8": np.empty((B, H, Np, d), np.uint8), "s8": np.empty((B, H, R), np.float32),
+    Np = regions(F, Hv, Wv, cap) * cap
+    T = Np // BLK
+    o = {"c8": np.empty((B, H, Np, d), np.uint8), "s8": np.empty((B, H, T), np.float32),
          "c4": np.empty((B, H, Np, d), np.uint8), "e4": np.empty((B, H, Np, d // 32), np.uint8)}
-    lib().or_quant_qk(B, H, F, Hv, Wv, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
-                      _p(o["e4"]))
+    assert lib().or_quant_qk(B, H, F, Hv, Wv, cap, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
+                             _p(o["e4"])) == 0
     return o
 
 
-def quant_v(X, F, Hv, Wv):
-    """-> dict(c8 [B,H,Np,d], s8 [B,H,d], c4 [B,H,Np,d], e4 [B,H,R,2,d])."""
+def quant_v(X, F, Hv, Wv, cap=BLK):
+    """-> dict(c8 [B,H,Np,d], s8 [B,H,d], c4 [B,H,Np,d], e4 [B,H,T,2,d])."""
     X = _u16(X)
     B, H, N, d = X.shape
-    R = regions(F, Hv, Wv)
-    Np = R * BLK
+    Np = regions(F, Hv, Wv, cap) * cap
+    T = Np // BLK
     o = {"c8": np.empty((B, H, Np, d), np.uint8), "s8": np.empty((B, H, d), np.float32),
-         "c4": np.empty((B, H, Np, d), np.uint8), "e4": np.empty((B, H, R, 2, d), np.uint8)}
-    lib().or_quant_v(B, H, F, Hv, Wv, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
-                     _p(o["e4"]))
+         "c4": np.empty((B, H, Np, d), np.uint8), "e4": np.empty((B, H, T, 2, d), np.uint8)}
+    assert lib().or_quant_v(B, H, F, Hv, Wv, cap, d, _p(X), _p(o["c8"]), _p(o["s8"]), _p(o["c4"]),
+                            _p(o["e4"])) == 0
     return o
 
 
 # ---------------------------------------------------------------- attention
-def _restore(x, F, Hv, Wv):
-    """[B,H,R,64,d] rows in reordered position order -> [B,H,N,d] in original
+def _restore(x, F, Hv, Wv, cap=BLK):
+    """[B,H,T,64,d] rows in reordered position order -> [B,H,N,d] in original
     token order (padding slots dropped)."""
     B, H = x.shape[:2]
     d = x.shape[-1]
-    perm = layout(F, Hv, Wv)
+    perm = layout(F, Hv, Wv, cap)
     keep = perm >= 0
     full = np.empty((B, H, F * Hv * Wv, d), np.float64)
     full[:, :, perm[keep], :] = x.reshape(B, H, -1, d)[:, :, keep]
     return full
 
 
-def attention(q, k, v, tier, F, Hv, Wv, qblocks=None, amb=False):
-    """Tiered attention.  qblocks=None: all rows, returned [B,H,N,d] in original
-    token order.  Otherwise [B,H,len(qblocks),64,d]; row (j,i) is original
-    token perm[qblocks[j]*64+i] (zero for a padding slot).  amb=True also
+def attention(q, k, v, tier, F, Hv, Wv, qblocks=None, amb=False, cap=BLK):
+    """Tiered attention with a [B,H,R,R] tier map over the regions of block
+    capacity cap.  qblocks=None: all rows, returned [B,H,N,d] in original
+    token order.  Otherwise qblocks are query tiles (64 positions each) and
+    the result is [B,H,len(qblocks),64,d]; row (j,i) is original token
+    perm[qblocks[j]*64+i] (zero for a padding slot).  amb=True also
     returns, laid out alike, the bound on how far each output can move when
     every weight-code decision inside the precision band (OR_AMB_REL) is
     taken either way: (out, amb)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     tier = np.ascontiguousarray(tier, np.uint8)
     B, H, N, d = q.shape
-    R = regions(F, Hv, Wv)
+    R = regions(F, Hv, Wv, cap)
     assert tier.shape == (B, H, R, R)
     qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
-    nq = R if qb is None else len(qb)
+    nq = R * cap // BLK if qb is None else len(qb)
     out = np.empty((B, H, nq, BLK, d), np.float64)
     ab = np.empty((B, H, nq, BLK, d), np.float64) if amb else None
-    lib().or_attention(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), nq,
-                       None if qb is None else _p(qb), _p(out), None if ab is None else _p(ab))
+    rc = lib().or_attention(B, H, F, Hv, Wv, cap, d, _p(q), _p(k), _p(v), _p(tier), nq,
+                            None if qb is None else _p(qb), _p(out), None if ab is None else _p(ab))
+    if rc:
+        raise ValueError("attention: bad shape or tier map")
     if qb is None:
-        out = _restore(out, F, Hv, Wv)
-        ab = None if ab is None else _restore(ab, F, Hv, Wv)
+        out = _restore(out, F, Hv, Wv, cap)
+        ab = None if ab is None else _restore(ab, F, Hv, Wv, cap)
     return (out, ab) if amb else out
 
 
-def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks):
+def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks, cap):
     q, k, v, qp, kp, vp = (_u16(x) for x in (q, k, v, qp, kp, vp))
     tier = np.ascontiguousarray(tier, np.uint8)
     B, H, N, d = q.shape
@@ -383,7 +391,7 @@ def _pfx_args(q, k, v, tier, qp, kp, vp, valid, qblocks):
     va = None if valid is None else np.ascontiguousarray(valid, np.int32)
     assert va is None or va.shape == (B,)
     qb = None if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
-    nq = R if qb is None else len(qb)
+    nq = R * cap // BLK if qb is None else len(qb)
     return q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R)
 
 
@@ -399,7 +407,7 @@ def _prows(prefix_rows, Lp):
 
 
 def attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, pt=16, qblocks=None,
-                  prefix_rows=True, amb=False):
+                  prefix_rows=True, amb=False, cap=BLK):
     """Tiered attention with a text prefix (App. C.1).  q, k, v: video
     [B,H,N,d]; qp, kp, vp: prefix [B,H,Lp,d]; valid: [B] valid prefix keys
     (None: all).  pt: precision of the prefix interactions (16 or 32).
@@ -408,12 +416,12 @@ def attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, pt=16, qbloc
     None), and with amb=True also the video rows' band bound (prefix rows
     take only unquantized weights)."""
     q, k, v, tier, qp, kp, vp, va, qb, nq, (B, H, N, d, Lp, R) = _pfx_args(
-        q, k, v, tier, qp, kp, vp, valid, qblocks)
+        q, k, v, tier, qp, kp, vp, valid, qblocks, cap)
     npr, pr = _prows(prefix_rows, Lp)
     out = np.empty((B, H, nq, BLK, d), np.float64)
     outp = np.empty((B, H, npr, d), np.float64) if prefix_rows is not False else None
     ab = np.empty((B, H, nq, BLK, d), np.float64) if amb else None
-    rc = lib().or_attention_pfx(B, H, F, Hv, Wv, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
+    rc = lib().or_attention_pfx(B, H, F, Hv, Wv, cap, d, _p(q), _p(k), _p(v), Lp, _p(qp), _p(kp),
                                 _p(vp), None if va is None else _p(va), pt, _p(tier), nq,
                                 None if qb is None else _p(qb), npr,
                                 None if pr is None else _p(pr), _p(out),
@@ -421,27 +429,28 @@ def attention_pfx(q, k, v, tier, F, Hv, Wv, qp, kp, vp, valid=None, pt=16, qbloc
                                 None if ab is None else _p(ab))
     assert rc == 0
     if qblocks is None:
-        out = _restore(out, F, Hv, Wv)
-        ab = None if ab is None else _restore(ab, F, Hv, Wv)
+        out = _restore(out, F, Hv, Wv, cap)
+        ab = None if ab is None else _restore(ab, F, Hv, Wv, cap)
     return (out, outp, ab) if amb else (out, outp)
 
 
-def attention_trace(q, k, v, tier, F, Hv, Wv, u, cap=None):
-    """One head ([N,d] inputs, [R,R] tier), one reordered query position u."""
+def attention_trace(q, k, v, tier, F, Hv, Wv, u, maxn=None, cap=BLK):
+    """One head ([N,d] inputs, [R,R] tier over the regions of capacity cap),
+    one reordered query position u."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     tier = np.ascontiguousarray(tier, np.uint8)
     N, d = q.shape
-    if cap is None:
-        cap = N + 64
-    key = np.empty(cap, np.int32)
-    tt = np.empty(cap, np.int32)
-    s, w, wq, m = (np.empty(cap, np.float64) for _ in range(4))
+    if maxn is None:
+        maxn = N + 64
+    key = np.empty(maxn, np.int32)
+    tt = np.empty(maxn, np.int32)
+    s, w, wq, m = (np.empty(maxn, np.float64) for _ in range(4))
     Z = C.c_double()
     out = np.empty(d, np.float64)
-    n = lib().or_attention_trace(F, Hv, Wv, d, _p(q), _p(k), _p(v), _p(tier), int(u), cap,
+    n = lib().or_attention_trace(F, Hv, Wv, cap, d, _p(q), _p(k), _p(v), _p(tier), int(u), maxn,
                                  _p(key), _p(tt), _p(s), _p(w), _p(wq), _p(m), C.byref(Z),
                                  _p(out))
-    n = min(n, cap)
+    n = min(n, maxn)
     return {"key": key[:n], "tier": tt[:n], "s": s[:n], "w": w[:n], "wq": wq[:n], "m": m[:n],
             "Z": Z.value, "out": out}
 
