@@ -115,17 +115,17 @@ def cpu_baseline(w, q, k, v, hi, lo, full, sm, gpu_head0, tier_head0):
 
     qs, ks, vs = q[:1, :1].copy(), k[:1, :1].copy(), v[:1, :1].copy()
     t0 = time.perf_counter()
-    pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam, full_bp=full, skip_means=sm)
+    pl = O.plan(qs, ks, w.F, w.Hv, w.Wv, hi, lo, w.lam, full_bp=full, skip_means=sm, cap=w.cap)
     t_plan = time.perf_counter() - t0
-    R = w.R
+    R = w.T   # query tiles of 64 rows (the regions at capacity 64)
     n_many = 401
     sel1 = np.array([R // 2], np.int32)
     selm = np.array([(j * R) // n_many for j in range(n_many)], np.int32)
     t0 = time.perf_counter()
-    O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=sel1)
+    O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=sel1, cap=w.cap)
     t1 = time.perf_counter() - t0
     t0 = time.perf_counter()
-    ref_m = O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=selm)
+    ref_m = O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=selm, cap=w.cap)
     tm = time.perf_counter() - t0
     per_region = max((tm - t1) / (n_many - 1), 1e-9)
     per_head_fixed = max(t1 - per_region, 0.0)
@@ -139,15 +139,15 @@ def cpu_baseline(w, q, k, v, hi, lo, full, sm, gpu_head0, tier_head0):
         "cores": threads,
         "kind": "oracle",
         "sample": ("1 of %d heads: full plan (%.2f s), tiered attention on 1 and on %d query "
-                   "regions (%.2f s, %.2f s); per-head fixed %.2f s + %.4f s per region, "
-                   "extrapolated to %d regions x %d heads = %.0f s"
+                   "tiles of 64 rows (%.2f s, %.2f s); per-head fixed %.2f s + %.4f s per tile, "
+                   "extrapolated to %d tiles x %d heads = %.0f s"
                    % (w.B * w.H, t_plan, n_many, t1, tm, per_head_fixed, per_region, R,
                       w.B * w.H, total)),
     }
     # accuracy of the GPU result on sampled query regions of head 0
     acc_regions = np.array([(j * R) // N_ACC_REGIONS for j in range(N_ACC_REGIONS)], np.int32)
-    ref, amb = O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=acc_regions, amb=True)
-    perm = O.layout(w.F, w.Hv, w.Wv)
+    ref, amb = O.attention(qs, ks, vs, pl["tier"], w.F, w.Hv, w.Wv, qblocks=acc_regions, amb=True, cap=w.cap)
+    perm = O.layout(w.F, w.Hv, w.Wv, cap=w.cap)
     tok = perm[(acc_regions[:, None] * 64 + np.arange(64)).ravel()]
     keep = tok >= 0
     ref = ref.reshape(-1, w.d)[keep]
@@ -199,7 +199,7 @@ def measure(args, w, hi, lo, full, q, k, v, torch, da2, synth):
         del src, dst
     oj = torch.empty((w.B, Lp + w.N, w.H, w.d), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
     o = oj[:, :, Lp:]
-    L = da2.Layout.for_tensor(qd, w.F, w.Hv, w.Wv, prefix=Lp)
+    L = da2.Layout.for_tensor(qd, w.F, w.Hv, w.Wv, prefix=Lp, cap=w.cap)
     P = da2.Plan(L)
     stream = torch.cuda.current_stream()
     valid = torch.full((w.B,), nv, dtype=torch.int32, device=dev) if Lp else None
@@ -249,10 +249,11 @@ def measure(args, w, hi, lo, full, q, k, v, torch, da2, synth):
     print("[bench] timed %d steps: %.3f ms/step (plan %.3f, attention call %.3f, kernel %.3f)"
           % (args.steps, ms_step, plan_ms, attn_call_ms, attn_kernel_ms), file=sys.stderr, flush=True)
 
-    # work accounting (head-scope quotas, identical for every (b, h))
+    # work accounting (head-scope quotas, identical for every (b, h)); a
+    # region pair of capacity cap is (cap / 64)^2 tiles of 64 x 64
     R = w.R
     t16, t8c, tk = da2.quotas3(R * R, full, hi, lo)
-    tile_flop = 4.0 * 64 * 64 * w.d
+    tile_flop = 4.0 * 64 * 64 * w.d * (w.cap // 64) ** 2
     f16 = w.B * w.H * t16 * tile_flop
     f8 = w.B * w.H * (t8c - t16) * tile_flop
     f4 = w.B * w.H * (tk - t8c) * tile_flop
@@ -285,6 +286,7 @@ def measure(args, w, hi, lo, full, q, k, v, torch, da2, synth):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.d,
                    "frames": w.F, "height": w.Hv, "width": w.Wv, "tokens": w.N, "regions": R,
+                   "capacity": w.cap,
                    "budget_bp": ({"bf16": full} if full else {}) | {"8bit": hi, "mxfp4": lo},
                    "lambda": w.lam, "ranking": "head",
                    "storage": "[B,N,H,d] bf16", "output": "bf16",

@@ -21,13 +21,19 @@
  * Conventions
  *   - Tokens of one (batch, head) are N = frames*height*width latent
  *     positions in (frame, y, x) raster order.  Each frame is partitioned
- *     into R_f = ceil(height*width/64) connected regions of 48..64 tokens
- *     (Sec. 3.3 ragged 2D partition, App. C.2), the same for every frame;
- *     R = frames*R_f regions, numbered frame-major.  When height and width
- *     are multiples of 8 the regions are the 8x8 cells in raster order.
- *     Inside a region its tokens take slots 0..n_a-1 in raster order, and
- *     slots n_a..63 are padding (App. C.1: n_a excludes padding).
- *     da2_layout_regions and da2_layout_slots describe the partition.
+ *     into R_f = ceil(height*width/C) connected regions of balanced token
+ *     counts (Sec. 3.3 ragged 2D partition, App. C.2), C the block
+ *     capacity (64, or 128 as in the paper's operator study), the same for
+ *     every frame; R = frames*R_f regions, numbered frame-major.  When C is
+ *     64 and height and width are multiples of 8 the regions are the 8x8
+ *     cells in raster order.  Inside a region its tokens take slots
+ *     0..n_a-1 in raster order, and slots n_a..C-1 are padding (App. C.1:
+ *     n_a excludes padding); every 64 slots of a region must hold at least
+ *     48 tokens.  da2_layout_regions and da2_layout_slots describe the
+ *     partition.  Pooling, the draft map and the ranking work on regions;
+ *     attention works on tiles of 64 slots (a region of capacity 128 is two
+ *     tiles), every tile of a region pair taking the pair's tier, and the
+ *     INT8 steps of Q and K are per 64-slot tile.
  *   - Q, K, V are bfloat16 device arrays addressed as
  *     base + b*stride_b + h*stride_h + n*stride_n + c (element units, the
  *     channel index c is contiguous).  head_dim is 64 or 128.  Base pointers
@@ -36,7 +42,8 @@
  *     (fp32 or bf16).
  *   - Tier maps are uint8 [B, H, R, R] (query region a, key region b) with
  *     values 16 (16-bit: bf16 operands), 8 (8-bit), 4 (MXFP4), 1 (block mean)
- *     or 0 (skip).  A block-mean tile ("Triage: Skip, Skim, or Refine
+ *     or 0 (skip); block-mean tiles need C = 64 (at C = 128 a 1 counts as
+ *     an unknown value, which is a skip).  A block-mean tile ("Triage: Skip, Skim, or Refine
  *     Attention Tiles in Video Diffusion Transformers", abstract: a skipped
  *     tile replaced by its block means) scores all its query-key pairs with
  *     the mean of its scores, q_a . k_b / sqrt(d) over the valid-token means
@@ -76,6 +83,7 @@ typedef struct {
     int64_t stride_b, stride_h, stride_n; /* element strides of Q/K/V/O */
     int32_t prefix;                  /* Lp: text-prefix tokens per sequence (0: none;
                                         at most 4096), see da2_attention_prefixed */
+    int32_t capacity;                /* C: tokens per region, 64 or 128 (0 means 64) */
 } da2_shape;
 
 typedef struct {
@@ -87,7 +95,8 @@ typedef struct {
     int32_t full_bp; /* share in the 16-bit tier (bf16 operands, the paper's 16-bit
                         path); full_bp + hi_bp + lo_bp <= 10000 */
     int32_t skip_means; /* 0: pairs outside the quotas are skipped; 1: they become
-                           block-mean tiles (tier 1, see below) */
+                           block-mean tiles (tier 1, see below; C = 64 only,
+                           DA2_ERR_INVALID_ARG otherwise) */
 } da2_budget;
 
 typedef struct da2_layout_s da2_layout_t;
@@ -102,7 +111,7 @@ void da2_layout_destroy(da2_layout_t *layout);
  * to *regions_per_frame when it is not NULL.  Host only. */
 int32_t da2_layout_regions(const da2_layout_t *layout, int32_t *regions_per_frame);
 
-/* The partition of one frame (host destination, int32 [R_f*64]): for slot i
+/* The partition of one frame (host destination, int32 [R_f*C]): for slot i
  * of region r, the token y*width + x it holds, or -1 for a padding slot.
  * Region r of frame f is region f*R_f + r of the tier map.  Host only. */
 da2_status da2_layout_slots(const da2_layout_t *layout, int32_t *dst);
@@ -179,17 +188,19 @@ da2_status da2_attention_prefixed(da2_plan_t *plan, const void *q, const void *k
                                   hipStream_t stream);
 
 /* Debug exports in canonical layouts, for tests (device destination):
- *   (Np = 64 R reordered positions, region by region, padding slots included)
+ *   (Np = C R reordered positions, region by region, padding slots included;
+ *   T = Np / 64 tiles of 64 positions; T = R at C = 64)
  *   DA2_DBG_Q_I8 / K_I8             : INT8 codes (two's complement bytes) [B,H,Np,d]
- *   DA2_DBG_Q_I8_SCALE / K_...      : fp32 steps [B,H,R]
+ *   DA2_DBG_Q_I8_SCALE / K_...      : fp32 steps [B,H,T]
  *   DA2_DBG_V_FP8 / V_FP8_SCALE     : E4M3 codes [B,H,Np,d];  fp32 [B,H,d]
  *   DA2_DBG_Q_MX / K_MX / V_MX      : uint8 E2M1 codes [B,H,Np,d] (one per byte)
- *   DA2_DBG_Q_MX_SCALE / K_...      : uint8 E8M0 [B,H,Np,d/32];  V: [B,H,R,2,d]
+ *   DA2_DBG_Q_MX_SCALE / K_...      : uint8 E8M0 [B,H,Np,d/32];  V: [B,H,T,2,d]
  *   DA2_DBG_Q_AVG / K_AVG           : fp64 [B,H,R,d];  Q_MAX / K_MAX: fp32 [B,H,R,d]
  *   DA2_DBG_KEYS                    : uint32 [B,H,R,R] (bits of fp32 draft score)
- *   DA2_DBG_SCHEDULE                : int32 [B,H,R,3+R]: n16, n8, n4, then the
- *                                     16-bit key regions ascending, then 8-bit
- *                                     ascending, then MXFP4 ascending, then -1
+ *   DA2_DBG_SCHEDULE                : int32 [B,H,T,3+T]: per query tile the tile
+ *                                     counts n16, n8, n4, then the 16-bit key
+ *                                     tiles ascending, then 8-bit ascending,
+ *                                     then MXFP4 ascending, then -1
  * V entries are valid after da2_attention. */
 enum {
     DA2_DBG_Q_I8 = 0, DA2_DBG_Q_I8_SCALE, DA2_DBG_Q_MX, DA2_DBG_Q_MX_SCALE,

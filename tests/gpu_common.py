@@ -24,15 +24,16 @@ def host(t, dtype):
     return t.cpu().numpy().view(dtype)
 
 
-def run_plan(q, k, F, Hv, Wv, hi, lo, lam=0.2, scope=0, layout_bnhd=False, full=0):
-    """Plan on the GPU.  Returns (plan, qd, kd) keeping the tensors alive."""
+def run_plan(q, k, F, Hv, Wv, hi, lo, lam=0.2, scope=0, layout_bnhd=False, full=0, cap=64):
+    """Plan on the GPU (block capacity cap).  Returns (plan, qd, kd) keeping
+    the tensors alive."""
     from video_diffusion_dit_frame_amd import da2
 
     qd, kd = dev(q), dev(k)
     if layout_bnhd:
         qd = qd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
         kd = kd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
-    L = da2.Layout.for_tensor(qd, F, Hv, Wv)
+    L = da2.Layout.for_tensor(qd, F, Hv, Wv, cap=cap)
     P = da2.Plan(L)
     P.plan(qd, kd, hi, lo, lam, scope, full_bp=full)
     return P, qd, kd
@@ -51,18 +52,23 @@ def run_attention(P, qd, kd, v, out_dtype=torch.float32, layout_bnhd=False):
     return o
 
 
-def schedule_from_tier(tier):
-    """Expected schedule rows from a tier map: n16, n8, n4, the 16-bit key
-    regions ascending, FP8 ascending, MXFP4 ascending, -1 padding."""
+def schedule_from_tier(tier, tpr=1):
+    """Expected schedule rows from a region tier map, one per query tile
+    (tpr tiles per region): tile counts n16, n8, n4, then the key tiles of
+    the 16-bit key regions ascending, 8-bit ascending, MXFP4 ascending, -1
+    padding."""
     B, H, R, _ = tier.shape
-    out = np.full((B, H, R, R + 3), -1, np.int32)
+    T = R * tpr
+    out = np.full((B, H, T, T + 3), -1, np.int32)
     for b in range(B):
         for h in range(H):
             for a in range(R):
                 lists = [np.nonzero(tier[b, h, a] == p)[0] for p in (16, 8, 4)]
-                out[b, h, a, :3] = [len(x) for x in lists]
                 cat = np.concatenate(lists)
-                out[b, h, a, 3:3 + len(cat)] = cat
+                tiles = (cat[:, None] * tpr + np.arange(tpr)).ravel()
+                for i in range(tpr):
+                    out[b, h, a * tpr + i, :3] = [len(x) * tpr for x in lists]
+                    out[b, h, a * tpr + i, 3:3 + len(tiles)] = tiles
     return out
 
 

@@ -41,10 +41,11 @@ void launch_import_tier(const da2_layout_s &, const uint8_t *, char *, hipStream
         }                                                                   \
     } while (0)
 
-static void one_layout(int B, int H, int d, int F, int Hv, int Wv, int prefix)
+static void one_layout(int B, int H, int d, int F, int Hv, int Wv, int prefix, int cap = 0)
 {
     const int64_t N = (int64_t)F * Hv * Wv;
-    da2_shape s = {B, H, d, F, Hv, Wv, H * N * d, N * d, d, prefix};
+    const int C = cap ? cap : 64;
+    da2_shape s = {B, H, d, F, Hv, Wv, H * N * d, N * d, d, prefix, cap};
     da2_layout_t *L = nullptr;
     const da2_status st = da2_layout_create(&s, &L);
     if (st != DA2_OK) {
@@ -53,12 +54,12 @@ static void one_layout(int B, int H, int d, int F, int Hv, int Wv, int prefix)
     }
     int32_t rf = 0;
     const int32_t R = da2_layout_regions(L, &rf);
-    CHECK(R == F * rf && rf == (Hv * Wv + 63) / 64);
-    int32_t *slots = (int32_t *)malloc(sizeof(int32_t) * rf * 64);
+    CHECK(R == F * rf && rf == (Hv * Wv + C - 1) / C);
+    int32_t *slots = (int32_t *)malloc(sizeof(int32_t) * rf * C);
     CHECK(da2_layout_slots(L, slots) == DA2_OK);
     // every token of the frame exactly once
     int32_t *seen = (int32_t *)calloc((size_t)Hv * Wv, sizeof(int32_t));
-    for (int i = 0; i < rf * 64; i++)
+    for (int i = 0; i < rf * C; i++)
         if (slots[i] >= 0) {
             CHECK(slots[i] < Hv * Wv);
             seen[slots[i]]++;
@@ -82,6 +83,10 @@ static void one_layout(int B, int H, int d, int F, int Hv, int Wv, int prefix)
     for (auto &b : bad)
         CHECK(da2_plan(P, q, k, &b, nullptr) == DA2_ERR_INVALID_ARG);
     da2_budget good = {1000, 3000, 0.2, 0, 0, 0};
+    if (C > 64) {   // block-mean tiles need capacity 64
+        da2_budget means = {1000, 3000, 0.2, 0, 0, 1};
+        CHECK(da2_plan(P, q, k, &means, nullptr) == DA2_ERR_INVALID_ARG);
+    }
     CHECK(da2_plan(P, (const char *)q + 2, k, &good, nullptr) == DA2_ERR_INVALID_ARG);   // misaligned
     CHECK(da2_plan(P, nullptr, k, &good, nullptr) == DA2_ERR_INVALID_ARG);
     // no plan yet: attention refuses before any launch
@@ -105,7 +110,11 @@ int main()
     for (int Hv = 1; Hv <= 48; Hv++)
         for (int Wv = 1; Wv <= 48; Wv++)
             one_layout(1, 2, (Hv + Wv) % 2 ? 64 : 128, 2, Hv, Wv, (Hv * Wv) % 3 ? 0 : 90);
+    for (int Hv = 8; Hv <= 40; Hv += 3)
+        for (int Wv = 8; Wv <= 40; Wv += 5)
+            one_layout(1, 2, 64, 2, Hv, Wv, (Hv * Wv) % 2 ? 0 : 70, 128);
     one_layout(1, 40, 128, 21, 48, 80, 0);     // a Wan-14B 720p layer
+    one_layout(1, 40, 128, 21, 48, 80, 0, 128);   // the same at capacity 128
     one_layout(1, 24, 128, 33, 34, 60, 256);   // HunyuanVideo 544p with a prefix
     int64_t t16, t8, tk;
     da2_quotas(1260 * 1260, 500, 1000, 3000, &t16, &t8, &tk);

@@ -22,12 +22,12 @@ def test_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
-def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None, prefix=0):
+def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None, prefix=0, cap=0):
     N = F * Hv * Wv
     sn = d if sn is None else sn
     sh = N * d if sh is None else sh
     sb = H * N * d if sb is None else sb
-    s = da2.Shape(B, H, d, F, Hv, Wv, sb, sh, sn, prefix)
+    s = da2.Shape(B, H, d, F, Hv, Wv, sb, sh, sn, prefix, cap)
     h = C.c_void_p()
     st = da2.lib().da2_layout_create(C.byref(s), C.byref(h))
     return st, h
@@ -50,6 +50,13 @@ def _layout(B=1, H=2, d=64, F=2, Hv=16, Wv=16, sb=None, sh=None, sn=None, prefix
     (dict(prefix=-1), SHAPE),
     (dict(prefix=4097), SHAPE),
     (dict(prefix=4096, sn=1 << 19), SHAPE),  # prefix rows past 32-bit byte offsets
+    (dict(cap=64), OK),
+    (dict(cap=128), OK),
+    (dict(cap=128, Hv=12, Wv=20), OK),      # regions of 120: a second tile of 56
+    (dict(cap=128, Hv=9, Wv=10), SHAPE),    # one region of 90: a second tile of 26
+    (dict(cap=96), SHAPE),
+    (dict(cap=256), SHAPE),
+    (dict(cap=128, F=140, Hv=128, Wv=128), SHAPE),  # more than 8192 tiles
 ])
 def test_layout_validation(kw, want):
     st, h = _layout(**kw)
@@ -214,3 +221,49 @@ def test_noalloc_refuses_a_workspace_beyond_its_array():
     st, small = _layout(B=1, H=2, d=128, F=2, Hv=64, Wv=72)
     assert st == OK and L.da2_workspace_bytes(small) <= cap
     L.da2_layout_destroy(small)
+
+
+def test_capacity_128_layout_and_workspace():
+    """At C = 128 the layout reports its regions (R = F ceil(HW/128)) and
+    128-slot frame table; the plan's pieces are per region, the attention's
+    per 64-slot tile (twice as many)."""
+    L = da2.lib()
+    st, lay = _layout(B=1, H=2, d=64, F=3, Hv=24, Wv=40, cap=128)
+    assert st == OK
+    rf = C.c_int32()
+    assert L.da2_layout_regions(lay, C.byref(rf)) == 3 * 8 and rf.value == 8
+    tab = np.empty((8, 128), np.int32)
+    assert L.da2_layout_slots(lay, tab.ctypes.data_as(C.c_void_p)) == OK
+    assert ((tab >= 0).sum(axis=1) == 120).all()
+    BH, R, T, d = 2, 24, 48, 64
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["KEYS"]) == BH * R * R * 4
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["Q_AVG"]) == BH * R * d * 8
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["Q_I8_SCALE"]) == BH * T * 4
+    assert L.da2_plan_debug_bytes(lay, da2.DBG["SCHEDULE"]) == BH * T * (T + 3) * 4
+    need = L.da2_workspace_bytes(lay)
+    p = C.c_void_p()
+    assert L.da2_plan_create(lay, C.c_void_p(1 << 20), need, C.byref(p)) == OK
+    q = C.c_void_p(1 << 24)
+    b = da2.Budget(1000, 3000, 0.2, 0, 0, 1)   # block means: capacity 64 only
+    assert L.da2_plan(p, q, q, C.byref(b), None) == INVALID
+    L.da2_plan_destroy(p)
+    L.da2_layout_destroy(lay)
+
+
+@pytest.mark.parametrize("Hv,Wv", [(16, 16), (48, 80), (12, 20), (24, 40), (30, 52), (34, 60), (17, 31), (84, 48)])
+def test_partition_agrees_with_oracle_capacity_128(orc, Hv, Wv):
+    """The library's partition and the oracle's at C = 128: slot tables
+    bit-exact where the library accepts the frame (each 64 slots of a region
+    holding at least 48 tokens), refused exactly where it cannot."""
+    tok, nv = orc.partition_c(Hv, Wv, 128)
+    s = da2.Shape(1, 1, 64, 1, Hv, Wv, Hv * Wv * 64, Hv * Wv * 64, 64, 0, 128)
+    h = C.c_void_p()
+    st = da2.lib().da2_layout_create(C.byref(s), C.byref(h))
+    if nv.min() < 112:
+        assert st == SHAPE
+        return
+    assert st == OK
+    out = np.empty_like(tok)
+    assert da2.lib().da2_layout_slots(h, out.ctypes.data_as(C.c_void_p)) == OK
+    da2.lib().da2_layout_destroy(h)
+    assert np.array_equal(out, tok)

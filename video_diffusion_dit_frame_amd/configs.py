@@ -1,4 +1,5 @@
-"""Workloads: video-DiT attention layers (8x8 spatial regions, 64 tokens).
+"""Workloads: video-DiT attention layers (regions of cap = 64 tokens, the 8x8
+cells when the sides divide, or 128).
 
 Each entry: batch B, heads H, head_dim d, latent frames F x height Hv x width
 Wv (tokens N = F*Hv*Wv in raster order), and budgets as (8-bit, MXFP4) shares
@@ -21,6 +22,7 @@ class Workload:
     seed: int
     outliers: bool = True
     lam: float = 0.2
+    cap: int = 64
 
     @property
     def N(self) -> int:
@@ -28,8 +30,13 @@ class Workload:
 
     @property
     def R(self) -> int:
-        """Regions: frames x ceil(Hv Wv / 64)."""
-        return self.F * (-(-self.Hv * self.Wv // 64))
+        """Regions: frames x ceil(Hv Wv / cap)."""
+        return self.F * (-(-self.Hv * self.Wv // self.cap))
+
+    @property
+    def T(self) -> int:
+        """Attention tiles of 64 slots: cap / 64 per region."""
+        return self.R * self.cap // 64
 
 
 SEED0 = 20260926
@@ -43,6 +50,10 @@ WORKLOADS = {
     # at 832 x 480 and HunyuanVideo at 960 x 544 (spatial compression 16)
     "wan1.3b-480p": Workload("wan1.3b-480p", 1, 12, 128, 21, 30, 52, ((1500, 3500),), SEED0 + 5),
     "hunyuan-544p": Workload("hunyuan-544p", 1, 24, 128, 33, 34, 60, ((1000, 3000),), SEED0 + 6),
+    # the Wan-14B 720p layer at block capacity 128 (the capacity of the
+    # paper's operator study): 30 regions of 128 tokens per frame
+    "wan14b-720p-c128": Workload("wan14b-720p-c128", 1, 40, 128, 21, 48, 80, ((1000, 3000),), SEED0 + 2,
+                                 cap=128),
     "sweep-wan14b-cfg": Workload("sweep-wan14b-cfg", 2, 40, 128, 21, 48, 80,
                                  ((500, 1500), (1000, 3000), (2000, 4000), (0, 6000), (10000, 0)),
                                  SEED0 + 4),

@@ -26,10 +26,13 @@ da2_status check_shape(const da2_shape *s)
         return DA2_ERR_UNSUPPORTED_SHAPE;
     if (s->head_dim != 64 && s->head_dim != 128)
         return DA2_ERR_UNSUPPORTED_SHAPE;
+    if (s->capacity != 0 && s->capacity != 64 && s->capacity != 128)
+        return DA2_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)s->height * s->width > 4096 * kBlk)
         return DA2_ERR_UNSUPPORTED_SHAPE;
-    const int64_t Rf = ((int64_t)s->height * s->width + kBlk - 1) / kBlk;
-    if ((int64_t)s->frames * Rf > kMaxRegions || (int64_t)s->batch * s->heads > 65535)
+    const int64_t C = s->capacity ? s->capacity : kBlk;
+    const int64_t tiles = ((int64_t)s->height * s->width + C - 1) / C * (C / kBlk);
+    if ((int64_t)s->frames * tiles > kMaxRegions || (int64_t)s->batch * s->heads > 65535)
         return DA2_ERR_UNSUPPORTED_SHAPE;
     if (s->stride_n < s->head_dim || s->stride_b < 0 || s->stride_h < 0)
         return DA2_ERR_INVALID_ARG;
@@ -49,8 +52,9 @@ da2_status check_shape(const da2_shape *s)
 
 void carve(da2_layout_s &L)
 {
-    // operand arrays hold every reordered position (padding slots included)
-    const size_t BH = L.BH, N = L.Np, R = L.R, d = L.d;
+    // operand arrays hold every reordered position (padding slots included);
+    // R counts tiles, G regions (the plan's pieces)
+    const size_t BH = L.BH, N = L.Np, R = L.R, G = L.Rg, d = L.d;
     Workspace &W = L.ws;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -82,16 +86,16 @@ void carve(da2_layout_s &L)
     W.ftok = take(L.ragged ? (size_t)L.Rf * kBlk * 4 : 0);
     W.nreg = take(L.ragged ? R * 4 : 0);
     W.vamax = take(BH * d * 4);
-    W.qavg = take(BH * R * d * 8);
-    W.kavg = take(BH * R * d * 8);
-    W.qmax = take(BH * R * d * 4);
-    W.kmax = take(BH * R * d * 4);
-    W.la = take(BH * R * R * 8);
-    W.lm = take(BH * R * R * 8);
-    W.rmax = take(BH * 2 * R * 8);
-    W.zsum = take(BH * 2 * R * 8);
-    W.keys = take(BH * R * R * 4);
-    W.tier = take(BH * R * R);
+    W.qavg = take(BH * G * d * 8);
+    W.kavg = take(BH * G * d * 8);
+    W.qmax = take(BH * G * d * 4);
+    W.kmax = take(BH * G * d * 4);
+    W.la = take(BH * G * G * 8);
+    W.lm = take(BH * G * G * 8);
+    W.rmax = take(BH * 2 * G * 8);
+    W.zsum = take(BH * 2 * G * 8);
+    W.keys = take(BH * G * G * 4);
+    W.tier = take(BH * G * G);
     W.sched = take(BH * R * R * 4);
     W.cnt = take(BH * R * kTargets * 4);
     W.qord = take(BH * R * 4);
@@ -163,23 +167,28 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
     if (!L)
         return DA2_ERR_INVALID_ARG;
     L->s = *shape;
+    L->C = shape->capacity ? shape->capacity : kBlk;
+    L->tpr = L->C / kBlk;
     L->N = shape->frames * shape->height * shape->width;
     L->Ry = shape->height / 8;
     L->Rx = shape->width / 8;
-    if (shape->height % 8 == 0 && shape->width % 8 == 0) {
+    if (L->C == kBlk && shape->height % 8 == 0 && shape->width % 8 == 0) {
         // the 8x8 grid: slots follow from a closed form
         L->Rf = L->Ry * L->Rx;
+        L->Rfg = L->Rf;
     } else {
-        const int Rf = (shape->height * shape->width + kBlk - 1) / kBlk;
-        L->ftok = (int32_t *)malloc(sizeof(int32_t) * Rf * kBlk);
-        if (!L->ftok || partition_frame(shape->height, shape->width, L->ftok) != Rf) {
+        // a slot table: region r's C slots are tiles r*tpr .. r*tpr + tpr - 1
+        const int Rfg = (shape->height * shape->width + L->C - 1) / L->C;
+        L->ftok = (int32_t *)malloc(sizeof(int32_t) * Rfg * L->C);
+        if (!L->ftok || partition_frame(shape->height, shape->width, L->C, L->ftok) != Rfg) {
             free(L->ftok);
             free(L);
             return DA2_ERR_UNSUPPORTED_SHAPE;
         }
-        L->Rf = Rf;
+        L->Rfg = Rfg;
+        L->Rf = Rfg * L->tpr;
         L->ragged = 1;
-        for (int r = 0; r < Rf; r++) {
+        for (int r = 0; r < L->Rf; r++) {   // padding of every tile
             int n = 0;
             while (n < kBlk && L->ftok[r * kBlk + n] >= 0)
                 n++;
@@ -187,6 +196,7 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
         }
     }
     L->R = shape->frames * L->Rf;
+    L->Rg = shape->frames * L->Rfg;
     if (L->ragged) {
         L->nreg = (int32_t *)malloc(sizeof(int32_t) * L->R);
         if (!L->nreg) {
@@ -205,7 +215,7 @@ da2_status da2_layout_create(const da2_shape *shape, da2_layout_t **out)
     L->Np = L->R * kBlk;
     L->BH = shape->batch * shape->heads;
     L->d = shape->head_dim;
-    L->nchunk = ((int64_t)L->R * L->R + 4095) / 4096;
+    L->nchunk = ((int64_t)L->Rg * L->Rg + 4095) / 4096;
     L->ptiles = (shape->prefix + kBlk - 1) / kBlk;
     L->pchunks = L->ptiles ? (L->ptiles + L->R + kPrefixChunkTiles - 1) / kPrefixChunkTiles : 0;
     carve(*L);
@@ -229,8 +239,8 @@ int32_t da2_layout_regions(const da2_layout_t *layout, int32_t *regions_per_fram
     if (!layout)
         return 0;
     if (regions_per_frame)
-        *regions_per_frame = layout->Rf;
-    return layout->R;
+        *regions_per_frame = layout->Rfg;
+    return layout->Rg;
 }
 
 da2_status da2_layout_slots(const da2_layout_t *layout, int32_t *dst)
@@ -351,7 +361,9 @@ da2_status da2_plan(da2_plan_t *P, const void *q, const void *k, const da2_budge
     if (bud->skip_means != 0 && bud->skip_means != 1)
         return DA2_ERR_INVALID_ARG;
     const da2_layout_s &L = P->L;
-    const int64_t n = bud->scope == 0 ? (int64_t)L.R * L.R : (int64_t)L.R;
+    if (bud->skip_means && L.tpr > 1)
+        return DA2_ERR_INVALID_ARG;
+    const int64_t n = bud->scope == 0 ? (int64_t)L.Rg * L.Rg : (int64_t)L.Rg;
     int64_t t16, t8, tk;
     da2_quotas(n, bud->full_bp, bud->hi_bp, bud->lo_bp, &t16, &t8, &tk);
     P->ready = 0;
@@ -393,9 +405,10 @@ da2_status da2_plan_from_tier_map(da2_plan_t *P, const void *q, const void *k,
     launch_prep_qk(L, k, 1, P->ws, stream);
     launch_import_tier(L, tier_map, P->ws, stream);
     launch_schedule(L, P->ws, stream);
-    // the map may hold block-mean tiles: their scores are the draft's
-    // average-branch logits
-    launch_draft_logits(L, P->ws, stream);
+    // the map may hold block-mean tiles (capacity 64 only): their scores are
+    // the draft's average-branch logits
+    if (L.tpr == 1)
+        launch_draft_logits(L, P->ws, stream);
     da2_status st = launched();
     if (st != DA2_OK)
         return st;
@@ -404,7 +417,7 @@ da2_status da2_plan_from_tier_map(da2_plan_t *P, const void *q, const void *k,
     P->ready = 1;
     P->has_keys = 0;
     P->has16 = 1;  // the imported map may hold 16-bit tiles
-    P->has_mean = 1;
+    P->has_mean = L.tpr == 1;
     return DA2_OK;
 }
 
@@ -415,7 +428,7 @@ da2_status da2_plan_tier_map(const da2_plan_t *P, uint8_t *dst, hipStream_t stre
     if (!P->ready)
         return DA2_ERR_PLAN_MISMATCH;
     const da2_layout_s &L = P->L;
-    hipError_t e = hipMemcpyAsync(dst, P->ws + L.ws.tier, (size_t)L.BH * L.R * L.R,
+    hipError_t e = hipMemcpyAsync(dst, P->ws + L.ws.tier, (size_t)L.BH * L.Rg * L.Rg,
                                   hipMemcpyDeviceToDevice, stream);
     return e == hipSuccess ? DA2_OK : DA2_ERR_HIP;
 }
@@ -475,7 +488,7 @@ size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which)
 {
     if (!layout)
         return 0;
-    const size_t BH = layout->BH, N = layout->Np, R = layout->R, d = layout->d;
+    const size_t BH = layout->BH, N = layout->Np, R = layout->R, G = layout->Rg, d = layout->d;
     switch (which) {
     case DA2_DBG_Q_I8: case DA2_DBG_K_I8: case DA2_DBG_V_FP8:
     case DA2_DBG_Q_MX: case DA2_DBG_K_MX: case DA2_DBG_V_MX:
@@ -489,11 +502,11 @@ size_t da2_plan_debug_bytes(const da2_layout_t *layout, int32_t which)
     case DA2_DBG_V_MX_SCALE:
         return BH * R * 2 * d;
     case DA2_DBG_Q_AVG: case DA2_DBG_K_AVG:
-        return BH * R * d * 8;
+        return BH * G * d * 8;
     case DA2_DBG_Q_MAX: case DA2_DBG_K_MAX:
-        return BH * R * d * 4;
+        return BH * G * d * 4;
     case DA2_DBG_KEYS:
-        return BH * R * R * 4;
+        return BH * G * G * 4;
     case DA2_DBG_SCHEDULE:
         return BH * R * (R + kTargets) * 4;
     default:

@@ -9,18 +9,19 @@
 
 namespace da2 {
 
-constexpr int kBlk = 64;          // tokens per region: one 8x8 spatial cell
-constexpr int kMaxRegions = 8192; // R limit (keeps R*R in 32 bits, row scope in LDS)
+constexpr int kBlk = 64;          // slots per tile (a region at capacity 64: one 8x8 cell)
+constexpr int kMaxRegions = 8192; // tile limit (keeps R*R in 32 bits, row scope in LDS)
 constexpr int kMaxTimed = 4096;   // attention calls recorded while timing
 constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
 constexpr int kPrefixChunkTiles = 128; // tiles per chunk of a prefix query row
 constexpr int kMaxPrefix = 4096;  // text-prefix tokens per sequence
-constexpr int kMinFill = 48;      // fewest valid tokens of a region (at most 16 padding slots)
+constexpr int kMinFill = 48;      // fewest valid tokens of a tile (at most 16 padding slots)
+constexpr int kMaxTpr = 2;        // tiles per region at the largest block capacity (128)
 constexpr uint8_t kMeanTier = 1;  // tier of a block-mean tile (skip replaced by block means)
 
 // ---------------------------------------------------------------------------
 // Workspace: one region of caller memory carved into these buffers.
-// Packed operand layouts (per (b,h) slice "bh", per region a):
+// Packed operand layouts (per (b,h) slice "bh", per tile a of 64 slots):
 //   Q int8 : [bh][a][w=2][kc=d/64][lane=64][32 B]   B operand of S^T = K Q^T:
 //            lane l holds row 32 w + l % 32, channels 64 kc + 32 (l / 32) .. +31
 //   K int8 : [bh][a][m=2][kc][lane][32 B]           A operand, key rows permuted
@@ -39,9 +40,12 @@ constexpr uint8_t kMeanTier = 1;  // tier of a block-mean tile (skip replaced by
 //   V fp8 values : the layout of V bf16, holding the value of every FP8
 //            value code (unscaled) as bf16 (exact: E4M3 has 4 significant
 //            bits); the value operand of the 8-bit tier's P^T V
-//   frame slot table (ragged layouts) : int32 [R_f][64], token y*W_v + x of
-//            each slot of the frame's regions, -1 for padding; int32 [R]
-//            valid tokens of every region
+//   frame slot table (ragged layouts) : int32 [Rf tiles][64], token
+//            y*W_v + x of each slot of the frame's regions, -1 for padding;
+//            int32 [R] valid tokens of every tile
+//   pooled descriptors, draft logits, keys and the tier map are per region
+//            ([bh][Rg][d], [bh][Rg][Rg]); the schedule, its counts and the
+//            work order per tile ([bh][R][R], [bh][R][3], [bh][R])
 //   prefix partials : fp32 [bh][chunk][row][d] unnormalised outputs and
 //            float2 [bh][chunk][row] (running max, sum) of the prefix query
 //            rows' chunks, rows padded to ptiles*64
@@ -54,7 +58,7 @@ struct Workspace {
     size_t v8b;          // bf16 image of the FP8 value codes (8-bit tier P^T V)
     size_t vavg, magg, cagg;  // block-mean tiles: region mean values; per query region the
                               // gathered term (max logit, weight) and its value sum
-    size_t ftok, nreg;   // ragged layouts: frame slot table, valid tokens per region
+    size_t ftok, nreg;   // ragged layouts: frame slot table, valid tokens per tile
     size_t qavg, kavg, qmax, kmax;
     size_t la, lm, rmax, zsum, keys, tier;
     size_t sched, cnt;
@@ -72,15 +76,23 @@ struct RankState {      // one per (segment, target)
 
 }  // namespace da2
 
+// Regions and tiles.  A region of capacity C holds C slots, tpr = C / 64
+// tiles of 64.  Everything the attention side touches (operands, schedule,
+// work order, slot tables) is per tile: R tiles, Rf per frame, and the tile
+// is what the kernels call a region.  The plan side (pooled descriptors,
+// draft logits and keys, ranking, tier map) is per region: Rg regions, Rfg
+// per frame.  At C = 64 the two coincide.
 struct da2_layout_s {
     da2_shape s;
     int N, R, Ry, Rx, BH, d;
     int Np;                   // reordered positions R*64 (padding slots included)
-    int Rf;                   // regions per frame
+    int Rf;                   // tiles per frame
+    int C, tpr;               // block capacity and tiles per region
+    int Rg, Rfg;              // regions, regions per frame
     int ragged;               // 0: the 8x8 grid (closed form); 1: slot table
-    int pmax;                 // most padding slots of any region (0..16)
+    int pmax;                 // most padding slots of any tile (0..16)
     int32_t *ftok;            // ragged: frame slot table [Rf*64] (host, owned)
-    int32_t *nreg;            // ragged: valid tokens of every region [R] (host, owned by
+    int32_t *nreg;            // ragged: valid tokens of every tile [R] (host, owned by
                               // the layout; a plan's copy of the layout does not use it)
     int64_t nchunk;           // rank chunks per head (head scope)
     int ptiles;               // 64-key tiles of the text prefix (ceil(prefix / 64))
@@ -91,7 +103,7 @@ struct da2_layout_s {
 struct da2_plan_s {
     da2_layout_s L;           // its ftok is the plan's own copy
     int tables_ready;         // frame slot table uploaded to the workspace
-    int32_t *nreg;            // ragged: valid tokens of every region [R] (host)
+    int32_t *nreg;            // ragged: valid tokens of every tile [R] (host)
     char *ws;
     size_t ws_bytes;
     const void *q, *k;        // inputs the plan was built on
@@ -117,9 +129,10 @@ struct PrefixIo {
 // Launchers (defined in the kernel translation units).
 // ---------------------------------------------------------------------------
 void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, hipStream_t st);
-// Spatial partition of one Hv x Wv frame (defined in da2_partition.cpp):
-// fills tok [Rf*64] (y*Wv + x or -1) and returns Rf, or -1 without one.
-int partition_frame(int Hv, int Wv, int32_t *tok);
+// Spatial partition of one Hv x Wv frame into regions of capacity C
+// (defined in da2_partition.cpp): fills tok [Rf*C] (y*Wv + x or -1) and
+// returns Rf, or -1 without one.
+int partition_frame(int Hv, int Wv, int C, int32_t *tok);
 void launch_prep_v(const da2_layout_s &L, const void *v, int with16, int with_mean, char *ws, hipStream_t st);
 void launch_prep_vp(const da2_layout_s &L, const PrefixIo &px, char *ws, hipStream_t st);
 void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st);

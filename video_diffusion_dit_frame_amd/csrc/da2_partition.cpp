@@ -1,5 +1,5 @@
 // da2_partition.cpp -- the spatial partition of a latent frame into regions of
-// at most C = 64 tokens (DraftAttention2, Sec. 3.3: a ragged 2D partition with
+// at most C tokens, C = 64 or 128 (DraftAttention2, Sec. 3.3: a ragged 2D partition with
 // balanced token counts across regions, the smallest total perimeter among
 // candidate partitions, the minimum number of blocks and less than one block
 // of padding per frame; App. C.2: R_f = ceil(H_v W_v / C)).
@@ -20,8 +20,9 @@
 // slots in raster order, the remaining slots are padding.  For H_v, W_v
 // multiples of 8 the result is the 8x8 grid.
 //
-// The attention kernels handle at most 16 padding slots per region, so a
-// frame whose regions hold fewer than 48 tokens (q < 48) is refused here.
+// The attention kernels handle at most 16 padding slots per 64-slot tile,
+// and a region's padding slots all lie in its last tile, so a frame whose
+// regions hold fewer than C - 16 tokens is refused here.
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -130,13 +131,13 @@ Choice best_composition(int E, int L, int Rf, int q, bool big)
 
 }  // namespace
 
-int partition_frame(int Hv, int Wv, int32_t *tok)
+int partition_frame(int Hv, int Wv, int C, int32_t *tok)
 {
-    if (Hv < 1 || Wv < 1)
+    if (Hv < 1 || Wv < 1 || C < kBlk || C % kBlk)
         return -1;
-    const int n = Hv * Wv, Rf = (n + kBlk - 1) / kBlk, q = n / Rf;
+    const int n = Hv * Wv, Rf = (n + C - 1) / C, q = n / Rf;
     const bool big = n % Rf != 0;
-    if (q < kMinFill)
+    if (q < C - (kBlk - kMinFill))
         return -1;
     const Choice rows = best_composition(Hv, Wv, Rf, q, big);
     const Choice cols = best_composition(Wv, Hv, Rf, q, big);
@@ -163,11 +164,11 @@ int partition_frame(int Hv, int Wv, int32_t *tok)
         line0 += h;
     }
     std::vector<int> fill(Rf, 0);
-    for (int i = 0; i < Rf * kBlk; i++)
+    for (int i = 0; i < Rf * C; i++)
         tok[i] = -1;
     for (int t = 0; t < n; t++) {
         const int r = region[t];
-        tok[r * kBlk + fill[r]++] = t;   // raster order inside the region
+        tok[r * C + fill[r]++] = t;   // raster order inside the region
     }
     return Rf;
 }

@@ -142,19 +142,19 @@ void launch_debug(const da2_layout_s &L, int which, const char *ws, void *dst, h
         hipMemcpyAsync(dst, ws + W.vs8, sizeof(float) * L.BH * d, hipMemcpyDeviceToDevice, st);
         break;
     case DA2_DBG_Q_AVG:
-        hipMemcpyAsync(dst, ws + W.qavg, sizeof(double) * L.BH * L.R * d, hipMemcpyDeviceToDevice, st);
+        hipMemcpyAsync(dst, ws + W.qavg, sizeof(double) * L.BH * L.Rg * d, hipMemcpyDeviceToDevice, st);
         break;
     case DA2_DBG_K_AVG:
-        hipMemcpyAsync(dst, ws + W.kavg, sizeof(double) * L.BH * L.R * d, hipMemcpyDeviceToDevice, st);
+        hipMemcpyAsync(dst, ws + W.kavg, sizeof(double) * L.BH * L.Rg * d, hipMemcpyDeviceToDevice, st);
         break;
     case DA2_DBG_Q_MAX:
-        hipMemcpyAsync(dst, ws + W.qmax, sizeof(float) * L.BH * L.R * d, hipMemcpyDeviceToDevice, st);
+        hipMemcpyAsync(dst, ws + W.qmax, sizeof(float) * L.BH * L.Rg * d, hipMemcpyDeviceToDevice, st);
         break;
     case DA2_DBG_K_MAX:
-        hipMemcpyAsync(dst, ws + W.kmax, sizeof(float) * L.BH * L.R * d, hipMemcpyDeviceToDevice, st);
+        hipMemcpyAsync(dst, ws + W.kmax, sizeof(float) * L.BH * L.Rg * d, hipMemcpyDeviceToDevice, st);
         break;
     case DA2_DBG_KEYS:
-        hipMemcpyAsync(dst, ws + W.keys, sizeof(uint32_t) * L.BH * L.R * L.R, hipMemcpyDeviceToDevice, st);
+        hipMemcpyAsync(dst, ws + W.keys, sizeof(uint32_t) * L.BH * L.Rg * L.Rg, hipMemcpyDeviceToDevice, st);
         break;
     case DA2_DBG_SCHEDULE: {
         const int64_t rows = (int64_t)L.BH * L.R;

@@ -709,17 +709,22 @@ __global__ __launch_bounds__(256) void k_rank_rows(const uint32_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Schedule: per query region, the 16-bit key regions ascending, then FP8
-// ascending, then MXFP4 ascending; counts n16, n8, n4.  One wave per row.
+// Schedule: per query tile, the key tiles of its region's 16-bit key regions
+// ascending, then 8-bit ascending, then MXFP4 ascending; counts n16, n8, n4
+// of tiles.  The tier map is per region pair (G regions of tpr tiles each);
+// a kept key region b contributes its tiles b tpr .. b tpr + tpr - 1 in
+// order.  One wave per query tile (blockIdx.x); the tiles of one region
+// get the same list.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tier, int R,
+__global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tier, int R, int tpr,
                                                  int32_t *__restrict__ sched,
                                                  int32_t *__restrict__ cnt)
 {
     __shared__ __attribute__((aligned(16))) uint8_t rowl[kMaxRegions];
-    const int64_t row = (int64_t)blockIdx.y * R + blockIdx.x;
+    const int T = R * tpr;                                  // tiles per head
+    const int64_t row = (int64_t)blockIdx.y * T + blockIdx.x;
     const int l = threadIdx.x;
-    const uint8_t *tg = tier + row * R;
+    const uint8_t *tg = tier + ((int64_t)blockIdx.y * R + blockIdx.x / tpr) * R;
     // stage the row in LDS: dword reads when the row starts on a dword
     int b4 = 0;
     if ((reinterpret_cast<uintptr_t>(tg) & 3) == 0) {
@@ -744,27 +749,31 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
     n16 = wave_sum_u32(n16);
     n8 = wave_sum_u32(n8);
     n4 = wave_sum_u32(n4);
-    int32_t *out = sched + row * R;
-    uint32_t o16 = 0, o8 = n16, o4 = n16 + n8;
+    int32_t *out = sched + row * T;
+    uint32_t o16 = 0, o8 = n16, o4 = n16 + n8;   // in regions
     for (int b0 = 0; b0 < R; b0 += 64) {
         int b = b0 + l;
         uint8_t v = b < R ? tr[b] : 0;
         uint64_t m16 = __ballot(v == 16), m8 = __ballot(v == 8), m4 = __ballot(v == 4);
         uint64_t lt = (l == 0) ? 0ull : (~0ull >> (64 - l));
+        int pos = -1;
         if (v == 16)
-            out[o16 + __popcll(m16 & lt)] = b;
+            pos = o16 + __popcll(m16 & lt);
         if (v == 8)
-            out[o8 + __popcll(m8 & lt)] = b;
+            pos = o8 + __popcll(m8 & lt);
         if (v == 4)
-            out[o4 + __popcll(m4 & lt)] = b;
+            pos = o4 + __popcll(m4 & lt);
+        if (pos >= 0)
+            for (int j = 0; j < tpr; j++)
+                out[pos * tpr + j] = b * tpr + j;
         o16 += __popcll(m16);
         o8 += __popcll(m8);
         o4 += __popcll(m4);
     }
     if (l == 0) {
-        cnt[row * kTargets] = (int32_t)n16;
-        cnt[row * kTargets + 1] = (int32_t)n8;
-        cnt[row * kTargets + 2] = (int32_t)n4;
+        cnt[row * kTargets] = (int32_t)(n16 * tpr);
+        cnt[row * kTargets + 1] = (int32_t)(n8 * tpr);
+        cnt[row * kTargets + 2] = (int32_t)(n4 * tpr);
     }
 }
 
@@ -805,12 +814,14 @@ __global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt,
     }
 }
 
-__global__ void k_copy_tier(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t n)
+// Imported tier map: unknown values are skips; block-mean tiles exist at
+// capacity 64 only (means: whether they are known).
+__global__ void k_copy_tier(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t n, int means)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) {
         uint8_t v = src[i];
-        dst[i] = (v == 16 || v == 8 || v == 4 || v == kMeanTier) ? v : 0;
+        dst[i] = (v == 16 || v == 8 || v == 4 || (means && v == kMeanTier)) ? v : 0;
     }
 }
 
@@ -826,7 +837,7 @@ __global__ void k_skip_means_kernel(uint8_t *__restrict__ tier, int64_t n)
 
 void launch_skip_means(const da2_layout_s &L, char *ws, hipStream_t st)
 {
-    const int64_t n = (int64_t)L.BH * L.R * L.R;
+    const int64_t n = (int64_t)L.BH * L.Rg * L.Rg;
     k_skip_means_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((uint8_t *)(ws + L.ws.tier), n);
 }
 
@@ -836,32 +847,32 @@ void launch_draft_logits(const da2_layout_s &L, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
     const double inv_sqrt_d = 1.0 / __builtin_sqrt((double)L.d);
-    const int T2 = (L.R + 127) / 128;
+    const int T2 = (L.Rg + 127) / 128;
     double *La = (double *)(ws + W.la), *Lm = (double *)(ws + W.lm);
     unsigned long long *rmax = (unsigned long long *)(ws + W.rmax);
-    const int64_t nmax = (int64_t)L.BH * 2 * L.R * 2;  // as 32-bit words
+    const int64_t nmax = (int64_t)L.BH * 2 * L.Rg * 2;  // as 32-bit words
     k_fill_words<<<(unsigned)((nmax + 255) / 256), 256, 0, st>>>((uint32_t *)rmax, nmax);
     dim3 g(T2, T2, 2 * L.BH);
     if (L.d == 128)
         k_logits<128><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
                                          (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
-                                         L.R, inv_sqrt_d, La, Lm, rmax);
+                                         L.Rg, inv_sqrt_d, La, Lm, rmax);
     else
         k_logits<64><<<g, 256, 0, st>>>((const double *)(ws + W.qavg), (const double *)(ws + W.kavg),
                                         (const float *)(ws + W.qmax), (const float *)(ws + W.kmax),
-                                        L.R, inv_sqrt_d, La, Lm, rmax);
+                                        L.Rg, inv_sqrt_d, La, Lm, rmax);
 }
 
 void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
-    const int T = (L.R + 63) / 64;
+    const int T = (L.Rg + 63) / 64;
     double *La = (double *)(ws + W.la), *Lm = (double *)(ws + W.lm);
     unsigned long long *rmax = (unsigned long long *)(ws + W.rmax);
     double *zsum = (double *)(ws + W.zsum);
     launch_draft_logits(L, ws, st);
-    k_rowsum<<<dim3(T, L.BH, 2), 256, 0, st>>>(La, Lm, L.R, rmax, zsum);
-    k_keys<<<dim3(L.R, L.BH), 256, 0, st>>>(La, Lm, L.R, lambda, rmax, zsum,
+    k_rowsum<<<dim3(T, L.BH, 2), 256, 0, st>>>(La, Lm, L.Rg, rmax, zsum);
+    k_keys<<<dim3(L.Rg, L.BH), 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum,
                                             (uint32_t *)(ws + W.keys));
 }
 
@@ -872,13 +883,13 @@ void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int
     const uint32_t *keys = (const uint32_t *)(ws + W.keys);
     uint8_t *tier = (uint8_t *)(ws + W.tier);
     if (scope == 1) {
-        k_rank_rows<<<(unsigned)((int64_t)L.BH * L.R), 256, sizeof(uint32_t) * L.R, st>>>(
-            keys, L.R, t16, t8c, tk, tier);
+        k_rank_rows<<<(unsigned)((int64_t)L.BH * L.Rg), 256, sizeof(uint32_t) * L.Rg, st>>>(
+            keys, L.Rg, t16, t8c, tk, tier);
         return;
     }
     RankState *rs = (RankState *)(ws + W.rank_state);
     uint32_t *hist = (uint32_t *)(ws + W.rank_hist), *eq = (uint32_t *)(ws + W.rank_eq);
-    const int64_t seglen = (int64_t)L.R * L.R;
+    const int64_t seglen = (int64_t)L.Rg * L.Rg;
     const int64_t nchunk = L.nchunk;
     k_rank_init<<<(L.BH * kTargets * 256 + 255) / 256, 256, 0, st>>>(rs, hist, L.BH, t16, t8c, tk);
     dim3 g((unsigned)nchunk, L.BH);
@@ -893,7 +904,7 @@ void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int
 void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
-    k_schedule<<<dim3(L.R, L.BH), 64, 0, st>>>((const uint8_t *)(ws + W.tier), L.R,
+    k_schedule<<<dim3(L.R, L.BH), 64, 0, st>>>((const uint8_t *)(ws + W.tier), L.Rg, L.tpr,
                                                 (int32_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
     k_qorder<<<dim3(8, L.BH), 256, 0, st>>>((const int32_t *)(ws + W.cnt), L.R, L.Rf,
                                             (int32_t *)(ws + W.qord));
@@ -901,8 +912,9 @@ void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
 
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st)
 {
-    int64_t n = (int64_t)L.BH * L.R * L.R;
-    k_copy_tier<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(src, (uint8_t *)(ws + L.ws.tier), n);
+    int64_t n = (int64_t)L.BH * L.Rg * L.Rg;
+    k_copy_tier<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(src, (uint8_t *)(ws + L.ws.tier), n,
+                                                             L.tpr == 1);
 }
 
 }  // namespace da2

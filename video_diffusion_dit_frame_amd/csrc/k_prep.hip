@@ -63,8 +63,9 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
 
     const int t = threadIdx.x;
     const int64_t blk = (int64_t)bh * R + a;
-    // pooled descriptors: channel t, valid tokens in slot order
-    if (t < D) {
+    // pooled descriptors: channel t, valid tokens in slot order (regions of
+    // more than one tile pool in k_pool: avg is null then)
+    if (avg && t < D) {
         double s = 0.0;
         float m = bf16_to_f32(tile[t]);
         for (int i = 0; i < na; i++) {
@@ -133,6 +134,48 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
         *reinterpret_cast<uint4 *>(op4 + blk * (kBlk * D / 2) + (int64_t)t * 16) =
             make_uint4(w4[0], w4[1], w4[2], w4[3]);
         op4s[blk * (2 * D) + t] = (uint8_t)(E + 127);
+    }
+}
+
+// Pooled descriptors of regions of tpr > 1 tiles (block capacity tpr * 64):
+// one workgroup per (b, h, region) gathers the region's slots into LDS, and
+// channel t sums its valid tokens in slot order (fp64, tile after tile) and
+// takes their signed maximum, as k_prep_qk does for a one-tile region.  The
+// valid tokens fill the region's first slots.
+template <int D>
+__global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ x, int64_t sb, int64_t sh,
+                                              int64_t sn, int H, int G, int tpr, Geo g,
+                                              double *__restrict__ avg, float *__restrict__ mx)
+{
+    constexpr int CH = D / 8;  // 16-byte chunks per token row
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kMaxTpr * kBlk * D];
+    const int a = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
+    const int slots = tpr * kBlk;
+    for (int ci = threadIdx.x; ci < slots * CH; ci += 256) {
+        const int i = ci / CH, c8 = ci - i * CH;
+        const int n = slot_token<true>(g, a * tpr + i / kBlk, i % kBlk);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (n >= 0)
+            v = *reinterpret_cast<const uint4 *>(xb + (int64_t)n * sn + c8 * 8);
+        *reinterpret_cast<uint4 *>(tile + i * D + c8 * 8) = v;
+    }
+    const int i0 = threadIdx.x;
+    const int na = __syncthreads_count(i0 < slots && slot_token<true>(g, a * tpr + i0 / kBlk, i0 % kBlk) >= 0);
+    const int t = threadIdx.x;
+    if (t < D) {
+        double s = 0.0;
+        float m = bf16_to_f32(tile[t]);
+        for (int i = 0; i < na; i++) {
+            float v = bf16_to_f32(tile[i * D + t]);
+            s += (double)v;
+            if (v > m)
+                m = v;
+        }
+        const int64_t r = (int64_t)bh * G + a;
+        avg[r * D + t] = s / (double)na;
+        mx[r * D + t] = m;
     }
 }
 
@@ -330,9 +373,11 @@ void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, 
     uint16_t *op16 = (uint16_t *)(ws + W.k16);
     const da2_shape &s = L.s;
     const Geo g = layout_geo(L, ws);
+    // one-tile regions pool in k_prep_qk, larger ones in k_pool
+    double *avg1 = L.tpr == 1 ? avg : nullptr;
 #define DA2_PREP_QK(DD, RG)                                                                           \
     k_prep_qk<DD, RG><<<grid, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.R, g, is_key, \
-                                            op8, s8, op4, op4s, avg, mx, op16)
+                                            op8, s8, op4, op4s, avg1, mx, op16)
     if (L.d == 128) {
         if (L.ragged)
             DA2_PREP_QK(128, true);
@@ -345,6 +390,13 @@ void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, 
             DA2_PREP_QK(64, false);
     }
 #undef DA2_PREP_QK
+    if (L.tpr > 1) {
+        dim3 gp(L.Rg, L.BH);
+        if (L.d == 128)
+            k_pool<128><<<gp, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.Rg, L.tpr, g, avg, mx);
+        else
+            k_pool<64><<<gp, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.Rg, L.tpr, g, avg, mx);
+    }
 }
 
 void launch_prep_v(const da2_layout_s &L, const void *v, int with16, int with_mean, char *ws, hipStream_t st)

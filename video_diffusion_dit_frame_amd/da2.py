@@ -32,7 +32,7 @@ class Shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("heads", C.c_int32), ("head_dim", C.c_int32),
                 ("frames", C.c_int32), ("height", C.c_int32), ("width", C.c_int32),
                 ("stride_b", C.c_int64), ("stride_h", C.c_int64), ("stride_n", C.c_int64),
-                ("prefix", C.c_int32)]
+                ("prefix", C.c_int32), ("capacity", C.c_int32)]
 
 
 class Budget(C.Structure):
@@ -140,32 +140,35 @@ def quotas(n, hi_bp, lo_bp):
 
 class Layout:
     """Region layout for one shape.  q/k/v/o are addressed with the given
-    element strides (channel stride 1)."""
+    element strides (channel stride 1).  cap: block capacity (64 or 128);
+    R regions (Rf per frame) of cap slots, T = R cap / 64 tiles."""
 
-    def __init__(self, B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix=0):
+    def __init__(self, B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix=0, cap=64):
         self.B, self.H, self.d, self.F, self.Hv, self.Wv = B, H, d, F, Hv, Wv
         self.N = F * Hv * Wv
         self.prefix = prefix
-        self.shape = Shape(B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix)
+        self.cap = cap
+        self.shape = Shape(B, H, d, F, Hv, Wv, stride_b, stride_h, stride_n, prefix, cap)
         h = C.c_void_p()
         _check(lib().da2_layout_create(C.byref(self.shape), C.byref(h)), "da2_layout_create")
         self.handle = h
         rf = C.c_int32()
         self.R = int(lib().da2_layout_regions(h, C.byref(rf)))
         self.Rf = rf.value
-        self.Np = 64 * self.R
+        self.Np = cap * self.R
+        self.T = self.Np // 64
 
     def slots(self):
-        """One frame's partition: int32 [R_f, 64], token y*Wv + x of each slot
+        """One frame's partition: int32 [R_f, cap], token y*Wv + x of each slot
         (-1: padding)."""
         import numpy as np
 
-        out = np.empty((self.Rf, 64), np.int32)
+        out = np.empty((self.Rf, self.cap), np.int32)
         _check(lib().da2_layout_slots(self.handle, out.ctypes.data_as(C.c_void_p)), "da2_layout_slots")
         return out
 
     @classmethod
-    def for_tensor(cls, x: torch.Tensor, F, Hv, Wv, bhnd=True, prefix=0):
+    def for_tensor(cls, x: torch.Tensor, F, Hv, Wv, bhnd=True, prefix=0, cap=64):
         """x: a [B, H, N, d] view (bhnd) or a [B, N, H, d] view, channel-contiguous."""
         if bhnd:
             B, H, N, d = x.shape
@@ -174,7 +177,7 @@ class Layout:
             B, N, H, d = x.shape
             sb, sn, sh, sc = x.stride()
         assert sc == 1 and N == F * Hv * Wv
-        return cls(B, H, d, F, Hv, Wv, sb, sh, sn, prefix)
+        return cls(B, H, d, F, Hv, Wv, sb, sh, sn, prefix, cap)
 
     @property
     def workspace_bytes(self) -> int:
