@@ -16,7 +16,6 @@ constexpr int kTargets = 3;       // ranking thresholds: T16, T16+T8, T16+T8+T4
 constexpr int kPrefixChunkTiles = 128; // tiles per chunk of a prefix query row
 constexpr int kMaxPrefix = 4096;  // text-prefix tokens per sequence
 constexpr int kMinFill = 48;      // fewest valid tokens of a tile (at most 16 padding slots)
-constexpr int kMaxTpr = 2;        // tiles per region at the largest block capacity (128)
 constexpr uint8_t kMeanTier = 1;  // tier of a block-mean tile (skip replaced by block means)
 
 // ---------------------------------------------------------------------------

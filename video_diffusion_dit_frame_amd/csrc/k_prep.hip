@@ -22,20 +22,35 @@
 namespace da2 {
 namespace {
 
-// Copy the 64 x D bf16 tile of region a into LDS (row i = slot i; padding
-// slots of a ragged layout are zero rows).
-template <int D, bool RAG>
-__device__ __forceinline__ void load_region(const uint16_t *__restrict__ x, int64_t sn, int a,
+// Copy the NT x 64 x D bf16 tiles a0 .. a0 + NT - 1 into LDS (row i = slot
+// i of the run; padding slots of a ragged layout are zero rows).  All slot
+// lookups first, then all row loads, then the stores, so that every load of
+// the 256 threads is in flight at once.
+template <int D, bool RAG, int NT = 1>
+__device__ __forceinline__ void load_region(const uint16_t *__restrict__ x, int64_t sn, int a0,
                                             const Geo &g, uint16_t *tile)
 {
     constexpr int CH = D / 8;  // 16-byte chunks per token row
-    for (int ci = threadIdx.x; ci < kBlk * CH; ci += 256) {
-        int i = ci / CH, c8 = ci - i * CH;
-        int n = slot_token<RAG>(g, a, i);
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (n >= 0)
-            v = *reinterpret_cast<const uint4 *>(x + (int64_t)n * sn + c8 * 8);
-        *reinterpret_cast<uint4 *>(tile + i * D + c8 * 8) = v;
+    constexpr int ITER = NT * kBlk * CH / 256;
+    static_assert(ITER * 256 == NT * kBlk * CH, "whole rounds of 256 chunks");
+    int n[ITER];
+#pragma unroll
+    for (int u = 0; u < ITER; u++) {
+        const int i = (int)(threadIdx.x + 256 * u) / CH;
+        n[u] = slot_token<RAG>(g, a0 + i / kBlk, i % kBlk);
+    }
+    uint4 v[ITER];
+#pragma unroll
+    for (int u = 0; u < ITER; u++) {
+        const int ci = threadIdx.x + 256 * u, i = ci / CH, c8 = ci - i * CH;
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (n[u] >= 0)
+            v[u] = *reinterpret_cast<const uint4 *>(x + (int64_t)n[u] * sn + c8 * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < ITER; u++) {
+        const int ci = threadIdx.x + 256 * u, i = ci / CH, c8 = ci - i * CH;
+        *reinterpret_cast<uint4 *>(tile + i * D + c8 * 8) = v[u];
     }
 }
 
@@ -142,27 +157,19 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
 // channel t sums its valid tokens in slot order (fp64, tile after tile) and
 // takes their signed maximum, as k_prep_qk does for a one-tile region.  The
 // valid tokens fill the region's first slots.
-template <int D>
+template <int D, int TPR>
 __global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ x, int64_t sb, int64_t sh,
-                                              int64_t sn, int H, int G, int tpr, Geo g,
+                                              int64_t sn, int H, int G, Geo g,
                                               double *__restrict__ avg, float *__restrict__ mx)
 {
-    constexpr int CH = D / 8;  // 16-byte chunks per token row
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kMaxTpr * kBlk * D];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[TPR * kBlk * D];
     const int a = blockIdx.x, bh = blockIdx.y;
     const int b = bh / H, h = bh - b * H;
     const uint16_t *xb = x + (int64_t)b * sb + (int64_t)h * sh;
-    const int slots = tpr * kBlk;
-    for (int ci = threadIdx.x; ci < slots * CH; ci += 256) {
-        const int i = ci / CH, c8 = ci - i * CH;
-        const int n = slot_token<true>(g, a * tpr + i / kBlk, i % kBlk);
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (n >= 0)
-            v = *reinterpret_cast<const uint4 *>(xb + (int64_t)n * sn + c8 * 8);
-        *reinterpret_cast<uint4 *>(tile + i * D + c8 * 8) = v;
-    }
+    constexpr int slots = TPR * kBlk;
+    load_region<D, true, TPR>(xb, sn, a * TPR, g, tile);
     const int i0 = threadIdx.x;
-    const int na = __syncthreads_count(i0 < slots && slot_token<true>(g, a * tpr + i0 / kBlk, i0 % kBlk) >= 0);
+    const int na = __syncthreads_count(i0 < slots && slot_token<true>(g, a * TPR + i0 / kBlk, i0 % kBlk) >= 0);
     const int t = threadIdx.x;
     if (t < D) {
         double s = 0.0;
@@ -390,12 +397,12 @@ void launch_prep_qk(const da2_layout_s &L, const void *x, int is_key, char *ws, 
             DA2_PREP_QK(64, false);
     }
 #undef DA2_PREP_QK
-    if (L.tpr > 1) {
+    if (L.tpr > 1) {   // capacity 128: two tiles per region
         dim3 gp(L.Rg, L.BH);
         if (L.d == 128)
-            k_pool<128><<<gp, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.Rg, L.tpr, g, avg, mx);
+            k_pool<128, 2><<<gp, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.Rg, g, avg, mx);
         else
-            k_pool<64><<<gp, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.Rg, L.tpr, g, avg, mx);
+            k_pool<64, 2><<<gp, 256, 0, st>>>(xp, s.stride_b, s.stride_h, s.stride_n, s.heads, L.Rg, g, avg, mx);
     }
 }
 
