@@ -314,17 +314,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t *base,
 }
 
 // Copy UNITS kilobytes at byte offset off of a resource to LDS dst with
-// direct-to-LDS buffer loads; wave w of the two copies units w, w+2, ...
+// direct-to-LDS buffer loads; wave w of the NW copies units w, w+NW, ...
 // Each unit is one instruction: 64 lanes x 16 bytes landing at dst + 16 l.
-template <int UNITS>
+template <int UNITS, int NW>
 __device__ __forceinline__ void copy_kb(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint8_t *dst, int w,
                                         uint32_t loff16)
 {
 #pragma unroll
-    for (int j = 0; j < UNITS / 2; j++) {
-        const int u = 2 * j + w;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + u * 1024), 16, loff16,
-                                                 off + u * 1024, 0, 0);
+    for (int j = 0; j < (UNITS + NW - 1) / NW; j++) {
+        const int u = NW * j + w;
+        if (UNITS % NW == 0 || u < UNITS)   // fewer units than waves (d = 64, four waves)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + u * 1024), 16, loff16,
+                                                     off + u * 1024, 0, 0);
     }
 }
 
@@ -353,18 +354,18 @@ __device__ __forceinline__ Src head_sources(const AttnArgs &A, int64_t hbase, in
 
 // LDS images of the MXFP4 phase, in separate double-buffered key and value
 // streams (D = head dim): key [0, 32D) codes, [32D, 34D) E8M0; value the same.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void issue_k4(const Src &S, int kb, uint8_t *dst, int w, int l)
 {
-    copy_kb<kBlk * D / 2048>(S.k4, (uint32_t)kb * (kBlk * D / 2), dst, w, (uint32_t)l * 16u);
+    copy_kb<kBlk * D / 2048, NW>(S.k4, (uint32_t)kb * (kBlk * D / 2), dst, w, (uint32_t)l * 16u);
     if (w == 0 && l * 4 < 2 * D)
         copy_dword(S.k4s, (uint32_t)kb * (2 * D), dst + 32 * D, (uint32_t)l * 4u);
 }
 
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void issue_v4(const Src &S, int kb, uint8_t *dst, int w, int l)
 {
-    copy_kb<kBlk * D / 2048>(S.v4, (uint32_t)kb * (kBlk * D / 2), dst, w, (uint32_t)l * 16u);
+    copy_kb<kBlk * D / 2048, NW>(S.v4, (uint32_t)kb * (kBlk * D / 2), dst, w, (uint32_t)l * 16u);
     if (w == 1 && l * 4 < 2 * D)
         copy_dword(S.v4s, (uint32_t)kb * (2 * D), dst + 32 * D, (uint32_t)l * 4u);
 }
@@ -437,8 +438,9 @@ __device__ __forceinline__ uint8_t *chunk16(uint8_t *b0, uint8_t *b1, int c)
 // Key sources of the tiles that run on the bf16 matrix core.  A key source
 // says which tile the i-th step takes, copies that tile's key image (64 key
 // rows x D channels as bf16: chunk (m, s) holds for lane l key row
-// key_of_row(l % 32, m), channels 16 s + 8 (l / 32) .. + 7) into this wave's
-// half of the key buffers, and tells how many of its keys are valid.
+// key_of_row(l % 32, m), channels 16 s + 8 (l / 32) .. + 7; chunk (m, s) in
+// key buffer m) -- wave w of NW copying its share of the chunks -- and
+// tells how many of its keys are valid.
 // ---------------------------------------------------------------------------
 // Video regions of one head: the schedule's list, or (DENSE) the regions
 // first, first + 1, ... in order.  IMG: copy a prepared key image (the FP8
@@ -446,10 +448,12 @@ __device__ __forceinline__ uint8_t *chunk16(uint8_t *b0, uint8_t *b1, int c)
 // tier on the 8x8 grid) the rows are gathered straight from K at a fixed
 // byte offset per lane from the region's first token.  RAG: mask the
 // region's padding slots.
-template <int D, bool DENSE, bool IMG, bool RAG>
+template <int D, bool DENSE, bool IMG, bool RAG, int NW = 2>
 struct VideoKeys {
+    static_assert(IMG || NW == 2, "the gathered grid image is copied by two waves");
     static constexpr bool kMasked = RAG;
-    static constexpr int kCopies = D / 16;   // copies per wave and tile
+    static constexpr int kCopies = D / 8 / NW;   // copies per wave and tile
+    static constexpr int kWaves = NW;
     const int32_t *list;
     int first;
     const uint16_t *kh;            // K of this head
@@ -480,17 +484,19 @@ struct VideoKeys {
     }
     __device__ __forceinline__ int id(int i) const { return DENSE ? first + i : sload_i32(list + i); }
     __device__ __forceinline__ int valid(int kb) const { return RAG ? sload_i32(nreg + kb) : kBlk; }
-    __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
+    __device__ __forceinline__ void issue_key(int kb, uint8_t *kb0, uint8_t *kb1) const
     {
         if (IMG) {
-            // chunks (w, s) of the region's key image: 1 KB each
+            // chunks w kCopies .. of the region's key image: 1 KB each
             const __amdgpu_buffer_rsrc_t ksrc = head_rsrc(kimg, ibytes);
 #pragma unroll
-            for (int s = 0; s < D / 16; s++)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, koff,
-                                                         (uint32_t)kb * (kBlk * D * 2) + (w * (D / 16) + s) * 1024,
-                                                         0, 0);
+            for (int s = 0; s < kCopies; s++) {
+                const int ch = w * kCopies + s;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)chunk16<D>(kb0, kb1, ch), 16, koff,
+                                                         (uint32_t)kb * (kBlk * D * 2) + ch * 1024, 0, 0);
+            }
         } else {
+            uint8_t *dst = w ? kb1 : kb0;
             const int t0 = region_token(kb, 0, Ry, Rx, Hv, Wv);
             const __amdgpu_buffer_rsrc_t ksrc = head_rsrc((const uint8_t *)(kh + (int64_t)t0 * osn), kspan);
 #pragma unroll
@@ -506,15 +512,16 @@ struct VideoKeys {
 // tiles first, first + 1, ...  Rows past the valid ones are read from the
 // last valid row (their logits are masked, so only the address matters);
 // their value rows are zero in the value image.
-template <int D>
+template <int D, int NW = 2>
 struct PrefixKeys {
     static constexpr bool kMasked = true;
-    static constexpr int kCopies = D / 16;
+    static constexpr int kCopies = D / 8 / NW;   // copies per wave and tile: half m, chunks s0 ..
+    static constexpr int kWaves = NW;
     int first;
     __amdgpu_buffer_rsrc_t ksrc;   // prefix K rows of this head
     const uint8_t *vbase;          // prefix value images of this head
     int64_t vbytes;
-    int kpos, nv;
+    int kpos, nv, m, s0;
     uint32_t lane_off;             // channel offset of this lane, bytes
     int64_t osn;
 
@@ -522,7 +529,9 @@ struct PrefixKeys {
                                           int l)
         : first(first_), nv(nv_), osn(A.osn)
     {
-        kpos = key_of_row(l & 31, w);
+        m = w / (NW / 2);
+        s0 = (w % (NW / 2)) * kCopies;
+        kpos = key_of_row(l & 31, m);
         lane_off = (uint32_t)(16 * (l >> 5));
         ksrc = head_rsrc((const uint8_t *)(A.kp + hoff), A.pkspan);
         vbase = A.vp16 + (int64_t)bh * A.ptiles * (kBlk * D * 2);
@@ -530,24 +539,25 @@ struct PrefixKeys {
     }
     __device__ __forceinline__ int id(int i) const { return first + i; }
     __device__ __forceinline__ int valid(int kb) const { return nv - kBlk * kb; }
-    __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
+    __device__ __forceinline__ void issue_key(int kb, uint8_t *kb0, uint8_t *kb1) const
     {
         const int row = min(kBlk * kb + kpos, nv - 1);
         const uint32_t off = (uint32_t)(row * osn * 2) + lane_off;
+        uint8_t *dst = m ? kb1 : kb0;
 #pragma unroll
-        for (int s = 0; s < D / 16; s++)
+        for (int s = s0; s < s0 + kCopies; s++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void *)(dst + s * 1024), 16, off, 32 * s, 0, 0);
     }
 };
 
 // INT8 key tiles of the schedule's video regions of one head (the 8-bit
 // tier): the prepared operand of region kb, [m][kc][lane][32 B] (lane l: slot
-// key_of_row(l % 32, m), channels 64 kc + 32 (l / 32) .. + 31); wave w copies
-// half m = w into its key buffer.
-template <int D, bool RAG>
+// key_of_row(l % 32, m), channels 64 kc + 32 (l / 32) .. + 31), 1 KB chunks;
+// wave w of NW copies chunks w kCopies .. into the key buffer.
+template <int D, bool RAG, int NW = 2>
 struct Int8Keys {
     static constexpr bool kMasked = RAG;
-    static constexpr int kCopies = D / 32;
+    static constexpr int kCopies = D / 16 / NW;   // 1 KB chunks per wave and tile
     const int32_t *list;
     const int32_t *nreg;
     const uint8_t *vbase;          // bf16 values of the FP8 value codes of the head's regions
@@ -565,7 +575,6 @@ struct Int8Keys {
     }
     __device__ __forceinline__ int id(int i) const { return sload_i32(list + i); }
     __device__ __forceinline__ int valid(int kb) const { return RAG ? sload_i32(nreg + kb) : kBlk; }
-    // wave w copies half m = w of region kb's tile to dst + w * (half bytes)
     __device__ __forceinline__ void issue_key(int kb, uint8_t *dst) const
     {
 #pragma unroll
@@ -648,24 +657,23 @@ __device__ __forceinline__ void run_bf16(uint8_t *kb0, uint8_t *kb1, uint8_t *vb
 {
     constexpr int CB = D / 32;
     constexpr int NK = Keys::kCopies;              // key copies per wave and tile
+    constexpr int NW = Keys::kWaves;
     constexpr int VB = kBlk * D * 2;               // value image of a tile
     const int hf = l >> 5;
     const __amdgpu_buffer_rsrc_t vsrc = head_rsrc(K.vbase, K.vbytes);
     int kb = K.id(0);
     int kbn = n > 1 ? K.id(1) : 0;
-    K.issue_key(kb, w ? kb1 : kb0);
+    K.issue_key(kb, kb0, kb1);
     for (int i = 0; i < n; i++) {
         // key image of tile i complete (both waves' halves); both waves are
         // done with the value buffer
         __builtin_amdgcn_s_waitcnt(vm_wait(0));
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < VB / 2048; j++) {
-            // unit 2j + w lies in the first buffer exactly when j < D / 32
-            const int u = 2 * j + w;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vsrc, (lds_void *)((j < D / 32 ? vb0 : vb1) + (u % (D / 16)) * 1024), 16, (uint32_t)l * 16u,
-                (uint32_t)kb * VB + u * 1024, 0, 0);
+        for (int j = 0; j < VB / 1024 / NW; j++) {
+            const int u = NW * j + w;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrc, (lds_void *)chunk16<D>(vb0, vb1, u), 16, (uint32_t)l * 16u,
+                                                     (uint32_t)kb * VB + u * 1024, 0, 0);
         }
         const int nk = Keys::kMasked ? K.valid(kb) : kBlk;
         v16f sc[2];
@@ -684,7 +692,7 @@ __device__ __forceinline__ void run_bf16(uint8_t *kb0, uint8_t *kb1, uint8_t *vb
         __syncthreads();
         const bool more = i + 1 < n;
         if (more)
-            K.issue_key(kbn, w ? kb1 : kb0);
+            K.issue_key(kbn, kb0, kb1);
         if (Keys::kMasked)
             mask_keys(sc, nk, hf);
         float al;
@@ -749,7 +757,7 @@ struct Par {
 // pair (last read by step i-1), reads K(i+1) from kb0 and issues its logits,
 // then, once both waves are done reading kb0, copies K(i+2): every copy has
 // about a step to land.
-template <int D, bool RAG>
+template <int D, bool RAG, int NW>
 __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t *kb1, uint8_t *vb0, uint8_t *vb1,
                                        uint8_t *xb, const int32_t *lst, int n, const v4u (&q)[D / 16], float qs,
                                        int64_t hbase, int w, int l, v16f (&acc)[D / 32], Row &row)
@@ -757,7 +765,7 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
     constexpr int CB = D / 32;
     constexpr int VB = kBlk * D * 2;               // value image of a tile
     const int hf = l >> 5;
-    const Int8Keys<D, RAG> K(A, lst, hbase, w, l);
+    const Int8Keys<D, RAG, NW> K(A, lst, hbase, w, l);
     const __amdgpu_buffer_rsrc_t vsrc = head_rsrc(K.vbase, K.vbytes);
     v16f Sa[2], Sb[2];   // logits of tiles of alternating parity
     v4u P[4];            // bf16 weights of the previous tile, then of this one
@@ -767,12 +775,10 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
 
     auto issue_value = [&](int kbv, uint8_t *b0, uint8_t *b1) {
 #pragma unroll
-        for (int j = 0; j < VB / 2048; j++) {
-            // unit 2j + w lies in the first buffer exactly when j < D / 32
-            const int u = 2 * j + w;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vsrc, (lds_void *)((j < D / 32 ? b0 : b1) + (u % (D / 16)) * 1024), 16, (uint32_t)l * 16u,
-                (uint32_t)kbv * VB + u * 1024, 0, 0);
+        for (int j = 0; j < VB / 1024 / NW; j++) {
+            const int u = NW * j + w;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrc, (lds_void *)chunk16<D>(b0, b1, u), 16, (uint32_t)l * 16u,
+                                                     (uint32_t)kbv * VB + u * 1024, 0, 0);
         }
     };
     // integer logits S of the tile in kb0: exact sums (at most 127^2 D in
@@ -964,7 +970,7 @@ __device__ __forceinline__ void mask_padding(v16f &s1, int n, int hf)
 // One attention workgroup's state: two waves, one query region (wave w owns
 // queries 32 w .. 32 w + 31).  RAG: ragged layout (slot tables); PMAX: most
 // padding slots of a key region (0, 4 or 16).
-template <int D, bool RAG, int PMAX>
+template <int D, bool RAG, int PMAX, int NW>
 struct Attn {
     static constexpr int KC = D / 64;   // 64-channel steps of QK^T
     static constexpr int CB = D / 32;   // 32-channel blocks of the output
@@ -976,7 +982,7 @@ struct Attn {
     const int32_t *list;   // key regions of the MXFP4 tiles, ascending
     int64_t hbase;
     Src src;
-    int n, w, l, hf, bh;
+    int n, w, wq, l, hf, bh;   // w: this wave's share of the copies (of NW); wq: its 32 rows of the query tile
     int64_t qblk;
     float qs;
     v8i qv[KC];   // this wave's queries: MXFP4 codes (dwords 0-3) and exponent (dword 4)
@@ -1049,8 +1055,8 @@ struct Attn {
         __syncthreads();
         settle();
         if (i + 2 < n)
-            issue_k4<D>(src, kr2, kw, w, l);
-        issue_v4<D>(src, kr0, vw, w, l);
+            issue_k4<D, NW>(src, kr2, kw, w, l);
+        issue_v4<D, NW>(src, kr0, vw, w, l);
         VRegs<D> V;
         KRegs<D> K;
         // main block: weights of tile i on the vector unit, products of tiles
@@ -1133,7 +1139,7 @@ struct Attn {
     {
 #pragma unroll
         for (int kc = 0; kc < KC; kc++) {
-            const int chunk = (w * KC + kc) * 64 + l;
+            const int chunk = (wq * KC + kc) * 64 + l;
             const uint4 c = const_cast<const uint4 &>(
                 *reinterpret_cast<const volatile uint4 *>(A.q4 + qblk * (kBlk * D / 2) + chunk * 16));
             qv[kc][0] = c.x;
@@ -1155,16 +1161,16 @@ struct Attn {
         kr0 = sload_i32(list);
         kr1 = n > 1 ? sload_i32(list + 1) : 0;
         kr2 = n > 2 ? sload_i32(list + 2) : 0;
-        issue_k4<D>(src, kr0, kb0, w, l);
+        issue_k4<D, NW>(src, kr0, kb0, w, l);
         if (n > 1)
-            issue_k4<D>(src, kr1, kb1, w, l);
+            issue_k4<D, NW>(src, kr1, kb1, w, l);
         if (PMAX > 0)
             nk0 = sload_i32(A.nreg + kr0);
         // step 0 multiplies P = 0 into the value buffer of the other parity:
         // clear it so that no stale code can make a NaN
 #pragma unroll
-        for (int u = 0; u < kBlk * D / (128 * 16); u++)
-            *reinterpret_cast<v4u *>(vb1 + (u * 128 + threadIdx.x) * 16) = (v4u){};
+        for (int u = 0; u < kBlk * D / (NW * 64 * 16); u++)
+            *reinterpret_cast<v4u *>(vb1 + (u * NW * 64 + threadIdx.x) * 16) = (v4u){};
         P0 = (v8i){};
         P1 = (v8i){};
         E0 = 127;
@@ -1222,21 +1228,21 @@ struct Attn {
         const int64_t hoff = (int64_t)bb * A.osb + (int64_t)hh * A.osh;
         v4u q16[D / 16];
         if (np > 0 || n16 > 0) {
-            int qt = slot_token<RAG>(A.geo, a, 32 * w + (l & 31));
+            int qt = slot_token<RAG>(A.geo, a, 32 * wq + (l & 31));
             if (qt < 0)   // padding slot: any valid row (its output is not written)
                 qt = slot_token<RAG>(A.geo, a, 0);
             load_q16<D>(A.q + hoff + (int64_t)qt * A.osn, l, q16);
             if (np > 0)
-                run_bf16<D>(kb0, kb1, vb0, vb1, PrefixKeys<D>(A, 0, hoff, bh, nv, w, l), np, q16, scale_c4(A), w, l,
+                run_bf16<D>(kb0, kb1, vb0, vb1, PrefixKeys<D, NW>(A, 0, hoff, bh, nv, w, l), np, q16, scale_c4(A), w, l,
                             acc, row);
             if (n16 > 0)
-                run_bf16<D>(kb0, kb1, vb0, vb1, VideoKeys<D, false, RAG, RAG>(A, A.k16, list16, 0, hoff, hbase, w, l),
+                run_bf16<D>(kb0, kb1, vb0, vb1, VideoKeys<D, false, RAG, RAG, NW>(A, A.k16, list16, 0, hoff, hbase, w, l),
                             n16, q16, scale_c4(A), w, l, acc, row);
         }
         if (n8 > 0) {
             vunits(true);
-            load_q8<D>(A.q8 + qblk * (kBlk * D), w, l, q16);
-            run_i8<D, RAG>(A, kb0, kb1, vb0, vb1, xb, list8, n8, q16, qs, hbase, w, l, acc, row);
+            load_q8<D>(A.q8 + qblk * (kBlk * D), wq, l, q16);
+            run_i8<D, RAG, NW>(A, kb0, kb1, vb0, vb1, xb, list8, n8, q16, qs, hbase, w, l, acc, row);
             vunits(false);
         }
     }
@@ -1269,7 +1275,7 @@ struct Attn {
         }
         const float zt = pair_sum(row.z);
         const float inv = zt > 0.0f ? 1.0f / zt : 0.0f;
-        const int qi = 32 * w + (l & 31);
+        const int qi = 32 * wq + (l & 31);
         const int tok = slot_token<RAG>(A.geo, a, qi);
         const int b = bh / A.H, h = bh - b * A.H;
         const int64_t obase = (int64_t)b * A.osb + (int64_t)h * A.osh + (int64_t)tok * A.osn;
@@ -1280,6 +1286,7 @@ struct Attn {
     __device__ __forceinline__ void init(int w_, int bh_, int64_t qblk_)
     {
         w = w_;
+        wq = NW == 4 ? (w_ & 1) : w_;
         l = threadIdx.x & 63;
         hf = l >> 5;
         bh = bh_;
@@ -1297,9 +1304,12 @@ struct Attn {
 };
 
 // One query region per workgroup: 16-bit phase (text prefix, then 16-bit
-// tiles), 8-bit phase, MXFP4 phase, epilogue.
-template <int D, bool RAG, int PMAX>
-__global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
+// tiles), 8-bit phase, MXFP4 phase, epilogue.  NW = 2: a region of one tile,
+// two waves of 32 rows.  NW = 4 (block capacity 128): a region of two tiles
+// with the same key list, four waves; every copied key and value tile then
+// serves 128 query rows.
+template <int D, bool RAG, int PMAX, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void k_attn(const AttnArgs A)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t kb0[kBlk * D];
     __shared__ __attribute__((aligned(1024))) uint8_t kb1[kBlk * D];
@@ -1315,18 +1325,20 @@ __global__ __launch_bounds__(128, 2) void k_attn(const AttnArgs A)
     // shared last-level cache.  The plan's work order maps a slot to its
     // query region (k_qorder: the share's regions are frame-fastest, ranked
     // by kept tile count).
-    const int R = A.R;
-    const int span = (R + 7) / 8;
+    const int R = A.R;                           // tiles
+    const int QU = NW == 4 ? R / 2 : R;          // query regions
+    const int span = (QU + 7) / 8;
     const int xcd = (int)(blockIdx.x & 7), kk = (int)(blockIdx.x >> 3);
     const int bh = kk / span;
     const int j = xcd * span + (kk - bh * span);
-    if (j >= R)
+    if (j >= QU)
         return;
-    const int a = sload_i32(A.qord + (int64_t)bh * R + j);
+    const int au = sload_i32(A.qord + (int64_t)bh * QU + j);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int a = NW == 4 ? 2 * au + (w >> 1) : au;   // this wave's query tile
     const int64_t qblk = (int64_t)bh * R + a;
 
-    Attn<D, RAG, PMAX> S{A, kb0, kb1, vb0, vb1, xb};
+    Attn<D, RAG, PMAX, NW> S{A, kb0, kb1, vb0, vb1, xb};
     S.init(w, bh, qblk);
     const int n16 = sload_i32(A.cnt + qblk * kTargets);
     const int n8 = sload_i32(A.cnt + qblk * kTargets + 1);
@@ -1368,7 +1380,7 @@ __device__ __forceinline__ void prefix_rows(const AttnArgs &A, uint8_t *kb0, uin
     const int np = (nv + kBlk - 1) / kBlk;
     const int t0 = c * kPrefixChunkTiles, t1 = min(t0 + kPrefixChunkTiles, np + A.R);
     if (t0 < np)
-        run_bf16<D>(kb0, kb1, vb0, vb1, PrefixKeys<D>(A, t0, hoff, bh, nv, w, l), min(t1, np) - t0, q16,
+        run_bf16<D>(kb0, kb1, vb0, vb1, PrefixKeys<D, 2>(A, t0, hoff, bh, nv, w, l), min(t1, np) - t0, q16,
                     scale_c4(A), w, l, acc, st);
     const int r0 = max(t0, np) - np, r1 = t1 - np;
     if (r1 > r0)
@@ -1617,20 +1629,30 @@ void launch_attention(const da2_layout_s &L, char *ws, const void *q, const void
                                               L.R, (const float *)(ws + W.vavg), (float2 *)(ws + W.magg),
                                               (float *)(ws + W.cagg));
     }
-    dim3 grid(8 * ((L.R + 7) / 8) * L.BH);
+    // one workgroup per query region: one tile and two waves, or (capacity
+    // 128) two tiles and four waves
+    const int QU = L.tpr == 2 ? L.Rg : L.R;
+    dim3 grid(8 * ((QU + 7) / 8) * L.BH);
     // kernel variant: the 8x8 grid, or a ragged layout whose key regions
     // have no padding, at most 4 or at most 16 padding slots
     const int pm = !L.ragged ? -1 : (L.pmax == 0 ? 0 : (L.pmax <= 4 ? 4 : 16));
 #define DA2_ATTN(DD)                                                    \
     do {                                                                \
-        if (pm < 0)                                                     \
-            k_attn<DD, false, 0><<<grid, 128, 0, st>>>(A);              \
+        if (L.tpr == 2) {                                               \
+            if (pm == 0)                                                \
+                k_attn<DD, true, 0, 4><<<grid, 256, 0, st>>>(A);        \
+            else if (pm == 4)                                           \
+                k_attn<DD, true, 4, 4><<<grid, 256, 0, st>>>(A);        \
+            else                                                        \
+                k_attn<DD, true, 16, 4><<<grid, 256, 0, st>>>(A);       \
+        } else if (pm < 0)                                              \
+            k_attn<DD, false, 0, 2><<<grid, 128, 0, st>>>(A);           \
         else if (pm == 0)                                               \
-            k_attn<DD, true, 0><<<grid, 128, 0, st>>>(A);               \
+            k_attn<DD, true, 0, 2><<<grid, 128, 0, st>>>(A);            \
         else if (pm == 4)                                               \
-            k_attn<DD, true, 4><<<grid, 128, 0, st>>>(A);               \
+            k_attn<DD, true, 4, 2><<<grid, 128, 0, st>>>(A);            \
         else                                                            \
-            k_attn<DD, true, 16><<<grid, 128, 0, st>>>(A);              \
+            k_attn<DD, true, 16, 2><<<grid, 128, 0, st>>>(A);           \
     } while (0)
     if (ev)
         hipEventRecord(ev[0], st);

@@ -786,10 +786,12 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
 // an XCD runs together then walk ascending key lists of similar length from
 // about the same time, so more of their tile reads hit its L2; the longest
 // workgroups of the last head also start first.  One workgroup per (share,
-// head); a share holds at most ceil(kMaxRegions / 8) regions.
+// head); a share holds at most ceil(kMaxRegions / 8) regions.  The unit is a
+// query region of tpr tiles (its first tile's counts; every tile of a
+// region has the same list); qord holds R units per head.
 constexpr int kMaxShare = (kMaxRegions + 7) / 8;
 
-__global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt, int R, int RF,
+__global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt, int R, int RF, int tpr,
                                                 int32_t *__restrict__ qord)
 {
     __shared__ int32_t len[kMaxShare];
@@ -798,7 +800,7 @@ __global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt,
     const int64_t row0 = (int64_t)bh * R;
     for (int i = threadIdx.x; i < n; i += 256) {
         const int j = j0 + i, a = (j % NF) * RF + j / NF;
-        const int32_t *c = cnt + (row0 + a) * kTargets;
+        const int32_t *c = cnt + ((row0 + a) * tpr) * kTargets;
         len[i] = c[0] + c[1] + c[2];
     }
     __syncthreads();
@@ -906,8 +908,14 @@ void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
     const Workspace &W = L.ws;
     k_schedule<<<dim3(L.R, L.BH), 64, 0, st>>>((const uint8_t *)(ws + W.tier), L.Rg, L.tpr,
                                                 (int32_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
-    k_qorder<<<dim3(8, L.BH), 256, 0, st>>>((const int32_t *)(ws + W.cnt), L.R, L.Rf,
-                                            (int32_t *)(ws + W.qord));
+    // work order over query regions: tiles at capacity 64, pairs of tiles
+    // (one four-wave workgroup each) at capacity 128
+    if (L.tpr == 2)
+        k_qorder<<<dim3(8, L.BH), 256, 0, st>>>((const int32_t *)(ws + W.cnt), L.Rg, L.Rfg, 2,
+                                                (int32_t *)(ws + W.qord));
+    else
+        k_qorder<<<dim3(8, L.BH), 256, 0, st>>>((const int32_t *)(ws + W.cnt), L.R, L.Rf, 1,
+                                                (int32_t *)(ws + W.qord));
 }
 
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st)
