@@ -769,7 +769,7 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
     const __amdgpu_buffer_rsrc_t vsrc = head_rsrc(K.vbase, K.vbytes);
     v16f Sa[2], Sb[2];   // logits of tiles of alternating parity
     v4u P[4];            // bf16 weights of the previous tile, then of this one
-    float al = 1.0f;
+    float R, al = 1.0f;
     int kr0 = sload_i32(lst), kr1 = n > 1 ? sload_i32(lst + 1) : 0, kr2 = n > 2 ? sload_i32(lst + 2) : 0;
     int nk0 = RAG ? sload_i32(A.nreg + kr0) : kBlk;
 
@@ -781,12 +781,13 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
                                                      (uint32_t)kbv * VB + u * 1024, 0, 0);
         }
     };
-    // integer logits S of the tile in kb0: exact sums (at most 127^2 D in
-    // size), exact in the fp32 they are converted to, so the accumulators
-    // start at zero and the row maximum enters only through the bias of
-    // t = fma(S, ch, b)
-    auto logits = [&](v16f (&sn)[2]) {
+    // integer logits of the tile in kb0, accumulators starting at -Ri
+    auto logits = [&](int Ri, v16f (&sn)[2]) {
         v16i s[2];
+        v16i neg;
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            neg[j] = -Ri;
 #pragma unroll
         for (int e = 0; e < D / 32; e++) {
             v4i k[2];
@@ -795,14 +796,18 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
                 k[mm] = __builtin_bit_cast(v4i, lds_v4u(kb0 + mm * 32 * D + ((e >> 1) * 64 + l) * 32 + 16 * (e & 1)));
 #pragma unroll
             for (int mm = 0; mm < 2; mm++)
-                s[mm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k[mm], __builtin_bit_cast(v4i, q[e]),
-                                                             e ? s[mm] : (v16i){}, 0, 0, 0);
+                s[mm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(k[mm], __builtin_bit_cast(v4i, q[e]), e ? s[mm] : neg, 0,
+                                                             0, 0);
         }
 #pragma unroll
         for (int mm = 0; mm < 2; mm++)
 #pragma unroll
             for (int r = 0; r < 16; r++)
                 sn[mm][r] = (float)s[mm][r];
+    };
+    // R' = M / c rounded to an integer within the exact range of the sums
+    auto offset = [&](const Scale &c) {
+        return __builtin_rintf(fminf(fmaxf(row_offset(row, c), -0x1p22f), 0x1p22f));
     };
     // P^T V of the previous tile (weights P) from the pair (v0, v1)
     auto pv = [&](uint8_t *v0, uint8_t *v1) {
@@ -824,8 +829,8 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
                 acc[cb] *= al;
         }
     };
-    // step i of parity PAR: sc the logits of tile i, P the weights of tile
-    // i-1, al the factor acc owes before their product
+    // step i of parity PAR: sc the logits of tile i (offset R), P the
+    // weights of tile i-1, al the factor acc owes before their product
     auto step = [&](auto par, int i, v16f (&sc)[2], v16f (&sn)[2]) {
         constexpr int PAR = decltype(par)::value;
         uint8_t *vw0 = PAR ? kb1 : vb0, *vw1 = PAR ? xb : vb1;   // pair of tile i
@@ -841,9 +846,12 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
         const Scale c = scale_fp8(qs, sload_f32(A.ks8 + hbase + kr0), A);
         bool raised;
         float al_i;
-        const float bias = tile_update(row, c, 0.0f, pair_max(lane_max(sc)), al_i, raised);
-        if (i + 1 < n)
-            logits(sn);
+        const float bias = tile_update(row, c, R, pair_max(lane_max(sc)), al_i, raised);
+        float Rn = 0.0f;
+        if (i + 1 < n) {
+            Rn = offset(scale_fp8(qs, sload_f32(A.ks8 + hbase + kr1), A));
+            logits((int)Rn, sn);
+        }
         // both waves are done reading kb0: refill it with tile i+2
         __syncthreads();
         if (i + 2 < n)
@@ -869,6 +877,7 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
         }
         row.z += z;
         al = al_i;
+        R = Rn;
         kr0 = kr1;
         kr1 = kr2;
         kr2 = sload_i32(lst + min(i + 3, n - 1));
@@ -876,11 +885,19 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
             nk0 = sload_i32(A.nreg + kr0);
     };
 
-    // prologue: the logits of tile 0
+    // prologue: the logits of tile 0 (a fresh row first finds its offset)
     K.issue_key(kr0, kb0);
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
     __syncthreads();
-    logits(Sa);
+    if (__builtin_amdgcn_readfirstlane(row.mh == -__builtin_huge_valf() ? 1 : 0)) {
+        logits(0, Sa);
+        if (RAG)
+            mask_keys(Sa, nk0, hf);
+        R = pair_max(lane_max(Sa));
+    } else {
+        R = offset(scale_fp8(qs, sload_f32(A.ks8 + hbase + kr0), A));
+    }
+    logits((int)R, Sa);
     __syncthreads();
     if (n > 1)
         K.issue_key(kr1, kb0);
