@@ -830,9 +830,11 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
         }
     };
     // step i of parity PAR: sc the logits of tile i (offset R), P the
-    // weights of tile i-1, al the factor acc owes before their product
-    auto step = [&](auto par, int i, v16f (&sc)[2], v16f (&sn)[2]) {
+    // weights of tile i-1, al the factor acc owes before their product.
+    // FIRST: step 0, with no earlier tile to multiply.
+    auto step = [&](auto par, auto first, int i, v16f (&sc)[2], v16f (&sn)[2]) {
         constexpr int PAR = decltype(par)::value;
+        constexpr bool FIRST = decltype(first)::value != 0;
         uint8_t *vw0 = PAR ? kb1 : vb0, *vw1 = PAR ? xb : vb1;   // pair of tile i
         uint8_t *vr0 = PAR ? vb0 : kb1, *vr1 = PAR ? vb1 : xb;   // pair of tile i-1
         // K(i+1) and V(i-1) complete; both waves are done with step i-1
@@ -842,39 +844,70 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
         issue_value(kr0, vw0, vw1);
         if (RAG)
             mask_keys(sc, nk0, hf);
-        // running max of tile i; the offset and logits of tile i+1
+        // running max of tile i; the offset and logits of tile i+1 (on the
+        // last step from a stale key image: computed, never used)
         const Scale c = scale_fp8(qs, sload_f32(A.ks8 + hbase + kr0), A);
         bool raised;
         float al_i;
         const float bias = tile_update(row, c, R, pair_max(lane_max(sc)), al_i, raised);
-        float Rn = 0.0f;
-        if (i + 1 < n) {
-            Rn = offset(scale_fp8(qs, sload_f32(A.ks8 + hbase + kr1), A));
-            logits((int)Rn, sn);
-        }
+        const float Rn = offset(scale_fp8(qs, sload_f32(A.ks8 + hbase + kr1), A));
+        logits((int)Rn, sn);
         // both waves are done reading kb0: refill it with tile i+2
         __syncthreads();
         if (i + 2 < n)
             K.issue_key(kr2, kb0);
-        // P^T V of tile i-1 on the matrix core, then the weights of tile i
-        if (i > 0)
-            pv(vr0, vr1);
+        // main block, one region per quarter of the tile's 32 logits per
+        // lane: the unquantized weights 2^t in place of the logits, and a
+        // quarter of P^T V of tile i-1 (its value operands read at the top of
+        // the region, its products spread through the exponentials)
         float z = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             const int mm = t >> 1, r0 = 8 * (t & 1);
-            float e[8];
+            v4u vv[CB];
+            if (!FIRST) {
+#pragma unroll
+                for (int j = 0; j < CB; j++) {
+                    const int m = t * CB + j;   // product (block m / 4, key chunk m % 4)
+                    vv[j] = lds_v4u(chunk16<D>(vr0, vr1, m) + l * 16);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 8; j++)
-                e[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + j], c.ch, bias));
-            z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-            const uint32_t w0 = (uint32_t)pk_fp8_256(e[0], e[1], e[2], e[3]);
-            const uint32_t w1 = (uint32_t)pk_fp8_256(e[4], e[5], e[6], e[7]);
+                sc[mm][r0 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mm][r0 + j], c.ch, bias));
+            z += ((sc[mm][r0] + sc[mm][r0 + 1]) + (sc[mm][r0 + 2] + sc[mm][r0 + 3])) +
+                 ((sc[mm][r0 + 4] + sc[mm][r0 + 5]) + (sc[mm][r0 + 6] + sc[mm][r0 + 7]));
+            if (!FIRST) {
+#pragma unroll
+                for (int j = 0; j < CB; j++) {
+                    const int m = t * CB + j;
+                    acc[m / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv[j]), as_bf16x8(P[m % 4]),
+                                                                        acc[m / 4], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, CB, 0);   // value reads
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+                for (int j = 0; j < CB; j++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 16 / CB, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the weight codes of tile i (bf16 images of e4m3(256 w))
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const int mm = t >> 1, r0 = 8 * (t & 1);
+            const uint32_t w0 = (uint32_t)pk_fp8_256(sc[mm][r0], sc[mm][r0 + 1], sc[mm][r0 + 2], sc[mm][r0 + 3]);
+            const uint32_t w1 = (uint32_t)pk_fp8_256(sc[mm][r0 + 4], sc[mm][r0 + 5], sc[mm][r0 + 6], sc[mm][r0 + 7]);
             P[t][0] = fp8_pair_bf16(w0, 0);
             P[t][1] = fp8_pair_bf16(w0, 1);
             P[t][2] = fp8_pair_bf16(w1, 0);
             P[t][3] = fp8_pair_bf16(w1, 1);
         }
+        // keep the weights in this block: sunk past the next step's barrier
+        // they would leave the products above nothing to overlap with
+        asm volatile("" ::"v"(z), "v"(P[0]), "v"(P[1]), "v"(P[2]), "v"(P[3]));
         row.z += z;
         al = al_i;
         R = Rn;
@@ -901,13 +934,14 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
     __syncthreads();
     if (n > 1)
         K.issue_key(kr1, kb0);
-    int i = 0;
+    step(Par<0>{}, Par<1>{}, 0, Sa, Sb);
+    int i = 1;
     for (; i + 1 < n; i += 2) {
-        step(Par<0>{}, i, Sa, Sb);
-        step(Par<1>{}, i + 1, Sb, Sa);
+        step(Par<1>{}, Par<0>{}, i, Sb, Sa);
+        step(Par<0>{}, Par<0>{}, i + 1, Sa, Sb);
     }
     if (i < n)
-        step(Par<0>{}, i, Sa, Sb);
+        step(Par<1>{}, Par<0>{}, i, Sb, Sa);
     // drain: P^T V of the last tile
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
     __syncthreads();
