@@ -55,8 +55,8 @@ def parse():
     ap.add_argument("--workload", default="wan14b-720p")
     ap.add_argument("--budget", type=int, default=0, help="index into the workload's budget list")
     ap.add_argument("--full-bp", type=int, default=0, help="16-bit share (basis points)")
-    ap.add_argument("--hi-bp", type=int, default=None, help="FP8 share, overriding --budget")
-    ap.add_argument("--lo-bp", type=int, default=None, help="MXFP4 share, overriding --budget")
+    ap.add_argument("--hi-bp", type=int, default=None, help="8-bit share (INT8 Q K^T, FP8 weights and values; basis points), overriding --budget")
+    ap.add_argument("--lo-bp", type=int, default=None, help="MXFP4 share (basis points), overriding --budget")
     ap.add_argument("--prefix", type=int, default=0, help="text-prefix tokens (joint attention)")
     ap.add_argument("--prefix-valid", type=int, default=None,
                     help="valid prefix keys per sequence (default: all)")
