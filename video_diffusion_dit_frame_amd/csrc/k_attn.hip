@@ -856,10 +856,13 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
         __syncthreads();
         if (i + 2 < n)
             K.issue_key(kr2, kb0);
-        // main block, one region per quarter of the tile's 32 logits per
-        // lane: the unquantized weights 2^t in place of the logits, and a
-        // quarter of P^T V of tile i-1 (its value operands read at the top of
-        // the region, its products spread through the exponentials)
+        // main block, one region per quarter t of the tile's 32 logits per
+        // lane: the products of key chunk t of P^T V of tile i-1 (weights
+        // P[t], value operands read at the top of the region) spread through
+        // the quarter's unquantized weights 2^t (in place of its logits);
+        // then the quarter's weight codes (bf16 images of e4m3(256 w)) go
+        // into P[t], whose old value the products have read.  Every output
+        // block still adds its key chunks in the order 0, 1, 2, 3.
         float z = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
@@ -867,10 +870,8 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
             v4u vv[CB];
             if (!FIRST) {
 #pragma unroll
-                for (int j = 0; j < CB; j++) {
-                    const int m = t * CB + j;   // product (block m / 4, key chunk m % 4)
-                    vv[j] = lds_v4u(chunk16<D>(vr0, vr1, m) + l * 16);
-                }
+                for (int cb = 0; cb < CB; cb++)
+                    vv[cb] = lds_v4u(chunk16<D>(vr0, vr1, cb * 4 + t) + l * 16);
             }
 #pragma unroll
             for (int j = 0; j < 8; j++)
@@ -879,31 +880,26 @@ __device__ __forceinline__ void run_i8(const AttnArgs &A, uint8_t *kb0, uint8_t 
                  ((sc[mm][r0 + 4] + sc[mm][r0 + 5]) + (sc[mm][r0 + 6] + sc[mm][r0 + 7]));
             if (!FIRST) {
 #pragma unroll
-                for (int j = 0; j < CB; j++) {
-                    const int m = t * CB + j;
-                    acc[m / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv[j]), as_bf16x8(P[m % 4]),
-                                                                        acc[m / 4], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, CB, 0);   // value reads
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-#pragma unroll
-                for (int j = 0; j < CB; j++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 16 / CB, 0);
-                }
+                for (int cb = 0; cb < CB; cb++)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv[cb]), as_bf16x8(P[t]), acc[cb],
+                                                                     0, 0, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // the weight codes of tile i (bf16 images of e4m3(256 w))
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const int mm = t >> 1, r0 = 8 * (t & 1);
             const uint32_t w0 = (uint32_t)pk_fp8_256(sc[mm][r0], sc[mm][r0 + 1], sc[mm][r0 + 2], sc[mm][r0 + 3]);
             const uint32_t w1 = (uint32_t)pk_fp8_256(sc[mm][r0 + 4], sc[mm][r0 + 5], sc[mm][r0 + 6], sc[mm][r0 + 7]);
             P[t][0] = fp8_pair_bf16(w0, 0);
             P[t][1] = fp8_pair_bf16(w0, 1);
             P[t][2] = fp8_pair_bf16(w1, 0);
             P[t][3] = fp8_pair_bf16(w1, 1);
+            if (!FIRST) {
+                __builtin_amdgcn_sched_group_barrier(0x100, CB, 0);   // value reads
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+                for (int j = 0; j < CB; j++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 24 / CB, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // keep the weights in this block: sunk past the next step's barrier
         // they would leave the products above nothing to overlap with
