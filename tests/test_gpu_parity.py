@@ -125,6 +125,10 @@ def _tier_families(B, H, R, seed):
     s[:, :, :, R // 2] = 8       # a single FP8 tile per row
     s[:, :, 1::2, R // 2] = 4    # or a single MXFP4 tile
     fam["single_tile"] = s
+    f = np.zeros((B, H, R, R), np.uint8)
+    for a in range(R):           # 1, 2, 3 or 4 FP8 tiles per row: both step parities, each loop exit
+        f[:, :, a, (a + np.arange(a % 4 + 1) * 5) % R] = 8
+    fam["few8"] = f
     return fam
 
 
