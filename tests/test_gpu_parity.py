@@ -100,6 +100,43 @@ def test_row_scope_tier_map():
     assert ((tier == 8).sum(axis=3) == T8).all() and ((tier == 4).sum(axis=3) == Tk - T8).all()
 
 
+@pytest.mark.parametrize("zero", ["all", "half_q"])
+@pytest.mark.parametrize("hi,lo", [(1000, 3000), (3000, 3000), (5000, 4500)])
+def test_tied_keys_rank_by_pair_index(zero, hi, lo):
+    """Equal ranking keys across rows and rank chunks: with zero Q and K every
+    draft row is uniform, so all keys of a head are equal and the tiers follow
+    the pair index alone (App. C.1 ranking with the index tie-break); with the
+    queries of every other region zero, half the rows tie at 1/R among keys
+    of the other rows.  96 regions: 9216 keys per head over three chunks of
+    4096, the last one partial.  Tier maps, schedules and attention against
+    the oracle."""
+    B, H, F, Hv, Wv, d = 1, 2, 2, 64, 48, 64
+    q, k, v = G.inputs(B, H, F, Hv, Wv, d, 404 + hi, False)
+    perm = O.layout(F, Hv, Wv)
+    if zero == "all":
+        q[:] = 0
+        k[:] = 0
+    else:
+        R = F * (Hv // 8) * (Wv // 8)
+        for a in range(0, R, 2):
+            q[:, :, perm[a * 64:(a + 1) * 64]] = 0
+    P, qd, kd = G.run_plan(q, k, F, Hv, Wv, hi, lo)
+    ref = O.plan(q, k, F, Hv, Wv, hi, lo)
+    tier = P.tier_map().cpu().numpy()
+    assert np.array_equal(tier, ref["tier"])
+    if zero == "all":
+        R = tier.shape[-1]
+        T8, Tk = O.quotas(R * R, hi, lo)
+        idx = np.arange(R * R).reshape(R, R)
+        want = np.where(idx < T8, 8, np.where(idx < Tk, 4, 0))
+        assert (tier == want).all()
+    sch = G.host(P.debug("SCHEDULE"), np.int32).reshape(tier.shape[:3] + (-1,))
+    assert np.array_equal(sch, G.schedule_from_tier(ref["tier"]))
+    o = G.run_attention(P, qd, kd, v).cpu().numpy()
+    oref, amb = O.attention(q, k, v, tier, F, Hv, Wv, amb=True)
+    G.check_close(o, oref, "tied keys %s (%d,%d)" % (zero, hi, lo), amb=amb)
+
+
 @pytest.mark.parametrize("lam", [0.0, 1.0])
 def test_lambda_extremes_bit_exact(lam):
     c = _case(TINY)

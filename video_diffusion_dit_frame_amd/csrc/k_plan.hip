@@ -478,6 +478,49 @@ __global__ __launch_bounds__(256) void k_rank_eqcount(const uint32_t *__restrict
         eq[((int64_t)seg * nchunk + blockIdx.x) * kTargets + t] = r[t][0] + r[t][1] + r[t][2] + r[t][3];
 }
 
+// Exclusive prefix of the equal-key counts over the chunks of each segment,
+// in place: eq[seg][c][tg] becomes the number of keys equal to threshold tg
+// in chunks 0 .. c-1.  One workgroup per segment walks its chunks 256 at a
+// time with a carried total.
+__global__ __launch_bounds__(256) void k_rank_eqscan(uint32_t *__restrict__ eq, int64_t nchunk)
+{
+    __shared__ uint32_t wsum[kTargets][4];
+    const int seg = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    uint32_t carry[kTargets] = {};
+    for (int64_t c0 = 0; c0 < nchunk; c0 += 256) {
+        const int64_t c = c0 + t;
+        uint32_t *e = eq + ((int64_t)seg * nchunk + c) * kTargets;
+        uint32_t v[kTargets], x[kTargets];
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++) {
+            v[tg] = c < nchunk ? e[tg] : 0u;
+            x[tg] = v[tg];
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+            for (int tg = 0; tg < kTargets; tg++) {
+                const uint32_t y = __shfl_up(x[tg], o, 64);
+                x[tg] += lane >= o ? y : 0u;
+            }
+        if (lane == 63)
+#pragma unroll
+            for (int tg = 0; tg < kTargets; tg++)
+                wsum[tg][wv] = x[tg];
+        __syncthreads();
+#pragma unroll
+        for (int tg = 0; tg < kTargets; tg++) {
+            uint32_t off = carry[tg];
+            for (int w = 0; w < wv; w++)
+                off += wsum[tg][w];
+            if (c < nchunk)
+                e[tg] = off + x[tg] - v[tg];
+            carry[tg] += wsum[tg][0] + wsum[tg][1] + wsum[tg][2] + wsum[tg][3];
+        }
+        __syncthreads();
+    }
+}
+
 // Tier of a key from its membership in the cumulative top sets.
 __device__ __forceinline__ uint8_t tier_of(const bool (&in)[kTargets])
 {
@@ -485,118 +528,74 @@ __device__ __forceinline__ uint8_t tier_of(const bool (&in)[kTargets])
 }
 
 // Final tier per key: above a threshold, or equal to it and among the first
-// `rank + 1` equal keys by pair index.
+// `rank + 1` equal keys by pair index.  Thread t of the chunk's workgroup
+// takes keys c0 + 256 j + t (coalesced); in pair-index order the chunk's
+// keys run j-major, then wave, then lane.  The equal keys before a key are
+// those of earlier chunks (eq, already an exclusive prefix over chunks), of
+// earlier rows j, of earlier waves in row j and of lower lanes in its own
+// wave (a ballot): per target one ballot and one popcount per row j and
+// wave, exchanged once through LDS.
 __global__ __launch_bounds__(256) void k_rank_tier(const uint32_t *__restrict__ keys,
                                                    int64_t seglen, int64_t nchunk,
                                                    const RankState *__restrict__ st,
                                                    const uint32_t *__restrict__ eq,
                                                    uint8_t *__restrict__ tier)
 {
+    constexpr int J = kChunk / 256;
     __shared__ uint32_t base[kTargets];
-    __shared__ uint32_t wsum[kTargets][4];
-    __shared__ uint32_t kl[kChunk];  // the chunk's keys, staged by coalesced reads
-    __shared__ uint8_t tl[kChunk];   // their tiers, written back by coalesced stores
-    const int seg = blockIdx.y, t = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) uint32_t wcnt[kTargets][J][4];   // equal keys per (row j, wave)
+    const int seg = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t ch = blockIdx.x;
     RankState s[kTargets];
 #pragma unroll
     for (int tg = 0; tg < kTargets; tg++)
         s[tg] = st[seg * kTargets + tg];
-    // equal keys in earlier chunks of this segment
-    if (t < 64) {
-        uint32_t p[kTargets];
-#pragma unroll
-        for (int tg = 0; tg < kTargets; tg++)
-            p[tg] = 0;
-        for (int64_t c = t; c < ch; c += 64)
-#pragma unroll
-            for (int tg = 0; tg < kTargets; tg++)
-                p[tg] += eq[((int64_t)seg * nchunk + c) * kTargets + tg];
-#pragma unroll
-        for (int tg = 0; tg < kTargets; tg++) {
-            p[tg] = wave_sum_u32(p[tg]);
-            if (t == 0)
-                base[tg] = p[tg];
-        }
-    }
     const int64_t c0 = ch * kChunk;
     const uint32_t *kp = keys + (int64_t)seg * seglen;
+    uint32_t kv[J];
 #pragma unroll
-    for (int j = 0; j < kChunk / 256; j++) {
+    for (int j = 0; j < J; j++) {
         const int64_t i = c0 + j * 256 + t;
-        kl[j * 256 + t] = i < seglen ? kp[i] : 0u;
+        kv[j] = i < seglen ? kp[i] : 0u;
     }
-    __syncthreads();
-    // this thread owns 16 consecutive keys
-    const int64_t i0 = c0 + (int64_t)t * 16;
-    uint32_t kv[16];
-    uint32_t e[kTargets];
+    // equal keys in earlier chunks of this segment
+    if (t < kTargets)
+        base[t] = eq[((int64_t)seg * nchunk + ch) * kTargets + t];
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-    for (int tg = 0; tg < kTargets; tg++)
-        e[tg] = 0;
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-        int64_t i = i0 + j;
-        kv[j] = kl[t * 16 + j];
-#pragma unroll
-        for (int tg = 0; tg < kTargets; tg++)
-            e[tg] += (i < seglen && s[tg].active && kv[j] == s[tg].prefix);
-    }
-    // exclusive scan of the equal-key counts over the threads: inside each
-    // wave by lane shuffles, then across the four waves through LDS
-    const int lane = t & 63, wv = t >> 6;
-    uint32_t x[kTargets];
-#pragma unroll
-    for (int tg = 0; tg < kTargets; tg++)
-        x[tg] = e[tg];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1)
+    for (int j = 0; j < J; j++) {
+        const bool valid = c0 + j * 256 + t < seglen;
 #pragma unroll
         for (int tg = 0; tg < kTargets; tg++) {
-            const uint32_t y = __shfl_up(x[tg], o, 64);
-            x[tg] += lane >= o ? y : 0u;
+            const uint64_t m = __ballot(valid && s[tg].active && kv[j] == s[tg].prefix);
+            if (lane == 0)
+                wcnt[tg][j][wv] = (uint32_t)__popcll(m);
         }
-    if (lane == 63)
-#pragma unroll
-        for (int tg = 0; tg < kTargets; tg++)
-            wsum[tg][wv] = x[tg];
+    }
     __syncthreads();
     uint32_t r[kTargets];
 #pragma unroll
-    for (int tg = 0; tg < kTargets; tg++) {
-        uint32_t off = 0;
-        for (int w = 0; w < wv; w++)
-            off += wsum[tg][w];
-        r[tg] = base[tg] + off + x[tg] - e[tg];
-    }
+    for (int tg = 0; tg < kTargets; tg++)
+        r[tg] = base[tg];
     uint8_t *tp = tier + (int64_t)seg * seglen;
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-        int64_t i = i0 + j;
-        if (i >= seglen)
-            break;
-        uint32_t k = kv[j];
+    for (int j = 0; j < J; j++) {
+        const int64_t i = c0 + j * 256 + t;
+        const bool valid = i < seglen;
+        const uint32_t k = kv[j];
         bool in[kTargets];
 #pragma unroll
         for (int tg = 0; tg < kTargets; tg++) {
-            in[tg] = false;
-            if (s[tg].active) {
-                if (k > s[tg].prefix)
-                    in[tg] = true;
-                else if (k == s[tg].prefix) {
-                    in[tg] = r[tg] <= s[tg].rank;
-                    r[tg]++;
-                }
-            }
+            const uint4 wc = *reinterpret_cast<const uint4 *>(&wcnt[tg][j][0]);
+            const uint32_t before = (wv > 0 ? wc.x : 0u) + (wv > 1 ? wc.y : 0u) + (wv > 2 ? wc.z : 0u);
+            const bool e = valid && s[tg].active && k == s[tg].prefix;
+            const uint64_t m = __ballot(e);
+            const uint32_t rank = r[tg] + before + (uint32_t)__popcll(m & lt);
+            in[tg] = s[tg].active && (k > s[tg].prefix || (e && rank <= s[tg].rank));
+            r[tg] += wc.x + wc.y + wc.z + wc.w;
         }
-        tl[t * 16 + j] = tier_of(in);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kChunk / 256; j++) {
-        const int64_t i = c0 + j * 256 + t;
-        if (i < seglen)
-            tp[i] = tl[j * 256 + t];
+        if (valid)
+            tp[i] = tier_of(in);
     }
 }
 
@@ -720,7 +719,7 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
                                                  int32_t *__restrict__ sched,
                                                  int32_t *__restrict__ cnt)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t rowl[kMaxRegions];
+    extern __shared__ __attribute__((aligned(16))) uint8_t rowl[];   // R bytes, rounded up to 16
     const int T = R * tpr;                                  // tiles per head
     const int64_t row = (int64_t)blockIdx.y * T + blockIdx.x;
     const int l = threadIdx.x;
@@ -900,13 +899,14 @@ void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int
         k_rank_select<<<L.BH, 256, 0, st>>>(rs, hist, shift);
     }
     k_rank_eqcount<<<g, 256, 0, st>>>(keys, seglen, nchunk, rs, eq);
+    k_rank_eqscan<<<L.BH, 256, 0, st>>>(eq, nchunk);
     k_rank_tier<<<g, 256, 0, st>>>(keys, seglen, nchunk, rs, eq, tier);
 }
 
 void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
 {
     const Workspace &W = L.ws;
-    k_schedule<<<dim3(L.R, L.BH), 64, 0, st>>>((const uint8_t *)(ws + W.tier), L.Rg, L.tpr,
+    k_schedule<<<dim3(L.R, L.BH), 64, (L.Rg + 15) & ~15, st>>>((const uint8_t *)(ws + W.tier), L.Rg, L.tpr,
                                                 (int32_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
     // work order over query regions: tiles at capacity 64, pairs of tiles
     // (one four-wave workgroup each) at capacity 128
