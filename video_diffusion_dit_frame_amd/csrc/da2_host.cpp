@@ -98,7 +98,7 @@ void carve(da2_layout_s &L)
     W.tier = take(BH * G * G);
     W.sched = take(BH * R * R * 4);
     W.cnt = take(BH * R * kTargets * 4);
-    W.qord = take(BH * R * 4);
+    W.qord = take(BH * (R + 8) * 4);   // 8 shares of ceil(units / 8) slots per head
     W.rank_state = take(BH * kTargets * sizeof(RankState));
     W.rank_hist = take(BH * kTargets * 256 * 4);
     W.rank_eq = take(BH * (size_t)L.nchunk * kTargets * 4);

@@ -1366,21 +1366,21 @@ __global__ __launch_bounds__(64 * NW, 2) void k_attn(const AttnArgs A)
 
     // XCD-aware work mapping.  Workgroups are dealt to the 8 XCDs round robin
     // (block L runs on XCD L % 8).  Every XCD walks the heads in the same
-    // order and takes its own contiguous eighth (work slots j) of each head's
-    // query regions, so all XCDs work on the same head at a time and that
-    // head's key/value tiles (about 31 MB for a 720p Wan layer) stay in the
-    // shared last-level cache.  The plan's work order maps a slot to its
-    // query region (k_qorder: the share's regions are frame-fastest, ranked
-    // by kept tile count).
+    // order and takes its own eighth (work slots j) of each head's query
+    // regions, so all XCDs work on the same head at a time and that head's
+    // key/value tiles (about 31 MB for a 720p Wan layer) stay in the shared
+    // last-level cache.  The plan's work order maps a slot to its query
+    // region (k_qorder: an XCD's eighth of a head holds regions of about the
+    // same kept tile count, largest first; -1 marks an empty slot).
     const int R = A.R;                           // tiles
     const int QU = NW == 4 ? R / 2 : R;          // query regions
     const int span = (QU + 7) / 8;
     const int xcd = (int)(blockIdx.x & 7), kk = (int)(blockIdx.x >> 3);
     const int bh = kk / span;
     const int j = xcd * span + (kk - bh * span);
-    if (j >= QU)
+    const int au = sload_i32(A.qord + (int64_t)bh * 8 * span + j);
+    if (au < 0)   // an empty slot of the last share
         return;
-    const int au = sload_i32(A.qord + (int64_t)bh * QU + j);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int a = NW == 4 ? 2 * au + (w >> 1) : au;   // this wave's query tile
     const int64_t qblk = (int64_t)bh * R + a;

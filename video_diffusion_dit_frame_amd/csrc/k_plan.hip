@@ -778,40 +778,44 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
 
 // Attention work order.  The attention kernel deals its workgroups to the 8
 // XCDs round robin; XCD x takes work slots j = x*span .. x*span + span - 1
-// (span = ceil(R/8)) of every head.  The slots of a share start as its query
-// regions in frame-fastest order (regions at one spatial position in
-// consecutive latent frames keep largely the same key regions) and are then
-// ranked by kept tile count, largest first, ties in that order.  Workgroups
-// an XCD runs together then walk ascending key lists of similar length from
-// about the same time, so more of their tile reads hit its L2; the longest
-// workgroups of the last head also start first.  One workgroup per (share,
-// head); a share holds at most ceil(kMaxRegions / 8) regions.  The unit is a
-// query region of tpr tiles (its first tile's counts; every tile of a
-// region has the same list); qord holds R units per head.
-constexpr int kMaxShare = (kMaxRegions + 7) / 8;
-
-__global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt, int R, int RF, int tpr,
+// (span = ceil(U/8) units) of every head.  A head's units (query regions of
+// tpr tiles; a unit's first tile holds its counts) are ranked by kept tile
+// count, largest first, ties in frame-fastest order (regions at one spatial
+// position in consecutive latent frames keep largely the same key regions),
+// and cut into 8 shares of span consecutive ranks.  A share holds units of
+// about the same length: run together on one XCD, they walk their ascending
+// key lists at about the same pace, so their tile reads meet in that XCD's
+// L2.  XCD x takes share (x + h) mod 8 of head h, so over the heads every XCD
+// gets every share.  Slots of ranks past the last unit hold -1.
+// Grid: (ceil(U / 256), heads); U ints of LDS.
+__global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt, int U, int RF, int tpr,
                                                 int32_t *__restrict__ qord)
 {
-    __shared__ int32_t len[kMaxShare];
-    const int span = (R + 7) / 8, j0 = (int)blockIdx.x * span, bh = (int)blockIdx.y;
-    const int n = min(span, R - j0), NF = R / RF;
-    const int64_t row0 = (int64_t)bh * R;
-    for (int i = threadIdx.x; i < n; i += 256) {
-        const int j = j0 + i, a = (j % NF) * RF + j / NF;
+    extern __shared__ int32_t len[];
+    const int bh = (int)blockIdx.y, span = (U + 7) / 8, NF = U / RF;
+    const int64_t row0 = (int64_t)bh * U;
+    for (int a = threadIdx.x; a < U; a += 256) {
         const int32_t *c = cnt + ((row0 + a) * tpr) * kTargets;
-        len[i] = c[0] + c[1] + c[2];
+        len[a] = c[0] + c[1] + c[2];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) {
-        const int me = len[i];
+    int32_t *q = qord + (int64_t)bh * 8 * span;
+    const int rot = bh % 8;
+    const int a = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (a < U) {
+        const int me = len[a], fa = (a % RF) * NF + a / RF;
         int r = 0;
-        for (int k = 0; k < n; k++) {
-            const int o = len[k];
-            r += (o > me) | ((o == me) & (k < i));
+        for (int b = 0; b < U; b++) {
+            const int o = len[b], fb = (b % RF) * NF + b / RF;
+            r += (o > me) | ((o == me) & (fb < fa));
         }
-        const int j = j0 + i;
-        qord[row0 + j0 + r] = (j % NF) * RF + j / NF;
+        const int sh = r / span, i = r - sh * span;
+        q[((sh - rot + 8) % 8) * span + i] = a;
+    }
+    // the 8 span - U (at most 7) ranks past the last unit: empty slots
+    if (blockIdx.x == 0 && (int)threadIdx.x < 8 * span - U) {
+        const int r = U + (int)threadIdx.x, sh = r / span, i = r - sh * span;
+        q[((sh - rot + 8) % 8) * span + i] = -1;
     }
 }
 
@@ -910,12 +914,9 @@ void launch_schedule(const da2_layout_s &L, char *ws, hipStream_t st)
                                                 (int32_t *)(ws + W.sched), (int32_t *)(ws + W.cnt));
     // work order over query regions: tiles at capacity 64, pairs of tiles
     // (one four-wave workgroup each) at capacity 128
-    if (L.tpr == 2)
-        k_qorder<<<dim3(8, L.BH), 256, 0, st>>>((const int32_t *)(ws + W.cnt), L.Rg, L.Rfg, 2,
-                                                (int32_t *)(ws + W.qord));
-    else
-        k_qorder<<<dim3(8, L.BH), 256, 0, st>>>((const int32_t *)(ws + W.cnt), L.R, L.Rf, 1,
-                                                (int32_t *)(ws + W.qord));
+    const int U = L.tpr == 2 ? L.Rg : L.R, UF = L.tpr == 2 ? L.Rfg : L.Rf;
+    k_qorder<<<dim3((U + 255) / 256, L.BH), 256, sizeof(int32_t) * U, st>>>((const int32_t *)(ws + W.cnt), U, UF,
+                                                                            L.tpr, (int32_t *)(ws + W.qord));
 }
 
 void launch_import_tier(const da2_layout_s &L, const uint8_t *src, char *ws, hipStream_t st)
