@@ -294,3 +294,20 @@ def test_degenerate_budgets_and_single_region(d, hi, lo):
                 for a in range(R):
                     if not (tier[b, h, a] > 0).any():
                         assert (o[b, h, perm[a * 64:(a + 1) * 64]] == 0).all()
+
+
+# Region counts around the draft scoring's per-thread chunk boundaries
+# (256 key regions per chunk): one chunk, one full chunk, two chunks, and an
+# odd count over four.  (Counts past 2048 take the separate row-sum and key
+# kernels: the 8192-region test covers them.)
+@pytest.mark.parametrize("F,Hv,Wv", [(1, 8, 8 * 255), (1, 8, 8 * 256), (1, 8, 8 * 257), (3, 8, 8 * 331)])
+def test_draft_keys_chunk_boundaries(F, Hv, Wv):
+    d = 64
+    q, k, v = G.inputs(1, 1, F, Hv, Wv, d, 4000 + Wv, True)
+    P, qd, kd = G.run_plan(q, k, F, Hv, Wv, 1000, 3000)
+    ref = O.plan(q, k, F, Hv, Wv, 1000, 3000)
+    R = P.layout.R
+    assert R == F * Wv // 8
+    keys = G.host(P.debug("KEYS"), np.uint32).reshape(ref["keys"].shape)
+    assert np.array_equal(keys, ref["keys"])
+    assert np.array_equal(P.tier_map().cpu().numpy(), ref["tier"])

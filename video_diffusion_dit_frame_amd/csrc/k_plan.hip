@@ -321,6 +321,105 @@ __global__ __launch_bounds__(256) void k_keys(const double *__restrict__ La,
 }
 
 // ---------------------------------------------------------------------------
+// Row sums and keys in one pass, for region counts up to 256 * kSoftmaxNJMax:
+// one workgroup per kSoftmaxRows query regions of a head.  Every thread
+// forms the exponentials of its NJ key regions (b = t + 256 j) of both
+// branches and both rows once and keeps them in registers.  The row sums go
+// through LDS one 256-key chunk at a time: the workgroup writes chunk j, and
+// one lane per (row, branch) adds it to its running sum strictly in key
+// order (the same Z as k_rowsum).  Then every thread turns its registers
+// into p = e / Z, the mixture and the key, as k_keys does.  The logits are
+// read from HBM once and each exponential is formed once; the small LDS
+// footprint leaves room for eight workgroups per CU, whose in-order sums
+// run side by side.
+// ---------------------------------------------------------------------------
+constexpr int kSoftmaxRows = 2;    // query regions per workgroup
+constexpr int kSoftmaxNJMax = 8;   // key chunks of 256 per row (R <= 2048)
+
+template <int NJ>
+__global__ __launch_bounds__(256) void k_softmax_keys(const double *__restrict__ La,
+                                                      const double *__restrict__ Lm, int R, double lambda,
+                                                      const unsigned long long *__restrict__ rmax,
+                                                      double *__restrict__ zsum, uint32_t *__restrict__ keys)
+{
+    constexpr int NC = 2 * kSoftmaxRows;  // (row, branch) chains: c = 2 g + br
+    __shared__ double es[NC][257];        // one chunk; odd pitch: the summing lanes hit distinct banks
+    __shared__ double zs[NC];
+    const int a0 = blockIdx.x * kSoftmaxRows, bh = blockIdx.y, t = threadIdx.x;
+    double e[NC][NJ];
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+        const int a = a0 + (c >> 1), br = c & 1;
+        const double *L = (br ? Lm : La) + ((int64_t)bh * R + (a < R ? a : 0)) * R;
+        double x[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const int b = t + 256 * j;
+            x[j] = (a < R && b < R) ? L[b] : 0.0;
+        }
+        const double m = a < R ? unord64(rmax[((int64_t)bh * 2 + br) * R + a]) : 0.0;
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const int b = t + 256 * j;
+            e[c][j] = (a < R && b < R) ? exp_draft(x[j] - m) : 0.0;
+        }
+    }
+    const bool summer = t < NC && a0 + (t >> 1) < R;
+    double z = 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+        if (j)
+            __syncthreads();   // chunk j - 1 consumed
+#pragma unroll
+        for (int c = 0; c < NC; c++)
+            es[c][t] = e[c][j];
+        __syncthreads();
+        if (summer) {
+            const int nb = R - 256 * j < 256 ? R - 256 * j : 256;
+            const double *row = es[t];
+            int i = 0;
+            for (; i + 8 <= nb; i += 8) {
+                double v[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+                    v[u] = row[i + u];
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+                    z += v[u];
+            }
+            for (; i < nb; i++)
+                z += row[i];
+        }
+    }
+    if (summer) {
+        zs[t] = z;
+        zsum[((int64_t)bh * 2 + (t & 1)) * R + a0 + (t >> 1)] = z;
+    }
+    __syncthreads();
+    const double w0 = 1.0 - lambda;
+#pragma unroll
+    for (int g = 0; g < kSoftmaxRows; g++) {
+        const int a = a0 + g;
+        if (a >= R)
+            break;
+        const double za = zs[2 * g], zm = zs[2 * g + 1];
+        uint32_t *kr = keys + ((int64_t)bh * R + a) * R;
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+            const int b = t + 256 * j;
+            if (b < R) {
+                const double pa = e[2 * g][j] / za;
+                const double pm = e[2 * g + 1][j] / zm;
+                const double t0 = w0 * pa;
+                const double t1 = lambda * pm;
+                const double A = t0 + t1;
+                kr[b] = __float_as_uint((float)A);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Head-scope radix select for the kTargets cumulative thresholds T16,
 // T16 + T8 and T16 + T8 + T4 at once.
 // ---------------------------------------------------------------------------
@@ -791,24 +890,26 @@ __global__ __launch_bounds__(64) void k_schedule(const uint8_t *__restrict__ tie
 __global__ __launch_bounds__(256) void k_qorder(const int32_t *__restrict__ cnt, int U, int RF, int tpr,
                                                 int32_t *__restrict__ qord)
 {
-    extern __shared__ int32_t len[];
+    // one sort key per unit: tile count above (< 2^16), then the unit's
+    // frame-fastest position reversed (< U <= 2^13), so that the rank is the
+    // number of larger keys
+    extern __shared__ uint32_t okey[];
     const int bh = (int)blockIdx.y, span = (U + 7) / 8, NF = U / RF;
     const int64_t row0 = (int64_t)bh * U;
     for (int a = threadIdx.x; a < U; a += 256) {
         const int32_t *c = cnt + ((row0 + a) * tpr) * kTargets;
-        len[a] = c[0] + c[1] + c[2];
+        const uint32_t len = (uint32_t)(c[0] + c[1] + c[2]), fa = (uint32_t)((a % RF) * NF + a / RF);
+        okey[a] = (len << 16) | (0xffffu - fa);
     }
     __syncthreads();
     int32_t *q = qord + (int64_t)bh * 8 * span;
     const int rot = bh % 8;
     const int a = (int)blockIdx.x * 256 + (int)threadIdx.x;
     if (a < U) {
-        const int me = len[a], fa = (a % RF) * NF + a / RF;
+        const uint32_t me = okey[a];
         int r = 0;
-        for (int b = 0; b < U; b++) {
-            const int o = len[b], fb = (b % RF) * NF + b / RF;
-            r += (o > me) | ((o == me) & (fb < fa));
-        }
+        for (int b = 0; b < U; b++)
+            r += okey[b] > me;
         const int sh = r / span, i = r - sh * span;
         q[((sh - rot + 8) % 8) * span + i] = a;
     }
@@ -875,10 +976,24 @@ void launch_draft(const da2_layout_s &L, double lambda, char *ws, hipStream_t st
     double *La = (double *)(ws + W.la), *Lm = (double *)(ws + W.lm);
     unsigned long long *rmax = (unsigned long long *)(ws + W.rmax);
     double *zsum = (double *)(ws + W.zsum);
+    uint32_t *keys = (uint32_t *)(ws + W.keys);
     launch_draft_logits(L, ws, st);
+    const int nj = (L.Rg + 255) / 256;
+    if (nj <= kSoftmaxNJMax) {
+        const dim3 g((L.Rg + kSoftmaxRows - 1) / kSoftmaxRows, L.BH);
+        switch (nj) {
+        case 1: k_softmax_keys<1><<<g, 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys); break;
+        case 2: k_softmax_keys<2><<<g, 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys); break;
+        case 3: k_softmax_keys<3><<<g, 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys); break;
+        case 4: k_softmax_keys<4><<<g, 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys); break;
+        case 5: k_softmax_keys<5><<<g, 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys); break;
+        case 6: k_softmax_keys<6><<<g, 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys); break;
+        default: k_softmax_keys<8><<<g, 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys); break;
+        }
+        return;
+    }
     k_rowsum<<<dim3(T, L.BH, 2), 256, 0, st>>>(La, Lm, L.Rg, rmax, zsum);
-    k_keys<<<dim3(L.Rg, L.BH), 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum,
-                                            (uint32_t *)(ws + W.keys));
+    k_keys<<<dim3(L.Rg, L.BH), 256, 0, st>>>(La, Lm, L.Rg, lambda, rmax, zsum, keys);
 }
 
 void launch_rank(const da2_layout_s &L, int scope, int64_t t16, int64_t t8c, int64_t tk, char *ws,
