@@ -74,6 +74,13 @@ struct LogitStage {
     static constexpr int NV = MAXB ? TM * CK / 4 / 256 : TM * CK / 2 / 256;  // vectors per thread
     typename std::conditional<MAXB, float4, double2>::type x[NV], y[NV];
 
+    // Vector e of the stage: 16 consecutive rows per 16 lanes, and the
+    // row's channel vectors over the lane groups, so that the transposing
+    // LDS stores of one 16-lane group go to 16 consecutive rows (distinct
+    // banks) while the global loads still read 64 contiguous bytes per row.
+    static constexpr int VPR = MAXB ? CK / 4 : CK / 2;   // vectors per row
+    __device__ __forceinline__ static int row_of(int e) { return (e & 15) + 16 * (e / (16 * VPR)); }
+
     __device__ __forceinline__ void load(const void *qb_, const void *kb_, int a0, int b0, int R, int c0, int t)
     {
 #pragma unroll
@@ -81,7 +88,7 @@ struct LogitStage {
             const int e = t + 256 * i;
             if (MAXB) {
                 const float *qb = (const float *)qb_, *kb = (const float *)kb_;
-                const int r = e / (CK / 4), c = 4 * (e % (CK / 4));
+                const int r = row_of(e), c = 4 * ((e >> 4) & (CK / 4 - 1));
                 float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), yv = make_float4(0.f, 0.f, 0.f, 0.f);
                 if (a0 + r < R)
                     xv = *reinterpret_cast<const float4 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
@@ -91,7 +98,7 @@ struct LogitStage {
                 y[i] = *reinterpret_cast<decltype(&y[i])>(&yv);
             } else {
                 const double *qb = (const double *)qb_, *kb = (const double *)kb_;
-                const int r = e / (CK / 2), c = 2 * (e % (CK / 2));
+                const int r = row_of(e), c = 2 * ((e >> 4) & (CK / 2 - 1));
                 double2 xv = make_double2(0.0, 0.0), yv = make_double2(0.0, 0.0);
                 if (a0 + r < R)
                     xv = *reinterpret_cast<const double2 *>(qb + (int64_t)(a0 + r) * D + c0 + c);
@@ -110,13 +117,13 @@ struct LogitStage {
         for (int i = 0; i < NV; i++) {
             const int e = t + 256 * i;
             if (MAXB) {
-                const int r = e / (CK / 4), c = 4 * (e % (CK / 4));
+                const int r = row_of(e), c = 4 * ((e >> 4) & (CK / 4 - 1));
                 const float4 xv = *reinterpret_cast<const float4 *>(&x[i]);
                 const float4 yv = *reinterpret_cast<const float4 *>(&y[i]);
                 sq[c][r] = xv.x; sq[c + 1][r] = xv.y; sq[c + 2][r] = xv.z; sq[c + 3][r] = xv.w;
                 sk[c][r] = yv.x; sk[c + 1][r] = yv.y; sk[c + 2][r] = yv.z; sk[c + 3][r] = yv.w;
             } else {
-                const int r = e / (CK / 2), c = 2 * (e % (CK / 2));
+                const int r = row_of(e), c = 2 * ((e >> 4) & (CK / 2 - 1));
                 const double2 xv = *reinterpret_cast<const double2 *>(&x[i]);
                 const double2 yv = *reinterpret_cast<const double2 *>(&y[i]);
                 sq[c][r] = xv.x; sq[c + 1][r] = xv.y;
