@@ -103,11 +103,24 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
             *reinterpret_cast<uint4 *>(op16 + blk * (kBlk * D) + (int64_t)u * 8) = v;
         }
     }
-    // INT8 block step
-    float am = 0.0f;
-    for (int e = t; e < kBlk * D; e += 256)
-        am = fmaxf(am, __builtin_fabsf(bf16_to_f32(tile[e])));
-    am = wave_max_f32(am);
+    // operand chunks: t -> (half, kc, lane); 2*KC*64 = 2*D chunks per block,
+    // 32 values each, covering the tile once.  The chunk's values are read
+    // before the INT8 block step, whose absolute maximum is then the
+    // workgroup's maximum of the chunks' maxima (padding rows are zeros).
+    const bool chunk = t < 2 * D;
+    const int half = t / (KC * 64), kc = (t / 64) % KC, l = t & 63;
+    float xv[32];
+    float ga = 0.0f;
+    if (chunk) {
+        const int row = is_key ? key_of_row(l & 31, half) : 32 * half + (l & 31);
+        const uint16_t *src = tile + row * D + 64 * kc + 32 * (l >> 5);
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            xv[j] = bf16_to_f32(src[j]);
+            ga = fmaxf(ga, __builtin_fabsf(xv[j]));
+        }
+    }
+    float am = wave_max_f32(ga);
     if ((t & 63) == 0)
         red[t >> 6] = am;
     __syncthreads();
@@ -120,19 +133,7 @@ __global__ __launch_bounds__(256) void k_prep_qk(const uint16_t *__restrict__ x,
     if (t == 0)
         s8[blk] = sc;
 
-    // operand chunks: t -> (half, kc, lane); 2*KC*64 = 2*D chunks per block
-    if (t < 2 * D) {
-        const int half = t / (KC * 64), kc = (t / 64) % KC, l = t & 63;
-        const int row = is_key ? key_of_row(l & 31, half) : 32 * half + (l & 31);
-        const int c0 = 64 * kc + 32 * (l >> 5);
-        const uint16_t *src = tile + row * D + c0;
-        float xv[32];
-        float ga = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; j++) {
-            xv[j] = bf16_to_f32(src[j]);
-            ga = fmaxf(ga, __builtin_fabsf(xv[j]));
-        }
+    if (chunk) {
         uint32_t w8[8];
 #pragma unroll
         for (int q = 0; q < 8; q++)
